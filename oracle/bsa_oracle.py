@@ -1,0 +1,351 @@
+"""Plain fp64 CPU oracle for training-free block-sparse video-DiT attention.
+
+TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check of
+``__graft_entry__`` and the ``cpu_baseline`` leg of ``bench.py`` may import or
+call anything here.  The HIP library never uses it and shares no code with it.
+
+Everything is float64 numpy on ONE head at a time: ``X`` arrays are ``[N, d]``
+for the N valid tokens of one (batch, head) pair, flattened t-major
+(token n = (t * H_grid + y) * W_grid + x).  Inputs arrive as bf16 and are
+upcast exactly; nothing is blocked, fused or reordered beyond what the
+definitions below state.
+
+Sources (pages as titled):
+  [HVA]   "HyperVAttention: Efficient Sparse Attention with Spatio-Temporal
+          Clustering for Video Diffusion", section 2 (Preliminaries), Eq. 2-4,
+          and Appendix A.1 (Top-p, Min-kc).
+  [RSA]   "Rectified SpaAttn: Revisiting Attention Sparsity for Efficient Video
+          Generation", abstract: pooled query-key interactions.
+  [HyMoR] "HyMoR-Attn: Granularity-Matched Repair of Omitted Attention Support
+          for Video Diffusion", abstract: Macro backbone, Micro residual over
+          omitted blocks, exact LSE merging.
+  [LVSA]  "Long Video Sparse Attention" abstract (page titled "FreqFormer ..."):
+          structured window pattern plus rotating global anchors.
+  [MOD]   "Mixture of Distributions Matters: Dynamic Sparse Attention for
+          Efficient Video Diffusion Transformers", Metrics (density = computed
+          B x B blocks / total) and Block-wise Attention Computation.
+
+Readings where the pages are silent (each one is listed with its reason in the
+design notes of the repository):
+  * the ragged tail block holds only valid tokens; pooling averages over them
+    and attention never sees a padded key;
+  * top-k keeps ``k`` blocks ordered by (score descending, index ascending);
+  * top-p is inclusive ("at least p"), then clamped to [k_min, k_cap];
+  * forced blocks (diagonal, static window/anchors) are a union added after
+    top-k/top-p and are not counted in the budget;
+  * the micro rule is the 16-token pooled score restricted to omitted blocks,
+    top-m per 64-row query block (parity unpinned against the pages: HyMoR
+    gives no formula; it is pinned only against its own definition);
+  * LSE is the natural log of the softmax normaliser with the scale inside;
+    an empty support yields LSE = -inf and O = 0.
+"""
+
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+NEG_INF = -math.inf
+
+
+# ----------------------------------------------------------------------------
+# Blocks and pooling
+# ----------------------------------------------------------------------------
+
+def n_blocks(N: int, b: int) -> int:
+    """Number of b-token blocks covering N tokens (the last one may be ragged)."""
+    return -(-N // b)
+
+
+def block_tokens(N: int, b: int, j: int) -> np.ndarray:
+    """Indices of the valid tokens of block j: {b*j, ..., min(b*j+b, N) - 1}."""
+    return np.arange(b * j, min(b * j + b, N))
+
+
+def block_sizes(N: int, b: int) -> np.ndarray:
+    """Valid token count of every block (the cluster sizes s_j of [HVA] Eq. 2)."""
+    return np.array([len(block_tokens(N, b, j)) for j in range(n_blocks(N, b))],
+                    dtype=np.float64)
+
+
+def pool_means(X: np.ndarray, b: int) -> np.ndarray:
+    """Per-block mean of the token vectors.
+
+    [RSA] pools queries and keys over blocks; [HVA] section 2 defines a
+    centroid as the mean of its members.  Only valid tokens count.
+    """
+    X = np.asarray(X, dtype=np.float64)
+    N = X.shape[0]
+    return np.stack([X[block_tokens(N, b, j)].mean(axis=0)
+                     for j in range(n_blocks(N, b))])
+
+
+def pooled_scores(Qbar: np.ndarray, Kbar: np.ndarray, scale: float) -> np.ndarray:
+    """Centroid-level logits S_ij = <mu_i^q, mu_j^k> * scale ([HVA] Eq. 2, left)."""
+    return scale * (np.asarray(Qbar, np.float64) @ np.asarray(Kbar, np.float64).T)
+
+
+# ----------------------------------------------------------------------------
+# Selection
+# ----------------------------------------------------------------------------
+
+def rank_desc(values: np.ndarray) -> np.ndarray:
+    """Indices ordered by value descending, ties by index ascending."""
+    values = np.asarray(values, dtype=np.float64)
+    idx = np.arange(values.shape[0])
+    return np.lexsort((idx, -values))
+
+
+def topk_set(score_row: np.ndarray, k: int) -> set[int]:
+    """The k key blocks with the highest pooled score (density budget of
+    [MOD] / Top-K selection); ties go to the lower block index."""
+    order = rank_desc(score_row)
+    return set(int(j) for j in order[:max(0, k)])
+
+
+def size_weighted_softmax(score_row: np.ndarray, sizes: np.ndarray) -> np.ndarray:
+    """P'_ij = s_j exp(S_ij) / sum_o s_o exp(S_io)  ([HVA] Eq. 2, right)."""
+    s = np.asarray(score_row, dtype=np.float64)
+    w = np.asarray(sizes, dtype=np.float64) * np.exp(s - s.max())
+    return w / w.sum()
+
+
+def topp_length(P: np.ndarray, p: float) -> int:
+    """Size of TopP(P; p): the smallest prefix, in descending order of P, whose
+    cumulative probability is at least p ([HVA] Eq. 3)."""
+    order = rank_desc(P)
+    c = np.cumsum(P[order])
+    hit = np.nonzero(c >= p)[0]
+    return int(hit[0]) + 1 if hit.size else int(P.shape[0])
+
+
+def topp_set(score_row: np.ndarray, sizes: np.ndarray, p: float,
+             k_min: int = 1, k_cap: int | None = None) -> set[int]:
+    """Top-p over the size-weighted centroid softmax, clamped to
+    [k_min, k_cap] blocks ([HVA] Eq. 2-3; Min-kc of Appendix A.1 as a floor,
+    the density cap as a ceiling)."""
+    P = size_weighted_softmax(score_row, sizes)
+    n = P.shape[0]
+    L = topp_length(P, p)
+    L = max(L, k_min)
+    if k_cap is not None:
+        L = min(L, k_cap)
+    L = min(L, n)
+    order = rank_desc(P)
+    return set(int(j) for j in order[:L])
+
+
+def block_frame_span(N: int, b: int, frame_tokens: int, j: int) -> tuple[int, int]:
+    """Lowest and highest latent frame index touched by block j (t-major
+    layout: token n lies in frame n // frame_tokens)."""
+    toks = block_tokens(N, b, j)
+    return int(toks[0]) // frame_tokens, int(toks[-1]) // frame_tokens
+
+
+def window_anchor_set(N: int, b: int, i: int, frame_tokens: int,
+                      window_frames: int, n_anchors: int,
+                      anchor_offset: int) -> set[int]:
+    """Static block mask of [LVSA]: a temporal window plus rotating global
+    anchors.
+
+    Window: key block j is kept for query block i when some token of j lies
+    within ``window_frames`` latent frames of some token of i.
+    Anchors: ``n_anchors`` key blocks evenly strided over the sequence,
+    rotated by ``anchor_offset`` (the rotation the caller draws per call).
+    """
+    nB = n_blocks(N, b)
+    lo_i, hi_i = block_frame_span(N, b, frame_tokens, i)
+    out = set()
+    for j in range(nB):
+        lo_j, hi_j = block_frame_span(N, b, frame_tokens, j)
+        if lo_j <= hi_i + window_frames and hi_j >= lo_i - window_frames:
+            out.add(j)
+    if n_anchors > 0:
+        stride = nB // n_anchors
+        for a in range(n_anchors):
+            out.add((anchor_offset + a * stride) % nB)
+    return out
+
+
+def select_rows(scores: np.ndarray | None, N: int, b: int, mode: str, *,
+                k: int = 0, p: float = 0.9, k_min: int = 1,
+                k_cap: int | None = None, force_diag: bool = False,
+                static: dict | None = None) -> list[list[int]]:
+    """Per query block, the ascending list of selected key blocks for one head.
+
+    ``mode`` is "topk", "topp" or "static".  The forced set (the diagonal
+    and/or the [LVSA] window+anchors ``static`` mask) is a union on top of the
+    scored selection.
+    """
+    nB = n_blocks(N, b)
+    sizes = block_sizes(N, b)
+    rows = []
+    for i in range(nB):
+        if mode == "topk":
+            sel = topk_set(scores[i], k)
+        elif mode == "topp":
+            sel = topp_set(scores[i], sizes, p, k_min, k_cap)
+        elif mode == "static":
+            sel = set()
+        else:
+            raise ValueError(mode)
+        if force_diag:
+            sel.add(i)
+        if static is not None:
+            sel |= window_anchor_set(N, b, i, **static)
+        rows.append(sorted(sel))
+    return rows
+
+
+def density(rows_per_head: list[list[list[int]]], nB: int) -> float:
+    """Computed B x B blocks over all blocks ([MOD] Metrics)."""
+    tot = sum(len(r) for rows in rows_per_head for r in rows)
+    return tot / (len(rows_per_head) * nB * nB)
+
+
+# ----------------------------------------------------------------------------
+# Attention over a support
+# ----------------------------------------------------------------------------
+
+def attend(q: np.ndarray, K: np.ndarray, V: np.ndarray, scale: float):
+    """Scaled dot-product attention of queries q [m,d] over keys K,V [n,d].
+
+    Returns (O [m,d], LSE [m]) with LSE_t = ln sum_tau exp(scale q_t . k_tau).
+    An empty key set gives O = 0 and LSE = -inf.
+    """
+    q = np.asarray(q, np.float64)
+    m, d = q.shape
+    if K.shape[0] == 0:
+        return np.zeros((m, V.shape[1])), np.full(m, NEG_INF)
+    z = scale * (q @ np.asarray(K, np.float64).T)
+    mx = z.max(axis=1, keepdims=True)
+    e = np.exp(z - mx)
+    s = e.sum(axis=1)
+    lse = mx[:, 0] + np.log(s)
+    O = (e @ np.asarray(V, np.float64)) / s[:, None]
+    return O, lse
+
+
+def block_sparse_attention(Q, K, V, rows: list[list[int]], b: int, scale: float):
+    """O_i = Attn(Q_i, {K_j, V_j}_{j in A_i}) for every query block i
+    ([HVA] Eq. 4 with the identity permutation; the [HyMoR] Macro backbone).
+
+    Restricting each query block to the tokens of its selected key blocks is
+    the same as dense softmax(scale Q K^T + M) V with M in {0, -inf}.
+    """
+    Q = np.asarray(Q, np.float64)
+    N, d = Q.shape
+    O = np.zeros((N, V.shape[1]))
+    L = np.full(N, NEG_INF)
+    for i, sel in enumerate(rows):
+        qi = block_tokens(N, b, i)
+        keys = (np.concatenate([block_tokens(N, b, j) for j in sel])
+                if len(sel) else np.zeros(0, dtype=np.int64))
+        O[qi], L[qi] = attend(Q[qi], K[keys], V[keys], scale)
+    return O, L
+
+
+def dense_attention(Q, K, V, scale: float):
+    """Full attention over all N keys (the dense baseline)."""
+    return attend(Q, K, V, scale)
+
+
+# ----------------------------------------------------------------------------
+# Micro residual ([HyMoR]) and the exact LSE merge
+# ----------------------------------------------------------------------------
+
+def micro_candidates(Qt: np.ndarray, Kt: np.ndarray, macro_row: list[int], i: int,
+                     N: int, b: int, u: int, scale: float):
+    """All micro candidates of query block i: pairs (a, beta) where a indexes
+    the u-token query sub-tiles of block i and beta a u-token key tile whose
+    enclosing b-block was omitted by the macro selection.  Score
+    sigma = scale <Qt_{(b/u) i + a}, Kt_beta> on u-token pooled means.
+
+    Returns a list of (sigma, code) with code = (b/u) * beta + a.
+    """
+    r = b // u
+    nT = n_blocks(N, u)
+    omitted = np.ones(n_blocks(N, b), dtype=bool)
+    omitted[list(macro_row)] = False
+    out = []
+    for a in range(r):
+        qa = r * i + a
+        if qa >= nT:
+            continue
+        for beta in range(nT):
+            if not omitted[beta // r]:
+                continue
+            sigma = scale * float(Qt[qa] @ Kt[beta])
+            out.append((sigma, r * beta + a))
+    return out
+
+
+def micro_select_row(Qt, Kt, macro_row, i, N, b, u, scale, m):
+    """Online peak-preserving Micro selection for one query block: the top-m
+    candidates by (sigma descending, code ascending), returned as codes sorted
+    by (sub-tile a, key tile beta)."""
+    cand = micro_candidates(Qt, Kt, macro_row, i, N, b, u, scale)
+    cand.sort(key=lambda t: (-t[0], t[1]))
+    r = b // u
+    kept = [c for _, c in cand[:max(0, m)]]
+    kept.sort(key=lambda c: (c % r, c // r))
+    return kept
+
+
+def micro_attention(Q, K, V, micro_rows: list[list[int]], b: int, u: int,
+                    scale: float):
+    """Micro residual: each u-row query sub-tile attends over the union of its
+    selected u-key tiles.  Sub-tiles with no tile get O = 0, LSE = -inf."""
+    Q = np.asarray(Q, np.float64)
+    N, d = Q.shape
+    r = b // u
+    O = np.zeros((N, V.shape[1]))
+    L = np.full(N, NEG_INF)
+    for i, codes in enumerate(micro_rows):
+        for a in range(r):
+            qa = r * i + a
+            if qa * u >= N:
+                continue
+            qi = block_tokens(N, u, qa)
+            tiles = [c // r for c in codes if c % r == a]
+            keys = (np.concatenate([block_tokens(N, u, t) for t in tiles])
+                    if tiles else np.zeros(0, dtype=np.int64))
+            O[qi], L[qi] = attend(Q[qi], K[keys], V[keys], scale)
+    return O, L
+
+
+def lse_merge(O1, L1, O2, L2):
+    """Exact merge of two partial softmax results over disjoint supports
+    ([HyMoR] exact LSE merging):
+        L = ln(e^L1 + e^L2),  O = e^(L1 - L) O1 + e^(L2 - L) O2.
+    Both empty (L1 = L2 = -inf) gives O = 0, L = -inf."""
+    O1 = np.asarray(O1, np.float64)
+    O2 = np.asarray(O2, np.float64)
+    L1 = np.asarray(L1, np.float64)
+    L2 = np.asarray(L2, np.float64)
+    L = np.logaddexp(L1, L2)
+    both_empty = np.isneginf(L)
+    Ls = np.where(both_empty, 0.0, L)
+    w1 = np.where(np.isneginf(L1), 0.0, np.exp(L1 - Ls))
+    w2 = np.where(np.isneginf(L2), 0.0, np.exp(L2 - Ls))
+    O = w1[:, None] * O1 + w2[:, None] * O2
+    O[both_empty] = 0.0
+    return O, L
+
+
+# ----------------------------------------------------------------------------
+# Work accounting
+# ----------------------------------------------------------------------------
+
+def executed_flops(d: int, b: int, nnz_macro: int, u: int = 16,
+                   nnz_micro: int = 0) -> int:
+    """Tile-level work of the two attention passes: 4 d b^2 flops per selected
+    (query block, key block) pair and 4 d u^2 per micro tile (QK^T and PV,
+    two flops per multiply-add), tails counted as full tiles."""
+    return 4 * d * (b * b * nnz_macro + u * u * nnz_micro)
+
+
+def dense_flops(B: int, H: int, N: int, d: int) -> int:
+    """4 B H N^2 d flops of full attention over the valid tokens."""
+    return 4 * B * H * N * N * d

@@ -1,0 +1,13 @@
+"""Seeded synthetic video-DiT Q/K/V generator shared by the tests and the bench.
+
+Holds no attention, pooling or selection arithmetic: it only draws inputs.
+"""
+
+from .video_qkv import (  # noqa: F401
+    CONFIGS,
+    VideoSpec,
+    config_spec,
+    gen_qkv,
+    micro_heads,
+    rotation_offset,
+)

@@ -1,0 +1,370 @@
+"""Pins of the fp64 oracle against facts that do not come from the oracle:
+hand-worked fixtures, closed forms, invariants, library special cases and
+brute force on tiny inputs.  CPU only."""
+
+import itertools
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import scipy.special
+import torch
+
+from oracle import bsa_oracle as O
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _load(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+def _rand(seed, *shape):
+    return np.random.default_rng(seed).standard_normal(shape)
+
+
+# --------------------------------------------------------------- pooling / score
+
+def test_golden_pooled_score():
+    g = _load("pooled_score.json")
+    Q, K = np.array(g["Q"], float), np.array(g["K"], float)
+    Qb, Kb = O.pool_means(Q, g["b"]), O.pool_means(K, g["b"])
+    np.testing.assert_array_equal(Qb, g["Qbar"])
+    np.testing.assert_array_equal(Kb, g["Kbar"])
+    np.testing.assert_array_equal(O.pooled_scores(Qb, Kb, g["scale"]), g["S"])
+
+
+def test_pooled_score_is_mean_of_token_logits():
+    # bilinearity: <mean q, mean k> = mean over all token pairs of <q, k>,
+    # written out with explicit loops over tokens
+    N, b, d, s = 150, 64, 8, 0.3
+    Q, K = _rand(1, N, d), _rand(2, N, d)
+    S = O.pooled_scores(O.pool_means(Q, b), O.pool_means(K, b), s)
+    nB = O.n_blocks(N, b)
+    for i in range(nB):
+        for j in range(nB):
+            ti = range(b * i, min(b * i + b, N))
+            tj = range(b * j, min(b * j + b, N))
+            acc = 0.0
+            for t in ti:
+                for tau in tj:
+                    acc += s * sum(Q[t, c] * K[tau, c] for c in range(d))
+            assert abs(S[i, j] - acc / (len(ti) * len(tj))) < 1e-12
+
+
+def test_pool_constant_blocks_and_ragged_tail():
+    N, b, d = 64 * 3 + 5, 64, 4
+    X = np.zeros((N, d))
+    for j in range(4):
+        X[64 * j:64 * j + 64] = j + 0.5
+    P = O.pool_means(X, b)
+    np.testing.assert_array_equal(P[:, 0], [0.5, 1.5, 2.5, 3.5])
+    # tail mean uses only the 5 valid tokens
+    X2 = np.ones((N, d))
+    X2[-5:] = 7.0
+    assert O.pool_means(X2, b)[-1, 0] == 7.0
+    np.testing.assert_array_equal(O.block_sizes(N, b), [64, 64, 64, 5])
+
+
+# ------------------------------------------------------------------- top-k
+
+def test_topk_is_best_subset_by_brute_force():
+    rng = np.random.default_rng(3)
+    for trial in range(30):
+        n = int(rng.integers(2, 10))
+        k = int(rng.integers(1, n + 1))
+        row = rng.standard_normal(n)
+        best = max(itertools.combinations(range(n), k),
+                   key=lambda c: sum(row[j] for j in c))
+        assert O.topk_set(row, k) == set(best)
+
+
+def test_topk_ties_go_to_lower_index():
+    row = np.array([1.0, 3.0, 3.0, 2.0, 3.0])
+    assert O.topk_set(row, 1) == {1}
+    assert O.topk_set(row, 2) == {1, 2}
+    assert O.topk_set(row, 3) == {1, 2, 4}
+    assert O.topk_set(row, 4) == {1, 2, 3, 4}
+    assert O.topk_set(row, 0) == set()
+
+
+def test_select_rows_topk_with_diagonal_union():
+    S = np.array([[0.0, 5.0, 4.0], [9.0, 0.0, 1.0], [3.0, 2.0, 1.0]])
+    rows = O.select_rows(S, 3 * 64, 64, "topk", k=1, force_diag=True)
+    assert rows == [[0, 1], [0, 1], [0, 2]]
+
+
+# ------------------------------------------------------------------- top-p
+
+def test_golden_topp():
+    g = _load("topp_size_weighted.json")
+    for c in g["cases"]:
+        P = O.size_weighted_softmax(np.array(c["scores"]), np.array(c["sizes"], float))
+        np.testing.assert_allclose(P, c["P"], atol=c.get("P_tol", 1e-12))
+        for p, want in c["by_p"].items():
+            got = O.topp_set(np.array(c["scores"]), np.array(c["sizes"], float),
+                             float(p), k_min=1)
+            assert got == set(want), (c["note"], p)
+
+
+def test_topp_matches_brute_force_smallest_set():
+    # TopP = smallest set whose mass is at least p; among sets of that size the
+    # heaviest (unique for distinct masses)
+    rng = np.random.default_rng(4)
+    for trial in range(40):
+        n = int(rng.integers(1, 9))
+        row = rng.standard_normal(n) * 2
+        sizes = rng.integers(1, 65, size=n).astype(float)
+        p = float(rng.uniform(0.05, 0.99))
+        P = sizes * np.exp(row)
+        P /= P.sum()
+        best = None
+        for L in range(1, n + 1):
+            sets = [c for c in itertools.combinations(range(n), L)
+                    if sum(P[j] for j in c) >= p]
+            if sets:
+                best = max(sets, key=lambda c: sum(P[j] for j in c))
+                break
+        assert O.topp_set(row, sizes, p) == set(best)
+
+
+def test_topp_uniform_16_blocks_keeps_15():
+    # 16 equal blocks at p = 0.9: 14 blocks hold 0.875 < 0.9, 15 hold 0.9375
+    assert len(O.topp_set(np.zeros(16), np.full(16, 64.0), 0.9)) == 15
+
+
+def test_topp_equal_sizes_is_plain_softmax():
+    row = _rand(5, 40)
+    np.testing.assert_allclose(O.size_weighted_softmax(row, np.full(40, 64.0)),
+                               scipy.special.softmax(row), rtol=1e-13)
+
+
+def test_topp_clamps_to_kmin_and_cap():
+    row = np.array([10.0, 0.0, 0.0, 0.0, 0.0])
+    sz = np.full(5, 64.0)
+    assert O.topp_set(row, sz, 0.5) == {0}
+    assert len(O.topp_set(row, sz, 0.5, k_min=3)) == 3
+    flat = np.zeros(5)
+    assert len(O.topp_set(flat, sz, 0.99, k_cap=2)) == 2
+
+
+# ------------------------------------------------------------- static mask
+
+def test_golden_static_window_anchor():
+    g = _load("static_window_anchor.json")
+    for c in g["cases"]:
+        nB = O.n_blocks(c["N"], c["b"])
+        rows = [sorted(O.window_anchor_set(
+            c["N"], c["b"], i, c["frame_tokens"], c["window_frames"],
+            c["n_anchors"], c["anchor_offset"])) for i in range(nB)]
+        assert rows == c["rows"], c["note"]
+
+
+def test_static_window_matches_token_level_brute_force():
+    # window rule at block level == "some token pair within r frames"
+    for (T, Hg, Wg, b, r) in [(5, 3, 5, 8, 1), (7, 2, 3, 16, 2), (4, 4, 4, 64, 0),
+                              (6, 3, 7, 10, 1)]:
+        N, ft = T * Hg * Wg, Hg * Wg
+        nB = O.n_blocks(N, b)
+        for i in range(nB):
+            got = O.window_anchor_set(N, b, i, ft, r, 0, 0)
+            want = set()
+            for j in range(nB):
+                for t in range(b * i, min(b * i + b, N)):
+                    if any(abs(t // ft - tau // ft) <= r
+                           for tau in range(b * j, min(b * j + b, N))):
+                        want.add(j)
+                        break
+            assert got == want
+
+
+def test_static_anchor_rotation_and_density_at_long_horizon():
+    # 126 x 30 x 52 tokens, 64-blocks, 1-frame window, 4 anchors
+    N, b, ft = 126 * 30 * 52, 64, 30 * 52
+    nB = O.n_blocks(N, b)
+    assert nB == 3072
+    a0 = O.window_anchor_set(N, b, 1500, ft, 0, 4, 0) - \
+        O.window_anchor_set(N, b, 1500, ft, 0, 0, 0)
+    assert a0 <= {0, 768, 1536, 2304}
+    anchors = {(5 + a * 768) % nB for a in range(4)}
+    assert anchors <= O.window_anchor_set(N, b, 100, ft, 1, 4, 5)
+    # average row length of the literal 1-frame window + 4 anchors
+    tot = sum(len(O.window_anchor_set(N, b, i, ft, 1, 4, 5)) for i in range(0, nB, 7))
+    avg = tot / len(range(0, nB, 7))
+    assert 75 < avg < 82  # about 2.5% of 3072 blocks
+
+
+# --------------------------------------------------------------- attention
+
+def test_golden_attention_two_keys():
+    g = _load("attention_two_keys.json")
+    Ov, L = O.attend(np.array(g["q"]), np.array(g["K"]), np.array(g["V"]), g["scale"])
+    np.testing.assert_allclose(Ov, g["O"], atol=1e-12)
+    np.testing.assert_allclose(L, g["LSE"], atol=1e-12)
+
+
+def test_all_blocks_equals_torch_sdpa_fp64():
+    N, d, b = 200, 16, 64
+    s = 1 / math.sqrt(d)
+    Q, K, V = _rand(6, N, d), _rand(7, N, d), _rand(8, N, d)
+    rows = [list(range(O.n_blocks(N, b)))] * O.n_blocks(N, b)
+    Ov, L = O.block_sparse_attention(Q, K, V, rows, b, s)
+    tq, tk, tv = (torch.from_numpy(x)[None, None] for x in (Q, K, V))
+    ref = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, scale=s)
+    np.testing.assert_allclose(Ov, ref[0, 0].numpy(), atol=1e-12)
+    lse = torch.logsumexp(s * (tq[0, 0] @ tk[0, 0].T), dim=-1).numpy()
+    np.testing.assert_allclose(L, lse, atol=1e-12)
+
+
+def test_block_mask_equals_masked_dense_softmax():
+    # restricted attention == softmax(sQK^T + M)V with M in {0,-inf}, built
+    # by torch on the full matrix
+    N, d, b = 150, 8, 64
+    s = 0.37
+    Q, K, V = _rand(9, N, d), _rand(10, N, d), _rand(11, N, d)
+    rows = [[0, 2], [1], [0, 1, 2]]
+    Ov, L = O.block_sparse_attention(Q, K, V, rows, b, s)
+    M = torch.full((N, N), -math.inf, dtype=torch.float64)
+    for i, sel in enumerate(rows):
+        for j in sel:
+            M[b * i:b * i + b, b * j:b * j + b] = 0.0
+    logits = s * torch.from_numpy(Q) @ torch.from_numpy(K).T + M
+    ref = torch.softmax(logits, -1) @ torch.from_numpy(V)
+    np.testing.assert_allclose(Ov, ref.numpy(), atol=1e-12)
+    np.testing.assert_allclose(L, torch.logsumexp(logits, -1).numpy(), atol=1e-12)
+
+
+def test_zero_query_gives_mean_of_values():
+    N, d, b = 130, 4, 64
+    Q = np.zeros((N, d))
+    K, V = _rand(12, N, d), _rand(13, N, d)
+    rows = [[1, 2], [0], [2]]
+    Ov, L = O.block_sparse_attention(Q, K, V, rows, b, 0.5)
+    np.testing.assert_allclose(Ov[0], V[64:130].mean(0), atol=1e-13)
+    np.testing.assert_allclose(L[0], math.log(66), atol=1e-13)
+    np.testing.assert_allclose(Ov[129], V[128:130].mean(0), atol=1e-13)
+    np.testing.assert_allclose(L[129], math.log(2), atol=1e-13)
+
+
+def test_single_key_support():
+    N, d, b = 65, 4, 64
+    Q, K, V = _rand(14, N, d), _rand(15, N, d), _rand(16, N, d)
+    Ov, L = O.block_sparse_attention(Q, K, V, [[1], [1]], b, 0.5)
+    np.testing.assert_allclose(Ov, np.repeat(V[64:65], N, 0), atol=1e-14)
+    np.testing.assert_allclose(L, 0.5 * Q @ K[64], atol=1e-13)
+
+
+def test_empty_row_gives_zero_and_neg_inf():
+    Q, K, V = _rand(17, 70, 4), _rand(18, 70, 4), _rand(19, 70, 4)
+    Ov, L = O.block_sparse_attention(Q, K, V, [[], [0]], 64, 0.5)
+    assert np.all(Ov[:64] == 0) and np.all(np.isneginf(L[:64]))
+    assert np.all(np.isfinite(L[64:]))
+
+
+# ------------------------------------------------------------------- merge
+
+def test_merge_of_disjoint_supports_equals_union():
+    rng = np.random.default_rng(20)
+    N, d, s = 90, 6, 0.4
+    Q, K, V = _rand(21, N, d), _rand(22, N, d), _rand(23, N, d)
+    for trial in range(10):
+        perm = rng.permutation(N)
+        cut = int(rng.integers(1, N))
+        S1, S2 = np.sort(perm[:cut]), np.sort(perm[cut:])
+        O1, L1 = O.attend(Q, K[S1], V[S1], s)
+        O2, L2 = O.attend(Q, K[S2], V[S2], s)
+        Om, Lm = O.lse_merge(O1, L1, O2, L2)
+        Ou, Lu = O.attend(Q, K, V, s)
+        np.testing.assert_allclose(Om, Ou, atol=1e-12)
+        np.testing.assert_allclose(Lm, Lu, atol=1e-12)
+
+
+def test_merge_with_empty_parts():
+    O1, L1 = _rand(24, 3, 4), np.array([0.3, -1.0, 2.0])
+    Oe, Le = np.zeros((3, 4)), np.full(3, -math.inf)
+    Om, Lm = O.lse_merge(O1, L1, Oe, Le)
+    np.testing.assert_allclose(Om, O1, atol=1e-15)
+    np.testing.assert_allclose(Lm, L1, atol=1e-15)
+    Om, Lm = O.lse_merge(Oe, Le, O1, L1)
+    np.testing.assert_allclose(Om, O1, atol=1e-15)
+    Om, Lm = O.lse_merge(Oe, Le, Oe, Le)
+    assert np.all(Om == 0) and np.all(np.isneginf(Lm))
+
+
+# ------------------------------------------------------------------- micro
+
+def test_micro_score_is_mean_of_tile_logits():
+    N, b, u, d, s = 140, 64, 16, 4, 0.25
+    Q, K = _rand(25, N, d), _rand(26, N, d)
+    Qt, Kt = O.pool_means(Q, u), O.pool_means(K, u)
+    cand = O.micro_candidates(Qt, Kt, [1], 0, N, b, u, s)
+    codes = {c for _, c in cand}
+    # omitted blocks are 0 and 2 -> key tiles 0..3 and 8 (tile 8 = tokens 128..139)
+    assert {c // 4 for c in codes} == {0, 1, 2, 3, 8}
+    assert {c % 4 for c in codes} == {0, 1, 2, 3}
+    for sig, c in cand:
+        a, beta = c % 4, c // 4
+        qi = range(16 * a, 16 * a + 16)
+        kj = range(16 * beta, min(16 * beta + 16, N))
+        want = np.mean([s * Q[t] @ K[tau] for t in qi for tau in kj])
+        assert abs(sig - want) < 1e-12
+
+
+def test_micro_select_order_and_ties():
+    Qt = np.ones((8, 1))
+    Kt = np.array([[3.0], [1.0], [3.0], [2.0], [9.0], [9.0], [9.0], [9.0]])
+    # macro keeps block 1 (tiles 4..7), so candidates are tiles 0..3
+    got = O.micro_select_row(Qt, Kt, [1], 0, 128, 64, 16, 1.0, 3)
+    # tiles 0 and 2 score 3 for every sub-tile a; ranked by code 4*beta+a:
+    # (0,a=0)=0,(0,1)=1,(0,2)=2 win; output sorted by (a, beta)
+    assert got == [0, 1, 2]
+    got = O.micro_select_row(Qt, Kt, [1], 0, 128, 64, 16, 1.0, 6)
+    assert got == [0, 8, 1, 9, 2, 3]
+
+
+def test_macro_plus_all_micro_equals_full_attention():
+    N, b, u, d = 64 * 4 + 20, 64, 16, 8
+    s = 1 / math.sqrt(d)
+    Q, K, V = _rand(27, N, d), _rand(28, N, d), _rand(29, N, d)
+    S = O.pooled_scores(O.pool_means(Q, b), O.pool_means(K, b), s)
+    rows = O.select_rows(S, N, b, "topk", k=2, force_diag=True)
+    Qt, Kt = O.pool_means(Q, u), O.pool_means(K, u)
+    mrows = [O.micro_select_row(Qt, Kt, rows[i], i, N, b, u, s, 10 ** 6)
+             for i in range(len(rows))]
+    Om, Lm = O.block_sparse_attention(Q, K, V, rows, b, s)
+    Ou, Lu = O.micro_attention(Q, K, V, mrows, b, u, s)
+    Of, Lf = O.lse_merge(Om, Lm, Ou, Lu)
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        *(torch.from_numpy(x)[None, None] for x in (Q, K, V)), scale=s)[0, 0].numpy()
+    np.testing.assert_allclose(Of, ref, atol=1e-12)
+    np.testing.assert_allclose(
+        Lf, scipy.special.logsumexp(s * Q @ K.T, axis=1), atol=1e-12)
+
+
+def test_flop_accounting():
+    assert O.executed_flops(128, 64, 1) == 4 * 128 * 64 * 64
+    assert O.dense_flops(1, 12, 32760, 128) == 4 * 12 * 32760 ** 2 * 128
+    assert O.executed_flops(64, 64, 0, 16, 3) == 4 * 64 * 256 * 3
+
+
+@pytest.mark.parametrize("mistake", ["scale", "tail"])
+def test_pins_catch_planted_mistakes(mistake, monkeypatch):
+    """A plausible slip in the oracle must fail a pin: plant it and check."""
+    N, d, b = 200, 16, 64
+    s = 1 / math.sqrt(d)
+    Q, K, V = _rand(6, N, d), _rand(7, N, d), _rand(8, N, d)
+    if mistake == "scale":
+        real = O.attend
+        monkeypatch.setattr(O, "attend", lambda q, k, v, sc: real(q, k, v, sc * 1.01))
+    else:
+        # a ragged tail "padded" by wrapping around to the first tokens
+        monkeypatch.setattr(O, "block_tokens",
+                            lambda N_, b_, j: np.arange(b_ * j, b_ * j + b_) % N_)
+    rows = [list(range(O.n_blocks(N, b)))] * O.n_blocks(N, b)
+    Ov, _ = O.block_sparse_attention(Q, K, V, rows, b, s)
+    tq, tk, tv = (torch.from_numpy(x)[None, None] for x in (Q, K, V))
+    ref = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, scale=s)
+    assert not np.allclose(Ov, ref[0, 0].numpy(), atol=1e-9)
