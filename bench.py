@@ -1,0 +1,223 @@
+#!/usr/bin/env python
+"""Benchmark of the block-sparse video-DiT attention hot path on one MI355X.
+
+One step = pooled scoring (bsa_score_blocks) + top-k block selection
+(bsa_select_blocks) + block-sparse attention (bsa_sparse_attn_fwd, including
+its fp16 V^T staging) over one layer shaped like Wan-2.1-1.3B at 480p:
+B=1, H=12, d=128, 21x30x52 = 32760 tokens, 64-token blocks, top-k at 25%
+density (k = 128 of 512 key blocks).  Inputs are the seeded synthetic
+generator's bf16 Q/K/V, resident in HBM before timing starts.
+
+Prints ONE JSON line.  `value` is the executed attention TFLOP of a step
+divided by the whole step time.  Kernel-level figures (the attention kernel
+alone, measured with HIP events on the stream it runs on), the speedup over
+the library's dense flash attention, per-stage times, the roofline entry of
+the dominant kernel and the fp64 CPU oracle timed on a bounded sample of the
+same workload are reported beside it.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "block-sparse attn executed TFLOP/s, % bf16 MFMA peak, speedup vs dense"
+PEAK_TFLOPS = 2500.0   # MI355X dense bf16/fp16 matrix peak
+HBM_GBS = 8000.0       # MI355X HBM3E
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+                    help="time budget of the CPU oracle sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--stage-reps", type=int, default=10)
+    return ap.parse_args()
+
+
+def events_ms(fn, reps, stream):
+    import torch
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    times = []
+    for _ in range(reps):
+        start.record(stream)
+        fn()
+        end.record(stream)
+        end.synchronize()
+        times.append(start.elapsed_time(end))
+    times.sort()
+    return times[len(times) // 2], times
+
+
+def cpu_oracle_sample(Q, K, V, rows_by_head, budget_s):
+    """Time the fp64 oracle on whole query blocks of the same workload
+    (pooling + scores + top-k of the row, then attention over its support)
+    until the time budget is used; returns executed TFLOP/s and the sample."""
+    import numpy as np
+    from oracle import bsa_oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count() or 1
+    B, H, N, d = Q.shape
+    nB = O.n_blocks(N, 64)
+    k = rows_by_head["k"]
+    scale = 1.0 / math.sqrt(d)
+    rng = np.random.default_rng(0)
+    done_blocks, flops = 0, 0
+    t0 = time.perf_counter()
+    h = 0
+    while time.perf_counter() - t0 < budget_s:
+        q = Q[0, h].double().numpy()
+        kk = K[0, h].double().numpy()
+        v = V[0, h].double().numpy()
+        Qb, Kb = O.pool_means(q, 64), O.pool_means(kk, 64)
+        for i in rng.choice(nB, size=8, replace=False):
+            S_i = O.pooled_scores(Qb[i:i + 1], Kb, scale)[0]
+            sel = sorted(O.topk_set(S_i, k))
+            qi = O.block_tokens(N, 64, int(i))
+            keys = np.concatenate([O.block_tokens(N, 64, j) for j in sel])
+            O.attend(q[qi], kk[keys], v[keys], scale)
+            done_blocks += 1
+            flops += O.executed_flops(d, 64, len(sel))
+            if time.perf_counter() - t0 >= budget_s:
+                break
+        h = (h + 1) % H
+    el = time.perf_counter() - t0
+    return dict(value=flops / el / 1e12, unit="TFLOP/s", cores=int(threads), kind="oracle",
+                sample=f"{done_blocks} query blocks (pool+score+top-k+fp64 attention over "
+                       f"{k} key blocks each) of the same layer, {el:.1f} s")
+
+
+def traffic_entry(kernel_src):
+    """HBM bytes per launch of the attention kernel from the committed
+    rocprofv3 counter summary, or None when the kernel changed since."""
+    path = os.path.join(ROOT, "profiles", "attn_fwd_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    sha = hashlib.sha256(open(kernel_src, "rb").read()).hexdigest()
+    if rec.get("kernel_src_sha256") != sha:
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this benchmark measures one GPU; runs on more than one "
+                                   "GPU are not part of this build (heads shard with no "
+                                   "exchange; see the design notes)"}))
+        sys.exit(2)
+
+    import torch
+    import block_sparse_attention_pool_amd as bsa
+    from synth import CONFIGS, config_spec, gen_qkv
+
+    cfg = 1
+    c = CONFIGS[cfg]
+    spec = config_spec(cfg)
+    Qc, Kc, Vc = gen_qkv(spec)
+    dev = torch.device("cuda:0")
+    Q, K, V = (x.to(dev) for x in (Qc, Kc, Vc))
+    B, H, N, d = Q.shape
+    nB = bsa.n_blocks(N)
+    k = bsa.budget_blocks(c["density"], nB)
+    scale = 1.0 / math.sqrt(d)
+    stream = torch.cuda.current_stream(dev)
+
+    ws = bsa.attn_workspace(Q)
+    O_buf = torch.empty(Q.shape, dtype=torch.float32, device=dev)
+    L_buf = torch.empty(Q.shape[:3], dtype=torch.float32, device=dev)
+
+    def step():
+        sc = bsa.bsa_score_blocks(Q, K)
+        rp, ci, nnz = bsa.bsa_select_blocks(sc["scores"], Q, mode="topk", k=k)
+        bsa.bsa_sparse_attn_fwd(Q, K, V, rp, ci, out=O_buf, lse=L_buf, workspace=ws)
+        return rp, ci, nnz
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        rp, ci, nnz = step()
+    torch.cuda.synchronize()
+    step_s = (time.perf_counter() - t0) / args.steps
+    nnz_v = int(nnz.item())
+    exec_flops = 4 * d * 64 * 64 * nnz_v
+    dense_flops = 4 * B * H * N * N * d
+
+    # Kernel-level: the attention kernel alone (V^T already staged: V=None).
+    attn_ms, attn_all = events_ms(
+        lambda: bsa.bsa_sparse_attn_fwd(Q, K, None, rp, ci, out=O_buf, lse=L_buf, workspace=ws),
+        args.stage_reps, stream)
+    dense_ms, _ = events_ms(
+        lambda: bsa.bsa_dense_attn_fwd(Q, K, None, out=O_buf, lse=L_buf, workspace=ws),
+        max(3, args.stage_reps // 2), stream)
+    score_ms, _ = events_ms(lambda: bsa.bsa_score_blocks(Q, K), args.stage_reps, stream)
+    sc = bsa.bsa_score_blocks(Q, K)
+    select_ms, _ = events_ms(lambda: bsa.bsa_select_blocks(sc["scores"], Q, mode="topk", k=k),
+                             args.stage_reps, stream)
+    vt_ms_total, _ = events_ms(
+        lambda: bsa.bsa_sparse_attn_fwd(Q, K, V, rp, ci, out=O_buf, lse=L_buf, workspace=ws),
+        args.stage_reps, stream)
+
+    attn_tflops = exec_flops / (attn_ms * 1e-3) / 1e12
+    kernel_src = os.path.join(ROOT, "block_sparse_attention_pool_amd", "csrc", "attn.hip")
+    traffic = traffic_entry(kernel_src)
+    pool_bytes = 4 * B * H * N * d + 8 * B * H * nB * d
+    out = {
+        "metric": METRIC,
+        "value": round(exec_flops / step_s / 1e12, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(step_s * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded structured video Q/K/V)",
+        "config": {"workload": c["name"], "B": B, "H": H, "N": N, "d": d, "block": 64,
+                   "selection": f"top-k {c['density']:.0%} (k={k} of {nB})",
+                   "density": round(nnz_v / (B * H * nB * nB), 4)},
+        "attn_kernel_ms": round(attn_ms, 4),
+        "attn_kernel_tflops": round(attn_tflops, 2),
+        "pct_mfma_peak": round(100 * attn_tflops / PEAK_TFLOPS, 2),
+        "dense_equiv_tflops": round(dense_flops / (attn_ms * 1e-3) / 1e12, 2),
+        "dense_kernel_ms": round(dense_ms, 4),
+        "dense_kernel_tflops": round(dense_flops / (dense_ms * 1e-3) / 1e12, 2),
+        "speedup_vs_dense": round(dense_ms / attn_ms, 3),
+        "pipeline_speedup_vs_dense": round(dense_ms / (step_s * 1e3), 3),
+        "stages_ms": {"score_blocks": round(score_ms, 4), "select_blocks": round(select_ms, 4),
+                      "sparse_attn_fwd_with_v_staging": round(vt_ms_total, 4),
+                      "attn_kernel": round(attn_ms, 4)},
+        "score_blocks_gbs": round(pool_bytes / (score_ms * 1e-3) / 1e9, 1),
+        "roofline": {"bound": "mfma", "achieved": round(attn_tflops, 2), "peak": PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(attn_tflops / PEAK_TFLOPS, 4),
+                     "traffic": traffic},
+    }
+    if not args.no_cpu_baseline:
+        rows = {"k": k}
+        out["cpu_baseline"] = cpu_oracle_sample(Qc, Kc, Vc, rows, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

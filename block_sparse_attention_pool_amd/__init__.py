@@ -1,0 +1,347 @@
+"""Python binding of the gfx950 block-sparse attention library (libbsa.so).
+
+Argument marshalling only: every function below allocates its outputs with
+torch (device memory and streams are all torch is used for), passes raw
+pointers and sizes to the C entry point of the same name declared in
+``include/bsa.h``, and raises on a non-zero status.  All computation runs in
+the HIP kernels of the library.  The library must have been built
+(``python -m block_sparse_attention_pool_amd.build``); importing this module
+fails loudly when it is missing.
+
+Tensors Q, K, V are bf16 ``[B, H, N, d]`` on the GPU with the last dimension
+contiguous (any strides otherwise, shared by Q, K, V and the outputs).
+"""
+
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from fractions import Fraction
+
+import torch
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "_lib", "libbsa.so")
+
+BSA_OK = 0
+BSA_F32, BSA_BF16 = 0, 1
+SELECT_MODES = {"topk": 0, "topp": 1, "static": 2, "micro": 3}
+BLOCK = 64
+MICRO = 16
+
+
+class BsaError(RuntimeError):
+    pass
+
+
+class _Shape(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int32), ("H", ctypes.c_int32), ("N", ctypes.c_int32),
+                ("d", ctypes.c_int32), ("stride_b", ctypes.c_int64),
+                ("stride_h", ctypes.c_int64), ("stride_n", ctypes.c_int64)]
+
+
+class _SelectParams(ctypes.Structure):
+    _fields_ = [("mode", ctypes.c_int32), ("k", ctypes.c_int32), ("p", ctypes.c_float),
+                ("k_min", ctypes.c_int32), ("k_cap", ctypes.c_int32),
+                ("force_diag", ctypes.c_int32), ("use_static", ctypes.c_int32),
+                ("frame_tokens", ctypes.c_int32), ("window_frames", ctypes.c_int32),
+                ("n_anchors", ctypes.c_int32), ("anchor_offset", ctypes.c_int32),
+                ("micro", ctypes.c_int32), ("micro_m", ctypes.c_int32),
+                ("scale", ctypes.c_float), ("head_mask", ctypes.c_void_p),
+                ("macro_row_ptr", ctypes.c_void_p), ("macro_col_idx", ctypes.c_void_p),
+                ("qpool16", ctypes.c_void_p), ("kpool16", ctypes.c_void_p)]
+
+
+def _load():
+    if not os.path.exists(_LIB_PATH):
+        raise ImportError(
+            f"{_LIB_PATH} is missing: build it with "
+            "`python -m block_sparse_attention_pool_amd.build` (hipcc, gfx950)")
+    lib = ctypes.CDLL(_LIB_PATH)
+    P, I32, I64, F32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float
+    SP = ctypes.POINTER(_Shape)
+    PP = ctypes.POINTER(_SelectParams)
+    sig = {
+        "bsa_version": ([], ctypes.c_char_p),
+        "bsa_last_error": ([], ctypes.c_char_p),
+        "bsa_score_blocks": ([P, P, SP, I32, F32, P, P, P, I32, P, P, P], I32),
+        "bsa_select_workspace_bytes": ([SP, I32, PP], I64),
+        "bsa_select_max_nnz": ([SP, I32, PP], I64),
+        "bsa_select_blocks": ([P, SP, I32, PP, P, P, I64, P, P, I64, P], I32),
+        "bsa_attn_workspace_bytes": ([SP], I64),
+        "bsa_sparse_attn_fwd": ([P, P, P, SP, I32, F32, P, P, P, I32, P, P, I64, P], I32),
+        "bsa_dense_attn_fwd": ([P, P, P, SP, F32, P, I32, P, P, I64, P], I32),
+        "bsa_micro_residual_fwd": ([P, P, P, SP, I32, I32, F32, P, P, P, P, I32, P, P, I64, P],
+                                   I32),
+        "bsa_lse_merge": ([P, P, P, P, SP, I32, P, P, P, P], I32),
+    }
+    for name, (args, res) in sig.items():
+        fn = getattr(lib, name)
+        fn.argtypes = args
+        fn.restype = res
+    return lib
+
+
+_lib = _load()
+EXPORTED = ("bsa_version", "bsa_last_error", "bsa_score_blocks", "bsa_select_workspace_bytes",
+            "bsa_select_max_nnz", "bsa_select_blocks", "bsa_attn_workspace_bytes",
+            "bsa_sparse_attn_fwd", "bsa_dense_attn_fwd", "bsa_micro_residual_fwd",
+            "bsa_lse_merge")
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def bsa_version() -> str:
+    return _lib.bsa_version().decode()
+
+
+def bsa_last_error() -> str:
+    return _lib.bsa_last_error().decode()
+
+
+def _check(status: int, what: str):
+    if status != BSA_OK:
+        raise BsaError(f"{what} failed (status {status}): {bsa_last_error()}")
+
+
+# ----------------------------------------------------------------- marshalling
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream, device):
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def shape_of(Q: torch.Tensor) -> _Shape:
+    """bsa_shape of a [B, H, N, d] tensor (element strides, d contiguous)."""
+    if Q.dim() != 4:
+        raise ValueError("expected a [B, H, N, d] tensor")
+    B, H, N, d = Q.shape
+    if Q.stride(3) != 1:
+        raise ValueError("the last dimension must be contiguous")
+    return _Shape(B, H, N, d, Q.stride(0), Q.stride(1), Q.stride(2))
+
+
+def _same_layout(*ts):
+    ts = [t for t in ts if t is not None]
+    ref = ts[0]
+    for t in ts[1:]:
+        if t.shape != ref.shape or t.stride() != ref.stride():
+            raise ValueError("Q, K, V (and outputs) must share shape and strides")
+        if t.dtype != torch.bfloat16 or ref.dtype != torch.bfloat16:
+            raise ValueError("Q, K, V must be bfloat16")
+
+
+def _out_like(Q, dtype):
+    return torch.empty_strided(Q.shape, Q.stride(), dtype=dtype, device=Q.device)
+
+
+def _odt(dtype):
+    if dtype == torch.float32:
+        return BSA_F32
+    if dtype == torch.bfloat16:
+        return BSA_BF16
+    raise ValueError("output dtype must be float32 or bfloat16")
+
+
+def n_blocks(N: int, b: int = BLOCK) -> int:
+    return -(-N // b)
+
+
+def budget_blocks(density: float, nB: int) -> int:
+    """Blocks kept for a density budget: ceil(density * nB), exact in
+    decimal so that 0.25 * 512 is 128 and not 128.00000000000003."""
+    return math.ceil(Fraction(str(density)) * nB)
+
+
+def cap_blocks(density: float, nB: int) -> int:
+    """Largest row length under a density cap: floor(density * nB)."""
+    return math.floor(Fraction(str(density)) * nB)
+
+
+def _head_mask(head_mask, H):
+    if head_mask is None:
+        return None, None
+    arr = (ctypes.c_uint8 * H)(*[1 if h else 0 for h in head_mask])
+    return arr, ctypes.cast(arr, ctypes.c_void_p)
+
+
+# ---------------------------------------------------------------- entry points
+
+def bsa_score_blocks(Q, K, *, block: int = BLOCK, scale: float | None = None,
+                     scores: bool = True, micro: int = 0, stream=None):
+    """Pooled means and pooled block scores.  Returns a dict with qpool,
+    kpool [B,H,nB,d], scores [B,H,nB,nB] (or None) and, when micro=16,
+    qpool16, kpool16 [B,H,nT,d]; all float32."""
+    _same_layout(Q, K)
+    shp = shape_of(Q)
+    B, H, N, d = Q.shape
+    scale = 1.0 / math.sqrt(d) if scale is None else scale
+    nB, nT = n_blocks(N, block), n_blocks(N, MICRO)
+    f32 = dict(dtype=torch.float32, device=Q.device)
+    out = dict(qpool=torch.empty((B, H, nB, d), **f32), kpool=torch.empty((B, H, nB, d), **f32),
+               scores=torch.empty((B, H, nB, nB), **f32) if scores else None,
+               qpool16=torch.empty((B, H, nT, d), **f32) if micro else None,
+               kpool16=torch.empty((B, H, nT, d), **f32) if micro else None)
+    st = _lib.bsa_score_blocks(_ptr(Q), _ptr(K), ctypes.byref(shp), block, scale,
+                               _ptr(out["qpool"]), _ptr(out["kpool"]), _ptr(out["scores"]),
+                               micro, _ptr(out["qpool16"]), _ptr(out["kpool16"]),
+                               _stream(stream, Q.device))
+    _check(st, "bsa_score_blocks")
+    return out
+
+
+def make_select_params(mode: str = "topk", *, k: int = 0, p: float = 0.9, k_min: int = 1,
+                       k_cap: int | None = None, force_diag: bool = False,
+                       static: dict | None = None, micro: dict | None = None,
+                       nB: int | None = None):
+    sp = _SelectParams()
+    sp.mode = SELECT_MODES[mode]
+    sp.k = k
+    sp.p = p
+    sp.k_min = k_min
+    sp.k_cap = (nB if nB is not None else 1 << 30) if k_cap is None else k_cap
+    sp.force_diag = 1 if force_diag else 0
+    if static is not None:
+        sp.use_static = 1
+        sp.frame_tokens = static["frame_tokens"]
+        sp.window_frames = static["window_frames"]
+        sp.n_anchors = static.get("n_anchors", 0)
+        sp.anchor_offset = static.get("anchor_offset", 0)
+    keep = []
+    if micro is not None:
+        sp.micro = micro.get("micro", MICRO)
+        sp.micro_m = micro["m"]
+        sp.scale = micro["scale"]
+        row_ptr, col_idx = micro["macro"]
+        sp.macro_row_ptr = row_ptr.data_ptr()
+        sp.macro_col_idx = col_idx.data_ptr()
+        sp.qpool16 = micro["qpool16"].data_ptr()
+        sp.kpool16 = micro["kpool16"].data_ptr()
+        if micro.get("head_mask") is not None:
+            H = micro["qpool16"].shape[1]
+            arr, ptr = _head_mask(micro["head_mask"], H)
+            keep.append(arr)
+            sp.head_mask = ptr.value
+    return sp, keep
+
+
+def bsa_select_blocks(scores, Q_like, *, block: int = BLOCK, mode: str = "topk", k: int = 0,
+                      p: float = 0.9, k_min: int = 1, k_cap: int | None = None,
+                      force_diag: bool = False, static: dict | None = None,
+                      micro: dict | None = None, stream=None):
+    """CSR block lists.  ``Q_like`` supplies the shape ([B,H,N,d] tensor).
+    Returns (row_ptr int32 [B*H*nB+1], col_idx int32 [capacity], nnz int64
+    device scalar); the first nnz entries of col_idx are valid."""
+    shp = shape_of(Q_like)
+    nB = n_blocks(shp.N, block)
+    sp, keep = make_select_params(mode, k=k, p=p, k_min=k_min, k_cap=k_cap,
+                                  force_diag=force_diag, static=static, micro=micro, nB=nB)
+    ws_bytes = _lib.bsa_select_workspace_bytes(ctypes.byref(shp), block, ctypes.byref(sp))
+    if ws_bytes < 0:
+        raise BsaError(f"bsa_select_workspace_bytes: {bsa_last_error()}")
+    cap = _lib.bsa_select_max_nnz(ctypes.byref(shp), block, ctypes.byref(sp))
+    dev = Q_like.device
+    rows = shp.B * shp.H * nB
+    row_ptr = torch.empty(rows + 1, dtype=torch.int32, device=dev)
+    col_idx = torch.empty(max(cap, 1), dtype=torch.int32, device=dev)
+    nnz = torch.empty(1, dtype=torch.int64, device=dev)
+    ws = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
+    st = _lib.bsa_select_blocks(_ptr(scores), ctypes.byref(shp), block, ctypes.byref(sp),
+                                _ptr(row_ptr), _ptr(col_idx), cap, _ptr(nnz), _ptr(ws),
+                                ws.numel(), _stream(stream, dev))
+    _check(st, "bsa_select_blocks")
+    del keep
+    return row_ptr, col_idx, nnz
+
+
+def attn_workspace(Q) -> torch.Tensor:
+    shp = shape_of(Q)
+    n = _lib.bsa_attn_workspace_bytes(ctypes.byref(shp))
+    if n < 0:
+        raise BsaError(f"bsa_attn_workspace_bytes: {bsa_last_error()}")
+    return torch.empty(max(n, 256), dtype=torch.uint8, device=Q.device)
+
+
+def bsa_sparse_attn_fwd(Q, K, V, row_ptr, col_idx, *, block: int = BLOCK,
+                        scale: float | None = None, out_dtype=torch.float32, out=None,
+                        lse=None, workspace=None, stream=None):
+    """Block-sparse attention forward.  Returns (O [B,H,N,d] out_dtype,
+    LSE float32 [B,H,N]).  V=None reuses the fp16 V^T already in
+    ``workspace`` from an earlier call on the same V."""
+    _same_layout(Q, K, V)
+    shp = shape_of(Q)
+    scale = 1.0 / math.sqrt(shp.d) if scale is None else scale
+    O = _out_like(Q, out_dtype) if out is None else out
+    L = torch.empty(Q.shape[:3], dtype=torch.float32, device=Q.device) if lse is None else lse
+    ws = attn_workspace(Q) if workspace is None else workspace
+    st = _lib.bsa_sparse_attn_fwd(_ptr(Q), _ptr(K), _ptr(V), ctypes.byref(shp), block, scale,
+                                  _ptr(row_ptr), _ptr(col_idx), _ptr(O), _odt(O.dtype), _ptr(L),
+                                  _ptr(ws), ws.numel(), _stream(stream, Q.device))
+    _check(st, "bsa_sparse_attn_fwd")
+    return O, L
+
+
+def bsa_dense_attn_fwd(Q, K, V, *, scale: float | None = None, out_dtype=torch.float32,
+                       out=None, lse=None, workspace=None, stream=None):
+    """Full attention with the same engine.  Returns (O, LSE)."""
+    _same_layout(Q, K, V)
+    shp = shape_of(Q)
+    scale = 1.0 / math.sqrt(shp.d) if scale is None else scale
+    O = _out_like(Q, out_dtype) if out is None else out
+    L = torch.empty(Q.shape[:3], dtype=torch.float32, device=Q.device) if lse is None else lse
+    ws = attn_workspace(Q) if workspace is None else workspace
+    st = _lib.bsa_dense_attn_fwd(_ptr(Q), _ptr(K), _ptr(V), ctypes.byref(shp), scale, _ptr(O),
+                                 _odt(O.dtype), _ptr(L), _ptr(ws), ws.numel(),
+                                 _stream(stream, Q.device))
+    _check(st, "bsa_dense_attn_fwd")
+    return O, L
+
+
+def bsa_micro_residual_fwd(Q, K, V, mrow_ptr, midx, *, head_mask=None, block: int = BLOCK,
+                           micro: int = MICRO, scale: float | None = None,
+                           out_dtype=torch.float32, out=None, lse=None, workspace=None,
+                           stream=None):
+    """Micro-tile residual attention.  Heads outside ``head_mask`` are left
+    untouched in ``out``/``lse`` (fresh outputs hold garbage there)."""
+    _same_layout(Q, K, V)
+    shp = shape_of(Q)
+    scale = 1.0 / math.sqrt(shp.d) if scale is None else scale
+    O = _out_like(Q, out_dtype) if out is None else out
+    L = torch.empty(Q.shape[:3], dtype=torch.float32, device=Q.device) if lse is None else lse
+    ws = attn_workspace(Q) if workspace is None else workspace
+    arr, hm = _head_mask(head_mask, shp.H)
+    st = _lib.bsa_micro_residual_fwd(_ptr(Q), _ptr(K), _ptr(V), ctypes.byref(shp), block, micro,
+                                     scale, _ptr(mrow_ptr), _ptr(midx), hm, _ptr(O),
+                                     _odt(O.dtype), _ptr(L), _ptr(ws), ws.numel(),
+                                     _stream(stream, Q.device))
+    _check(st, "bsa_micro_residual_fwd")
+    return O, L
+
+
+def bsa_lse_merge(O1, L1, O2, L2, *, head_mask=None, out=None, lse_out=None, stream=None):
+    """Exact LSE merge of two partial results.  out/lse_out may be O1/L1."""
+    if O1.dtype != O2.dtype or O1.shape != O2.shape or O1.stride() != O2.stride():
+        raise ValueError("O1 and O2 must share dtype, shape and strides")
+    shp = shape_of(O1)
+    O = _out_like(O1, O1.dtype) if out is None else out
+    L = torch.empty_like(L1) if lse_out is None else lse_out
+    arr, hm = _head_mask(head_mask, shp.H)
+    st = _lib.bsa_lse_merge(_ptr(O1), _ptr(L1), _ptr(O2), _ptr(L2), ctypes.byref(shp),
+                            _odt(O1.dtype), hm, _ptr(O), _ptr(L), _stream(stream, O1.device))
+    _check(st, "bsa_lse_merge")
+    return O, L
+
+
+def csr_rows(row_ptr: torch.Tensor, col_idx: torch.Tensor, nnz: torch.Tensor):
+    """Host copy of a CSR as a list of lists (for inspection and tests)."""
+    rp = row_ptr.cpu().tolist()
+    n = int(nnz.item())
+    ci = col_idx[:n].cpu().tolist()
+    return [ci[rp[r]:rp[r + 1]] for r in range(len(rp) - 1)]

@@ -1,0 +1,499 @@
+// C-ABI entry points declared in include/bsa.h: argument validation (before
+// any HIP call), workspace carving and kernel launches on the caller's
+// stream.  No state is kept between calls and nothing is allocated.
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "bsa.h"
+#include "bsa_internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+bsa_status fail(bsa_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+bsa_status hip_status(hipError_t e, const char* where) {
+  if (e == hipSuccess) return BSA_OK;
+  return fail(BSA_ERR_HIP, "%s: %s", where, hipGetErrorString(e));
+}
+
+bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p % a) == 0; }
+
+int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+int64_t align256(int64_t x) { return (x + 255) & ~int64_t(255); }
+
+bsa_status check_shape(const bsa_shape* s) {
+  if (s == nullptr) return fail(BSA_ERR_INVALID_ARG, "shape is NULL");
+  if (s->B < 1 || s->H < 1 || s->N < 1)
+    return fail(BSA_ERR_INVALID_ARG, "shape B=%d H=%d N=%d must all be >= 1", s->B, s->H, s->N);
+  if (s->d != 64 && s->d != 128)
+    return fail(BSA_ERR_UNSUPPORTED, "head dim d=%d unsupported (64 or 128)", s->d);
+  if (s->H > bsa::kMaxHeads)
+    return fail(BSA_ERR_UNSUPPORTED, "H=%d exceeds %d heads", s->H, bsa::kMaxHeads);
+  if (s->B > 32767) return fail(BSA_ERR_UNSUPPORTED, "B=%d exceeds 32767", s->B);
+  if (s->stride_n < s->d || s->stride_h < 0 || s->stride_b < 0)
+    return fail(BSA_ERR_INVALID_ARG, "strides (b=%lld h=%lld n=%lld) inconsistent with d=%d",
+                (long long)s->stride_b, (long long)s->stride_h, (long long)s->stride_n, s->d);
+  if (s->stride_n % 8 || s->stride_h % 8 || s->stride_b % 8)
+    return fail(BSA_ERR_INVALID_ARG, "strides must be multiples of 8 elements");
+  const int64_t nB = cdiv(s->N, 64);
+  if ((int64_t)s->B * s->H * nB >= INT32_MAX / 2)
+    return fail(BSA_ERR_UNSUPPORTED, "too many query blocks");
+  return BSA_OK;
+}
+
+bsa_status check_ptr(const void* p, const char* name, uintptr_t align = 16) {
+  if (p == nullptr) return fail(BSA_ERR_INVALID_ARG, "%s is NULL", name);
+  if (!aligned(p, align))
+    return fail(BSA_ERR_INVALID_ARG, "%s is not %u-byte aligned", name, (unsigned)align);
+  return BSA_OK;
+}
+
+#define BSA_TRY(expr)                   \
+  do {                                  \
+    const bsa_status _st = (expr);      \
+    if (_st != BSA_OK) return _st;      \
+  } while (0)
+
+bsa::HeadList all_heads(int H) {
+  bsa::HeadList l;
+  l.n = H;
+  for (int h = 0; h < H; ++h) l.h[h] = h;
+  return l;
+}
+
+bsa::HeadList heads_from_mask(const uint8_t* mask, int H) {
+  bsa::HeadList l;
+  l.n = 0;
+  for (int h = 0; h < H; ++h)
+    if (mask == nullptr || mask[h]) l.h[l.n++] = h;
+  return l;
+}
+
+int next_pow2(int x) {
+  int p = 2;
+  while (p < x) p <<= 1;
+  return p;
+}
+
+struct SelectPlan {
+  int64_t rows, nB, W, nT;
+  int64_t bytes_a, bytes_b, bytes_c, total;
+  bsa::HeadList heads;
+};
+
+bsa_status plan_select(const bsa_shape* s, int32_t block, const bsa_select_params* p,
+                       SelectPlan* out) {
+  BSA_TRY(check_shape(s));
+  if (block != 64) return fail(BSA_ERR_UNSUPPORTED, "block=%d unsupported (64)", block);
+  if (p == nullptr) return fail(BSA_ERR_INVALID_ARG, "params is NULL");
+  SelectPlan pl{};
+  pl.nB = cdiv(s->N, 64);
+  pl.rows = (int64_t)s->B * s->H * pl.nB;
+  pl.W = cdiv(pl.nB, 32);
+  pl.nT = cdiv(s->N, 16);
+  switch (p->mode) {
+    case BSA_SELECT_TOPK:
+    case BSA_SELECT_TOPP:
+    case BSA_SELECT_STATIC:
+      if (p->mode != BSA_SELECT_STATIC && pl.nB > 4096)
+        return fail(BSA_ERR_UNSUPPORTED, "scored selection needs nB <= 4096 (nB=%lld)",
+                    (long long)pl.nB);
+      if (pl.W > 128) return fail(BSA_ERR_UNSUPPORTED, "nB=%lld exceeds 4096", (long long)pl.nB);
+      pl.bytes_a = align256(pl.rows * pl.W * 4);  // row bitmasks
+      pl.bytes_b = align256(pl.rows * 4);         // row counts
+      pl.bytes_c = 0;
+      break;
+    case BSA_SELECT_MICRO: {
+      if (p->micro != 16) return fail(BSA_ERR_UNSUPPORTED, "micro=%d unsupported (16)", p->micro);
+      if (p->micro_m < 0) return fail(BSA_ERR_INVALID_ARG, "micro_m=%d < 0", p->micro_m);
+      if (pl.W > 128) return fail(BSA_ERR_UNSUPPORTED, "nB=%lld exceeds 4096", (long long)pl.nB);
+      pl.heads = heads_from_mask(p->head_mask, s->H);
+      const int64_t nbatch = (int64_t)s->B * pl.heads.n;
+      if (nbatch > 65535) return fail(BSA_ERR_UNSUPPORTED, "too many micro heads");
+      pl.bytes_a = align256(nbatch * pl.nT * pl.nT * 4);        // tile scores
+      pl.bytes_b = align256(pl.rows * (int64_t)p->micro_m * 4);  // per-row slots
+      pl.bytes_c = align256(pl.rows * 4);                        // row counts
+      break;
+    }
+    default:
+      return fail(BSA_ERR_INVALID_ARG, "unknown selection mode %d", p->mode);
+  }
+  pl.total = pl.bytes_a + pl.bytes_b + pl.bytes_c;
+  *out = pl;
+  return BSA_OK;
+}
+
+int64_t max_nnz(const bsa_shape* s, const bsa_select_params* p, const SelectPlan& pl) {
+  if (p->mode == BSA_SELECT_MICRO) {
+    const int64_t per = std::min<int64_t>(p->micro_m, 4 * pl.nT);
+    return (int64_t)s->B * pl.heads.n * pl.nB * per;
+  }
+  int64_t per = pl.nB;
+  if (!p->use_static) {
+    int64_t base = 0;
+    if (p->mode == BSA_SELECT_TOPK) base = p->k;
+    else if (p->mode == BSA_SELECT_TOPP) base = std::max(p->k_cap, 1);
+    per = std::min<int64_t>(pl.nB, base + (p->force_diag ? 1 : 0));
+  }
+  return pl.rows * per;
+}
+
+bsa_status check_attn_common(const uint16_t* Q, const uint16_t* K, const uint16_t* V,
+                             const bsa_shape* s, const void* O, int32_t o_dtype,
+                             const float* LSE, const void* ws, int64_t ws_bytes) {
+  BSA_TRY(check_shape(s));
+  BSA_TRY(check_ptr(Q, "Q"));
+  BSA_TRY(check_ptr(K, "K"));
+  if (V != nullptr) BSA_TRY(check_ptr(V, "V"));
+  BSA_TRY(check_ptr(O, "O"));
+  BSA_TRY(check_ptr(LSE, "LSE", 4));
+  BSA_TRY(check_ptr(ws, "workspace", 256));
+  if (o_dtype != BSA_F32 && o_dtype != BSA_BF16)
+    return fail(BSA_ERR_INVALID_ARG, "o_dtype=%d (BSA_F32 or BSA_BF16)", o_dtype);
+  const int64_t need = bsa_attn_workspace_bytes(s);
+  if (ws_bytes < need)
+    return fail(BSA_ERR_CAPACITY, "workspace %lld bytes < required %lld", (long long)ws_bytes,
+                (long long)need);
+  return BSA_OK;
+}
+
+bsa_status run_attn(const uint16_t* Q, const uint16_t* K, const uint16_t* V, const bsa_shape* s,
+                    float scale, const int32_t* row_ptr, const int32_t* col_idx, void* O,
+                    int32_t o_dtype, float* LSE, void* ws, bool dense, hipStream_t st) {
+  const int nB = (int)cdiv(s->N, 64);
+  bsa::TransposeArgs t{};
+  t.V = V;
+  t.Vt = (uint16_t*)ws;
+  t.sb = s->stride_b;
+  t.sh = s->stride_h;
+  t.sn = s->stride_n;
+  t.H = s->H;
+  t.N = s->N;
+  t.nB = nB;
+  t.Npad = nB * 64;
+  t.heads = all_heads(s->H);
+  if (V != nullptr)
+    BSA_TRY(hip_status(bsa::launch_transpose_v(t, s->B, s->d, st), "transpose_v launch"));
+  bsa::AttnArgs a{};
+  a.Q = Q;
+  a.K = K;
+  a.Vt = (const uint16_t*)ws;
+  a.O = O;
+  a.LSE = LSE;
+  a.row_ptr = row_ptr;
+  a.col_idx = col_idx;
+  a.sb = s->stride_b;
+  a.sh = s->stride_h;
+  a.sn = s->stride_n;
+  a.B = s->B;
+  a.H = s->H;
+  a.N = s->N;
+  a.nB = nB;
+  a.Npad = nB * 64;
+  a.scale_log2 = scale * 1.4426950408889634f;
+  a.rows = s->B * s->H * nB;
+  a.per_xcd = (int)cdiv(a.rows, 8);
+  return hip_status(bsa::launch_attn(a, s->d, dense, o_dtype == BSA_BF16, st), "attn launch");
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* bsa_version(void) { return "bsa 0.1.0 gfx950"; }
+
+const char* bsa_last_error(void) { return g_last_error.c_str(); }
+
+bsa_status bsa_score_blocks(const uint16_t* Q, const uint16_t* K, const bsa_shape* shape,
+                            int32_t block, float scale, float* qpool, float* kpool,
+                            float* scores, int32_t micro, float* qpool16, float* kpool16,
+                            void* stream) {
+  BSA_TRY(check_shape(shape));
+  if (block != 64) return fail(BSA_ERR_UNSUPPORTED, "block=%d unsupported (64)", block);
+  BSA_TRY(check_ptr(Q, "Q"));
+  BSA_TRY(check_ptr(K, "K"));
+  BSA_TRY(check_ptr(qpool, "qpool"));
+  BSA_TRY(check_ptr(kpool, "kpool"));
+  if (scores != nullptr) BSA_TRY(check_ptr(scores, "scores", 4));
+  if (micro != 0 && micro != 16) return fail(BSA_ERR_UNSUPPORTED, "micro=%d (0 or 16)", micro);
+  if (micro == 16) {
+    BSA_TRY(check_ptr(qpool16, "qpool16"));
+    BSA_TRY(check_ptr(kpool16, "kpool16"));
+  }
+  const int nB = (int)cdiv(shape->N, 64);
+  if ((int64_t)shape->B * shape->H > 65535)
+    return fail(BSA_ERR_UNSUPPORTED, "B*H exceeds 65535");
+  hipStream_t st = (hipStream_t)stream;
+  bsa::PoolArgs p{};
+  p.Q = Q;
+  p.K = K;
+  p.sb = shape->stride_b;
+  p.sh = shape->stride_h;
+  p.sn = shape->stride_n;
+  p.H = shape->H;
+  p.N = shape->N;
+  p.D = shape->d;
+  p.nB = nB;
+  p.nT = (int)cdiv(shape->N, 16);
+  p.qpool = qpool;
+  p.kpool = kpool;
+  p.qpool16 = micro ? qpool16 : nullptr;
+  p.kpool16 = micro ? kpool16 : nullptr;
+  BSA_TRY(hip_status(bsa::launch_pool(p, shape->B, st), "pool launch"));
+  if (scores != nullptr) {
+    bsa::GemmArgs g{};
+    g.A = qpool;
+    g.Bm = kpool;
+    g.C = scores;
+    g.H = shape->H;
+    g.M = nB;
+    g.Nc = nB;
+    g.D = shape->d;
+    g.scale = scale;
+    g.heads = all_heads(shape->H);
+    BSA_TRY(hip_status(bsa::launch_score_gemm(g, shape->B * shape->H, st), "score launch"));
+  }
+  return BSA_OK;
+}
+
+int64_t bsa_select_workspace_bytes(const bsa_shape* shape, int32_t block,
+                                   const bsa_select_params* params) {
+  SelectPlan pl;
+  if (plan_select(shape, block, params, &pl) != BSA_OK) return -1;
+  return pl.total;
+}
+
+int64_t bsa_select_max_nnz(const bsa_shape* shape, int32_t block,
+                           const bsa_select_params* params) {
+  SelectPlan pl;
+  if (plan_select(shape, block, params, &pl) != BSA_OK) return -1;
+  return max_nnz(shape, params, pl);
+}
+
+bsa_status bsa_select_blocks(const float* scores, const bsa_shape* shape, int32_t block,
+                             const bsa_select_params* p, int32_t* row_ptr, int32_t* col_idx,
+                             int64_t col_cap, int64_t* out_nnz, void* workspace,
+                             int64_t workspace_bytes, void* stream) {
+  SelectPlan pl;
+  BSA_TRY(plan_select(shape, block, p, &pl));
+  BSA_TRY(check_ptr(row_ptr, "row_ptr", 4));
+  BSA_TRY(check_ptr(out_nnz, "out_nnz", 8));
+  if (col_cap < 0) return fail(BSA_ERR_INVALID_ARG, "col_cap < 0");
+  if (col_cap > 0) BSA_TRY(check_ptr(col_idx, "col_idx", 4));
+  if (pl.total > 0) BSA_TRY(check_ptr(workspace, "workspace", 256));
+  if (workspace_bytes < pl.total)
+    return fail(BSA_ERR_CAPACITY, "workspace %lld bytes < required %lld",
+                (long long)workspace_bytes, (long long)pl.total);
+  const int64_t bound = max_nnz(shape, p, pl);
+  if (bound > INT32_MAX)
+    return fail(BSA_ERR_UNSUPPORTED, "up to %lld entries exceed int32 row pointers",
+                (long long)bound);
+  hipStream_t st = (hipStream_t)stream;
+  char* ws = (char*)workspace;
+  const int rows = (int)pl.rows;
+
+  if (p->mode == BSA_SELECT_MICRO) {
+    if (p->macro_row_ptr == nullptr || p->macro_col_idx == nullptr)
+      return fail(BSA_ERR_INVALID_ARG, "MICRO mode needs the macro CSR");
+    BSA_TRY(check_ptr(p->qpool16, "qpool16"));
+    BSA_TRY(check_ptr(p->kpool16, "kpool16"));
+    float* sigma = (float*)ws;
+    int32_t* slots = (int32_t*)(ws + pl.bytes_a);
+    int32_t* counts = (int32_t*)(ws + pl.bytes_a + pl.bytes_b);
+    BSA_TRY(hip_status(bsa::launch_fill_i32(counts, rows, 0, st), "fill launch"));
+    if (pl.heads.n > 0 && p->micro_m > 0) {
+      bsa::GemmArgs g{};
+      g.A = p->qpool16;
+      g.Bm = p->kpool16;
+      g.C = sigma;
+      g.H = shape->H;
+      g.M = (int)pl.nT;
+      g.Nc = (int)pl.nT;
+      g.D = shape->d;
+      g.scale = p->scale;
+      g.heads = pl.heads;
+      BSA_TRY(hip_status(bsa::launch_score_gemm(g, shape->B * pl.heads.n, st), "micro score"));
+      bsa::MicroSelectArgs m{};
+      m.sigma = sigma;
+      m.macro_row_ptr = p->macro_row_ptr;
+      m.macro_col_idx = p->macro_col_idx;
+      m.slots = slots;
+      m.counts = counts;
+      m.H = shape->H;
+      m.nB = (int)pl.nB;
+      m.nT = (int)pl.nT;
+      m.W = (int)pl.W;
+      m.m = p->micro_m;
+      m.heads = pl.heads;
+      BSA_TRY(hip_status(bsa::launch_micro_select(m, shape->B, st), "micro select"));
+    }
+    BSA_TRY(hip_status(bsa::launch_scan(counts, rows, row_ptr, out_nnz, st), "scan launch"));
+    BSA_TRY(hip_status(
+        bsa::launch_emit_slots(slots, std::max(p->micro_m, 1), rows, row_ptr, col_idx, col_cap, st),
+        "emit launch"));
+    return BSA_OK;
+  }
+
+  const bool scored = p->mode == BSA_SELECT_TOPK || p->mode == BSA_SELECT_TOPP;
+  if (scored) BSA_TRY(check_ptr(scores, "scores", 4));
+  if (p->mode == BSA_SELECT_TOPK && p->k < 0) return fail(BSA_ERR_INVALID_ARG, "k=%d < 0", p->k);
+  if (p->mode == BSA_SELECT_TOPP) {
+    if (!(p->p > 0.f && p->p <= 1.f)) return fail(BSA_ERR_INVALID_ARG, "p=%g not in (0,1]", p->p);
+    if (p->k_min < 0 || p->k_cap < p->k_min)
+      return fail(BSA_ERR_INVALID_ARG, "need 0 <= k_min <= k_cap (k_min=%d k_cap=%d)", p->k_min,
+                  p->k_cap);
+  }
+  if (p->use_static) {
+    if (p->frame_tokens <= 0) return fail(BSA_ERR_INVALID_ARG, "frame_tokens must be > 0");
+    if (p->window_frames < 0) return fail(BSA_ERR_INVALID_ARG, "window_frames must be >= 0");
+    if (p->n_anchors < 0) return fail(BSA_ERR_INVALID_ARG, "n_anchors must be >= 0");
+  }
+  bsa::SelectArgs a{};
+  a.scores = scores;
+  a.bits = (uint32_t*)ws;
+  a.counts = (int32_t*)(ws + pl.bytes_a);
+  a.N = shape->N;
+  a.nB = (int)pl.nB;
+  a.W = (int)pl.W;
+  a.P2 = next_pow2((int)pl.nB);
+  a.mode = p->mode;
+  a.k = p->k;
+  a.k_min = p->k_min;
+  a.k_cap = p->k_cap;
+  a.p = p->p;
+  a.force_diag = p->force_diag ? 1 : 0;
+  a.use_static = p->use_static ? 1 : 0;
+  a.frame_tokens = p->frame_tokens;
+  a.window_frames = p->window_frames;
+  a.n_anchors = p->n_anchors;
+  a.anchor_offset = p->anchor_offset;
+  BSA_TRY(hip_status(bsa::launch_select(a, rows, st), "select launch"));
+  BSA_TRY(hip_status(bsa::launch_scan(a.counts, rows, row_ptr, out_nnz, st), "scan launch"));
+  BSA_TRY(hip_status(bsa::launch_emit_bits(a.bits, a.W, rows, row_ptr, col_idx, col_cap, st),
+                     "emit launch"));
+  return BSA_OK;
+}
+
+int64_t bsa_attn_workspace_bytes(const bsa_shape* shape) {
+  if (check_shape(shape) != BSA_OK) return -1;
+  const int64_t npad = cdiv(shape->N, 64) * 64;
+  return align256((int64_t)shape->B * shape->H * shape->d * npad * 2);
+}
+
+bsa_status bsa_sparse_attn_fwd(const uint16_t* Q, const uint16_t* K, const uint16_t* V,
+                               const bsa_shape* shape, int32_t block, float scale,
+                               const int32_t* row_ptr, const int32_t* col_idx, void* O,
+                               int32_t o_dtype, float* LSE, void* workspace,
+                               int64_t workspace_bytes, void* stream) {
+  BSA_TRY(check_attn_common(Q, K, V, shape, O, o_dtype, LSE, workspace, workspace_bytes));
+  if (block != 64) return fail(BSA_ERR_UNSUPPORTED, "block=%d unsupported (64)", block);
+  BSA_TRY(check_ptr(row_ptr, "row_ptr", 4));
+  if (col_idx == nullptr) return fail(BSA_ERR_INVALID_ARG, "col_idx is NULL");
+  return run_attn(Q, K, V, shape, scale, row_ptr, col_idx, O, o_dtype, LSE, workspace, false,
+                  (hipStream_t)stream);
+}
+
+bsa_status bsa_dense_attn_fwd(const uint16_t* Q, const uint16_t* K, const uint16_t* V,
+                              const bsa_shape* shape, float scale, void* O, int32_t o_dtype,
+                              float* LSE, void* workspace, int64_t workspace_bytes,
+                              void* stream) {
+  BSA_TRY(check_attn_common(Q, K, V, shape, O, o_dtype, LSE, workspace, workspace_bytes));
+  return run_attn(Q, K, V, shape, scale, nullptr, nullptr, O, o_dtype, LSE, workspace, true,
+                  (hipStream_t)stream);
+}
+
+bsa_status bsa_micro_residual_fwd(const uint16_t* Q, const uint16_t* K, const uint16_t* V,
+                                  const bsa_shape* shape, int32_t block, int32_t micro,
+                                  float scale, const int32_t* mrow_ptr, const int32_t* midx,
+                                  const uint8_t* head_mask, void* O_mu, int32_t o_dtype,
+                                  float* LSE_mu, void* workspace, int64_t workspace_bytes,
+                                  void* stream) {
+  BSA_TRY(check_attn_common(Q, K, V, shape, O_mu, o_dtype, LSE_mu, workspace, workspace_bytes));
+  if (block != 64) return fail(BSA_ERR_UNSUPPORTED, "block=%d unsupported (64)", block);
+  if (micro != 16) return fail(BSA_ERR_UNSUPPORTED, "micro=%d unsupported (16)", micro);
+  BSA_TRY(check_ptr(mrow_ptr, "mrow_ptr", 4));
+  const bsa::HeadList heads = heads_from_mask(head_mask, shape->H);
+  if (heads.n == 0) return BSA_OK;
+  if ((int64_t)shape->B * heads.n > 65535)
+    return fail(BSA_ERR_UNSUPPORTED, "B * micro heads exceeds 65535");
+  if (midx == nullptr) return fail(BSA_ERR_INVALID_ARG, "midx is NULL");
+  hipStream_t st = (hipStream_t)stream;
+  const int nB = (int)cdiv(shape->N, 64);
+  bsa::TransposeArgs t{};
+  t.V = V;
+  t.Vt = (uint16_t*)workspace;
+  t.sb = shape->stride_b;
+  t.sh = shape->stride_h;
+  t.sn = shape->stride_n;
+  t.H = shape->H;
+  t.N = shape->N;
+  t.nB = nB;
+  t.Npad = nB * 64;
+  t.heads = heads;
+  if (V != nullptr)
+    BSA_TRY(hip_status(bsa::launch_transpose_v(t, shape->B, shape->d, st), "transpose_v launch"));
+  bsa::MicroAttnArgs a{};
+  a.Q = Q;
+  a.K = K;
+  a.Vt = (const uint16_t*)workspace;
+  a.O = O_mu;
+  a.LSE = LSE_mu;
+  a.row_ptr = mrow_ptr;
+  a.idx = midx;
+  a.sb = shape->stride_b;
+  a.sh = shape->stride_h;
+  a.sn = shape->stride_n;
+  a.H = shape->H;
+  a.N = shape->N;
+  a.nB = nB;
+  a.Npad = nB * 64;
+  a.scale_log2 = scale * 1.4426950408889634f;
+  a.heads = heads;
+  return hip_status(bsa::launch_micro_attn(a, shape->B, shape->d, o_dtype == BSA_BF16, st),
+                    "micro attn launch");
+}
+
+bsa_status bsa_lse_merge(const void* O1, const float* L1, const void* O2, const float* L2,
+                         const bsa_shape* shape, int32_t o_dtype, const uint8_t* head_mask,
+                         void* O, float* L, void* stream) {
+  BSA_TRY(check_shape(shape));
+  BSA_TRY(check_ptr(O1, "O1"));
+  BSA_TRY(check_ptr(O2, "O2"));
+  BSA_TRY(check_ptr(O, "O"));
+  BSA_TRY(check_ptr(L1, "L1", 4));
+  BSA_TRY(check_ptr(L2, "L2", 4));
+  BSA_TRY(check_ptr(L, "L", 4));
+  if (o_dtype != BSA_F32 && o_dtype != BSA_BF16)
+    return fail(BSA_ERR_INVALID_ARG, "o_dtype=%d (BSA_F32 or BSA_BF16)", o_dtype);
+  const bsa::HeadList heads = heads_from_mask(head_mask, shape->H);
+  if (heads.n == 0) return BSA_OK;
+  bsa::MergeArgs a{};
+  a.O1 = O1;
+  a.L1 = L1;
+  a.O2 = O2;
+  a.L2 = L2;
+  a.O = O;
+  a.L = L;
+  a.sb = shape->stride_b;
+  a.sh = shape->stride_h;
+  a.sn = shape->stride_n;
+  a.H = shape->H;
+  a.N = shape->N;
+  a.D = shape->d;
+  a.heads = heads;
+  return hip_status(bsa::launch_merge(a, shape->B, o_dtype == BSA_BF16, (hipStream_t)stream),
+                    "merge launch");
+}
+
+}  // extern "C"

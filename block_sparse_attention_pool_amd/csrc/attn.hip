@@ -1,0 +1,463 @@
+// Attention kernels for gfx950.
+//
+//  * transpose_v: V [N, d] bf16 -> key-major V^T [d, Npad] fp16 per head,
+//    zero padded, with the 16 keys of every chunk stored in the order the
+//    matrix-core operand layout consumes them, so every PV operand is one
+//    contiguous load.  The PV product runs on fp16 operands: bf16 V converts
+//    to fp16 exactly (within fp16 range) and P, bounded by 2^8 through the
+//    lazy rescale, keeps 3 more mantissa bits than bf16 would give it.
+//  * attn_fwd: block-sparse (CSR rows) or dense flash attention forward.
+//    HyperVAttention section 2, Eq. 4 (attention restricted to the selected
+//    key blocks; identity permutation) and the HyMoR-Attn Macro backbone.
+//  * micro_attn: HyMoR-Attn Micro residual over 16x16 tiles.
+//  * merge: HyMoR-Attn exact LSE merging.
+//
+// Matrix-core formulation (v_mfma_f32_32x32x16_bf16, wave64).  A wave owns
+// 32 query rows.  It computes S^T = K Q^T (m = key, n = query, k = d) so that
+// each lane holds 32 scores of ONE query (its column): the row max and sum of
+// the online softmax are in-lane plus a single exchange with lane^32, and
+// the rescale of the output is one scalar per lane.  The PV product is
+// O^T = V^T P^T (m = d, n = query, k = key); the S^T accumulator registers
+// of a lane are exactly its P^T operand for a 16-key chunk once the keys of
+// the chunk are permuted consistently on the V^T side (done by transpose_v).
+#include "bsa_device.h"
+#include "bsa_internal.h"
+
+namespace bsa {
+
+// Position p (0..15) inside a 16-key chunk of V^T holds key
+// 8*((p%8)/4) + 4*(p/8) + (p%4): lane group g = p/8, slot j = p%8 of the
+// 32x32x16 operand maps to key 8*(j/4) + 4*g + j%4, which is the key order
+// of the 32x32 accumulator rows the lane holds.
+__device__ __forceinline__ int vt_key_of_pos(int p) {
+  return 8 * ((p & 7) >> 2) + 4 * (p >> 3) + (p & 3);
+}
+
+// ---------------------------------------------------------------- V^T
+
+template <int D>
+__global__ __launch_bounds__(256) void transpose_v_kernel(TransposeArgs a) {
+  constexpr int C = D / 8;
+  __shared__ uint32_t tile[64][D / 2 + 1];  // bf16 pairs; +1 word breaks bank aliasing
+
+  const int j = blockIdx.x;
+  const int h = a.heads.h[blockIdx.y];
+  const int b = blockIdx.z;
+  const int tid = threadIdx.x;
+  const uint16_t* V = a.V + (int64_t)b * a.sb + (int64_t)h * a.sh;
+  uint16_t* Vt = a.Vt + ((int64_t)b * a.H + h) * D * a.Npad;
+
+  for (int f = tid; f < 64 * C; f += 256) {
+    const int row = f / C, c = f % C;
+    const int key = j * kBlock + row;
+    u32x4 v = {0u, 0u, 0u, 0u};
+    if (key < a.N) v = *(const u32x4*)(V + (int64_t)key * a.sn + c * 8);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) tile[row][c * 4 + e] = v[e];
+  }
+  __syncthreads();
+  const uint16_t* t16 = (const uint16_t*)&tile[0][0];
+  constexpr int RS = D + 2;  // row stride of the tile in bf16 elements
+  for (int f = tid; f < D * 8; f += 256) {
+    const int d = f >> 3, u = f & 7;  // 8 output keys at positions 8u..8u+7
+    uint32_t w[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int p0 = 8 * u + 2 * e;
+      const int k0 = 16 * (p0 >> 4) + vt_key_of_pos(p0 & 15);
+      const int k1 = 16 * ((p0 + 1) >> 4) + vt_key_of_pos((p0 + 1) & 15);
+      w[e] = bf16_bits_to_f16_bits(t16[k0 * RS + d]) |
+             (bf16_bits_to_f16_bits(t16[k1 * RS + d]) << 16);
+    }
+    const u32x4 out = {w[0], w[1], w[2], w[3]};
+    *(u32x4*)(Vt + (int64_t)d * a.Npad + j * kBlock + 8 * u) = out;
+  }
+}
+
+// ---------------------------------------------------------- attention
+
+template <bool OUT_BF16>
+__device__ __forceinline__ void store4(void* O, int64_t off, float x0, float x1, float x2, float x3) {
+  if constexpr (OUT_BF16) {
+    const u32x2 v = {pack_bf16x2(x0, x1), pack_bf16x2(x2, x3)};
+    *(u32x2*)((uint16_t*)O + off) = v;
+  } else {
+    const f32x4 v = {x0, x1, x2, x3};
+    *(f32x4*)((float*)O + off) = v;
+  }
+}
+
+// One workgroup per (b, h, 64-row query block), two waves of 32 rows.  Per
+// selected key block the 64 x d K tile and the d x 64 V^T tile are staged
+// in LDS (16-byte chunks XOR-swizzled by row to spread the banks).
+template <int D, bool DENSE, bool OUT_BF16>
+__global__ __launch_bounds__(128) void attn_fwd_kernel(AttnArgs a) {
+  constexpr int DC = D / 8;      // 16-byte chunks per K row
+  constexpr int KS = D / 16;     // k-steps of the QK^T product
+  constexpr int DT = D / 32;     // 32-row d tiles of the PV product
+  __shared__ __attribute__((aligned(16))) uint16_t sK[64 * D];
+  __shared__ __attribute__((aligned(16))) uint16_t sV[D * 64];
+
+  // XCD-aware order: dispatch w runs on XCD w % 8; give each XCD a
+  // contiguous range of (head, query block) rows so its L2 sees one head's
+  // neighbouring query blocks, whose key selections overlap.
+  const int w = blockIdx.x;
+  const int L = (w & 7) * a.per_xcd + (w >> 3);
+  if (L >= a.rows) return;
+  const int i = L % a.nB;
+  const int bh = L / a.nB;
+  const int b = bh / a.H, h = bh % a.H;
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63;
+  const int n = lane & 31, g = lane >> 5;
+  const int64_t base = (int64_t)b * a.sb + (int64_t)h * a.sh;
+  const uint16_t* Qh = a.Q + base;
+  const uint16_t* Kh = a.K + base;
+  const uint16_t* Vth = a.Vt + (int64_t)bh * D * a.Npad;
+
+  const int q = i * kBlock + wave * 32 + n;
+  bf16x8 qf[KS];
+#pragma unroll
+  for (int s = 0; s < KS; ++s) {
+    u32x4 v = {0u, 0u, 0u, 0u};
+    if (q < a.N) v = *(const u32x4*)(Qh + (int64_t)q * a.sn + 16 * s + 8 * g);
+    qf[s] = __builtin_bit_cast(bf16x8, v);
+  }
+
+  f32x16 o[DT];
+#pragma unroll
+  for (int t = 0; t < DT; ++t)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) o[t][r] = 0.f;
+  float m_run = -INFINITY, l_run = 0.f;
+  const float c = a.scale_log2;
+
+  int e0, e1;
+  if constexpr (DENSE) {
+    e0 = 0;
+    e1 = a.nB;
+  } else {
+    e0 = a.row_ptr[L];
+    e1 = a.row_ptr[L + 1];
+  }
+  for (int e = e0; e < e1; ++e) {
+    const int j = DENSE ? e : a.col_idx[e];
+    __syncthreads();  // the previous tiles are consumed
+#pragma unroll
+    for (int it = 0; it < 64 * DC / 128; ++it) {
+      const int f = tid + 128 * it;
+      const int row = f / DC, ch = f % DC;
+      const int key = j * kBlock + row;
+      u32x4 v = {0u, 0u, 0u, 0u};
+      if (key < a.N) v = *(const u32x4*)(Kh + (int64_t)key * a.sn + ch * 8);
+      *(u32x4*)(sK + row * D + ((ch ^ (row % DC)) * 8)) = v;
+    }
+#pragma unroll
+    for (int it = 0; it < D * 8 / 128; ++it) {
+      const int f = tid + 128 * it;
+      const int row = f >> 3, ch = f & 7;
+      const u32x4 v = *(const u32x4*)(Vth + (int64_t)row * a.Npad + j * kBlock + ch * 8);
+      *(u32x4*)(sV + row * 64 + ((ch ^ (row & 7)) * 8)) = v;
+    }
+    __syncthreads();
+
+    // S^T for keys 0..31 (s0) and 32..63 (s1) of the block.
+    f32x16 s0, s1;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      s0[r] = 0.f;
+      s1[r] = 0.f;
+    }
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      const int r0 = n, r1 = 32 + n;
+      const bf16x8 k0 = *(const bf16x8*)(sK + r0 * D + (((2 * s + g) ^ (r0 % DC)) * 8));
+      const bf16x8 k1 = *(const bf16x8*)(sK + r1 * D + (((2 * s + g) ^ (r1 % DC)) * 8));
+      s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k0, qf[s], s0, 0, 0, 0);
+      s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k1, qf[s], s1, 0, 0, 0);
+    }
+    // Lane holds keys 8*(r/4) + 4*g + r%4 (+32 for s1) of query q.
+    if (j == a.nB - 1) {
+      const int nvalid = a.N - j * kBlock;
+      if (nvalid < kBlock) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int kk = 8 * (r >> 2) + 4 * g + (r & 3);
+          if (kk >= nvalid) s0[r] = -INFINITY;
+          if (kk + 32 >= nvalid) s1[r] = -INFINITY;
+        }
+      }
+    }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, fmaxf(s0[r], s1[r]));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float m_new = fmaxf(m_run, mx * c);
+    // Lazy rescale: keep a stale running max while the new one exceeds it
+    // by at most 8 (in log2 units); probabilities then stay below 2^8, which
+    // fp32 sums and bf16 operands hold exactly as well.  The result is the
+    // same softmax because the final normaliser uses the same max.
+    if (__any(m_new > m_run + 8.0f)) {
+      const float alpha = (m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
+      l_run *= alpha;
+#pragma unroll
+      for (int t = 0; t < DT; ++t)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) o[t][r] *= alpha;
+      m_run = m_new;
+    }
+    float ps = 0.f;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      s0[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s0[r], c, -m_run));
+      s1[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s1[r], c, -m_run));
+      ps += s0[r] + s1[r];
+    }
+    l_run += ps;
+    f16x8 pf[4];
+#pragma unroll
+    for (int cc = 0; cc < 4; ++cc) {
+      const f32x16& src = (cc < 2) ? s0 : s1;
+      const int r0 = 8 * (cc & 1);
+      const u32x4 pk = {pack_f16x2(src[r0 + 0], src[r0 + 1]), pack_f16x2(src[r0 + 2], src[r0 + 3]),
+                        pack_f16x2(src[r0 + 4], src[r0 + 5]), pack_f16x2(src[r0 + 6], src[r0 + 7])};
+      pf[cc] = __builtin_bit_cast(f16x8, pk);
+    }
+#pragma unroll
+    for (int t = 0; t < DT; ++t) {
+      const int row = 32 * t + n;
+#pragma unroll
+      for (int cc = 0; cc < 4; ++cc) {
+        const f16x8 va = *(const f16x8*)(sV + row * 64 + (((2 * cc + g) ^ (row & 7)) * 8));
+        o[t] = __builtin_amdgcn_mfma_f32_32x32x16_f16(va, pf[cc], o[t], 0, 0, 0);
+      }
+    }
+  }
+
+  const float l_tot = l_run + __shfl_xor(l_run, 32);
+  const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+  const float lse = l_tot > 0.f ? (m_run + __builtin_log2f(l_tot)) * kLn2 : -INFINITY;
+  if (q < a.N) {
+    const int64_t orow = base + (int64_t)q * a.sn;
+#pragma unroll
+    for (int t = 0; t < DT; ++t)
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) {
+        const int d0 = 32 * t + 8 * rr + 4 * g;
+        store4<OUT_BF16>(a.O, orow + d0, o[t][4 * rr] * inv, o[t][4 * rr + 1] * inv,
+                         o[t][4 * rr + 2] * inv, o[t][4 * rr + 3] * inv);
+      }
+    if (g == 0) a.LSE[(int64_t)bh * a.N + q] = lse;
+  }
+}
+
+// ---------------------------------------------------------------- micro
+
+// One workgroup per (b, micro head, query block); wave a handles query
+// sub-tile a (16 rows) over its selected 16-key tiles.  16x16x32 products
+// for S^T = K Q^T (lane holds 4 keys of one query), 16x16x16 products for
+// O^T = V^T P^T (fp16) whose P^T operand is exactly those 4 accumulator
+// registers.
+template <int D, bool OUT_BF16>
+__global__ __launch_bounds__(256) void micro_attn_kernel(MicroAttnArgs a) {
+  constexpr int KS = D / 32;
+  constexpr int DT = D / 16;
+  const int i = blockIdx.x;
+  const int z = blockIdx.y;
+  const int nh = a.heads.n;
+  const int b = z / nh, h = a.heads.h[z % nh];
+  const int64_t bh = (int64_t)b * a.H + h;
+  const int64_t r = bh * a.nB + i;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int n16 = lane & 15, g4 = lane >> 4;
+  const int q0 = i * kBlock + wave * kMicro;
+  if (q0 >= a.N) return;
+
+  // This sub-tile's segment of the row (entries sorted by sub-tile, then tile).
+  const int rb = a.row_ptr[r], re = a.row_ptr[r + 1];
+  int lt = 0, le = 0;
+  for (int e = rb + lane; e < re; e += 64) {
+    const int sub = a.idx[e] & 3;
+    lt += sub < wave;
+    le += sub <= wave;
+  }
+  lt = wave_sum(lt);
+  le = wave_sum(le);
+  const int es = rb + lt, ee = rb + le;
+
+  const int64_t base = (int64_t)b * a.sb + (int64_t)h * a.sh;
+  const uint16_t* Qh = a.Q + base;
+  const uint16_t* Kh = a.K + base;
+  const uint16_t* Vth = a.Vt + bh * D * a.Npad;
+  const int q = q0 + n16;
+  bf16x8 qf[KS];
+#pragma unroll
+  for (int s = 0; s < KS; ++s) {
+    u32x4 v = {0u, 0u, 0u, 0u};
+    if (q < a.N) v = *(const u32x4*)(Qh + (int64_t)q * a.sn + 32 * s + 8 * g4);
+    qf[s] = __builtin_bit_cast(bf16x8, v);
+  }
+  f32x4 o[DT];
+#pragma unroll
+  for (int t = 0; t < DT; ++t) o[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_run = -INFINITY, l_run = 0.f;
+  const float c = a.scale_log2;
+  const int vpos = 4 * (2 * (g4 & 1) + (g4 >> 1));  // position of keys 4*g4.. in the chunk
+
+  for (int e = es; e < ee; ++e) {
+    const int beta = a.idx[e] >> 2;
+    const int key = beta * kMicro + n16;
+    f32x4 sacc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      u32x4 v = {0u, 0u, 0u, 0u};
+      if (key < a.N) v = *(const u32x4*)(Kh + (int64_t)key * a.sn + 32 * s + 8 * g4);
+      sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, v), qf[s], sacc,
+                                                     0, 0, 0);
+    }
+    // lane holds keys beta*16 + 4*g4 + rr of query q
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr)
+      if (beta * kMicro + 4 * g4 + rr >= a.N) sacc[rr] = -INFINITY;
+    float mx = fmaxf(fmaxf(sacc[0], sacc[1]), fmaxf(sacc[2], sacc[3]));
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float m_new = fmaxf(m_run, mx * c);
+    if (__any(m_new > m_run + 8.0f)) {
+      const float alpha = (m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
+      l_run *= alpha;
+#pragma unroll
+      for (int t = 0; t < DT; ++t) o[t] *= alpha;
+      m_run = m_new;
+    }
+    float p[4];
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr) {
+      p[rr] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[rr], c, -m_run));
+      l_run += p[rr];
+    }
+    const u32x2 pk = {pack_f16x2(p[0], p[1]), pack_f16x2(p[2], p[3])};
+    const f16x4 pb = __builtin_bit_cast(f16x4, pk);
+#pragma unroll
+    for (int t = 0; t < DT; ++t) {
+      const u32x2 v = *(const u32x2*)(Vth + (int64_t)(16 * t + n16) * a.Npad + beta * kMicro + vpos);
+      o[t] = __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4, v), pb, o[t], 0, 0, 0);
+    }
+  }
+  float l_tot = l_run + __shfl_xor(l_run, 16);
+  l_tot += __shfl_xor(l_tot, 32);
+  const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+  const float lse = l_tot > 0.f ? (m_run + __builtin_log2f(l_tot)) * kLn2 : -INFINITY;
+  if (q < a.N) {
+    const int64_t orow = base + (int64_t)q * a.sn;
+#pragma unroll
+    for (int t = 0; t < DT; ++t)
+      store4<OUT_BF16>(a.O, orow + 16 * t + 4 * g4, o[t][0] * inv, o[t][1] * inv, o[t][2] * inv,
+                       o[t][3] * inv);
+    if (g4 == 0) a.LSE[bh * a.N + q] = lse;
+  }
+}
+
+// ---------------------------------------------------------------- merge
+
+// Each row is handled by D/8 consecutive lanes of one wave, 8 elements per
+// lane; every lane loads L1/L2 before any lane stores, so O/L may alias
+// O1/L1.
+template <bool BF16>
+__global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
+  const int h = a.heads.h[blockIdx.y];
+  const int b = blockIdx.z;
+  const int C = a.D / 8;
+  const int64_t f = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t q = f / C;
+  const int cidx = (int)(f % C);
+  if (q >= a.N) return;
+  const int64_t lrow = ((int64_t)b * a.H + h) * a.N + q;
+  const float l1 = a.L1[lrow], l2 = a.L2[lrow];
+  const float mx = fmaxf(l1, l2);
+  float Lm, w1, w2;
+  if (mx == -INFINITY) {
+    Lm = -INFINITY;
+    w1 = 0.f;
+    w2 = 0.f;
+  } else {
+    Lm = mx + logf(expf(l1 - mx) + expf(l2 - mx));
+    w1 = expf(l1 - Lm);
+    w2 = expf(l2 - Lm);
+  }
+  const int64_t off = (int64_t)b * a.sb + (int64_t)h * a.sh + q * a.sn + cidx * 8;
+  if constexpr (BF16) {
+    const u32x4 x = *(const u32x4*)((const uint16_t*)a.O1 + off);
+    const u32x4 y = *(const u32x4*)((const uint16_t*)a.O2 + off);
+    u32x4 out;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float lo = w1 * bf16_bits_to_f32(x[e] & 0xFFFFu) + w2 * bf16_bits_to_f32(y[e] & 0xFFFFu);
+      const float hi = w1 * bf16_bits_to_f32(x[e] >> 16) + w2 * bf16_bits_to_f32(y[e] >> 16);
+      out[e] = pack_bf16x2(lo, hi);
+    }
+    *(u32x4*)((uint16_t*)a.O + off) = out;
+  } else {
+    const f32x4* x = (const f32x4*)((const float*)a.O1 + off);
+    const f32x4* y = (const f32x4*)((const float*)a.O2 + off);
+    const f32x4 x0 = x[0], x1 = x[1], y0 = y[0], y1 = y[1];
+    f32x4* out = (f32x4*)((float*)a.O + off);
+    out[0] = w1 * x0 + w2 * y0;
+    out[1] = w1 * x1 + w2 * y1;
+  }
+  if (cidx == 0) a.L[lrow] = Lm;
+}
+
+// -------------------------------------------------------------- launchers
+
+hipError_t launch_transpose_v(const TransposeArgs& a, int B, int D, hipStream_t s) {
+  dim3 grid(a.nB, a.heads.n, B);
+  if (D == 128)
+    hipLaunchKernelGGL(transpose_v_kernel<128>, grid, dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL(transpose_v_kernel<64>, grid, dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+template <int D, bool DENSE>
+static void launch_attn_t(const AttnArgs& a, bool out_bf16, hipStream_t s) {
+  dim3 grid(8 * a.per_xcd);
+  if (out_bf16)
+    hipLaunchKernelGGL((attn_fwd_kernel<D, DENSE, true>), grid, dim3(128), 0, s, a);
+  else
+    hipLaunchKernelGGL((attn_fwd_kernel<D, DENSE, false>), grid, dim3(128), 0, s, a);
+}
+
+hipError_t launch_attn(const AttnArgs& a, int D, bool dense, bool out_bf16, hipStream_t s) {
+  if (D == 128) {
+    if (dense) launch_attn_t<128, true>(a, out_bf16, s);
+    else launch_attn_t<128, false>(a, out_bf16, s);
+  } else {
+    if (dense) launch_attn_t<64, true>(a, out_bf16, s);
+    else launch_attn_t<64, false>(a, out_bf16, s);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_micro_attn(const MicroAttnArgs& a, int B, int D, bool out_bf16, hipStream_t s) {
+  dim3 grid(a.nB, B * a.heads.n);
+  if (D == 128) {
+    if (out_bf16) hipLaunchKernelGGL((micro_attn_kernel<128, true>), grid, dim3(256), 0, s, a);
+    else hipLaunchKernelGGL((micro_attn_kernel<128, false>), grid, dim3(256), 0, s, a);
+  } else {
+    if (out_bf16) hipLaunchKernelGGL((micro_attn_kernel<64, true>), grid, dim3(256), 0, s, a);
+    else hipLaunchKernelGGL((micro_attn_kernel<64, false>), grid, dim3(256), 0, s, a);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_merge(const MergeArgs& a, int B, bool bf16, hipStream_t s) {
+  const int64_t threads = (int64_t)a.N * (a.D / 8);
+  dim3 grid((unsigned)((threads + 255) / 256), a.heads.n, B);
+  if (bf16) hipLaunchKernelGGL(merge_kernel<true>, grid, dim3(256), 0, s, a);
+  else hipLaunchKernelGGL(merge_kernel<false>, grid, dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace bsa

@@ -1,0 +1,129 @@
+// Kernel argument structs and launchers shared by the C-ABI layer (api.hip)
+// and the kernel translation units.  Host and device visible.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace bsa {
+
+constexpr int kMaxHeads = 256;  // heads per (b) a head list can name
+
+// Compact list of head indices, passed by value to kernels.
+struct HeadList {
+  int32_t n;
+  int32_t h[kMaxHeads];
+};
+
+struct PoolArgs {
+  const uint16_t* Q;
+  const uint16_t* K;
+  int64_t sb, sh, sn;
+  int H, N, D, nB, nT;
+  float* qpool;
+  float* kpool;
+  float* qpool16;  // may be null
+  float* kpool16;  // may be null
+};
+
+struct GemmArgs {
+  const float* A;   // [B*H, M, D]
+  const float* Bm;  // [B*H, Nc, D]
+  float* C;         // [nbatch, M, Nc]
+  int H, M, Nc, D;
+  float scale;
+  HeadList heads;   // batch z -> (z / heads.n, heads.h[z % heads.n])
+};
+
+struct SelectArgs {
+  const float* scores;  // [rows, nB] or null
+  uint32_t* bits;       // [rows, W]
+  int32_t* counts;      // [rows]
+  int N, nB, W, P2;
+  int mode, k, k_min, k_cap;
+  float p;
+  int force_diag, use_static;
+  int frame_tokens, window_frames, n_anchors, anchor_offset;
+};
+
+struct MicroSelectArgs {
+  const float* sigma;          // [B*nh, nT, nT]
+  const int32_t* macro_row_ptr;
+  const int32_t* macro_col_idx;
+  int32_t* slots;              // [rows, m]
+  int32_t* counts;             // [rows]
+  int H, nB, nT, W, m;
+  HeadList heads;
+};
+
+struct AttnArgs {
+  const uint16_t* Q;
+  const uint16_t* K;
+  const uint16_t* Vt;  // [B*H, D, Npad] key-major, 16-key chunks permuted
+  void* O;
+  float* LSE;
+  const int32_t* row_ptr;
+  const int32_t* col_idx;
+  int64_t sb, sh, sn;
+  int B, H, N, nB, Npad;
+  float scale_log2;  // softmax scale * log2(e)
+  int rows;          // B*H*nB
+  int per_xcd;       // ceil(rows / 8)
+};
+
+struct MicroAttnArgs {
+  const uint16_t* Q;
+  const uint16_t* K;
+  const uint16_t* Vt;
+  void* O;
+  float* LSE;
+  const int32_t* row_ptr;
+  const int32_t* idx;
+  int64_t sb, sh, sn;
+  int H, N, nB, Npad;
+  float scale_log2;
+  HeadList heads;
+};
+
+struct TransposeArgs {
+  const uint16_t* V;
+  uint16_t* Vt;
+  int64_t sb, sh, sn;
+  int H, N, nB, Npad;
+  HeadList heads;  // heads to transpose (all for macro/dense attention)
+};
+
+struct MergeArgs {
+  const void* O1;
+  const float* L1;
+  const void* O2;
+  const float* L2;
+  void* O;
+  float* L;
+  int64_t sb, sh, sn;
+  int H, N, D;
+  HeadList heads;
+};
+
+hipError_t launch_pool(const PoolArgs& a, int B, hipStream_t s);
+hipError_t launch_score_gemm(const GemmArgs& a, int nbatch, hipStream_t s);
+hipError_t launch_fill_i32(int32_t* p, int64_t n, int32_t v, hipStream_t s);
+hipError_t launch_select(const SelectArgs& a, int rows, hipStream_t s);
+hipError_t launch_scan(const int32_t* counts, int rows, int32_t* row_ptr,
+                       int64_t* out_nnz, hipStream_t s);
+hipError_t launch_emit_bits(const uint32_t* bits, int W, int rows,
+                            const int32_t* row_ptr, int32_t* col_idx,
+                            int64_t cap, hipStream_t s);
+hipError_t launch_micro_select(const MicroSelectArgs& a, int B, hipStream_t s);
+hipError_t launch_emit_slots(const int32_t* slots, int m, int rows,
+                             const int32_t* row_ptr, int32_t* col_idx,
+                             int64_t cap, hipStream_t s);
+hipError_t launch_transpose_v(const TransposeArgs& a, int B, int D,
+                              hipStream_t s);
+hipError_t launch_attn(const AttnArgs& a, int D, bool dense, bool out_bf16,
+                       hipStream_t s);
+hipError_t launch_micro_attn(const MicroAttnArgs& a, int B, int D,
+                             bool out_bf16, hipStream_t s);
+hipError_t launch_merge(const MergeArgs& a, int B, bool bf16, hipStream_t s);
+
+}  // namespace bsa

@@ -1,0 +1,155 @@
+// Block pooling and pooled block scores (Rectified SpaAttn: pooled query-key
+// interactions; HyperVAttention section 2, Eq. 2 left, centroids = member
+// means).  Both are HBM/ALU bound; no matrix cores: the scores feed an exact
+// selection, so they stay in float32 end to end.
+#include "bsa_device.h"
+#include "bsa_internal.h"
+
+namespace bsa {
+
+// One workgroup per (64-token block i, head h, batch b, tensor Q|K).
+// 256 threads: thread = (16-byte chunk c of a row, token group g).  Each
+// group sums a run of consecutive tokens; groups are then combined into the
+// four 16-token tile sums and the 64-token block sum.  Only valid tokens
+// (index < N) contribute and the divisor is the valid count.
+template <int D>
+__global__ __launch_bounds__(256) void pool_kernel(PoolArgs a) {
+  constexpr int C = D / 8;        // 16-byte chunks per token row
+  constexpr int G = 256 / C;      // token groups
+  constexpr int TPG = 64 / G;     // tokens per group
+  constexpr int GPT = 16 / TPG;   // groups per 16-token tile
+  __shared__ float part[G][D + 4];
+  __shared__ float tile[4][D];
+
+  const int i = blockIdx.x;
+  const int h = blockIdx.y;
+  const int b = blockIdx.z >> 1;
+  const bool isK = blockIdx.z & 1;
+  const uint16_t* X = (isK ? a.K : a.Q) + (int64_t)b * a.sb + (int64_t)h * a.sh;
+  const int tid = threadIdx.x;
+  const int c = tid % C;
+  const int g = tid / C;
+
+  float acc[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) acc[e] = 0.f;
+#pragma unroll
+  for (int t = 0; t < TPG; ++t) {
+    const int tok = i * kBlock + g * TPG + t;
+    if (tok < a.N) {
+      const u32x4 v = *(const u32x4*)(X + (int64_t)tok * a.sn + c * 8);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        acc[2 * e] += bf16_bits_to_f32(v[e] & 0xFFFFu);
+        acc[2 * e + 1] += bf16_bits_to_f32(v[e] >> 16);
+      }
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < 8; ++e) part[g][c * 8 + e] = acc[e];
+  __syncthreads();
+
+  const int64_t bh = (int64_t)b * a.H + h;
+  float* pool16 = isK ? a.kpool16 : a.qpool16;
+  for (int idx = tid; idx < 4 * D; idx += 256) {
+    const int t = idx / D, e = idx % D;
+    float s = 0.f;
+#pragma unroll
+    for (int gg = 0; gg < GPT; ++gg) s += part[t * GPT + gg][e];
+    tile[t][e] = s;
+    const int t0 = i * kBlock + t * kMicro;
+    const int cnt = min(kMicro, a.N - t0);
+    if (pool16 != nullptr && cnt > 0)
+      pool16[(bh * a.nT + 4 * i + t) * D + e] = s / (float)cnt;
+  }
+  __syncthreads();
+  float* pool = isK ? a.kpool : a.qpool;
+  const int cnt = min(kBlock, a.N - i * kBlock);
+  for (int e = tid; e < D; e += 256) {
+    const float s = (tile[0][e] + tile[1][e]) + (tile[2][e] + tile[3][e]);
+    pool[(bh * a.nB + i) * D + e] = s / (float)cnt;
+  }
+}
+
+// Batched float32 C = scale * A B^T with A [M, D], B [Nc, D] per batch.
+// 64x64 output tile per workgroup, 256 threads with 4x4 outputs each, the
+// shared dimension staged through LDS in chunks of 32.  Batch z maps to the
+// (b, h) pair through the head list so the same kernel serves the pooled
+// block scores (all heads) and the micro tile scores (selected heads).
+__global__ __launch_bounds__(256) void score_gemm_kernel(GemmArgs a) {
+  constexpr int TK = 32;
+  __shared__ float As[TK][64 + 4];
+  __shared__ float Bs[TK][64 + 4];
+
+  const int z = blockIdx.z;
+  const int b = z / a.heads.n;
+  const int h = a.heads.h[z % a.heads.n];
+  const int64_t src = (int64_t)b * a.H + h;
+  const float* A = a.A + src * a.M * a.D;
+  const float* Bm = a.Bm + src * a.Nc * a.D;
+  float* Cm = a.C + (int64_t)z * a.M * a.Nc;
+
+  const int m0 = blockIdx.y * 64, n0 = blockIdx.x * 64;
+  const int tid = threadIdx.x;
+  const int tx = tid & 15, ty = tid >> 4;
+  float acc[4][4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) acc[r][q] = 0.f;
+
+  for (int k0 = 0; k0 < a.D; k0 += TK) {
+    // 64 rows x 32 floats per operand = 512 float4; 2 per thread each.
+#pragma unroll
+    for (int it = 0; it < 2; ++it) {
+      const int f = tid + 256 * it;
+      const int row = f >> 3, c4 = (f & 7) * 4;
+      f32x4 va = {0.f, 0.f, 0.f, 0.f}, vb = {0.f, 0.f, 0.f, 0.f};
+      if (m0 + row < a.M) va = *(const f32x4*)(A + (int64_t)(m0 + row) * a.D + k0 + c4);
+      if (n0 + row < a.Nc) vb = *(const f32x4*)(Bm + (int64_t)(n0 + row) * a.D + k0 + c4);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        As[c4 + e][row] = va[e];
+        Bs[c4 + e][row] = vb[e];
+      }
+    }
+    __syncthreads();
+#pragma unroll 8
+    for (int k = 0; k < TK; ++k) {
+      const f32x4 av = *(const f32x4*)&As[k][ty * 4];
+      const f32x4 bv = *(const f32x4*)&Bs[k][tx * 4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) acc[r][q] = __builtin_fmaf(av[r], bv[q], acc[r][q]);
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int m = m0 + ty * 4 + r;
+    if (m >= a.M) continue;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int n = n0 + tx * 4 + q;
+      if (n < a.Nc) Cm[(int64_t)m * a.Nc + n] = a.scale * acc[r][q];
+    }
+  }
+}
+
+hipError_t launch_pool(const PoolArgs& a, int B, hipStream_t s) {
+  dim3 grid(a.nB, a.H, 2 * B);
+  if (a.D == 128)
+    hipLaunchKernelGGL(pool_kernel<128>, grid, dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL(pool_kernel<64>, grid, dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_score_gemm(const GemmArgs& a, int nbatch, hipStream_t s) {
+  dim3 grid((a.Nc + 63) / 64, (a.M + 63) / 64, nbatch);
+  hipLaunchKernelGGL(score_gemm_kernel, grid, dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace bsa

@@ -1,0 +1,472 @@
+// Block selection -> CSR lists.
+//
+// Macro rows (one workgroup per (b, h, query block i)):
+//   top-k:  the k key blocks of highest pooled score, ties to the lower
+//           index (block-sparse density budget);
+//   top-p:  HyperVAttention section 2, Eq. 2 (size-weighted centroid
+//           softmax) and Eq. 3 (smallest descending prefix with cumulative
+//           probability at least p), clamped to [k_min, k_cap];
+//   forced: diagonal and/or the LVSA temporal window + rotating anchors.
+// The row is built as a bitmask in LDS, counted, prefix-summed across rows
+// into row_ptr, and emitted as ascending column indices.
+//
+// Micro rows (HyMoR-Attn Micro selection, 16-token tiles inside omitted
+// blocks): one workgroup per (b, micro head, query block); radix selection
+// of the top-m candidate scores with ties to the lower code, emitted in
+// (sub-tile, key tile) order.
+#include <climits>
+
+#include "bsa_device.h"
+#include "bsa_internal.h"
+
+namespace bsa {
+
+enum { kTopK = 0, kTopP = 1, kStatic = 2 };
+
+// ---------------------------------------------------------------- helpers
+
+// Block-wide sum of an int over blockDim.x threads (multiple of 64).
+template <typename T>
+__device__ T block_sum(T v, T* red) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int nw = blockDim.x >> 6;
+  v = wave_sum(v);
+  __syncthreads();
+  if (lane == 0) red[wave] = v;
+  __syncthreads();
+  T t = 0;
+  for (int w = 0; w < nw; ++w) t += red[w];
+  return t;
+}
+
+template <typename T>
+__device__ T block_max(T v, T* red) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int nw = blockDim.x >> 6;
+  v = wave_max(v);
+  __syncthreads();
+  if (lane == 0) red[wave] = v;
+  __syncthreads();
+  T t = red[0];
+  for (int w = 1; w < nw; ++w) t = max(t, red[w]);
+  return t;
+}
+
+__device__ int block_min_int(int v, int* red) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int nw = blockDim.x >> 6;
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v = min(v, __shfl_xor(v, off));
+  __syncthreads();
+  if (lane == 0) red[wave] = v;
+  __syncthreads();
+  int t = red[0];
+  for (int w = 1; w < nw; ++w) t = min(t, red[w]);
+  return t;
+}
+
+// Exclusive prefix over the threads of the block (in thread order); also
+// returns the block total.
+template <typename T>
+__device__ T block_exclusive_scan(T v, T* red, T* total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int nw = blockDim.x >> 6;
+  const T inc = wave_inclusive_scan(v);
+  __syncthreads();
+  if (lane == 63) red[wave] = inc;
+  __syncthreads();
+  T off = 0, tot = 0;
+  for (int w = 0; w < nw; ++w) {
+    if (w < wave) off += red[w];
+    tot += red[w];
+  }
+  *total = tot;
+  return off + inc - v;
+}
+
+__device__ __forceinline__ float key_to_positive_float(uint64_t key) {
+  const uint32_t k32 = (uint32_t)(key >> 32);
+  return __uint_as_float(k32 & 0x7FFFFFFFu);  // keys of positive floats
+}
+
+// ----------------------------------------------------------- macro select
+
+__global__ __launch_bounds__(256) void select_kernel(SelectArgs a) {
+  __shared__ uint64_t keys[4096];
+  __shared__ uint32_t mask[128];
+  __shared__ double dred[8];
+  __shared__ float fred[8];
+  __shared__ int ired[8];
+
+  const int r = blockIdx.x;
+  const int i = r % a.nB;
+  const int tid = threadIdx.x;
+  for (int w = tid; w < a.W; w += 256) mask[w] = 0u;
+  __syncthreads();
+
+  if (a.mode == kTopK || a.mode == kTopP) {
+    const float* row = a.scores + (int64_t)r * a.nB;
+    float mx = -INFINITY;
+    if (a.mode == kTopP) {
+      for (int j = tid; j < a.nB; j += 256) mx = fmaxf(mx, row[j]);
+      mx = block_max(mx, fred);
+    }
+    const float tail_size = (float)(a.N - (a.nB - 1) * kBlock);
+    for (int j = tid; j < a.P2; j += 256) {
+      uint64_t key = 0;
+      if (j < a.nB) {
+        float v = row[j];
+        if (a.mode == kTopP) v = (j == a.nB - 1 ? tail_size : (float)kBlock) * expf(v - mx);
+        key = ((uint64_t)float_order_key(v) << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)j);
+      }
+      keys[j] = key;
+    }
+    __syncthreads();
+    // Bitonic sort, descending: (value desc, index asc) since the low word
+    // holds the complemented index.
+    for (int k = 2; k <= a.P2; k <<= 1) {
+      for (int jj = k >> 1; jj > 0; jj >>= 1) {
+        for (int t = tid; t < (a.P2 >> 1); t += 256) {
+          const int lo = 2 * jj * (t / jj) + (t % jj);
+          const int hi = lo + jj;
+          const uint64_t x = keys[lo], y = keys[hi];
+          const bool desc = (lo & k) == 0;
+          if (desc ? (x < y) : (x > y)) {
+            keys[lo] = y;
+            keys[hi] = x;
+          }
+        }
+        __syncthreads();
+      }
+    }
+    int L;
+    if (a.mode == kTopK) {
+      L = min(a.k, a.nB);
+    } else {
+      // Cumulative mass in descending order, in double.
+      const int E = max(1, a.P2 / 256);
+      const int start = tid * E;
+      double local = 0.0;
+      for (int e = 0; e < E; ++e) {
+        const int pos = start + e;
+        if (pos < a.nB) local += (double)key_to_positive_float(keys[pos]);
+      }
+      double total;
+      const double excl = block_exclusive_scan(local, dred, &total);
+      const double thr = (double)a.p * total;
+      int first = INT_MAX;
+      double run = excl;
+      for (int e = 0; e < E; ++e) {
+        const int pos = start + e;
+        if (pos >= a.nB) break;
+        run += (double)key_to_positive_float(keys[pos]);
+        if (run >= thr) {
+          first = pos;
+          break;
+        }
+      }
+      first = block_min_int(first, ired);
+      L = (first == INT_MAX) ? a.nB : first + 1;
+      L = max(L, a.k_min);
+      L = min(L, a.k_cap);
+      L = min(L, a.nB);
+    }
+    for (int pos = tid; pos < L; pos += 256) {
+      const uint32_t j = 0xFFFFFFFFu - (uint32_t)(keys[pos] & 0xFFFFFFFFull);
+      atomicOr(&mask[j >> 5], 1u << (j & 31));
+    }
+  }
+  if (a.force_diag && tid == 0) atomicOr(&mask[i >> 5], 1u << (i & 31));
+  if (a.use_static) {
+    const int ft = a.frame_tokens;
+    const int lo_i = (i * kBlock) / ft;
+    const int hi_i = (min(i * kBlock + kBlock, a.N) - 1) / ft;
+    for (int j = tid; j < a.nB; j += 256) {
+      const int lo_j = (j * kBlock) / ft;
+      const int hi_j = (min(j * kBlock + kBlock, a.N) - 1) / ft;
+      if (lo_j <= hi_i + a.window_frames && hi_j >= lo_i - a.window_frames)
+        atomicOr(&mask[j >> 5], 1u << (j & 31));
+    }
+    if (a.n_anchors > 0) {
+      const int64_t stride = a.nB / a.n_anchors;
+      const int64_t off = ((int64_t)a.anchor_offset % a.nB + a.nB) % a.nB;
+      for (int t = tid; t < a.n_anchors; t += 256) {
+        const int j = (int)((off + t * stride) % a.nB);
+        atomicOr(&mask[j >> 5], 1u << (j & 31));
+      }
+    }
+  }
+  __syncthreads();
+  int cnt = 0;
+  for (int w = tid; w < a.W; w += 256) {
+    const uint32_t v = mask[w];
+    a.bits[(int64_t)r * a.W + w] = v;
+    cnt += __popc(v);
+  }
+  cnt = block_sum(cnt, ired);
+  if (tid == 0) a.counts[r] = cnt;
+}
+
+// -------------------------------------------------------- row pointers
+
+__global__ __launch_bounds__(1024) void scan_kernel(const int32_t* counts, int rows,
+                                                    int32_t* row_ptr, int64_t* out_nnz) {
+  __shared__ int64_t red[16];
+  const int tid = threadIdx.x;
+  const int per = (rows + 1023) / 1024;
+  const int start = tid * per;
+  int64_t local = 0;
+  for (int e = 0; e < per; ++e) {
+    const int idx = start + e;
+    if (idx < rows) local += counts[idx];
+  }
+  int64_t total;
+  int64_t run = block_exclusive_scan(local, red, &total);
+  for (int e = 0; e < per; ++e) {
+    const int idx = start + e;
+    if (idx >= rows) break;
+    row_ptr[idx] = (int32_t)run;
+    run += counts[idx];
+  }
+  if (tid == 0) {
+    row_ptr[rows] = (int32_t)total;
+    *out_nnz = total;
+  }
+}
+
+// One wave per row: ascending indices of the set bits.
+__global__ __launch_bounds__(256) void emit_bits_kernel(const uint32_t* bits, int W, int rows,
+                                                        const int32_t* row_ptr,
+                                                        int32_t* col_idx, int64_t cap) {
+  const int r = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (r >= rows) return;
+  const int lane = threadIdx.x & 63;
+  const int wpl = (W + 63) / 64;
+  const int w0 = lane * wpl;
+  const uint32_t* rb = bits + (int64_t)r * W;
+  int cnt = 0;
+  for (int e = 0; e < wpl; ++e)
+    if (w0 + e < W) cnt += __popc(rb[w0 + e]);
+  const int incl = wave_inclusive_scan(cnt);
+  int64_t pos = (int64_t)row_ptr[r] + incl - cnt;
+  for (int e = 0; e < wpl; ++e) {
+    const int w = w0 + e;
+    if (w >= W) break;
+    uint32_t v = rb[w];
+    while (v) {
+      const int bit = __ffs(v) - 1;
+      if (pos < cap) col_idx[pos] = w * 32 + bit;
+      ++pos;
+      v &= v - 1;
+    }
+  }
+}
+
+__global__ void fill_i32_kernel(int32_t* p, int64_t n, int32_t v) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = v;
+}
+
+// ---------------------------------------------------------- micro select
+
+// Radix selection, most significant byte first, of the `remaining`-th
+// largest 32-bit key among the candidates for which fn(c, &key) is true.
+// On return `remaining` holds how many candidates equal to the returned
+// threshold must still be taken.  All threads of the block call it.
+template <class Fn>
+__device__ uint32_t block_radix_select(int ncand, int& remaining, Fn fn,
+                                       uint32_t* hist, int* shared_out) {
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  uint32_t prefix = 0, pmask = 0;
+  for (int shift = 24; shift >= 0; shift -= 8) {
+    for (int q = tid; q < 256; q += blockDim.x) hist[q] = 0u;
+    __syncthreads();
+    for (int c = tid; c < ncand; c += blockDim.x) {
+      uint32_t key;
+      if (fn(c, &key) && (key & pmask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1u);
+    }
+    __syncthreads();
+    if (wave == 0) {
+      const int b0 = 4 * lane;
+      const int h0 = hist[b0], h1 = hist[b0 + 1], h2 = hist[b0 + 2], h3 = hist[b0 + 3];
+      const int mine = h0 + h1 + h2 + h3;
+      // suffix sum over lanes: count of keys in bins >= 4*lane
+      int suf = mine;
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const int o = __shfl_down(suf, off);
+        if (lane + off < 64) suf += o;
+      }
+      const int above_lane = suf - mine;  // bins >= 4*(lane+1)
+      if (above_lane < remaining && suf >= remaining) {
+        int above = above_lane;
+        const int hb[4] = {h0, h1, h2, h3};
+        for (int q = 3; q >= 0; --q) {
+          if (above + hb[q] >= remaining) {
+            shared_out[0] = b0 + q;
+            shared_out[1] = above;
+            break;
+          }
+          above += hb[q];
+        }
+      }
+    }
+    __syncthreads();
+    const uint32_t digit = (uint32_t)shared_out[0];
+    remaining -= shared_out[1];
+    prefix |= digit << shift;
+    pmask |= 0xFFu << shift;
+    __syncthreads();
+  }
+  return prefix;
+}
+
+__global__ __launch_bounds__(1024) void micro_select_kernel(MicroSelectArgs a) {
+  __shared__ uint32_t omask[128];
+  __shared__ uint32_t hist[256];
+  __shared__ int sh_out[2];
+  __shared__ int ired[16];
+
+  const int i = blockIdx.x;
+  const int z = blockIdx.y;
+  const int nh = a.heads.n;
+  const int b = z / nh;
+  const int h = a.heads.h[z % nh];
+  const int64_t r = ((int64_t)b * a.H + h) * a.nB + i;
+  const int tid = threadIdx.x;
+
+  for (int w = tid; w < a.W; w += 1024) omask[w] = 0u;
+  __syncthreads();
+  const int rb = a.macro_row_ptr[r], re = a.macro_row_ptr[r + 1];
+  for (int e = rb + tid; e < re; e += 1024) {
+    const int j = a.macro_col_idx[e];
+    atomicOr(&omask[j >> 5], 1u << (j & 31));
+  }
+  __syncthreads();
+
+  const int nT = a.nT;
+  const int nq = min(4, nT - 4 * i);
+  const int ncand = nq * nT;
+  const float* sig = a.sigma + ((int64_t)z * nT + 4 * i) * nT;
+  auto valid = [&](int c) {
+    const int beta = c % nT;
+    const int blk = beta >> 2;
+    return ((omask[blk >> 5] >> (blk & 31)) & 1u) == 0u;
+  };
+  auto score_key = [&](int c, uint32_t* key) {
+    if (!valid(c)) return false;
+    *key = float_order_key(sig[c]);
+    return true;
+  };
+
+  int nvalid = 0;
+  for (int c = tid; c < ncand; c += 1024) nvalid += valid(c) ? 1 : 0;
+  nvalid = block_sum(nvalid, ired);
+
+  const int m = a.m;
+  uint32_t T = 0u, Tc = 0u;
+  int mode = 0;  // 0: take all valid; 1: key >= T; 2: key > T or (== T and ~code >= Tc)
+  if (nvalid > m) {
+    int remaining = m;
+    T = block_radix_select(ncand, remaining, score_key, hist, sh_out);
+    int n_eq = 0;
+    for (int c = tid; c < ncand; c += 1024) {
+      uint32_t key;
+      if (score_key(c, &key) && key == T) ++n_eq;
+    }
+    n_eq = block_sum(n_eq, ired);
+    if (n_eq == remaining) {
+      mode = 1;
+    } else {
+      // ties at the threshold: the lowest codes win (largest ~code)
+      auto tie_key = [&](int c, uint32_t* key) {
+        uint32_t k;
+        if (!score_key(c, &k) || k != T) return false;
+        const uint32_t code = 4u * (uint32_t)(c % nT) + (uint32_t)(c / nT);
+        *key = ~code;
+        return true;
+      };
+      int rem2 = remaining;
+      Tc = block_radix_select(ncand, rem2, tie_key, hist, sh_out);
+      mode = 2;
+    }
+  }
+
+  // Compaction in candidate order (sub-tile a major, key tile beta minor).
+  int32_t* out = a.slots + r * (int64_t)m;
+  int written = 0;
+  for (int base = 0; base < ncand; base += 1024) {
+    const int c = base + tid;
+    bool sel = false;
+    if (c < ncand) {
+      uint32_t key;
+      if (score_key(c, &key)) {
+        if (mode == 0) sel = true;
+        else if (mode == 1) sel = key >= T;
+        else {
+          const uint32_t code = 4u * (uint32_t)(c % nT) + (uint32_t)(c / nT);
+          sel = key > T || (key == T && ~code >= Tc);
+        }
+      }
+    }
+    int tot;
+    const int pos = block_exclusive_scan((int)sel, ired, &tot);
+    if (sel && written + pos < m) out[written + pos] = 4 * (c % nT) + c / nT;
+    written += tot;
+  }
+  if (tid == 0) a.counts[r] = min(written, m);
+}
+
+// One wave per row: copy the row's slots into the CSR column array.
+__global__ __launch_bounds__(256) void emit_slots_kernel(const int32_t* slots, int m, int rows,
+                                                         const int32_t* row_ptr,
+                                                         int32_t* col_idx, int64_t cap) {
+  const int r = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (r >= rows) return;
+  const int lane = threadIdx.x & 63;
+  const int64_t b = row_ptr[r];
+  const int n = row_ptr[r + 1] - row_ptr[r];
+  for (int e = lane; e < n; e += 64)
+    if (b + e < cap) col_idx[b + e] = slots[(int64_t)r * m + e];
+}
+
+// -------------------------------------------------------------- launchers
+
+hipError_t launch_fill_i32(int32_t* p, int64_t n, int32_t v, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(fill_i32_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, p, n, v);
+  return hipGetLastError();
+}
+
+hipError_t launch_select(const SelectArgs& a, int rows, hipStream_t s) {
+  hipLaunchKernelGGL(select_kernel, dim3(rows), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_scan(const int32_t* counts, int rows, int32_t* row_ptr, int64_t* out_nnz,
+                       hipStream_t s) {
+  hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(1024), 0, s, counts, rows, row_ptr, out_nnz);
+  return hipGetLastError();
+}
+
+hipError_t launch_emit_bits(const uint32_t* bits, int W, int rows, const int32_t* row_ptr,
+                            int32_t* col_idx, int64_t cap, hipStream_t s) {
+  hipLaunchKernelGGL(emit_bits_kernel, dim3((rows + 3) / 4), dim3(256), 0, s, bits, W, rows,
+                     row_ptr, col_idx, cap);
+  return hipGetLastError();
+}
+
+hipError_t launch_micro_select(const MicroSelectArgs& a, int B, hipStream_t s) {
+  hipLaunchKernelGGL(micro_select_kernel, dim3(a.nB, B * a.heads.n), dim3(1024), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_emit_slots(const int32_t* slots, int m, int rows, const int32_t* row_ptr,
+                             int32_t* col_idx, int64_t cap, hipStream_t s) {
+  hipLaunchKernelGGL(emit_slots_kernel, dim3((rows + 3) / 4), dim3(256), 0, s, slots, m, rows,
+                     row_ptr, col_idx, cap);
+  return hipGetLastError();
+}
+
+}  // namespace bsa

@@ -1,0 +1,269 @@
+/*
+ * bsa.h -- block-sparse self-attention for video diffusion transformers on
+ * AMD Instinct MI355X (gfx950).  Plain C ABI: pointers, sizes, status codes.
+ *
+ * The hot path, in call order:
+ *   bsa_score_blocks      mean-pool Q and K over 64-token blocks (and 16-token
+ *                         tiles) and form the pooled block scores;
+ *   bsa_select_blocks     per query block, the key blocks to keep (top-k,
+ *                         top-p, static window + rotating anchors, or the
+ *                         micro tiles inside omitted blocks) as CSR lists;
+ *   bsa_sparse_attn_fwd   block-sparse flash attention: O and per-row LSE;
+ *   bsa_micro_residual_fwd attention over the selected 16x16 micro tiles;
+ *   bsa_lse_merge         exact merge of two partial softmax results.
+ *   bsa_dense_attn_fwd    the same attention engine over every key (baseline).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * Tensors Q, K, V (and attention outputs O) are [B, H, N, d] with element
+ * strides stride_b, stride_h, stride_n taken from bsa_shape and the last
+ * dimension contiguous.  Q, K, V are bf16 (passed as uint16_t bit patterns);
+ * base pointers must be 16-byte aligned and the strides multiples of 8.
+ * Tokens are a video latent grid flattened t-major.  N is the number of
+ * valid tokens: the last 64-token block (and 16-token tile) may be ragged;
+ * padded positions are never read as keys nor written as queries.
+ * Per-row LSE arrays are float32 [B, H, N], contiguous.  All other arrays are
+ * contiguous as documented.  d must be 64 or 128; the block must be 64 and
+ * the micro tile 16.
+ *
+ * Every pointer except those marked "host" is device memory owned by the
+ * caller; the library keeps no state between calls and allocates nothing.
+ * Calls are asynchronous on `stream` (a hipStream_t; NULL = the default
+ * stream) and never synchronise.  Arguments are validated before anything is
+ * launched: a non-zero status means nothing was enqueued, and
+ * bsa_last_error() (thread-local) says why.  A launch failure reported by
+ * the HIP runtime returns BSA_ERR_HIP.  NaN/Inf inputs are not checked.
+ *
+ * Sources (pages as titled): "HyperVAttention: Efficient Sparse Attention
+ * with Spatio-Temporal Clustering for Video Diffusion" (HVA), section 2,
+ * Eq. 2-4; "HyMoR-Attn: Granularity-Matched Repair of Omitted Attention
+ * Support for Video Diffusion" (abstract: Macro backbone, Micro residual,
+ * exact LSE merging); "Rectified SpaAttn" (abstract: pooled query-key
+ * interactions); the "Long Video Sparse Attention" (LVSA) abstract (window
+ * pattern with rotating global anchors); "Mixture of Distributions Matters"
+ * (MOD-DiT: block-wise attention, density = computed blocks / all blocks).
+ */
+#ifndef BSA_H_
+#define BSA_H_
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t bsa_status;
+enum {
+  BSA_OK = 0,
+  BSA_ERR_INVALID_ARG = 1, /* null pointer, bad size, misalignment, ... */
+  BSA_ERR_UNSUPPORTED = 2, /* d not in {64,128}, block != 64, micro != 16, */
+                           /* too many blocks for a scored selection       */
+  BSA_ERR_CAPACITY = 3,    /* workspace smaller than required              */
+  BSA_ERR_HIP = 4          /* the HIP runtime reported an error            */
+};
+
+/* Element type of attention outputs O (and of merge inputs). */
+enum { BSA_F32 = 0, BSA_BF16 = 1 };
+
+typedef struct bsa_shape {
+  int32_t B, H, N, d;
+  int64_t stride_b, stride_h, stride_n; /* elements; last dim contiguous */
+} bsa_shape;
+
+/* Library version string, e.g. "bsa 0.1.0 gfx950". */
+const char* bsa_version(void);
+
+/* Message describing the last non-OK status returned on this thread. */
+const char* bsa_last_error(void);
+
+/* ------------------------------------------------------------------------
+ * bsa_score_blocks -- pooled block scores (Rectified SpaAttn: pooled
+ * query-key interactions; HVA section 2, Eq. 2 left, with centroids = block
+ * means).
+ *
+ *   qpool[b,h,i,:] = mean of Q[b,h,t,:] over the valid tokens t of block i
+ *   kpool[b,h,j,:] = same for K
+ *   scores[b,h,i,j] = scale * <qpool[b,h,i,:], kpool[b,h,j,:]>
+ *
+ * block: must be 64.  nB = ceil(N / 64).
+ * qpool, kpool: float32 [B, H, nB, d] (required).
+ * scores: float32 [B, H, nB, nB], or NULL to skip the score matrix.
+ * micro: 0, or 16 to also write the 16-token tile means qpool16 / kpool16,
+ *   float32 [B, H, nT, d] with nT = ceil(N / 16) (required when micro=16).
+ * Accumulation is float32 (no bf16 rounding of the means or scores).
+ * ---------------------------------------------------------------------- */
+bsa_status bsa_score_blocks(const uint16_t* Q, const uint16_t* K,
+                            const bsa_shape* shape, int32_t block, float scale,
+                            float* qpool, float* kpool, float* scores,
+                            int32_t micro, float* qpool16, float* kpool16,
+                            void* stream);
+
+/* ------------------------------------------------------------------------
+ * Selection parameters.
+ *
+ * mode BSA_SELECT_TOPK: keep the k key blocks of highest score, ties to the
+ *   lower block index (the Top-K density budget of block-sparse selectors).
+ * mode BSA_SELECT_TOPP: HVA Eq. 2 right and Eq. 3: size-weighted softmax
+ *   P_ij = n_j e^{S_ij} / sum_o n_o e^{S_io} (n_j = valid tokens of block
+ *   j); keep the smallest prefix in descending P whose cumulative mass is at
+ *   least p, clamped to [k_min, k_cap] blocks (HVA appendix A.1 "Min-kc" is
+ *   the floor; the density cap is the ceiling).
+ * mode BSA_SELECT_STATIC: no scores; only the forced set below.
+ * mode BSA_SELECT_MICRO: HyMoR Micro selection (reading: for query block i,
+ *   candidates are pairs (a, beta) of a 16-row query sub-tile a = 0..3 of
+ *   block i and a 16-key tile beta whose 64-block was omitted by the macro
+ *   lists; score sigma = scale * <qpool16[4i+a], kpool16[beta]>; keep the
+ *   micro_m best by (sigma descending, code ascending), code = 4*beta + a).
+ *   Entries are codes, sorted by (a, beta).  Heads with head_mask[h] == 0 get
+ *   empty rows.
+ *
+ * Forced set (a union on top of TOPK/TOPP, not counted in k or p; the whole
+ * row in STATIC mode):
+ *   force_diag: block i itself;
+ *   use_static: the LVSA static mask -- key block j is kept when some token
+ *   of j lies within window_frames latent frames of some token of block i
+ *   (frame of token t = t / frame_tokens), plus n_anchors global anchor
+ *   blocks (anchor_offset + a * floor(nB / n_anchors)) mod nB, a = 0..n-1.
+ *   The caller draws anchor_offset per call (rotation).
+ * ---------------------------------------------------------------------- */
+enum {
+  BSA_SELECT_TOPK = 0,
+  BSA_SELECT_TOPP = 1,
+  BSA_SELECT_STATIC = 2,
+  BSA_SELECT_MICRO = 3
+};
+
+typedef struct bsa_select_params {
+  int32_t mode;
+  int32_t k;        /* TOPK: blocks per row (0 <= k)                    */
+  float p;          /* TOPP: threshold in (0, 1]                         */
+  int32_t k_min;    /* TOPP: floor on the row length (>= 0)              */
+  int32_t k_cap;    /* TOPP: ceiling on the row length (>= k_min)        */
+  int32_t force_diag;
+  int32_t use_static;
+  int32_t frame_tokens;   /* > 0 when use_static                          */
+  int32_t window_frames;  /* >= 0                                         */
+  int32_t n_anchors;      /* >= 0                                         */
+  int32_t anchor_offset;  /* any value; taken modulo nB                   */
+  /* MICRO mode only */
+  int32_t micro;          /* 16                                           */
+  int32_t micro_m;        /* tiles kept per query block (>= 0)             */
+  float scale;            /* softmax scale of the micro score              */
+  const uint8_t* head_mask;      /* host [H]; NULL = every head            */
+  const int32_t* macro_row_ptr;  /* device, macro CSR of this shape        */
+  const int32_t* macro_col_idx;  /* device                                  */
+  const float* qpool16;          /* device [B,H,nT,d] from bsa_score_blocks */
+  const float* kpool16;          /* device [B,H,nT,d]                       */
+} bsa_select_params;
+
+/* Bytes of device workspace bsa_select_blocks needs for these arguments
+ * (returns -1 on invalid arguments; see bsa_last_error). */
+int64_t bsa_select_workspace_bytes(const bsa_shape* shape, int32_t block,
+                                   const bsa_select_params* params);
+
+/* Upper bound on the total entries bsa_select_blocks can emit. */
+int64_t bsa_select_max_nnz(const bsa_shape* shape, int32_t block,
+                           const bsa_select_params* params);
+
+/* ------------------------------------------------------------------------
+ * bsa_select_blocks -- CSR block lists, one row per (b, h, query block i),
+ * row index r = (b * H + h) * nB + i.
+ *
+ * scores: float32 [B, H, nB, nB] from bsa_score_blocks (TOPK/TOPP); NULL in
+ *   STATIC and MICRO mode.
+ * row_ptr: int32 [B*H*nB + 1]; row r is col_idx[row_ptr[r] .. row_ptr[r+1]).
+ * col_idx: int32 [col_cap]: ascending key block indices (MICRO: codes
+ *   4*beta + a, sorted by (a, beta)).  Entries at positions >= col_cap are
+ *   not written; *out_nnz tells the caller whether col_cap sufficed.
+ * out_nnz: device int64, receives the total number of entries.
+ * workspace: device, at least bsa_select_workspace_bytes(...) bytes; its
+ *   contents on entry do not matter.
+ * Limits: TOPK/TOPP need nB <= 4096 (N <= 262144 tokens); totals must fit
+ * in int32.
+ * ---------------------------------------------------------------------- */
+bsa_status bsa_select_blocks(const float* scores, const bsa_shape* shape,
+                             int32_t block, const bsa_select_params* params,
+                             int32_t* row_ptr, int32_t* col_idx,
+                             int64_t col_cap, int64_t* out_nnz,
+                             void* workspace, int64_t workspace_bytes,
+                             void* stream);
+
+/* Bytes of device workspace the attention entry points need (the key-major
+ * copy of V the PV products read).  Returns -1 on invalid arguments. */
+int64_t bsa_attn_workspace_bytes(const bsa_shape* shape);
+
+/* ------------------------------------------------------------------------
+ * bsa_sparse_attn_fwd -- block-sparse attention forward (HVA Eq. 4 on the
+ * original token order; the HyMoR Macro backbone).  For every valid query
+ * token t of block i, over the keys of the blocks in its CSR row:
+ *   LSE[t] = ln sum_tau exp(scale * q_t . k_tau)
+ *   O[t]   = sum_tau exp(scale * q_t . k_tau - LSE[t]) v_tau
+ * QK^T and PV run as bf16 matrix-core products with float32 accumulation;
+ * the softmax is online (flash style) in float32.  Rows with an empty list
+ * get O = 0 and LSE = -inf.
+ *
+ * row_ptr / col_idx: a CSR from bsa_select_blocks (or the caller); column
+ *   indices must lie in [0, nB).  Order within a row does not matter.
+ * O: [B, H, N, d] with the strides of `shape`, element type o_dtype
+ *   (BSA_F32 or BSA_BF16, round-to-nearest-even).
+ * LSE: float32 [B, H, N].
+ * workspace: device, >= bsa_attn_workspace_bytes(shape) bytes, 256-byte
+ *   aligned.  The call first writes a key-major fp16 copy of V into it (the
+ *   PV operand; V entries must lie within the fp16 range |v| <= 65504).
+ * V may be NULL: the workspace then must already hold that copy, written by
+ *   an earlier attention call on the same V and shape (all heads for the
+ *   sparse/dense calls; the masked heads for the micro call), so that the
+ *   macro, micro and dense passes over one V share a single conversion.
+ * ---------------------------------------------------------------------- */
+bsa_status bsa_sparse_attn_fwd(const uint16_t* Q, const uint16_t* K,
+                               const uint16_t* V, const bsa_shape* shape,
+                               int32_t block, float scale,
+                               const int32_t* row_ptr, const int32_t* col_idx,
+                               void* O, int32_t o_dtype, float* LSE,
+                               void* workspace, int64_t workspace_bytes,
+                               void* stream);
+
+/* bsa_dense_attn_fwd -- the same engine over all N keys for every query
+ * (full attention; the speedup baseline). Arguments as above. */
+bsa_status bsa_dense_attn_fwd(const uint16_t* Q, const uint16_t* K,
+                              const uint16_t* V, const bsa_shape* shape,
+                              float scale, void* O, int32_t o_dtype,
+                              float* LSE, void* workspace,
+                              int64_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * bsa_micro_residual_fwd -- HyMoR Micro residual: each 16-row query sub-tile
+ * a of block i attends over the union of the 16-key tiles beta of the
+ * entries (a, beta) in its micro row (codes 4*beta + a, as emitted by
+ * BSA_SELECT_MICRO).  Output as bsa_sparse_attn_fwd; sub-tiles without a
+ * tile get O = 0, LSE = -inf.  Heads with head_mask[h] == 0 (host [H];
+ * NULL = all heads) are skipped and their O_mu / LSE_mu left untouched.
+ * ---------------------------------------------------------------------- */
+bsa_status bsa_micro_residual_fwd(const uint16_t* Q, const uint16_t* K,
+                                  const uint16_t* V, const bsa_shape* shape,
+                                  int32_t block, int32_t micro, float scale,
+                                  const int32_t* mrow_ptr, const int32_t* midx,
+                                  const uint8_t* head_mask, void* O_mu,
+                                  int32_t o_dtype, float* LSE_mu,
+                                  void* workspace, int64_t workspace_bytes,
+                                  void* stream);
+
+/* ------------------------------------------------------------------------
+ * bsa_lse_merge -- HyMoR exact LSE merging of two partial attention results
+ * over disjoint key supports:
+ *   L = ln(e^L1 + e^L2);  O = e^(L1 - L) O1 + e^(L2 - L) O2
+ * Both -inf gives O = 0, L = -inf.  O1/O2/O share element type o_dtype and
+ * the strides of `shape`; L arrays are float32 [B, H, N].  O may alias O1
+ * and L may alias L1 (in-place).  Heads with head_mask[h] == 0 (host [H];
+ * NULL = all) are left untouched.
+ * ---------------------------------------------------------------------- */
+bsa_status bsa_lse_merge(const void* O1, const float* L1, const void* O2,
+                         const float* L2, const bsa_shape* shape,
+                         int32_t o_dtype, const uint8_t* head_mask, void* O,
+                         float* L, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BSA_H_ */

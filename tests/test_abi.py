@@ -1,0 +1,143 @@
+"""The C-ABI library: it loads, exports every entry point include/bsa.h
+declares, and its host-side validation rejects bad arguments before any
+GPU work (these calls return before touching the HIP runtime)."""
+
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _ensure_built():
+    lib = os.path.join(ROOT, "block_sparse_attention_pool_amd", "_lib", "libbsa.so")
+    if not os.path.exists(lib):
+        from block_sparse_attention_pool_amd import build as b
+        b.build()
+    return lib
+
+
+LIB = _ensure_built()
+import block_sparse_attention_pool_amd as bsa  # noqa: E402
+
+
+def header_functions():
+    src = open(os.path.join(ROOT, "include", "bsa.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(bsa_\w+)\s*\(", src)))
+
+
+def test_header_declares_the_hot_path():
+    fns = header_functions()
+    for name in ("bsa_score_blocks", "bsa_select_blocks", "bsa_sparse_attn_fwd",
+                 "bsa_micro_residual_fwd", "bsa_lse_merge", "bsa_dense_attn_fwd"):
+        assert name in fns
+
+
+def test_every_declared_symbol_is_exported():
+    out = subprocess.run(["nm", "-D", "--defined-only", LIB], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r"\bT (bsa_\w+)$", out, flags=re.M))
+    missing = [f for f in header_functions() if f not in exported]
+    assert not missing, missing
+    assert set(bsa.EXPORTED) == set(header_functions())
+
+
+def test_version():
+    assert "gfx950" in bsa.bsa_version()
+
+
+def _shape(B=1, H=2, N=1000, d=128, sb=None, sh=None, sn=None):
+    sn = d if sn is None else sn
+    sh = N * sn if sh is None else sh
+    sb = H * sh if sb is None else sb
+    return bsa._Shape(B, H, N, d, sb, sh, sn)
+
+
+def test_workspace_sizes():
+    s = _shape(B=1, H=2, N=1000, d=128)
+    npad = 16 * 64
+    assert bsa._lib.bsa_attn_workspace_bytes(ctypes.byref(s)) == 2 * 128 * npad * 2
+    sp, _ = bsa.make_select_params("topk", k=4, nB=16)
+    rows, W = 2 * 16, 1
+    ws = bsa._lib.bsa_select_workspace_bytes(ctypes.byref(s), 64, ctypes.byref(sp))
+    assert ws == 256 + 256 and rows * W * 4 <= 256
+    assert bsa._lib.bsa_select_max_nnz(ctypes.byref(s), 64, ctypes.byref(sp)) == rows * 4
+    sp.force_diag = 1
+    assert bsa._lib.bsa_select_max_nnz(ctypes.byref(s), 64, ctypes.byref(sp)) == rows * 5
+
+
+@pytest.mark.parametrize("kw,status,msg", [
+    (dict(d=96), 2, "head dim"),
+    (dict(N=0), 1, "must all be >= 1"),
+    (dict(sn=132), 1, "multiples of 8"),
+    (dict(sn=100), 1, "inconsistent"),
+    (dict(H=300), 2, "exceeds"),
+])
+def test_shape_validation(kw, status, msg):
+    s = _shape(**kw)
+    buf = ctypes.c_void_p(4096)
+    st = bsa._lib.bsa_score_blocks(buf, buf, ctypes.byref(s), 64, 0.1, buf, buf, None, 0,
+                                   None, None, None)
+    assert st == status
+    assert msg in bsa.bsa_last_error()
+
+
+def test_null_and_misaligned_pointers():
+    s = _shape()
+    good = ctypes.c_void_p(4096)
+    st = bsa._lib.bsa_score_blocks(None, good, ctypes.byref(s), 64, 0.1, good, good, None, 0,
+                                   None, None, None)
+    assert st == 1 and "Q is NULL" in bsa.bsa_last_error()
+    bad = ctypes.c_void_p(4098)
+    st = bsa._lib.bsa_score_blocks(good, bad, ctypes.byref(s), 64, 0.1, good, good, None, 0,
+                                   None, None, None)
+    assert st == 1 and "aligned" in bsa.bsa_last_error()
+    st = bsa._lib.bsa_score_blocks(good, good, ctypes.byref(s), 32, 0.1, good, good, None, 0,
+                                   None, None, None)
+    assert st == 2 and "block" in bsa.bsa_last_error()
+
+
+def test_attention_rejects_small_workspace_and_bad_dtype():
+    s = _shape()
+    p = ctypes.c_void_p(4096)
+    need = bsa._lib.bsa_attn_workspace_bytes(ctypes.byref(s))
+    st = bsa._lib.bsa_sparse_attn_fwd(p, p, p, ctypes.byref(s), 64, 0.1, p, p, p, 0, p, p,
+                                      need - 1, None)
+    assert st == 3 and "workspace" in bsa.bsa_last_error()
+    st = bsa._lib.bsa_dense_attn_fwd(p, p, p, ctypes.byref(s), 0.1, p, 7, p, p, need, None)
+    assert st == 1 and "o_dtype" in bsa.bsa_last_error()
+
+
+def test_select_rejects_bad_params():
+    s = _shape()
+    p = ctypes.c_void_p(4096)
+    sp, _ = bsa.make_select_params("topp", p=1.5, nB=16)
+    ws = bsa._lib.bsa_select_workspace_bytes(ctypes.byref(s), 64, ctypes.byref(sp))
+    st = bsa._lib.bsa_select_blocks(p, ctypes.byref(s), 64, ctypes.byref(sp), p, p, 100, p, p,
+                                    ws, None)
+    assert st == 1 and "p=" in bsa.bsa_last_error()
+    sp, _ = bsa.make_select_params("topk", k=4, nB=16)
+    st = bsa._lib.bsa_select_blocks(p, ctypes.byref(s), 64, ctypes.byref(sp), p, p, 100, p, p,
+                                    1, None)
+    assert st == 3
+    sp.mode = 9
+    assert bsa._lib.bsa_select_workspace_bytes(ctypes.byref(s), 64, ctypes.byref(sp)) == -1
+    assert "mode" in bsa.bsa_last_error()
+    # scored selection over more than 4096 blocks is refused up front
+    big = _shape(N=4097 * 64)
+    sp.mode = 0
+    assert bsa._lib.bsa_select_workspace_bytes(ctypes.byref(big), 64, ctypes.byref(sp)) == -1
+    sp.mode = 2
+    assert bsa._lib.bsa_select_workspace_bytes(ctypes.byref(big), 64, ctypes.byref(sp)) == -1
+
+
+def test_budget_resolution():
+    assert bsa.budget_blocks(0.25, 512) == 128
+    assert bsa.budget_blocks(0.25, 16) == 4
+    assert bsa.budget_blocks(0.15, 1857) == 279
+    assert bsa.cap_blocks(0.20, 1182) == 236
+    assert bsa.budget_blocks(0.1, 30) == 3
