@@ -43,6 +43,9 @@ def parse():
                     help="time budget of the CPU oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--stage-reps", type=int, default=10)
+    ap.add_argument("--calibration-copy", action="store_true",
+                    help="first run a plain 256 MiB device copy (reads 256 MiB, writes "
+                         "256 MiB) three times, to scale hardware byte counters")
     return ap.parse_args()
 
 
@@ -127,6 +130,14 @@ def main():
     import torch
     import block_sparse_attention_pool_amd as bsa
     from synth import CONFIGS, config_spec, gen_qkv
+
+    if args.calibration_copy:
+        src = torch.ones(64 << 20, dtype=torch.float32, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            torch.mul(src, 1.0, out=dst)
+        torch.cuda.synchronize()
+        del src, dst
 
     cfg = 1
     c = CONFIGS[cfg]

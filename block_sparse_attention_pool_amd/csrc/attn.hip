@@ -87,16 +87,120 @@ __device__ __forceinline__ void store4(void* O, int64_t off, float x0, float x1,
   }
 }
 
-// One workgroup per (b, h, 64-row query block), two waves of 32 rows.  Per
-// selected key block the 64 x d K tile and the d x 64 V^T tile are staged
-// in LDS (16-byte chunks XOR-swizzled by row to spread the banks).
+typedef __attribute__((address_space(3))) uint16_t lds_u16;
+
+// LDS byte address of a shared-memory pointer.
+__device__ __forceinline__ uint32_t lds_addr(const uint16_t* p) {
+  return (uint32_t)(uintptr_t)(const lds_u16*)p;
+}
+
+// One direct global->LDS copy of 16 bytes per lane: lane l's bytes from
+// sbase + voff land at LDS byte m0 + 16*l.  Written as asm (no output
+// registers; M0 and memory declared clobbered) so that the compiler does not
+// order later LDS reads behind it: completion is awaited explicitly with
+// s_waitcnt vmcnt before the barrier that publishes the tile.
+__device__ __forceinline__ void dma16(uint32_t m0, const void* sbase, uint32_t voff) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2"
+               :
+               : "s"(m0), "v"(voff), "s"(sbase)
+               : "memory", "m0");
+}
+
+// Per-lane byte offsets of the tile copies of one wave (loop invariant).
+// K tile (64 x D bf16): instruction t covers rows t*RPI .. t*RPI+RPI-1; lane
+// l of it lands at LDS row t*RPI + l/DC, 16-byte position l%DC, so it fetches
+// global chunk (l%DC) ^ (row%DC) -- the row-XOR swizzle.  V^T tile (D x 64
+// fp16): 8 rows of 128 bytes per instruction, positions XOR (row%8).
+template <int D>
+struct TileCopy {
+  static constexpr int DC = D / 8;
+  static constexpr int RPI = 64 / DC;
+  static constexpr int NK = (64 / RPI) / 2;  // K instructions per wave
+  static constexpr int NVI = (D / 8) / 2;    // V instructions per wave
+  uint32_t koff[NK];
+  uint32_t voff[NVI];
+
+  __device__ __forceinline__ void init(int64_t sn, int Npad, int wave, int lane) {
+#pragma unroll
+    for (int u = 0; u < NK; ++u) {
+      const int t = wave + 2 * u;
+      const int r = t * RPI + lane / DC;
+      const int c = (lane % DC) ^ (r % DC);
+      koff[u] = (uint32_t)((r * sn + c * 8) * 2);
+    }
+#pragma unroll
+    for (int u = 0; u < NVI; ++u) {
+      const int t = wave + 2 * u;
+      const int r = t * 8 + lane / 8;
+      const int c = (lane % 8) ^ (r % 8);
+      voff[u] = (uint32_t)((r * (int64_t)Npad + c * 8) * 2);
+    }
+  }
+
+  // K rows past N (ragged last block) are clamped to row N-1; their scores
+  // are masked to -inf, so only in-bounds reads matter.
+  __device__ __forceinline__ void k_tile(const uint16_t* Kh, int64_t sn, int j, int N,
+                                         const uint16_t* sK, int wave, int lane) const {
+    const uint16_t* base = Kh + (int64_t)j * kBlock * sn;
+    if (j * kBlock + kBlock <= N) {
+#pragma unroll
+      for (int u = 0; u < NK; ++u) dma16(lds_addr(sK + (wave + 2 * u) * 512), base, koff[u]);
+    } else {
+      const int last = N - 1 - j * kBlock;
+#pragma unroll
+      for (int u = 0; u < NK; ++u) {
+        const int t = wave + 2 * u;
+        const int r = t * RPI + lane / DC;
+        const int c = (lane % DC) ^ (r % DC);
+        dma16(lds_addr(sK + t * 512), base, (uint32_t)((min(r, last) * sn + c * 8) * 2));
+      }
+    }
+  }
+
+  __device__ __forceinline__ void v_tile(const uint16_t* Vth, int j, const uint16_t* sV,
+                                         int wave) const {
+    const uint16_t* base = Vth + j * kBlock;
+#pragma unroll
+    for (int u = 0; u < NVI; ++u) dma16(lds_addr(sV + (wave + 2 * u) * 512), base, voff[u]);
+  }
+};
+
+// s_waitcnt vmcnt(n) with the other counters left alone (gfx9 encoding).
+template <int n>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(n >= 0 && n < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+// s_waitcnt lgkmcnt(0): this wave's LDS reads have returned.
+__device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
+
+// Workgroup execution barrier without the memory fence __syncthreads()
+// implies (that fence would also drain the asynchronous tile copies).  Every
+// call is preceded by the explicit waits that make the LDS contents it
+// publishes complete; the memory clobber keeps the compiler from moving LDS
+// accesses across it.
+__device__ __forceinline__ void exec_barrier() { asm volatile("s_barrier" ::: "memory"); }
+
+typedef __attribute__((address_space(4))) const int32_t const_i32;
+
+// One workgroup per (b, h, 64-row query block), two waves of 32 rows each.
+// Per selected key block the 64 x D K tile and the D x 64 V^T tile sit in
+// LDS (16-byte chunks XOR-swizzled by row).  The K buffer is refilled with
+// the next block as soon as both waves have finished QK^T, the V buffer as
+// soon as they have finished PV, so each copy overlaps the other half of
+// the iteration without a second buffer.  32 KB of LDS and at most 256
+// registers per lane leave room for four workgroups (two waves per SIMD)
+// per compute unit.
 template <int D, bool DENSE, bool OUT_BF16>
-__global__ __launch_bounds__(128) void attn_fwd_kernel(AttnArgs a) {
+__global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2)))
+void attn_fwd_kernel(AttnArgs a) {
   constexpr int DC = D / 8;      // 16-byte chunks per K row
   constexpr int KS = D / 16;     // k-steps of the QK^T product
   constexpr int DT = D / 32;     // 32-row d tiles of the PV product
-  __shared__ __attribute__((aligned(16))) uint16_t sK[64 * D];
-  __shared__ __attribute__((aligned(16))) uint16_t sV[D * 64];
+  constexpr int NV = TileCopy<D>::NVI;  // V^T copy instructions per wave per tile
+  __shared__ __attribute__((aligned(1024))) uint16_t sK[64 * D];
+  __shared__ __attribute__((aligned(1024))) uint16_t sV[D * 64];
 
   // XCD-aware order: dispatch w runs on XCD w % 8; give each XCD a
   // contiguous range of (head, query block) rows so its L2 sees one head's
@@ -109,12 +213,25 @@ __global__ __launch_bounds__(128) void attn_fwd_kernel(AttnArgs a) {
   const int b = bh / a.H, h = bh % a.H;
 
   const int tid = threadIdx.x;
-  const int wave = tid >> 6, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int n = lane & 31, g = lane >> 5;
   const int64_t base = (int64_t)b * a.sb + (int64_t)h * a.sh;
   const uint16_t* Qh = a.Q + base;
   const uint16_t* Kh = a.K + base;
   const uint16_t* Vth = a.Vt + (int64_t)bh * D * a.Npad;
+
+  // Row pointers and column indices are read-only for the kernel's
+  // lifetime: scalar loads (counted apart from the tile copies).
+  const_i32* row_ptr = (const_i32*)a.row_ptr;
+  const_i32* col_idx = (const_i32*)a.col_idx;
+  int e0, e1;
+  if constexpr (DENSE) {
+    e0 = 0;
+    e1 = a.nB;
+  } else {
+    e0 = row_ptr[L];
+    e1 = row_ptr[L + 1];
+  }
 
   const int q = i * kBlock + wave * 32 + n;
   bf16x8 qf[KS];
@@ -133,34 +250,22 @@ __global__ __launch_bounds__(128) void attn_fwd_kernel(AttnArgs a) {
   float m_run = -INFINITY, l_run = 0.f;
   const float c = a.scale_log2;
 
-  int e0, e1;
-  if constexpr (DENSE) {
-    e0 = 0;
-    e1 = a.nB;
-  } else {
-    e0 = a.row_ptr[L];
-    e1 = a.row_ptr[L + 1];
+  // The Q fragments must have arrived before the loop: otherwise the
+  // compiler places that wait inside the loop, where it would also drain
+  // the tile copies in flight.
+  wait_vmcnt<0>();
+  TileCopy<D> cp;
+  cp.init(a.sn, a.Npad, wave, lane);
+  int j = 0;
+  if (e0 < e1) {
+    j = DENSE ? e0 : col_idx[e0];
+    cp.k_tile(Kh, a.sn, j, a.N, sK, wave, lane);
+    cp.v_tile(Vth, j, sV, wave);
   }
   for (int e = e0; e < e1; ++e) {
-    const int j = DENSE ? e : a.col_idx[e];
-    __syncthreads();  // the previous tiles are consumed
-#pragma unroll
-    for (int it = 0; it < 64 * DC / 128; ++it) {
-      const int f = tid + 128 * it;
-      const int row = f / DC, ch = f % DC;
-      const int key = j * kBlock + row;
-      u32x4 v = {0u, 0u, 0u, 0u};
-      if (key < a.N) v = *(const u32x4*)(Kh + (int64_t)key * a.sn + ch * 8);
-      *(u32x4*)(sK + row * D + ((ch ^ (row % DC)) * 8)) = v;
-    }
-#pragma unroll
-    for (int it = 0; it < D * 8 / 128; ++it) {
-      const int f = tid + 128 * it;
-      const int row = f >> 3, ch = f & 7;
-      const u32x4 v = *(const u32x4*)(Vth + (int64_t)row * a.Npad + j * kBlock + ch * 8);
-      *(u32x4*)(sV + row * 64 + ((ch ^ (row & 7)) * 8)) = v;
-    }
-    __syncthreads();
+    const int jn = (e + 1 < e1) ? (DENSE ? e + 1 : col_idx[e + 1]) : j;
+    wait_vmcnt<NV>();  // this wave's K tile has landed (V may still fly)
+    exec_barrier();    // ... and the other wave's
 
     // S^T for keys 0..31 (s0) and 32..63 (s1) of the block.
     f32x16 s0, s1;
@@ -177,6 +282,11 @@ __global__ __launch_bounds__(128) void attn_fwd_kernel(AttnArgs a) {
       s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k0, qf[s], s0, 0, 0, 0);
       s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k1, qf[s], s1, 0, 0, 0);
     }
+    wait_lgkm0();      // this wave's reads of sK have returned
+    wait_vmcnt<0>();   // V tile of this block has landed
+    exec_barrier();    // both waves are done with sK; sV is complete
+    if (e + 1 < e1) cp.k_tile(Kh, a.sn, jn, a.N, sK, wave, lane);
+
     // Lane holds keys 8*(r/4) + 4*g + r%4 (+32 for s1) of query q.
     if (j == a.nB - 1) {
       const int nvalid = a.N - j * kBlock;
@@ -196,8 +306,8 @@ __global__ __launch_bounds__(128) void attn_fwd_kernel(AttnArgs a) {
     const float m_new = fmaxf(m_run, mx * c);
     // Lazy rescale: keep a stale running max while the new one exceeds it
     // by at most 8 (in log2 units); probabilities then stay below 2^8, which
-    // fp32 sums and bf16 operands hold exactly as well.  The result is the
-    // same softmax because the final normaliser uses the same max.
+    // fp32 sums and fp16 operands hold.  The result is the same softmax
+    // because the final normaliser uses the same max.
     if (__any(m_new > m_run + 8.0f)) {
       const float alpha = (m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
       l_run *= alpha;
@@ -227,12 +337,18 @@ __global__ __launch_bounds__(128) void attn_fwd_kernel(AttnArgs a) {
 #pragma unroll
     for (int t = 0; t < DT; ++t) {
       const int row = 32 * t + n;
+      f16x8 va[4];
 #pragma unroll
-      for (int cc = 0; cc < 4; ++cc) {
-        const f16x8 va = *(const f16x8*)(sV + row * 64 + (((2 * cc + g) ^ (row & 7)) * 8));
-        o[t] = __builtin_amdgcn_mfma_f32_32x32x16_f16(va, pf[cc], o[t], 0, 0, 0);
-      }
+      for (int cc = 0; cc < 4; ++cc)
+        va[cc] = *(const f16x8*)(sV + row * 64 + (((2 * cc + g) ^ (row & 7)) * 8));
+#pragma unroll
+      for (int cc = 0; cc < 4; ++cc)
+        o[t] = __builtin_amdgcn_mfma_f32_32x32x16_f16(va[cc], pf[cc], o[t], 0, 0, 0);
     }
+    wait_lgkm0();      // this wave's reads of sV have returned
+    exec_barrier();    // both waves are done with sV
+    if (e + 1 < e1) cp.v_tile(Vth, jn, sV, wave);
+    j = jn;
   }
 
   const float l_tot = l_run + __shfl_xor(l_run, 32);
