@@ -52,12 +52,12 @@ class _SelectParams(ctypes.Structure):
                 ("qpool16", ctypes.c_void_p), ("kpool16", ctypes.c_void_p)]
 
 
-def _load():
-    if not os.path.exists(_LIB_PATH):
+def _load(path: str = _LIB_PATH):
+    if not os.path.exists(path):
         raise ImportError(
-            f"{_LIB_PATH} is missing: build it with "
+            f"{path} is missing: build it with "
             "`python -m block_sparse_attention_pool_amd.build` (hipcc, gfx950)")
-    lib = ctypes.CDLL(_LIB_PATH)
+    lib = ctypes.CDLL(path)
     P, I32, I64, F32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float
     SP = ctypes.POINTER(_Shape)
     PP = ctypes.POINTER(_SelectParams)

@@ -20,6 +20,8 @@
 // O^T = V^T P^T (m = d, n = query, k = key); the S^T accumulator registers
 // of a lane are exactly its P^T operand for a 16-key chunk once the keys of
 // the chunk are permuted consistently on the V^T side (done by transpose_v).
+#include <type_traits>
+
 #include "bsa_device.h"
 #include "bsa_internal.h"
 
@@ -94,23 +96,41 @@ __device__ __forceinline__ uint32_t lds_addr(const uint16_t* p) {
   return (uint32_t)(uintptr_t)(const lds_u16*)p;
 }
 
-// One direct global->LDS copy of 16 bytes per lane: lane l's bytes from
-// sbase + voff land at LDS byte m0 + 16*l.  Written as asm (no output
-// registers; M0 and memory declared clobbered) so that the compiler does not
-// order later LDS reads behind it: completion is awaited explicitly with
-// s_waitcnt vmcnt before the barrier that publishes the tile.
-__device__ __forceinline__ void dma16(uint32_t m0, const void* sbase, uint32_t voff) {
-  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2"
-               :
-               : "s"(m0), "v"(voff), "s"(sbase)
-               : "memory", "m0");
+// Compile-time loop: f(std::integral_constant<int, U>) for U in [B, E).
+template <int B, int E, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (B < E) {
+    f(std::integral_constant<int, B>{});
+    static_for<B + 1, E>(f);
+  }
 }
+
+// One direct global->LDS copy of 16 bytes per lane: lane l's bytes from
+// sbase + voff land at LDS byte (m0base + OFF) + 16*l.  Written as asm (no
+// output registers; M0, SCC and memory declared clobbered) so that the
+// compiler does not order later LDS reads behind it: completion is awaited
+// explicitly with s_waitcnt vmcnt before the barrier that publishes the tile.
+template <int OFF>
+__device__ __forceinline__ void dma16(uint32_t m0base, const void* sbase, uint32_t voff) {
+  asm volatile("s_add_u32 m0, %0, %3\n\tglobal_load_lds_dwordx4 %1, %2"
+               :
+               : "s"(m0base), "v"(voff), "s"(sbase), "i"(OFF)
+               : "memory", "m0", "scc");
+}
+
+// XOR swizzle of the 16-byte chunks of V^T tile row r (128-byte rows).  A
+// 128-bit LDS read is served 16 lanes at a time by 64 four-byte banks; the
+// 16 lanes read 16 consecutive rows, and rows r and r+8 share banks unless
+// their chunk positions differ, hence the (r/2)%8 pattern.  K tile rows are
+// 256 bytes, where r%16 already separates 16 consecutive rows.
+__device__ __forceinline__ int vswz(int r) { return (r >> 1) & 7; }
 
 // Per-lane byte offsets of the tile copies of one wave (loop invariant).
 // K tile (64 x D bf16): instruction t covers rows t*RPI .. t*RPI+RPI-1; lane
 // l of it lands at LDS row t*RPI + l/DC, 16-byte position l%DC, so it fetches
 // global chunk (l%DC) ^ (row%DC) -- the row-XOR swizzle.  V^T tile (D x 64
-// fp16): 8 rows of 128 bytes per instruction, positions XOR (row%8).
+// fp16): 8 rows of 128 bytes per instruction, positions XOR vswz(row).  Wave w
+// issues instructions t = w, w+2, ...: 1 KB of LDS each, 2 KB apart.
 template <int D>
 struct TileCopy {
   static constexpr int DC = D / 8;
@@ -119,8 +139,10 @@ struct TileCopy {
   static constexpr int NVI = (D / 8) / 2;    // V instructions per wave
   uint32_t koff[NK];
   uint32_t voff[NVI];
+  uint32_t kbase, vbase;  // LDS byte address of this wave's first instruction
 
-  __device__ __forceinline__ void init(int64_t sn, int Npad, int wave, int lane) {
+  __device__ __forceinline__ void init(int64_t sn, int Npad, int wave, int lane,
+                                       const uint16_t* sK, const uint16_t* sV) {
 #pragma unroll
     for (int u = 0; u < NK; ++u) {
       const int t = wave + 2 * u;
@@ -132,38 +154,63 @@ struct TileCopy {
     for (int u = 0; u < NVI; ++u) {
       const int t = wave + 2 * u;
       const int r = t * 8 + lane / 8;
-      const int c = (lane % 8) ^ (r % 8);
+      const int c = (lane % 8) ^ vswz(r);
       voff[u] = (uint32_t)((r * (int64_t)Npad + c * 8) * 2);
     }
+    kbase = __builtin_amdgcn_readfirstlane(lds_addr(sK) + wave * 1024);
+    vbase = __builtin_amdgcn_readfirstlane(lds_addr(sV) + wave * 1024);
   }
 
   // K rows past N (ragged last block) are clamped to row N-1; their scores
   // are masked to -inf, so only in-bounds reads matter.
-  __device__ __forceinline__ void k_tile(const uint16_t* Kh, int64_t sn, int j, int N,
-                                         const uint16_t* sK, int wave, int lane) const {
+  __device__ __forceinline__ void k_tile(const uint16_t* Kh, int64_t sn, int j, int N, int wave,
+                                         int lane) const {
     const uint16_t* base = Kh + (int64_t)j * kBlock * sn;
     if (j * kBlock + kBlock <= N) {
-#pragma unroll
-      for (int u = 0; u < NK; ++u) dma16(lds_addr(sK + (wave + 2 * u) * 512), base, koff[u]);
+      static_for<0, NK>([&](auto uc) {
+        constexpr int u = decltype(uc)::value;
+        dma16<u * 2048>(kbase, base, koff[u]);
+      });
     } else {
       const int last = N - 1 - j * kBlock;
-#pragma unroll
-      for (int u = 0; u < NK; ++u) {
-        const int t = wave + 2 * u;
-        const int r = t * RPI + lane / DC;
+      static_for<0, NK>([&](auto uc) {
+        constexpr int u = decltype(uc)::value;
+        const int r = (wave + 2 * u) * RPI + lane / DC;
         const int c = (lane % DC) ^ (r % DC);
-        dma16(lds_addr(sK + t * 512), base, (uint32_t)((min(r, last) * sn + c * 8) * 2));
-      }
+        dma16<u * 2048>(kbase, base, (uint32_t)((min(r, last) * sn + c * 8) * 2));
+      });
     }
   }
 
-  __device__ __forceinline__ void v_tile(const uint16_t* Vth, int j, const uint16_t* sV,
-                                         int wave) const {
+  __device__ __forceinline__ void v_tile(const uint16_t* Vth, int j) const {
     const uint16_t* base = Vth + j * kBlock;
-#pragma unroll
-    for (int u = 0; u < NVI; ++u) dma16(lds_addr(sV + (wave + 2 * u) * 512), base, voff[u]);
+    static_for<0, NVI>([&](auto uc) {
+      constexpr int u = decltype(uc)::value;
+      dma16<u * 2048>(vbase, base, voff[u]);
+    });
   }
 };
+
+// max(a, b, c) in one instruction.  (fmaxf on matrix-core results compiles
+// to an extra quieting max per operand.)
+__device__ __forceinline__ float max3f(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+
+// max(x[l], x[l ^ 32]): lanes l and l^32 exchange through one permlane swap.
+__device__ __forceinline__ float pair_max32(float x) {
+  const uint32_t u = __float_as_uint(x);
+  const auto sw = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+}
+
+// Sum of the two fp16 halves of a packed word added to acc (fp32).
+__device__ __forceinline__ float add_f16x2(uint32_t packed, float acc) {
+  const f16x2 ones = {(_Float16)1.0f, (_Float16)1.0f};
+  return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, packed), ones, acc, false);
+}
 
 // s_waitcnt vmcnt(n) with the other counters left alone (gfx9 encoding).
 template <int n>
@@ -255,17 +302,75 @@ void attn_fwd_kernel(AttnArgs a) {
   // the tile copies in flight.
   wait_vmcnt<0>();
   TileCopy<D> cp;
-  cp.init(a.sn, a.Npad, wave, lane);
-  int j = 0;
+  cp.init(a.sn, a.Npad, wave, lane, sK, sV);
+
+  // O^T += V^T P^T for one key block whose V^T tile is in sV.
+  // The V^T fragments of d tile t+1 are read while the products of tile t run.
+  auto v_frags = [&](int t, f16x8(&va)[4]) {
+    const int row = 32 * t + n;
+#pragma unroll
+    for (int cc = 0; cc < 4; ++cc)
+      va[cc] = *(const f16x8*)(sV + row * 64 + (((2 * cc + g) ^ vswz(row)) * 8));
+  };
+  auto pv = [&](const f16x8(&pf)[4]) {
+    f16x8 va[2][4];
+    v_frags(0, va[0]);
+#pragma unroll
+    for (int t = 0; t < DT; ++t) {
+      if (t + 1 < DT) v_frags(t + 1, va[(t + 1) & 1]);
+#pragma unroll
+      for (int cc = 0; cc < 4; ++cc)
+        o[t] = __builtin_amdgcn_mfma_f32_32x32x16_f16(va[t & 1][cc], pf[cc], o[t], 0, 0, 0);
+    }
+  };
+
+  // exp2 of the scaled scores against the running max, packed to fp16 (the
+  // PV operand); the row sum adds exactly those rounded values (a dot with
+  // (1, 1) in fp32), so numerator and normaliser agree.
+  auto softmax_pack = [&](f32x16& s0, f32x16& s1, f16x8(&pf)[4]) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      s0[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s0[r], c, -m_run));
+      s1[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s1[r], c, -m_run));
+    }
+    float ps0 = 0.f, ps1 = 0.f;
+#pragma unroll
+    for (int cc = 0; cc < 4; ++cc) {
+      const f32x16& src = (cc < 2) ? s0 : s1;
+      const int r0 = 8 * (cc & 1);
+      const u32x4 pk = {pack_f16x2(src[r0 + 0], src[r0 + 1]), pack_f16x2(src[r0 + 2], src[r0 + 3]),
+                        pack_f16x2(src[r0 + 4], src[r0 + 5]), pack_f16x2(src[r0 + 6], src[r0 + 7])};
+      ps0 = add_f16x2(pk[0], add_f16x2(pk[1], ps0));
+      ps1 = add_f16x2(pk[2], add_f16x2(pk[3], ps1));
+      pf[cc] = __builtin_bit_cast(f16x8, pk);
+    }
+    l_run += ps0 + ps1;
+  };
+
+  // Software pipeline over the row's key blocks, two barriers per block.
+  // Iteration e:
+  //   A  K(e) has landed and every wave is done with sV  -> copy V(e-1)
+  //      QK^T(e) from sK
+  //   B  V(e-1) has landed and every wave is done with sK -> copy K(e+1)
+  //      softmax(e) interleaved with the PV products of block e-1 (sV)
+  // The first iteration runs its PV step on a zero P against V(e0) (a real,
+  // finite tile), which adds exact zeros and keeps the loop body free of
+  // branches between the softmax and the PV products.
+  f16x8 pf_prev[4];
+#pragma unroll
+  for (int cc = 0; cc < 4; ++cc) pf_prev[cc] = f16x8{};
+  int j = 0, jprev = 0;
   if (e0 < e1) {
     j = DENSE ? e0 : col_idx[e0];
-    cp.k_tile(Kh, a.sn, j, a.N, sK, wave, lane);
-    cp.v_tile(Vth, j, sV, wave);
+    jprev = j;
+    cp.k_tile(Kh, a.sn, j, a.N, wave, lane);
   }
   for (int e = e0; e < e1; ++e) {
     const int jn = (e + 1 < e1) ? (DENSE ? e + 1 : col_idx[e + 1]) : j;
-    wait_vmcnt<NV>();  // this wave's K tile has landed (V may still fly)
-    exec_barrier();    // ... and the other wave's
+    wait_lgkm0();      // this wave's reads of sV (block e-2) have returned
+    wait_vmcnt<0>();   // this wave's copy of K(e) has landed
+    exec_barrier();    // ... and the other wave's; sV is free
+    cp.v_tile(Vth, jprev);
 
     // S^T for keys 0..31 (s0) and 32..63 (s1) of the block.
     f32x16 s0, s1;
@@ -274,6 +379,7 @@ void attn_fwd_kernel(AttnArgs a) {
       s0[r] = 0.f;
       s1[r] = 0.f;
     }
+    __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
       const int r0 = n, r1 = 32 + n;
@@ -282,10 +388,11 @@ void attn_fwd_kernel(AttnArgs a) {
       s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k0, qf[s], s0, 0, 0, 0);
       s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k1, qf[s], s1, 0, 0, 0);
     }
+    __builtin_amdgcn_s_setprio(0);
     wait_lgkm0();      // this wave's reads of sK have returned
-    wait_vmcnt<0>();   // V tile of this block has landed
-    exec_barrier();    // both waves are done with sK; sV is complete
-    if (e + 1 < e1) cp.k_tile(Kh, a.sn, jn, a.N, sK, wave, lane);
+    wait_vmcnt<0>();   // V(e-1) has landed
+    exec_barrier();    // both waves are done with sK; sV holds V(e-1)
+    if (e + 1 < e1) cp.k_tile(Kh, a.sn, jn, a.N, wave, lane);
 
     // Lane holds keys 8*(r/4) + 4*g + r%4 (+32 for s1) of query q.
     if (j == a.nB - 1) {
@@ -299,11 +406,22 @@ void attn_fwd_kernel(AttnArgs a) {
         }
       }
     }
-    float mx = -INFINITY;
+    // Row max over the lane's 32 scores (a tree of 3-input maxima), then
+    // over the lane pair (l, l^32) that holds the other 32 keys.
+    float m11[11];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, fmaxf(s0[r], s1[r]));
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    for (int k = 0; k < 5; ++k) {
+      m11[k] = max3f(s0[3 * k], s0[3 * k + 1], s0[3 * k + 2]);
+      m11[5 + k] = max3f(s1[3 * k], s1[3 * k + 1], s1[3 * k + 2]);
+    }
+    m11[10] = max3f(s0[15], s1[15], m11[0]);
+    const float m3a = max3f(m11[1], m11[2], m11[3]);
+    const float m3b = max3f(m11[4], m11[5], m11[6]);
+    const float m3c = max3f(m11[7], m11[8], m11[9]);
+    float mx = max3f(m3a, m3b, max3f(m3c, m11[10], m3c));
+    mx = pair_max32(mx);
     const float m_new = fmaxf(m_run, mx * c);
+    f16x8 pf[4];
     // Lazy rescale: keep a stale running max while the new one exceeds it
     // by at most 8 (in log2 units); probabilities then stay below 2^8, which
     // fp32 sums and fp16 operands hold.  The result is the same softmax
@@ -315,40 +433,37 @@ void attn_fwd_kernel(AttnArgs a) {
       for (int t = 0; t < DT; ++t)
 #pragma unroll
         for (int r = 0; r < 16; ++r) o[t][r] *= alpha;
+      // block e-1 is not yet in O: bring its packed P to the new scale too
+      const _Float16 ah = (_Float16)alpha;
+#pragma unroll
+      for (int cc = 0; cc < 4; ++cc) pf_prev[cc] *= ah;
       m_run = m_new;
     }
-    float ps = 0.f;
+    softmax_pack(s0, s1, pf);  // VALU work of block e ...
+    pv(pf_prev);               // ... independent of the PV products of block e-1
+    // Interleave them: the fragment reads of the first two d tiles up front,
+    // then per d tile four products each followed by seven vector ALU
+    // instructions of the softmax, and the reads of the tile after next.
+    __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);  // DS reads
+    static_for<0, DT>([&](auto) {
+      static_for<0, 4>([&](auto) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x002, 7, 0);  // VALU
+      });
+      __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);  // DS reads
+    });
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      s0[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s0[r], c, -m_run));
-      s1[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s1[r], c, -m_run));
-      ps += s0[r] + s1[r];
-    }
-    l_run += ps;
-    f16x8 pf[4];
-#pragma unroll
-    for (int cc = 0; cc < 4; ++cc) {
-      const f32x16& src = (cc < 2) ? s0 : s1;
-      const int r0 = 8 * (cc & 1);
-      const u32x4 pk = {pack_f16x2(src[r0 + 0], src[r0 + 1]), pack_f16x2(src[r0 + 2], src[r0 + 3]),
-                        pack_f16x2(src[r0 + 4], src[r0 + 5]), pack_f16x2(src[r0 + 6], src[r0 + 7])};
-      pf[cc] = __builtin_bit_cast(f16x8, pk);
-    }
-#pragma unroll
-    for (int t = 0; t < DT; ++t) {
-      const int row = 32 * t + n;
-      f16x8 va[4];
-#pragma unroll
-      for (int cc = 0; cc < 4; ++cc)
-        va[cc] = *(const f16x8*)(sV + row * 64 + (((2 * cc + g) ^ (row & 7)) * 8));
-#pragma unroll
-      for (int cc = 0; cc < 4; ++cc)
-        o[t] = __builtin_amdgcn_mfma_f32_32x32x16_f16(va[cc], pf[cc], o[t], 0, 0, 0);
-    }
-    wait_lgkm0();      // this wave's reads of sV have returned
-    exec_barrier();    // both waves are done with sV
-    if (e + 1 < e1) cp.v_tile(Vth, jn, sV, wave);
+    for (int cc = 0; cc < 4; ++cc) pf_prev[cc] = pf[cc];
+    jprev = j;
     j = jn;
+  }
+  if (e0 < e1) {
+    wait_lgkm0();
+    exec_barrier();    // every wave is done with sV
+    cp.v_tile(Vth, jprev);
+    wait_vmcnt<0>();
+    exec_barrier();
+    pv(pf_prev);
   }
 
   const float l_tot = l_run + __shfl_xor(l_run, 32);
