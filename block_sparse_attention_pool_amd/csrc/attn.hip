@@ -141,8 +141,17 @@ struct TileCopy {
   uint32_t voff[NVI];
   uint32_t kbase, vbase;  // LDS byte address of this wave's first instruction
 
+  uint32_t kr[NK];  // the same for the last key block, rows clamped to N-1
   __device__ __forceinline__ void init(int64_t sn, int Npad, int wave, int lane,
-                                       const uint16_t* sK, const uint16_t* sV) {
+                                       const uint16_t* sK, const uint16_t* sV, int N, int nB) {
+    const int last = N - 1 - (nB - 1) * kBlock;
+#pragma unroll
+    for (int u = 0; u < NK; ++u) {
+      const int t = wave + 2 * u;
+      const int r = t * RPI + lane / DC;
+      const int c = (lane % DC) ^ (r % DC);
+      kr[u] = (uint32_t)((min(r, last) * sn + c * 8) * 2);
+    }
 #pragma unroll
     for (int u = 0; u < NK; ++u) {
       const int t = wave + 2 * u;
@@ -162,24 +171,15 @@ struct TileCopy {
   }
 
   // K rows past N (ragged last block) are clamped to row N-1; their scores
-  // are masked to -inf, so only in-bounds reads matter.
-  __device__ __forceinline__ void k_tile(const uint16_t* Kh, int64_t sn, int j, int N, int wave,
-                                         int lane) const {
+  // are masked to -inf, so only in-bounds reads matter.  The choice between
+  // the two offset sets is a select, not a branch.
+  __device__ __forceinline__ void k_tile(const uint16_t* Kh, int64_t sn, int j, int nB) const {
     const uint16_t* base = Kh + (int64_t)j * kBlock * sn;
-    if (j * kBlock + kBlock <= N) {
-      static_for<0, NK>([&](auto uc) {
-        constexpr int u = decltype(uc)::value;
-        dma16<u * 2048>(kbase, base, koff[u]);
-      });
-    } else {
-      const int last = N - 1 - j * kBlock;
-      static_for<0, NK>([&](auto uc) {
-        constexpr int u = decltype(uc)::value;
-        const int r = (wave + 2 * u) * RPI + lane / DC;
-        const int c = (lane % DC) ^ (r % DC);
-        dma16<u * 2048>(kbase, base, (uint32_t)((min(r, last) * sn + c * 8) * 2));
-      });
-    }
+    const bool rag = j == nB - 1;
+    static_for<0, NK>([&](auto uc) {
+      constexpr int u = decltype(uc)::value;
+      dma16<u * 2048>(kbase, base, rag ? kr[u] : koff[u]);
+    });
   }
 
   __device__ __forceinline__ void v_tile(const uint16_t* Vth, int j) const {
@@ -302,7 +302,7 @@ void attn_fwd_kernel(AttnArgs a) {
   // the tile copies in flight.
   wait_vmcnt<0>();
   TileCopy<D> cp;
-  cp.init(a.sn, a.Npad, wave, lane, sK, sV);
+  cp.init(a.sn, a.Npad, wave, lane, sK, sV, a.N, a.nB);
 
   // O^T += V^T P^T for one key block whose V^T tile is in sV.
   // The V^T fragments of d tile t+1 are read while the products of tile t run.
@@ -363,7 +363,7 @@ void attn_fwd_kernel(AttnArgs a) {
   if (e0 < e1) {
     j = DENSE ? e0 : col_idx[e0];
     jprev = j;
-    cp.k_tile(Kh, a.sn, j, a.N, wave, lane);
+    cp.k_tile(Kh, a.sn, j, a.nB);
   }
   for (int e = e0; e < e1; ++e) {
     const int jn = (e + 1 < e1) ? (DENSE ? e + 1 : col_idx[e + 1]) : j;
@@ -388,11 +388,18 @@ void attn_fwd_kernel(AttnArgs a) {
       s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k0, qf[s], s0, 0, 0, 0);
       s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k1, qf[s], s1, 0, 0, 0);
     }
+    // K fragments are read three k-steps ahead of their products.
+    __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
+    static_for<0, KS - 3>([&](auto) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    });
+    __builtin_amdgcn_sched_group_barrier(0x008, 6, 0);
     __builtin_amdgcn_s_setprio(0);
     wait_lgkm0();      // this wave's reads of sK have returned
     wait_vmcnt<0>();   // V(e-1) has landed
     exec_barrier();    // both waves are done with sK; sV holds V(e-1)
-    if (e + 1 < e1) cp.k_tile(Kh, a.sn, jn, a.N, wave, lane);
+    if (e + 1 < e1) cp.k_tile(Kh, a.sn, jn, a.nB);
 
     // Lane holds keys 8*(r/4) + 4*g + r%4 (+32 for s1) of query q.
     if (j == a.nB - 1) {
