@@ -1,6 +1,7 @@
 // Block selection -> CSR lists.
 //
-// Macro rows (one workgroup per (b, h, query block i)):
+// Macro rows (one workgroup per (b, h, query block i); top-k and static
+// rows of up to 1024 key blocks: one wave per row, see select_topk_kernel):
 //   top-k:  the k key blocks of highest pooled score, ties to the lower
 //           index (block-sparse density budget);
 //   top-p:  HyperVAttention section 2, Eq. 2 (size-weighted centroid
@@ -205,6 +206,91 @@ __global__ __launch_bounds__(256) void select_kernel(SelectArgs a) {
   }
   cnt = block_sum(cnt, ired);
   if (tid == 0) a.counts[r] = cnt;
+}
+
+// Top-k and static rows, one wave per row.  The row's scores are held as
+// order-preserving 32-bit keys, E per lane (element e of lane l is block
+// 64e + l).  The k-th largest key T is found by a bitwise descent: the
+// largest T with at least k keys >= T, counted with one ballot per element.
+// Keys above T are taken, and of the keys equal to T the lowest block
+// indices, so ties go to the lower index as in the sorting kernel above.
+// The forced blocks (diagonal, window, anchors) are a union on top.  The
+// ballot of element e is words 2e and 2e+1 of the row's bitmask.
+template <int E>
+__global__ __launch_bounds__(256) void select_topk_kernel(SelectArgs a, int rows) {
+  const int r = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (r >= rows) return;
+  const int lane = threadIdx.x & 63;
+  const int i = r % a.nB;
+  const bool scored = a.mode == kTopK;
+  const int k = scored ? min(a.k, a.nB) : 0;
+  const bool all = k >= a.nB;
+
+  uint32_t key[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const int j = 64 * e + lane;
+    key[e] = (scored && j < a.nB) ? float_order_key(a.scores[(int64_t)r * a.nB + j]) : 0u;
+  }
+  // Keys of padding lanes are 0 and every candidate is >= 1, so they are
+  // never counted.
+  uint32_t T = 0;
+  int take = 0;  // keys equal to T still to take, lowest index first
+  if (k > 0 && !all) {
+    for (int b = 31; b >= 0; --b) {
+      const uint32_t cand = T | (1u << b);
+      int c = 0;
+#pragma unroll
+      for (int e = 0; e < E; ++e) c += __popcll(__ballot(key[e] >= cand));
+      if (c >= k) T = cand;
+    }
+    int gt = 0;
+#pragma unroll
+    for (int e = 0; e < E; ++e) gt += __popcll(__ballot(key[e] > T));
+    take = k - gt;
+  }
+
+  int lo_i = 0, hi_i = 0;
+  int64_t stride = 0, off = 0;
+  if (a.use_static) {
+    lo_i = (i * kBlock) / a.frame_tokens;
+    hi_i = (min(i * kBlock + kBlock, a.N) - 1) / a.frame_tokens;
+    if (a.n_anchors > 0) {
+      stride = a.nB / a.n_anchors;
+      off = ((int64_t)a.anchor_offset % a.nB + a.nB) % a.nB;
+    }
+  }
+  const uint64_t below = (1ull << lane) - 1ull;  // lanes under this one
+  uint32_t word = 0u;
+  int cnt = 0, ties_before = 0;
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const int j = 64 * e + lane;
+    const bool valid = j < a.nB;
+    bool sel = valid && (all || (k > 0 && key[e] > T));
+    if (take > 0) {
+      const bool tie = valid && key[e] == T;
+      const uint64_t tb = __ballot(tie);
+      if (tie && ties_before + __popcll(tb & below) < take) sel = true;
+      ties_before += __popcll(tb);
+    }
+    if (valid && a.force_diag && j == i) sel = true;
+    if (valid && a.use_static) {
+      const int lo_j = (j * kBlock) / a.frame_tokens;
+      const int hi_j = (min(j * kBlock + kBlock, a.N) - 1) / a.frame_tokens;
+      if (lo_j <= hi_i + a.window_frames && hi_j >= lo_i - a.window_frames) sel = true;
+      if (a.n_anchors > 0) {
+        const int64_t dj = ((int64_t)j - off + a.nB) % a.nB;
+        if (stride > 0 ? (dj % stride == 0 && dj / stride < a.n_anchors) : dj == 0) sel = true;
+      }
+    }
+    const uint64_t m = __ballot(sel);
+    cnt += __popcll(m);
+    if (lane == 2 * e) word = (uint32_t)m;
+    if (lane == 2 * e + 1) word = (uint32_t)(m >> 32);
+  }
+  if (lane < a.W) a.bits[(int64_t)r * a.W + lane] = word;
+  if (lane == 0) a.counts[r] = cnt;
 }
 
 // -------------------------------------------------------- row pointers
@@ -440,7 +526,14 @@ hipError_t launch_fill_i32(int32_t* p, int64_t n, int32_t v, hipStream_t s) {
 }
 
 hipError_t launch_select(const SelectArgs& a, int rows, hipStream_t s) {
-  hipLaunchKernelGGL(select_kernel, dim3(rows), dim3(256), 0, s, a);
+  const dim3 grid((rows + 3) / 4);
+  if (a.mode != kTopP && a.nB <= 512) {
+    hipLaunchKernelGGL(select_topk_kernel<8>, grid, dim3(256), 0, s, a, rows);
+  } else if (a.mode != kTopP && a.nB <= 1024) {
+    hipLaunchKernelGGL(select_topk_kernel<16>, grid, dim3(256), 0, s, a, rows);
+  } else {
+    hipLaunchKernelGGL(select_kernel, dim3(rows), dim3(256), 0, s, a);
+  }
   return hipGetLastError();
 }
 

@@ -163,6 +163,30 @@ def test_static_select(grid, r, na, off):
         assert got[bh] == rows
 
 
+# Rows of 300 and 700 key blocks: the one-wave-per-row selection with a
+# partial last bitmask word (300 = 9 words + 12 bits) and with 16 keys per
+# lane (700 > 512); 2000 blocks take the sorting kernel.
+@pytest.mark.parametrize("grid,k,diag", [((3, 10, 640), 75, False), ((3, 10, 640), 400, True),
+                                         ((7, 40, 160), 175, True), ((5, 50, 512), 500, True)])
+def test_topk_select_long_rows(grid, k, diag):
+    spec = VideoSpec(1, 1, 64, grid, 108)
+    say("topk long rows", grid, k, diag)
+    _, _, _, got, ora = _select_case(spec, "topk", k=k, force_diag=diag)
+    F = forced_rows(spec.N, diag, None)
+    for bh, (S, rows) in ora.items():
+        PT.compare_topk_rows(got[bh], rows, S, k, F)
+
+
+@pytest.mark.parametrize("grid,r,na,off", [((7, 40, 160), 1, 5, 3), ((5, 50, 512), 0, 7, -4)])
+def test_static_select_long_rows(grid, r, na, off):
+    spec = VideoSpec(1, 1, 64, grid, 109)
+    say("static long rows", grid, r, na, off)
+    st = dict(frame_tokens=spec.frame_tokens, window_frames=r, n_anchors=na, anchor_offset=off)
+    _, _, _, got, ora = _select_case(spec, "static", static=st)
+    for bh, (_, rows) in ora.items():
+        assert got[bh] == rows
+
+
 def test_topk_plus_static_union():
     spec = VideoSpec(1, 2, 128, (8, 6, 11), 107)
     say("topk + static")
