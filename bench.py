@@ -1,19 +1,24 @@
 #!/usr/bin/env python
 """Benchmark of the block-sparse video-DiT attention hot path on one MI355X.
 
-One step = pooled scoring (bsa_score_blocks) + top-k block selection
+One step = pooled scoring (bsa_score_blocks) + block selection
 (bsa_select_blocks) + block-sparse attention (bsa_sparse_attn_fwd, including
-its fp16 V^T staging) over one layer shaped like Wan-2.1-1.3B at 480p:
-B=1, H=12, d=128, 21x30x52 = 32760 tokens, 64-token blocks, top-k at 25%
-density (k = 128 of 512 key blocks).  Inputs are the seeded synthetic
-generator's bf16 Q/K/V, resident in HBM before timing starts.
+its fp16 V^T staging), plus micro-tile selection, residual and LSE merge where
+the workload has them.  The default workload is one layer shaped like
+Wan-2.1-1.3B at 480p: B=1, H=12, d=128, 21x30x52 = 32760 tokens, 64-token
+blocks, top-k at 25% density (k = 128 of 512 key blocks).  ``--config N``
+selects another of the five workloads (0 tiny reference, 1 the default,
+2 Wan-2.1-14B 720p top-p, 3 HunyuanVideo 720p top-k + micro residual,
+4 long-horizon static window).  Inputs are the seeded synthetic generator's
+bf16 Q/K/V, resident in HBM before timing starts.
 
 Prints ONE JSON line.  `value` is the executed attention TFLOP of a step
-divided by the whole step time.  Kernel-level figures (the attention kernel
-alone, measured with HIP events on the stream it runs on), the speedup over
-the library's dense flash attention, per-stage times, the roofline entry of
-the dominant kernel and the fp64 CPU oracle timed on a bounded sample of the
-same workload are reported beside it.
+(64x64 block pairs plus 16x16 micro tiles) divided by the whole step time.
+Kernel-level figures (the attention kernel alone, measured with HIP events on
+the stream it runs on), the speedup over the library's dense flash attention,
+per-stage times and bandwidths, the roofline entry of the dominant kernel and
+(default workload) the fp64 CPU oracle timed on a bounded sample of the same
+workload are reported beside it.
 """
 
 from __future__ import annotations
@@ -43,6 +48,11 @@ def parse():
                     help="time budget of the CPU oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--stage-reps", type=int, default=10)
+    ap.add_argument("--config", type=int, default=1, choices=range(5),
+                    help="workload: 0 tiny, 1 wan2.1-1.3b-480p (default), 2 wan2.1-14b-720p, "
+                         "3 hunyuanvideo-720p, 4 long-horizon static window")
+    ap.add_argument("--window-frames", type=int, default=None,
+                    help="static window radius in frames (workload 4; default: the literal 1)")
     ap.add_argument("--calibration-copy", action="store_true",
                     help="first run a plain 256 MiB device copy (reads 256 MiB, writes "
                          "256 MiB) three times, to scale hardware byte counters")
@@ -129,7 +139,7 @@ def main():
 
     import torch
     import block_sparse_attention_pool_amd as bsa
-    from synth import CONFIGS, config_spec, gen_qkv
+    from synth import CONFIGS, config_spec, gen_qkv, micro_heads, rotation_offset
 
     if args.calibration_copy:
         src = torch.ones(64 << 20, dtype=torch.float32, device="cuda:0")
@@ -139,7 +149,7 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
-    cfg = 1
+    cfg = args.config
     c = CONFIGS[cfg]
     spec = config_spec(cfg)
     Qc, Kc, Vc = gen_qkv(spec)
@@ -147,51 +157,121 @@ def main():
     Q, K, V = (x.to(dev) for x in (Qc, Kc, Vc))
     B, H, N, d = Q.shape
     nB = bsa.n_blocks(N)
-    k = bsa.budget_blocks(c["density"], nB)
     scale = 1.0 / math.sqrt(d)
     stream = torch.cuda.current_stream(dev)
+    mode = c["mode"]
+
+    # selection parameters of the workload
+    sel = {}
+    if mode == "topk":
+        k = bsa.budget_blocks(c["density"], nB)
+        sel = dict(k=k, force_diag=c.get("force_diag", False))
+        sel_desc = f"top-k {c['density']:.0%} (k={k} of {nB})" + (" + diagonal" if sel["force_diag"] else "")
+    elif mode == "topp":
+        cap = bsa.cap_blocks(c["cap_density"], nB)
+        sel = dict(p=c["p"], k_min=1, k_cap=cap)
+        sel_desc = f"top-p {c['p']} size-weighted, cap {c['cap_density']:.0%} ({cap} of {nB})"
+    else:
+        wf = c["window_frames"] if args.window_frames is None else args.window_frames
+        sel = dict(static=dict(frame_tokens=spec.frame_tokens, window_frames=wf,
+                               n_anchors=c["n_anchors"], anchor_offset=rotation_offset(cfg, 0, nB)))
+        sel_desc = f"static window +-{wf} frames + {c['n_anchors']} anchors"
+    micro = None
+    if "micro_head_frac" in c or "micro_m" in c:
+        heads = micro_heads(cfg)
+        m = c["micro_m"] if "micro_m" in c else int(round(c["micro_density"] * 64 * N / 256))
+        micro = dict(m=m, mask=[h in heads for h in range(H)], heads=heads)
+        sel_desc += f"; micro m={m} on {len(heads)} of {H} heads"
 
     ws = bsa.attn_workspace(Q)
     O_buf = torch.empty(Q.shape, dtype=torch.float32, device=dev)
     L_buf = torch.empty(Q.shape[:3], dtype=torch.float32, device=dev)
+    if micro is not None:
+        Om_buf = torch.empty_like(O_buf)
+        Lm_buf = torch.empty_like(L_buf)
+
+    def score():
+        return bsa.bsa_score_blocks(Q, K, scores=(mode != "static"), micro=16 if micro else 0)
+
+    def select(sc):
+        return bsa.bsa_select_blocks(sc["scores"], Q, mode=mode, **sel)
+
+    def micro_select(sc, rp, ci):
+        return bsa.bsa_select_blocks(
+            None, Q, mode="micro",
+            micro=dict(m=micro["m"], scale=scale, head_mask=micro["mask"], macro=(rp, ci),
+                       qpool16=sc["qpool16"], kpool16=sc["kpool16"]))
 
     def step():
-        sc = bsa.bsa_score_blocks(Q, K)
-        rp, ci, nnz = bsa.bsa_select_blocks(sc["scores"], Q, mode="topk", k=k)
+        # the static window needs no scores: the selection runs on the mask alone
+        sc = score() if mode != "static" else {"scores": None}
+        rp, ci, nnz = select(sc)
         bsa.bsa_sparse_attn_fwd(Q, K, V, rp, ci, out=O_buf, lse=L_buf, workspace=ws)
-        return rp, ci, nnz
+        mnnz = None
+        if micro is not None:
+            mrp, mci, mnnz = micro_select(sc, rp, ci)
+            bsa.bsa_micro_residual_fwd(Q, K, None, mrp, mci, head_mask=micro["mask"],
+                                       out=Om_buf, lse=Lm_buf, workspace=ws)
+            bsa.bsa_lse_merge(O_buf, L_buf, Om_buf, Lm_buf, head_mask=micro["mask"],
+                              out=O_buf, lse_out=L_buf)
+        return sc, rp, ci, nnz, mnnz
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(args.steps):
-        rp, ci, nnz = step()
+        sc, rp, ci, nnz, mnnz = step()
     torch.cuda.synchronize()
     step_s = (time.perf_counter() - t0) / args.steps
     nnz_v = int(nnz.item())
-    exec_flops = 4 * d * 64 * 64 * nnz_v
+    mnnz_v = int(mnnz.item()) if mnnz is not None else 0
+    macro_flops = 4 * d * 64 * 64 * nnz_v
+    exec_flops = macro_flops + 4 * d * 16 * 16 * mnnz_v
     dense_flops = 4 * B * H * N * N * d
 
     # Kernel-level: the attention kernel alone (V^T already staged: V=None).
-    attn_ms, attn_all = events_ms(
+    reps = args.stage_reps
+    attn_ms, _ = events_ms(
         lambda: bsa.bsa_sparse_attn_fwd(Q, K, None, rp, ci, out=O_buf, lse=L_buf, workspace=ws),
-        args.stage_reps, stream)
+        reps, stream)
     dense_ms, _ = events_ms(
         lambda: bsa.bsa_dense_attn_fwd(Q, K, None, out=O_buf, lse=L_buf, workspace=ws),
-        max(3, args.stage_reps // 2), stream)
-    score_ms, _ = events_ms(lambda: bsa.bsa_score_blocks(Q, K), args.stage_reps, stream)
-    sc = bsa.bsa_score_blocks(Q, K)
-    select_ms, _ = events_ms(lambda: bsa.bsa_select_blocks(sc["scores"], Q, mode="topk", k=k),
-                             args.stage_reps, stream)
-    vt_ms_total, _ = events_ms(
+        max(3, reps // 2) if dense_flops < 2e13 else 3, stream)
+    score_ms, _ = events_ms(score, reps, stream) if mode != "static" else (0.0, None)
+    select_ms, _ = events_ms(lambda: select(sc), reps, stream)
+    attn_v_ms, _ = events_ms(
         lambda: bsa.bsa_sparse_attn_fwd(Q, K, V, rp, ci, out=O_buf, lse=L_buf, workspace=ws),
-        args.stage_reps, stream)
+        reps, stream)
+    stages = {"score_blocks": round(score_ms, 4), "select_blocks": round(select_ms, 4),
+              "sparse_attn_fwd_with_v_staging": round(attn_v_ms, 4),
+              "attn_kernel": round(attn_ms, 4)}
+    gbs = {}
+    if mode != "static":
+        # pooling reads Q and K and writes the means; the score kernel writes nB^2 scores
+        gbs["score_blocks"] = round((4 * B * H * N * d + 8 * B * H * nB * d
+                                     + 4 * B * H * nB * nB) / (score_ms * 1e-3) / 1e9, 1)
+        gbs["select_blocks"] = round((4 * B * H * nB * nB + 4 * nnz_v)
+                                     / (select_ms * 1e-3) / 1e9, 1)
+    if micro is not None:
+        mrp, mci, _ = micro_select(sc, rp, ci)
+        msel_ms, _ = events_ms(lambda: micro_select(sc, rp, ci), reps, stream)
+        mattn_ms, _ = events_ms(
+            lambda: bsa.bsa_micro_residual_fwd(Q, K, None, mrp, mci, head_mask=micro["mask"],
+                                               out=Om_buf, lse=Lm_buf, workspace=ws),
+            reps, stream)
+        merge_ms, _ = events_ms(
+            lambda: bsa.bsa_lse_merge(O_buf, L_buf, Om_buf, Lm_buf, head_mask=micro["mask"],
+                                      out=O_buf, lse_out=L_buf), reps, stream)
+        stages.update({"micro_select": round(msel_ms, 4), "micro_residual_fwd": round(mattn_ms, 4),
+                       "lse_merge": round(merge_ms, 4)})
+        rows_m = B * len(micro["heads"]) * N
+        gbs["lse_merge"] = round(rows_m * (3 * d * 4 + 12) / (merge_ms * 1e-3) / 1e9, 1)
+        stages["micro_tflops"] = round(4 * d * 256 * mnnz_v / (mattn_ms * 1e-3) / 1e12, 2)
 
-    attn_tflops = exec_flops / (attn_ms * 1e-3) / 1e12
+    attn_tflops = macro_flops / (attn_ms * 1e-3) / 1e12
     kernel_src = os.path.join(ROOT, "block_sparse_attention_pool_amd", "csrc", "attn.hip")
-    traffic = traffic_entry(kernel_src)
-    pool_bytes = 4 * B * H * N * d + 8 * B * H * nB * d
+    traffic = traffic_entry(kernel_src) if cfg == 1 else None
     out = {
         "metric": METRIC,
         "value": round(exec_flops / step_s / 1e12, 2),
@@ -206,7 +286,7 @@ def main():
         "dtype": "bf16",
         "data": "synthetic (seeded structured video Q/K/V)",
         "config": {"workload": c["name"], "B": B, "H": H, "N": N, "d": d, "block": 64,
-                   "selection": f"top-k {c['density']:.0%} (k={k} of {nB})",
+                   "selection": sel_desc,
                    "density": round(nnz_v / (B * H * nB * nB), 4)},
         "attn_kernel_ms": round(attn_ms, 4),
         "attn_kernel_tflops": round(attn_tflops, 2),
@@ -216,16 +296,14 @@ def main():
         "dense_kernel_tflops": round(dense_flops / (dense_ms * 1e-3) / 1e12, 2),
         "speedup_vs_dense": round(dense_ms / attn_ms, 3),
         "pipeline_speedup_vs_dense": round(dense_ms / (step_s * 1e3), 3),
-        "stages_ms": {"score_blocks": round(score_ms, 4), "select_blocks": round(select_ms, 4),
-                      "sparse_attn_fwd_with_v_staging": round(vt_ms_total, 4),
-                      "attn_kernel": round(attn_ms, 4)},
-        "score_blocks_gbs": round(pool_bytes / (score_ms * 1e-3) / 1e9, 1),
+        "stages_ms": stages,
+        "stage_gbs": gbs,
         "roofline": {"bound": "mfma", "achieved": round(attn_tflops, 2), "peak": PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(attn_tflops / PEAK_TFLOPS, 4),
                      "traffic": traffic},
     }
-    if not args.no_cpu_baseline:
-        rows = {"k": k}
+    if not args.no_cpu_baseline and cfg == 1:
+        rows = {"k": sel["k"]}
         out["cpu_baseline"] = cpu_oracle_sample(Qc, Kc, Vc, rows, args.cpu_seconds)
     print(json.dumps(out), flush=True)
 

@@ -80,12 +80,6 @@ bsa::HeadList heads_from_mask(const uint8_t* mask, int H) {
   return l;
 }
 
-int next_pow2(int x) {
-  int p = 2;
-  while (p < x) p <<= 1;
-  return p;
-}
-
 struct SelectPlan {
   int64_t rows, nB, W, nT;
   int64_t bytes_a, bytes_b, bytes_c, total;
@@ -366,7 +360,6 @@ bsa_status bsa_select_blocks(const float* scores, const bsa_shape* shape, int32_
   a.N = shape->N;
   a.nB = (int)pl.nB;
   a.W = (int)pl.W;
-  a.P2 = next_pow2((int)pl.nB);
   a.mode = p->mode;
   a.k = p->k;
   a.k_min = p->k_min;

@@ -39,7 +39,7 @@ struct SelectArgs {
   const float* scores;  // [rows, nB] or null
   uint32_t* bits;       // [rows, W]
   int32_t* counts;      // [rows]
-  int N, nB, W, P2;
+  int N, nB, W;
   int mode, k, k_min, k_cap;
   float p;
   int force_diag, use_static;

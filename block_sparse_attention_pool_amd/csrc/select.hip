@@ -1,15 +1,15 @@
 // Block selection -> CSR lists.
 //
-// Macro rows (one workgroup per (b, h, query block i); top-k and static
-// rows of up to 1024 key blocks: one wave per row, see select_topk_kernel):
+// Macro rows (one wave per (b, h, query block i), select_wave_kernel):
 //   top-k:  the k key blocks of highest pooled score, ties to the lower
 //           index (block-sparse density budget);
 //   top-p:  HyperVAttention section 2, Eq. 2 (size-weighted centroid
 //           softmax) and Eq. 3 (smallest descending prefix with cumulative
 //           probability at least p), clamped to [k_min, k_cap];
 //   forced: diagonal and/or the LVSA temporal window + rotating anchors.
-// The row is built as a bitmask in LDS, counted, prefix-summed across rows
-// into row_ptr, and emitted as ascending column indices.
+// The row is built as a bitmask (one ballot per 64 key blocks), counted,
+// prefix-summed across rows into row_ptr, and emitted as ascending column
+// indices.
 //
 // Micro rows (HyMoR-Attn Micro selection, 16-token tiles inside omitted
 // blocks): one workgroup per (b, micro head, query block); radix selection
@@ -40,32 +40,6 @@ __device__ T block_sum(T v, T* red) {
   return t;
 }
 
-template <typename T>
-__device__ T block_max(T v, T* red) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int nw = blockDim.x >> 6;
-  v = wave_max(v);
-  __syncthreads();
-  if (lane == 0) red[wave] = v;
-  __syncthreads();
-  T t = red[0];
-  for (int w = 1; w < nw; ++w) t = max(t, red[w]);
-  return t;
-}
-
-__device__ int block_min_int(int v, int* red) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int nw = blockDim.x >> 6;
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) v = min(v, __shfl_xor(v, off));
-  __syncthreads();
-  if (lane == 0) red[wave] = v;
-  __syncthreads();
-  int t = red[0];
-  for (int w = 1; w < nw; ++w) t = min(t, red[w]);
-  return t;
-}
-
 // Exclusive prefix over the threads of the block (in thread order); also
 // returns the block total.
 template <typename T>
@@ -85,155 +59,104 @@ __device__ T block_exclusive_scan(T v, T* red, T* total) {
   return off + inc - v;
 }
 
-__device__ __forceinline__ float key_to_positive_float(uint64_t key) {
-  const uint32_t k32 = (uint32_t)(key >> 32);
-  return __uint_as_float(k32 & 0x7FFFFFFFu);  // keys of positive floats
-}
-
 // ----------------------------------------------------------- macro select
 
-__global__ __launch_bounds__(256) void select_kernel(SelectArgs a) {
-  __shared__ uint64_t keys[4096];
-  __shared__ uint32_t mask[128];
-  __shared__ double dred[8];
-  __shared__ float fred[8];
-  __shared__ int ired[8];
-
-  const int r = blockIdx.x;
-  const int i = r % a.nB;
-  const int tid = threadIdx.x;
-  for (int w = tid; w < a.W; w += 256) mask[w] = 0u;
-  __syncthreads();
-
-  if (a.mode == kTopK || a.mode == kTopP) {
-    const float* row = a.scores + (int64_t)r * a.nB;
-    float mx = -INFINITY;
-    if (a.mode == kTopP) {
-      for (int j = tid; j < a.nB; j += 256) mx = fmaxf(mx, row[j]);
-      mx = block_max(mx, fred);
-    }
-    const float tail_size = (float)(a.N - (a.nB - 1) * kBlock);
-    for (int j = tid; j < a.P2; j += 256) {
-      uint64_t key = 0;
-      if (j < a.nB) {
-        float v = row[j];
-        if (a.mode == kTopP) v = (j == a.nB - 1 ? tail_size : (float)kBlock) * expf(v - mx);
-        key = ((uint64_t)float_order_key(v) << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)j);
-      }
-      keys[j] = key;
-    }
-    __syncthreads();
-    // Bitonic sort, descending: (value desc, index asc) since the low word
-    // holds the complemented index.
-    for (int k = 2; k <= a.P2; k <<= 1) {
-      for (int jj = k >> 1; jj > 0; jj >>= 1) {
-        for (int t = tid; t < (a.P2 >> 1); t += 256) {
-          const int lo = 2 * jj * (t / jj) + (t % jj);
-          const int hi = lo + jj;
-          const uint64_t x = keys[lo], y = keys[hi];
-          const bool desc = (lo & k) == 0;
-          if (desc ? (x < y) : (x > y)) {
-            keys[lo] = y;
-            keys[hi] = x;
-          }
-        }
-        __syncthreads();
-      }
-    }
-    int L;
-    if (a.mode == kTopK) {
-      L = min(a.k, a.nB);
-    } else {
-      // Cumulative mass in descending order, in double.
-      const int E = max(1, a.P2 / 256);
-      const int start = tid * E;
-      double local = 0.0;
-      for (int e = 0; e < E; ++e) {
-        const int pos = start + e;
-        if (pos < a.nB) local += (double)key_to_positive_float(keys[pos]);
-      }
-      double total;
-      const double excl = block_exclusive_scan(local, dred, &total);
-      const double thr = (double)a.p * total;
-      int first = INT_MAX;
-      double run = excl;
-      for (int e = 0; e < E; ++e) {
-        const int pos = start + e;
-        if (pos >= a.nB) break;
-        run += (double)key_to_positive_float(keys[pos]);
-        if (run >= thr) {
-          first = pos;
-          break;
-        }
-      }
-      first = block_min_int(first, ired);
-      L = (first == INT_MAX) ? a.nB : first + 1;
-      L = max(L, a.k_min);
-      L = min(L, a.k_cap);
-      L = min(L, a.nB);
-    }
-    for (int pos = tid; pos < L; pos += 256) {
-      const uint32_t j = 0xFFFFFFFFu - (uint32_t)(keys[pos] & 0xFFFFFFFFull);
-      atomicOr(&mask[j >> 5], 1u << (j & 31));
-    }
-  }
-  if (a.force_diag && tid == 0) atomicOr(&mask[i >> 5], 1u << (i & 31));
-  if (a.use_static) {
-    const int ft = a.frame_tokens;
-    const int lo_i = (i * kBlock) / ft;
-    const int hi_i = (min(i * kBlock + kBlock, a.N) - 1) / ft;
-    for (int j = tid; j < a.nB; j += 256) {
-      const int lo_j = (j * kBlock) / ft;
-      const int hi_j = (min(j * kBlock + kBlock, a.N) - 1) / ft;
-      if (lo_j <= hi_i + a.window_frames && hi_j >= lo_i - a.window_frames)
-        atomicOr(&mask[j >> 5], 1u << (j & 31));
-    }
-    if (a.n_anchors > 0) {
-      const int64_t stride = a.nB / a.n_anchors;
-      const int64_t off = ((int64_t)a.anchor_offset % a.nB + a.nB) % a.nB;
-      for (int t = tid; t < a.n_anchors; t += 256) {
-        const int j = (int)((off + t * stride) % a.nB);
-        atomicOr(&mask[j >> 5], 1u << (j & 31));
-      }
-    }
-  }
-  __syncthreads();
-  int cnt = 0;
-  for (int w = tid; w < a.W; w += 256) {
-    const uint32_t v = mask[w];
-    a.bits[(int64_t)r * a.W + w] = v;
-    cnt += __popc(v);
-  }
-  cnt = block_sum(cnt, ired);
-  if (tid == 0) a.counts[r] = cnt;
-}
-
-// Top-k and static rows, one wave per row.  The row's scores are held as
+// Top-k, top-p and static rows, one wave per row.  The row is held as
 // order-preserving 32-bit keys, E per lane (element e of lane l is block
-// 64e + l).  The k-th largest key T is found by a bitwise descent: the
-// largest T with at least k keys >= T, counted with one ballot per element.
-// Keys above T are taken, and of the keys equal to T the lowest block
-// indices, so ties go to the lower index as in the sorting kernel above.
+// 64e + l): keys of the pooled scores for top-k, of the size-weighted
+// exponentials n_j exp(S_j - max S) for top-p.
+//   top-p: the cut of the descending prefix is found without sorting.  The
+//     block where the cumulative mass first reaches p * total has the
+//     largest key T with mass(key >= T) >= p * total (a bitwise descent over
+//     the key, masses summed in double); the prefix length is the number of
+//     keys above T plus as many of the equal keys as that sum needs, then
+//     clamped to [k_min, k_cap].
+//   top-k (and top-p's prefix of that length): the k-th largest key T is
+//     the largest T with at least k keys >= T, counted with one ballot per
+//     element; keys above T are taken, and of the keys equal to T the lowest
+//     block indices, so ties go to the lower index.
 // The forced blocks (diagonal, window, anchors) are a union on top.  The
 // ballot of element e is words 2e and 2e+1 of the row's bitmask.
+__device__ __forceinline__ double wave_sum_f64(double v) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off);
+  return v;
+}
+
 template <int E>
-__global__ __launch_bounds__(256) void select_topk_kernel(SelectArgs a, int rows) {
+__global__ __launch_bounds__(256) void select_wave_kernel(SelectArgs a, int rows) {
   const int r = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (r >= rows) return;
   const int lane = threadIdx.x & 63;
   const int i = r % a.nB;
-  const bool scored = a.mode == kTopK;
-  const int k = scored ? min(a.k, a.nB) : 0;
-  const bool all = k >= a.nB;
+  const bool scored = a.mode != kStatic;
 
   uint32_t key[E];
+  float val[E];  // top-p: the size-weighted exponentials
+  if (scored) {
+    const float* row = a.scores + (int64_t)r * a.nB;
+    float x[E];
+    float mx = -INFINITY;
 #pragma unroll
-  for (int e = 0; e < E; ++e) {
-    const int j = 64 * e + lane;
-    key[e] = (scored && j < a.nB) ? float_order_key(a.scores[(int64_t)r * a.nB + j]) : 0u;
+    for (int e = 0; e < E; ++e) {
+      const int j = 64 * e + lane;
+      x[e] = j < a.nB ? row[j] : -INFINITY;
+      mx = fmaxf(mx, x[e]);
+    }
+    if (a.mode == kTopP) mx = wave_max(mx);
+    const float tail_size = (float)(a.N - (a.nB - 1) * kBlock);
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      const int j = 64 * e + lane;
+      float v = x[e];
+      if (a.mode == kTopP) v = (j == a.nB - 1 ? tail_size : (float)kBlock) * expf(v - mx);
+      val[e] = j < a.nB ? v : 0.f;
+      key[e] = j < a.nB ? float_order_key(v) : 0u;
+    }
   }
-  // Keys of padding lanes are 0 and every candidate is >= 1, so they are
-  // never counted.
+  // Keys of padding lanes are 0 and every candidate below is >= 1, so they
+  // are never counted.
+  int k = 0;
+  if (a.mode == kTopK) {
+    k = min(a.k, a.nB);
+  } else if (a.mode == kTopP) {
+    double tot = 0.0;
+#pragma unroll
+    for (int e = 0; e < E; ++e) tot += (double)val[e];
+    tot = wave_sum_f64(tot);
+    const double thr = (double)a.p * tot;
+    uint32_t T = 0;
+    for (int b = 31; b >= 0; --b) {
+      const uint32_t cand = T | (1u << b);
+      double m = 0.0;
+#pragma unroll
+      for (int e = 0; e < E; ++e) m += key[e] >= cand ? (double)val[e] : 0.0;
+      if (wave_sum_f64(m) >= thr) T = cand;
+    }
+    double above = 0.0;
+    float vT = 0.f;
+    int n_above = 0, n_eq = 0;
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      above += key[e] > T ? (double)val[e] : 0.0;
+      if (key[e] == T && 64 * e + lane < a.nB) vT = val[e];
+      n_above += __popcll(__ballot(key[e] > T));
+      n_eq += __popcll(__ballot(key[e] == T && 64 * e + lane < a.nB));
+    }
+    above = wave_sum_f64(above);
+    vT = wave_max(vT);
+    // equal keys are equal values: take the fewest that reach the threshold
+    int t = n_eq;
+    if (vT > 0.f) t = (int)ceil((thr - above) / (double)vT);
+    t = max(1, min(t, n_eq));
+    // (no key equal to T: p*total <= 0 gives T = ~0u and a prefix of one
+    // block, p > 1 gives T = 0 and the whole row)
+    int L = n_eq > 0 ? n_above + t : max(1, n_above);
+    L = max(L, a.k_min);
+    L = min(L, a.k_cap);
+    k = min(L, a.nB);
+  }
+  const bool all = k >= a.nB;
   uint32_t T = 0;
   int take = 0;  // keys equal to T still to take, lowest index first
   if (k > 0 && !all) {
@@ -250,46 +173,69 @@ __global__ __launch_bounds__(256) void select_topk_kernel(SelectArgs a, int rows
     take = k - gt;
   }
 
-  int lo_i = 0, hi_i = 0;
+  const uint64_t below = (1ull << lane) - 1ull;  // lanes under this one
+  uint32_t word[2] = {0u, 0u};  // lane l holds words l and l + 64 (up to 4096 blocks)
+  int ties_before = 0;
+  if (k > 0) {
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      const bool valid = 64 * e + lane < a.nB;
+      bool sel = valid && (all || key[e] > T);
+      if (take > 0) {
+        const bool tie = valid && key[e] == T;
+        const uint64_t tb = __ballot(tie);
+        if (tie && ties_before + __popcll(tb & below) < take) sel = true;
+        ties_before += __popcll(tb);
+      }
+      // words 2e and 2e+1 belong to lanes (2e) % 64 and (2e+1) % 64, slot e / 32
+      const uint64_t m = __ballot(sel);
+      if (lane == (2 * e) % 64) word[e / 32] = (uint32_t)m;
+      if (lane == (2 * e + 1) % 64) word[e / 32] = (uint32_t)(m >> 32);
+    }
+  }
+  // Forced blocks, OR-ed word by word.  The window is an interval of key
+  // blocks [ja, jb]: a block's first and last frames never decrease with its
+  // index, so lo_j <= hi_i + r and hi_j >= lo_i - r each cut the row once.
+  int ja = 1, jb = 0;
   int64_t stride = 0, off = 0;
   if (a.use_static) {
-    lo_i = (i * kBlock) / a.frame_tokens;
-    hi_i = (min(i * kBlock + kBlock, a.N) - 1) / a.frame_tokens;
+    const int64_t ft = a.frame_tokens;
+    const int64_t lo_i = (int64_t)i * kBlock / ft;
+    const int64_t hi_i = (int64_t)(min(i * kBlock + kBlock, a.N) - 1) / ft;
+    // hi_j >= F  <=>  min(64j + 63, N - 1) >= F ft  <=>  64j + 63 >= F ft (F ft <= N - 1)
+    const int64_t F = lo_i - a.window_frames;
+    const int64_t G = hi_i + a.window_frames;
+    ja = F * ft <= 63 ? 0 : (int)((F * ft - 63 + 63) / 64);
+    if (F * ft > a.N - 1) ja = a.nB;  // no block reaches that frame
+    // lo_j <= G  <=>  64j / ft <= G  <=>  64j <= (G + 1) ft - 1
+    jb = G < 0 ? -1 : (int)min((int64_t)a.nB - 1, ((G + 1) * ft - 1) / 64);
     if (a.n_anchors > 0) {
       stride = a.nB / a.n_anchors;
       off = ((int64_t)a.anchor_offset % a.nB + a.nB) % a.nB;
     }
   }
-  const uint64_t below = (1ull << lane) - 1ull;  // lanes under this one
-  uint32_t word = 0u;
-  int cnt = 0, ties_before = 0;
+  int cnt = 0;
 #pragma unroll
-  for (int e = 0; e < E; ++e) {
-    const int j = 64 * e + lane;
-    const bool valid = j < a.nB;
-    bool sel = valid && (all || (k > 0 && key[e] > T));
-    if (take > 0) {
-      const bool tie = valid && key[e] == T;
-      const uint64_t tb = __ballot(tie);
-      if (tie && ties_before + __popcll(tb & below) < take) sel = true;
-      ties_before += __popcll(tb);
-    }
-    if (valid && a.force_diag && j == i) sel = true;
-    if (valid && a.use_static) {
-      const int lo_j = (j * kBlock) / a.frame_tokens;
-      const int hi_j = (min(j * kBlock + kBlock, a.N) - 1) / a.frame_tokens;
-      if (lo_j <= hi_i + a.window_frames && hi_j >= lo_i - a.window_frames) sel = true;
-      if (a.n_anchors > 0) {
-        const int64_t dj = ((int64_t)j - off + a.nB) % a.nB;
-        if (stride > 0 ? (dj % stride == 0 && dj / stride < a.n_anchors) : dj == 0) sel = true;
+  for (int q = 0; q < 2; ++q) {
+    const int w = 64 * q + lane;
+    if (w >= a.W) continue;
+    const int j0 = 32 * w;
+    uint32_t f = 0u;
+    if (a.force_diag && i >= j0 && i < j0 + 32) f |= 1u << (i - j0);
+    if (a.use_static) {
+      const int lo = max(ja, j0), hi = min(jb, j0 + 31);
+      if (lo <= hi) f |= (uint32_t)((((uint64_t)1 << (hi - lo + 1)) - 1) << (lo - j0));
+      for (int t = 0; t < a.n_anchors; ++t) {
+        const int j = (int)((off + (int64_t)t * stride) % a.nB);
+        if (j >= j0 && j < j0 + 32) f |= 1u << (j - j0);
       }
     }
-    const uint64_t m = __ballot(sel);
-    cnt += __popcll(m);
-    if (lane == 2 * e) word = (uint32_t)m;
-    if (lane == 2 * e + 1) word = (uint32_t)(m >> 32);
+    const uint32_t valid = a.nB - j0 >= 32 ? 0xFFFFFFFFu : ((1u << (a.nB - j0)) - 1u);
+    word[q] = (word[q] | f) & valid;
+    a.bits[(int64_t)r * a.W + w] = word[q];
+    cnt += __popc(word[q]);
   }
-  if (lane < a.W) a.bits[(int64_t)r * a.W + lane] = word;
+  cnt = wave_sum(cnt);
   if (lane == 0) a.counts[r] = cnt;
 }
 
@@ -526,13 +472,15 @@ hipError_t launch_fill_i32(int32_t* p, int64_t n, int32_t v, hipStream_t s) {
 }
 
 hipError_t launch_select(const SelectArgs& a, int rows, hipStream_t s) {
-  const dim3 grid((rows + 3) / 4);
-  if (a.mode != kTopP && a.nB <= 512) {
-    hipLaunchKernelGGL(select_topk_kernel<8>, grid, dim3(256), 0, s, a, rows);
-  } else if (a.mode != kTopP && a.nB <= 1024) {
-    hipLaunchKernelGGL(select_topk_kernel<16>, grid, dim3(256), 0, s, a, rows);
+  const dim3 grid((rows + 3) / 4), block(256);
+  if (a.nB <= 512 || a.mode == kStatic) {
+    hipLaunchKernelGGL(select_wave_kernel<8>, grid, block, 0, s, a, rows);
+  } else if (a.nB <= 1024) {
+    hipLaunchKernelGGL(select_wave_kernel<16>, grid, block, 0, s, a, rows);
+  } else if (a.nB <= 2048) {
+    hipLaunchKernelGGL(select_wave_kernel<32>, grid, block, 0, s, a, rows);
   } else {
-    hipLaunchKernelGGL(select_kernel, dim3(rows), dim3(256), 0, s, a);
+    hipLaunchKernelGGL(select_wave_kernel<64>, grid, block, 0, s, a, rows);
   }
   return hipGetLastError();
 }

@@ -163,11 +163,12 @@ def test_static_select(grid, r, na, off):
         assert got[bh] == rows
 
 
-# Rows of 300 and 700 key blocks: the one-wave-per-row selection with a
-# partial last bitmask word (300 = 9 words + 12 bits) and with 16 keys per
-# lane (700 > 512); 2000 blocks take the sorting kernel.
+# Rows of 300, 700, 2000 and 2560 key blocks: the one-wave-per-row
+# selection with a partial last bitmask word (300 = 9 words + 12 bits) and
+# with 8, 16, 32 and 64 keys per lane.
 @pytest.mark.parametrize("grid,k,diag", [((3, 10, 640), 75, False), ((3, 10, 640), 400, True),
-                                         ((7, 40, 160), 175, True), ((5, 50, 512), 500, True)])
+                                         ((7, 40, 160), 175, True), ((5, 50, 512), 500, True),
+                                         ((5, 64, 512), 384, False)])
 def test_topk_select_long_rows(grid, k, diag):
     spec = VideoSpec(1, 1, 64, grid, 108)
     say("topk long rows", grid, k, diag)
@@ -175,6 +176,17 @@ def test_topk_select_long_rows(grid, k, diag):
     F = forced_rows(spec.N, diag, None)
     for bh, (S, rows) in ora.items():
         PT.compare_topk_rows(got[bh], rows, S, k, F)
+
+
+@pytest.mark.parametrize("grid,p,kmin,kcap", [((7, 40, 160), 0.9, 1, 140), ((5, 50, 512), 0.9, 1, 400),
+                                               ((5, 50, 512), 0.5, 3, 2000), ((3, 10, 640), 0.99, 1, 60)])
+def test_topp_select_long_rows(grid, p, kmin, kcap):
+    spec = VideoSpec(1, 1, 64, grid, 110)
+    say("topp long rows", grid, p, kmin, kcap)
+    _, _, _, got, ora = _select_case(spec, "topp", p=p, k_min=kmin, k_cap=kcap)
+    sizes = O.block_sizes(spec.N, 64)
+    for bh, (S, rows) in ora.items():
+        PT.compare_topp_rows(got[bh], rows, S, sizes, p, kmin, kcap)
 
 
 @pytest.mark.parametrize("grid,r,na,off", [((7, 40, 160), 1, 5, 3), ((5, 50, 512), 0, 7, -4)])
