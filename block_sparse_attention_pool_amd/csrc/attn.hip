@@ -1,9 +1,10 @@
 // Attention kernels for gfx950.
 //
-//  * transpose_v: V [N, d] bf16 -> key-major V^T [d, Npad] fp16 per head,
-//    zero padded, with the 16 keys of every chunk stored in the order the
-//    matrix-core operand layout consumes them, so every PV operand is one
-//    contiguous load.  The PV product runs on fp16 operands: bf16 V converts
+//  * transpose_v: V [N, d] bf16 -> key-major fp16 V^T per head, zero
+//    padded, stored as [64-key block][16-key chunk][d][16]: one 16-key tile
+//    (the micro tile) is 4 KB contiguous and a 64-key tile 16 KB.  Inside
+//    each chunk the keys are in the order the matrix-core operand layout
+//    consumes them, so every PV operand is one contiguous load.  The PV product runs on fp16 operands: bf16 V converts
 //    to fp16 exactly (within fp16 range) and P, bounded by 2^8 through the
 //    lazy rescale, keeps 3 more mantissa bits than bf16 would give it.
 //  * attn_fwd: block-sparse (CSR rows) or dense flash attention forward.
@@ -72,7 +73,8 @@ __global__ __launch_bounds__(256) void transpose_v_kernel(TransposeArgs a) {
              (bf16_bits_to_f16_bits(t16[k1 * RS + d]) << 16);
     }
     const u32x4 out = {w[0], w[1], w[2], w[3]};
-    *(u32x4*)(Vt + (int64_t)d * a.Npad + j * kBlock + 8 * u) = out;
+    // chunk u/2 of block j, row d, positions 8 (u%2) .. +7
+    *(u32x4*)(Vt + ((int64_t)(4 * j + (u >> 1)) * D + d) * kMicro + 8 * (u & 1)) = out;
   }
 }
 
@@ -129,7 +131,8 @@ __device__ __forceinline__ int vswz(int r) { return (r >> 1) & 7; }
 // K tile (64 x D bf16): instruction t covers rows t*RPI .. t*RPI+RPI-1; lane
 // l of it lands at LDS row t*RPI + l/DC, 16-byte position l%DC, so it fetches
 // global chunk (l%DC) ^ (row%DC) -- the row-XOR swizzle.  V^T tile (D x 64
-// fp16): 8 rows of 128 bytes per instruction, positions XOR vswz(row).  Wave w
+// fp16 in LDS): 8 rows of 128 bytes per instruction, positions XOR
+// vswz(row); a lane's 8 keys come from one 16-key chunk in global memory.  Wave w
 // issues instructions t = w, w+2, ...: 1 KB of LDS each, 2 KB apart.
 template <int D>
 struct TileCopy {
@@ -164,7 +167,8 @@ struct TileCopy {
       const int t = wave + 2 * u;
       const int r = t * 8 + lane / 8;
       const int c = (lane % 8) ^ vswz(r);
-      voff[u] = (uint32_t)((r * (int64_t)Npad + c * 8) * 2);
+      // 8 keys 8c .. 8c+7 of row r: chunk c/2, half c%2
+      voff[u] = (uint32_t)((((c >> 1) * D + r) * kMicro + (c & 1) * 8) * 2);
     }
     kbase = __builtin_amdgcn_readfirstlane(lds_addr(sK) + wave * 1024);
     vbase = __builtin_amdgcn_readfirstlane(lds_addr(sV) + wave * 1024);
@@ -183,7 +187,7 @@ struct TileCopy {
   }
 
   __device__ __forceinline__ void v_tile(const uint16_t* Vth, int j) const {
-    const uint16_t* base = Vth + j * kBlock;
+    const uint16_t* base = Vth + (int64_t)j * kBlock * D;
     static_for<0, NVI>([&](auto uc) {
       constexpr int u = decltype(uc)::value;
       dma16<u * 2048>(vbase, base, voff[u]);
@@ -496,7 +500,8 @@ void attn_fwd_kernel(AttnArgs a) {
 // sub-tile a (16 rows) over its selected 16-key tiles.  16x16x32 products
 // for S^T = K Q^T (lane holds 4 keys of one query), 16x16x16 products for
 // O^T = V^T P^T (fp16) whose P^T operand is exactly those 4 accumulator
-// registers.
+// registers.  A tile's K rows (4 KB) and V^T chunk (4 KB) are contiguous;
+// the fragments of tile e+1 are loaded while tile e is computed.
 template <int D, bool OUT_BF16>
 __global__ __launch_bounds__(256) void micro_attn_kernel(MicroAttnArgs a) {
   constexpr int KS = D / 32;
@@ -543,21 +548,35 @@ __global__ __launch_bounds__(256) void micro_attn_kernel(MicroAttnArgs a) {
   const float c = a.scale_log2;
   const int vpos = 4 * (2 * (g4 & 1) + (g4 >> 1));  // position of keys 4*g4.. in the chunk
 
-  for (int e = es; e < ee; ++e) {
-    const int beta = a.idx[e] >> 2;
-    const int key = beta * kMicro + n16;
-    f32x4 sacc = {0.f, 0.f, 0.f, 0.f};
+  struct Frags {
+    bf16x8 k[KS];
+    u32x2 v[DT];
+    int beta;
+  };
+  const_i32* idx = (const_i32*)a.idx;
+  auto load = [&](int e, Frags& f) {
+    f.beta = idx[e] >> 2;
+    const int key = f.beta * kMicro + n16;
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
       u32x4 v = {0u, 0u, 0u, 0u};
       if (key < a.N) v = *(const u32x4*)(Kh + (int64_t)key * a.sn + 32 * s + 8 * g4);
-      sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, v), qf[s], sacc,
-                                                     0, 0, 0);
+      f.k[s] = __builtin_bit_cast(bf16x8, v);
     }
+    // chunk beta of the head: [d][16] fp16, rows 16t + n16
+    const uint16_t* vc = Vth + (int64_t)f.beta * D * kMicro;
+#pragma unroll
+    for (int t = 0; t < DT; ++t) f.v[t] = *(const u32x2*)(vc + (16 * t + n16) * kMicro + vpos);
+  };
+  auto compute = [&](const Frags& f) {
+    f32x4 sacc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < KS; ++s)
+      sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(f.k[s], qf[s], sacc, 0, 0, 0);
     // lane holds keys beta*16 + 4*g4 + rr of query q
 #pragma unroll
     for (int rr = 0; rr < 4; ++rr)
-      if (beta * kMicro + 4 * g4 + rr >= a.N) sacc[rr] = -INFINITY;
+      if (f.beta * kMicro + 4 * g4 + rr >= a.N) sacc[rr] = -INFINITY;
     float mx = fmaxf(fmaxf(sacc[0], sacc[1]), fmaxf(sacc[2], sacc[3]));
     mx = fmaxf(mx, __shfl_xor(mx, 16));
     mx = fmaxf(mx, __shfl_xor(mx, 32));
@@ -571,18 +590,27 @@ __global__ __launch_bounds__(256) void micro_attn_kernel(MicroAttnArgs a) {
     }
     float p[4];
 #pragma unroll
-    for (int rr = 0; rr < 4; ++rr) {
-      p[rr] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[rr], c, -m_run));
-      l_run += p[rr];
-    }
+    for (int rr = 0; rr < 4; ++rr) p[rr] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[rr], c, -m_run));
     const u32x2 pk = {pack_f16x2(p[0], p[1]), pack_f16x2(p[2], p[3])};
+    // the row sum adds the rounded fp16 values the product uses
+    l_run = add_f16x2(pk[0], add_f16x2(pk[1], l_run));
     const f16x4 pb = __builtin_bit_cast(f16x4, pk);
 #pragma unroll
-    for (int t = 0; t < DT; ++t) {
-      const u32x2 v = *(const u32x2*)(Vth + (int64_t)(16 * t + n16) * a.Npad + beta * kMicro + vpos);
-      o[t] = __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4, v), pb, o[t], 0, 0, 0);
-    }
+    for (int t = 0; t < DT; ++t)
+      o[t] = __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4, f.v[t]), pb, o[t], 0, 0, 0);
+  };
+  // two fragment sets, alternating
+  Frags fa, fb;
+  int e = es;
+  if (e < ee) load(e, fa);
+  for (; e + 1 < ee; e += 2) {
+    load(e + 1, fb);
+    compute(fa);
+    if (e + 2 < ee) load(e + 2, fa);
+    compute(fb);
   }
+  if (e < ee) compute(fa);
+
   float l_tot = l_run + __shfl_xor(l_run, 16);
   l_tot += __shfl_xor(l_tot, 32);
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
