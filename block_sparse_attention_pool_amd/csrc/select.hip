@@ -302,22 +302,22 @@ __global__ void fill_i32_kernel(int32_t* p, int64_t n, int32_t v) {
 // ---------------------------------------------------------- micro select
 
 // Radix selection, most significant byte first, of the `remaining`-th
-// largest 32-bit key among the candidates for which fn(c, &key) is true.
+// largest 32-bit key among the keys each thread hands to the visitor
+// (each(f) calls f(key) for every candidate key of the calling thread).
 // On return `remaining` holds how many candidates equal to the returned
 // threshold must still be taken.  All threads of the block call it.
-template <class Fn>
-__device__ uint32_t block_radix_select(int ncand, int& remaining, Fn fn,
-                                       uint32_t* hist, int* shared_out) {
+template <class Each>
+__device__ uint32_t block_radix_select(int& remaining, Each each, uint32_t* hist,
+                                       int* shared_out) {
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   uint32_t prefix = 0, pmask = 0;
   for (int shift = 24; shift >= 0; shift -= 8) {
     for (int q = tid; q < 256; q += blockDim.x) hist[q] = 0u;
     __syncthreads();
-    for (int c = tid; c < ncand; c += blockDim.x) {
-      uint32_t key;
-      if (fn(c, &key) && (key & pmask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1u);
-    }
+    each([&](uint32_t key) {
+      if ((key & pmask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1u);
+    });
     __syncthreads();
     if (wave == 0) {
       const int b0 = 4 * lane;
@@ -354,11 +354,18 @@ __device__ uint32_t block_radix_select(int ncand, int& remaining, Fn fn,
   return prefix;
 }
 
+// The row's candidates are read once into registers, E per thread
+// (candidate c = e * 1024 + thread, c = a * nT + beta); key 0 marks a
+// candidate inside a selected macro block (valid keys are made >= 1).  The
+// m-th largest key T is found by radix selection over the registers; of
+// the keys equal to T the lowest codes 4 beta + a are taken.
+template <int E>
 __global__ __launch_bounds__(1024) void micro_select_kernel(MicroSelectArgs a) {
   __shared__ uint32_t omask[128];
   __shared__ uint32_t hist[256];
   __shared__ int sh_out[2];
   __shared__ int ired[16];
+  __shared__ int wcnt[16][E];
 
   const int i = blockIdx.x;
   const int z = blockIdx.y;
@@ -367,6 +374,7 @@ __global__ __launch_bounds__(1024) void micro_select_kernel(MicroSelectArgs a) {
   const int h = a.heads.h[z % nh];
   const int64_t r = ((int64_t)b * a.H + h) * a.nB + i;
   const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
 
   for (int w = tid; w < a.W; w += 1024) omask[w] = 0u;
   __syncthreads();
@@ -381,73 +389,89 @@ __global__ __launch_bounds__(1024) void micro_select_kernel(MicroSelectArgs a) {
   const int nq = min(4, nT - 4 * i);
   const int ncand = nq * nT;
   const float* sig = a.sigma + ((int64_t)z * nT + 4 * i) * nT;
-  auto valid = [&](int c) {
-    const int beta = c % nT;
-    const int blk = beta >> 2;
-    return ((omask[blk >> 5] >> (blk & 31)) & 1u) == 0u;
+  // codes 4 beta + a of the thread's candidates, walked in element order
+  // (c grows by 1024 per element: beta and a advance without a division)
+  const int beta0 = tid % nT, a0 = tid / nT;
+  auto for_codes = [&](auto f) {
+    int beta = beta0, sub = a0;
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      f(e, beta, 4u * (uint32_t)beta + (uint32_t)sub);
+      beta += 1024;
+      while (beta >= nT) {
+        beta -= nT;
+        ++sub;
+      }
+    }
   };
-  auto score_key = [&](int c, uint32_t* key) {
-    if (!valid(c)) return false;
-    *key = float_order_key(sig[c]);
-    return true;
-  };
-
+  uint32_t key[E];
   int nvalid = 0;
-  for (int c = tid; c < ncand; c += 1024) nvalid += valid(c) ? 1 : 0;
+  for_codes([&](int e, int beta, uint32_t) {
+    const int c = e * 1024 + tid;
+    key[e] = 0u;
+    if (c < ncand) {
+      const int blk = beta >> 2;
+      if (((omask[blk >> 5] >> (blk & 31)) & 1u) == 0u) key[e] = max(1u, float_order_key(sig[c]));
+    }
+    nvalid += key[e] != 0u;
+  });
   nvalid = block_sum(nvalid, ired);
 
   const int m = a.m;
-  uint32_t T = 0u, Tc = 0u;
-  int mode = 0;  // 0: take all valid; 1: key >= T; 2: key > T or (== T and ~code >= Tc)
-  if (nvalid > m) {
+  uint32_t T = 0u, C = 0xFFFFFFFFu;  // threshold key; largest code taken at T
+  const bool all = nvalid <= m;
+  if (!all) {
     int remaining = m;
-    T = block_radix_select(ncand, remaining, score_key, hist, sh_out);
+    T = block_radix_select(remaining, [&](auto f) {
+#pragma unroll
+      for (int e = 0; e < E; ++e)
+        if (key[e] != 0u) f(key[e]);
+    }, hist, sh_out);
     int n_eq = 0;
-    for (int c = tid; c < ncand; c += 1024) {
-      uint32_t key;
-      if (score_key(c, &key) && key == T) ++n_eq;
-    }
+#pragma unroll
+    for (int e = 0; e < E; ++e) n_eq += key[e] == T;
     n_eq = block_sum(n_eq, ired);
-    if (n_eq == remaining) {
-      mode = 1;
-    } else {
+    if (remaining < n_eq) {
       // ties at the threshold: the lowest codes win (largest ~code)
-      auto tie_key = [&](int c, uint32_t* key) {
-        uint32_t k;
-        if (!score_key(c, &k) || k != T) return false;
-        const uint32_t code = 4u * (uint32_t)(c % nT) + (uint32_t)(c / nT);
-        *key = ~code;
-        return true;
-      };
       int rem2 = remaining;
-      Tc = block_radix_select(ncand, rem2, tie_key, hist, sh_out);
-      mode = 2;
+      C = ~block_radix_select(rem2, [&](auto f) {
+        for_codes([&](int e, int, uint32_t code) {
+          if (key[e] == T) f(~code);
+        });
+      }, hist, sh_out);
     }
   }
 
-  // Compaction in candidate order (sub-tile a major, key tile beta minor).
-  int32_t* out = a.slots + r * (int64_t)m;
-  int written = 0;
-  for (int base = 0; base < ncand; base += 1024) {
-    const int c = base + tid;
-    bool sel = false;
-    if (c < ncand) {
-      uint32_t key;
-      if (score_key(c, &key)) {
-        if (mode == 0) sel = true;
-        else if (mode == 1) sel = key >= T;
-        else {
-          const uint32_t code = 4u * (uint32_t)(c % nT) + (uint32_t)(c / nT);
-          sel = key > T || (key == T && ~code >= Tc);
-        }
-      }
+  // Compaction in candidate order (sub-tile a major, key tile beta minor):
+  // candidate e * 1024 + 64 w + lane comes after every candidate of
+  // element e' < e and of wave w' < w at element e.
+  bool sel[E];
+  for_codes([&](int e, int, uint32_t code) {
+    sel[e] = key[e] != 0u && (all || key[e] > T || (key[e] == T && code <= C));
+    const int cnt = __popcll(__ballot(sel[e]));
+    if (lane == 0) wcnt[wave][e] = cnt;
+  });
+  __syncthreads();
+  // lane e: exclusive offset of (element e, this wave) and the row total
+  int before_w = 0, tot_e = 0;
+  if (lane < E) {
+    for (int w = 0; w < 16; ++w) {
+      const int v = wcnt[w][lane];
+      tot_e += v;
+      if (w < wave) before_w += v;
     }
-    int tot;
-    const int pos = block_exclusive_scan((int)sel, ired, &tot);
-    if (sel && written + pos < m) out[written + pos] = 4 * (c % nT) + c / nT;
-    written += tot;
   }
-  if (tid == 0) a.counts[r] = min(written, m);
+  const int incl = wave_inclusive_scan(tot_e);
+  const int off_e = incl - tot_e + before_w;
+  const int total = __shfl(incl, 63);
+  const uint64_t below = (1ull << lane) - 1ull;
+  int32_t* out = a.slots + r * (int64_t)m;
+  for_codes([&](int e, int, uint32_t code) {
+    const uint64_t bal = __ballot(sel[e]);
+    const int pos = __shfl(off_e, e) + __popcll(bal & below);
+    if (sel[e] && pos < m) out[pos] = (int32_t)code;
+  });
+  if (tid == 0) a.counts[r] = min(total, m);
 }
 
 // One wave per row: copy the row's slots into the CSR column array.
@@ -499,7 +523,15 @@ hipError_t launch_emit_bits(const uint32_t* bits, int W, int rows, const int32_t
 }
 
 hipError_t launch_micro_select(const MicroSelectArgs& a, int B, hipStream_t s) {
-  hipLaunchKernelGGL(micro_select_kernel, dim3(a.nB, B * a.heads.n), dim3(1024), 0, s, a);
+  const dim3 grid(a.nB, B * a.heads.n), block(1024);
+  const int ncand = 4 * a.nT;  // candidates of one query block, at most
+  if (ncand <= 8 * 1024) {
+    hipLaunchKernelGGL(micro_select_kernel<8>, grid, block, 0, s, a);
+  } else if (ncand <= 32 * 1024) {
+    hipLaunchKernelGGL(micro_select_kernel<32>, grid, block, 0, s, a);
+  } else {
+    hipLaunchKernelGGL(micro_select_kernel<64>, grid, block, 0, s, a);
+  }
   return hipGetLastError();
 }
 
