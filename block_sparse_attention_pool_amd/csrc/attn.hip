@@ -120,20 +120,17 @@ __device__ __forceinline__ void dma16(uint32_t m0base, const void* sbase, uint32
                : "memory", "m0", "scc");
 }
 
-// XOR swizzle of the 16-byte chunks of V^T tile row r (128-byte rows).  A
-// 128-bit LDS read is served 16 lanes at a time by 64 four-byte banks; the
-// 16 lanes read 16 consecutive rows, and rows r and r+8 share banks unless
-// their chunk positions differ, hence the (r/2)%8 pattern.  K tile rows are
-// 256 bytes, where r%16 already separates 16 consecutive rows.
-__device__ __forceinline__ int vswz(int r) { return (r >> 1) & 7; }
-
 // Per-lane byte offsets of the tile copies of one wave (loop invariant).
 // K tile (64 x D bf16): instruction t covers rows t*RPI .. t*RPI+RPI-1; lane
 // l of it lands at LDS row t*RPI + l/DC, 16-byte position l%DC, so it fetches
-// global chunk (l%DC) ^ (row%DC) -- the row-XOR swizzle.  V^T tile (D x 64
-// fp16 in LDS): 8 rows of 128 bytes per instruction, positions XOR
-// vswz(row); a lane's 8 keys come from one 16-key chunk in global memory.  Wave w
-// issues instructions t = w, w+2, ...: 1 KB of LDS each, 2 KB apart.
+// global chunk (l%DC) ^ (row%DC) -- the row-XOR swizzle (a 128-bit LDS read
+// is served 16 lanes at a time by 64 four-byte banks; K rows are 256 bytes,
+// so r%16 separates 16 consecutive rows).  V^T tile: kept in LDS as it is
+// in global memory, chunk-major [4][D][16] fp16 (32-byte rows), so every
+// copy instruction reads 1 KB of contiguous global memory; the two 16-byte
+// halves of a row are swapped when (row/8) is odd, which puts the 16 rows a
+// PV operand read touches at once on distinct banks.  Wave w issues
+// instructions t = w, w+2, ...: 1 KB of LDS each, 2 KB apart.
 template <int D>
 struct TileCopy {
   static constexpr int DC = D / 8;
@@ -164,11 +161,13 @@ struct TileCopy {
     }
 #pragma unroll
     for (int u = 0; u < NVI; ++u) {
+      // LDS byte p = 1024 t + 16 lane of the chunk-major tile [4][D][16]:
+      // chunk p / (32 D), row (p / 32) % D, half (p / 16) % 2, which holds
+      // the global half h ^ ((row / 8) % 2) of the same chunk and row
       const int t = wave + 2 * u;
-      const int r = t * 8 + lane / 8;
-      const int c = (lane % 8) ^ vswz(r);
-      // 8 keys 8c .. 8c+7 of row r: chunk c/2, half c%2
-      voff[u] = (uint32_t)((((c >> 1) * D + r) * kMicro + (c & 1) * 8) * 2);
+      const int pb = 1024 * t + 16 * lane;
+      const int ch = pb / (32 * D), r = (pb / 32) % D, hf = (pb / 16) & 1;
+      voff[u] = (uint32_t)((ch * D + r) * 32 + 16 * (hf ^ ((r >> 3) & 1)));
     }
     kbase = __builtin_amdgcn_readfirstlane(lds_addr(sK) + wave * 1024);
     vbase = __builtin_amdgcn_readfirstlane(lds_addr(sV) + wave * 1024);
@@ -314,7 +313,7 @@ void attn_fwd_kernel(AttnArgs a) {
     const int row = 32 * t + n;
 #pragma unroll
     for (int cc = 0; cc < 4; ++cc)
-      va[cc] = *(const f16x8*)(sV + row * 64 + (((2 * cc + g) ^ vswz(row)) * 8));
+      va[cc] = *(const f16x8*)(sV + (cc * D + row) * 16 + ((g ^ ((row >> 3) & 1)) * 8));
   };
   auto pv = [&](const f16x8(&pf)[4]) {
     f16x8 va[2][4];
