@@ -198,9 +198,10 @@ int64_t bsa_attn_workspace_bytes(const bsa_shape* shape);
  * token t of block i, over the keys of the blocks in its CSR row:
  *   LSE[t] = ln sum_tau exp(scale * q_t . k_tau)
  *   O[t]   = sum_tau exp(scale * q_t . k_tau - LSE[t]) v_tau
- * QK^T and PV run as bf16 matrix-core products with float32 accumulation;
- * the softmax is online (flash style) in float32.  Rows with an empty list
- * get O = 0 and LSE = -inf.
+ * QK^T runs as a bf16 matrix-core product on the inputs, PV as an fp16 one
+ * (P rounded to fp16, V converted from bf16 exactly), both with float32
+ * accumulation; the softmax is online (flash style) in float32.  Rows with
+ * an empty list get O = 0 and LSE = -inf.
  *
  * row_ptr / col_idx: a CSR from bsa_select_blocks (or the caller); column
  *   indices must lie in [0, nB).  Order within a row does not matter.
