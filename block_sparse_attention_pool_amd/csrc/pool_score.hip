@@ -72,10 +72,12 @@ __global__ __launch_bounds__(256) void pool_kernel(PoolArgs a) {
 }
 
 // Batched float32 C = scale * A B^T with A [M, D], B [Nc, D] per batch.
-// 64x64 output tile per workgroup, 256 threads with 4x4 outputs each, the
-// shared dimension staged through LDS in chunks of 32.  Batch z maps to the
-// (b, h) pair through the head list so the same kernel serves the pooled
-// block scores (all heads) and the micro tile scores (selected heads).
+// 64x64 output tile per workgroup, the shared dimension staged through LDS
+// in chunks of 32; each of the 4 waves computes one 32x32 quarter with the
+// float32 matrix-core product v_mfma_f32_32x32x2_f32 (fp32 products and
+// accumulation: no rounding of the means).  Batch z maps to the (b, h) pair
+// through the head list so the same kernel serves the pooled block scores
+// (all heads) and the micro tile scores (selected heads).
 __global__ __launch_bounds__(256) void score_gemm_kernel(GemmArgs a) {
   constexpr int TK = 32;
   __shared__ float As[TK][64 + 4];
@@ -91,12 +93,12 @@ __global__ __launch_bounds__(256) void score_gemm_kernel(GemmArgs a) {
 
   const int m0 = blockIdx.y * 64, n0 = blockIdx.x * 64;
   const int tid = threadIdx.x;
-  const int tx = tid & 15, ty = tid >> 4;
-  float acc[4][4];
+  const int wave = tid >> 6, lane = tid & 63;
+  const int wm = (wave >> 1) * 32, wn = (wave & 1) * 32;  // this wave's quarter
+  const int l32 = lane & 31, kh = lane >> 5;
+  f32x16 acc;
 #pragma unroll
-  for (int r = 0; r < 4; ++r)
-#pragma unroll
-    for (int q = 0; q < 4; ++q) acc[r][q] = 0.f;
+  for (int r = 0; r < 16; ++r) acc[r] = 0.f;
 
   for (int k0 = 0; k0 < a.D; k0 += TK) {
     // 64 rows x 32 floats per operand = 512 float4; 2 per thread each.
@@ -114,25 +116,21 @@ __global__ __launch_bounds__(256) void score_gemm_kernel(GemmArgs a) {
       }
     }
     __syncthreads();
-#pragma unroll 8
-    for (int k = 0; k < TK; ++k) {
-      const f32x4 av = *(const f32x4*)&As[k][ty * 4];
-      const f32x4 bv = *(const f32x4*)&Bs[k][tx * 4];
+    // k-step s covers shared indices 2s, 2s+1: lane holds A[wm + l32][2s + kh]
+    // and B[wn + l32][2s + kh]
 #pragma unroll
-      for (int r = 0; r < 4; ++r)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) acc[r][q] = __builtin_fmaf(av[r], bv[q], acc[r][q]);
-    }
+    for (int s2 = 0; s2 < TK / 2; ++s2)
+      acc = __builtin_amdgcn_mfma_f32_32x32x2f32(As[2 * s2 + kh][wm + l32], Bs[2 * s2 + kh][wn + l32],
+                                                 acc, 0, 0, 0);
     __syncthreads();
   }
+  // lane holds rows 8 (r/4) + 4 kh + r%4 of column l32 of the quarter
+  const int n = n0 + wn + l32;
+  if (n < a.Nc) {
 #pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const int m = m0 + ty * 4 + r;
-    if (m >= a.M) continue;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int n = n0 + tx * 4 + q;
-      if (n < a.Nc) Cm[(int64_t)m * a.Nc + n] = a.scale * acc[r][q];
+    for (int r = 0; r < 16; ++r) {
+      const int m = m0 + wm + 8 * (r >> 2) + 4 * kh + (r & 3);
+      if (m < a.M) Cm[(int64_t)m * a.Nc + n] = a.scale * acc[r];
     }
   }
 }
