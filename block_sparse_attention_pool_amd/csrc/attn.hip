@@ -315,9 +315,10 @@ void attn_fwd_kernel(AttnArgs a) {
     for (int cc = 0; cc < 4; ++cc)
       va[cc] = *(const f16x8*)(sV + (cc * D + row) * 16 + ((g ^ ((row >> 3) & 1)) * 8));
   };
-  auto pv = [&](const f16x8(&pf)[4]) {
+  auto pv = [&](const f16x8(&pf)[4], const f16x8(&va0)[4]) {
     f16x8 va[2][4];
-    v_frags(0, va[0]);
+#pragma unroll
+    for (int cc = 0; cc < 4; ++cc) va[0][cc] = va0[cc];
 #pragma unroll
     for (int t = 0; t < DT; ++t) {
       if (t + 1 < DT) v_frags(t + 1, va[(t + 1) & 1]);
@@ -404,6 +405,8 @@ void attn_fwd_kernel(AttnArgs a) {
     exec_barrier();    // both waves are done with sK; sV holds V(e-1)
     if (e + 1 < e1) cp.k_tile(Kh, a.sn, jn, a.nB);
 
+    f16x8 va0[4];  // V^T fragments of block e-1's first d tile, read early
+    v_frags(0, va0);
     // Lane holds keys 8*(r/4) + 4*g + r%4 (+32 for s1) of query q.
     if (j == a.nB - 1) {
       const int nvalid = a.N - j * kBlock;
@@ -449,19 +452,11 @@ void attn_fwd_kernel(AttnArgs a) {
       for (int cc = 0; cc < 4; ++cc) pf_prev[cc] *= ah;
       m_run = m_new;
     }
-    softmax_pack(s0, s1, pf);  // VALU work of block e ...
-    pv(pf_prev);               // ... independent of the PV products of block e-1
-    // Interleave them: the fragment reads of the first two d tiles up front,
-    // then per d tile four products each followed by seven vector ALU
-    // instructions of the softmax, and the reads of the tile after next.
-    __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);  // DS reads
-    static_for<0, DT>([&](auto) {
-      static_for<0, 4>([&](auto) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-        __builtin_amdgcn_sched_group_barrier(0x002, 7, 0);  // VALU
-      });
-      __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);  // DS reads
-    });
+    // The vector work of block e and the (independent) PV products of block
+    // e-1 share one basic block, so the compiler interleaves them.
+    softmax_pack(s0, s1, pf);
+    pv(pf_prev, va0);
+
 #pragma unroll
     for (int cc = 0; cc < 4; ++cc) pf_prev[cc] = pf[cc];
     jprev = j;
@@ -473,7 +468,9 @@ void attn_fwd_kernel(AttnArgs a) {
     cp.v_tile(Vth, jprev);
     wait_vmcnt<0>();
     exec_barrier();
-    pv(pf_prev);
+    f16x8 va0[4];
+    v_frags(0, va0);
+    pv(pf_prev, va0);
   }
 
   const float l_tot = l_run + __shfl_xor(l_run, 32);
