@@ -241,28 +241,47 @@ __global__ __launch_bounds__(256) void select_wave_kernel(SelectArgs a, int rows
 
 // -------------------------------------------------------- row pointers
 
+// Exclusive prefix of the per-row counts into row_ptr (and the total into
+// row_ptr[rows] and *out_nnz), one workgroup: the counts stream through LDS
+// in chunks of 16384 (coalesced loads and stores), each thread scans 16
+// consecutive entries of a chunk, and a running carry links the chunks.
 __global__ __launch_bounds__(1024) void scan_kernel(const int32_t* counts, int rows,
                                                     int32_t* row_ptr, int64_t* out_nnz) {
+  constexpr int kChunk = 16384, kPer = 16;
+  __shared__ int32_t buf[kChunk + kChunk / kPer];  // one pad word per 16 entries
   __shared__ int64_t red[16];
   const int tid = threadIdx.x;
-  const int per = (rows + 1023) / 1024;
-  const int start = tid * per;
-  int64_t local = 0;
-  for (int e = 0; e < per; ++e) {
-    const int idx = start + e;
-    if (idx < rows) local += counts[idx];
-  }
-  int64_t total;
-  int64_t run = block_exclusive_scan(local, red, &total);
-  for (int e = 0; e < per; ++e) {
-    const int idx = start + e;
-    if (idx >= rows) break;
-    row_ptr[idx] = (int32_t)run;
-    run += counts[idx];
+  auto at = [](int k) { return k + k / kPer; };
+  int64_t carry = 0;
+  for (int base = 0; base < rows; base += kChunk) {
+    const int n = min(kChunk, rows - base);
+    for (int k = tid; k < n; k += 1024) buf[at(k)] = counts[base + k];
+    __syncthreads();
+    int64_t local = 0;
+#pragma unroll
+    for (int e = 0; e < kPer; ++e) {
+      const int k = tid * kPer + e;
+      if (k < n) local += buf[at(k)];
+    }
+    int64_t total;
+    int64_t run = carry + block_exclusive_scan(local, red, &total);
+#pragma unroll
+    for (int e = 0; e < kPer; ++e) {
+      const int k = tid * kPer + e;
+      if (k < n) {
+        const int v = buf[at(k)];
+        buf[at(k)] = (int32_t)run;
+        run += v;
+      }
+    }
+    __syncthreads();
+    for (int k = tid; k < n; k += 1024) row_ptr[base + k] = buf[at(k)];
+    carry += total;
+    __syncthreads();
   }
   if (tid == 0) {
-    row_ptr[rows] = (int32_t)total;
-    *out_nnz = total;
+    row_ptr[rows] = (int32_t)carry;
+    *out_nnz = carry;
   }
 }
 
