@@ -63,8 +63,9 @@ __device__ T block_exclusive_scan(T v, T* red, T* total) {
 
 // Top-k, top-p and static rows, one wave per row.  The row is held as
 // order-preserving 32-bit keys, E per lane (element e of lane l is block
-// 64e + l): keys of the pooled scores for top-k, of the size-weighted
-// exponentials n_j exp(S_j - max S) for top-p.
+// 64e + l; E = 8, 16, 24, 32, 48 or 64, the smallest that holds the row):
+// keys of the pooled scores for top-k, of the size-weighted exponentials
+// n_j exp(S_j - max S) for top-p.
 //   top-p: the cut of the descending prefix is found without sorting.  The
 //     block where the cumulative mass first reaches p * total has the
 //     largest key T with mass(key >= T) >= p * total (a bitwise descent over
@@ -520,8 +521,12 @@ hipError_t launch_select(const SelectArgs& a, int rows, hipStream_t s) {
     hipLaunchKernelGGL(select_wave_kernel<8>, grid, block, 0, s, a, rows);
   } else if (a.nB <= 1024) {
     hipLaunchKernelGGL(select_wave_kernel<16>, grid, block, 0, s, a, rows);
+  } else if (a.nB <= 1536) {
+    hipLaunchKernelGGL(select_wave_kernel<24>, grid, block, 0, s, a, rows);
   } else if (a.nB <= 2048) {
     hipLaunchKernelGGL(select_wave_kernel<32>, grid, block, 0, s, a, rows);
+  } else if (a.nB <= 3072) {
+    hipLaunchKernelGGL(select_wave_kernel<48>, grid, block, 0, s, a, rows);
   } else {
     hipLaunchKernelGGL(select_wave_kernel<64>, grid, block, 0, s, a, rows);
   }

@@ -163,12 +163,13 @@ def test_static_select(grid, r, na, off):
         assert got[bh] == rows
 
 
-# Rows of 300, 700, 2000 and 2560 key blocks: the one-wave-per-row
-# selection with a partial last bitmask word (300 = 9 words + 12 bits) and
-# with 8, 16, 32 and 64 keys per lane.
+# Rows of 300, 700, 1172, 2000, 2560 and 3584 key blocks: the
+# one-wave-per-row selection with a partial last bitmask word (300 = 9 words
+# + 12 bits) and with 8, 16, 24, 32, 48 and 64 keys per lane.
 @pytest.mark.parametrize("grid,k,diag", [((3, 10, 640), 75, False), ((3, 10, 640), 400, True),
-                                         ((7, 40, 160), 175, True), ((5, 50, 512), 500, True),
-                                         ((5, 64, 512), 384, False)])
+                                         ((7, 40, 160), 175, True), ((5, 50, 300), 293, False),
+                                         ((5, 50, 512), 500, True), ((5, 64, 512), 384, False),
+                                         ((7, 64, 512), 540, True)])
 def test_topk_select_long_rows(grid, k, diag):
     spec = VideoSpec(1, 1, 64, grid, 108)
     say("topk long rows", grid, k, diag)
