@@ -4,9 +4,10 @@
 //    padded, stored as [64-key block][16-key chunk][d][16]: one 16-key tile
 //    (the micro tile) is 4 KB contiguous and a 64-key tile 16 KB.  Inside
 //    each chunk the keys are in the order the matrix-core operand layout
-//    consumes them, so every PV operand is one contiguous load.  The PV product runs on fp16 operands: bf16 V converts
-//    to fp16 exactly (within fp16 range) and P, bounded by 2^8 through the
-//    lazy rescale, keeps 3 more mantissa bits than bf16 would give it.
+//    consumes them, so every PV operand is one contiguous load.  The PV
+//    product runs on fp16 operands: bf16 V converts to fp16 exactly (within
+//    fp16 range) and P, bounded by 2^8 through the lazy rescale, keeps 3
+//    more mantissa bits than bf16 would give it.
 //  * attn_fwd: block-sparse (CSR rows) or dense flash attention forward.
 //    HyperVAttention section 2, Eq. 4 (attention restricted to the selected
 //    key blocks; identity permutation) and the HyMoR-Attn Macro backbone.
@@ -142,7 +143,7 @@ struct TileCopy {
   uint32_t kbase, vbase;  // LDS byte address of this wave's first instruction
 
   uint32_t kr[NK];  // the same for the last key block, rows clamped to N-1
-  __device__ __forceinline__ void init(int64_t sn, int Npad, int wave, int lane,
+  __device__ __forceinline__ void init(int64_t sn, int wave, int lane,
                                        const uint16_t* sK, const uint16_t* sV, int N, int nB) {
     const int last = N - 1 - (nB - 1) * kBlock;
 #pragma unroll
@@ -235,8 +236,8 @@ __device__ __forceinline__ void exec_barrier() { asm volatile("s_barrier" ::: "m
 typedef __attribute__((address_space(4))) const int32_t const_i32;
 
 // One workgroup per (b, h, 64-row query block), two waves of 32 rows each.
-// Per selected key block the 64 x D K tile and the D x 64 V^T tile sit in
-// LDS (16-byte chunks XOR-swizzled by row).  The K buffer is refilled with
+// Per selected key block the 64 x D K tile (16-byte chunks XOR-swizzled by
+// row) and the chunk-major V^T tile sit in LDS.  The K buffer is refilled with
 // the next block as soon as both waves have finished QK^T, the V buffer as
 // soon as they have finished PV, so each copy overlaps the other half of
 // the iteration without a second buffer.  32 KB of LDS and at most 256
@@ -248,7 +249,6 @@ void attn_fwd_kernel(AttnArgs a) {
   constexpr int DC = D / 8;      // 16-byte chunks per K row
   constexpr int KS = D / 16;     // k-steps of the QK^T product
   constexpr int DT = D / 32;     // 32-row d tiles of the PV product
-  constexpr int NV = TileCopy<D>::NVI;  // V^T copy instructions per wave per tile
   __shared__ __attribute__((aligned(1024))) uint16_t sK[64 * D];
   __shared__ __attribute__((aligned(1024))) uint16_t sV[D * 64];
 
@@ -305,7 +305,7 @@ void attn_fwd_kernel(AttnArgs a) {
   // the tile copies in flight.
   wait_vmcnt<0>();
   TileCopy<D> cp;
-  cp.init(a.sn, a.Npad, wave, lane, sK, sV, a.N, a.nB);
+  cp.init(a.sn, wave, lane, sK, sV, a.N, a.nB);
 
   // O^T += V^T P^T for one key block whose V^T tile is in sV.
   // The V^T fragments of d tile t+1 are read while the products of tile t run.

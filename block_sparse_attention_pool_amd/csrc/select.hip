@@ -185,8 +185,8 @@ __global__ __launch_bounds__(256) void select_wave_kernel(SelectArgs a, int rows
       if (take > 0) {
         const bool tie = valid && key[e] == T;
         const uint64_t tb = __ballot(tie);
-        if (tie && ties_before + __popcll(tb & below) < take) sel = true;
-        ties_before += __popcll(tb);
+        if (tie && ties_before + (int)__popcll(tb & below) < take) sel = true;
+        ties_before += (int)__popcll(tb);
       }
       // words 2e and 2e+1 belong to lanes (2e) % 64 and (2e+1) % 64, slot e / 32
       const uint64_t m = __ballot(sel);
