@@ -37,6 +37,8 @@ sys.path.insert(0, ROOT)
 METRIC = "block-sparse attn executed TFLOP/s, % bf16 MFMA peak, speedup vs dense"
 PEAK_TFLOPS = 2500.0   # MI355X dense bf16/fp16 matrix peak
 HBM_GBS = 8000.0       # MI355X HBM3E
+N_ROTATIONS = 3        # static workload: anchor offsets cycled over the steps
+FLUSH_BYTES = 512 << 20  # larger than L2 (8 x 4 MB) plus the 256 MB Infinity Cache
 
 
 def parse():
@@ -175,7 +177,8 @@ def main():
         wf = c["window_frames"] if args.window_frames is None else args.window_frames
         sel = dict(static=dict(frame_tokens=spec.frame_tokens, window_frames=wf,
                                n_anchors=c["n_anchors"], anchor_offset=rotation_offset(cfg, 0, nB)))
-        sel_desc = f"static window +-{wf} frames + {c['n_anchors']} anchors"
+        sel_desc = (f"static window +-{wf} frames + {c['n_anchors']} anchors rotating over "
+                    f"{N_ROTATIONS} offsets")
     micro = None
     if "micro_head_frac" in c or "micro_m" in c:
         heads = micro_heads(cfg)
@@ -193,7 +196,12 @@ def main():
     def score():
         return bsa.bsa_score_blocks(Q, K, scores=(mode != "static"), micro=16 if micro else 0)
 
-    def select(sc):
+    offsets = [rotation_offset(cfg, call, nB) for call in range(N_ROTATIONS)]
+
+    def select(sc, call=0):
+        if mode == "static":
+            # the anchors rotate: each call draws its own offset
+            sel["static"]["anchor_offset"] = offsets[call % N_ROTATIONS]
         return bsa.bsa_select_blocks(sc["scores"], Q, mode=mode, **sel)
 
     def micro_select(sc, rp, ci):
@@ -202,10 +210,10 @@ def main():
             micro=dict(m=micro["m"], scale=scale, head_mask=micro["mask"], macro=(rp, ci),
                        qpool16=sc["qpool16"], kpool16=sc["kpool16"]))
 
-    def step():
+    def step(call=0):
         # the static window needs no scores: the selection runs on the mask alone
         sc = score() if mode != "static" else {"scores": None}
-        rp, ci, nnz = select(sc)
+        rp, ci, nnz = select(sc, call)
         bsa.bsa_sparse_attn_fwd(Q, K, V, rp, ci, out=O_buf, lse=L_buf, workspace=ws)
         mnnz = None
         if micro is not None:
@@ -216,18 +224,26 @@ def main():
                               out=O_buf, lse_out=L_buf)
         return sc, rp, ci, nnz, mnnz
 
-    for _ in range(args.warmup):
-        step()
+    for w in range(args.warmup):
+        step(w)
     torch.cuda.synchronize()
+    nnz_all, mnnz_all = [], []
     t0 = time.perf_counter()
-    for _ in range(args.steps):
-        sc, rp, ci, nnz, mnnz = step()
+    for s_i in range(args.steps):
+        sc, rp, ci, nnz, mnnz = step(s_i)
+        nnz_all.append(nnz)
+        if mnnz is not None:
+            mnnz_all.append(mnnz)
     torch.cuda.synchronize()
     step_s = (time.perf_counter() - t0) / args.steps
+    # executed work of the timed steps (rows differ per call when the anchors rotate)
+    nnz_mean = sum(int(x.item()) for x in nnz_all) / len(nnz_all)
+    mnnz_mean = sum(int(x.item()) for x in mnnz_all) / len(mnnz_all) if mnnz_all else 0.0
+    exec_flops = 4 * d * (64 * 64 * nnz_mean + 16 * 16 * mnnz_mean)
+    # kernel-level figures below use the lists of the last step
     nnz_v = int(nnz.item())
     mnnz_v = int(mnnz.item()) if mnnz is not None else 0
     macro_flops = 4 * d * 64 * 64 * nnz_v
-    exec_flops = macro_flops + 4 * d * 16 * 16 * mnnz_v
     dense_flops = 4 * B * H * N * N * d
 
     # Kernel-level: the attention kernel alone (V^T already staged: V=None).
@@ -235,6 +251,18 @@ def main():
     attn_ms, _ = events_ms(
         lambda: bsa.bsa_sparse_attn_fwd(Q, K, None, rp, ci, out=O_buf, lse=L_buf, workspace=ws),
         reps, stream)
+    # Cold caches: a 512 MB write between reps evicts L2 and the Infinity Cache.
+    flush = torch.empty(FLUSH_BYTES // 4, dtype=torch.float32, device=dev)
+    cold = []
+    for _ in range(max(3, reps // 2)):
+        flush.zero_()
+        ms, _ = events_ms(
+            lambda: bsa.bsa_sparse_attn_fwd(Q, K, None, rp, ci, out=O_buf, lse=L_buf, workspace=ws),
+            1, stream)
+        cold.append(ms)
+    cold.sort()
+    attn_cold_ms = cold[len(cold) // 2]
+    del flush
     dense_ms, _ = events_ms(
         lambda: bsa.bsa_dense_attn_fwd(Q, K, None, out=O_buf, lse=L_buf, workspace=ws),
         max(3, reps // 2) if dense_flops < 2e13 else 3, stream)
@@ -287,9 +315,11 @@ def main():
         "data": "synthetic (seeded structured video Q/K/V)",
         "config": {"workload": c["name"], "B": B, "H": H, "N": N, "d": d, "block": 64,
                    "selection": sel_desc,
-                   "density": round(nnz_v / (B * H * nB * nB), 4)},
+                   "density": round(nnz_mean / (B * H * nB * nB), 4)},
         "attn_kernel_ms": round(attn_ms, 4),
         "attn_kernel_tflops": round(attn_tflops, 2),
+        "attn_kernel_ms_cold_cache": round(attn_cold_ms, 4),
+        "attn_kernel_tflops_cold_cache": round(macro_flops / (attn_cold_ms * 1e-3) / 1e12, 2),
         "pct_mfma_peak": round(100 * attn_tflops / PEAK_TFLOPS, 2),
         "dense_equiv_tflops": round(dense_flops / (attn_ms * 1e-3) / 1e12, 2),
         "dense_kernel_ms": round(dense_ms, 4),

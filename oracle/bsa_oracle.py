@@ -37,7 +37,9 @@ design notes of the repository):
     top-m per 64-row query block (parity unpinned against the pages: HyMoR
     gives no formula; it is pinned only against its own definition);
   * LSE is the natural log of the softmax normaliser with the scale inside;
-    an empty support yields LSE = -inf and O = 0.
+    an empty support yields LSE = -inf and O = 0;
+  * the omission risk of a query token is the share of its full softmax mass
+    outside its sparse support (HyMoR names the risk, not its formula).
 """
 
 from __future__ import annotations
@@ -332,6 +334,106 @@ def lse_merge(O1, L1, O2, L2):
     O = w1[:, None] * O1 + w2[:, None] * O2
     O[both_empty] = 0.0
     return O, L
+
+
+# ----------------------------------------------------------------------------
+# Omission risk ([HyMoR] offline risk calibration of layers and heads)
+#
+# Reading: the page states that the risk of omitting valuable support is
+# stable per layer and head and is calibrated offline, but gives no formula.
+# The risk of a query token here is the share of its full softmax mass that
+# falls on keys outside its sparse support; a repair (the Micro residual)
+# brings back the mass of the keys it adds.  A head's risk is the mean over
+# its valid tokens.
+# ----------------------------------------------------------------------------
+
+def softmax_mass_outside(q: np.ndarray, K: np.ndarray, keys: np.ndarray,
+                         scale: float) -> np.ndarray:
+    """For queries q [m,d] attending over ALL keys K [N,d], the softmax mass
+    on the keys NOT in the index set ``keys``:
+        w_t = sum_{tau not in keys} exp(z_t,tau) / sum_tau exp(z_t,tau),
+    z = scale q K^T (the full-attention distribution of each query)."""
+    z = scale * (np.asarray(q, np.float64) @ np.asarray(K, np.float64).T)
+    p = np.exp(z - z.max(axis=1, keepdims=True))
+    p /= p.sum(axis=1, keepdims=True)
+    outside = np.ones(K.shape[0], dtype=bool)
+    outside[np.asarray(keys, dtype=np.int64)] = False
+    return p[:, outside].sum(axis=1)
+
+
+def omitted_mass(Q, K, rows: list[list[int]], b: int, scale: float) -> np.ndarray:
+    """Per valid query token t of block i: the full-attention softmax mass of
+    t outside the tokens of the key blocks in row i (1 for an empty row)."""
+    Q = np.asarray(Q, np.float64)
+    N = Q.shape[0]
+    w = np.zeros(N)
+    for i, sel in enumerate(rows):
+        qi = block_tokens(N, b, i)
+        keys = (np.concatenate([block_tokens(N, b, j) for j in sel])
+                if len(sel) else np.zeros(0, dtype=np.int64))
+        w[qi] = softmax_mass_outside(Q[qi], K, keys, scale)
+    return w
+
+
+def micro_mass(Q, K, micro_rows: list[list[int]], b: int, u: int,
+               scale: float) -> np.ndarray:
+    """Per valid query token t of sub-tile a of block i: the full-attention
+    softmax mass of t on the union of the u-key tiles of its micro entries
+    (a, beta) -- the mass the Micro residual adds to the Macro support."""
+    Q = np.asarray(Q, np.float64)
+    N = Q.shape[0]
+    r = b // u
+    g = np.zeros(N)
+    for i, codes in enumerate(micro_rows):
+        for a in range(r):
+            qa = r * i + a
+            if qa * u >= N:
+                continue
+            qi = block_tokens(N, u, qa)
+            tiles = [c // r for c in codes if c % r == a]
+            if not tiles:
+                continue
+            keys = np.concatenate([block_tokens(N, u, t) for t in tiles])
+            g[qi] = 1.0 - softmax_mass_outside(Q[qi], K, keys, scale)
+    return g
+
+
+def risk_from_lse(L_sparse, L_full, L_repaired=None):
+    """Per-row omitted and recovered mass from log-sum-exps alone.  Since
+    e^L is the softmax normaliser over a support, the omitted share of a row
+    is 1 - e^(L_sparse - L_full) and the share a disjoint repair adds is
+    e^(L_repaired - L_full) - e^(L_sparse - L_full).  Rows whose full LSE is
+    -inf (no keys at all) count as 0 for both.  Returns (w, g); g is zeros
+    when no repaired LSE is given."""
+    Ls = np.asarray(L_sparse, np.float64)
+    Lf = np.asarray(L_full, np.float64)
+    empty = np.isneginf(Lf)
+    Lf_safe = np.where(empty, 0.0, Lf)
+    kept = np.where(np.isneginf(Ls), 0.0, np.exp(Ls - Lf_safe))
+    w = np.where(empty, 0.0, 1.0 - kept)
+    if L_repaired is None:
+        return w, np.zeros_like(w)
+    Lr = np.asarray(L_repaired, np.float64)
+    rep = np.where(np.isneginf(Lr), 0.0, np.exp(Lr - Lf_safe))
+    g = np.where(empty, 0.0, rep - kept)
+    return w, g
+
+
+def head_risk(w: np.ndarray, g: np.ndarray) -> tuple[float, float, float]:
+    """(mean omitted mass, largest omitted mass, mean recovered mass) over the
+    valid tokens of one head."""
+    w = np.asarray(w, np.float64)
+    g = np.asarray(g, np.float64)
+    if w.size == 0:
+        return 0.0, 0.0, 0.0
+    return float(w.mean()), float(w.max()), float(g.mean())
+
+
+def heads_at_risk(mean_omitted: np.ndarray, n: int) -> list[int]:
+    """The n heads of largest mean omitted mass (ties to the lower index),
+    ascending: the heads an offline calibration hands the Micro residual."""
+    order = sorted(range(len(mean_omitted)), key=lambda h: (-float(mean_omitted[h]), h))
+    return sorted(order[:max(0, n)])
 
 
 # ----------------------------------------------------------------------------

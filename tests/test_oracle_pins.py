@@ -344,6 +344,122 @@ def test_macro_plus_all_micro_equals_full_attention():
         Lf, scipy.special.logsumexp(s * Q @ K.T, axis=1), atol=1e-12)
 
 
+# ------------------------------------------------------------ omission risk
+
+def test_golden_omission_three_keys():
+    g = _load("omission_three_keys.json")
+    q, K = np.array(g["q"]), np.array(g["K"])
+    w = O.softmax_mass_outside(q, K, np.array(g["support"]), g["scale"])
+    np.testing.assert_allclose(w, [g["omitted"]], atol=1e-15)
+    rep = np.array(g["support"] + g["repair"])
+    w2 = O.softmax_mass_outside(q, K, rep, g["scale"])
+    np.testing.assert_allclose(w[0] - w2[0], g["recovered"], atol=1e-15)
+    wl, gl = O.risk_from_lse([g["LSE_sparse"]], [g["LSE_full"]], [g["LSE_repaired"]])
+    np.testing.assert_allclose(wl, [g["omitted"]], atol=1e-15)
+    np.testing.assert_allclose(gl, [g["recovered"]], atol=1e-15)
+
+
+def _risk_instance(seed=30, N=64 * 5 + 23, d=8):
+    s = 1 / math.sqrt(d)
+    Q, K, V = _rand(seed, N, d), _rand(seed + 1, N, d), _rand(seed + 2, N, d)
+    S = O.pooled_scores(O.pool_means(Q, 64), O.pool_means(K, 64), s)
+    rows = O.select_rows(S, N, 64, "topk", k=2)
+    rows[1] = []  # an empty row: everything omitted
+    return Q, K, V, rows, s
+
+
+def test_risk_from_lse_equals_mass_outside_the_support():
+    # the LSE form (normalisers of the two supports) against the mass summed
+    # key by key over the full-attention distribution
+    Q, K, V, rows, s = _risk_instance()
+    N = Q.shape[0]
+    w_def = O.omitted_mass(Q, K, rows, 64, s)
+    _, Ls = O.block_sparse_attention(Q, K, V, rows, 64, s)
+    _, Lf = O.dense_attention(Q, K, V, s)
+    w, g = O.risk_from_lse(Ls, Lf)
+    np.testing.assert_allclose(w, w_def, atol=1e-13)
+    assert np.all(g == 0)
+    assert np.all(w[64:128] == 1.0) and np.all((w >= 0) & (w <= 1))
+    # repair: the Micro residual over a few tiles of the omitted blocks
+    Qt, Kt = O.pool_means(Q, 16), O.pool_means(K, 16)
+    mrows = [O.micro_select_row(Qt, Kt, rows[i], i, N, 64, 16, s, 5)
+             for i in range(len(rows))]
+    _, Lu = O.micro_attention(Q, K, V, mrows, 64, 16, s)
+    _, Lr = O.lse_merge(np.zeros((N, 8)), Ls, np.zeros((N, 8)), Lu)
+    w, g = O.risk_from_lse(Ls, Lf, Lr)
+    np.testing.assert_allclose(g, O.micro_mass(Q, K, mrows, 64, 16, s), atol=1e-13)
+    assert np.all(g <= w + 1e-15) and np.any(g > 0)
+
+
+def test_risk_zero_query_closed_form():
+    # q = 0: every key weighs the same, so the omitted share of a token of
+    # block i is 1 - (tokens of its support) / N
+    N, b = 64 * 3 + 9, 64
+    Q, K = np.zeros((N, 4)), _rand(31, N, 4)
+    rows = [[0], [0, 2], [1, 3], [3]]
+    w = O.omitted_mass(Q, K, rows, b, 0.7)
+    sizes = O.block_sizes(N, b)
+    for i, sel in enumerate(rows):
+        want = 1 - sum(sizes[j] for j in sel) / N
+        np.testing.assert_allclose(w[O.block_tokens(N, b, i)], want, atol=1e-14)
+    Ls = np.array([math.log(sum(sizes[j] for j in rows[t // b])) for t in range(N)])
+    wl, _ = O.risk_from_lse(Ls, np.full(N, math.log(N)))
+    np.testing.assert_allclose(wl, w, atol=1e-14)
+
+
+def test_risk_full_support_all_micro_and_edges():
+    Q, K, V, rows, s = _risk_instance(seed=33)
+    N, nB = Q.shape[0], O.n_blocks(Q.shape[0], 64)
+    full = [list(range(nB))] * nB
+    np.testing.assert_allclose(O.omitted_mass(Q, K, full, 64, s), 0.0, atol=1e-14)
+    # every candidate tile as micro repair: the repair recovers all omitted mass
+    Qt, Kt = O.pool_means(Q, 16), O.pool_means(K, 16)
+    mrows = [O.micro_select_row(Qt, Kt, rows[i], i, N, 64, 16, s, 10 ** 6) for i in range(nB)]
+    np.testing.assert_allclose(O.micro_mass(Q, K, mrows, 64, 16, s),
+                               O.omitted_mass(Q, K, rows, 64, s), atol=1e-13)
+    # -inf conventions: empty support omits all, no keys at all counts 0
+    w, g = O.risk_from_lse([-math.inf, 0.5, -math.inf], [1.0, 0.5, -math.inf],
+                           [0.0, 0.5, -math.inf])
+    np.testing.assert_allclose(w, [1.0, 0.0, 0.0], atol=1e-15)
+    np.testing.assert_allclose(g, [math.exp(-1.0), 0.0, 0.0], atol=1e-15)
+
+
+def test_head_risk_and_heads_at_risk():
+    assert O.head_risk(np.array([0.1, 0.4, 0.1]), np.array([0.0, 0.3, 0.0])) == \
+        pytest.approx((0.2, 0.4, 0.1), abs=1e-15)
+    assert O.head_risk(np.zeros(0), np.zeros(0)) == (0.0, 0.0, 0.0)
+    risk = np.array([0.2, 0.5, 0.2, 0.9, 0.2])
+    assert O.heads_at_risk(risk, 2) == [1, 3]
+    assert O.heads_at_risk(risk, 3) == [0, 1, 3]   # tie at 0.2 -> lowest index
+    assert O.heads_at_risk(risk, 0) == []
+    assert O.heads_at_risk(risk, 9) == [0, 1, 2, 3, 4]
+
+
+@pytest.mark.parametrize("mistake", ["swap", "tail", "plain_exp"])
+def test_risk_pins_catch_planted_mistakes(mistake, monkeypatch):
+    """Plausible slips in the risk functions fail the pins above."""
+    g = _load("omission_three_keys.json")
+    if mistake == "swap":
+        real = O.risk_from_lse
+        monkeypatch.setattr(O, "risk_from_lse", lambda a, b, c=None: real(b, a, c))
+        w, _ = O.risk_from_lse([g["LSE_sparse"]], [g["LSE_full"]])
+        assert abs(w[0] - g["omitted"]) > 1e-3
+    elif mistake == "tail":
+        monkeypatch.setattr(O, "block_tokens",
+                            lambda N_, b_, j: np.arange(b_ * j, min(b_ * j + b_, N_ - 1)))
+        N, b = 64 * 3 + 9, 64
+        Q, K = np.zeros((N, 4)), _rand(31, N, 4)
+        w = O.omitted_mass(Q, K, [[0], [0, 3], [1, 3], [3]], b, 0.7)
+        assert abs(w[64] - (1 - (64 + 9) / N)) > 1e-3
+    else:
+        # mass from exp(z) without the normaliser of the full distribution
+        monkeypatch.setattr(O, "softmax_mass_outside", lambda q, K, keys, sc: 1.0 - np.exp(
+            sc * np.asarray(q) @ np.asarray(K)[np.asarray(keys, int)].T).sum(axis=1))
+        w = O.softmax_mass_outside(np.array(g["q"]), np.array(g["K"]),
+                                   np.array(g["support"]), g["scale"])
+        assert abs(w[0] - g["omitted"]) > 1e-3
+
+
 def test_flop_accounting():
     assert O.executed_flops(128, 64, 1) == 4 * 128 * 64 * 64
     assert O.dense_flops(1, 12, 32760, 128) == 4 * 12 * 32760 ** 2 * 128
