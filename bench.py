@@ -263,9 +263,11 @@ def main():
     cold.sort()
     attn_cold_ms = cold[len(cold) // 2]
     del flush
+    L_sparse = L_buf.clone()
     dense_ms, _ = events_ms(
         lambda: bsa.bsa_dense_attn_fwd(Q, K, None, out=O_buf, lse=L_buf, workspace=ws),
         max(3, reps // 2) if dense_flops < 2e13 else 3, stream)
+    L_full = L_buf.clone()
     score_ms, _ = events_ms(score, reps, stream) if mode != "static" else (0.0, None)
     select_ms, _ = events_ms(lambda: select(sc), reps, stream)
     attn_v_ms, _ = events_ms(
@@ -296,6 +298,31 @@ def main():
         rows_m = B * len(micro["heads"]) * N
         gbs["lse_merge"] = round(rows_m * (3 * d * 4 + 12) / (merge_ms * 1e-3) / 1e9, 1)
         stages["micro_tflops"] = round(4 * d * 256 * mnnz_v / (mattn_ms * 1e-3) / 1e12, 2)
+
+    # Offline head calibration: omitted softmax share per head (sparse vs full
+    # attention) and, with the micro residual, the share it brings back.
+    L_rep = None
+    if micro is not None:
+        L_rep = L_sparse.clone()
+        bsa.bsa_lse_merge(O_buf, L_sparse, Om_buf, Lm_buf, head_mask=micro["mask"],
+                          out=O_buf, lse_out=L_rep)
+    risk = bsa.bsa_omission_risk(L_sparse, L_full, L_rep)
+    risk_ms, _ = events_ms(lambda: bsa.bsa_omission_risk(L_sparse, L_full, L_rep, out=risk),
+                           reps, stream)
+    risk_h = risk[0].cpu()
+    mean_w = [round(float(x), 5) for x in risk_h[:, 0]]
+    risk_out = {"kernel_ms": round(risk_ms, 4),
+                "gbs": round(B * H * N * (12 if L_rep is not None else 8)
+                             / (risk_ms * 1e-3) / 1e9, 1),
+                "mean_omitted_share_per_head": mean_w,
+                "max_omitted_share": round(float(risk_h[:, 1].max()), 5)}
+    if micro is not None:
+        mh = micro["heads"]
+        omitted = sum(float(risk_h[h, 0]) for h in mh)
+        risk_out["micro_recovered_share"] = round(
+            sum(float(risk_h[h, 2]) for h in mh) / omitted, 5) if omitted > 0 else None
+        risk_out["heads_at_risk"] = bsa.heads_at_risk(mean_w, len(mh))
+        risk_out["micro_heads"] = list(mh)
 
     attn_tflops = macro_flops / (attn_ms * 1e-3) / 1e12
     kernel_src = os.path.join(ROOT, "block_sparse_attention_pool_amd", "csrc", "attn.hip")
@@ -328,6 +355,7 @@ def main():
         "pipeline_speedup_vs_dense": round(dense_ms / (step_s * 1e3), 3),
         "stages_ms": stages,
         "stage_gbs": gbs,
+        "omission_risk": risk_out,
         "roofline": {"bound": "mfma", "achieved": round(attn_tflops, 2), "peak": PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(attn_tflops / PEAK_TFLOPS, 4),
                      "traffic": traffic},

@@ -5,7 +5,7 @@ torch (device memory and streams are all torch is used for), passes raw
 pointers and sizes to the C entry point of the same name declared in
 ``include/bsa.h``, and raises on a non-zero status.  All computation runs in
 the HIP kernels of the library.  The library must have been built
-(``python -m block_sparse_attention_pool_amd.build``); importing this module
+(``python block_sparse_attention_pool_amd/build.py``); importing this module
 fails loudly when it is missing.
 
 Tensors Q, K, V are bf16 ``[B, H, N, d]`` on the GPU with the last dimension
@@ -56,7 +56,7 @@ def _load(path: str = _LIB_PATH):
     if not os.path.exists(path):
         raise ImportError(
             f"{path} is missing: build it with "
-            "`python -m block_sparse_attention_pool_amd.build` (hipcc, gfx950)")
+            "`python block_sparse_attention_pool_amd/build.py` (hipcc, gfx950)")
     lib = ctypes.CDLL(path)
     P, I32, I64, F32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float
     SP = ctypes.POINTER(_Shape)
@@ -74,6 +74,8 @@ def _load(path: str = _LIB_PATH):
         "bsa_micro_residual_fwd": ([P, P, P, SP, I32, I32, F32, P, P, P, P, I32, P, P, I64, P],
                                    I32),
         "bsa_lse_merge": ([P, P, P, P, SP, I32, P, P, P, P], I32),
+        "bsa_omission_risk_workspace_bytes": ([SP], I64),
+        "bsa_omission_risk": ([P, P, P, SP, P, P, I64, P], I32),
     }
     for name, (args, res) in sig.items():
         fn = getattr(lib, name)
@@ -86,7 +88,7 @@ _lib = _load()
 EXPORTED = ("bsa_version", "bsa_last_error", "bsa_score_blocks", "bsa_select_workspace_bytes",
             "bsa_select_max_nnz", "bsa_select_blocks", "bsa_attn_workspace_bytes",
             "bsa_sparse_attn_fwd", "bsa_dense_attn_fwd", "bsa_micro_residual_fwd",
-            "bsa_lse_merge")
+            "bsa_lse_merge", "bsa_omission_risk_workspace_bytes", "bsa_omission_risk")
 
 
 def library_path() -> str:
@@ -337,6 +339,39 @@ def bsa_lse_merge(O1, L1, O2, L2, *, head_mask=None, out=None, lse_out=None, str
                             _odt(O1.dtype), hm, _ptr(O), _ptr(L), _stream(stream, O1.device))
     _check(st, "bsa_lse_merge")
     return O, L
+
+
+def bsa_omission_risk(lse_sparse, lse_full, lse_repaired=None, *, out=None, stream=None):
+    """Per-head omission risk from the LSE of a sparse pass, of full
+    attention and (optionally) of the repaired pass.  Returns float64
+    [B, H, 3] on the device: mean omitted share, largest omitted share and
+    mean recovered share over the N rows of each head."""
+    for t in (lse_sparse, lse_full, lse_repaired):
+        if t is not None and (t.dtype != torch.float32 or t.dim() != 3 or not t.is_contiguous()
+                              or t.shape != lse_sparse.shape):
+            raise ValueError("LSE arrays must be contiguous float32 [B, H, N] of one shape")
+    B, H, N = lse_sparse.shape
+    shp = _Shape(B, H, N, 0, 0, 0, 0)
+    n = _lib.bsa_omission_risk_workspace_bytes(ctypes.byref(shp))
+    if n < 0:
+        raise BsaError(f"bsa_omission_risk_workspace_bytes: {bsa_last_error()}")
+    dev = lse_sparse.device
+    ws = torch.empty(max(n, 256), dtype=torch.uint8, device=dev)
+    risk = torch.empty((B, H, 3), dtype=torch.float64, device=dev) if out is None else out
+    st = _lib.bsa_omission_risk(_ptr(lse_sparse), _ptr(lse_full), _ptr(lse_repaired),
+                                ctypes.byref(shp), _ptr(risk), _ptr(ws), ws.numel(),
+                                _stream(stream, dev))
+    _check(st, "bsa_omission_risk")
+    return risk
+
+
+def heads_at_risk(mean_omitted, n: int) -> list[int]:
+    """Offline calibration: the ``n`` heads with the largest mean omitted
+    share (equal values go to the lower head index), in ascending order --
+    the head set handed to the Micro residual."""
+    vals = [float(v) for v in mean_omitted]
+    ranked = sorted(range(len(vals)), key=lambda h: (-vals[h], h))
+    return sorted(ranked[:max(0, n)])
 
 
 def csr_rows(row_ptr: torch.Tensor, col_idx: torch.Tensor, nnz: torch.Tensor):

@@ -1,6 +1,6 @@
 """Build the gfx950 HIP library ``_lib/libbsa.so`` in-tree with hipcc.
 
-    python -m block_sparse_attention_pool_amd.build
+    python block_sparse_attention_pool_amd/build.py
 
 Each ``csrc/*.hip`` file is compiled in parallel to a position-independent
 object, then linked into one shared library.  The build always recompiles.

@@ -65,6 +65,18 @@ bsa_status check_ptr(const void* p, const char* name, uintptr_t align = 16) {
     if (_st != BSA_OK) return _st;      \
   } while (0)
 
+// The omission-risk reduction reads only B, H and N (LSE arrays are
+// contiguous [B, H, N]); heads map to grid rows, at most 65535 of them.
+bsa_status check_risk_shape(const bsa_shape* s, int64_t* chunks) {
+  if (s == nullptr) return fail(BSA_ERR_INVALID_ARG, "shape is NULL");
+  if (s->B < 1 || s->H < 1 || s->N < 1)
+    return fail(BSA_ERR_INVALID_ARG, "shape B=%d H=%d N=%d must all be >= 1", s->B, s->H, s->N);
+  const int64_t bh = (int64_t)s->B * s->H;
+  if (bh > 65535) return fail(BSA_ERR_UNSUPPORTED, "B*H=%lld exceeds 65535", (long long)bh);
+  *chunks = cdiv(s->N, bsa::kRiskRowsPerChunk);
+  return BSA_OK;
+}
+
 bsa::HeadList all_heads(int H) {
   bsa::HeadList l;
   l.n = H;
@@ -487,6 +499,38 @@ bsa_status bsa_lse_merge(const void* O1, const float* L1, const void* O2, const 
   a.heads = heads;
   return hip_status(bsa::launch_merge(a, shape->B, o_dtype == BSA_BF16, (hipStream_t)stream),
                     "merge launch");
+}
+
+int64_t bsa_omission_risk_workspace_bytes(const bsa_shape* shape) {
+  int64_t chunks = 0;
+  if (check_risk_shape(shape, &chunks) != BSA_OK) return -1;
+  return align256((int64_t)shape->B * shape->H * chunks * 3 * 8);
+}
+
+bsa_status bsa_omission_risk(const float* lse_sparse, const float* lse_full,
+                             const float* lse_repaired, const bsa_shape* shape, double* risk,
+                             void* workspace, int64_t workspace_bytes, void* stream) {
+  int64_t chunks = 0;
+  BSA_TRY(check_risk_shape(shape, &chunks));
+  BSA_TRY(check_ptr(lse_sparse, "lse_sparse", 4));
+  BSA_TRY(check_ptr(lse_full, "lse_full", 4));
+  if (lse_repaired != nullptr) BSA_TRY(check_ptr(lse_repaired, "lse_repaired", 4));
+  BSA_TRY(check_ptr(risk, "risk", 8));
+  BSA_TRY(check_ptr(workspace, "workspace", 8));
+  const int64_t need = bsa_omission_risk_workspace_bytes(shape);
+  if (workspace_bytes < need)
+    return fail(BSA_ERR_CAPACITY, "workspace %lld bytes < %lld required",
+                (long long)workspace_bytes, (long long)need);
+  bsa::RiskArgs a{};
+  a.Ls = lse_sparse;
+  a.Lf = lse_full;
+  a.Lr = lse_repaired;
+  a.partial = (double*)workspace;
+  a.risk = risk;
+  a.N = shape->N;
+  a.chunks = (int)chunks;
+  a.BH = shape->B * shape->H;
+  return hip_status(bsa::launch_risk(a, (hipStream_t)stream), "omission risk launch");
 }
 
 }  // extern "C"

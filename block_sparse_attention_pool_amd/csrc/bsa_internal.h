@@ -105,6 +105,18 @@ struct MergeArgs {
   HeadList heads;
 };
 
+// Omission risk: rows of one head are reduced in chunks of kRiskRowsPerChunk.
+constexpr int kRiskRowsPerChunk = 2048;
+
+struct RiskArgs {
+  const float* Ls;  // [BH, N] sparse-support LSE
+  const float* Lf;  // [BH, N] full-attention LSE
+  const float* Lr;  // [BH, N] repaired LSE, or null
+  double* partial;  // [BH, chunks, 3] workspace
+  double* risk;     // [BH, 3]
+  int N, chunks, BH;
+};
+
 hipError_t launch_pool(const PoolArgs& a, int B, hipStream_t s);
 hipError_t launch_score_gemm(const GemmArgs& a, int nbatch, hipStream_t s);
 hipError_t launch_fill_i32(int32_t* p, int64_t n, int32_t v, hipStream_t s);
@@ -125,5 +137,6 @@ hipError_t launch_attn(const AttnArgs& a, int D, bool dense, bool out_bf16,
 hipError_t launch_micro_attn(const MicroAttnArgs& a, int B, int D,
                              bool out_bf16, hipStream_t s);
 hipError_t launch_merge(const MergeArgs& a, int B, bool bf16, hipStream_t s);
+hipError_t launch_risk(const RiskArgs& a, hipStream_t s);
 
 }  // namespace bsa

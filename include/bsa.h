@@ -12,6 +12,8 @@
  *   bsa_micro_residual_fwd attention over the selected 16x16 micro tiles;
  *   bsa_lse_merge         exact merge of two partial softmax results.
  *   bsa_dense_attn_fwd    the same attention engine over every key (baseline).
+ *   bsa_omission_risk     per-head share of the full softmax mass a sparse
+ *                         support omits (offline head calibration).
  *
  * Conventions shared by every entry point
  * ---------------------------------------
@@ -262,6 +264,36 @@ bsa_status bsa_lse_merge(const void* O1, const float* L1, const void* O2,
                          const float* L2, const bsa_shape* shape,
                          int32_t o_dtype, const uint8_t* head_mask, void* O,
                          float* L, void* stream);
+
+/* ------------------------------------------------------------------------
+ * bsa_omission_risk -- per-head omission risk of a sparse support.  The
+ * HyMoR-Attn abstract finds the risk of omitting valuable support stable per
+ * layer and head and calibrates it offline to pick the heads that get the
+ * Micro residual; it gives no formula.  Reading used here: the risk of a
+ * query row is the share of its full softmax mass outside its support,
+ *   w = 1 - exp(LSE_sparse - LSE_full),
+ * and a repair over a disjoint support (the Micro residual merged by
+ * bsa_lse_merge) brings back
+ *   g = exp(LSE_repaired - LSE_full) - exp(LSE_sparse - LSE_full).
+ * Rows whose LSE_full is -inf count 0 for both; an empty support
+ * (LSE_sparse = -inf) has w = 1.
+ *
+ * lse_sparse, lse_full: float32 [B, H, N] (bsa_sparse_attn_fwd and
+ *   bsa_dense_attn_fwd on the same Q, K); lse_repaired: float32 [B, H, N]
+ *   or NULL (then g = 0).  Only B, H and N of `shape` are read; B*H must be
+ *   at most 65535.
+ * risk: float64 [B, H, 3]: mean of w over the N rows, largest w, mean of g.
+ *   Per-row shares are computed in float32 (expm1 forms), sums in float64
+ *   in a fixed order (deterministic).
+ * workspace: device, >= bsa_omission_risk_workspace_bytes(shape) bytes,
+ *   8-byte aligned; its contents on entry do not matter.
+ * ---------------------------------------------------------------------- */
+int64_t bsa_omission_risk_workspace_bytes(const bsa_shape* shape);
+
+bsa_status bsa_omission_risk(const float* lse_sparse, const float* lse_full,
+                             const float* lse_repaired, const bsa_shape* shape,
+                             double* risk, void* workspace,
+                             int64_t workspace_bytes, void* stream);
 
 #ifdef __cplusplus
 }

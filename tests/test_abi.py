@@ -15,7 +15,11 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 def _ensure_built():
     lib = os.path.join(ROOT, "block_sparse_attention_pool_amd", "_lib", "libbsa.so")
     if not os.path.exists(lib):
-        from block_sparse_attention_pool_amd import build as b
+        import importlib.util
+        path = os.path.join(ROOT, "block_sparse_attention_pool_amd", "build.py")
+        spec = importlib.util.spec_from_file_location("bsa_build", path)
+        b = importlib.util.module_from_spec(spec)
+        spec.loader.exec_module(b)
         b.build()
     return lib
 
@@ -141,3 +145,36 @@ def test_budget_resolution():
     assert bsa.budget_blocks(0.15, 1857) == 279
     assert bsa.cap_blocks(0.20, 1182) == 236
     assert bsa.budget_blocks(0.1, 30) == 3
+
+
+def test_omission_risk_validation_and_workspace():
+    s = _shape(B=2, H=3, N=5000)
+    chunks = -(-5000 // 2048)
+    need = bsa._lib.bsa_omission_risk_workspace_bytes(ctypes.byref(s))
+    assert need == -(-(2 * 3 * chunks * 24) // 256) * 256
+    p = ctypes.c_void_p(4096)
+    st = bsa._lib.bsa_omission_risk(p, p, None, ctypes.byref(s), p, p, need - 1, None)
+    assert st == 3 and "workspace" in bsa.bsa_last_error()
+    st = bsa._lib.bsa_omission_risk(None, p, None, ctypes.byref(s), p, p, need, None)
+    assert st == 1 and "lse_sparse is NULL" in bsa.bsa_last_error()
+    st = bsa._lib.bsa_omission_risk(p, p, ctypes.c_void_p(4098), ctypes.byref(s), p, p, need,
+                                    None)
+    assert st == 1 and "lse_repaired" in bsa.bsa_last_error()
+    st = bsa._lib.bsa_omission_risk(p, p, None, ctypes.byref(s), ctypes.c_void_p(4100), p, need,
+                                    None)
+    assert st == 1 and "risk" in bsa.bsa_last_error()
+    # only B, H, N are read: any d is accepted; too many heads is refused
+    assert bsa._lib.bsa_omission_risk_workspace_bytes(ctypes.byref(_shape(d=96))) > 0
+    assert bsa._lib.bsa_omission_risk_workspace_bytes(ctypes.byref(_shape(B=300, H=256))) == -1
+    assert "65535" in bsa.bsa_last_error()
+    assert bsa._lib.bsa_omission_risk_workspace_bytes(ctypes.byref(_shape(N=0))) == -1
+
+
+def test_heads_at_risk_matches_the_oracle_rule():
+    import numpy as np
+    from oracle import bsa_oracle as O
+    rng = np.random.default_rng(5)
+    for H in (1, 7, 24, 40):
+        risk = np.round(rng.random(H), 1)   # coarse values: many ties
+        for n in (0, 1, H // 3, H, H + 2):
+            assert bsa.heads_at_risk(risk, n) == O.heads_at_risk(risk, n)
