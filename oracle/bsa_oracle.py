@@ -22,8 +22,10 @@ Sources (pages as titled):
   [LVSA]  "Long Video Sparse Attention" abstract (page titled "FreqFormer ..."):
           structured window pattern plus rotating global anchors.
   [MOD]   "Mixture of Distributions Matters: Dynamic Sparse Attention for
-          Efficient Video Diffusion Transformers", Metrics (density = computed
-          B x B blocks / total) and Block-wise Attention Computation.
+          Efficient Video Diffusion Transformers", Pattern Mixtures (the
+          parallel-diagonal, vertical and block-diagonal bases), Metrics
+          (density = computed B x B blocks / total) and Block-wise Attention
+          Computation (block size 128).
 
 Readings where the pages are silent (each one is listed with its reason in the
 design notes of the repository):
@@ -38,6 +40,11 @@ design notes of the repository):
     gives no formula; it is pinned only against its own definition);
   * LSE is the natural log of the softmax normaliser with the scale inside;
     an empty support yields LSE = -inf and O = 0;
+  * [MOD]'s parallel-diagonal offsets delta_k = k - n + 1 are read with
+    k = 0 .. 2n-2, i.e. all 2n-1 diagonals -(n-1) .. n-1 of the n x n block
+    map (the page's 1-based k would start at 2-n and end off the map);
+  * a 128-token block selection is executed on 64-token tiles: every kept
+    128 x 128 pair is its 2 x 2 tiles, the token support unchanged;
   * the omission risk of a query token is the share of its full softmax mass
     outside its sparse support (HyMoR names the risk, not its formula).
 """
@@ -170,15 +177,53 @@ def window_anchor_set(N: int, b: int, i: int, frame_tokens: int,
     return out
 
 
+def pattern_set(nB: int, i: int, diagonals=(), columns=()) -> set[int]:
+    """Key blocks of query block i under a chosen set of [MOD] structural
+    patterns (Pattern Mixtures): a parallel-diagonal pattern of offset delta
+    marks block (i, i + delta) of the n x n block map (inter-frame temporal
+    continuity); a vertical pattern marks one key column j for every query
+    block (global anchors / sinks).  The mask of several patterns is their
+    union; offsets that fall off the map mark nothing."""
+    out = set()
+    for delta in diagonals:
+        j = i + int(delta)
+        if 0 <= j < nB:
+            out.add(j)
+    for j in columns:
+        if not 0 <= int(j) < nB:
+            raise ValueError(f"column {j} outside [0, {nB})")
+        out.add(int(j))
+    return out
+
+
+def expand_rows(rows: list[list[int]], N: int, b_from: int, b_to: int) -> list[list[int]]:
+    """Rows over b_from-token blocks re-expressed over b_to-token blocks
+    (b_from a multiple of b_to): query block i' takes the row of its
+    enclosing block i' // r (r = b_from / b_to) and every key block J becomes
+    the valid blocks r J .. r J + r - 1.  The token support of every query is
+    unchanged."""
+    r = b_from // b_to
+    assert r * b_to == b_from
+    n_to = n_blocks(N, b_to)
+    out = []
+    for i2 in range(n_to):
+        src = rows[i2 // r]
+        out.append(sorted(r * J + e for J in src for e in range(r) if r * J + e < n_to))
+    return out
+
+
 def select_rows(scores: np.ndarray | None, N: int, b: int, mode: str, *,
                 k: int = 0, p: float = 0.9, k_min: int = 1,
                 k_cap: int | None = None, force_diag: bool = False,
-                static: dict | None = None) -> list[list[int]]:
+                static: dict | None = None,
+                patterns: dict | None = None) -> list[list[int]]:
     """Per query block, the ascending list of selected key blocks for one head.
 
-    ``mode`` is "topk", "topp" or "static".  The forced set (the diagonal
-    and/or the [LVSA] window+anchors ``static`` mask) is a union on top of the
-    scored selection.
+    ``mode`` is "topk", "topp" or "static".  The forced set (the diagonal,
+    the [LVSA] window+anchors ``static`` mask and the [MOD] ``patterns``
+    {"diagonals": offsets, "columns": key blocks}) is a union on top of the
+    scored selection.  ``b`` is the block of the selection (64 or 128 in the
+    library; the [MOD] block-wise attention uses 128).
     """
     nB = n_blocks(N, b)
     sizes = block_sizes(N, b)
@@ -196,6 +241,9 @@ def select_rows(scores: np.ndarray | None, N: int, b: int, mode: str, *,
             sel.add(i)
         if static is not None:
             sel |= window_anchor_set(N, b, i, **static)
+        if patterns is not None:
+            sel |= pattern_set(nB, i, patterns.get("diagonals", ()),
+                               patterns.get("columns", ()))
         rows.append(sorted(sel))
     return rows
 

@@ -197,6 +197,106 @@ def test_static_anchor_rotation_and_density_at_long_horizon():
     assert 75 < avg < 82  # about 2.5% of 3072 blocks
 
 
+# ------------------------------------------------ MOD patterns and block 128
+
+def _basis_C(n):
+    """The 2n-1 parallel-diagonal basis matrices: numpy's eye with a diagonal
+    offset puts ones at (i, i + offset)."""
+    return {k - n + 1: np.eye(n, k=k - n + 1, dtype=np.int64) for k in range(2 * n - 1)}
+
+
+def test_parallel_diagonal_basis_partitions_the_block_map():
+    n = 7
+    C = _basis_C(n)
+    assert len(C) == 2 * n - 1 and all(M.sum() > 0 for M in C.values())
+    np.testing.assert_array_equal(sum(C.values()), np.ones((n, n), dtype=np.int64))
+
+
+def test_pattern_set_equals_union_of_basis_matrices():
+    rng = np.random.default_rng(40)
+    for n in (1, 5, 13):
+        C = _basis_C(n)
+        for trial in range(6):
+            diags = sorted(set(rng.integers(-(n + 1), n + 2, size=3).tolist()))
+            cols = sorted(set(rng.integers(0, n, size=2).tolist()))
+            M = np.zeros((n, n), dtype=np.int64)
+            for dlt in diags:
+                if dlt in C:
+                    M |= C[dlt]
+            for j in cols:
+                D = np.zeros((n, n), dtype=np.int64)
+                D[:, j] = 1          # vertical basis: one key column for every query
+                M |= D
+            for i in range(n):
+                assert O.pattern_set(n, i, diags, cols) == set(np.nonzero(M[i])[0].tolist())
+    with pytest.raises(ValueError):
+        O.pattern_set(4, 0, (), (4,))
+
+
+def test_pattern_pin_catches_a_flipped_offset(monkeypatch):
+    real = O.pattern_set
+    monkeypatch.setattr(O, "pattern_set",
+                        lambda n, i, diagonals=(), columns=(): real(n, i, [-x for x in diagonals],
+                                                                   columns))
+    n, C = 6, _basis_C(6)
+    assert any(O.pattern_set(n, i, [2], []) != set(np.nonzero(C[2][i])[0].tolist())
+               for i in range(n))
+
+
+def test_intra_frame_block_diagonal_matches_token_level_definition():
+    # block (i, j) is in the block-diagonal support iff some query token of i
+    # and key token of j share a frame: the window of radius 0, no anchors
+    N, ft = 64 * 7 + 13, 150
+    for b in (64, 128):
+        nB = O.n_blocks(N, b)
+        for i in range(nB):
+            fi = {int(t) // ft for t in O.block_tokens(N, b, i)}
+            want = {j for j in range(nB)
+                    if fi & {int(t) // ft for t in O.block_tokens(N, b, j)}}
+            assert O.window_anchor_set(N, b, i, ft, 0, 0, 0) == want
+
+
+def test_select_rows_with_patterns_is_a_union():
+    N, b, s = 64 * 9 + 7, 64, 0.3
+    Q, K = _rand(41, N, 8), _rand(42, N, 8)
+    S = O.pooled_scores(O.pool_means(Q, b), O.pool_means(K, b), s)
+    pats = dict(diagonals=[-3, 0, 4], columns=[1, 9])
+    base = O.select_rows(S, N, b, "topk", k=2)
+    got = O.select_rows(S, N, b, "topk", k=2, patterns=pats)
+    for i in range(len(base)):
+        assert set(got[i]) == set(base[i]) | O.pattern_set(len(base), i, **pats)
+
+
+def test_block128_expansion_keeps_the_token_support():
+    N, d = 128 * 4 + 70, 8          # 5 blocks of 128 (tail 70), 10 blocks of 64 (tail 6)
+    s = 1 / math.sqrt(d)
+    Q, K, V = _rand(43, N, d), _rand(44, N, d), _rand(45, N, d)
+    S = O.pooled_scores(O.pool_means(Q, 128), O.pool_means(K, 128), s)
+    rows128 = O.select_rows(S, N, 128, "topk", k=2, patterns=dict(diagonals=[1]))
+    rows64 = O.expand_rows(rows128, N, 128, 64)
+    assert len(rows64) == O.n_blocks(N, 64) == 10
+    # token-level supports are identical for every query token
+    for t in range(N):
+        sup128 = {int(x) for J in rows128[t // 128] for x in O.block_tokens(N, 128, J)}
+        sup64 = {int(x) for j in rows64[t // 64] for x in O.block_tokens(N, 64, j)}
+        assert sup128 == sup64
+    Oa, La = O.block_sparse_attention(Q, K, V, rows128, 128, s)
+    Ob, Lb = O.block_sparse_attention(Q, K, V, rows64, 64, s)
+    np.testing.assert_allclose(Oa, Ob, atol=1e-12)
+    np.testing.assert_allclose(La, Lb, atol=1e-12)
+
+
+def test_pooled_score_at_block128_is_mean_of_token_logits():
+    N, b, d, s = 128 * 2 + 33, 128, 6, 0.4
+    Q, K = _rand(46, N, d), _rand(47, N, d)
+    S = O.pooled_scores(O.pool_means(Q, b), O.pool_means(K, b), s)
+    for i in range(O.n_blocks(N, b)):
+        for j in range(O.n_blocks(N, b)):
+            ti, tj = O.block_tokens(N, b, i), O.block_tokens(N, b, j)
+            want = sum(s * float(Q[a] @ K[c]) for a in ti for c in tj) / (len(ti) * len(tj))
+            assert abs(S[i, j] - want) < 1e-11
+
+
 # --------------------------------------------------------------- attention
 
 def test_golden_attention_two_keys():
