@@ -55,6 +55,13 @@ def parse():
                          "3 hunyuanvideo-720p, 4 long-horizon static window")
     ap.add_argument("--window-frames", type=int, default=None,
                     help="static window radius in frames (workload 4; default: the literal 1)")
+    ap.add_argument("--block", type=int, default=64, choices=(64, 128),
+                    help="selection block in tokens (128: MOD-DiT's block-wise size; the "
+                         "attention still runs 64-token tiles)")
+    ap.add_argument("--mod-mask", action="store_true",
+                    help="replace the workload's selection by a fixed MOD-DiT-style structural "
+                         "mask: intra-frame block-diagonal, temporal diagonals at 1 and 2 "
+                         "frames, 4 vertical columns")
     ap.add_argument("--calibration-copy", action="store_true",
                     help="first run a plain 256 MiB device copy (reads 256 MiB, writes "
                          "256 MiB) three times, to scale hardware byte counters")
@@ -141,7 +148,7 @@ def main():
 
     import torch
     import block_sparse_attention_pool_amd as bsa
-    from synth import CONFIGS, config_spec, gen_qkv, micro_heads, rotation_offset
+    from synth import CONFIGS, config_spec, gen_qkv, micro_heads, mod_pattern_mask, rotation_offset
 
     if args.calibration_copy:
         src = torch.ones(64 << 20, dtype=torch.float32, device="cuda:0")
@@ -158,14 +165,19 @@ def main():
     dev = torch.device("cuda:0")
     Q, K, V = (x.to(dev) for x in (Qc, Kc, Vc))
     B, H, N, d = Q.shape
-    nB = bsa.n_blocks(N)
+    blk = args.block
+    nB = bsa.n_blocks(N, blk)      # selection blocks
     scale = 1.0 / math.sqrt(d)
     stream = torch.cuda.current_stream(dev)
-    mode = c["mode"]
+    mode = "static" if args.mod_mask else c["mode"]
 
     # selection parameters of the workload
     sel = {}
-    if mode == "topk":
+    if args.mod_mask:
+        sel = mod_pattern_mask(spec, blk)
+        sel_desc = (f"MOD-style mask: intra-frame + diagonals {sel['patterns']['diagonals']} + "
+                    f"columns {sel['patterns']['columns']}")
+    elif mode == "topk":
         k = bsa.budget_blocks(c["density"], nB)
         sel = dict(k=k, force_diag=c.get("force_diag", False))
         sel_desc = f"top-k {c['density']:.0%} (k={k} of {nB})" + (" + diagonal" if sel["force_diag"] else "")
@@ -179,6 +191,8 @@ def main():
                                n_anchors=c["n_anchors"], anchor_offset=rotation_offset(cfg, 0, nB)))
         sel_desc = (f"static window +-{wf} frames + {c['n_anchors']} anchors rotating over "
                     f"{N_ROTATIONS} offsets")
+    if blk != 64:
+        sel_desc += f"; {blk}-token selection blocks on 64-token tiles"
     micro = None
     if "micro_head_frac" in c or "micro_m" in c:
         heads = micro_heads(cfg)
@@ -194,15 +208,16 @@ def main():
         Lm_buf = torch.empty_like(L_buf)
 
     def score():
-        return bsa.bsa_score_blocks(Q, K, scores=(mode != "static"), micro=16 if micro else 0)
+        return bsa.bsa_score_blocks(Q, K, block=blk, scores=(mode != "static"),
+                                    micro=16 if micro else 0)
 
     offsets = [rotation_offset(cfg, call, nB) for call in range(N_ROTATIONS)]
 
     def select(sc, call=0):
-        if mode == "static":
+        if mode == "static" and not args.mod_mask:
             # the anchors rotate: each call draws its own offset
             sel["static"]["anchor_offset"] = offsets[call % N_ROTATIONS]
-        return bsa.bsa_select_blocks(sc["scores"], Q, mode=mode, **sel)
+        return bsa.bsa_select_blocks(sc["scores"], Q, block=blk, mode=mode, **sel)
 
     def micro_select(sc, rp, ci):
         return bsa.bsa_select_blocks(
@@ -212,7 +227,7 @@ def main():
 
     def step(call=0):
         # the static window needs no scores: the selection runs on the mask alone
-        sc = score() if mode != "static" else {"scores": None}
+        sc = score() if (mode != "static" or micro) else {"scores": None}
         rp, ci, nnz = select(sc, call)
         bsa.bsa_sparse_attn_fwd(Q, K, V, rp, ci, out=O_buf, lse=L_buf, workspace=ws)
         mnnz = None
@@ -326,7 +341,8 @@ def main():
 
     attn_tflops = macro_flops / (attn_ms * 1e-3) / 1e12
     kernel_src = os.path.join(ROOT, "block_sparse_attention_pool_amd", "csrc", "attn.hip")
-    traffic = traffic_entry(kernel_src) if cfg == 1 else None
+    # the committed counters were taken on the default workload and selection
+    traffic = traffic_entry(kernel_src) if (cfg == 1 and blk == 64 and not args.mod_mask) else None
     out = {
         "metric": METRIC,
         "value": round(exec_flops / step_s / 1e12, 2),
@@ -340,9 +356,10 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic (seeded structured video Q/K/V)",
-        "config": {"workload": c["name"], "B": B, "H": H, "N": N, "d": d, "block": 64,
+        "config": {"workload": c["name"] + ("+mod-mask" if args.mod_mask else ""),
+                   "B": B, "H": H, "N": N, "d": d, "block": blk,
                    "selection": sel_desc,
-                   "density": round(nnz_mean / (B * H * nB * nB), 4)},
+                   "density": round(nnz_mean / (B * H * bsa.n_blocks(N) ** 2), 4)},
         "attn_kernel_ms": round(attn_ms, 4),
         "attn_kernel_tflops": round(attn_tflops, 2),
         "attn_kernel_ms_cold_cache": round(attn_cold_ms, 4),
@@ -360,7 +377,7 @@ def main():
                      "unit": "TFLOP/s", "frac": round(attn_tflops / PEAK_TFLOPS, 4),
                      "traffic": traffic},
     }
-    if not args.no_cpu_baseline and cfg == 1:
+    if not args.no_cpu_baseline and cfg == 1 and blk == 64 and not args.mod_mask:
         rows = {"k": sel["k"]}
         out["cpu_baseline"] = cpu_oracle_sample(Qc, Kc, Vc, rows, args.cpu_seconds)
     print(json.dumps(out), flush=True)

@@ -49,7 +49,9 @@ class _SelectParams(ctypes.Structure):
                 ("micro", ctypes.c_int32), ("micro_m", ctypes.c_int32),
                 ("scale", ctypes.c_float), ("head_mask", ctypes.c_void_p),
                 ("macro_row_ptr", ctypes.c_void_p), ("macro_col_idx", ctypes.c_void_p),
-                ("qpool16", ctypes.c_void_p), ("kpool16", ctypes.c_void_p)]
+                ("qpool16", ctypes.c_void_p), ("kpool16", ctypes.c_void_p),
+                ("n_diagonals", ctypes.c_int32), ("diagonals", ctypes.c_void_p),
+                ("n_columns", ctypes.c_int32), ("columns", ctypes.c_void_p)]
 
 
 def _load(path: str = _LIB_PATH):
@@ -202,7 +204,9 @@ def bsa_score_blocks(Q, K, *, block: int = BLOCK, scale: float | None = None,
 def make_select_params(mode: str = "topk", *, k: int = 0, p: float = 0.9, k_min: int = 1,
                        k_cap: int | None = None, force_diag: bool = False,
                        static: dict | None = None, micro: dict | None = None,
-                       nB: int | None = None):
+                       patterns: dict | None = None, nB: int | None = None):
+    """bsa_select_params for the arguments of bsa_select_blocks, plus the
+    host arrays it points to (keep them alive for the call)."""
     sp = _SelectParams()
     sp.mode = SELECT_MODES[mode]
     sp.k = k
@@ -217,6 +221,13 @@ def make_select_params(mode: str = "topk", *, k: int = 0, p: float = 0.9, k_min:
         sp.n_anchors = static.get("n_anchors", 0)
         sp.anchor_offset = static.get("anchor_offset", 0)
     keep = []
+    if patterns is not None:
+        for field, cnt in (("diagonals", "n_diagonals"), ("columns", "n_columns")):
+            vals = [int(v) for v in patterns.get(field, ())]
+            arr = (ctypes.c_int32 * max(1, len(vals)))(*vals)
+            keep.append(arr)
+            setattr(sp, cnt, len(vals))
+            setattr(sp, field, ctypes.cast(arr, ctypes.c_void_p).value)
     if micro is not None:
         sp.micro = micro.get("micro", MICRO)
         sp.micro_m = micro["m"]
@@ -237,20 +248,25 @@ def make_select_params(mode: str = "topk", *, k: int = 0, p: float = 0.9, k_min:
 def bsa_select_blocks(scores, Q_like, *, block: int = BLOCK, mode: str = "topk", k: int = 0,
                       p: float = 0.9, k_min: int = 1, k_cap: int | None = None,
                       force_diag: bool = False, static: dict | None = None,
-                      micro: dict | None = None, stream=None):
+                      micro: dict | None = None, patterns: dict | None = None, stream=None):
     """CSR block lists.  ``Q_like`` supplies the shape ([B,H,N,d] tensor).
-    Returns (row_ptr int32 [B*H*nB+1], col_idx int32 [capacity], nnz int64
-    device scalar); the first nnz entries of col_idx are valid."""
+    ``block`` is the selection block (64 or 128; scores, k and the forced
+    set count in it); the lists are always emitted on 64-token tiles.
+    ``patterns`` = {"diagonals": offsets, "columns": key blocks} adds MOD-DiT
+    structural patterns.  Returns (row_ptr int32 [B*H*ceil(N/64)+1], col_idx
+    int32 [capacity], nnz int64 device scalar); the first nnz entries of
+    col_idx are valid."""
     shp = shape_of(Q_like)
     nB = n_blocks(shp.N, block)
     sp, keep = make_select_params(mode, k=k, p=p, k_min=k_min, k_cap=k_cap,
-                                  force_diag=force_diag, static=static, micro=micro, nB=nB)
+                                  force_diag=force_diag, static=static, micro=micro,
+                                  patterns=patterns, nB=nB)
     ws_bytes = _lib.bsa_select_workspace_bytes(ctypes.byref(shp), block, ctypes.byref(sp))
     if ws_bytes < 0:
         raise BsaError(f"bsa_select_workspace_bytes: {bsa_last_error()}")
     cap = _lib.bsa_select_max_nnz(ctypes.byref(shp), block, ctypes.byref(sp))
     dev = Q_like.device
-    rows = shp.B * shp.H * nB
+    rows = shp.B * shp.H * n_blocks(shp.N, BLOCK)
     row_ptr = torch.empty(rows + 1, dtype=torch.int32, device=dev)
     col_idx = torch.empty(max(cap, 1), dtype=torch.int32, device=dev)
     nnz = torch.empty(1, dtype=torch.int64, device=dev)

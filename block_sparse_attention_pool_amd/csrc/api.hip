@@ -92,35 +92,65 @@ bsa::HeadList heads_from_mask(const uint8_t* mask, int H) {
   return l;
 }
 
+// Selection of a (b, h) batch of rows.  `sel` quantities are counted in
+// selection blocks (64 or 128 tokens), `rows`/`nB`/`W` in the 64-token tiles
+// the CSR is emitted on (equal when block = 64).
 struct SelectPlan {
   int64_t rows, nB, W, nT;
-  int64_t bytes_a, bytes_b, bytes_c, total;
+  int64_t block, rows_sel, nB_sel, W_sel;
+  int64_t bytes_a, bytes_b, bytes_c, bytes_d, total;
   bsa::HeadList heads;
 };
 
 bsa_status plan_select(const bsa_shape* s, int32_t block, const bsa_select_params* p,
                        SelectPlan* out) {
   BSA_TRY(check_shape(s));
-  if (block != 64) return fail(BSA_ERR_UNSUPPORTED, "block=%d unsupported (64)", block);
+  if (block != 64 && block != 128)
+    return fail(BSA_ERR_UNSUPPORTED, "block=%d unsupported (64 or 128)", block);
   if (p == nullptr) return fail(BSA_ERR_INVALID_ARG, "params is NULL");
   SelectPlan pl{};
   pl.nB = cdiv(s->N, 64);
   pl.rows = (int64_t)s->B * s->H * pl.nB;
   pl.W = cdiv(pl.nB, 32);
   pl.nT = cdiv(s->N, 16);
+  pl.block = block;
+  pl.nB_sel = cdiv(s->N, block);
+  pl.rows_sel = (int64_t)s->B * s->H * pl.nB_sel;
+  pl.W_sel = cdiv(pl.nB_sel, 32);
+  if (p->mode != BSA_SELECT_MICRO) {
+    if (p->n_diagonals < 0 || p->n_diagonals > bsa::kMaxPatterns || p->n_columns < 0 ||
+        p->n_columns > bsa::kMaxPatterns)
+      return fail(BSA_ERR_INVALID_ARG, "n_diagonals=%d, n_columns=%d (0..%d each)",
+                  p->n_diagonals, p->n_columns, bsa::kMaxPatterns);
+    if ((p->n_diagonals > 0 && p->diagonals == nullptr) ||
+        (p->n_columns > 0 && p->columns == nullptr))
+      return fail(BSA_ERR_INVALID_ARG, "pattern list is NULL");
+    for (int t = 0; t < p->n_diagonals; ++t)
+      if (p->diagonals[t] < -(1 << 24) || p->diagonals[t] > (1 << 24))
+        return fail(BSA_ERR_INVALID_ARG, "diagonal offset %d out of range", p->diagonals[t]);
+    for (int t = 0; t < p->n_columns; ++t)
+      if (p->columns[t] < 0 || p->columns[t] >= pl.nB_sel)
+        return fail(BSA_ERR_INVALID_ARG, "column %d outside [0, %lld)", p->columns[t],
+                    (long long)pl.nB_sel);
+  }
   switch (p->mode) {
     case BSA_SELECT_TOPK:
     case BSA_SELECT_TOPP:
     case BSA_SELECT_STATIC:
-      if (p->mode != BSA_SELECT_STATIC && pl.nB > 4096)
+      if (p->mode != BSA_SELECT_STATIC && pl.nB_sel > 4096)
         return fail(BSA_ERR_UNSUPPORTED, "scored selection needs nB <= 4096 (nB=%lld)",
-                    (long long)pl.nB);
+                    (long long)pl.nB_sel);
       if (pl.W > 128) return fail(BSA_ERR_UNSUPPORTED, "nB=%lld exceeds 4096", (long long)pl.nB);
-      pl.bytes_a = align256(pl.rows * pl.W * 4);  // row bitmasks
-      pl.bytes_b = align256(pl.rows * 4);         // row counts
-      pl.bytes_c = 0;
+      pl.bytes_a = align256(pl.rows_sel * pl.W_sel * 4);  // row bitmasks
+      pl.bytes_b = align256(pl.rows_sel * 4);             // row counts
+      if (block != 64) {
+        pl.bytes_c = align256(pl.rows * pl.W * 4);  // the rows on 64-token tiles
+        pl.bytes_d = align256(pl.rows * 4);
+      }
       break;
     case BSA_SELECT_MICRO: {
+      if (block != 64)
+        return fail(BSA_ERR_UNSUPPORTED, "MICRO selection works on the 64-token CSR (block=64)");
       if (p->micro != 16) return fail(BSA_ERR_UNSUPPORTED, "micro=%d unsupported (16)", p->micro);
       if (p->micro_m < 0) return fail(BSA_ERR_INVALID_ARG, "micro_m=%d < 0", p->micro_m);
       if (pl.W > 128) return fail(BSA_ERR_UNSUPPORTED, "nB=%lld exceeds 4096", (long long)pl.nB);
@@ -135,7 +165,7 @@ bsa_status plan_select(const bsa_shape* s, int32_t block, const bsa_select_param
     default:
       return fail(BSA_ERR_INVALID_ARG, "unknown selection mode %d", p->mode);
   }
-  pl.total = pl.bytes_a + pl.bytes_b + pl.bytes_c;
+  pl.total = pl.bytes_a + pl.bytes_b + pl.bytes_c + pl.bytes_d;
   *out = pl;
   return BSA_OK;
 }
@@ -145,13 +175,16 @@ int64_t max_nnz(const bsa_shape* s, const bsa_select_params* p, const SelectPlan
     const int64_t per = std::min<int64_t>(p->micro_m, 4 * pl.nT);
     return (int64_t)s->B * pl.heads.n * pl.nB * per;
   }
-  int64_t per = pl.nB;
+  int64_t per = pl.nB_sel;
   if (!p->use_static) {
     int64_t base = 0;
-    if (p->mode == BSA_SELECT_TOPK) base = p->k;
+    if (p->mode == BSA_SELECT_TOPK) base = std::max(p->k, 0);
     else if (p->mode == BSA_SELECT_TOPP) base = std::max(p->k_cap, 1);
-    per = std::min<int64_t>(pl.nB, base + (p->force_diag ? 1 : 0));
+    per = std::min<int64_t>(pl.nB_sel, base + (p->force_diag ? 1 : 0) + p->n_diagonals +
+                                           p->n_columns);
   }
+  // each selection block covers block / 64 tiles
+  per = std::min<int64_t>(pl.nB, per * (pl.block / 64));
   return pl.rows * per;
 }
 
@@ -226,7 +259,8 @@ bsa_status bsa_score_blocks(const uint16_t* Q, const uint16_t* K, const bsa_shap
                             float* scores, int32_t micro, float* qpool16, float* kpool16,
                             void* stream) {
   BSA_TRY(check_shape(shape));
-  if (block != 64) return fail(BSA_ERR_UNSUPPORTED, "block=%d unsupported (64)", block);
+  if (block != 64 && block != 128)
+    return fail(BSA_ERR_UNSUPPORTED, "block=%d unsupported (64 or 128)", block);
   BSA_TRY(check_ptr(Q, "Q"));
   BSA_TRY(check_ptr(K, "K"));
   BSA_TRY(check_ptr(qpool, "qpool"));
@@ -237,7 +271,7 @@ bsa_status bsa_score_blocks(const uint16_t* Q, const uint16_t* K, const bsa_shap
     BSA_TRY(check_ptr(qpool16, "qpool16"));
     BSA_TRY(check_ptr(kpool16, "kpool16"));
   }
-  const int nB = (int)cdiv(shape->N, 64);
+  const int nB = (int)cdiv(shape->N, block);
   if ((int64_t)shape->B * shape->H > 65535)
     return fail(BSA_ERR_UNSUPPORTED, "B*H exceeds 65535");
   hipStream_t st = (hipStream_t)stream;
@@ -252,6 +286,7 @@ bsa_status bsa_score_blocks(const uint16_t* Q, const uint16_t* K, const bsa_shap
   p.D = shape->d;
   p.nB = nB;
   p.nT = (int)cdiv(shape->N, 16);
+  p.block = block;
   p.qpool = qpool;
   p.kpool = kpool;
   p.qpool16 = micro ? qpool16 : nullptr;
@@ -370,8 +405,9 @@ bsa_status bsa_select_blocks(const float* scores, const bsa_shape* shape, int32_
   a.bits = (uint32_t*)ws;
   a.counts = (int32_t*)(ws + pl.bytes_a);
   a.N = shape->N;
-  a.nB = (int)pl.nB;
-  a.W = (int)pl.W;
+  a.nB = (int)pl.nB_sel;
+  a.W = (int)pl.W_sel;
+  a.block = (int)pl.block;
   a.mode = p->mode;
   a.k = p->k;
   a.k_min = p->k_min;
@@ -383,9 +419,24 @@ bsa_status bsa_select_blocks(const float* scores, const bsa_shape* shape, int32_
   a.window_frames = p->window_frames;
   a.n_anchors = p->n_anchors;
   a.anchor_offset = p->anchor_offset;
-  BSA_TRY(hip_status(bsa::launch_select(a, rows, st), "select launch"));
-  BSA_TRY(hip_status(bsa::launch_scan(a.counts, rows, row_ptr, out_nnz, st), "scan launch"));
-  BSA_TRY(hip_status(bsa::launch_emit_bits(a.bits, a.W, rows, row_ptr, col_idx, col_cap, st),
+  a.n_diag = p->n_diagonals;
+  a.n_col = p->n_columns;
+  for (int t = 0; t < a.n_diag; ++t) a.diag[t] = p->diagonals[t];
+  for (int t = 0; t < a.n_col; ++t) a.col[t] = p->columns[t];
+  BSA_TRY(hip_status(bsa::launch_select(a, (int)pl.rows_sel, st), "select launch"));
+  const uint32_t* bits = a.bits;
+  const int32_t* counts = a.counts;
+  if (pl.block != 64) {
+    uint32_t* bits64 = (uint32_t*)(ws + pl.bytes_a + pl.bytes_b);
+    int32_t* counts64 = (int32_t*)(ws + pl.bytes_a + pl.bytes_b + pl.bytes_c);
+    BSA_TRY(hip_status(bsa::launch_expand_bits(a.bits, a.W, a.nB, bits64, counts64, (int)pl.W,
+                                               (int)pl.nB, rows, st),
+                       "expand launch"));
+    bits = bits64;
+    counts = counts64;
+  }
+  BSA_TRY(hip_status(bsa::launch_scan(counts, rows, row_ptr, out_nnz, st), "scan launch"));
+  BSA_TRY(hip_status(bsa::launch_emit_bits(bits, (int)pl.W, rows, row_ptr, col_idx, col_cap, st),
                      "emit launch"));
   return BSA_OK;
 }

@@ -20,6 +20,7 @@ struct PoolArgs {
   const uint16_t* K;
   int64_t sb, sh, sn;
   int H, N, D, nB, nT;
+  int block;       // tokens per pooled block: 64 or 128
   float* qpool;
   float* kpool;
   float* qpool16;  // may be null
@@ -35,15 +36,21 @@ struct GemmArgs {
   HeadList heads;   // batch z -> (z / heads.n, heads.h[z % heads.n])
 };
 
+constexpr int kMaxPatterns = 64;  // diagonal offsets / columns per selection
+
 struct SelectArgs {
   const float* scores;  // [rows, nB] or null
   uint32_t* bits;       // [rows, W]
   int32_t* counts;      // [rows]
   int N, nB, W;
+  int block;            // tokens per selection block: 64 or 128
   int mode, k, k_min, k_cap;
   float p;
   int force_diag, use_static;
   int frame_tokens, window_frames, n_anchors, anchor_offset;
+  int n_diag, n_col;                 // MOD-DiT parallel-diagonal / vertical patterns
+  int32_t diag[kMaxPatterns];        // offsets: key block i + diag[t]
+  int32_t col[kMaxPatterns];         // key blocks
 };
 
 struct MicroSelectArgs {
@@ -121,6 +128,9 @@ hipError_t launch_pool(const PoolArgs& a, int B, hipStream_t s);
 hipError_t launch_score_gemm(const GemmArgs& a, int nbatch, hipStream_t s);
 hipError_t launch_fill_i32(int32_t* p, int64_t n, int32_t v, hipStream_t s);
 hipError_t launch_select(const SelectArgs& a, int rows, hipStream_t s);
+hipError_t launch_expand_bits(const uint32_t* bits_sel, int W_sel, int nB_sel,
+                              uint32_t* bits64, int32_t* counts64, int W64, int nB64,
+                              int rows64, hipStream_t s);
 hipError_t launch_scan(const int32_t* counts, int rows, int32_t* row_ptr,
                        int64_t* out_nnz, hipStream_t s);
 hipError_t launch_emit_bits(const uint32_t* bits, int W, int rows,

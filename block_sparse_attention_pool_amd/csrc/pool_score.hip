@@ -7,19 +7,22 @@
 
 namespace bsa {
 
-// One workgroup per (64-token block i, head h, batch b, tensor Q|K).
+// One workgroup per (BLK-token block i, head h, batch b, tensor Q|K), BLK =
+// 64 or 128 (the 128-token blocks of MOD-DiT's block-wise attention).
 // 256 threads: thread = (16-byte chunk c of a row, token group g).  Each
 // group sums a run of consecutive tokens; groups are then combined into the
-// four 16-token tile sums and the 64-token block sum.  Only valid tokens
+// BLK/16 16-token tile sums and the block sum.  Only valid tokens
 // (index < N) contribute and the divisor is the valid count.
-template <int D>
+template <int D, int BLK>
 __global__ __launch_bounds__(256) void pool_kernel(PoolArgs a) {
   constexpr int C = D / 8;        // 16-byte chunks per token row
   constexpr int G = 256 / C;      // token groups
-  constexpr int TPG = 64 / G;     // tokens per group
+  constexpr int TPG = BLK / G;    // tokens per group
   constexpr int GPT = 16 / TPG;   // groups per 16-token tile
+  constexpr int NT = BLK / kMicro;  // 16-token tiles per block
+  static_assert(GPT >= 1 && GPT * TPG == 16, "a token group never straddles two tiles");
   __shared__ float part[G][D + 4];
-  __shared__ float tile[4][D];
+  __shared__ float tile[NT][D];
 
   const int i = blockIdx.x;
   const int h = blockIdx.y;
@@ -35,7 +38,7 @@ __global__ __launch_bounds__(256) void pool_kernel(PoolArgs a) {
   for (int e = 0; e < 8; ++e) acc[e] = 0.f;
 #pragma unroll
   for (int t = 0; t < TPG; ++t) {
-    const int tok = i * kBlock + g * TPG + t;
+    const int tok = i * BLK + g * TPG + t;
     if (tok < a.N) {
       const u32x4 v = *(const u32x4*)(X + (int64_t)tok * a.sn + c * 8);
 #pragma unroll
@@ -51,22 +54,23 @@ __global__ __launch_bounds__(256) void pool_kernel(PoolArgs a) {
 
   const int64_t bh = (int64_t)b * a.H + h;
   float* pool16 = isK ? a.kpool16 : a.qpool16;
-  for (int idx = tid; idx < 4 * D; idx += 256) {
+  for (int idx = tid; idx < NT * D; idx += 256) {
     const int t = idx / D, e = idx % D;
     float s = 0.f;
 #pragma unroll
     for (int gg = 0; gg < GPT; ++gg) s += part[t * GPT + gg][e];
     tile[t][e] = s;
-    const int t0 = i * kBlock + t * kMicro;
+    const int t0 = i * BLK + t * kMicro;
     const int cnt = min(kMicro, a.N - t0);
     if (pool16 != nullptr && cnt > 0)
-      pool16[(bh * a.nT + 4 * i + t) * D + e] = s / (float)cnt;
+      pool16[(bh * a.nT + NT * i + t) * D + e] = s / (float)cnt;
   }
   __syncthreads();
   float* pool = isK ? a.kpool : a.qpool;
-  const int cnt = min(kBlock, a.N - i * kBlock);
+  const int cnt = min(BLK, a.N - i * BLK);
   for (int e = tid; e < D; e += 256) {
-    const float s = (tile[0][e] + tile[1][e]) + (tile[2][e] + tile[3][e]);
+    float s = (tile[0][e] + tile[1][e]) + (tile[2][e] + tile[3][e]);
+    if constexpr (NT == 8) s += (tile[4][e] + tile[5][e]) + (tile[6][e] + tile[7][e]);
     pool[(bh * a.nB + i) * D + e] = s / (float)cnt;
   }
 }
@@ -137,10 +141,17 @@ __global__ __launch_bounds__(256) void score_gemm_kernel(GemmArgs a) {
 
 hipError_t launch_pool(const PoolArgs& a, int B, hipStream_t s) {
   dim3 grid(a.nB, a.H, 2 * B);
-  if (a.D == 128)
-    hipLaunchKernelGGL(pool_kernel<128>, grid, dim3(256), 0, s, a);
-  else
-    hipLaunchKernelGGL(pool_kernel<64>, grid, dim3(256), 0, s, a);
+  if (a.block == 128) {
+    if (a.D == 128)
+      hipLaunchKernelGGL((pool_kernel<128, 128>), grid, dim3(256), 0, s, a);
+    else
+      hipLaunchKernelGGL((pool_kernel<64, 128>), grid, dim3(256), 0, s, a);
+  } else {
+    if (a.D == 128)
+      hipLaunchKernelGGL((pool_kernel<128, 64>), grid, dim3(256), 0, s, a);
+    else
+      hipLaunchKernelGGL((pool_kernel<64, 64>), grid, dim3(256), 0, s, a);
+  }
   return hipGetLastError();
 }
 

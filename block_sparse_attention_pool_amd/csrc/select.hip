@@ -6,10 +6,14 @@
 //   top-p:  HyperVAttention section 2, Eq. 2 (size-weighted centroid
 //           softmax) and Eq. 3 (smallest descending prefix with cumulative
 //           probability at least p), clamped to [k_min, k_cap];
-//   forced: diagonal and/or the LVSA temporal window + rotating anchors.
+//   forced: diagonal and/or the LVSA temporal window + rotating anchors
+//           and/or MOD-DiT structural patterns (parallel diagonals at given
+//           offsets, vertical key columns).
 // The row is built as a bitmask (one ballot per 64 key blocks), counted,
 // prefix-summed across rows into row_ptr, and emitted as ascending column
-// indices.
+// indices.  Blocks are 64 or 128 tokens; a 128-token selection is emitted
+// on the 64-token tiles the attention kernels run (each kept 128 x 128 pair
+// becomes its 2 x 2 tiles), through expand_bits_kernel.
 //
 // Micro rows (HyMoR-Attn Micro selection, 16-token tiles inside omitted
 // blocks): one workgroup per (b, micro head, query block); radix selection
@@ -105,12 +109,12 @@ __global__ __launch_bounds__(256) void select_wave_kernel(SelectArgs a, int rows
       mx = fmaxf(mx, x[e]);
     }
     if (a.mode == kTopP) mx = wave_max(mx);
-    const float tail_size = (float)(a.N - (a.nB - 1) * kBlock);
+    const float tail_size = (float)(a.N - (a.nB - 1) * a.block);
 #pragma unroll
     for (int e = 0; e < E; ++e) {
       const int j = 64 * e + lane;
       float v = x[e];
-      if (a.mode == kTopP) v = (j == a.nB - 1 ? tail_size : (float)kBlock) * expf(v - mx);
+      if (a.mode == kTopP) v = (j == a.nB - 1 ? tail_size : (float)a.block) * expf(v - mx);
       val[e] = j < a.nB ? v : 0.f;
       key[e] = j < a.nB ? float_order_key(v) : 0u;
     }
@@ -201,15 +205,17 @@ __global__ __launch_bounds__(256) void select_wave_kernel(SelectArgs a, int rows
   int64_t stride = 0, off = 0;
   if (a.use_static) {
     const int64_t ft = a.frame_tokens;
-    const int64_t lo_i = (int64_t)i * kBlock / ft;
-    const int64_t hi_i = (int64_t)(min(i * kBlock + kBlock, a.N) - 1) / ft;
-    // hi_j >= F  <=>  min(64j + 63, N - 1) >= F ft  <=>  64j + 63 >= F ft (F ft <= N - 1)
+    const int64_t bs = a.block;
+    const int64_t lo_i = (int64_t)i * bs / ft;
+    const int64_t hi_i = (min((int64_t)i * bs + bs, (int64_t)a.N) - 1) / ft;
+    // hi_j >= F  <=>  min(bs j + bs - 1, N - 1) >= F ft  <=>  bs j + bs - 1 >= F ft
+    // (when F ft <= N - 1), i.e. j >= ceil((F ft - bs + 1) / bs) = floor(F ft / bs)
     const int64_t F = lo_i - a.window_frames;
     const int64_t G = hi_i + a.window_frames;
-    ja = F * ft <= 63 ? 0 : (int)((F * ft - 63 + 63) / 64);
+    ja = F * ft <= bs - 1 ? 0 : (int)(F * ft / bs);
     if (F * ft > a.N - 1) ja = a.nB;  // no block reaches that frame
-    // lo_j <= G  <=>  64j / ft <= G  <=>  64j <= (G + 1) ft - 1
-    jb = G < 0 ? -1 : (int)min((int64_t)a.nB - 1, ((G + 1) * ft - 1) / 64);
+    // lo_j <= G  <=>  bs j / ft <= G  <=>  bs j <= (G + 1) ft - 1
+    jb = G < 0 ? -1 : (int)min((int64_t)a.nB - 1, ((G + 1) * ft - 1) / bs);
     if (a.n_anchors > 0) {
       stride = a.nB / a.n_anchors;
       off = ((int64_t)a.anchor_offset % a.nB + a.nB) % a.nB;
@@ -231,6 +237,15 @@ __global__ __launch_bounds__(256) void select_wave_kernel(SelectArgs a, int rows
         if (j >= j0 && j < j0 + 32) f |= 1u << (j - j0);
       }
     }
+    // MOD-DiT patterns: diagonal offsets off the block map mark nothing
+    for (int t = 0; t < a.n_diag; ++t) {
+      const int j = i + a.diag[t];
+      if (j >= j0 && j < j0 + 32) f |= 1u << (j - j0);
+    }
+    for (int t = 0; t < a.n_col; ++t) {
+      const int j = a.col[t];
+      if (j >= j0 && j < j0 + 32) f |= 1u << (j - j0);
+    }
     const uint32_t valid = a.nB - j0 >= 32 ? 0xFFFFFFFFu : ((1u << (a.nB - j0)) - 1u);
     word[q] = (word[q] | f) & valid;
     a.bits[(int64_t)r * a.W + w] = word[q];
@@ -238,6 +253,47 @@ __global__ __launch_bounds__(256) void select_wave_kernel(SelectArgs a, int rows
   }
   cnt = wave_sum(cnt);
   if (lane == 0) a.counts[r] = cnt;
+}
+
+// ---------------------------------------------- 128-token blocks on 64 tiles
+
+// Spread the 16 low bits of x to the even bit positions of a 32-bit word.
+__device__ __forceinline__ uint32_t spread16(uint32_t x) {
+  x &= 0xFFFFu;
+  x = (x | (x << 8)) & 0x00FF00FFu;
+  x = (x | (x << 4)) & 0x0F0F0F0Fu;
+  x = (x | (x << 2)) & 0x33333333u;
+  x = (x | (x << 1)) & 0x55555555u;
+  return x;
+}
+
+// One wave per 64-token query block r = (b, h, i): it takes the row of its
+// 128-token block (b, h, i / 2), every kept key block J becoming 64-token
+// blocks 2J and 2J + 1 (the second only when it exists).  Word w of the
+// 64-block row covers 128-blocks 16w .. 16w + 15: half (w & 1) of word
+// w / 2 of the 128-block row, each bit doubled.
+__global__ __launch_bounds__(256) void expand_bits_kernel(const uint32_t* bits_sel, int W_sel,
+                                                          int nB_sel, uint32_t* bits64,
+                                                          int32_t* counts64, int W64, int nB64,
+                                                          int rows64) {
+  const int r = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (r >= rows64) return;
+  const int lane = threadIdx.x & 63;
+  const int64_t bh = r / nB64;
+  const int i = r % nB64;
+  const uint32_t* src = bits_sel + (bh * nB_sel + i / 2) * W_sel;
+  int cnt = 0;
+  for (int w = lane; w < W64; w += 64) {
+    const uint32_t half = w / 2 < W_sel ? src[w / 2] >> (16 * (w & 1)) : 0u;
+    const uint32_t x = spread16(half);
+    const int j0 = 32 * w;
+    const uint32_t valid = nB64 - j0 >= 32 ? 0xFFFFFFFFu : ((1u << (nB64 - j0)) - 1u);
+    const uint32_t word = (x | (x << 1)) & valid;
+    bits64[(int64_t)r * W64 + w] = word;
+    cnt += __popc(word);
+  }
+  cnt = wave_sum(cnt);
+  if (lane == 0) counts64[r] = cnt;
 }
 
 // -------------------------------------------------------- row pointers
@@ -530,6 +586,14 @@ hipError_t launch_select(const SelectArgs& a, int rows, hipStream_t s) {
   } else {
     hipLaunchKernelGGL(select_wave_kernel<64>, grid, block, 0, s, a, rows);
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_expand_bits(const uint32_t* bits_sel, int W_sel, int nB_sel,
+                              uint32_t* bits64, int32_t* counts64, int W64, int nB64,
+                              int rows64, hipStream_t s) {
+  hipLaunchKernelGGL(expand_bits_kernel, dim3((rows64 + 3) / 4), dim3(256), 0, s, bits_sel,
+                     W_sel, nB_sel, bits64, counts64, W64, nB64, rows64);
   return hipGetLastError();
 }
 

@@ -87,7 +87,8 @@ const char* bsa_last_error(void);
  *   kpool[b,h,j,:] = same for K
  *   scores[b,h,i,j] = scale * <qpool[b,h,i,:], kpool[b,h,j,:]>
  *
- * block: must be 64.  nB = ceil(N / 64).
+ * block: 64, or 128 (the block size of MOD-DiT's block-wise attention).
+ *   nB = ceil(N / block).
  * qpool, kpool: float32 [B, H, nB, d] (required).
  * scores: float32 [B, H, nB, nB], or NULL to skip the score matrix.
  * micro: 0, or 16 to also write the 16-token tile means qpool16 / kpool16,
@@ -126,7 +127,21 @@ bsa_status bsa_score_blocks(const uint16_t* Q, const uint16_t* K,
  *   of j lies within window_frames latent frames of some token of block i
  *   (frame of token t = t / frame_tokens), plus n_anchors global anchor
  *   blocks (anchor_offset + a * floor(nB / n_anchors)) mod nB, a = 0..n-1.
- *   The caller draws anchor_offset per call (rotation).
+ *   The caller draws anchor_offset per call (rotation).  window_frames = 0
+ *   is MOD-DiT's block-diagonal (intra-frame) pattern;
+ *   diagonals / columns: MOD-DiT's parallel-diagonal and vertical patterns
+ *   (section "Pattern Mixtures"): query block i keeps key block i + delta
+ *   for each offset delta (offsets off the block map mark nothing) and every
+ *   listed key column.  Which patterns to use (MOD ranks them by intensities
+ *   fitted to dense attention maps of a model) is the caller's choice.
+ *
+ * Blocks (all modes but MICRO): block = 64, or 128 for selection on 128-token
+ * blocks -- scores, k, k_cap, the forced set, diagonals and columns are then
+ * in 128-token blocks -- and the CSR is emitted on the 64-token tiles the
+ * attention kernels run: 64-token query block i' takes the row of 128-token
+ * block i'/2, each kept 128-token key block J becoming blocks 2J and 2J+1
+ * (when 2J+1 exists), which leaves every query's token support unchanged.
+ * MICRO mode needs block = 64 (it reads the 64-token macro CSR).
  * ---------------------------------------------------------------------- */
 enum {
   BSA_SELECT_TOPK = 0,
@@ -156,6 +171,11 @@ typedef struct bsa_select_params {
   const int32_t* macro_col_idx;  /* device                                  */
   const float* qpool16;          /* device [B,H,nT,d] from bsa_score_blocks */
   const float* kpool16;          /* device [B,H,nT,d]                       */
+  /* structural patterns (all modes but MICRO), at most 64 of each        */
+  int32_t n_diagonals;
+  const int32_t* diagonals;      /* host [n_diagonals]: offsets delta       */
+  int32_t n_columns;
+  const int32_t* columns;        /* host [n_columns]: key blocks in [0, nB) */
 } bsa_select_params;
 
 /* Bytes of device workspace bsa_select_blocks needs for these arguments
@@ -168,20 +188,20 @@ int64_t bsa_select_max_nnz(const bsa_shape* shape, int32_t block,
                            const bsa_select_params* params);
 
 /* ------------------------------------------------------------------------
- * bsa_select_blocks -- CSR block lists, one row per (b, h, query block i),
- * row index r = (b * H + h) * nB + i.
+ * bsa_select_blocks -- CSR block lists, one row per (b, h, 64-token query
+ * block i), row index r = (b * H + h) * nB64 + i, nB64 = ceil(N / 64).
  *
- * scores: float32 [B, H, nB, nB] from bsa_score_blocks (TOPK/TOPP); NULL in
- *   STATIC and MICRO mode.
- * row_ptr: int32 [B*H*nB + 1]; row r is col_idx[row_ptr[r] .. row_ptr[r+1]).
+ * scores: float32 [B, H, nB, nB] from bsa_score_blocks with the same block
+ *   (TOPK/TOPP); NULL in STATIC and MICRO mode.
+ * row_ptr: int32 [B*H*nB64 + 1]; row r is col_idx[row_ptr[r] .. row_ptr[r+1]).
  * col_idx: int32 [col_cap]: ascending key block indices (MICRO: codes
  *   4*beta + a, sorted by (a, beta)).  Entries at positions >= col_cap are
  *   not written; *out_nnz tells the caller whether col_cap sufficed.
  * out_nnz: device int64, receives the total number of entries.
  * workspace: device, at least bsa_select_workspace_bytes(...) bytes; its
  *   contents on entry do not matter.
- * Limits: TOPK/TOPP need nB <= 4096 (N <= 262144 tokens); totals must fit
- * in int32.
+ * Limits: TOPK/TOPP need nB <= 4096 selection blocks; every mode needs
+ * nB64 <= 4096 (N <= 262144 tokens); totals must fit in int32.
  * ---------------------------------------------------------------------- */
 bsa_status bsa_select_blocks(const float* scores, const bsa_shape* shape,
                              int32_t block, const bsa_select_params* params,

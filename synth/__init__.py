@@ -9,5 +9,6 @@ from .video_qkv import (  # noqa: F401
     config_spec,
     gen_qkv,
     micro_heads,
+    mod_pattern_mask,
     rotation_offset,
 )

@@ -185,3 +185,24 @@ def spike_codes(spec: VideoSpec):
     """(query tile codes, key tile codes) of a spiked spec, for recall checks."""
     q, k, _ = _spike_plan(spec)
     return q, k
+
+
+def mod_pattern_mask(spec: VideoSpec, block: int, frames=(1, 2), n_columns: int = 4) -> dict:
+    """A fixed MOD-DiT-style structural mask for a layer of this shape, as
+    selection arguments: the intra-frame block-diagonal (window of radius 0),
+    parallel diagonals at the block offsets of tokens ``frames`` latent
+    frames apart in either direction (the nearest offset below and above
+    dt * frame_tokens / block), and ``n_columns`` vertical key columns (the
+    first block, a sink, plus evenly strided blocks).  MOD chooses its
+    patterns from intensities fitted to a model's dense attention maps;
+    with no model, this set stands in for that choice."""
+    nB = -(-spec.N // block)
+    diags = set()
+    for dt in frames:
+        lo = (dt * spec.frame_tokens) // block
+        for off in (lo, lo + 1):
+            diags.update((off, -off))
+    cols = sorted({(c * nB) // n_columns for c in range(n_columns)})
+    return dict(static=dict(frame_tokens=spec.frame_tokens, window_frames=0,
+                            n_anchors=0, anchor_offset=0),
+                patterns=dict(diagonals=sorted(diags), columns=cols))

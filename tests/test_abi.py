@@ -178,3 +178,48 @@ def test_heads_at_risk_matches_the_oracle_rule():
         risk = np.round(rng.random(H), 1)   # coarse values: many ties
         for n in (0, 1, H // 3, H, H + 2):
             assert bsa.heads_at_risk(risk, n) == O.heads_at_risk(risk, n)
+
+
+def test_block128_selection_workspace_and_bounds():
+    s = _shape(B=1, H=2, N=1000)          # 8 blocks of 128, 16 of 64
+    sp, _ = bsa.make_select_params("topk", k=3, nB=8)
+    ws = bsa._lib.bsa_select_workspace_bytes(ctypes.byref(s), 128, ctypes.byref(sp))
+    # 128-block bitmasks + counts, then the 64-tile bitmasks + counts
+    assert ws == 4 * 256
+    # each kept 128-block is two tiles: 3 blocks -> at most 6 of 16 tiles per row
+    assert bsa._lib.bsa_select_max_nnz(ctypes.byref(s), 128, ctypes.byref(sp)) == 2 * 16 * 6
+    assert bsa._lib.bsa_select_workspace_bytes(ctypes.byref(s), 96, ctypes.byref(sp)) == -1
+    assert "block=96" in bsa.bsa_last_error()
+    sm, _ = bsa.make_select_params("micro", micro=dict(
+        m=4, scale=0.1, macro=(_FakeT(4096), _FakeT(4096)), qpool16=_FakeT(4096),
+        kpool16=_FakeT(4096)))
+    assert bsa._lib.bsa_select_workspace_bytes(ctypes.byref(s), 128, ctypes.byref(sm)) == -1
+    assert "MICRO" in bsa.bsa_last_error()
+
+
+class _FakeT:
+    """Stands in for a device tensor where only an address is read."""
+    def __init__(self, addr):
+        self.addr = addr
+
+    def data_ptr(self):
+        return self.addr
+
+
+def test_pattern_validation():
+    s = _shape(B=1, H=1, N=1000)          # 16 blocks of 64
+    sp, keep = bsa.make_select_params("static", patterns=dict(diagonals=[-2, 40], columns=[15]))
+    assert bsa._lib.bsa_select_workspace_bytes(ctypes.byref(s), 64, ctypes.byref(sp)) > 0
+    # patterns add one block each per row to the bound (static mode without
+    # a window keeps only the forced set)
+    assert bsa._lib.bsa_select_max_nnz(ctypes.byref(s), 64, ctypes.byref(sp)) == 16 * 3
+    sp, keep = bsa.make_select_params("static", patterns=dict(columns=[16]))
+    assert bsa._lib.bsa_select_workspace_bytes(ctypes.byref(s), 64, ctypes.byref(sp)) == -1
+    assert "column 16" in bsa.bsa_last_error()
+    sp, keep = bsa.make_select_params("topk", k=1, patterns=dict(diagonals=list(range(65))))
+    assert bsa._lib.bsa_select_workspace_bytes(ctypes.byref(s), 64, ctypes.byref(sp)) == -1
+    assert "n_diagonals=65" in bsa.bsa_last_error()
+    sp, keep = bsa.make_select_params("topk", k=1)
+    sp.n_columns = 2                       # count without a list
+    assert bsa._lib.bsa_select_workspace_bytes(ctypes.byref(s), 64, ctypes.byref(sp)) == -1
+    assert "NULL" in bsa.bsa_last_error()
