@@ -235,6 +235,10 @@ __device__ __forceinline__ void exec_barrier() { asm volatile("s_barrier" ::: "m
 
 typedef __attribute__((address_space(4))) const int32_t const_i32;
 
+// Average key-tile bytes per row above which the sparse kernel interleaves
+// its rows across the XCDs: twice the 4 MB L2 of one XCD.
+constexpr int64_t kWideRowBytes = int64_t(8) << 20;
+
 // One workgroup per (b, h, 64-row query block), two waves of 32 rows each.
 // Per selected key block the 64 x D K tile (16-byte chunks XOR-swizzled by
 // row) and the chunk-major V^T tile sit in LDS.  The K buffer is refilled with
@@ -252,11 +256,29 @@ void attn_fwd_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(1024))) uint16_t sK[64 * D];
   __shared__ __attribute__((aligned(1024))) uint16_t sV[D * 64];
 
-  // XCD-aware order: dispatch w runs on XCD w % 8; give each XCD a
-  // contiguous range of (head, query block) rows so its L2 sees one head's
-  // neighbouring query blocks, whose key selections overlap.
+  // XCD-aware row order: dispatch w runs on XCD w % 8.  By default each XCD
+  // takes a contiguous range of (head, query block) rows, so its L2 sees one
+  // head's neighbouring query blocks, whose key selections overlap.  When
+  // the rows' key supports average more than twice an XCD's 4 MB L2 (many
+  // far-reaching blocks per row), that reuse is lost anyway; the rows are
+  // then dealt to the XCDs in interleaved chunks of 8, so that all XCDs work
+  // on neighbouring rows of one head at a time and share its tiles through
+  // the Infinity Cache instead of streaming eight heads' keys from HBM.  The
+  // choice reads the total entry count, so it needs no host round trip.
   const int w = blockIdx.x;
-  const int L = (w & 7) * a.per_xcd + (w >> 3);
+  const int xcd = w & 7, slot = w >> 3;
+  bool interleave = false;
+  if constexpr (!DENSE) {
+    const int64_t total = ((const_i32*)a.row_ptr)[a.rows];
+    interleave = total * (kBlock * D * 2 * 2) > (int64_t)a.rows * kWideRowBytes;
+  }
+  int L;
+  if (interleave) {
+    L = ((slot >> 3) * 8 + xcd) * 8 + (slot & 7);
+  } else {
+    if (slot >= a.per_xcd) return;
+    L = xcd * a.per_xcd + slot;
+  }
   if (L >= a.rows) return;
   const int i = L % a.nB;
   const int bh = L / a.nB;
@@ -684,7 +706,8 @@ hipError_t launch_transpose_v(const TransposeArgs& a, int B, int D, hipStream_t 
 
 template <int D, bool DENSE>
 static void launch_attn_t(const AttnArgs& a, bool out_bf16, hipStream_t s) {
-  dim3 grid(8 * a.per_xcd);
+  // room for either row order of the sparse kernel (8 XCDs x whole chunks of 8)
+  dim3 grid(DENSE ? 8 * a.per_xcd : 64 * ((a.rows + 63) / 64));
   if (out_bf16)
     hipLaunchKernelGGL((attn_fwd_kernel<D, DENSE, true>), grid, dim3(128), 0, s, a);
   else
