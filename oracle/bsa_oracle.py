@@ -46,7 +46,10 @@ design notes of the repository):
   * a 128-token block selection is executed on 64-token tiles: every kept
     128 x 128 pair is its 2 x 2 tiles, the token support unchanged;
   * the omission risk of a query token is the share of its full softmax mass
-    outside its sparse support (HyMoR names the risk, not its formula).
+    outside its sparse support (HyMoR names the risk, not its formula);
+  * RSA's pooled rectification is read as attention over the pooled keys of
+    the omitted blocks (log-size bias), LSE-merged with the sparse result;
+    its gain-aware gate has no stated rule and is not modelled.
 """
 
 from __future__ import annotations
@@ -382,6 +385,57 @@ def lse_merge(O1, L1, O2, L2):
     O = w1[:, None] * O1 + w2[:, None] * O2
     O[both_empty] = 0.0
     return O, L
+
+
+# ----------------------------------------------------------------------------
+# Pooled rectification of omitted blocks ([RSA] reading)
+#
+# [RSA] rectifies sparse attention with pooled query-key interactions: the
+# kept (critical) blocks are over-weighted and the omitted (non-critical)
+# ones lose their weight entirely.  It gives no formulas.  Reading used
+# here: every omitted key block j contributes its pooled estimate -- the
+# block's softmax normaliser n_j exp(scale q . Kbar_j) and its value sum
+# n_j exp(scale q . Kbar_j) Vbar_j (exact when the block's keys are all
+# equal) -- and the estimate is combined with the sparse result by the
+# exact LSE merge, which also lowers the kept blocks' weights to their share
+# of the larger normaliser.  The page's gain-aware gate has no stated rule
+# and is not modelled.
+# ----------------------------------------------------------------------------
+
+def pooled_omitted_attention(Q, K, V, rows: list[list[int]], b: int, scale: float):
+    """For every valid query token t of block i, attention over the pooled
+    keys of the blocks NOT in row i, each with log-size bias ln n_j:
+        z_j = scale q_t . Kbar_j + ln n_j,
+        LSE_t = ln sum_j e^{z_j},  O_t = sum_j e^{z_j - LSE_t} Vbar_j.
+    A row that keeps every block gets O = 0, LSE = -inf."""
+    Q = np.asarray(Q, np.float64)
+    N = Q.shape[0]
+    nB = n_blocks(N, b)
+    Kb, Vb = pool_means(K, b), pool_means(V, b)
+    logn = np.log(block_sizes(N, b))
+    O = np.zeros((N, Vb.shape[1]))
+    L = np.full(N, NEG_INF)
+    for i, sel in enumerate(rows):
+        om = np.ones(nB, dtype=bool)
+        om[list(sel)] = False
+        if not om.any():
+            continue
+        qi = block_tokens(N, b, i)
+        z = scale * (Q[qi] @ Kb[om].T) + logn[om]
+        mx = z.max(axis=1, keepdims=True)
+        e = np.exp(z - mx)
+        ssum = e.sum(axis=1)
+        L[qi] = mx[:, 0] + np.log(ssum)
+        O[qi] = (e @ Vb[om]) / ssum[:, None]
+    return O, L
+
+
+def pooled_rectified_attention(Q, K, V, rows: list[list[int]], b: int, scale: float):
+    """Sparse attention over the kept blocks, rectified by the pooled
+    estimate of the omitted ones through the exact LSE merge."""
+    Os, Ls = block_sparse_attention(Q, K, V, rows, b, scale)
+    Op, Lp = pooled_omitted_attention(Q, K, V, rows, b, scale)
+    return lse_merge(Os, Ls, Op, Lp)
 
 
 # ----------------------------------------------------------------------------

@@ -444,6 +444,85 @@ def test_macro_plus_all_micro_equals_full_attention():
         Lf, scipy.special.logsumexp(s * Q @ K.T, axis=1), atol=1e-12)
 
 
+# ------------------------------------------------------- pooled rectification
+
+def _blockwise_constant_keys(seed, N, b, d):
+    """Keys equal within every block (each block's keys are its first key)."""
+    K = _rand(seed, N, d)
+    for j in range(O.n_blocks(N, b)):
+        t = O.block_tokens(N, b, j)
+        K[t] = K[t[0]]
+    return K
+
+
+def test_rectification_is_exact_for_blockwise_constant_keys():
+    # a block whose keys are all equal contributes exactly n_j e^{s q.k}
+    # to the normaliser and n_j e^{s q.k} Vbar_j to the output, so the
+    # rectified result is full attention (torch SDPA in fp64), whatever V is
+    N, b, d = 64 * 5 + 21, 64, 8       # ragged tail of 21 tokens
+    s = 1 / math.sqrt(d)
+    Q, V = _rand(50, N, d), _rand(51, N, d)
+    K = _blockwise_constant_keys(52, N, b, d)
+    nB = O.n_blocks(N, b)
+    rows = [[i] for i in range(nB)]
+    rows[2] = []                           # an empty row: pooled keys only
+    rows[4] = list(range(nB))              # nothing omitted: the sparse result
+    Orc, Lrc = O.pooled_rectified_attention(Q, K, V, rows, b, s)
+    tq, tk, tv = (torch.from_numpy(x)[None, None] for x in (Q, K, V))
+    ref = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, scale=s)[0, 0].numpy()
+    np.testing.assert_allclose(Orc, ref, atol=1e-12)
+    np.testing.assert_allclose(Lrc, scipy.special.logsumexp(s * Q @ K.T, axis=1), atol=1e-12)
+
+
+def test_pooled_part_of_a_full_row_is_empty_and_merge_keeps_sparse():
+    N, b, d = 64 * 3, 64, 4
+    Q, K, V = _rand(53, N, d), _rand(54, N, d), _rand(55, N, d)
+    rows = [[0, 1, 2], [1], [0, 2]]
+    Op, Lp = O.pooled_omitted_attention(Q, K, V, rows, b, 0.5)
+    assert np.all(np.isneginf(Lp[:64])) and np.all(Op[:64] == 0)
+    Os, Ls = O.block_sparse_attention(Q, K, V, rows, b, 0.5)
+    Orc, Lrc = O.pooled_rectified_attention(Q, K, V, rows, b, 0.5)
+    np.testing.assert_allclose(Orc[:64], Os[:64], atol=1e-14)
+    np.testing.assert_allclose(Lrc[:64], Ls[:64], atol=1e-14)
+
+
+def test_pooled_part_is_a_size_weighted_mixture_of_block_means():
+    # brute force from the definition with explicit loops: weights n_j
+    # e^{s q.Kbar_j} over the omitted blocks, normalised; output the
+    # weighted mean of the value means
+    N, b, d, s = 64 * 2 + 10, 64, 3, 0.7
+    Q, K, V = _rand(56, N, d), _rand(57, N, d), _rand(58, N, d)
+    rows = [[0], [2], []]
+    Op, Lp = O.pooled_omitted_attention(Q, K, V, rows, b, s)
+    for t in (0, 63, 64, 130, N - 1):
+        i = t // b
+        num, den = np.zeros(d), 0.0
+        for j in range(3):
+            if j in rows[i]:
+                continue
+            toks = range(b * j, min(b * j + b, N))
+            kb = sum(K[x] for x in toks) / len(toks)
+            vb = sum(V[x] for x in toks) / len(toks)
+            w = len(toks) * math.exp(s * float(Q[t] @ kb))
+            num += w * vb
+            den += w
+        np.testing.assert_allclose(Op[t], num / den, atol=1e-13)
+        assert abs(Lp[t] - math.log(den)) < 1e-13
+
+
+def test_rectification_pin_catches_a_dropped_size_bias(monkeypatch):
+    real_sizes = O.block_sizes
+    monkeypatch.setattr(O, "block_sizes", lambda N_, b_: np.ones_like(real_sizes(N_, b_)))
+    N, b, d = 64 * 3 + 5, 64, 4
+    s = 0.5
+    Q, V = _rand(59, N, d), _rand(60, N, d)
+    K = _blockwise_constant_keys(61, N, b, d)
+    Orc, _ = O.pooled_rectified_attention(Q, K, V, [[0], [1], [], [3]], b, s)
+    tq, tk, tv = (torch.from_numpy(x)[None, None] for x in (Q, K, V))
+    ref = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, scale=s)[0, 0].numpy()
+    assert not np.allclose(Orc, ref, atol=1e-6)
+
+
 # ------------------------------------------------------------ omission risk
 
 def test_golden_omission_three_keys():
