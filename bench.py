@@ -62,6 +62,9 @@ def parse():
                     help="replace the workload's selection by a fixed MOD-DiT-style structural "
                          "mask: intra-frame block-diagonal, temporal diagonals at 1 and 2 "
                          "frames, 4 vertical columns")
+    ap.add_argument("--rectify", action="store_true",
+                    help="add the pooled rectification of omitted blocks to the step and "
+                         "report its cost and its effect on the error against dense attention")
     ap.add_argument("--calibration-copy", action="store_true",
                     help="first run a plain 256 MiB device copy (reads 256 MiB, writes "
                          "256 MiB) three times, to scale hardware byte counters")
@@ -201,6 +204,7 @@ def main():
         sel_desc += f"; micro m={m} on {len(heads)} of {H} heads"
 
     ws = bsa.attn_workspace(Q)
+    ws_rect = bsa.rectify_workspace(Q) if args.rectify else None
     O_buf = torch.empty(Q.shape, dtype=torch.float32, device=dev)
     L_buf = torch.empty(Q.shape[:3], dtype=torch.float32, device=dev)
     if micro is not None:
@@ -230,6 +234,8 @@ def main():
         sc = score() if (mode != "static" or micro) else {"scores": None}
         rp, ci, nnz = select(sc, call)
         bsa.bsa_sparse_attn_fwd(Q, K, V, rp, ci, out=O_buf, lse=L_buf, workspace=ws)
+        if args.rectify:
+            bsa.bsa_pooled_rectify(Q, K, V, rp, ci, O_buf, L_buf, workspace=ws_rect)
         mnnz = None
         if micro is not None:
             mrp, mci, mnnz = micro_select(sc, rp, ci)
@@ -339,10 +345,40 @@ def main():
         risk_out["heads_at_risk"] = bsa.heads_at_risk(mean_w, len(mh))
         risk_out["micro_heads"] = list(mh)
 
+    rect_out = None
+    if args.rectify:
+        # its cost, and mean |O - O_dense| over the whole layer before and after
+        Os = torch.empty_like(O_buf)
+        Ls = torch.empty_like(L_buf)
+        bsa.bsa_sparse_attn_fwd(Q, K, None, rp, ci, out=Os, lse=Ls, workspace=ws)
+        Or, Lr = Os.clone(), Ls.clone()
+        bsa.bsa_pooled_rectify(Q, K, V, rp, ci, Or, Lr, workspace=ws_rect)
+        Od = torch.empty_like(O_buf)
+        Ld = torch.empty_like(L_buf)
+        bsa.bsa_dense_attn_fwd(Q, K, None, out=Od, lse=Ld, workspace=ws)
+
+        def rect_once():
+            Or.copy_(Os)
+            Lr.copy_(Ls)
+            bsa.bsa_pooled_rectify(Q, K, V, rp, ci, Or, Lr, workspace=ws_rect)
+
+        copy_ms, _ = events_ms(lambda: (Or.copy_(Os), Lr.copy_(Ls)), reps, stream)
+        rect_ms, _ = events_ms(rect_once, reps, stream)
+        rect_ms = max(rect_ms - copy_ms, 1e-6)
+        omitted_pairs = B * H * bsa.n_blocks(N) ** 2 - nnz_v
+        rect_out = {"kernel_ms": round(rect_ms, 4),
+                    "tflops": round(4 * d * 64 * omitted_pairs / (rect_ms * 1e-3) / 1e12, 2),
+                    "mean_abs_err_vs_dense_sparse": float((Os - Od).abs().mean()),
+                    "mean_abs_err_vs_dense_rectified": float((Or - Od).abs().mean()),
+                    "mean_abs_lse_err_vs_dense_sparse": float((Ls - Ld).abs().mean()),
+                    "mean_abs_lse_err_vs_dense_rectified": float((Lr - Ld).abs().mean())}
+        del Os, Or, Od
+
     attn_tflops = macro_flops / (attn_ms * 1e-3) / 1e12
     kernel_src = os.path.join(ROOT, "block_sparse_attention_pool_amd", "csrc", "attn.hip")
     # the committed counters were taken on the default workload and selection
-    traffic = traffic_entry(kernel_src) if (cfg == 1 and blk == 64 and not args.mod_mask) else None
+    traffic = (traffic_entry(kernel_src)
+               if (cfg == 1 and blk == 64 and not args.mod_mask and not args.rectify) else None)
     out = {
         "metric": METRIC,
         "value": round(exec_flops / step_s / 1e12, 2),
@@ -373,11 +409,13 @@ def main():
         "stages_ms": stages,
         "stage_gbs": gbs,
         "omission_risk": risk_out,
+        **({"pooled_rectify": rect_out} if rect_out is not None else {}),
         "roofline": {"bound": "mfma", "achieved": round(attn_tflops, 2), "peak": PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(attn_tflops / PEAK_TFLOPS, 4),
                      "traffic": traffic},
     }
-    if not args.no_cpu_baseline and cfg == 1 and blk == 64 and not args.mod_mask:
+    if not args.no_cpu_baseline and cfg == 1 and blk == 64 and not args.mod_mask \
+            and not args.rectify:
         rows = {"k": sel["k"]}
         out["cpu_baseline"] = cpu_oracle_sample(Qc, Kc, Vc, rows, args.cpu_seconds)
     print(json.dumps(out), flush=True)

@@ -77,6 +77,8 @@ def _load(path: str = _LIB_PATH):
                                    I32),
         "bsa_lse_merge": ([P, P, P, P, SP, I32, P, P, P, P], I32),
         "bsa_omission_risk_workspace_bytes": ([SP], I64),
+        "bsa_pooled_rectify_workspace_bytes": ([SP], I64),
+        "bsa_pooled_rectify": ([P, P, P, SP, I32, F32, P, P, P, I32, P, P, I64, P], I32),
         "bsa_omission_risk": ([P, P, P, SP, P, P, I64, P], I32),
     }
     for name, (args, res) in sig.items():
@@ -90,7 +92,8 @@ _lib = _load()
 EXPORTED = ("bsa_version", "bsa_last_error", "bsa_score_blocks", "bsa_select_workspace_bytes",
             "bsa_select_max_nnz", "bsa_select_blocks", "bsa_attn_workspace_bytes",
             "bsa_sparse_attn_fwd", "bsa_dense_attn_fwd", "bsa_micro_residual_fwd",
-            "bsa_lse_merge", "bsa_omission_risk_workspace_bytes", "bsa_omission_risk")
+            "bsa_lse_merge", "bsa_omission_risk_workspace_bytes", "bsa_omission_risk",
+            "bsa_pooled_rectify_workspace_bytes", "bsa_pooled_rectify")
 
 
 def library_path() -> str:
@@ -355,6 +358,31 @@ def bsa_lse_merge(O1, L1, O2, L2, *, head_mask=None, out=None, lse_out=None, str
                             _odt(O1.dtype), hm, _ptr(O), _ptr(L), _stream(stream, O1.device))
     _check(st, "bsa_lse_merge")
     return O, L
+
+
+def rectify_workspace(Q) -> torch.Tensor:
+    shp = shape_of(Q)
+    n = _lib.bsa_pooled_rectify_workspace_bytes(ctypes.byref(shp))
+    if n < 0:
+        raise BsaError(f"bsa_pooled_rectify_workspace_bytes: {bsa_last_error()}")
+    return torch.empty(max(n, 256), dtype=torch.uint8, device=Q.device)
+
+
+def bsa_pooled_rectify(Q, K, V, row_ptr, col_idx, O, LSE, *, block: int = BLOCK,
+                       scale: float | None = None, workspace=None, stream=None):
+    """Adds the pooled estimate of every row's omitted key blocks to the
+    sparse result (O, LSE) of the same CSR, in place.  Returns (O, LSE)."""
+    _same_layout(Q, K, V)
+    shp = shape_of(Q)
+    if O.shape != Q.shape or O.stride() != Q.stride():
+        raise ValueError("O must share shape and strides with Q")
+    scale = 1.0 / math.sqrt(shp.d) if scale is None else scale
+    ws = rectify_workspace(Q) if workspace is None else workspace
+    st = _lib.bsa_pooled_rectify(_ptr(Q), _ptr(K), _ptr(V), ctypes.byref(shp), block, scale,
+                                 _ptr(row_ptr), _ptr(col_idx), _ptr(O), _odt(O.dtype), _ptr(LSE),
+                                 _ptr(ws), ws.numel(), _stream(stream, Q.device))
+    _check(st, "bsa_pooled_rectify")
+    return O, LSE
 
 
 def bsa_omission_risk(lse_sparse, lse_full, lse_repaired=None, *, out=None, stream=None):

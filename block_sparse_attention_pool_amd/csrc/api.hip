@@ -77,6 +77,25 @@ bsa_status check_risk_shape(const bsa_shape* s, int64_t* chunks) {
   return BSA_OK;
 }
 
+struct RectifyPlan {
+  int64_t nB, nBp, BH, bytes_f, bytes_h, total;
+};
+
+bsa_status plan_rectify(const bsa_shape* s, RectifyPlan* pl) {
+  BSA_TRY(check_shape(s));
+  pl->nB = cdiv(s->N, 64);
+  if (pl->nB > 32 * bsa::kMaxRowWords)
+    return fail(BSA_ERR_UNSUPPORTED, "nB=%lld exceeds %d blocks", (long long)pl->nB,
+                32 * bsa::kMaxRowWords);
+  pl->BH = (int64_t)s->B * s->H;
+  if (pl->BH > 65535) return fail(BSA_ERR_UNSUPPORTED, "B*H exceeds 65535");
+  pl->nBp = cdiv(pl->nB, 16) * 16;
+  pl->bytes_f = align256(pl->BH * pl->nB * s->d * 4);   // each of Kbar, Vbar (float32)
+  pl->bytes_h = align256(pl->BH * pl->nBp * s->d * 2);  // each of Khi, Klo, Vbar^T (16-bit)
+  pl->total = 2 * pl->bytes_f + 3 * pl->bytes_h;
+  return BSA_OK;
+}
+
 bsa::HeadList all_heads(int H) {
   bsa::HeadList l;
   l.n = H;
@@ -582,6 +601,76 @@ bsa_status bsa_omission_risk(const float* lse_sparse, const float* lse_full,
   a.chunks = (int)chunks;
   a.BH = shape->B * shape->H;
   return hip_status(bsa::launch_risk(a, (hipStream_t)stream), "omission risk launch");
+}
+
+int64_t bsa_pooled_rectify_workspace_bytes(const bsa_shape* shape) {
+  RectifyPlan pl;
+  if (plan_rectify(shape, &pl) != BSA_OK) return -1;
+  return pl.total;
+}
+
+bsa_status bsa_pooled_rectify(const uint16_t* Q, const uint16_t* K, const uint16_t* V,
+                              const bsa_shape* shape, int32_t block, float scale,
+                              const int32_t* row_ptr, const int32_t* col_idx, void* O,
+                              int32_t o_dtype, float* LSE, void* workspace,
+                              int64_t workspace_bytes, void* stream) {
+  RectifyPlan pl;
+  BSA_TRY(plan_rectify(shape, &pl));
+  if (block != 64) return fail(BSA_ERR_UNSUPPORTED, "block=%d unsupported (64)", block);
+  BSA_TRY(check_ptr(Q, "Q"));
+  BSA_TRY(check_ptr(K, "K"));
+  BSA_TRY(check_ptr(V, "V"));
+  BSA_TRY(check_ptr(O, "O"));
+  BSA_TRY(check_ptr(LSE, "LSE", 4));
+  BSA_TRY(check_ptr(row_ptr, "row_ptr", 4));
+  BSA_TRY(check_ptr(col_idx, "col_idx", 4));
+  BSA_TRY(check_ptr(workspace, "workspace", 256));
+  if (o_dtype != BSA_F32 && o_dtype != BSA_BF16)
+    return fail(BSA_ERR_INVALID_ARG, "o_dtype=%d (BSA_F32 or BSA_BF16)", o_dtype);
+  if (workspace_bytes < pl.total)
+    return fail(BSA_ERR_CAPACITY, "workspace %lld bytes < required %lld",
+                (long long)workspace_bytes, (long long)pl.total);
+  hipStream_t st = (hipStream_t)stream;
+  char* ws = (char*)workspace;
+  float* Kf = (float*)ws;
+  float* Vf = (float*)(ws + pl.bytes_f);
+  // block means of K and V: the pooling kernel with K in the query slot
+  bsa::PoolArgs p{};
+  p.Q = K;
+  p.K = V;
+  p.sb = shape->stride_b;
+  p.sh = shape->stride_h;
+  p.sn = shape->stride_n;
+  p.H = shape->H;
+  p.N = shape->N;
+  p.D = shape->d;
+  p.nB = (int)pl.nB;
+  p.nT = (int)cdiv(shape->N, 16);
+  p.block = 64;
+  p.qpool = Kf;
+  p.kpool = Vf;
+  BSA_TRY(hip_status(bsa::launch_pool(p, shape->B, st), "pool launch"));
+  bsa::RectifyArgs a{};
+  a.Q = Q;
+  a.Kf = Kf;
+  a.Vf = Vf;
+  a.Khi = (uint16_t*)(ws + 2 * pl.bytes_f);
+  a.Klo = (uint16_t*)(ws + 2 * pl.bytes_f + pl.bytes_h);
+  a.Vt = (uint16_t*)(ws + 2 * pl.bytes_f + 2 * pl.bytes_h);
+  a.row_ptr = row_ptr;
+  a.col_idx = col_idx;
+  a.O = O;
+  a.LSE = LSE;
+  a.sb = shape->stride_b;
+  a.sh = shape->stride_h;
+  a.sn = shape->stride_n;
+  a.H = shape->H;
+  a.N = shape->N;
+  a.nB = (int)pl.nB;
+  a.nBp = (int)pl.nBp;
+  a.scale_log2 = scale * 1.4426950408889634f;
+  return hip_status(bsa::launch_rectify(a, (int)pl.BH, shape->d, o_dtype == BSA_BF16, st),
+                    "rectify launch");
 }
 
 }  // extern "C"

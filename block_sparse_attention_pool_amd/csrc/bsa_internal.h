@@ -124,6 +124,25 @@ struct RiskArgs {
   int N, chunks, BH;
 };
 
+// Pooled rectification of omitted blocks.
+constexpr int kMaxRowWords = 128;  // bitmap words of a row of up to 4096 blocks
+
+struct RectifyArgs {
+  const uint16_t* Q;
+  const float* Kf;   // [BH, nB, D] 64-token means of K (workspace)
+  const float* Vf;   // [BH, nB, D] 64-token means of V (workspace)
+  uint16_t* Khi;     // [BH, nBp, D] bf16 high part of Kbar
+  uint16_t* Klo;     // [BH, nBp, D] bf16 low part
+  uint16_t* Vt;      // [BH, nBp/16, D, 16] fp16 Vbar, 16-block chunks
+  const int32_t* row_ptr;
+  const int32_t* col_idx;
+  void* O;           // in: sparse result; out: rectified
+  float* LSE;
+  int64_t sb, sh, sn;
+  int H, N, nB, nBp;
+  float scale_log2;
+};
+
 hipError_t launch_pool(const PoolArgs& a, int B, hipStream_t s);
 hipError_t launch_score_gemm(const GemmArgs& a, int nbatch, hipStream_t s);
 hipError_t launch_fill_i32(int32_t* p, int64_t n, int32_t v, hipStream_t s);
@@ -148,5 +167,6 @@ hipError_t launch_micro_attn(const MicroAttnArgs& a, int B, int D,
                              bool out_bf16, hipStream_t s);
 hipError_t launch_merge(const MergeArgs& a, int B, bool bf16, hipStream_t s);
 hipError_t launch_risk(const RiskArgs& a, hipStream_t s);
+hipError_t launch_rectify(const RectifyArgs& a, int BH, int D, bool out_bf16, hipStream_t s);
 
 }  // namespace bsa

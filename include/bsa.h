@@ -12,6 +12,8 @@
  *   bsa_micro_residual_fwd attention over the selected 16x16 micro tiles;
  *   bsa_lse_merge         exact merge of two partial softmax results.
  *   bsa_dense_attn_fwd    the same attention engine over every key (baseline).
+ *   bsa_pooled_rectify    add the pooled estimate of the omitted blocks to a
+ *                         sparse result (exact LSE merge).
  *   bsa_omission_risk     per-head share of the full softmax mass a sparse
  *                         support omits (offline head calibration).
  *
@@ -284,6 +286,41 @@ bsa_status bsa_lse_merge(const void* O1, const float* L1, const void* O2,
                          const float* L2, const bsa_shape* shape,
                          int32_t o_dtype, const uint8_t* head_mask, void* O,
                          float* L, void* stream);
+
+/* ------------------------------------------------------------------------
+ * bsa_pooled_rectify -- pooled rectification of omitted blocks ("Rectified
+ * SpaAttn", abstract: sparse attention over-weights the kept blocks and
+ * loses the omitted ones; pooled query-key interactions correct both).  The
+ * page gives no formulas.  Reading used here: for every valid query token t
+ * of 64-token block i, each key block j NOT in row i contributes its pooled
+ * estimate, with Kbar_j, Vbar_j the means of K, V over the n_j valid tokens
+ * of block j:
+ *   LSE_p[t] = ln sum_j n_j exp(scale q_t . Kbar_j)
+ *   O_p[t]   = sum_j n_j exp(scale q_t . Kbar_j - LSE_p[t]) Vbar_j
+ * (exact when block j's keys are all equal), and the call replaces the
+ * sparse result (O, LSE) by its exact LSE merge with (O_p, LSE_p), as
+ * bsa_lse_merge would.  A row that keeps every block is left as it is.  The
+ * page's gain-aware gate has no stated rule and is not applied.
+ *
+ * O, LSE: on entry the bsa_sparse_attn_fwd result for the same Q, K, V and
+ *   CSR (o_dtype BSA_F32 or BSA_BF16); on return the rectified result.
+ * row_ptr / col_idx: the 64-token CSR the sparse result was computed on.
+ * block: 64.  Limits: nB = ceil(N / 64) <= 4096, B*H <= 65535.
+ * Precision: q . Kbar on bf16 matrix-core products with Kbar split into
+ *   bf16 high and low parts (about 16 mantissa bits), Vbar as fp16, float32
+ *   accumulation and softmax.
+ * workspace: device, >= bsa_pooled_rectify_workspace_bytes(shape) bytes,
+ *   256-byte aligned (the pooled means and their matrix-core copies).
+ * ---------------------------------------------------------------------- */
+int64_t bsa_pooled_rectify_workspace_bytes(const bsa_shape* shape);
+
+bsa_status bsa_pooled_rectify(const uint16_t* Q, const uint16_t* K,
+                              const uint16_t* V, const bsa_shape* shape,
+                              int32_t block, float scale,
+                              const int32_t* row_ptr, const int32_t* col_idx,
+                              void* O, int32_t o_dtype, float* LSE,
+                              void* workspace, int64_t workspace_bytes,
+                              void* stream);
 
 /* ------------------------------------------------------------------------
  * bsa_omission_risk -- per-head omission risk of a sparse support.  The

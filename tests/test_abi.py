@@ -223,3 +223,26 @@ def test_pattern_validation():
     sp.n_columns = 2                       # count without a list
     assert bsa._lib.bsa_select_workspace_bytes(ctypes.byref(s), 64, ctypes.byref(sp)) == -1
     assert "NULL" in bsa.bsa_last_error()
+
+
+def test_pooled_rectify_validation_and_workspace():
+    s = _shape(B=1, H=2, N=1000)          # 16 blocks, padded to 16
+    need = bsa._lib.bsa_pooled_rectify_workspace_bytes(ctypes.byref(s))
+    f32 = -(-(2 * 16 * 128 * 4) // 256) * 256
+    h16 = -(-(2 * 16 * 128 * 2) // 256) * 256
+    assert need == 2 * f32 + 3 * h16
+    p = ctypes.c_void_p(4096)
+    st = bsa._lib.bsa_pooled_rectify(p, p, p, ctypes.byref(s), 64, 0.1, p, p, p, 0, p, p,
+                                     need - 1, None)
+    assert st == 3 and "workspace" in bsa.bsa_last_error()
+    st = bsa._lib.bsa_pooled_rectify(p, p, None, ctypes.byref(s), 64, 0.1, p, p, p, 0, p, p,
+                                     need, None)
+    assert st == 1 and "V is NULL" in bsa.bsa_last_error()
+    st = bsa._lib.bsa_pooled_rectify(p, p, p, ctypes.byref(s), 128, 0.1, p, p, p, 0, p, p,
+                                     need, None)
+    assert st == 2 and "block" in bsa.bsa_last_error()
+    st = bsa._lib.bsa_pooled_rectify(p, p, p, ctypes.byref(s), 64, 0.1, p, p, p, 5, p, p,
+                                     need, None)
+    assert st == 1 and "o_dtype" in bsa.bsa_last_error()
+    big = _shape(N=4097 * 64)
+    assert bsa._lib.bsa_pooled_rectify_workspace_bytes(ctypes.byref(big)) == -1

@@ -1,0 +1,143 @@
+"""GPU parity of the pooled rectification of omitted blocks
+(bsa_pooled_rectify) against the fp64 oracle, with the attention tolerances
+(O max <= 1e-2, mean <= 1e-3, LSE <= 1e-3): small ragged shapes, both head
+dims, float32 and bf16 outputs, strided layouts, rows that keep nothing and
+rows that keep everything; the exact case (keys equal within every block:
+rectified attention is full attention); the 32K-token layer at full size on
+sampled query blocks."""
+
+import math
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import bsa_oracle as O
+from synth import CONFIGS, VideoSpec, config_spec, gen_qkv
+import parity as PT
+
+pytestmark = pytest.mark.gpu
+
+if torch.cuda.is_available():
+    import block_sparse_attention_pool_amd as bsa
+else:  # collected on CPU, skipped by the marker
+    bsa = None
+
+DEV = "cuda:0"
+
+
+def say(*a):
+    print("[gpu-rectify]", *a, file=sys.stderr, flush=True)
+
+
+def oracle_rows(Q, K, b, h, k, diag):
+    N, d = Q.shape[2], Q.shape[3]
+    q, kk = PT.head64(Q, b, h), PT.head64(K, b, h)
+    S = O.pooled_scores(O.pool_means(q, 64), O.pool_means(kk, 64), 1 / math.sqrt(d))
+    return O.select_rows(S, N, 64, "topk", k=k, force_diag=diag)
+
+
+def run_case(Q, K, V, rows, out_dtype=torch.float32, strided=False):
+    B, H, N, d = Q.shape
+    if strided:
+        Qd, Kd, Vd = [x.transpose(1, 2).contiguous().to(DEV).transpose(1, 2) for x in (Q, K, V)]
+    else:
+        Qd, Kd, Vd = (x.to(DEV) for x in (Q, K, V))
+    rp, ci = PT.rows_to_csr([r for b in range(B) for h in range(H) for r in rows[(b, h)]])
+    rp, ci = rp.to(DEV), ci.to(DEV)
+    O_ = torch.empty_strided(Qd.shape, Qd.stride(), dtype=out_dtype, device=DEV)
+    Og, Lg = bsa.bsa_sparse_attn_fwd(Qd, Kd, Vd, rp, ci, out=O_)
+    L_sparse = Lg.clone()
+    bsa.bsa_pooled_rectify(Qd, Kd, Vd, rp, ci, Og, Lg)
+    torch.cuda.synchronize()
+    return Og, Lg, L_sparse
+
+
+SMALL = [
+    ((3, 7, 9), 3, 128, 141),
+    ((5, 15, 21), 2, 128, 142),
+    ((4, 16, 16), 2, 64, 143),
+    ((1, 1, 65), 1, 64, 144),
+    ((2, 9, 50), 1, 128, 145),     # 900 tokens: 15 blocks, one partial 16-block step
+]
+
+
+@pytest.mark.parametrize("grid,H,d,key", SMALL)
+@pytest.mark.parametrize("out_dtype,strided", [(torch.float32, False), (torch.bfloat16, True)])
+def test_rectify_small(grid, H, d, key, out_dtype, strided):
+    spec = VideoSpec(1, H, d, grid, key)
+    say("rectify", grid, H, d, out_dtype, strided)
+    Q, K, V = gen_qkv(spec)
+    N = spec.N
+    nB = O.n_blocks(N, 64)
+    rows = {}
+    for h in range(H):
+        rows[(0, h)] = oracle_rows(Q, K, 0, h, 1, True)
+        if nB > 2:
+            rows[(0, h)][1] = []                      # keeps nothing: pooled keys only
+            rows[(0, h)][nB - 1] = list(range(nB))    # keeps everything: unchanged
+    Og, Lg, Ls = run_case(Q, K, V, rows, out_dtype, strided)
+    for h in range(H):
+        q, k, v = PT.head64(Q, 0, h), PT.head64(K, 0, h), PT.head64(V, 0, h)
+        Oref, Lref = O.pooled_rectified_attention(q, k, v, rows[(0, h)], 64, 1 / math.sqrt(d))
+        # a bf16 O is rounded by the sparse kernel's store and again by the
+        # rectified store: two half-ulp roundings
+        e = PT.compare_o_lse(Og[0, h], Lg[0, h], Oref, Lref, f"h{h}",
+                             bf16=out_dtype == torch.bfloat16, roundings=2)
+        say("   max/mean |dO|", e)
+        if nB > 2:
+            # a row that keeps every block is left exactly as it was
+            t = O.block_tokens(N, 64, nB - 1)
+            assert torch.equal(Lg[0, h, t[0]:t[-1] + 1], Ls[0, h, t[0]:t[-1] + 1])
+    # the pooled part only adds mass
+    assert bool((Lg >= Ls - 1e-6).all())
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_rectify_exact_for_blockwise_constant_keys(d):
+    spec = VideoSpec(1, 2, d, (3, 10, 13), 146)     # 390 tokens, ragged tail of 6
+    Q, K, V = gen_qkv(spec)
+    N = spec.N
+    for j in range(O.n_blocks(N, 64)):
+        t = torch.from_numpy(O.block_tokens(N, 64, j))
+        K[:, :, t] = K[:, :, t[:1]]
+    say("rectify exact case", d)
+    rows = {(0, h): [[i] for i in range(O.n_blocks(N, 64))] for h in range(2)}
+    Og, Lg, _ = run_case(Q, K, V, rows)
+    for h in range(2):
+        q, k, v = PT.head64(Q, 0, h), PT.head64(K, 0, h), PT.head64(V, 0, h)
+        Oref, Lref = O.dense_attention(q, k, v, 1 / math.sqrt(d))
+        PT.compare_o_lse(Og[0, h], Lg[0, h], Oref, Lref, f"h{h} vs full attention")
+
+
+def test_rectify_workload_sampled():
+    cfg = 1
+    c = CONFIGS[cfg]
+    spec = config_spec(cfg)
+    Q, K, V = gen_qkv(spec)
+    B, H, N, d = Q.shape
+    nB = O.n_blocks(N, 64)
+    k = bsa.budget_blocks(c["density"], nB)
+    heads = [0, H - 1]
+    say(f"rectify on {c['name']}: oracle lists of heads {heads}")
+    rows = {(0, h): (oracle_rows(Q, K, 0, h, k, False) if h in heads else [[] for _ in range(nB)])
+            for h in range(H)}
+    Og, Lg, Ls = run_case(Q, K, V, rows)
+    assert torch.isfinite(Lg).all() and bool((Lg >= Ls - 1e-6).all())
+    rng = np.random.default_rng(400)
+    scale = 1 / math.sqrt(d)
+    for h in heads:
+        q, kk, v = PT.head64(Q, 0, h), PT.head64(K, 0, h), PT.head64(V, 0, h)
+        sampled = sorted(set(rng.choice(nB, 4, replace=False).tolist()) | {nB - 1})
+        # the oracle's pooled part on the sampled rows only (a row that keeps
+        # every block has no pooled part and costs nothing)
+        rows_s = [rows[(0, h)][i] if i in sampled else list(range(nB)) for i in range(nB)]
+        Op, Lp = O.pooled_omitted_attention(q, kk, v, rows_s, 64, scale)
+        for i in sampled:
+            qi = O.block_tokens(N, 64, i)
+            keys = np.concatenate([O.block_tokens(N, 64, j) for j in rows[(0, h)][i]])
+            Os, Lsr = O.attend(q[qi], kk[keys], v[keys], scale)
+            Oref, Lref = O.lse_merge(Os, Lsr, Op[qi], Lp[qi])
+            PT.compare_o_lse(Og[0, h, qi[0]:qi[-1] + 1], Lg[0, h, qi[0]:qi[-1] + 1], Oref, Lref,
+                             f"h{h} blk{i}")
