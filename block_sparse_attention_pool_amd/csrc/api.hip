@@ -96,6 +96,28 @@ bsa_status plan_rectify(const bsa_shape* s, RectifyPlan* pl) {
   return BSA_OK;
 }
 
+// Attention workspace: the fp16 V^T copy, then the micro residual's
+// sub-tile ordering (signatures, order, bin counts and offsets, a total),
+// sized for every head.
+struct MicroOrderPlan {
+  int64_t vt_bytes, sig_off, order_off, hist_off, offs_off, nnz_off, order_bytes;
+};
+
+MicroOrderPlan plan_micro_order(const bsa_shape* s) {
+  MicroOrderPlan m{};
+  const int64_t nB = cdiv(s->N, 64), nT = cdiv(s->N, 16);
+  const int64_t bh = (int64_t)s->B * s->H;
+  m.vt_bytes = align256(bh * s->d * nB * 64 * 2);
+  const int64_t slots = bh * nB * 4, bins = bh * (nT + 1);
+  m.sig_off = m.vt_bytes;
+  m.order_off = m.sig_off + align256(slots * 4);
+  m.hist_off = m.order_off + align256(slots * 4);
+  m.offs_off = m.hist_off + align256(bins * 4);
+  m.nnz_off = m.offs_off + align256((bins + 1) * 4);
+  m.order_bytes = m.nnz_off + 256 - m.vt_bytes;
+  return m;
+}
+
 bsa::HeadList all_heads(int H) {
   bsa::HeadList l;
   l.n = H;
@@ -462,8 +484,8 @@ bsa_status bsa_select_blocks(const float* scores, const bsa_shape* shape, int32_
 
 int64_t bsa_attn_workspace_bytes(const bsa_shape* shape) {
   if (check_shape(shape) != BSA_OK) return -1;
-  const int64_t npad = cdiv(shape->N, 64) * 64;
-  return align256((int64_t)shape->B * shape->H * shape->d * npad * 2);
+  const MicroOrderPlan m = plan_micro_order(shape);
+  return m.vt_bytes + m.order_bytes;
 }
 
 bsa_status bsa_sparse_attn_fwd(const uint16_t* Q, const uint16_t* K, const uint16_t* V,
@@ -535,6 +557,17 @@ bsa_status bsa_micro_residual_fwd(const uint16_t* Q, const uint16_t* K, const ui
   a.Npad = nB * 64;
   a.scale_log2 = scale * 1.4426950408889634f;
   a.heads = heads;
+  const MicroOrderPlan m = plan_micro_order(shape);
+  char* ws = (char*)workspace;
+  a.sig = (int32_t*)(ws + m.sig_off);
+  a.order = (int32_t*)(ws + m.order_off);
+  a.hist = (int32_t*)(ws + m.hist_off);
+  a.offsets = (int32_t*)(ws + m.offs_off);
+  a.nnz = (int64_t*)(ws + m.nnz_off);
+  a.nT = (int)cdiv(shape->N, 16);
+  a.slots = (int)((int64_t)shape->B * heads.n * nB * 4);
+  a.bins = shape->B * heads.n * (a.nT + 1);
+  a.per_xcd = (int)cdiv(cdiv(a.slots, 4), 8);
   return hip_status(bsa::launch_micro_attn(a, shape->B, shape->d, o_dtype == BSA_BF16, st),
                     "micro attn launch");
 }

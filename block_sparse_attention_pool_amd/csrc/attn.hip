@@ -520,28 +520,40 @@ void attn_fwd_kernel(AttnArgs a) {
 // O^T = V^T P^T (fp16) whose P^T operand is exactly those 4 accumulator
 // registers.  A tile's K rows (4 KB) and V^T chunk (4 KB) are contiguous;
 // the fragments of tile e+1 are loaded while tile e is computed.
+//
+// Sub-tiles run in the order of `order`: sorted, per head, by the first key
+// tile each one selects, and dealt to the XCDs in contiguous ranges, so that
+// sub-tiles gathering the same tiles run together on one XCD and share them
+// through its L2.  Each sub-tile is computed on its own, so the order changes
+// no result.
 template <int D, bool OUT_BF16>
 __global__ __launch_bounds__(256) void micro_attn_kernel(MicroAttnArgs a) {
   constexpr int KS = D / 32;
   constexpr int DT = D / 16;
-  const int i = blockIdx.x;
-  const int z = blockIdx.y;
+  const int w = blockIdx.x;
+  const int Lw = (w & 7) * a.per_xcd + (w >> 3);
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int slot = 4 * Lw + wave;
+  if (Lw >= (a.slots + 3) / 4 || slot >= a.slots) return;
+  const int sid = a.order[slot];
+  const int sub = sid & 3;
+  const int i = (sid >> 2) % a.nB;
+  const int z = (sid >> 2) / a.nB;
   const int nh = a.heads.n;
   const int b = z / nh, h = a.heads.h[z % nh];
   const int64_t bh = (int64_t)b * a.H + h;
   const int64_t r = bh * a.nB + i;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int n16 = lane & 15, g4 = lane >> 4;
-  const int q0 = i * kBlock + wave * kMicro;
+  const int q0 = i * kBlock + sub * kMicro;
   if (q0 >= a.N) return;
 
   // This sub-tile's segment of the row (entries sorted by sub-tile, then tile).
   const int rb = a.row_ptr[r], re = a.row_ptr[r + 1];
   int lt = 0, le = 0;
   for (int e = rb + lane; e < re; e += 64) {
-    const int sub = a.idx[e] & 3;
-    lt += sub < wave;
-    le += sub <= wave;
+    const int es_sub = a.idx[e] & 3;
+    lt += es_sub < sub;
+    le += es_sub <= sub;
   }
   lt = wave_sum(lt);
   le = wave_sum(le);
@@ -643,6 +655,39 @@ __global__ __launch_bounds__(256) void micro_attn_kernel(MicroAttnArgs a) {
   }
 }
 
+// Signature of every sub-tile: its global bin (z, first key tile selected),
+// nT for an empty sub-tile; a row's entries are sorted by (sub-tile, key
+// tile), so the first entry of sub-tile a is found by binary search.
+__global__ __launch_bounds__(256) void micro_sig_kernel(MicroAttnArgs a) {
+  const int sid = blockIdx.x * 256 + threadIdx.x;
+  if (sid >= a.slots) return;
+  const int sub = sid & 3;
+  const int i = (sid >> 2) % a.nB;
+  const int z = (sid >> 2) / a.nB;
+  const int nh = a.heads.n;
+  const int b = z / nh, h = a.heads.h[z % nh];
+  const int64_t r = ((int64_t)b * a.H + h) * a.nB + i;
+  int lo = a.row_ptr[r], hi = a.row_ptr[r + 1];
+  const int end = hi;
+  while (lo < hi) {  // first entry whose sub-tile is >= sub
+    const int mid = (lo + hi) >> 1;
+    if ((a.idx[mid] & 3) < sub) lo = mid + 1;
+    else hi = mid;
+  }
+  const int first = (lo < end && (a.idx[lo] & 3) == sub) ? (a.idx[lo] >> 2) : a.nT;
+  const int bin = z * (a.nT + 1) + first;
+  a.sig[sid] = bin;
+  atomicAdd(&a.hist[bin], 1);
+}
+
+// Place every sub-tile at its bin's next position (any order inside a bin).
+__global__ __launch_bounds__(256) void micro_scatter_kernel(MicroAttnArgs a) {
+  const int sid = blockIdx.x * 256 + threadIdx.x;
+  if (sid >= a.slots) return;
+  const int pos = atomicAdd(&a.offsets[a.sig[sid]], 1);
+  a.order[pos] = sid;
+}
+
 // ---------------------------------------------------------------- merge
 
 // Each row is handled by D/8 consecutive lanes of one wave, 8 elements per
@@ -726,7 +771,15 @@ hipError_t launch_attn(const AttnArgs& a, int D, bool dense, bool out_bf16, hipS
 }
 
 hipError_t launch_micro_attn(const MicroAttnArgs& a, int B, int D, bool out_bf16, hipStream_t s) {
-  dim3 grid(a.nB, B * a.heads.n);
+  (void)B;
+  hipError_t e = launch_fill_i32(a.hist, a.bins, 0, s);
+  if (e != hipSuccess) return e;
+  const dim3 sgrid((a.slots + 255) / 256);
+  hipLaunchKernelGGL(micro_sig_kernel, sgrid, dim3(256), 0, s, a);
+  e = launch_scan(a.hist, a.bins, a.offsets, a.nnz, s);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(micro_scatter_kernel, sgrid, dim3(256), 0, s, a);
+  dim3 grid(8 * a.per_xcd);
   if (D == 128) {
     if (out_bf16) hipLaunchKernelGGL((micro_attn_kernel<128, true>), grid, dim3(256), 0, s, a);
     else hipLaunchKernelGGL((micro_attn_kernel<128, false>), grid, dim3(256), 0, s, a);

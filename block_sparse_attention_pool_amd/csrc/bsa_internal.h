@@ -90,6 +90,15 @@ struct MicroAttnArgs {
   int H, N, nB, Npad;
   float scale_log2;
   HeadList heads;
+  // sub-tile order: entry k of `order` is sub-tile (z * nB + i) * 4 + a (z =
+  // b * heads.n + micro head slot); workgroup slots are dealt to the XCDs in
+  // contiguous ranges of that order
+  int32_t* sig;      // [slots] global bin of each sub-tile (workspace)
+  int32_t* order;    // [slots] (workspace)
+  int32_t* hist;     // [bins] counts, then (after the scan) cursors
+  int32_t* offsets;  // [bins + 1] (workspace)
+  int64_t* nnz;      // scan total (workspace)
+  int slots, bins, nT, per_xcd;
 };
 
 struct TransposeArgs {

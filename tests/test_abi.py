@@ -64,7 +64,13 @@ def _shape(B=1, H=2, N=1000, d=128, sb=None, sh=None, sn=None):
 def test_workspace_sizes():
     s = _shape(B=1, H=2, N=1000, d=128)
     npad = 16 * 64
-    assert bsa._lib.bsa_attn_workspace_bytes(ctypes.byref(s)) == 2 * 128 * npad * 2
+    # the fp16 V^T copy, then the micro residual's sub-tile ordering: signatures
+    # and order (2 heads x 16 blocks x 4 sub-tiles), bin counts and offsets
+    # (2 heads x 64 bins, + 1), a total
+    a256 = lambda x: -(-x // 256) * 256
+    vt = 2 * 128 * npad * 2
+    order = 2 * a256(128 * 4) + a256(128 * 4) + a256(129 * 4) + 256
+    assert bsa._lib.bsa_attn_workspace_bytes(ctypes.byref(s)) == vt + order
     sp, _ = bsa.make_select_params("topk", k=4, nB=16)
     rows, W = 2 * 16, 1
     ws = bsa._lib.bsa_select_workspace_bytes(ctypes.byref(s), 64, ctypes.byref(sp))
