@@ -13,7 +13,8 @@ definitions below state.
 Sources (pages as titled):
   [HVA]   "HyperVAttention: Efficient Sparse Attention with Spatio-Temporal
           Clustering for Video Diffusion", section 2 (Preliminaries), Eq. 2-4,
-          and Appendix A.1 (Top-p, Min-kc).
+          section 4.1 (3D local-window clustering, Eq. 5), Appendix A.1
+          (Top-p, Min-kc) and A.2 (Algorithm 2).
   [RSA]   "Rectified SpaAttn: Revisiting Attention Sparsity for Efficient Video
           Generation", abstract: pooled query-key interactions.
   [HyMoR] "HyMoR-Attn: Granularity-Matched Repair of Omitted Attention Support
@@ -47,6 +48,9 @@ design notes of the repository):
     128 x 128 pair is its 2 x 2 tiles, the token support unchanged;
   * the omission risk of a query token is the share of its full softmax mass
     outside its sparse support (HyMoR names the risk, not its formula);
+  * [HVA] local-window clustering: argmin ties go to the lower centroid
+    index; the last iteration's assignment and the final centroids are
+    returned;
   * RSA's pooled rectification is read as attention over the pooled keys of
     the omitted blocks (log-size bias), LSE-merged with the sparse result;
     its gain-aware gate has no stated rule and is not modelled.
@@ -536,6 +540,89 @@ def heads_at_risk(mean_omitted: np.ndarray, n: int) -> list[int]:
     ascending: the heads an offline calibration hands the Micro residual."""
     order = sorted(range(len(mean_omitted)), key=lambda h: (-float(mean_omitted[h]), h))
     return sorted(order[:max(0, n)])
+
+
+# ----------------------------------------------------------------------------
+# 3D local-window clustering ([HVA] section 4.1, Eq. 5, Appendix A.2 Alg. 2)
+#
+# Tokens are a T x H x W lattice (t-major).  A fixed grid of cells of size
+# (kt, kh, kw) gives one centroid per cell, initialised at the cell's centre
+# token (clamped to the lattice).  Each iteration assigns every token to the
+# nearest centroid among the cells of a (wt, wh, ww) window around its own
+# cell (the window clipped to the grid), then moves every centroid to the
+# mean of its tokens (a centroid with none keeps its position).  Readings:
+# ties go to the lower centroid index (cells numbered t-major); the returned
+# assignment is that of the last iteration, the centroids those after the
+# last update.
+# ----------------------------------------------------------------------------
+
+def cluster_grid(thw, cell, window):
+    """Cells per axis K = ceil(dim / k) and the window clipped to the grid."""
+    K = tuple(-(-thw[a] // cell[a]) for a in range(3))
+    w = tuple(min(window[a], K[a]) for a in range(3))
+    return K, w
+
+
+def window_start(g: int, w: int, K: int) -> int:
+    """First cell of the window around cell g on one axis: g - floor(w/2),
+    clipped to [0, K - w]."""
+    return min(max(g - w // 2, 0), K - w)
+
+
+def local_window_clustering(X, thw, cell, window, iters: int):
+    """Returns (assignment [N] int, centroids [Nc, d], counts [Nc])."""
+    X = np.asarray(X, np.float64)
+    T, H, W = thw
+    N, d = X.shape
+    assert N == T * H * W and iters >= 1
+    K, w = cluster_grid(thw, cell, window)
+    Kt, Kh, Kw = K
+    cells = [(ut, uh, uw) for ut in range(Kt) for uh in range(Kh) for uw in range(Kw)]
+    cid = lambda ut, uh, uw: (ut * Kh + uh) * Kw + uw
+    tok = lambda t, h, x: (t * H + h) * W + x
+    mu = np.stack([X[tok(min(ut * cell[0] + cell[0] // 2, T - 1),
+                         min(uh * cell[1] + cell[1] // 2, H - 1),
+                         min(uw * cell[2] + cell[2] // 2, W - 1))]
+                   for ut, uh, uw in cells])
+    a = np.zeros(N, dtype=np.int64)
+    for _ in range(iters):
+        for ut, uh, uw in cells:
+            ts = range(ut * cell[0], min(ut * cell[0] + cell[0], T))
+            hs = range(uh * cell[1], min(uh * cell[1] + cell[1], H))
+            ws = range(uw * cell[2], min(uw * cell[2] + cell[2], W))
+            toks = np.array([tok(t, h, x) for t in ts for h in hs for x in ws])
+            st, sh, sw = (window_start(ut, w[0], Kt), window_start(uh, w[1], Kh),
+                          window_start(uw, w[2], Kw))
+            cand = np.array([cid(vt, vh, vw) for vt in range(st, st + w[0])
+                             for vh in range(sh, sh + w[1]) for vw in range(sw, sw + w[2])])
+            dist = ((X[toks][:, None, :] - mu[cand][None, :, :]) ** 2).sum(axis=2)
+            a[toks] = cand[np.argmin(dist, axis=1)]   # first minimum = lowest index
+        counts = np.bincount(a, minlength=len(cells))
+        sums = np.zeros_like(mu)
+        np.add.at(sums, a, X)
+        moved = counts > 0
+        mu[moved] = sums[moved] / counts[moved, None]
+    return a, mu, counts
+
+
+def assignment_margins(X, thw, cell, window, mu):
+    """Per token, the gap between its second-nearest and nearest squared
+    distance over its window's centroids (a tie has gap 0)."""
+    X = np.asarray(X, np.float64)
+    T, H, W = thw
+    K, w = cluster_grid(thw, cell, window)
+    Kt, Kh, Kw = K
+    out = np.zeros(X.shape[0])
+    for t in range(T):
+        for h in range(H):
+            for x in range(W):
+                g = (t // cell[0], h // cell[1], x // cell[2])
+                st = [window_start(g[i], w[i], K[i]) for i in range(3)]
+                cand = [(vt * Kh + vh) * Kw + vw for vt in range(st[0], st[0] + w[0])
+                        for vh in range(st[1], st[1] + w[1]) for vw in range(st[2], st[2] + w[2])]
+                dd = np.sort(((X[(t * H + h) * W + x] - mu[cand]) ** 2).sum(axis=1))
+                out[(t * H + h) * W + x] = dd[1] - dd[0] if len(dd) > 1 else np.inf
+    return out
 
 
 # ----------------------------------------------------------------------------

@@ -444,6 +444,106 @@ def test_macro_plus_all_micro_equals_full_attention():
         Lf, scipy.special.logsumexp(s * Q @ K.T, axis=1), atol=1e-12)
 
 
+# ------------------------------------------------------ local-window clustering
+
+def _brute_force_clustering(X, thw, cell, window, iters):
+    """Algorithm 2 with explicit loops over tokens, cells and dimensions."""
+    T, H, W = thw
+    K = [-(-thw[a] // cell[a]) for a in range(3)]
+    w = [min(window[a], K[a]) for a in range(3)]
+    ncell = K[0] * K[1] * K[2]
+    mu = []
+    for ut in range(K[0]):
+        for uh in range(K[1]):
+            for uw in range(K[2]):
+                c = [min(u * cell[i] + cell[i] // 2, thw[i] - 1) for i, u in enumerate((ut, uh, uw))]
+                mu.append(list(X[(c[0] * H + c[1]) * W + c[2]]))
+    assign = [0] * (T * H * W)
+    counts = [0] * ncell
+    for _ in range(iters):
+        for t in range(T):
+            for h in range(H):
+                for x in range(W):
+                    g = (t // cell[0], h // cell[1], x // cell[2])
+                    best, best_u = None, None
+                    s0 = [min(max(g[i] - w[i] // 2, 0), K[i] - w[i]) for i in range(3)]
+                    for vt in range(s0[0], s0[0] + w[0]):
+                        for vh in range(s0[1], s0[1] + w[1]):
+                            for vw in range(s0[2], s0[2] + w[2]):
+                                u = (vt * K[1] + vh) * K[2] + vw
+                                dd = sum((X[(t * H + h) * W + x][e] - mu[u][e]) ** 2
+                                         for e in range(X.shape[1]))
+                                if best is None or dd < best or (dd == best and u < best_u):
+                                    best, best_u = dd, u
+                    assign[(t * H + h) * W + x] = best_u
+        counts = [0] * ncell
+        sums = [[0.0] * X.shape[1] for _ in range(ncell)]
+        for n, u in enumerate(assign):
+            counts[u] += 1
+            for e in range(X.shape[1]):
+                sums[u][e] += X[n][e]
+        for u in range(ncell):
+            if counts[u]:
+                mu[u] = [v / counts[u] for v in sums[u]]
+    return np.array(assign), np.array(mu), np.array(counts)
+
+
+@pytest.mark.parametrize("thw,cell,window,iters", [((3, 5, 7), (1, 2, 3), (2, 2, 2), 1),
+                                                   ((4, 6, 5), (2, 2, 2), (3, 2, 3), 3),
+                                                   ((2, 7, 9), (2, 3, 2), (1, 3, 3), 2)])
+def test_clustering_matches_brute_force(thw, cell, window, iters):
+    X = _rand(70, thw[0] * thw[1] * thw[2], 3)
+    a, mu, c = O.local_window_clustering(X, thw, cell, window, iters)
+    ab, mub, cb = _brute_force_clustering(X, thw, cell, window, iters)
+    np.testing.assert_array_equal(a, ab)
+    np.testing.assert_allclose(mu, mub, atol=1e-12)
+    np.testing.assert_array_equal(c, cb)
+
+
+def test_clustering_with_a_global_window_is_lloyd_kmeans():
+    # a window covering the whole grid searches every centroid: Algorithm 2
+    # is then plain k-means (Lloyd) from the cell-centre initialisation
+    from sklearn.cluster import KMeans
+    thw, cell, iters = (3, 8, 8), (3, 4, 4), 4
+    X = _rand(71, 3 * 8 * 8, 5) + np.repeat(np.arange(3 * 8 * 8)[:, None] // 48, 5, axis=1)
+    a, mu, c = O.local_window_clustering(X, thw, cell, (9, 9, 9), iters)
+    init = np.stack([X[(min(ut * 3 + 1, 2) * 8 + (uh * 4 + 2)) * 8 + (uw * 4 + 2)]
+                     for ut in range(1) for uh in range(2) for uw in range(2)])
+    # no cluster empties on these inputs, so the library's relocation of
+    # empty clusters never applies
+    assert np.all(c > 0)
+    km = KMeans(n_clusters=4, init=init, n_init=1, max_iter=iters, tol=0.0,
+                algorithm="lloyd").fit(X)
+    np.testing.assert_allclose(mu, km.cluster_centers_, atol=1e-10)
+
+
+def test_clustering_cell_constant_tokens_stay_put():
+    thw, cell = (4, 6, 6), (2, 3, 3)
+    T, H, W = thw
+    rng = np.random.default_rng(72)
+    centres = rng.standard_normal((8, 4)) * 10
+    X = np.zeros((T * H * W, 4))
+    for t in range(T):
+        for h in range(H):
+            for x in range(W):
+                X[(t * H + h) * W + x] = centres[((t // 2) * 2 + h // 3) * 2 + x // 3]
+    a, mu, c = O.local_window_clustering(X, thw, cell, (2, 2, 2), 3)
+    np.testing.assert_array_equal(a, [((t // 2) * 2 + h // 3) * 2 + x // 3
+                                      for t in range(T) for h in range(H) for x in range(W)])
+    np.testing.assert_allclose(mu, centres, atol=1e-12)
+    np.testing.assert_array_equal(c, np.full(8, 18))
+
+
+def test_clustering_pin_catches_an_unclipped_window(monkeypatch):
+    monkeypatch.setattr(O, "window_start", lambda g, w, K: max(g - w // 2, 0))
+    thw, cell, window = (4, 6, 5), (2, 2, 2), (3, 2, 3)
+    X = _rand(70, 4 * 6 * 5, 3)
+    with pytest.raises(Exception):
+        a, mu, c = O.local_window_clustering(X, thw, cell, window, 3)
+        ab, mub, cb = _brute_force_clustering(X, thw, cell, window, 3)
+        np.testing.assert_array_equal(a, ab)
+
+
 # ------------------------------------------------------- pooled rectification
 
 def _blockwise_constant_keys(seed, N, b, d):
