@@ -54,6 +54,11 @@ class _SelectParams(ctypes.Structure):
                 ("n_columns", ctypes.c_int32), ("columns", ctypes.c_void_p)]
 
 
+class _ClusterParams(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in ("T", "Hg", "W", "kt", "kh", "kw", "wt", "wh", "ww",
+                                              "iters")]
+
+
 def _load(path: str = _LIB_PATH):
     if not os.path.exists(path):
         raise ImportError(
@@ -63,6 +68,7 @@ def _load(path: str = _LIB_PATH):
     P, I32, I64, F32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float
     SP = ctypes.POINTER(_Shape)
     PP = ctypes.POINTER(_SelectParams)
+    CP = ctypes.POINTER(_ClusterParams)
     sig = {
         "bsa_version": ([], ctypes.c_char_p),
         "bsa_last_error": ([], ctypes.c_char_p),
@@ -78,6 +84,9 @@ def _load(path: str = _LIB_PATH):
         "bsa_lse_merge": ([P, P, P, P, SP, I32, P, P, P, P], I32),
         "bsa_omission_risk_workspace_bytes": ([SP], I64),
         "bsa_pooled_rectify_workspace_bytes": ([SP], I64),
+        "bsa_cluster_cells": ([SP, CP], I64),
+        "bsa_cluster_workspace_bytes": ([SP, CP], I64),
+        "bsa_local_window_cluster": ([P, SP, CP, P, P, P, P, I64, P], I32),
         "bsa_pooled_rectify": ([P, P, P, SP, I32, F32, P, P, P, I32, P, P, I64, P], I32),
         "bsa_omission_risk": ([P, P, P, SP, P, P, I64, P], I32),
     }
@@ -93,7 +102,8 @@ EXPORTED = ("bsa_version", "bsa_last_error", "bsa_score_blocks", "bsa_select_wor
             "bsa_select_max_nnz", "bsa_select_blocks", "bsa_attn_workspace_bytes",
             "bsa_sparse_attn_fwd", "bsa_dense_attn_fwd", "bsa_micro_residual_fwd",
             "bsa_lse_merge", "bsa_omission_risk_workspace_bytes", "bsa_omission_risk",
-            "bsa_pooled_rectify_workspace_bytes", "bsa_pooled_rectify")
+            "bsa_pooled_rectify_workspace_bytes", "bsa_pooled_rectify", "bsa_cluster_cells",
+            "bsa_cluster_workspace_bytes", "bsa_local_window_cluster")
 
 
 def library_path() -> str:
@@ -383,6 +393,31 @@ def bsa_pooled_rectify(Q, K, V, row_ptr, col_idx, O, LSE, *, block: int = BLOCK,
                                  _ptr(ws), ws.numel(), _stream(stream, Q.device))
     _check(st, "bsa_pooled_rectify")
     return O, LSE
+
+
+def bsa_local_window_cluster(X, thw, cell, window, iters: int = 1, *, stream=None):
+    """3D local-window clustering of a [B, H, N, d] bf16 tensor over the
+    token lattice thw = (T, Hg, W).  Returns (assign int32 [B, H, N],
+    centroids float32 [B, H, cells, d], counts int32 [B, H, cells])."""
+    if X.dtype != torch.bfloat16:
+        raise ValueError("X must be bfloat16")
+    shp = shape_of(X)
+    cp = _ClusterParams(*thw, *cell, *window, iters)
+    cells = _lib.bsa_cluster_cells(ctypes.byref(shp), ctypes.byref(cp))
+    if cells < 0:
+        raise BsaError(f"bsa_cluster_cells: {bsa_last_error()}")
+    nws = _lib.bsa_cluster_workspace_bytes(ctypes.byref(shp), ctypes.byref(cp))
+    B, H, N, d = X.shape
+    dev = X.device
+    assign = torch.empty((B, H, N), dtype=torch.int32, device=dev)
+    mu = torch.empty((B, H, cells, d), dtype=torch.float32, device=dev)
+    counts = torch.empty((B, H, cells), dtype=torch.int32, device=dev)
+    ws = torch.empty(max(nws, 256), dtype=torch.uint8, device=dev)
+    st = _lib.bsa_local_window_cluster(_ptr(X), ctypes.byref(shp), ctypes.byref(cp), _ptr(assign),
+                                       _ptr(mu), _ptr(counts), _ptr(ws), ws.numel(),
+                                       _stream(stream, dev))
+    _check(st, "bsa_local_window_cluster")
+    return assign, mu, counts
 
 
 def bsa_omission_risk(lse_sparse, lse_full, lse_repaired=None, *, out=None, stream=None):

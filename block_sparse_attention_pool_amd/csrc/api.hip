@@ -1,6 +1,7 @@
 // C-ABI entry points declared in include/bsa.h: argument validation (before
 // any HIP call), workspace carving and kernel launches on the caller's
 // stream.  No state is kept between calls and nothing is allocated.
+#include <algorithm>
 #include <cstdarg>
 #include <cstdio>
 #include <string>
@@ -116,6 +117,23 @@ MicroOrderPlan plan_micro_order(const bsa_shape* s) {
   m.nnz_off = m.offs_off + align256((bins + 1) * 4);
   m.order_bytes = m.nnz_off + 256 - m.vt_bytes;
   return m;
+}
+
+bsa_status plan_cluster(const bsa_shape* s, const bsa_cluster_params* p, int64_t* cells) {
+  if (s == nullptr || p == nullptr) return fail(BSA_ERR_INVALID_ARG, "shape or params is NULL");
+  if (s->B < 1 || s->H < 1 || s->N < 1)
+    return fail(BSA_ERR_INVALID_ARG, "shape B=%d H=%d N=%d must all be >= 1", s->B, s->H, s->N);
+  if (s->d != 64 && s->d != 128)
+    return fail(BSA_ERR_UNSUPPORTED, "head dim d=%d unsupported (64 or 128)", s->d);
+  if ((int64_t)s->B * s->H > 65535) return fail(BSA_ERR_UNSUPPORTED, "B*H exceeds 65535");
+  if (p->T < 1 || p->Hg < 1 || p->W < 1 || (int64_t)p->T * p->Hg * p->W != s->N)
+    return fail(BSA_ERR_INVALID_ARG, "lattice %d x %d x %d does not hold N=%d tokens", p->T, p->Hg,
+                p->W, s->N);
+  if (p->kt < 1 || p->kh < 1 || p->kw < 1 || p->wt < 1 || p->wh < 1 || p->ww < 1)
+    return fail(BSA_ERR_INVALID_ARG, "cell and window sizes must be >= 1");
+  if (p->iters < 1) return fail(BSA_ERR_INVALID_ARG, "iters=%d < 1", p->iters);
+  *cells = cdiv(p->T, p->kt) * cdiv(p->Hg, p->kh) * cdiv(p->W, p->kw);
+  return BSA_OK;
 }
 
 bsa::HeadList all_heads(int H) {
@@ -704,6 +722,66 @@ bsa_status bsa_pooled_rectify(const uint16_t* Q, const uint16_t* K, const uint16
   a.scale_log2 = scale * 1.4426950408889634f;
   return hip_status(bsa::launch_rectify(a, (int)pl.BH, shape->d, o_dtype == BSA_BF16, st),
                     "rectify launch");
+}
+
+int64_t bsa_cluster_cells(const bsa_shape* shape, const bsa_cluster_params* params) {
+  int64_t cells = 0;
+  if (plan_cluster(shape, params, &cells) != BSA_OK) return -1;
+  return cells;
+}
+
+int64_t bsa_cluster_workspace_bytes(const bsa_shape* shape, const bsa_cluster_params* params) {
+  int64_t cells = 0;
+  if (plan_cluster(shape, params, &cells) != BSA_OK) return -1;
+  return align256((int64_t)shape->B * shape->H * cells * 4);
+}
+
+bsa_status bsa_local_window_cluster(const uint16_t* X, const bsa_shape* shape,
+                                    const bsa_cluster_params* p, int32_t* assign,
+                                    float* centroids, int32_t* counts, void* workspace,
+                                    int64_t workspace_bytes, void* stream) {
+  int64_t cells = 0;
+  BSA_TRY(plan_cluster(shape, p, &cells));
+  if (shape->stride_n < shape->d || shape->stride_n % 8 || shape->stride_h % 8 ||
+      shape->stride_b % 8 || shape->stride_h < 0 || shape->stride_b < 0)
+    return fail(BSA_ERR_INVALID_ARG, "strides must be multiples of 8 elements (n >= d)");
+  BSA_TRY(check_ptr(X, "X"));
+  BSA_TRY(check_ptr(assign, "assign", 4));
+  BSA_TRY(check_ptr(centroids, "centroids", 16));
+  BSA_TRY(check_ptr(counts, "counts", 4));
+  BSA_TRY(check_ptr(workspace, "workspace", 4));
+  const int64_t need = bsa_cluster_workspace_bytes(shape, p);
+  if (workspace_bytes < need)
+    return fail(BSA_ERR_CAPACITY, "workspace %lld bytes < required %lld",
+                (long long)workspace_bytes, (long long)need);
+  if (cells > INT32_MAX / 2) return fail(BSA_ERR_UNSUPPORTED, "too many cells");
+  bsa::ClusterArgs a{};
+  a.X = X;
+  a.sb = shape->stride_b;
+  a.sh = shape->stride_h;
+  a.sn = shape->stride_n;
+  a.H = shape->H;
+  a.N = shape->N;
+  a.D = shape->d;
+  a.T = p->T;
+  a.Hg = p->Hg;
+  a.W = p->W;
+  a.kt = p->kt;
+  a.kh = p->kh;
+  a.kw = p->kw;
+  a.Kt = (int)cdiv(p->T, p->kt);
+  a.Kh = (int)cdiv(p->Hg, p->kh);
+  a.Kw = (int)cdiv(p->W, p->kw);
+  a.Nc = (int)cells;
+  a.wt = std::min(p->wt, a.Kt);
+  a.wh = std::min(p->wh, a.Kh);
+  a.ww = std::min(p->ww, a.Kw);
+  a.assign = assign;
+  a.mu = centroids;
+  a.norm = (float*)workspace;
+  a.counts = counts;
+  return hip_status(bsa::launch_cluster(a, shape->B * shape->H, p->iters, (hipStream_t)stream),
+                    "cluster launch");
 }
 
 }  // extern "C"

@@ -133,6 +133,21 @@ struct RiskArgs {
   int N, chunks, BH;
 };
 
+// 3D local-window clustering.
+struct ClusterArgs {
+  const uint16_t* X;   // [B, H, N, D] with strides (Q or K)
+  int64_t sb, sh, sn;
+  int H, N, D;
+  int T, Hg, W;        // token lattice, T * Hg * W = N
+  int kt, kh, kw;      // cell size
+  int Kt, Kh, Kw, Nc;  // cells per axis, centroids
+  int wt, wh, ww;      // window in cells, clipped to the grid
+  int32_t* assign;     // [BH, N]
+  float* mu;           // [BH, Nc, D]
+  float* norm;         // [BH, Nc] squared norms of the centroids (workspace)
+  int32_t* counts;     // [BH, Nc]
+};
+
 // Pooled rectification of omitted blocks.
 constexpr int kMaxRowWords = 128;  // bitmap words of a row of up to 4096 blocks
 
@@ -176,6 +191,7 @@ hipError_t launch_micro_attn(const MicroAttnArgs& a, int B, int D,
                              bool out_bf16, hipStream_t s);
 hipError_t launch_merge(const MergeArgs& a, int B, bool bf16, hipStream_t s);
 hipError_t launch_risk(const RiskArgs& a, hipStream_t s);
+hipError_t launch_cluster(const ClusterArgs& a, int BH, int iters, hipStream_t s);
 hipError_t launch_rectify(const RectifyArgs& a, int BH, int D, bool out_bf16, hipStream_t s);
 
 }  // namespace bsa

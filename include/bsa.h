@@ -14,6 +14,8 @@
  *   bsa_dense_attn_fwd    the same attention engine over every key (baseline).
  *   bsa_pooled_rectify    add the pooled estimate of the omitted blocks to a
  *                         sparse result (exact LSE merge).
+ *   bsa_local_window_cluster  3D local-window clustering of Q or K (the
+ *                         front end of cluster-induced blocks).
  *   bsa_omission_risk     per-head share of the full softmax mass a sparse
  *                         support omits (offline head calibration).
  *
@@ -321,6 +323,50 @@ bsa_status bsa_pooled_rectify(const uint16_t* Q, const uint16_t* K,
                               void* O, int32_t o_dtype, float* LSE,
                               void* workspace, int64_t workspace_bytes,
                               void* stream);
+
+/* ------------------------------------------------------------------------
+ * bsa_local_window_cluster -- 3D local-window clustering of one token
+ * tensor per head (HyperVAttention section 4.1, Eq. 5; Appendix A.2,
+ * Algorithm 2), the front end of its cluster-induced blocks.  The N tokens
+ * form a T x Hg x W lattice, t-major (token n = (t * Hg + y) * W + x).  A
+ * fixed grid of (kt, kh, kw) cells -- ceil(T/kt) x ceil(Hg/kh) x ceil(W/kw)
+ * of them, numbered t-major -- carries one centroid per cell, initialised
+ * at the cell's centre token (coordinates u*k + floor(k/2), clamped to the
+ * lattice).  Each of `iters` iterations assigns every token to the nearest
+ * centroid (squared Euclidean distance) among the cells of a (wt, wh, ww)
+ * window around its own cell -- per axis the cells g - floor(w/2) .. +w-1,
+ * shifted to stay inside the grid, w clipped to the cell count -- and then
+ * moves every centroid to the mean of its tokens (one with none stays).
+ * Reading where the page is silent: ties go to the lower centroid index.
+ *
+ * X: bf16 [B, H, N, d] with the strides of `shape` (queries or keys).
+ * assign: int32 [B, H, N], the last iteration's centroid of every token.
+ * centroids: float32 [B, H, cells, d] after the last update.
+ * counts: int32 [B, H, cells], tokens per centroid in the last assignment.
+ * workspace: >= bsa_cluster_workspace_bytes bytes (the centroids' squared
+ *   norms).
+ * Precision: distances as ||mu||^2 - 2 x.mu in float32 (near-ties within
+ *   float32 rounding may resolve either way); centroid sums in float32 in
+ *   token order, so repeated calls give identical results.
+ * ---------------------------------------------------------------------- */
+typedef struct bsa_cluster_params {
+  int32_t T, Hg, W;     /* token lattice, T * Hg * W == N                  */
+  int32_t kt, kh, kw;   /* cell size (>= 1)                                 */
+  int32_t wt, wh, ww;   /* window in cells (>= 1; clipped to the grid)      */
+  int32_t iters;        /* >= 1                                             */
+} bsa_cluster_params;
+
+/* Number of cells (centroids) per head, or -1 on invalid arguments. */
+int64_t bsa_cluster_cells(const bsa_shape* shape, const bsa_cluster_params* params);
+
+int64_t bsa_cluster_workspace_bytes(const bsa_shape* shape,
+                                    const bsa_cluster_params* params);
+
+bsa_status bsa_local_window_cluster(const uint16_t* X, const bsa_shape* shape,
+                                    const bsa_cluster_params* params,
+                                    int32_t* assign, float* centroids,
+                                    int32_t* counts, void* workspace,
+                                    int64_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------
  * bsa_omission_risk -- per-head omission risk of a sparse support.  The

@@ -252,3 +252,25 @@ def test_pooled_rectify_validation_and_workspace():
     assert st == 1 and "o_dtype" in bsa.bsa_last_error()
     big = _shape(N=4097 * 64)
     assert bsa._lib.bsa_pooled_rectify_workspace_bytes(ctypes.byref(big)) == -1
+
+
+def test_cluster_validation():
+    s = _shape(B=1, H=2, N=3 * 8 * 10)
+    cp = bsa._ClusterParams(3, 8, 10, 1, 3, 4, 2, 2, 2, 1)
+    assert bsa._lib.bsa_cluster_cells(ctypes.byref(s), ctypes.byref(cp)) == 3 * 3 * 3
+    assert bsa._lib.bsa_cluster_workspace_bytes(ctypes.byref(s), ctypes.byref(cp)) == 256
+    bad = bsa._ClusterParams(3, 8, 11, 1, 3, 4, 2, 2, 2, 1)   # 264 != 240 tokens
+    assert bsa._lib.bsa_cluster_cells(ctypes.byref(s), ctypes.byref(bad)) == -1
+    assert "lattice" in bsa.bsa_last_error()
+    cp.iters = 0
+    assert bsa._lib.bsa_cluster_cells(ctypes.byref(s), ctypes.byref(cp)) == -1
+    cp.iters, cp.kw = 1, 0
+    assert bsa._lib.bsa_cluster_cells(ctypes.byref(s), ctypes.byref(cp)) == -1
+    cp.kw = 4
+    p = ctypes.c_void_p(4096)
+    st = bsa._lib.bsa_local_window_cluster(p, ctypes.byref(s), ctypes.byref(cp), p, p, p, p, 255,
+                                           None)
+    assert st == 3 and "workspace" in bsa.bsa_last_error()
+    st = bsa._lib.bsa_local_window_cluster(None, ctypes.byref(s), ctypes.byref(cp), p, p, p, p,
+                                           256, None)
+    assert st == 1 and "X is NULL" in bsa.bsa_last_error()

@@ -1,0 +1,123 @@
+"""GPU parity of the 3D local-window clustering (bsa_local_window_cluster)
+against the fp64 oracle (HyperVAttention Algorithm 2).
+
+Assignments are integer decisions taken on float32 distances; the oracle
+takes them in float64.  A token whose oracle margin (second-nearest minus
+nearest squared distance in its window) is below BAND may resolve either
+way: it is exempt, and so are the centroids and counts of the clusters it
+joins on either side.  The float32 distance error is about 1e-4 at these
+sizes (d <= 128, squared distances of a few hundred), so BAND = 1e-3 leaves a
+tenfold margin.  All other assignments and counts must be identical and
+centroids agree to CENT_TOL (float32 means of up to a few thousand bf16
+values).  Every case asserts that no exemption happened before the last
+iteration (an earlier one would change everything after it)."""
+
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import bsa_oracle as O
+from synth import VideoSpec, config_spec, gen_qkv
+
+pytestmark = pytest.mark.gpu
+
+if torch.cuda.is_available():
+    import block_sparse_attention_pool_amd as bsa
+else:  # collected on CPU, skipped by the marker
+    bsa = None
+
+DEV = "cuda:0"
+BAND = 1e-3
+CENT_TOL = 1e-4
+
+
+def say(*a):
+    print("[gpu-cluster]", *a, file=sys.stderr, flush=True)
+
+
+def initial_centroids(x, thw, cell, window):
+    T, H, W = thw
+    K, _ = O.cluster_grid(thw, cell, window)
+    return np.stack([x[(min(ut * cell[0] + cell[0] // 2, T - 1) * H
+                        + min(uh * cell[1] + cell[1] // 2, H - 1)) * W
+                       + min(uw * cell[2] + cell[2] // 2, W - 1)]
+                     for ut in range(K[0]) for uh in range(K[1]) for uw in range(K[2])])
+
+
+def compare_head(x, thw, cell, window, iters, a_gpu, mu_gpu, c_gpu, what):
+    # margins of every iteration's assignment, on the centroids it used
+    mu_prev = initial_centroids(x, thw, cell, window)
+    for it in range(1, iters + 1):
+        margins = O.assignment_margins(x, thw, cell, window, mu_prev)
+        if it < iters:
+            assert margins.min() >= BAND, f"{what}: near-tie at iteration {it}; pick other inputs"
+            _, mu_prev, _ = O.local_window_clustering(x, thw, cell, window, it)
+    a, mu, c = O.local_window_clustering(x, thw, cell, window, iters)
+    diff = np.nonzero(a != a_gpu)[0]
+    assert np.all(margins[diff] < BAND), f"{what}: {len(diff)} assignments differ outside the tie band"
+    touched = set(a[diff].tolist()) | set(a_gpu[diff].tolist())
+    keep = np.array([u not in touched for u in range(len(c))])
+    np.testing.assert_array_equal(c[keep], c_gpu[keep], err_msg=what)
+    np.testing.assert_allclose(mu_gpu[keep], mu[keep], atol=CENT_TOL, rtol=0, err_msg=what)
+    assert c_gpu.sum() == x.shape[0]
+    return len(diff)
+
+
+CASES = [
+    # (grid, H, d, key, cell, window, iters)
+    ((3, 7, 9), 1, 128, 151, (1, 3, 3), (2, 2, 2), 3),
+    ((4, 16, 16), 2, 64, 152, (2, 4, 4), (2, 3, 3), 3),
+    ((5, 15, 21), 1, 128, 153, (2, 5, 5), (3, 3, 3), 2),   # ragged cells on two axes
+    ((6, 10, 13), 1, 64, 154, (3, 4, 4), (2, 2, 3), 4),
+    ((2, 9, 50), 1, 128, 155, (1, 3, 7), (2, 3, 5), 2),    # window clipped on t
+]
+
+
+@pytest.mark.parametrize("grid,H,d,key,cell,window,iters", CASES)
+def test_cluster_small(grid, H, d, key, cell, window, iters):
+    spec = VideoSpec(1, H, d, grid, key)
+    say("cluster", grid, cell, window, iters)
+    Q, K, _ = gen_qkv(spec)
+    for name, X in (("Q", Q), ("K", K)):
+        a, mu, c = bsa.bsa_local_window_cluster(X.to(DEV), grid, cell, window, iters)
+        torch.cuda.synchronize()
+        for h in range(H):
+            n = compare_head(X[0, h].double().numpy(), grid, cell, window, iters,
+                             a[0, h].cpu().numpy(), mu[0, h].double().cpu().numpy(),
+                             c[0, h].cpu().numpy(), f"{name} h{h}")
+            say(f"   {name} h{h}: {n} tie-exempt tokens")
+
+
+def test_cluster_strided_and_deterministic():
+    spec = VideoSpec(2, 2, 128, (3, 8, 10), 156)
+    Q, _, _ = gen_qkv(spec)
+    Qs = Q.transpose(1, 2).contiguous().to(DEV).transpose(1, 2)  # [B, N, H, d] storage
+    cell, window = (1, 2, 3), (2, 3, 3)
+    r1 = bsa.bsa_local_window_cluster(Qs, (3, 8, 10), cell, window, 3)
+    r2 = bsa.bsa_local_window_cluster(Q.to(DEV), (3, 8, 10), cell, window, 3)
+    torch.cuda.synchronize()
+    for x, y in zip(r1, r2):
+        assert torch.equal(x, y)
+    for b in range(2):
+        for h in range(2):
+            compare_head(Q[b, h].double().numpy(), (3, 8, 10), cell, window, 3,
+                         r1[0][b, h].cpu().numpy(), r1[1][b, h].double().cpu().numpy(),
+                         r1[2][b, h].cpu().numpy(), f"b{b} h{h}")
+
+
+@pytest.mark.parametrize("which,cell", [("Q", (11, 5, 5)), ("K", (11, 3, 3))])
+def test_cluster_hunyuanvideo_layer(which, cell):
+    """The 118,800-token HunyuanVideo layer with the page's grids (432 query,
+    1215 key cells) and (3, 8, 8) windows; one head, one iteration."""
+    spec = config_spec(3)
+    Q, K, _ = gen_qkv(spec, heads=[0])
+    X = Q if which == "Q" else K
+    thw = spec.grid
+    a, mu, c = bsa.bsa_local_window_cluster(X.to(DEV), thw, cell, (3, 8, 8), 1)
+    torch.cuda.synchronize()
+    say(f"HunyuanVideo {which}: {mu.shape[2]} cells; oracle running")
+    n = compare_head(X[0, 0].double().numpy(), thw, cell, (3, 8, 8), 1, a[0, 0].cpu().numpy(),
+                     mu[0, 0].double().cpu().numpy(), c[0, 0].cpu().numpy(), which)
+    say(f"   {n} tie-exempt tokens of {spec.N}")
