@@ -38,6 +38,12 @@ METRIC = "block-sparse attn executed TFLOP/s, % bf16 MFMA peak, speedup vs dense
 PEAK_TFLOPS = 2500.0   # MI355X dense bf16/fp16 matrix peak
 HBM_GBS = 8000.0       # MI355X HBM3E
 N_ROTATIONS = 3        # static workload: anchor offsets cycled over the steps
+FP32_TFLOPS = 78.6     # MI355X fp32 vector FMA rate without packed math
+# Local-window clustering cells (Q, K) per workload: the page's settings for
+# the 720p Wan and HunyuanVideo layers; the Wan setting for the others.
+CLUSTER_CELLS = {2: ((7, 6, 6), (6, 4, 4)), 3: ((11, 5, 5), (11, 3, 3))}
+CLUSTER_WINDOW = (3, 8, 8)
+CLUSTER_ITERS = 3
 FLUSH_BYTES = 512 << 20  # larger than L2 (8 x 4 MB) plus the 256 MB Infinity Cache
 
 
@@ -65,6 +71,9 @@ def parse():
     ap.add_argument("--rectify", action="store_true",
                     help="add the pooled rectification of omitted blocks to the step and "
                          "report its cost and its effect on the error against dense attention")
+    ap.add_argument("--cluster", action="store_true",
+                    help="also time the 3D local-window clustering of Q and K (all heads) with "
+                         "the page's grids and (3, 8, 8) windows, 3 iterations")
     ap.add_argument("--calibration-copy", action="store_true",
                     help="first run a plain 256 MiB device copy (reads 256 MiB, writes "
                          "256 MiB) three times, to scale hardware byte counters")
@@ -374,6 +383,29 @@ def main():
                     "mean_abs_lse_err_vs_dense_rectified": float((Lr - Ld).abs().mean())}
         del Os, Or, Od
 
+    cluster_out = None
+    if args.cluster:
+        cq, ck = CLUSTER_CELLS.get(cfg, CLUSTER_CELLS[2])
+        thw = spec.grid
+        res = {}
+        flops = 0
+        for name, X, cell in (("Q", Q, cq), ("K", K, ck)):
+            a_, mu_, c_ = bsa.bsa_local_window_cluster(X, thw, cell, CLUSTER_WINDOW, CLUSTER_ITERS)
+            ms, _ = events_ms(lambda: bsa.bsa_local_window_cluster(X, thw, cell, CLUSTER_WINDOW,
+                                                                     CLUSTER_ITERS), reps, stream)
+            Kc = [-(-thw[i] // cell[i]) for i in range(3)]
+            wv = 1
+            for i in range(3):
+                wv *= min(CLUSTER_WINDOW[i], Kc[i])
+            # assignment work: one d-long dot product per (token, window centroid)
+            flops += 2 * d * N * wv * B * H * CLUSTER_ITERS
+            res[name] = {"cells": int(mu_.shape[2]), "cell": list(cell), "ms": round(ms, 4)}
+        tot = res["Q"]["ms"] + res["K"]["ms"]
+        cluster_out = {"iters": CLUSTER_ITERS, "window": list(CLUSTER_WINDOW), **res,
+                       "ms_total": round(tot, 4),
+                       "assign_tflops": round(flops / (tot * 1e-3) / 1e12, 2),
+                       "frac_fp32_peak": round(flops / (tot * 1e-3) / 1e12 / FP32_TFLOPS, 4)}
+
     attn_tflops = macro_flops / (attn_ms * 1e-3) / 1e12
     kernel_src = os.path.join(ROOT, "block_sparse_attention_pool_amd", "csrc", "attn.hip")
     # the committed counters were taken on the default workload and selection
@@ -410,6 +442,7 @@ def main():
         "stage_gbs": gbs,
         "omission_risk": risk_out,
         **({"pooled_rectify": rect_out} if rect_out is not None else {}),
+        **({"local_window_cluster": cluster_out} if cluster_out is not None else {}),
         "roofline": {"bound": "mfma", "achieved": round(attn_tflops, 2), "peak": PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(attn_tflops / PEAK_TFLOPS, 4),
                      "traffic": traffic},
