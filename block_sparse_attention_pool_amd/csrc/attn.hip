@@ -235,9 +235,11 @@ __device__ __forceinline__ void exec_barrier() { asm volatile("s_barrier" ::: "m
 
 typedef __attribute__((address_space(4))) const int32_t const_i32;
 
-// Average key-tile bytes per row above which the sparse kernel interleaves
-// its rows across the XCDs: twice the 4 MB L2 of one XCD.
+// The sparse kernel interleaves its rows across the XCDs when they average
+// more key-tile bytes than twice the 4 MB L2 of one XCD and their runs of
+// consecutive blocks average fewer than kShortRun blocks.
 constexpr int64_t kWideRowBytes = int64_t(8) << 20;
+constexpr int kShortRun = 8;
 
 // One workgroup per (b, h, 64-row query block), two waves of 32 rows each.
 // Per selected key block the 64 x D K tile (16-byte chunks XOR-swizzled by
@@ -259,18 +261,33 @@ void attn_fwd_kernel(AttnArgs a) {
   // XCD-aware row order: dispatch w runs on XCD w % 8.  By default each XCD
   // takes a contiguous range of (head, query block) rows, so its L2 sees one
   // head's neighbouring query blocks, whose key selections overlap.  When
-  // the rows' key supports average more than twice an XCD's 4 MB L2 (many
-  // far-reaching blocks per row), that reuse is lost anyway; the rows are
-  // then dealt to the XCDs in interleaved chunks of 8, so that all XCDs work
-  // on neighbouring rows of one head at a time and share its tiles through
-  // the Infinity Cache instead of streaming eight heads' keys from HBM.  The
-  // choice reads the total entry count, so it needs no host round trip.
+  // the rows' key supports average more than twice an XCD's 4 MB L2 and are
+  // scattered (made of short runs of consecutive blocks), neighbouring rows
+  // share little and that reuse is lost; the rows are then dealt to the XCDs
+  // in interleaved chunks of 8, so that all XCDs work on neighbouring rows of
+  // one head at a time and share its tiles through the Infinity Cache instead
+  // of streaming eight heads' keys from HBM.  The choice reads the total
+  // entry count and one sample row (the middle query block of the first
+  // head, the same for every workgroup), so it needs no host round trip.
   const int w = blockIdx.x;
   const int xcd = w & 7, slot = w >> 3;
   bool interleave = false;
   if constexpr (!DENSE) {
-    const int64_t total = ((const_i32*)a.row_ptr)[a.rows];
-    interleave = total * (kBlock * D * 2 * 2) > (int64_t)a.rows * kWideRowBytes;
+    const_i32* rp = (const_i32*)a.row_ptr;
+    const int64_t total = rp[a.rows];
+    if (total * (kBlock * D * 2 * 2) > (int64_t)a.rows * kWideRowBytes) {
+      __shared__ int run_starts[2];
+      const int rs = a.nB / 2;
+      const int sb = rp[rs], se = rp[rs + 1];
+      int starts = 0;
+      for (int e = sb + (int)threadIdx.x; e < se; e += 128)
+        starts += (e == sb || a.col_idx[e] != a.col_idx[e - 1] + 1) ? 1 : 0;
+      starts = wave_sum(starts);
+      if ((threadIdx.x & 63) == 0) run_starts[threadIdx.x >> 6] = starts;
+      __syncthreads();
+      starts = run_starts[0] + run_starts[1];
+      interleave = starts * kShortRun > se - sb;  // mean run shorter than kShortRun blocks
+    }
   }
   int L;
   if (interleave) {
