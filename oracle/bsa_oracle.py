@@ -605,6 +605,17 @@ def local_window_clustering(X, thw, cell, window, iters: int):
     return a, mu, counts
 
 
+def cluster_permutation(assign, n_clusters: int):
+    """[HVA] Eq. 1: the permutation that places the tokens of each cluster
+    contiguously -- tokens ordered by (cluster, original index), a stable
+    sort -- and the start offset of every cluster (n_clusters + 1 entries)."""
+    a = np.asarray(assign, dtype=np.int64)
+    perm = np.argsort(a, kind="stable")
+    offsets = np.zeros(n_clusters + 1, dtype=np.int64)
+    offsets[1:] = np.cumsum(np.bincount(a, minlength=n_clusters))
+    return perm, offsets
+
+
 def assignment_margins(X, thw, cell, window, mu):
     """Per token, the gap between its second-nearest and nearest squared
     distance over its window's centroids (a tie has gap 0)."""

@@ -534,6 +534,20 @@ def test_clustering_cell_constant_tokens_stay_put():
     np.testing.assert_array_equal(c, np.full(8, 18))
 
 
+def test_cluster_permutation_properties():
+    rng = np.random.default_rng(73)
+    a = rng.integers(0, 9, size=200)
+    a[a == 4] = 5                       # an empty cluster
+    perm, off = O.cluster_permutation(a, 9)
+    assert sorted(perm.tolist()) == list(range(200))           # a permutation
+    assert off[0] == 0 and off[-1] == 200 and off[4] == off[5]
+    for u in range(9):
+        seg = perm[off[u]:off[u + 1]]
+        assert np.all(a[seg] == u)                             # contiguous clusters
+        assert np.all(np.diff(seg) > 0)                        # original order kept
+        assert len(seg) == np.sum(a == u)
+
+
 def test_clustering_pin_catches_an_unclipped_window(monkeypatch):
     monkeypatch.setattr(O, "window_start", lambda g, w, K: max(g - w // 2, 0))
     thw, cell, window = (4, 6, 5), (2, 2, 2), (3, 2, 3)
