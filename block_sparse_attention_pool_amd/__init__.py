@@ -87,6 +87,8 @@ def _load(path: str = _LIB_PATH):
         "bsa_cluster_cells": ([SP, CP], I64),
         "bsa_cluster_workspace_bytes": ([SP, CP], I64),
         "bsa_local_window_cluster": ([P, SP, CP, P, P, P, P, I64, P], I32),
+        "bsa_cluster_permute_workspace_bytes": ([SP, CP], I64),
+        "bsa_cluster_permute": ([P, P, SP, CP, P, P, P, I64, P], I32),
         "bsa_pooled_rectify": ([P, P, P, SP, I32, F32, P, P, P, I32, P, P, I64, P], I32),
         "bsa_omission_risk": ([P, P, P, SP, P, P, I64, P], I32),
     }
@@ -103,7 +105,8 @@ EXPORTED = ("bsa_version", "bsa_last_error", "bsa_score_blocks", "bsa_select_wor
             "bsa_sparse_attn_fwd", "bsa_dense_attn_fwd", "bsa_micro_residual_fwd",
             "bsa_lse_merge", "bsa_omission_risk_workspace_bytes", "bsa_omission_risk",
             "bsa_pooled_rectify_workspace_bytes", "bsa_pooled_rectify", "bsa_cluster_cells",
-            "bsa_cluster_workspace_bytes", "bsa_local_window_cluster")
+            "bsa_cluster_workspace_bytes", "bsa_local_window_cluster",
+            "bsa_cluster_permute_workspace_bytes", "bsa_cluster_permute")
 
 
 def library_path() -> str:
@@ -418,6 +421,28 @@ def bsa_local_window_cluster(X, thw, cell, window, iters: int = 1, *, stream=Non
                                        _stream(stream, dev))
     _check(st, "bsa_local_window_cluster")
     return assign, mu, counts
+
+
+def bsa_cluster_permute(assign, counts, X_like, thw, cell, window, *, stream=None):
+    """Tokens in cluster order (HVA Eq. 1) from bsa_local_window_cluster's
+    assign [B, H, N] and counts [B, H, cells].  Returns (perm int32
+    [B, H, N], offsets int32 [B, H, cells + 1])."""
+    shp = shape_of(X_like)
+    cp = _ClusterParams(*thw, *cell, *window, 1)
+    B, H, N, _ = X_like.shape
+    cells = counts.shape[2]
+    nws = _lib.bsa_cluster_permute_workspace_bytes(ctypes.byref(shp), ctypes.byref(cp))
+    if nws < 0:
+        raise BsaError(f"bsa_cluster_permute_workspace_bytes: {bsa_last_error()}")
+    dev = assign.device
+    perm = torch.empty((B, H, N), dtype=torch.int32, device=dev)
+    offsets = torch.empty((B, H, cells + 1), dtype=torch.int32, device=dev)
+    ws = torch.empty(max(nws, 256), dtype=torch.uint8, device=dev)
+    st = _lib.bsa_cluster_permute(_ptr(assign), _ptr(counts), ctypes.byref(shp), ctypes.byref(cp),
+                                  _ptr(perm), _ptr(offsets), _ptr(ws), ws.numel(),
+                                  _stream(stream, dev))
+    _check(st, "bsa_cluster_permute")
+    return perm, offsets
 
 
 def bsa_omission_risk(lse_sparse, lse_full, lse_repaired=None, *, out=None, stream=None):

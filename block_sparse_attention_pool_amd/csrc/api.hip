@@ -784,4 +784,55 @@ bsa_status bsa_local_window_cluster(const uint16_t* X, const bsa_shape* shape,
                     "cluster launch");
 }
 
+int64_t bsa_cluster_permute_workspace_bytes(const bsa_shape* shape,
+                                            const bsa_cluster_params* params) {
+  int64_t cells = 0;
+  if (plan_cluster(shape, params, &cells) != BSA_OK) return -1;
+  return align256(((int64_t)shape->B * shape->H * cells + 1) * 4) + 256;
+}
+
+bsa_status bsa_cluster_permute(const int32_t* assign, const int32_t* counts,
+                               const bsa_shape* shape, const bsa_cluster_params* p,
+                               int32_t* perm, int32_t* offsets, void* workspace,
+                               int64_t workspace_bytes, void* stream) {
+  int64_t cells = 0;
+  BSA_TRY(plan_cluster(shape, p, &cells));
+  BSA_TRY(check_ptr(assign, "assign", 4));
+  BSA_TRY(check_ptr(counts, "counts", 4));
+  BSA_TRY(check_ptr(perm, "perm", 4));
+  BSA_TRY(check_ptr(offsets, "offsets", 4));
+  BSA_TRY(check_ptr(workspace, "workspace", 256));
+  const int64_t need = bsa_cluster_permute_workspace_bytes(shape, p);
+  if (workspace_bytes < need)
+    return fail(BSA_ERR_CAPACITY, "workspace %lld bytes < required %lld",
+                (long long)workspace_bytes, (long long)need);
+  const int64_t rows = (int64_t)shape->B * shape->H * cells;
+  if (rows >= INT32_MAX / 2 || (int64_t)shape->B * shape->H * shape->N >= INT32_MAX)
+    return fail(BSA_ERR_UNSUPPORTED, "too many tokens for int32 offsets");
+  bsa::ClusterArgs a{};
+  a.H = shape->H;
+  a.N = shape->N;
+  a.D = shape->d;
+  a.T = p->T;
+  a.Hg = p->Hg;
+  a.W = p->W;
+  a.kt = p->kt;
+  a.kh = p->kh;
+  a.kw = p->kw;
+  a.Kt = (int)cdiv(p->T, p->kt);
+  a.Kh = (int)cdiv(p->Hg, p->kh);
+  a.Kw = (int)cdiv(p->W, p->kw);
+  a.Nc = (int)cells;
+  a.wt = std::min(p->wt, a.Kt);
+  a.wh = std::min(p->wh, a.Kh);
+  a.ww = std::min(p->ww, a.Kw);
+  a.assign = const_cast<int32_t*>(assign);
+  hipStream_t st = (hipStream_t)stream;
+  int32_t* gofs = (int32_t*)workspace;
+  int64_t* total = (int64_t*)((char*)workspace + align256((rows + 1) * 4));
+  BSA_TRY(hip_status(bsa::launch_scan(counts, (int)rows, gofs, total, st), "scan launch"));
+  return hip_status(bsa::launch_cluster_permute(a, shape->B * shape->H, gofs, perm, offsets, st),
+                    "permute launch");
+}
+
 }  // extern "C"

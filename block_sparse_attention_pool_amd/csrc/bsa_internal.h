@@ -192,6 +192,8 @@ hipError_t launch_micro_attn(const MicroAttnArgs& a, int B, int D,
 hipError_t launch_merge(const MergeArgs& a, int B, bool bf16, hipStream_t s);
 hipError_t launch_risk(const RiskArgs& a, hipStream_t s);
 hipError_t launch_cluster(const ClusterArgs& a, int BH, int iters, hipStream_t s);
+hipError_t launch_cluster_permute(const ClusterArgs& a, int BH, const int32_t* gofs,
+                                  int32_t* perm, int32_t* offsets, hipStream_t s);
 hipError_t launch_rectify(const RectifyArgs& a, int BH, int D, bool out_bf16, hipStream_t s);
 
 }  // namespace bsa

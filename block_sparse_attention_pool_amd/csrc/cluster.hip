@@ -222,7 +222,70 @@ __global__ __launch_bounds__(256) void cluster_update_kernel(ClusterArgs a) {
   }
 }
 
+// Eq. 1: the tokens of centroid u, in token order, at its place in the
+// head's permutation.  The same box of cells as the update is scanned; the
+// cluster's start comes from the scan of all heads' counts (minus the head's
+// first entry); writes stop at the segment's end, whatever the counts say.
+__global__ __launch_bounds__(256) void cluster_permute_kernel(ClusterArgs a,
+                                                              const int32_t* gofs,
+                                                              int32_t* perm,
+                                                              int32_t* offsets) {
+  __shared__ int wcnt[4];
+  const int u = blockIdx.x;
+  const int64_t bh = blockIdx.y;
+  const int uw = u % a.Kw, uh = (u / a.Kw) % a.Kh, ut = u / (a.Kw * a.Kh);
+  const int64_t base = gofs[bh * a.Nc];
+  const int start = (int)(gofs[bh * a.Nc + u] - base);
+  const int end = u + 1 < a.Nc ? (int)(gofs[bh * a.Nc + u + 1] - base) : a.N;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  if (tid == 0) {
+    offsets[bh * (a.Nc + 1) + u] = start;
+    if (u + 1 == a.Nc) offsets[bh * (a.Nc + 1) + a.Nc] = a.N;
+  }
+  int glt, ght, glh, ghh, glw, ghw;
+  covering_cells(ut, a.wt, a.Kt, glt, ght);
+  covering_cells(uh, a.wh, a.Kh, glh, ghh);
+  covering_cells(uw, a.ww, a.Kw, glw, ghw);
+  const int t0 = glt * a.kt, t1 = min((ght + 1) * a.kt, a.T);
+  const int h0 = glh * a.kh, h1 = min((ghh + 1) * a.kh, a.Hg);
+  const int w0 = glw * a.kw, w1 = min((ghw + 1) * a.kw, a.W);
+  const int Lt = max(t1 - t0, 0), Lh = max(h1 - h0, 0), Lw = max(w1 - w0, 0);
+  const int64_t P = (int64_t)Lt * Lh * Lw;
+  const int32_t* asg = a.assign + bh * a.N;
+  int32_t* pr = perm + bh * a.N;
+  int done = 0;
+  for (int64_t b0 = 0; b0 < P; b0 += 256) {
+    const int64_t p = b0 + tid;
+    int tok = 0;
+    bool m = false;
+    if (p < P) {
+      const int pt = (int)(p / ((int64_t)Lh * Lw)), ph = (int)((p / Lw) % Lh), pw = (int)(p % Lw);
+      tok = ((t0 + pt) * a.Hg + (h0 + ph)) * a.W + (w0 + pw);
+      m = asg[tok] == u;
+    }
+    const uint64_t bal = __ballot(m);
+    if (lane == 0) wcnt[wave] = __popcll(bal);
+    __syncthreads();
+    int off = done, tot = 0;
+    for (int q = 0; q < 4; ++q) {
+      if (q < wave) off += wcnt[q];
+      tot += wcnt[q];
+    }
+    const int pos = start + off + __popcll(bal & ((1ull << lane) - 1ull));
+    if (m && pos < end) pr[pos] = tok;
+    done += tot;
+    __syncthreads();  // wcnt is rewritten by the next chunk
+  }
+}
+
 }  // namespace
+
+hipError_t launch_cluster_permute(const ClusterArgs& a, int BH, const int32_t* gofs,
+                                  int32_t* perm, int32_t* offsets, hipStream_t s) {
+  hipLaunchKernelGGL(cluster_permute_kernel, dim3(a.Nc, BH), dim3(256), 0, s, a, gofs, perm,
+                     offsets);
+  return hipGetLastError();
+}
 
 hipError_t launch_cluster(const ClusterArgs& a, int BH, int iters, hipStream_t s) {
   const dim3 grid(a.Nc, BH);

@@ -16,6 +16,7 @@
  *                         sparse result (exact LSE merge).
  *   bsa_local_window_cluster  3D local-window clustering of Q or K (the
  *                         front end of cluster-induced blocks).
+ *   bsa_cluster_permute   tokens in cluster order (HVA Eq. 1).
  *   bsa_omission_risk     per-head share of the full softmax mass a sparse
  *                         support omits (offline head calibration).
  *
@@ -367,6 +368,29 @@ bsa_status bsa_local_window_cluster(const uint16_t* X, const bsa_shape* shape,
                                     int32_t* assign, float* centroids,
                                     int32_t* counts, void* workspace,
                                     int64_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * bsa_cluster_permute -- HyperVAttention Eq. 1: the permutation that places
+ * each cluster's tokens contiguously, tokens ordered by (cluster, original
+ * index), and every cluster's start.
+ *
+ * assign, counts: the outputs of bsa_local_window_cluster with the same
+ *   shape and params (counts must be the number of tokens of each cluster;
+ *   positions beyond a cluster's segment are not written otherwise).
+ * perm: int32 [B, H, N], perm[b,h,k] = original index of the token at
+ *   position k of the head's cluster order.
+ * offsets: int32 [B, H, cells + 1], cluster u occupies positions
+ *   offsets[u] .. offsets[u+1]-1 (offsets[cells] = N).
+ * workspace: >= bsa_cluster_permute_workspace_bytes bytes, 256-byte aligned.
+ * ---------------------------------------------------------------------- */
+int64_t bsa_cluster_permute_workspace_bytes(const bsa_shape* shape,
+                                            const bsa_cluster_params* params);
+
+bsa_status bsa_cluster_permute(const int32_t* assign, const int32_t* counts,
+                               const bsa_shape* shape,
+                               const bsa_cluster_params* params, int32_t* perm,
+                               int32_t* offsets, void* workspace,
+                               int64_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------
  * bsa_omission_risk -- per-head omission risk of a sparse support.  The

@@ -121,3 +121,23 @@ def test_cluster_hunyuanvideo_layer(which, cell):
     n = compare_head(X[0, 0].double().numpy(), thw, cell, (3, 8, 8), 1, a[0, 0].cpu().numpy(),
                      mu[0, 0].double().cpu().numpy(), c[0, 0].cpu().numpy(), which)
     say(f"   {n} tie-exempt tokens of {spec.N}")
+
+
+@pytest.mark.parametrize("grid,H,d,key,cell,window,iters", CASES[:3] + [
+    ((33, 45, 80), 1, 128, 3, (11, 5, 5), (3, 8, 8), 1)])
+def test_cluster_permutation(grid, H, d, key, cell, window, iters):
+    """HVA Eq. 1 on the GPU's clustering: tokens in (cluster, index) order and
+    the cluster offsets, identical to the oracle's stable sort of its own
+    assignment (the assignments agree exactly on these inputs)."""
+    spec = VideoSpec(1, H, d, grid, key)
+    Q, _, _ = gen_qkv(spec, heads=[0])
+    Qd = Q.to(DEV)
+    a, mu, c = bsa.bsa_local_window_cluster(Qd, grid, cell, window, iters)
+    perm, off = bsa.bsa_cluster_permute(a, c, Qd, grid, cell, window)
+    torch.cuda.synchronize()
+    x = Q[0, 0].double().numpy()
+    ao, _, co = O.local_window_clustering(x, grid, cell, window, iters)
+    assert np.array_equal(ao, a[0, 0].cpu().numpy()), "assignments differ: the case is not exact"
+    po, offo = O.cluster_permutation(ao, len(co))
+    np.testing.assert_array_equal(perm[0, 0].cpu().numpy(), po)
+    np.testing.assert_array_equal(off[0, 0].cpu().numpy(), offo)
