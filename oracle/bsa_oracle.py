@@ -616,6 +616,17 @@ def cluster_permutation(assign, n_clusters: int):
     return perm, offsets
 
 
+def cluster_topp_rows(mu_q, mu_k, sizes_k, scale: float, p: float, k_min: int = 1,
+                      k_cap: int | None = None) -> list[list[int]]:
+    """[HVA] Eq. 2-3 on clusters: for every query cluster i, the key clusters
+    of TopP(P'_i; p), P'_ij = s_j exp(S_ij) / sum_o s_o exp(S_io) with
+    S_ij = scale <mu_i^q, mu_j^k> and s_j the key cluster sizes, clamped to
+    [k_min, k_cap] (Min-kc of Appendix A.1 as the floor), ascending."""
+    S = pooled_scores(mu_q, mu_k, scale)
+    sizes = np.asarray(sizes_k, np.float64)
+    return [sorted(topp_set(S[i], sizes, p, k_min, k_cap)) for i in range(S.shape[0])]
+
+
 def assignment_margins(X, thw, cell, window, mu):
     """Per token, the gap between its second-nearest and nearest squared
     distance over its window's centroids (a tie has gap 0)."""

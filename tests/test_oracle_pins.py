@@ -548,6 +548,28 @@ def test_cluster_permutation_properties():
         assert len(seg) == np.sum(a == u)
 
 
+def test_cluster_topp_on_block_means_is_block_topp():
+    # 64-token blocks are clusters whose centroids are the block means and
+    # whose sizes are the valid counts: the cluster rule is the block rule
+    N, d, s = 64 * 9 + 30, 8, 0.35
+    Q, K = _rand(74, N, d), _rand(75, N, d)
+    Qb, Kb = O.pool_means(Q, 64), O.pool_means(K, 64)
+    S = O.pooled_scores(Qb, Kb, s)
+    for p, kmin, kcap in ((0.9, 1, None), (0.5, 3, 6), (0.99, 1, 4)):
+        rows = O.cluster_topp_rows(Qb, Kb, O.block_sizes(N, 64), s, p, kmin, kcap)
+        assert rows == O.select_rows(S, N, 64, "topp", p=p, k_min=kmin, k_cap=kcap)
+
+
+def test_cluster_topp_ignores_empty_clusters_unless_forced():
+    mu_q = np.array([[1.0, 0.0]])
+    mu_k = np.array([[1.0, 0.0], [5.0, 0.0], [0.0, 1.0]])
+    sizes = np.array([10, 0, 10])          # key cluster 1 is empty
+    rows = O.cluster_topp_rows(mu_q, mu_k, sizes, 1.0, 0.6)
+    assert rows == [[0]]                   # e^1 * 10 of (e^1 + 1) * 10: 0.73 >= 0.6
+    rows = O.cluster_topp_rows(mu_q, mu_k, sizes, 1.0, 0.6, k_min=3)
+    assert rows == [[0, 1, 2]]
+
+
 def test_clustering_pin_catches_an_unclipped_window(monkeypatch):
     monkeypatch.setattr(O, "window_start", lambda g, w, K: max(g - w // 2, 0))
     thw, cell, window = (4, 6, 5), (2, 2, 2), (3, 2, 3)
