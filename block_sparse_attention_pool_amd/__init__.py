@@ -89,6 +89,9 @@ def _load(path: str = _LIB_PATH):
         "bsa_local_window_cluster": ([P, SP, CP, P, P, P, P, I64, P], I32),
         "bsa_cluster_permute_workspace_bytes": ([SP, CP], I64),
         "bsa_cluster_permute": ([P, P, SP, CP, P, P, P, I64, P], I32),
+        "bsa_cluster_select_workspace_bytes": ([I32, I32, I32, I32], I64),
+        "bsa_cluster_select": ([P, P, P, I32, I32, I32, I32, I32, F32, F32, I32, I32, P, P, I64,
+                                P, P, I64, P], I32),
         "bsa_pooled_rectify": ([P, P, P, SP, I32, F32, P, P, P, I32, P, P, I64, P], I32),
         "bsa_omission_risk": ([P, P, P, SP, P, P, I64, P], I32),
     }
@@ -106,7 +109,8 @@ EXPORTED = ("bsa_version", "bsa_last_error", "bsa_score_blocks", "bsa_select_wor
             "bsa_lse_merge", "bsa_omission_risk_workspace_bytes", "bsa_omission_risk",
             "bsa_pooled_rectify_workspace_bytes", "bsa_pooled_rectify", "bsa_cluster_cells",
             "bsa_cluster_workspace_bytes", "bsa_local_window_cluster",
-            "bsa_cluster_permute_workspace_bytes", "bsa_cluster_permute")
+            "bsa_cluster_permute_workspace_bytes", "bsa_cluster_permute",
+            "bsa_cluster_select_workspace_bytes", "bsa_cluster_select")
 
 
 def library_path() -> str:
@@ -443,6 +447,32 @@ def bsa_cluster_permute(assign, counts, X_like, thw, cell, window, *, stream=Non
                                   _stream(stream, dev))
     _check(st, "bsa_cluster_permute")
     return perm, offsets
+
+
+def bsa_cluster_select(mu_q, mu_k, size_k, *, p: float = 0.9, k_min: int = 1,
+                       k_cap: int | None = None, scale: float | None = None, stream=None):
+    """Key clusters of every query cluster (HVA Eq. 2-3).  mu_q [B, H, Nq, d],
+    mu_k [B, H, Nk, d] float32, size_k [B, H, Nk] int32.  Returns (row_ptr
+    int32 [B*H*Nq+1], col_idx int32, nnz int64 device scalar)."""
+    B, H, Nq, d = mu_q.shape
+    Nk = mu_k.shape[2]
+    scale = 1.0 / math.sqrt(d) if scale is None else scale
+    k_cap = Nk if k_cap is None else k_cap
+    nws = _lib.bsa_cluster_select_workspace_bytes(B, H, Nq, Nk)
+    if nws < 0:
+        raise BsaError("bsa_cluster_select_workspace_bytes: invalid sizes")
+    dev = mu_q.device
+    rows = B * H * Nq
+    cap = rows * min(Nk, max(k_cap, 1))
+    row_ptr = torch.empty(rows + 1, dtype=torch.int32, device=dev)
+    col_idx = torch.empty(max(cap, 1), dtype=torch.int32, device=dev)
+    nnz = torch.empty(1, dtype=torch.int64, device=dev)
+    ws = torch.empty(max(nws, 256), dtype=torch.uint8, device=dev)
+    st = _lib.bsa_cluster_select(_ptr(mu_q), _ptr(mu_k), _ptr(size_k), B, H, Nq, Nk, d, scale, p,
+                                 k_min, k_cap, _ptr(row_ptr), _ptr(col_idx), cap, _ptr(nnz),
+                                 _ptr(ws), ws.numel(), _stream(stream, dev))
+    _check(st, "bsa_cluster_select")
+    return row_ptr, col_idx, nnz
 
 
 def bsa_omission_risk(lse_sparse, lse_full, lse_repaired=None, *, out=None, stream=None):

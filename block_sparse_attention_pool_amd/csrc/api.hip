@@ -467,6 +467,7 @@ bsa_status bsa_select_blocks(const float* scores, const bsa_shape* shape, int32_
   a.nB = (int)pl.nB_sel;
   a.W = (int)pl.W_sel;
   a.block = (int)pl.block;
+  a.rows_per_head = (int)pl.nB_sel;
   a.mode = p->mode;
   a.k = p->k;
   a.k_min = p->k_min;
@@ -833,6 +834,76 @@ bsa_status bsa_cluster_permute(const int32_t* assign, const int32_t* counts,
   BSA_TRY(hip_status(bsa::launch_scan(counts, (int)rows, gofs, total, st), "scan launch"));
   return hip_status(bsa::launch_cluster_permute(a, shape->B * shape->H, gofs, perm, offsets, st),
                     "permute launch");
+}
+
+int64_t bsa_cluster_select_workspace_bytes(int32_t B, int32_t H, int32_t Nq, int32_t Nk) {
+  if (B < 1 || H < 1 || Nq < 1 || Nk < 1 || Nk > 4096) return -1;
+  const int64_t rows = (int64_t)B * H * Nq;
+  return align256(rows * Nk * 4) + align256(rows * cdiv(Nk, 32) * 4) + align256(rows * 4);
+}
+
+bsa_status bsa_cluster_select(const float* mu_q, const float* mu_k, const int32_t* size_k,
+                              int32_t B, int32_t H, int32_t Nq, int32_t Nk, int32_t d,
+                              float scale, float p, int32_t k_min, int32_t k_cap,
+                              int32_t* row_ptr, int32_t* col_idx, int64_t col_cap,
+                              int64_t* out_nnz, void* workspace, int64_t workspace_bytes,
+                              void* stream) {
+  if (B < 1 || H < 1 || Nq < 1 || Nk < 1)
+    return fail(BSA_ERR_INVALID_ARG, "B=%d H=%d Nq=%d Nk=%d must all be >= 1", B, H, Nq, Nk);
+  if (Nk > 4096) return fail(BSA_ERR_UNSUPPORTED, "Nk=%d exceeds 4096 key clusters", Nk);
+  if (d != 64 && d != 128) return fail(BSA_ERR_UNSUPPORTED, "d=%d unsupported (64 or 128)", d);
+  if ((int64_t)B * H > 65535) return fail(BSA_ERR_UNSUPPORTED, "B*H exceeds 65535");
+  if (!(p > 0.f && p <= 1.f)) return fail(BSA_ERR_INVALID_ARG, "p=%g not in (0,1]", p);
+  if (k_min < 0 || k_cap < k_min)
+    return fail(BSA_ERR_INVALID_ARG, "need 0 <= k_min <= k_cap (k_min=%d k_cap=%d)", k_min,
+                k_cap);
+  BSA_TRY(check_ptr(mu_q, "mu_q", 16));
+  BSA_TRY(check_ptr(mu_k, "mu_k", 16));
+  BSA_TRY(check_ptr(size_k, "size_k", 4));
+  BSA_TRY(check_ptr(row_ptr, "row_ptr", 4));
+  BSA_TRY(check_ptr(out_nnz, "out_nnz", 8));
+  if (col_cap < 0) return fail(BSA_ERR_INVALID_ARG, "col_cap < 0");
+  if (col_cap > 0) BSA_TRY(check_ptr(col_idx, "col_idx", 4));
+  BSA_TRY(check_ptr(workspace, "workspace", 256));
+  const int64_t need = bsa_cluster_select_workspace_bytes(B, H, Nq, Nk);
+  if (workspace_bytes < need)
+    return fail(BSA_ERR_CAPACITY, "workspace %lld bytes < required %lld",
+                (long long)workspace_bytes, (long long)need);
+  const int64_t rows = (int64_t)B * H * Nq;
+  if (rows * std::min<int64_t>(Nk, k_cap) > INT32_MAX)
+    return fail(BSA_ERR_UNSUPPORTED, "entries exceed int32 row pointers");
+  hipStream_t st = (hipStream_t)stream;
+  char* ws = (char*)workspace;
+  float* scores = (float*)ws;
+  bsa::GemmArgs g{};
+  g.A = mu_q;
+  g.Bm = mu_k;
+  g.C = scores;
+  g.H = H;
+  g.M = Nq;
+  g.Nc = Nk;
+  g.D = d;
+  g.scale = scale;
+  g.heads = all_heads(H);
+  BSA_TRY(hip_status(bsa::launch_score_gemm(g, B * H, st), "score launch"));
+  bsa::SelectArgs a{};
+  a.scores = scores;
+  a.bits = (uint32_t*)(ws + align256(rows * Nk * 4));
+  a.counts = (int32_t*)(ws + align256(rows * Nk * 4) + align256(rows * cdiv(Nk, 32) * 4));
+  a.N = Nk * 64;  // no ragged block: every weight comes from size_k
+  a.nB = Nk;
+  a.W = (int)cdiv(Nk, 32);
+  a.block = 64;
+  a.mode = BSA_SELECT_TOPP;
+  a.p = p;
+  a.k_min = k_min;
+  a.k_cap = k_cap;
+  a.col_sizes = size_k;
+  a.rows_per_head = Nq;
+  BSA_TRY(hip_status(bsa::launch_select(a, (int)rows, st), "select launch"));
+  BSA_TRY(hip_status(bsa::launch_scan(a.counts, (int)rows, row_ptr, out_nnz, st), "scan launch"));
+  return hip_status(
+      bsa::launch_emit_bits(a.bits, a.W, (int)rows, row_ptr, col_idx, col_cap, st), "emit launch");
 }
 
 }  // extern "C"

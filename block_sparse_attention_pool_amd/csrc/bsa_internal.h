@@ -48,6 +48,8 @@ struct SelectArgs {
   float p;
   int force_diag, use_static;
   int frame_tokens, window_frames, n_anchors, anchor_offset;
+  const int32_t* col_sizes;          // top-p weights per key column [heads, nB], or null
+  int rows_per_head;                 // rows of one (b, h): nB for blocks, Nq for clusters
   int n_diag, n_col;                 // MOD-DiT parallel-diagonal / vertical patterns
   int32_t diag[kMaxPatterns];        // offsets: key block i + diag[t]
   int32_t col[kMaxPatterns];         // key blocks

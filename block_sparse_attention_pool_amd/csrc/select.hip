@@ -114,7 +114,13 @@ __global__ __launch_bounds__(256) void select_wave_kernel(SelectArgs a, int rows
     for (int e = 0; e < E; ++e) {
       const int j = 64 * e + lane;
       float v = x[e];
-      if (a.mode == kTopP) v = (j == a.nB - 1 ? tail_size : (float)a.block) * expf(v - mx);
+      if (a.mode == kTopP) {
+        // weight: the key block's valid tokens, or the given cluster size
+        const float n = a.col_sizes != nullptr
+                            ? (float)a.col_sizes[(int64_t)(r / a.rows_per_head) * a.nB + min(j, a.nB - 1)]
+                            : (j == a.nB - 1 ? tail_size : (float)a.block);
+        v = n * expf(v - mx);
+      }
       val[e] = j < a.nB ? v : 0.f;
       key[e] = j < a.nB ? float_order_key(v) : 0u;
     }

@@ -17,6 +17,7 @@
  *   bsa_local_window_cluster  3D local-window clustering of Q or K (the
  *                         front end of cluster-induced blocks).
  *   bsa_cluster_permute   tokens in cluster order (HVA Eq. 1).
+ *   bsa_cluster_select    key clusters per query cluster (HVA Eq. 2-3).
  *   bsa_omission_risk     per-head share of the full softmax mass a sparse
  *                         support omits (offline head calibration).
  *
@@ -391,6 +392,34 @@ bsa_status bsa_cluster_permute(const int32_t* assign, const int32_t* counts,
                                const bsa_cluster_params* params, int32_t* perm,
                                int32_t* offsets, void* workspace,
                                int64_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * bsa_cluster_select -- HyperVAttention section 2, Eq. 2-3 on clusters: for
+ * every query cluster i of every (b, h), the key clusters of
+ * TopP(P'_i; p) with P'_ij = s_j exp(S_ij) / sum_o s_o exp(S_io),
+ * S_ij = scale <mu_i^q, mu_j^k>, s_j the key cluster sizes; the prefix
+ * length clamped to [k_min, k_cap] (Min-kc of Appendix A.1 as the floor);
+ * ties to the lower index.  A CSR with one row per (b, h, i), row index
+ * (b * H + h) * Nq + i, ascending key cluster indices.
+ *
+ * mu_q: float32 [B, H, Nq, d]; mu_k: float32 [B, H, Nk, d] (the centroids of
+ *   bsa_local_window_cluster); size_k: int32 [B, H, Nk] (its counts).
+ * row_ptr: int32 [B*H*Nq + 1]; col_idx: int32 [col_cap]; out_nnz: device
+ *   int64 total (entries beyond col_cap are not written).
+ * workspace: >= bsa_cluster_select_workspace_bytes(B, H, Nq, Nk) bytes,
+ *   256-byte aligned.  Limits: Nk <= 4096, d in {64, 128}.
+ * ---------------------------------------------------------------------- */
+int64_t bsa_cluster_select_workspace_bytes(int32_t B, int32_t H, int32_t Nq,
+                                           int32_t Nk);
+
+bsa_status bsa_cluster_select(const float* mu_q, const float* mu_k,
+                              const int32_t* size_k, int32_t B, int32_t H,
+                              int32_t Nq, int32_t Nk, int32_t d, float scale,
+                              float p, int32_t k_min, int32_t k_cap,
+                              int32_t* row_ptr, int32_t* col_idx,
+                              int64_t col_cap, int64_t* out_nnz,
+                              void* workspace, int64_t workspace_bytes,
+                              void* stream);
 
 /* ------------------------------------------------------------------------
  * bsa_omission_risk -- per-head omission risk of a sparse support.  The

@@ -141,3 +141,49 @@ def test_cluster_permutation(grid, H, d, key, cell, window, iters):
     po, offo = O.cluster_permutation(ao, len(co))
     np.testing.assert_array_equal(perm[0, 0].cpu().numpy(), po)
     np.testing.assert_array_equal(off[0, 0].cpu().numpy(), offo)
+
+
+def _select_case(mu_q, mu_k, sizes, p, k_min, k_cap, what):
+    """GPU cluster top-p on float32 centroids against the oracle on the same
+    float32 values; lists compared with the top-p tie rules."""
+    import parity as PT
+    d = mu_q.shape[1]
+    t = lambda x, dt: torch.from_numpy(np.ascontiguousarray(x)).to(dt).to(DEV)[None, None]
+    rp, ci, nnz = bsa.bsa_cluster_select(t(mu_q, torch.float32), t(mu_k, torch.float32),
+                                         t(sizes, torch.int32), p=p, k_min=k_min, k_cap=k_cap)
+    torch.cuda.synchronize()
+    got = bsa.csr_rows(rp, ci, nnz)
+    q32 = mu_q.astype(np.float32).astype(np.float64)
+    k32 = mu_k.astype(np.float32).astype(np.float64)
+    rows = O.cluster_topp_rows(q32, k32, sizes, 1 / np.sqrt(d), p, k_min, k_cap)
+    S = O.pooled_scores(q32, k32, 1 / np.sqrt(d))
+    exempt = PT.compare_topp_rows(got, rows, S, np.asarray(sizes, np.float64), p, k_min, k_cap)
+    say(f"   {what}: {sum(len(r) for r in rows)} entries, {exempt} tie-exempt rows")
+    return exempt
+
+
+@pytest.mark.parametrize("grid,H,d,key,cell,window,iters", CASES[:4])
+@pytest.mark.parametrize("p,kmin_frac,cap_frac", [(0.9, 0.15, 1.0), (0.5, 0.0, 0.2)])
+def test_cluster_select(grid, H, d, key, cell, window, iters, p, kmin_frac, cap_frac):
+    spec = VideoSpec(1, H, d, grid, key)
+    Q, K, _ = gen_qkv(spec, heads=[0])
+    _, mu_q, _ = O.local_window_clustering(Q[0, 0].double().numpy(), grid, cell, window, iters)
+    _, mu_k, c_k = O.local_window_clustering(K[0, 0].double().numpy(), grid,
+                                             (cell[0], max(1, cell[1] - 1), cell[2]), window, iters)
+    Nk = len(c_k)
+    k_min = int(np.ceil(kmin_frac * Nk))
+    k_cap = max(k_min, int(np.floor(cap_frac * Nk)))
+    _select_case(mu_q, mu_k, c_k, p, k_min, k_cap, f"{grid} p={p}")
+
+
+def test_cluster_select_hunyuanvideo_sizes():
+    """The page's HunyuanVideo setting: 432 query and 1215 key clusters,
+    top-p 0.9, Min-kc 0.15 (183 key clusters at least); seeded centroids and
+    sizes summing to 118,800 tokens (some key clusters empty)."""
+    rng = np.random.default_rng(310)
+    mu_q = rng.standard_normal((432, 128)) * 0.7
+    mu_k = rng.standard_normal((1215, 128)) * 0.7
+    sizes = rng.multinomial(118800 - 1215 * 40, np.ones(1215) / 1215) + 40
+    sizes[::97] = 0
+    exempt = _select_case(mu_q, mu_k, sizes, 0.9, 183, 1215, "HunyuanVideo clusters")
+    assert exempt <= 2
