@@ -627,6 +627,36 @@ def cluster_topp_rows(mu_q, mu_k, sizes_k, scale: float, p: float, k_min: int = 
     return [sorted(topp_set(S[i], sizes, p, k_min, k_cap)) for i in range(S.shape[0])]
 
 
+def cluster_block_attention(Q, K, V, perm_q, off_q, perm_k, off_k, rows, scale: float):
+    """[HVA] Eq. 4: every query of query cluster i attends over the tokens of
+    the key clusters in row i (clusters as produced by cluster_permutation;
+    the result is written back in the original token order, O = Pi_q^-1 O').
+    Queries of a cluster with an empty row get O = 0, LSE = -inf."""
+    Q = np.asarray(Q, np.float64)
+    N = Q.shape[0]
+    O = np.zeros((N, np.asarray(V).shape[1]))
+    L = np.full(N, NEG_INF)
+    for i, sel in enumerate(rows):
+        qi = np.asarray(perm_q[off_q[i]:off_q[i + 1]], dtype=np.int64)
+        if qi.size == 0:
+            continue
+        keys = (np.concatenate([perm_k[off_k[j]:off_k[j + 1]] for j in sel]).astype(np.int64)
+                if len(sel) else np.zeros(0, dtype=np.int64))
+        O[qi], L[qi] = attend(Q[qi], K[keys], V[keys], scale)
+    return O, L
+
+
+def cluster_tile_pairs(off_q, off_k, rows, tile: int = 64) -> int:
+    """Work of executing Eq. 4 on tiles with every cluster padded to whole
+    tiles: sum over query clusters of ceil(s_i / tile) times the tiles of its
+    selected key clusters, sum of ceil(s_j / tile)."""
+    sq = np.diff(np.asarray(off_q))
+    sk = np.diff(np.asarray(off_k))
+    tq = -(-sq // tile)
+    tk = -(-sk // tile)
+    return int(sum(int(tq[i]) * int(sum(int(tk[j]) for j in sel)) for i, sel in enumerate(rows)))
+
+
 def assignment_margins(X, thw, cell, window, mu):
     """Per token, the gap between its second-nearest and nearest squared
     distance over its window's centroids (a tie has gap 0)."""

@@ -570,6 +570,40 @@ def test_cluster_topp_ignores_empty_clusters_unless_forced():
     assert rows == [[0, 1, 2]]
 
 
+def test_cluster_attention_all_clusters_is_full_attention():
+    N, d = 150, 8
+    s = 1 / math.sqrt(d)
+    Q, K, V = _rand(76, N, d), _rand(77, N, d), _rand(78, N, d)
+    rng = np.random.default_rng(79)
+    aq, ak = rng.integers(0, 7, N), rng.integers(0, 11, N)
+    pq, oq = O.cluster_permutation(aq, 7)
+    pk, ok = O.cluster_permutation(ak, 11)
+    Oc, Lc = O.cluster_block_attention(Q, K, V, pq, oq, pk, ok, [list(range(11))] * 7, s)
+    tq, tk, tv = (torch.from_numpy(x)[None, None] for x in (Q, K, V))
+    ref = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, scale=s)[0, 0].numpy()
+    np.testing.assert_allclose(Oc, ref, atol=1e-12)
+    np.testing.assert_allclose(Lc, scipy.special.logsumexp(s * Q @ K.T, axis=1), atol=1e-12)
+
+
+def test_cluster_attention_on_block_clusters_is_block_sparse_attention():
+    # clusters = 64-token blocks in order: Eq. 4 is block-sparse attention
+    N, d, b = 64 * 4 + 17, 6, 64
+    s = 0.4
+    Q, K, V = _rand(80, N, d), _rand(81, N, d), _rand(82, N, d)
+    a = np.arange(N) // b
+    perm, off = O.cluster_permutation(a, 5)
+    assert np.array_equal(perm, np.arange(N))
+    rows = [[0, 2], [1], [], [0, 3, 4], [4]]
+    Oc, Lc = O.cluster_block_attention(Q, K, V, perm, off, perm, off, rows, s)
+    Ob, Lb = O.block_sparse_attention(Q, K, V, rows, b, s)
+    np.testing.assert_allclose(Oc, Ob, atol=1e-13)
+    np.testing.assert_array_equal(np.isneginf(Lc), np.isneginf(Lb))
+    fin = ~np.isneginf(Lb)
+    np.testing.assert_allclose(Lc[fin], Lb[fin], atol=1e-13)
+    # tile work: query tiles x key tiles of the selected clusters
+    assert O.cluster_tile_pairs(off, off, rows) == 1 * 2 + 1 * 1 + 0 + 1 * 3 + 1 * 1
+
+
 def test_clustering_pin_catches_an_unclipped_window(monkeypatch):
     monkeypatch.setattr(O, "window_start", lambda g, w, K: max(g - w // 2, 0))
     thw, cell, window = (4, 6, 5), (2, 2, 2), (3, 2, 3)
