@@ -90,6 +90,9 @@ def _load(path: str = _LIB_PATH):
         "bsa_cluster_permute_workspace_bytes": ([SP, CP], I64),
         "bsa_cluster_permute": ([P, P, SP, CP, P, P, P, I64, P], I32),
         "bsa_cluster_select_workspace_bytes": ([I32, I32, I32, I32], I64),
+        "bsa_cluster_attn_workspace_bytes": ([SP, I32, I32, I32], I64),
+        "bsa_cluster_attn_fwd": ([P, P, P, SP, F32, I32, I32, P, P, P, P, P, P, P, I32, P, P, P, I64,
+                                  P], I32),
         "bsa_cluster_select": ([P, P, P, I32, I32, I32, I32, I32, F32, F32, I32, I32, P, P, I64,
                                 P, P, I64, P], I32),
         "bsa_pooled_rectify": ([P, P, P, SP, I32, F32, P, P, P, I32, P, P, I64, P], I32),
@@ -110,7 +113,8 @@ EXPORTED = ("bsa_version", "bsa_last_error", "bsa_score_blocks", "bsa_select_wor
             "bsa_pooled_rectify_workspace_bytes", "bsa_pooled_rectify", "bsa_cluster_cells",
             "bsa_cluster_workspace_bytes", "bsa_local_window_cluster",
             "bsa_cluster_permute_workspace_bytes", "bsa_cluster_permute",
-            "bsa_cluster_select_workspace_bytes", "bsa_cluster_select")
+            "bsa_cluster_select_workspace_bytes", "bsa_cluster_select",
+            "bsa_cluster_attn_workspace_bytes", "bsa_cluster_attn_fwd")
 
 
 def library_path() -> str:
@@ -473,6 +477,32 @@ def bsa_cluster_select(mu_q, mu_k, size_k, *, p: float = 0.9, k_min: int = 1,
                                  _ptr(ws), ws.numel(), _stream(stream, dev))
     _check(st, "bsa_cluster_select")
     return row_ptr, col_idx, nnz
+
+
+def bsa_cluster_attn_fwd(Q, K, V, perm_q, off_q, perm_k, off_k, crow_ptr, ccol, *,
+                         scale: float | None = None, out_dtype=torch.float32, stream=None):
+    """Attention over cluster-induced blocks (HVA Eq. 4).  Returns (O
+    [B,H,N,d] out_dtype, LSE float32 [B,H,N], executed tile pairs int64
+    device scalar)."""
+    _same_layout(Q, K, V)
+    shp = shape_of(Q)
+    Nq, Nk = off_q.shape[2] - 1, off_k.shape[2] - 1
+    scale = 1.0 / math.sqrt(shp.d) if scale is None else scale
+    odt = _odt(out_dtype)
+    nws = _lib.bsa_cluster_attn_workspace_bytes(ctypes.byref(shp), Nq, Nk, odt)
+    if nws < 0:
+        raise BsaError(f"bsa_cluster_attn_workspace_bytes: {bsa_last_error()}")
+    dev = Q.device
+    O = _out_like(Q, out_dtype)
+    L = torch.empty(Q.shape[:3], dtype=torch.float32, device=dev)
+    pairs = torch.empty(1, dtype=torch.int64, device=dev)
+    ws = torch.empty(max(nws, 256), dtype=torch.uint8, device=dev)
+    st = _lib.bsa_cluster_attn_fwd(_ptr(Q), _ptr(K), _ptr(V), ctypes.byref(shp), scale, Nq, Nk,
+                                   _ptr(perm_q), _ptr(off_q), _ptr(perm_k), _ptr(off_k),
+                                   _ptr(crow_ptr), _ptr(ccol), _ptr(O), odt, _ptr(L), _ptr(pairs),
+                                   _ptr(ws), ws.numel(), _stream(stream, dev))
+    _check(st, "bsa_cluster_attn_fwd")
+    return O, L, pairs
 
 
 def bsa_omission_risk(lse_sparse, lse_full, lse_repaired=None, *, out=None, stream=None):

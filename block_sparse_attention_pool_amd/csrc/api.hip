@@ -136,6 +136,53 @@ bsa_status plan_cluster(const bsa_shape* s, const bsa_cluster_params* p, int64_t
   return BSA_OK;
 }
 
+// Workspace of bsa_cluster_attn_fwd, carved in this order.
+struct ClusterAttnPlan {
+  int64_t NP, nTP, BH;
+  int64_t tq, tk, qp, kp, vp, vt, op, lp, kv, qc, cnt, rp, nnz, col, total, cap;
+};
+
+bsa_status plan_cluster_attn(const bsa_shape* s, int32_t Nq, int32_t Nk, int32_t o_dtype,
+                             ClusterAttnPlan* pl) {
+  BSA_TRY(check_shape(s));
+  if (Nq < 1 || Nk < 1) return fail(BSA_ERR_INVALID_ARG, "Nq=%d, Nk=%d must be >= 1", Nq, Nk);
+  if (o_dtype != BSA_F32 && o_dtype != BSA_BF16)
+    return fail(BSA_ERR_INVALID_ARG, "o_dtype=%d (BSA_F32 or BSA_BF16)", o_dtype);
+  ClusterAttnPlan p{};
+  p.BH = (int64_t)s->B * s->H;
+  if (p.BH > 65535) return fail(BSA_ERR_UNSUPPORTED, "B*H exceeds 65535");
+  p.nTP = cdiv(s->N, 64) + std::max(Nq, Nk);
+  p.NP = 64 * p.nTP;
+  p.cap = p.BH * p.nTP * p.nTP;  // every tile of every key cluster in every row
+  if (p.cap >= INT32_MAX || p.BH * p.NP * s->d >= ((int64_t)1 << 40))
+    return fail(BSA_ERR_UNSUPPORTED, "cluster layout too large (%lld tiles per head)",
+                (long long)p.nTP);
+  const int64_t d = s->d, osz = o_dtype == BSA_BF16 ? 2 : 4;
+  int64_t at = 0;
+  auto take = [&](int64_t bytes) {
+    const int64_t here = at;
+    at += align256(bytes);
+    return here;
+  };
+  p.tq = take(p.BH * (Nq + 1) * 4);
+  p.tk = take(p.BH * (Nk + 1) * 4);
+  p.qp = take(p.BH * p.NP * d * 2);
+  p.kp = take(p.BH * p.NP * d * 2);
+  p.vp = take(p.BH * p.NP * d * 2);
+  p.vt = take(p.BH * p.NP * d * 2);
+  p.op = take(p.BH * p.NP * d * osz);
+  p.lp = take(p.BH * p.NP * 4);
+  p.kv = take(p.BH * p.nTP * 4);
+  p.qc = take(p.BH * p.nTP * 4);
+  p.cnt = take(p.BH * p.nTP * 4);
+  p.rp = take((p.BH * p.nTP + 1) * 4);
+  p.nnz = take(8);
+  p.col = take(p.cap * 4);
+  p.total = at;
+  *pl = p;
+  return BSA_OK;
+}
+
 bsa::HeadList all_heads(int H) {
   bsa::HeadList l;
   l.n = H;
@@ -904,6 +951,119 @@ bsa_status bsa_cluster_select(const float* mu_q, const float* mu_k, const int32_
   BSA_TRY(hip_status(bsa::launch_scan(a.counts, (int)rows, row_ptr, out_nnz, st), "scan launch"));
   return hip_status(
       bsa::launch_emit_bits(a.bits, a.W, (int)rows, row_ptr, col_idx, col_cap, st), "emit launch");
+}
+
+int64_t bsa_cluster_attn_workspace_bytes(const bsa_shape* shape, int32_t Nq, int32_t Nk,
+                                         int32_t o_dtype) {
+  ClusterAttnPlan pl;
+  if (plan_cluster_attn(shape, Nq, Nk, o_dtype, &pl) != BSA_OK) return -1;
+  return pl.total;
+}
+
+bsa_status bsa_cluster_attn_fwd(const uint16_t* Q, const uint16_t* K, const uint16_t* V,
+                                const bsa_shape* shape, float scale, int32_t Nq, int32_t Nk,
+                                const int32_t* perm_q, const int32_t* off_q,
+                                const int32_t* perm_k, const int32_t* off_k,
+                                const int32_t* crow_ptr, const int32_t* ccol, void* O,
+                                int32_t o_dtype, float* LSE, int64_t* out_tile_pairs,
+                                void* workspace, int64_t workspace_bytes, void* stream) {
+  ClusterAttnPlan pl;
+  BSA_TRY(plan_cluster_attn(shape, Nq, Nk, o_dtype, &pl));
+  BSA_TRY(check_ptr(Q, "Q"));
+  BSA_TRY(check_ptr(K, "K"));
+  BSA_TRY(check_ptr(V, "V"));
+  BSA_TRY(check_ptr(O, "O"));
+  BSA_TRY(check_ptr(LSE, "LSE", 4));
+  BSA_TRY(check_ptr(perm_q, "perm_q", 4));
+  BSA_TRY(check_ptr(off_q, "off_q", 4));
+  BSA_TRY(check_ptr(perm_k, "perm_k", 4));
+  BSA_TRY(check_ptr(off_k, "off_k", 4));
+  BSA_TRY(check_ptr(crow_ptr, "crow_ptr", 4));
+  if (ccol == nullptr) return fail(BSA_ERR_INVALID_ARG, "ccol is NULL");
+  BSA_TRY(check_ptr(workspace, "workspace", 256));
+  if (workspace_bytes < pl.total)
+    return fail(BSA_ERR_CAPACITY, "workspace %lld bytes < required %lld",
+                (long long)workspace_bytes, (long long)pl.total);
+  hipStream_t st = (hipStream_t)stream;
+  char* ws = (char*)workspace;
+  const int D = shape->d;
+  const int BH = (int)pl.BH;
+  bsa::ClusterAttnArgs c{};
+  c.Q = Q;
+  c.K = K;
+  c.V = V;
+  c.sb = shape->stride_b;
+  c.sh = shape->stride_h;
+  c.sn = shape->stride_n;
+  c.H = shape->H;
+  c.N = shape->N;
+  c.Nq = Nq;
+  c.Nk = Nk;
+  c.NP = (int)pl.NP;
+  c.nTP = (int)pl.nTP;
+  c.perm_q = perm_q;
+  c.off_q = off_q;
+  c.perm_k = perm_k;
+  c.off_k = off_k;
+  c.crow_ptr = crow_ptr;
+  c.ccol = ccol;
+  c.tq = (int32_t*)(ws + pl.tq);
+  c.tk = (int32_t*)(ws + pl.tk);
+  c.Qp = (uint16_t*)(ws + pl.qp);
+  c.Kp = (uint16_t*)(ws + pl.kp);
+  c.Vp = (uint16_t*)(ws + pl.vp);
+  c.key_valid = (int32_t*)(ws + pl.kv);
+  c.qtile_cluster = (int32_t*)(ws + pl.qc);
+  c.counts = (int32_t*)(ws + pl.cnt);
+  c.row_ptr = (int32_t*)(ws + pl.rp);
+  c.col_idx = (int32_t*)(ws + pl.col);
+  c.cap = pl.cap;
+  c.Op = ws + pl.op;
+  c.Lp = (const float*)(ws + pl.lp);
+  c.O = O;
+  c.LSE = LSE;
+  int64_t* nnz = out_tile_pairs != nullptr ? out_tile_pairs : (int64_t*)(ws + pl.nnz);
+  BSA_TRY(hip_status(bsa::launch_cluster_attn_plan(c, BH, D, st), "cluster plan launch"));
+  BSA_TRY(hip_status(bsa::launch_scan(c.counts, (int)(pl.BH * pl.nTP), c.row_ptr, nnz, st),
+                     "scan launch"));
+  BSA_TRY(hip_status(bsa::launch_cluster_attn_emit(c, BH, st), "cluster emit launch"));
+  // padded tensors: [BH, NP, D], contiguous
+  const int64_t sn = D, sh = pl.NP * D, sb = shape->H * sh;
+  bsa::TransposeArgs t{};
+  t.V = c.Vp;
+  t.Vt = (uint16_t*)(ws + pl.vt);
+  t.sb = sb;
+  t.sh = sh;
+  t.sn = sn;
+  t.H = shape->H;
+  t.N = c.NP;
+  t.nB = c.nTP;
+  t.Npad = c.NP;
+  t.heads = all_heads(shape->H);
+  BSA_TRY(hip_status(bsa::launch_transpose_v(t, shape->B, D, st), "transpose_v launch"));
+  bsa::AttnArgs a{};
+  a.Q = c.Qp;
+  a.K = c.Kp;
+  a.Vt = t.Vt;
+  a.O = ws + pl.op;
+  a.LSE = (float*)(ws + pl.lp);
+  a.row_ptr = c.row_ptr;
+  a.col_idx = c.col_idx;
+  a.sb = sb;
+  a.sh = sh;
+  a.sn = sn;
+  a.B = shape->B;
+  a.H = shape->H;
+  a.N = c.NP;
+  a.nB = c.nTP;
+  a.Npad = c.NP;
+  a.scale_log2 = scale * 1.4426950408889634f;
+  a.rows = (int)(pl.BH * pl.nTP);
+  a.per_xcd = (int)cdiv(a.rows, 8);
+  a.key_valid = c.key_valid;
+  BSA_TRY(hip_status(bsa::launch_attn_keymask(a, D, o_dtype == BSA_BF16, st), "attn launch"));
+  return hip_status(bsa::launch_cluster_attn_scatter(c, BH, D, o_dtype == BSA_BF16, st),
+                    "cluster scatter launch");
 }
 
 }  // extern "C"

@@ -249,7 +249,11 @@ constexpr int kShortRun = 8;
 // the iteration without a second buffer.  32 KB of LDS and at most 256
 // registers per lane leave room for four workgroups (two waves per SIMD)
 // per compute unit.
-template <int D, bool DENSE, bool OUT_BF16>
+// KEYMASK: every key tile j has its own count of valid keys (a.key_valid,
+// [B*H, nB]); keys at or beyond it are masked.  Used for tensors laid out
+// with padded segments (cluster-induced blocks); the tensors hold whole
+// tiles, so no load is clamped.
+template <int D, bool DENSE, bool OUT_BF16, bool KEYMASK = false>
 __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2)))
 void attn_fwd_kernel(AttnArgs a) {
   constexpr int DC = D / 8;      // 16-byte chunks per K row
@@ -447,8 +451,9 @@ void attn_fwd_kernel(AttnArgs a) {
     f16x8 va0[4];  // V^T fragments of block e-1's first d tile, read early
     v_frags(0, va0);
     // Lane holds keys 8*(r/4) + 4*g + r%4 (+32 for s1) of query q.
-    if (j == a.nB - 1) {
-      const int nvalid = a.N - j * kBlock;
+    if (KEYMASK || j == a.nB - 1) {
+      const int nvalid = KEYMASK ? ((const_i32*)a.key_valid)[(int64_t)bh * a.nB + j]
+                                 : a.N - j * kBlock;
       if (nvalid < kBlock) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
@@ -774,6 +779,18 @@ static void launch_attn_t(const AttnArgs& a, bool out_bf16, hipStream_t s) {
     hipLaunchKernelGGL((attn_fwd_kernel<D, DENSE, true>), grid, dim3(128), 0, s, a);
   else
     hipLaunchKernelGGL((attn_fwd_kernel<D, DENSE, false>), grid, dim3(128), 0, s, a);
+}
+
+hipError_t launch_attn_keymask(const AttnArgs& a, int D, bool out_bf16, hipStream_t s) {
+  const dim3 grid(64 * ((a.rows + 63) / 64));
+  if (D == 128) {
+    if (out_bf16) hipLaunchKernelGGL((attn_fwd_kernel<128, false, true, true>), grid, dim3(128), 0, s, a);
+    else hipLaunchKernelGGL((attn_fwd_kernel<128, false, false, true>), grid, dim3(128), 0, s, a);
+  } else {
+    if (out_bf16) hipLaunchKernelGGL((attn_fwd_kernel<64, false, true, true>), grid, dim3(128), 0, s, a);
+    else hipLaunchKernelGGL((attn_fwd_kernel<64, false, false, true>), grid, dim3(128), 0, s, a);
+  }
+  return hipGetLastError();
 }
 
 hipError_t launch_attn(const AttnArgs& a, int D, bool dense, bool out_bf16, hipStream_t s) {

@@ -78,6 +78,7 @@ struct AttnArgs {
   float scale_log2;  // softmax scale * log2(e)
   int rows;          // B*H*nB
   int per_xcd;       // ceil(rows / 8)
+  const int32_t* key_valid;  // [B*H, nB] valid keys per tile (masked kernel only)
 };
 
 struct MicroAttnArgs {
@@ -150,6 +151,37 @@ struct ClusterArgs {
   int32_t* counts;     // [BH, Nc]
 };
 
+// Attention over cluster-induced blocks (padded cluster order).
+struct ClusterAttnArgs {
+  const uint16_t* Q;
+  const uint16_t* K;
+  const uint16_t* V;
+  int64_t sb, sh, sn;      // strides of Q, K, V, O
+  int H, N, Nq, Nk;
+  int NP, nTP;             // padded length per head and its tiles (NP / 64)
+  const int32_t* perm_q;   // [BH, N]
+  const int32_t* off_q;    // [BH, Nq + 1]
+  const int32_t* perm_k;
+  const int32_t* off_k;    // [BH, Nk + 1]
+  const int32_t* crow_ptr; // cluster lists [BH * Nq + 1]
+  const int32_t* ccol;
+  int32_t* tq;             // [BH, Nq + 1] tile offsets of the query clusters
+  int32_t* tk;             // [BH, Nk + 1]
+  uint16_t* Qp;            // [BH, NP, D] padded cluster order
+  uint16_t* Kp;
+  uint16_t* Vp;
+  int32_t* key_valid;      // [BH, nTP]
+  int32_t* qtile_cluster;  // [BH, nTP]
+  int32_t* counts;         // [BH, nTP]
+  int32_t* row_ptr;        // [BH * nTP + 1] tile lists
+  int32_t* col_idx;
+  int64_t cap;
+  const void* Op;          // [BH, NP, D] attention output in padded order
+  const float* Lp;         // [BH, NP]
+  void* O;
+  float* LSE;
+};
+
 // Pooled rectification of omitted blocks.
 constexpr int kMaxRowWords = 128;  // bitmap words of a row of up to 4096 blocks
 
@@ -189,6 +221,7 @@ hipError_t launch_transpose_v(const TransposeArgs& a, int B, int D,
                               hipStream_t s);
 hipError_t launch_attn(const AttnArgs& a, int D, bool dense, bool out_bf16,
                        hipStream_t s);
+hipError_t launch_attn_keymask(const AttnArgs& a, int D, bool out_bf16, hipStream_t s);
 hipError_t launch_micro_attn(const MicroAttnArgs& a, int B, int D,
                              bool out_bf16, hipStream_t s);
 hipError_t launch_merge(const MergeArgs& a, int B, bool bf16, hipStream_t s);
@@ -196,6 +229,10 @@ hipError_t launch_risk(const RiskArgs& a, hipStream_t s);
 hipError_t launch_cluster(const ClusterArgs& a, int BH, int iters, hipStream_t s);
 hipError_t launch_cluster_permute(const ClusterArgs& a, int BH, const int32_t* gofs,
                                   int32_t* perm, int32_t* offsets, hipStream_t s);
+hipError_t launch_cluster_attn_plan(const ClusterAttnArgs& a, int BH, int D, hipStream_t s);
+hipError_t launch_cluster_attn_emit(const ClusterAttnArgs& a, int BH, hipStream_t s);
+hipError_t launch_cluster_attn_scatter(const ClusterAttnArgs& a, int BH, int D, bool out_bf16,
+                                       hipStream_t s);
 hipError_t launch_rectify(const RectifyArgs& a, int BH, int D, bool out_bf16, hipStream_t s);
 
 }  // namespace bsa

@@ -18,6 +18,7 @@
  *                         front end of cluster-induced blocks).
  *   bsa_cluster_permute   tokens in cluster order (HVA Eq. 1).
  *   bsa_cluster_select    key clusters per query cluster (HVA Eq. 2-3).
+ *   bsa_cluster_attn_fwd  attention over cluster-induced blocks (HVA Eq. 4).
  *   bsa_omission_risk     per-head share of the full softmax mass a sparse
  *                         support omits (offline head calibration).
  *
@@ -420,6 +421,43 @@ bsa_status bsa_cluster_select(const float* mu_q, const float* mu_k,
                               int64_t col_cap, int64_t* out_nnz,
                               void* workspace, int64_t workspace_bytes,
                               void* stream);
+
+/* ------------------------------------------------------------------------
+ * bsa_cluster_attn_fwd -- attention over cluster-induced blocks
+ * (HyperVAttention section 2, Eq. 4): every query of query cluster i
+ * attends over the tokens of the key clusters in row i of the cluster CSR;
+ * O and LSE are written in the original token order (O = Pi_q^-1 O').
+ *   LSE[t] = ln sum_tau exp(scale q_t . k_tau), O[t] = sum_tau softmax v_tau
+ * over those keys; a query cluster with an empty row gets O = 0, LSE = -inf.
+ * Executed on 64-token tiles with every cluster padded to whole tiles (the
+ * tile-aligned cost of the page's Eq. 7 with tiles of 64 on both sides);
+ * padding keys are masked, so the result is exactly Eq. 4.  Precision as
+ * bsa_sparse_attn_fwd.
+ *
+ * perm_q / off_q: bsa_cluster_permute of the query clustering ([B,H,N],
+ *   [B,H,Nq+1]); perm_k / off_k the same for the keys ([B,H,Nk+1]).
+ * crow_ptr / ccol: cluster CSR with rows (b * H + h) * Nq + i and key cluster
+ *   indices in [0, Nk) (bsa_cluster_select).
+ * O: [B, H, N, d] with the strides of `shape`, o_dtype BSA_F32 or BSA_BF16;
+ *   LSE: float32 [B, H, N].
+ * out_tile_pairs: device int64 or NULL; receives the number of executed
+ *   (query tile, key tile) pairs.
+ * workspace: >= bsa_cluster_attn_workspace_bytes(shape, Nq, Nk, o_dtype)
+ *   bytes, 256-byte aligned (padded copies of Q, K, V and the output, the
+ *   tile lists): padded length per head 64 * (ceil(N/64) + max(Nq, Nk)).
+ * ---------------------------------------------------------------------- */
+int64_t bsa_cluster_attn_workspace_bytes(const bsa_shape* shape, int32_t Nq,
+                                         int32_t Nk, int32_t o_dtype);
+
+bsa_status bsa_cluster_attn_fwd(const uint16_t* Q, const uint16_t* K,
+                                const uint16_t* V, const bsa_shape* shape,
+                                float scale, int32_t Nq, int32_t Nk,
+                                const int32_t* perm_q, const int32_t* off_q,
+                                const int32_t* perm_k, const int32_t* off_k,
+                                const int32_t* crow_ptr, const int32_t* ccol,
+                                void* O, int32_t o_dtype, float* LSE,
+                                int64_t* out_tile_pairs, void* workspace,
+                                int64_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------
  * bsa_omission_risk -- per-head omission risk of a sparse support.  The

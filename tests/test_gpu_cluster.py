@@ -187,3 +187,108 @@ def test_cluster_select_hunyuanvideo_sizes():
     sizes[::97] = 0
     exempt = _select_case(mu_q, mu_k, sizes, 0.9, 183, 1215, "HunyuanVideo clusters")
     assert exempt <= 2
+
+
+# ------------------------------------------------- attention over clusters
+
+def _cluster_attn_case(Q, K, V, aq, ak, Nq, Nk, rows, out_dtype=torch.float32, sample=None):
+    """GPU Eq. 4 on oracle-made clusterings and lists against the oracle."""
+    import math
+    import parity as PT
+    N, d = Q.shape[2], Q.shape[3]
+    pq, oq = O.cluster_permutation(aq, Nq)
+    pk, ok = O.cluster_permutation(ak, Nk)
+    rp, ci = PT.rows_to_csr(rows)
+    t = lambda x: torch.from_numpy(np.asarray(x, dtype=np.int32)).to(DEV)
+    Og, Lg, pairs = bsa.bsa_cluster_attn_fwd(
+        Q.to(DEV), K.to(DEV), V.to(DEV), t(pq)[None, None], t(oq)[None, None], t(pk)[None, None],
+        t(ok)[None, None], rp.to(DEV), ci.to(DEV), out_dtype=out_dtype)
+    torch.cuda.synchronize()
+    assert int(pairs.item()) == O.cluster_tile_pairs(oq, ok, rows)
+    q, k, v = (X[0, 0].double().numpy() for X in (Q, K, V))
+    scale = 1 / math.sqrt(d)
+    if sample is None:
+        Oref, Lref = O.cluster_block_attention(q, k, v, pq, oq, pk, ok, rows, scale)
+        PT.compare_o_lse(Og[0, 0], Lg[0, 0], Oref, Lref, "cluster attention",
+                         bf16=out_dtype == torch.bfloat16)
+    else:
+        for i in sample:
+            qi = pq[oq[i]:oq[i + 1]]
+            if len(qi) == 0:
+                continue
+            keys = np.concatenate([pk[ok[j]:ok[j + 1]] for j in rows[i]] or [np.zeros(0, int)])
+            Oref, Lref = O.attend(q[qi], k[keys], v[keys], scale)
+            idx = torch.from_numpy(qi.astype(np.int64))
+            PT.compare_o_lse(Og[0, 0][idx.to(DEV)], Lg[0, 0][idx.to(DEV)], Oref, Lref,
+                             f"query cluster {i}")
+    return int(pairs.item())
+
+
+@pytest.mark.parametrize("grid,d,key,cq,ck,p", [((3, 7, 9), 128, 161, (1, 3, 3), (1, 2, 3), 0.9),
+                                               ((4, 16, 16), 64, 162, (2, 4, 4), (2, 2, 4), 0.5),
+                                               ((5, 15, 21), 128, 163, (2, 5, 5), (1, 5, 5), 0.7)])
+@pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16])
+def test_cluster_attention_small(grid, d, key, cq, ck, p, out_dtype):
+    import math
+    spec = VideoSpec(1, 1, d, grid, key)
+    Q, K, V = gen_qkv(spec)
+    x, y = Q[0, 0].double().numpy(), K[0, 0].double().numpy()
+    aq, mq, cnt_q = O.local_window_clustering(x, grid, cq, (2, 2, 2), 2)
+    ak, mk, cnt_k = O.local_window_clustering(y, grid, ck, (2, 2, 2), 2)
+    rows = O.cluster_topp_rows(mq, mk, cnt_k, 1 / math.sqrt(d), p, 1, len(cnt_k))
+    rows[0] = []                                   # a query cluster with an empty row
+    say("cluster attention", grid, len(cnt_q), "x", len(cnt_k), "clusters,",
+        int((cnt_q == 0).sum()), "empty query clusters")
+    _cluster_attn_case(Q, K, V, aq, ak, len(cnt_q), len(cnt_k), rows, out_dtype)
+
+
+def test_cluster_pipeline_end_to_end():
+    """GPU clustering, permutation, cluster top-p and Eq. 4 chained; the
+    integer decisions equal the oracle's here, so the outputs must too."""
+    import math
+    import parity as PT
+    grid, d, cq, ck, win = (4, 12, 16), 128, (2, 4, 4), (2, 3, 4), (2, 3, 3)
+    spec = VideoSpec(1, 1, d, grid, 164)
+    Q, K, V = gen_qkv(spec)
+    Qd, Kd, Vd = (X.to(DEV) for X in (Q, K, V))
+    aq, mq, cnt_q = bsa.bsa_local_window_cluster(Qd, grid, cq, win, 2)
+    ak, mk, cnt_k = bsa.bsa_local_window_cluster(Kd, grid, ck, win, 2)
+    pq, oq = bsa.bsa_cluster_permute(aq, cnt_q, Qd, grid, cq, win)
+    pk, ok = bsa.bsa_cluster_permute(ak, cnt_k, Kd, grid, ck, win)
+    Nk = cnt_k.shape[2]
+    rp, ci, nnz = bsa.bsa_cluster_select(mq, mk, cnt_k, p=0.9, k_min=2, k_cap=Nk)
+    Og, Lg, pairs = bsa.bsa_cluster_attn_fwd(Qd, Kd, Vd, pq, oq, pk, ok, rp, ci)
+    torch.cuda.synchronize()
+    x, y = Q[0, 0].double().numpy(), K[0, 0].double().numpy()
+    aq_o, mq_o, cq_o = O.local_window_clustering(x, grid, cq, win, 2)
+    ak_o, mk_o, ck_o = O.local_window_clustering(y, grid, ck, win, 2)
+    assert np.array_equal(aq_o, aq[0, 0].cpu().numpy())
+    assert np.array_equal(ak_o, ak[0, 0].cpu().numpy())
+    rows = O.cluster_topp_rows(mq_o, mk_o, ck_o, 1 / math.sqrt(d), 0.9, 2, Nk)
+    assert bsa.csr_rows(rp, ci, nnz) == rows, "cluster lists differ (a tie): pick other inputs"
+    pq_o, oq_o = O.cluster_permutation(aq_o, len(cq_o))
+    pk_o, ok_o = O.cluster_permutation(ak_o, len(ck_o))
+    Oref, Lref = O.cluster_block_attention(x, y, V[0, 0].double().numpy(), pq_o, oq_o, pk_o,
+                                           ok_o, rows, 1 / math.sqrt(d))
+    PT.compare_o_lse(Og[0, 0], Lg[0, 0], Oref, Lref, "pipeline")
+    assert int(pairs.item()) == O.cluster_tile_pairs(oq_o, ok_o, rows)
+
+
+def test_cluster_attention_hunyuanvideo_shape():
+    """118,800 tokens in 432 query and 1215 key clusters (the page's counts;
+    here each token's cluster is its grid cell), seeded cluster lists at
+    about 15% of the key clusters; sampled query clusters against the
+    oracle."""
+    spec = config_spec(3)
+    Q, K, V = gen_qkv(spec, heads=[0])
+    T, H, W = spec.grid
+    t, y, x = np.meshgrid(np.arange(T), np.arange(H), np.arange(W), indexing="ij")
+    cell = lambda k: ((t // k[0]) * -(-H // k[1]) + y // k[1]) * -(-W // k[2]) + x // k[2]
+    aq = cell((11, 5, 5)).reshape(-1)
+    ak = cell((11, 3, 3)).reshape(-1)
+    rng = np.random.default_rng(320)
+    rows = [sorted(rng.choice(1215, size=int(rng.integers(120, 240)), replace=False).tolist())
+            for _ in range(432)]
+    pairs = _cluster_attn_case(Q, K, V, aq, ak, 432, 1215, rows,
+                               sample=sorted(rng.choice(432, 6, replace=False).tolist()) + [431])
+    say(f"HunyuanVideo shape: {pairs} tile pairs")
