@@ -44,6 +44,7 @@ FP32_TFLOPS = 78.6     # MI355X fp32 vector FMA rate without packed math
 CLUSTER_CELLS = {2: ((7, 6, 6), (6, 4, 4)), 3: ((11, 5, 5), (11, 3, 3))}
 CLUSTER_WINDOW = (3, 8, 8)
 CLUSTER_ITERS = 3
+HVA_MIN_KC = {2: 0.18, 3: 0.15}   # the page's Min-kc per layer (Wan 720p, HunyuanVideo)
 FLUSH_BYTES = 512 << 20  # larger than L2 (8 x 4 MB) plus the 256 MB Infinity Cache
 
 
@@ -74,6 +75,10 @@ def parse():
     ap.add_argument("--cluster", action="store_true",
                     help="also time the 3D local-window clustering of Q and K (all heads) with "
                          "the page's grids and (3, 8, 8) windows, 3 iterations")
+    ap.add_argument("--hva", action="store_true",
+                    help="also run the cluster-induced block pipeline (local-window clustering, "
+                         "permutation, cluster top-p 0.9 with the page's Min-kc, attention over "
+                         "the clusters) and report its stages")
     ap.add_argument("--calibration-copy", action="store_true",
                     help="first run a plain 256 MiB device copy (reads 256 MiB, writes "
                          "256 MiB) three times, to scale hardware byte counters")
@@ -406,6 +411,64 @@ def main():
                        "assign_tflops": round(flops / (tot * 1e-3) / 1e12, 2),
                        "frac_fp32_peak": round(flops / (tot * 1e-3) / 1e12 / FP32_TFLOPS, 4)}
 
+    hva_out = None
+    if args.hva:
+        cq, ck = CLUSTER_CELLS.get(cfg, CLUSTER_CELLS[2])
+        thw, win, it = spec.grid, CLUSTER_WINDOW, CLUSTER_ITERS
+        min_kc = HVA_MIN_KC.get(cfg, 0.18)
+        st = {}
+
+        def clus():
+            return (bsa.bsa_local_window_cluster(Q, thw, cq, win, it),
+                    bsa.bsa_local_window_cluster(K, thw, ck, win, it))
+
+        (aq, mq, nq), (ak, mk, nk) = clus()
+        Nq, Nk = nq.shape[2], nk.shape[2]
+        k_min = math.ceil(min_kc * Nk)
+
+        def perm():
+            return (bsa.bsa_cluster_permute(aq, nq, Q, thw, cq, win),
+                    bsa.bsa_cluster_permute(ak, nk, K, thw, ck, win))
+
+        (pq, oq), (pk, ok) = perm()
+
+        def csel():
+            return bsa.bsa_cluster_select(mq, mk, nk, p=0.9, k_min=k_min, k_cap=Nk)
+
+        crp, cci, cnnz = csel()
+
+        def cattn():
+            return bsa.bsa_cluster_attn_fwd(Q, K, V, pq, oq, pk, ok, crp, cci)
+
+        _, _, pairs = cattn()
+        r3 = max(3, reps // 3)
+        st["cluster_qk"], _ = events_ms(clus, r3, stream)
+        st["permute_qk"], _ = events_ms(perm, r3, stream)
+        st["cluster_select"], _ = events_ms(csel, r3, stream)
+        st["cluster_attn"], _ = events_ms(cattn, r3, stream)
+        torch.cuda.synchronize()
+        pairs_v = int(pairs.item())
+        # token-level density of the cluster mask: sum_i s_i * sum_{j in A_i} s_j / N^2
+        sq = (oq[..., 1:] - oq[..., :-1]).double()
+        sk = (ok[..., 1:] - ok[..., :-1]).double()
+        rows_c = bsa.csr_rows(crp, cci, cnnz)
+        tok_pairs = 0.0
+        sk_list = sk.reshape(B * H, Nk).cpu().numpy()
+        sq_list = sq.reshape(B * H, Nq).cpu().numpy()
+        for r, cols in enumerate(rows_c):
+            z, i = divmod(r, Nq)
+            tok_pairs += sq_list[z][i] * sk_list[z][cols].sum()
+        hva_flops = 4 * d * 64 * 64 * pairs_v
+        total = sum(st.values())
+        hva_out = {"q_cells": Nq, "k_cells": Nk, "p": 0.9, "min_kc": min_kc, "k_min": k_min,
+                   "stages_ms": {k: round(v, 4) for k, v in st.items()},
+                   "tile_pairs": pairs_v,
+                   "token_density": round(tok_pairs / (B * H * N * N), 4),
+                   "tile_density": round(pairs_v / (B * H * bsa.n_blocks(N) ** 2), 4),
+                   "attn_tflops_executed": round(hva_flops / (st["cluster_attn"] * 1e-3) / 1e12, 2),
+                   "speedup_attn_vs_dense": round(dense_ms / st["cluster_attn"], 3),
+                   "speedup_pipeline_vs_dense": round(dense_ms / total, 3)}
+
     attn_tflops = macro_flops / (attn_ms * 1e-3) / 1e12
     kernel_src = os.path.join(ROOT, "block_sparse_attention_pool_amd", "csrc", "attn.hip")
     # the committed counters were taken on the default workload and selection
@@ -443,6 +506,7 @@ def main():
         "omission_risk": risk_out,
         **({"pooled_rectify": rect_out} if rect_out is not None else {}),
         **({"local_window_cluster": cluster_out} if cluster_out is not None else {}),
+        **({"hva_cluster_pipeline": hva_out} if hva_out is not None else {}),
         "roofline": {"bound": "mfma", "achieved": round(attn_tflops, 2), "peak": PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(attn_tflops / PEAK_TFLOPS, 4),
                      "traffic": traffic},
