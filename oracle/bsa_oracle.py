@@ -13,8 +13,9 @@ definitions below state.
 Sources (pages as titled):
   [HVA]   "HyperVAttention: Efficient Sparse Attention with Spatio-Temporal
           Clustering for Video Diffusion", section 2 (Preliminaries), Eq. 2-4,
-          section 4.1 (3D local-window clustering, Eq. 5), Appendix A.1
-          (Top-p, Min-kc) and A.2 (Algorithm 2).
+          section 4.1 (3D local-window clustering, Eq. 5), section 4.3
+          (hardware cost, Eq. 7-10, Algorithm 1), Appendix A.1 (Top-p,
+          Min-kc, R = 3 rounds) and A.2 (Algorithm 2).
   [RSA]   "Rectified SpaAttn: Revisiting Attention Sparsity for Efficient Video
           Generation", abstract: pooled query-key interactions.
   [HyMoR] "HyMoR-Attn: Granularity-Matched Repair of Omitted Attention Support
@@ -53,7 +54,11 @@ design notes of the repository):
     returned;
   * RSA's pooled rectification is read as attention over the pooled keys of
     the omitted blocks (log-size bias), LSE-merged with the sparse result;
-    its gain-aware gate has no stated rule and is not modelled.
+    its gain-aware gate has no stated rule and is not modelled;
+  * [HVA] Algorithm 1: the random bipartition is an input (a side bit per
+    round for every group, read at the group's lowest member); side-0 groups
+    choose, ties go to lower indices; a merged group is named by its lowest
+    member.
 """
 
 from __future__ import annotations
@@ -655,6 +660,130 @@ def cluster_tile_pairs(off_q, off_k, rows, tile: int = 64) -> int:
     tq = -(-sq // tile)
     tk = -(-sk // tile)
     return int(sum(int(tq[i]) * int(sum(int(tk[j]) for j in sel)) for i, sel in enumerate(rows)))
+
+
+def merge_cost(sq: int, chi, sizes_k, tau_q: int = 64, tau_k: int = 64, g: int = 1) -> int:
+    """[HVA] Eq. 7-8: the CTA-aligned work of one query group,
+    tau_q ceil(s^q / tau_q) * tau_k ceil(sum_j chi_j s_j^k / tau_k), with the
+    selected key clusters packed one after another.  ``g`` is the packing
+    grain of a key cluster: with g > 1 each cluster occupies g ceil(s_j / g)
+    key slots (g = 1 is the page's form)."""
+    sk = np.asarray(sizes_k, dtype=np.int64)
+    slots = g * (-(-sk // g))
+    keys = int(sum(int(slots[j]) for j in range(len(sk)) if chi[j]))
+    return (tau_q * (-(-int(sq) // tau_q))) * (tau_k * (-(-keys // tau_k)))
+
+
+def partition_cost(groups: list[list[int]], sizes_q, rows, sizes_k,
+                   tau_q: int = 64, tau_k: int = 64, g: int = 1) -> int:
+    """[HVA] Eq. 9: the total of Eq. 8 over a partition of the query
+    clusters; a group's key set is the union of its members' rows."""
+    total = 0
+    for S in groups:
+        chi = np.zeros(len(sizes_k), dtype=bool)
+        for i in S:
+            chi[list(rows[i])] = True
+        total += merge_cost(sum(int(sizes_q[i]) for i in S), chi, sizes_k, tau_q, tau_k, g)
+    return total
+
+
+def agglomerative_merge(sizes_q, rows, sizes_k, sides, tau_q: int = 64, tau_k: int = 64,
+                        g: int = 1):
+    """[HVA] Algorithm 1 (parallel agglomerative merging), Eq. 8 and 10.
+
+    Starts from singleton groups.  In round r every active group is put on
+    one side of the bipartition by ``sides[r][rep]`` (0 or 1), where ``rep``
+    is the group's lowest query-cluster index; the random draw is the
+    caller's.  Every group A on side 0 finds the group B on side 1 that
+    minimises the merge gain dC(A, B) = C(A u B) - C(A) - C(B) (Eq. 10; ties
+    to the lower B).  Among the groups A choosing the same B with a negative
+    gain, the one with the smallest gain is kept (ties to the lower A).  The
+    kept pairs are disjoint and all merge at the end of the round.
+
+    Returns (group id of every query cluster = its group's lowest member,
+    list of groups, each ascending, ordered by their lowest member)."""
+    nq = len(sizes_q)
+    nk = len(sizes_k)
+    grp = list(range(nq))
+    members = {i: [i] for i in range(nq)}
+    chi = {}
+    for i in range(nq):
+        c = np.zeros(nk, dtype=bool)
+        c[list(rows[i])] = True
+        chi[i] = c
+    sq = {i: int(sizes_q[i]) for i in range(nq)}
+
+    for r in range(len(sides)):
+        active = sorted(members)
+        side_a = [A for A in active if sides[r][A] == 0]
+        side_b = [B for B in active if sides[r][B] == 1]
+        if not side_a or not side_b:
+            continue
+        choice = {}
+        for A in side_a:
+            best = None
+            for B in side_b:
+                gain = merge_gain(sq[A], chi[A], sq[B], chi[B], sizes_k, tau_q, tau_k, g)
+                if best is None or gain < best[0]:
+                    best = (gain, B)
+            choice[A] = best
+        accepted = disjoint_merges(choice)
+        for B, (gain, A) in accepted.items():
+            lo, hi = min(A, B), max(A, B)
+            members[lo] = sorted(members[lo] + members.pop(hi))
+            chi[lo] = chi[lo] | chi.pop(hi)
+            sq[lo] = sq[lo] + sq.pop(hi)
+            for i in members[lo]:
+                grp[i] = lo
+    groups = [members[k] for k in sorted(members)]
+    return np.asarray(grp, dtype=np.int64), groups
+
+
+def merge_gain(sq_a: int, chi_a, sq_b: int, chi_b, sizes_k, tau_q: int = 64,
+               tau_k: int = 64, g: int = 1) -> int:
+    """[HVA] Eq. 10: dC(A, B) = C(A u B) - C(A) - C(B); the union adds the
+    query sizes and ORs the key-cluster masks (Eq. 8)."""
+    union = np.asarray(chi_a, bool) | np.asarray(chi_b, bool)
+    return (merge_cost(sq_a + sq_b, union, sizes_k, tau_q, tau_k, g)
+            - merge_cost(sq_a, chi_a, sizes_k, tau_q, tau_k, g)
+            - merge_cost(sq_b, chi_b, sizes_k, tau_q, tau_k, g))
+
+
+def disjoint_merges(choice: dict) -> dict:
+    """[HVA] Algorithm 1, the accepted set: from every chooser A's best
+    (gain, B), keep the pairs with a negative gain and, for each target B,
+    only the chooser of smallest gain (ties to the lower A).  Returns
+    {B: (gain, A)}."""
+    accepted = {}
+    for A in sorted(choice):
+        gain, B = choice[A]
+        if gain >= 0:
+            continue
+        if B not in accepted or gain < accepted[B][0]:
+            accepted[B] = (gain, A)
+    return accepted
+
+
+def group_rows(groups: list[list[int]], rows) -> list[list[int]]:
+    """[HVA] Eq. 8: every member of a merged group attends over the union of
+    the group's rows (chi_j(S) = max over members of m_ij)."""
+    out = [None] * sum(len(S) for S in groups)
+    for S in groups:
+        u = sorted(set().union(*[set(rows[i]) for i in S]))
+        for i in S:
+            out[i] = u
+    return out
+
+
+def packed_tile_pairs(off_q, off_k, groups: list[list[int]], rows, tile: int = 64,
+                      g: int = 16) -> int:
+    """Work of Eq. 4 on tiles when every query group fills whole query tiles
+    and its key clusters are packed one after another at a grain of g
+    tokens: sum over groups of ceil(s^q(S) / tile) * ceil(sum g ceil(s_j/g) / tile)
+    -- Eq. 8 divided by tile^2."""
+    sq = np.diff(np.asarray(off_q))
+    sk = np.diff(np.asarray(off_k))
+    return partition_cost(groups, sq, rows, sk, tile, tile, g) // (tile * tile)
 
 
 def assignment_margins(X, thw, cell, window, mu):

@@ -833,3 +833,181 @@ def test_pins_catch_planted_mistakes(mistake, monkeypatch):
     tq, tk, tv = (torch.from_numpy(x)[None, None] for x in (Q, K, V))
     ref = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, scale=s)
     assert not np.allclose(Ov, ref[0, 0].numpy(), atol=1e-9)
+
+
+# --------------------------------------------- HVA hardware cost and merging
+
+def _group_state(members, rows, nk):
+    chi = np.zeros(nk, dtype=bool)
+    for i in members:
+        chi[list(rows[i])] = True
+    return chi
+
+
+def test_golden_merge_cost():
+    g = _load("hva_merge_rounds.json")
+    for c in g["cost_cases"]:
+        got = O.merge_cost(c["sq"], np.array(c["chi"], bool), c["sizes_k"], g["tau_q"],
+                           g["tau_k"], c["g"])
+        assert got == c["cost"], c["note"]
+
+
+def test_golden_merge_rounds():
+    g = _load("hva_merge_rounds.json")
+    m = g["merge"]
+    sq, sk, rows = m["sizes_q"], m["sizes_k"], m["rows"]
+    nk = len(sk)
+    for i, c in enumerate(m["singleton_costs"]):
+        assert O.partition_cost([[i]], sq, rows, sk) == c
+
+    def gain(a_members, b_members):
+        return O.merge_gain(sum(sq[i] for i in a_members), _group_state(a_members, rows, nk),
+                            sum(sq[i] for i in b_members), _group_state(b_members, rows, nk), sk)
+
+    assert gain([1], [0]) == m["round1_gains"]["1->0"]
+    assert gain([1], [3]) == m["round1_gains"]["1->3"]
+    assert gain([2], [0]) == m["round1_gains"]["2->0"]
+    assert gain([2], [3]) == m["round1_gains"]["2->3"]
+    assert gain([0, 2], [1]) == m["round2_gains"]["0->1"]
+    assert gain([0, 2], [3]) == m["round2_gains"]["0->3"]
+    assert gain([3], [0, 1, 2]) == m["round3_gains"]["3->0"]
+    for r, key in [(1, "round1_groups"), (2, "round2_groups"), (3, "final_groups")]:
+        _, groups = O.agglomerative_merge(sq, rows, sk, m["sides"][:r])
+        assert groups == m[key], key
+    grp, groups = O.agglomerative_merge(sq, rows, sk, m["sides"])
+    assert grp.tolist() == m["final_group_of"]
+    assert O.partition_cost(groups, sq, rows, sk) == m["final_cost"]
+    assert _best_partition_cost(sq, rows, sk) == m["optimal_cost"]
+
+
+def _partitions(items):
+    if not items:
+        yield []
+        return
+    first, rest = items[0], items[1:]
+    for p in _partitions(rest):
+        for k in range(len(p)):
+            yield p[:k] + [[first] + p[k]] + p[k + 1:]
+        yield [[first]] + p
+
+
+def _best_partition_cost(sq, rows, sk, g=1):
+    """Eq. 9 solved exactly by enumerating every partition (tiny inputs)."""
+    return min(O.partition_cost(p, sq, rows, sk, 64, 64, g) for p in _partitions(list(range(len(sq)))))
+
+
+def _random_merge_instance(seed, nq, nk):
+    rng = np.random.default_rng(seed)
+    sq = rng.integers(0, 90, nq).tolist()
+    sk = rng.integers(1, 70, nk).tolist()
+    rows = [sorted(rng.choice(nk, int(rng.integers(0, nk + 1)), replace=False).tolist())
+            for _ in range(nq)]
+    sides = rng.integers(0, 2, (3, nq)).tolist()
+    return sq, sk, rows, sides
+
+
+@pytest.mark.parametrize("seed", range(12))
+@pytest.mark.parametrize("g", [1, 16])
+def test_merge_is_a_valid_partition_that_never_raises_the_cost(seed, g):
+    sq, sk, rows, sides = _random_merge_instance(900 + seed, 6, 5)
+    start = O.partition_cost([[i] for i in range(6)], sq, rows, sk, 64, 64, g)
+    prev = start
+    for r in range(1, 4):
+        grp, groups = O.agglomerative_merge(sq, rows, sk, sides[:r], g=g)
+        assert sorted(i for S in groups for i in S) == list(range(6))
+        for S in groups:
+            assert all(grp[i] == min(S) for i in S) and S == sorted(S)
+        cost = O.partition_cost(groups, sq, rows, sk, 64, 64, g)
+        assert cost <= prev          # every accepted merge has a negative gain
+        prev = cost
+    assert prev >= _best_partition_cost(sq, rows, sk, g)
+
+
+@pytest.mark.parametrize("seed", range(20))
+def test_merge_of_two_clusters_follows_the_sign_of_the_gain(seed):
+    sq, sk, rows, _ = _random_merge_instance(950 + seed, 2, 4)
+    grp, groups = O.agglomerative_merge(sq, rows, sk, [[0, 1]])
+    together = O.partition_cost([[0, 1]], sq, rows, sk) < O.partition_cost([[0], [1]], sq, rows, sk)
+    assert (groups == [[0, 1]]) == together
+
+
+def test_merge_without_rounds_or_with_one_side_keeps_singletons():
+    sq, sk, rows, _ = _random_merge_instance(990, 5, 4)
+    for sides in ([], [[0] * 5], [[1] * 5]):
+        grp, groups = O.agglomerative_merge(sq, rows, sk, sides)
+        assert groups == [[i] for i in range(5)] and grp.tolist() == list(range(5))
+
+
+def test_packed_pairs_and_group_rows():
+    off_q = [0, 64, 128, 192]        # three query clusters of 64
+    off_k = [0, 64, 192, 256]        # key clusters of 64, 128, 64
+    rows = [[0], [1, 2], [2]]
+    # tile-aligned clusters: packing changes nothing
+    singles = [[0], [1], [2]]
+    assert O.packed_tile_pairs(off_q, off_k, singles, O.group_rows(singles, rows)) == \
+        O.cluster_tile_pairs(off_q, off_k, rows) == 1 + 3 + 1
+    merged = [[0, 2], [1]]
+    gr = O.group_rows(merged, rows)
+    assert gr == [[0, 2], [1, 2], [0, 2]]
+    assert O.packed_tile_pairs(off_q, off_k, merged, gr) == 2 * 2 + 1 * 3
+    # 16-token grain: a key cluster of 20 takes 32 slots, packed with 40 -> 48
+    off_k2 = [0, 20, 60]
+    assert O.packed_tile_pairs([0, 10], off_k2, [[0]], [[0, 1]], g=16) == 2
+    assert O.packed_tile_pairs([0, 10], off_k2, [[0]], [[0, 1]], g=1) == 1
+
+
+def test_attention_over_merged_groups_is_masked_dense_softmax():
+    """Every query of a merged group attends over the union of the group's
+    key clusters: the token-level mask built directly, through SDPA in fp64."""
+    rng = np.random.default_rng(77)
+    N, d = 90, 16
+    Q, K, V = _rand(71, N, d), _rand(72, N, d), _rand(73, N, d)
+    aq = rng.integers(0, 5, N)
+    ak = rng.integers(0, 4, N)
+    rows = [[0], [1, 3], [2], [], [0, 2]]
+    groups = [[0, 2], [1], [3, 4]]
+    gr = O.group_rows(groups, rows)
+    pq, oq = O.cluster_permutation(aq, 5)
+    pk, ok = O.cluster_permutation(ak, 4)
+    Oc, Lc = O.cluster_block_attention(Q, K, V, pq, oq, pk, ok, gr, 1 / math.sqrt(d))
+    group_of = {i: gi for gi, S in enumerate(groups) for i in S}
+    keys_of = [set().union(*[set(rows[i]) for i in S]) for S in groups]
+    M = np.array([[ak[t] in keys_of[group_of[aq[s]]] for t in range(N)] for s in range(N)])
+    tq, tk, tv = (torch.from_numpy(x)[None, None] for x in (Q, K, V))
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        tq, tk, tv, attn_mask=torch.from_numpy(M)[None, None], scale=1 / math.sqrt(d))[0, 0].numpy()
+    has = M.any(axis=1)
+    np.testing.assert_allclose(Oc[has], ref[has], atol=1e-12)
+    assert np.all(Oc[~has] == 0) and np.all(np.isneginf(Lc[~has]))
+
+
+@pytest.mark.parametrize("mistake", ["gain_sign", "first_chooser", "no_union", "no_query_ceil"])
+def test_merge_pins_catch_planted_mistakes(mistake, monkeypatch):
+    g = _load("hva_merge_rounds.json")
+    m = g["merge"]
+    if mistake == "gain_sign":
+        real = O.merge_gain
+        monkeypatch.setattr(O, "merge_gain", lambda *a, **k: -real(*a, **k))
+    elif mistake == "first_chooser":
+        def first(choice):
+            out = {}
+            for A in sorted(choice):
+                gain, B = choice[A]
+                if gain < 0 and B not in out:
+                    out[B] = (gain, A)
+            return out
+        monkeypatch.setattr(O, "disjoint_merges", first)
+    elif mistake == "no_union":
+        real_cost = O.merge_cost
+
+        def gain_a_only(sq_a, chi_a, sq_b, chi_b, sizes_k, tau_q=64, tau_k=64, gg=1):
+            return (real_cost(sq_a + sq_b, chi_a, sizes_k, tau_q, tau_k, gg)
+                    - real_cost(sq_a, chi_a, sizes_k, tau_q, tau_k, gg)
+                    - real_cost(sq_b, chi_b, sizes_k, tau_q, tau_k, gg))
+        monkeypatch.setattr(O, "merge_gain", gain_a_only)
+    else:
+        monkeypatch.setattr(O, "merge_cost", lambda sq, chi, sk, tq=64, tk=64, gg=1: int(sq) * (
+            tk * (-(-int(sum(np.asarray(sk)[np.asarray(chi, bool)])) // tk))))
+    with pytest.raises(AssertionError):
+        test_golden_merge_cost()
+        test_golden_merge_rounds()
