@@ -45,6 +45,7 @@ CLUSTER_CELLS = {2: ((7, 6, 6), (6, 4, 4)), 3: ((11, 5, 5), (11, 3, 3))}
 CLUSTER_WINDOW = (3, 8, 8)
 CLUSTER_ITERS = 3
 HVA_MIN_KC = {2: 0.18, 3: 0.15}   # the page's Min-kc per layer (Wan 720p, HunyuanVideo)
+HVA_ROUNDS = 3                     # rounds of cluster merging (the page's R)
 FLUSH_BYTES = 512 << 20  # larger than L2 (8 x 4 MB) plus the 256 MB Infinity Cache
 
 
@@ -165,7 +166,8 @@ def main():
 
     import torch
     import block_sparse_attention_pool_amd as bsa
-    from synth import CONFIGS, config_spec, gen_qkv, micro_heads, mod_pattern_mask, rotation_offset
+    from synth import (CONFIGS, config_spec, gen_qkv, merge_sides, micro_heads, mod_pattern_mask,
+                       rotation_offset)
 
     if args.calibration_copy:
         src = torch.ones(64 << 20, dtype=torch.float32, device="cuda:0")
@@ -437,36 +439,60 @@ def main():
 
         crp, cci, cnnz = csel()
 
+        sides = torch.from_numpy(merge_sides(spec.key, B, H, HVA_ROUNDS, Nq)).to(dev)
+
+        def cmerge():
+            return bsa.bsa_cluster_merge(oq, ok, crp, cci, sides, N=N)
+
+        gof = cmerge()
+
         def cattn():
             return bsa.bsa_cluster_attn_fwd(Q, K, V, pq, oq, pk, ok, crp, cci)
 
+        def cattn_merged():
+            return bsa.bsa_cluster_attn_fwd(Q, K, V, pq, oq, pk, ok, crp, cci, gof)
+
         _, _, pairs = cattn()
+        _, _, pairs_m = cattn_merged()
         r3 = max(3, reps // 3)
         st["cluster_qk"], _ = events_ms(clus, r3, stream)
         st["permute_qk"], _ = events_ms(perm, r3, stream)
         st["cluster_select"], _ = events_ms(csel, r3, stream)
-        st["cluster_attn"], _ = events_ms(cattn, r3, stream)
+        st["cluster_merge"], _ = events_ms(cmerge, r3, stream)
+        st["cluster_attn_merged"], _ = events_ms(cattn_merged, r3, stream)
+        attn_unmerged_ms, _ = events_ms(cattn, r3, stream)
         torch.cuda.synchronize()
-        pairs_v = int(pairs.item())
-        # token-level density of the cluster mask: sum_i s_i * sum_{j in A_i} s_j / N^2
-        sq = (oq[..., 1:] - oq[..., :-1]).double()
-        sk = (ok[..., 1:] - ok[..., :-1]).double()
+        pairs_v, pairs_mv = int(pairs.item()), int(pairs_m.item())
+        groups = int(sum(len(set(g.tolist())) for g in gof.reshape(B * H, Nq).cpu()))
+        # token-level density of the cluster mask before and after merging:
+        # sum over query clusters of s_i times the tokens of its (group's) key clusters
+        sq = (oq[..., 1:] - oq[..., :-1]).double().reshape(B * H, Nq).cpu().numpy()
+        sk = (ok[..., 1:] - ok[..., :-1]).double().reshape(B * H, Nk).cpu().numpy()
         rows_c = bsa.csr_rows(crp, cci, cnnz)
-        tok_pairs = 0.0
-        sk_list = sk.reshape(B * H, Nk).cpu().numpy()
-        sq_list = sq.reshape(B * H, Nq).cpu().numpy()
-        for r, cols in enumerate(rows_c):
-            z, i = divmod(r, Nq)
-            tok_pairs += sq_list[z][i] * sk_list[z][cols].sum()
-        hva_flops = 4 * d * 64 * 64 * pairs_v
+        gl = gof.reshape(B * H, Nq).cpu().numpy()
+        tok_pairs = tok_pairs_m = 0.0
+        for z in range(B * H):
+            union = {}
+            for i in range(Nq):
+                union.setdefault(gl[z][i], set()).update(rows_c[z * Nq + i])
+            for i in range(Nq):
+                tok_pairs += sq[z][i] * sk[z][rows_c[z * Nq + i]].sum()
+                tok_pairs_m += sq[z][i] * sk[z][sorted(union[gl[z][i]])].sum()
+        hva_flops = 4 * d * 64 * 64 * pairs_mv
         total = sum(st.values())
+        full = B * H * N * N
         hva_out = {"q_cells": Nq, "k_cells": Nk, "p": 0.9, "min_kc": min_kc, "k_min": k_min,
+                   "merge_rounds": HVA_ROUNDS, "groups": groups,
                    "stages_ms": {k: round(v, 4) for k, v in st.items()},
-                   "tile_pairs": pairs_v,
-                   "token_density": round(tok_pairs / (B * H * N * N), 4),
-                   "tile_density": round(pairs_v / (B * H * bsa.n_blocks(N) ** 2), 4),
-                   "attn_tflops_executed": round(hva_flops / (st["cluster_attn"] * 1e-3) / 1e12, 2),
-                   "speedup_attn_vs_dense": round(dense_ms / st["cluster_attn"], 3),
+                   "tile_pairs": pairs_mv, "tile_pairs_unmerged": pairs_v,
+                   "token_density": round(tok_pairs_m / full, 4),
+                   "token_density_unmerged": round(tok_pairs / full, 4),
+                   "tile_density": round(pairs_mv / (B * H * bsa.n_blocks(N) ** 2), 4),
+                   "tile_density_unmerged": round(pairs_v / (B * H * bsa.n_blocks(N) ** 2), 4),
+                   "cluster_attn_unmerged_ms": round(attn_unmerged_ms, 4),
+                   "attn_tflops_executed": round(
+                       hva_flops / (st["cluster_attn_merged"] * 1e-3) / 1e12, 2),
+                   "speedup_attn_vs_dense": round(dense_ms / st["cluster_attn_merged"], 3),
                    "speedup_pipeline_vs_dense": round(dense_ms / total, 3)}
 
     attn_tflops = macro_flops / (attn_ms * 1e-3) / 1e12

@@ -91,8 +91,11 @@ def _load(path: str = _LIB_PATH):
         "bsa_cluster_permute": ([P, P, SP, CP, P, P, P, I64, P], I32),
         "bsa_cluster_select_workspace_bytes": ([I32, I32, I32, I32], I64),
         "bsa_cluster_attn_workspace_bytes": ([SP, I32, I32, I32], I64),
-        "bsa_cluster_attn_fwd": ([P, P, P, SP, F32, I32, I32, P, P, P, P, P, P, P, I32, P, P, P, I64,
-                                  P], I32),
+        "bsa_cluster_attn_fwd": ([P, P, P, SP, F32, I32, I32, P, P, P, P, P, P, P, P, I32, P, P, P,
+                                  I64, P], I32),
+        "bsa_cluster_merge_workspace_bytes": ([I32, I32, I32, I32, I32, I32], I64),
+        "bsa_cluster_merge": ([P, P, P, P, I32, I32, I32, I32, I32, P, I32, I32, I32, I32, P, P,
+                               I64, P], I32),
         "bsa_cluster_select": ([P, P, P, I32, I32, I32, I32, I32, F32, F32, I32, I32, P, P, I64,
                                 P, P, I64, P], I32),
         "bsa_pooled_rectify": ([P, P, P, SP, I32, F32, P, P, P, I32, P, P, I64, P], I32),
@@ -114,7 +117,8 @@ EXPORTED = ("bsa_version", "bsa_last_error", "bsa_score_blocks", "bsa_select_wor
             "bsa_cluster_workspace_bytes", "bsa_local_window_cluster",
             "bsa_cluster_permute_workspace_bytes", "bsa_cluster_permute",
             "bsa_cluster_select_workspace_bytes", "bsa_cluster_select",
-            "bsa_cluster_attn_workspace_bytes", "bsa_cluster_attn_fwd")
+            "bsa_cluster_attn_workspace_bytes", "bsa_cluster_attn_fwd",
+            "bsa_cluster_merge_workspace_bytes", "bsa_cluster_merge")
 
 
 def library_path() -> str:
@@ -479,11 +483,38 @@ def bsa_cluster_select(mu_q, mu_k, size_k, *, p: float = 0.9, k_min: int = 1,
     return row_ptr, col_idx, nnz
 
 
-def bsa_cluster_attn_fwd(Q, K, V, perm_q, off_q, perm_k, off_k, crow_ptr, ccol, *,
+def bsa_cluster_merge(off_q, off_k, crow_ptr, ccol, sides, *, N: int, tau_q: int = 64,
+                      tau_k: int = 64, grain: int = 16, stream=None):
+    """Merging of query clusters by tiled cost (HVA Algorithm 1).  off_q
+    [B,H,Nq+1], off_k [B,H,Nk+1] int32 cluster offsets; the cluster CSR of
+    bsa_cluster_select; sides uint8 [B,H,rounds,Nq] (the bipartition of every
+    round).  Returns group_of int32 [B,H,Nq] (each cluster's group named by
+    its lowest member)."""
+    B, H = off_q.shape[0], off_q.shape[1]
+    Nq, Nk = off_q.shape[2] - 1, off_k.shape[2] - 1
+    if sides.dtype != torch.uint8 or sides.dim() != 4 or tuple(sides.shape[:2]) != (B, H) \
+            or sides.shape[3] != Nq or not sides.is_contiguous():
+        raise ValueError("sides must be contiguous uint8 [B, H, rounds, Nq]")
+    rounds = sides.shape[2]
+    nws = _lib.bsa_cluster_merge_workspace_bytes(B, H, N, Nq, Nk, grain)
+    if nws < 0:
+        raise BsaError(f"bsa_cluster_merge_workspace_bytes: {bsa_last_error()}")
+    dev = off_q.device
+    group_of = torch.empty((B, H, Nq), dtype=torch.int32, device=dev)
+    ws = torch.empty(max(nws, 256), dtype=torch.uint8, device=dev)
+    st = _lib.bsa_cluster_merge(_ptr(off_q), _ptr(off_k), _ptr(crow_ptr), _ptr(ccol), B, H, N, Nq,
+                                Nk, _ptr(sides), rounds, tau_q, tau_k, grain, _ptr(group_of),
+                                _ptr(ws), ws.numel(), _stream(stream, dev))
+    _check(st, "bsa_cluster_merge")
+    return group_of
+
+
+def bsa_cluster_attn_fwd(Q, K, V, perm_q, off_q, perm_k, off_k, crow_ptr, ccol, group_of=None, *,
                          scale: float | None = None, out_dtype=torch.float32, stream=None):
-    """Attention over cluster-induced blocks (HVA Eq. 4).  Returns (O
-    [B,H,N,d] out_dtype, LSE float32 [B,H,N], executed tile pairs int64
-    device scalar)."""
+    """Attention over cluster-induced blocks (HVA Eq. 4), each query cluster
+    over the union of its group's rows when ``group_of`` [B,H,Nq] is given.
+    Returns (O [B,H,N,d] out_dtype, LSE float32 [B,H,N], executed tile pairs
+    int64 device scalar)."""
     _same_layout(Q, K, V)
     shp = shape_of(Q)
     Nq, Nk = off_q.shape[2] - 1, off_k.shape[2] - 1
@@ -499,7 +530,8 @@ def bsa_cluster_attn_fwd(Q, K, V, perm_q, off_q, perm_k, off_k, crow_ptr, ccol, 
     ws = torch.empty(max(nws, 256), dtype=torch.uint8, device=dev)
     st = _lib.bsa_cluster_attn_fwd(_ptr(Q), _ptr(K), _ptr(V), ctypes.byref(shp), scale, Nq, Nk,
                                    _ptr(perm_q), _ptr(off_q), _ptr(perm_k), _ptr(off_k),
-                                   _ptr(crow_ptr), _ptr(ccol), _ptr(O), odt, _ptr(L), _ptr(pairs),
+                                   _ptr(crow_ptr), _ptr(ccol), _ptr(group_of), _ptr(O), odt, _ptr(L),
+                                   _ptr(pairs),
                                    _ptr(ws), ws.numel(), _stream(stream, dev))
     _check(st, "bsa_cluster_attn_fwd")
     return O, L, pairs

@@ -136,27 +136,37 @@ bsa_status plan_cluster(const bsa_shape* s, const bsa_cluster_params* p, int64_t
   return BSA_OK;
 }
 
-// Workspace of bsa_cluster_attn_fwd, carved in this order.
+// Workspace of bsa_cluster_attn_fwd, carved in this order.  Queries are
+// padded per group to whole 64-tiles (at most ceil(N/64) + Nq tiles per
+// head), keys per cluster to whole 16-chunks plus one all-padding chunk (at
+// most ceil(N/16) + Nk + 1 chunks); both layouts share one length NP.
 struct ClusterAttnPlan {
-  int64_t NP, nTP, BH;
-  int64_t tq, tk, qp, kp, vp, vt, op, lp, kv, qc, cnt, rp, nnz, col, total, cap;
+  int64_t NP, nTP, BH, W;
+  int64_t gt, qpos, kc, tg, srcq, gmask, cnt, rp, pairs, nent, qp, kp, vp, vt, op, lp, col, total, cap;
 };
 
 bsa_status plan_cluster_attn(const bsa_shape* s, int32_t Nq, int32_t Nk, int32_t o_dtype,
                              ClusterAttnPlan* pl) {
   BSA_TRY(check_shape(s));
   if (Nq < 1 || Nk < 1) return fail(BSA_ERR_INVALID_ARG, "Nq=%d, Nk=%d must be >= 1", Nq, Nk);
+  if (Nq > bsa::kMaxClusters || Nk > bsa::kMaxClusters)
+    return fail(BSA_ERR_UNSUPPORTED, "Nq=%d, Nk=%d: at most %d clusters per head", Nq, Nk,
+                bsa::kMaxClusters);
   if (o_dtype != BSA_F32 && o_dtype != BSA_BF16)
     return fail(BSA_ERR_INVALID_ARG, "o_dtype=%d (BSA_F32 or BSA_BF16)", o_dtype);
   ClusterAttnPlan p{};
   p.BH = (int64_t)s->B * s->H;
   if (p.BH > 65535) return fail(BSA_ERR_UNSUPPORTED, "B*H exceeds 65535");
-  p.nTP = cdiv(s->N, 64) + std::max(Nq, Nk);
+  const int64_t q_tiles = cdiv(s->N, 64) + Nq;
+  const int64_t k_chunks = cdiv(s->N, 16) + Nk + 1;
+  p.nTP = std::max(q_tiles, cdiv(k_chunks, 4));
   p.NP = 64 * p.nTP;
-  p.cap = p.BH * p.nTP * p.nTP;  // every tile of every key cluster in every row
+  p.W = cdiv(Nk, 32);
+  // every label's row can hold every chunk, rounded up to a whole tile
+  p.cap = p.BH * Nq * (k_chunks + 3);
   if (p.cap >= INT32_MAX || p.BH * p.NP * s->d >= ((int64_t)1 << 40))
-    return fail(BSA_ERR_UNSUPPORTED, "cluster layout too large (%lld tiles per head)",
-                (long long)p.nTP);
+    return fail(BSA_ERR_UNSUPPORTED, "cluster layout too large (%lld chunk entries)",
+                (long long)p.cap);
   const int64_t d = s->d, osz = o_dtype == BSA_BF16 ? 2 : 4;
   int64_t at = 0;
   auto take = [&](int64_t bytes) {
@@ -164,20 +174,65 @@ bsa_status plan_cluster_attn(const bsa_shape* s, int32_t Nq, int32_t Nk, int32_t
     at += align256(bytes);
     return here;
   };
-  p.tq = take(p.BH * (Nq + 1) * 4);
-  p.tk = take(p.BH * (Nk + 1) * 4);
+  p.gt = take(p.BH * (Nq + 1) * 4);
+  p.qpos = take(p.BH * Nq * 4);
+  p.kc = take(p.BH * (Nk + 1) * 4);
+  p.tg = take(p.BH * p.nTP * 4);
+  p.srcq = take(p.BH * p.NP * 4);
+  p.gmask = take(p.BH * Nq * p.W * 4);
+  p.cnt = take(p.BH * Nq * 4);
+  p.rp = take((p.BH * Nq + 1) * 4);
+  p.pairs = take(8);
+  p.nent = take(8);
   p.qp = take(p.BH * p.NP * d * 2);
   p.kp = take(p.BH * p.NP * d * 2);
   p.vp = take(p.BH * p.NP * d * 2);
   p.vt = take(p.BH * p.NP * d * 2);
   p.op = take(p.BH * p.NP * d * osz);
   p.lp = take(p.BH * p.NP * 4);
-  p.kv = take(p.BH * p.nTP * 4);
-  p.qc = take(p.BH * p.nTP * 4);
-  p.cnt = take(p.BH * p.nTP * 4);
-  p.rp = take((p.BH * p.nTP + 1) * 4);
-  p.nnz = take(8);
   p.col = take(p.cap * 4);
+  p.total = at;
+  *pl = p;
+  return BSA_OK;
+}
+
+// Workspace of bsa_cluster_merge.
+struct ClusterMergePlan {
+  int64_t BH, W, nbits;
+  int64_t gsq, gk, alist, blist, nab, choice, gain, ukeys, gmask, planes, total;
+};
+
+bsa_status plan_cluster_merge(int32_t B, int32_t H, int32_t N, int32_t Nq, int32_t Nk,
+                              int32_t grain, ClusterMergePlan* pl) {
+  if (B < 1 || H < 1 || N < 1 || Nq < 1 || Nk < 1)
+    return fail(BSA_ERR_INVALID_ARG, "B=%d H=%d N=%d Nq=%d Nk=%d must be >= 1", B, H, N, Nq, Nk);
+  if (Nq > bsa::kMaxClusters || Nk > bsa::kMaxClusters)
+    return fail(BSA_ERR_UNSUPPORTED, "Nq=%d, Nk=%d: at most %d clusters per head", Nq, Nk,
+                bsa::kMaxClusters);
+  if (grain < 1) return fail(BSA_ERR_INVALID_ARG, "grain=%d must be >= 1", grain);
+  ClusterMergePlan p{};
+  p.BH = (int64_t)B * H;
+  if (p.BH > 65535) return fail(BSA_ERR_UNSUPPORTED, "B*H exceeds 65535");
+  p.W = cdiv(Nk, 32);
+  const int64_t cmax = cdiv(N, grain);  // largest slot count of a key cluster
+  p.nbits = 1;
+  while ((int64_t(1) << p.nbits) <= cmax) ++p.nbits;
+  int64_t at = 0;
+  auto take = [&](int64_t bytes) {
+    const int64_t here = at;
+    at += align256(bytes);
+    return here;
+  };
+  p.gsq = take(p.BH * Nq * 4);
+  p.gk = take(p.BH * Nq * 4);
+  p.alist = take(p.BH * Nq * 4);
+  p.blist = take(p.BH * Nq * 4);
+  p.nab = take(p.BH * 2 * 4);
+  p.choice = take(p.BH * Nq * 4);
+  p.gain = take(p.BH * Nq * 8);
+  p.ukeys = take(p.BH * Nq * 4);
+  p.gmask = take(p.BH * Nq * p.W * 4);
+  p.planes = take(p.BH * p.nbits * p.W * 4);
   p.total = at;
   *pl = p;
   return BSA_OK;
@@ -964,9 +1019,10 @@ bsa_status bsa_cluster_attn_fwd(const uint16_t* Q, const uint16_t* K, const uint
                                 const bsa_shape* shape, float scale, int32_t Nq, int32_t Nk,
                                 const int32_t* perm_q, const int32_t* off_q,
                                 const int32_t* perm_k, const int32_t* off_k,
-                                const int32_t* crow_ptr, const int32_t* ccol, void* O,
-                                int32_t o_dtype, float* LSE, int64_t* out_tile_pairs,
-                                void* workspace, int64_t workspace_bytes, void* stream) {
+                                const int32_t* crow_ptr, const int32_t* ccol,
+                                const int32_t* group_of, void* O, int32_t o_dtype, float* LSE,
+                                int64_t* out_tile_pairs, void* workspace, int64_t workspace_bytes,
+                                void* stream) {
   ClusterAttnPlan pl;
   BSA_TRY(plan_cluster_attn(shape, Nq, Nk, o_dtype, &pl));
   BSA_TRY(check_ptr(Q, "Q"));
@@ -980,6 +1036,8 @@ bsa_status bsa_cluster_attn_fwd(const uint16_t* Q, const uint16_t* K, const uint
   BSA_TRY(check_ptr(off_k, "off_k", 4));
   BSA_TRY(check_ptr(crow_ptr, "crow_ptr", 4));
   if (ccol == nullptr) return fail(BSA_ERR_INVALID_ARG, "ccol is NULL");
+  if (group_of != nullptr) BSA_TRY(check_ptr(group_of, "group_of", 4));
+  if (out_tile_pairs != nullptr) BSA_TRY(check_ptr(out_tile_pairs, "out_tile_pairs", 8));
   BSA_TRY(check_ptr(workspace, "workspace", 256));
   if (workspace_bytes < pl.total)
     return fail(BSA_ERR_CAPACITY, "workspace %lld bytes < required %lld",
@@ -1001,32 +1059,38 @@ bsa_status bsa_cluster_attn_fwd(const uint16_t* Q, const uint16_t* K, const uint
   c.Nk = Nk;
   c.NP = (int)pl.NP;
   c.nTP = (int)pl.nTP;
+  c.W = (int)pl.W;
   c.perm_q = perm_q;
   c.off_q = off_q;
   c.perm_k = perm_k;
   c.off_k = off_k;
   c.crow_ptr = crow_ptr;
   c.ccol = ccol;
-  c.tq = (int32_t*)(ws + pl.tq);
-  c.tk = (int32_t*)(ws + pl.tk);
-  c.Qp = (uint16_t*)(ws + pl.qp);
-  c.Kp = (uint16_t*)(ws + pl.kp);
-  c.Vp = (uint16_t*)(ws + pl.vp);
-  c.key_valid = (int32_t*)(ws + pl.kv);
-  c.qtile_cluster = (int32_t*)(ws + pl.qc);
+  c.group_of = group_of;
+  c.gtile = (int32_t*)(ws + pl.gt);
+  c.qpos = (int32_t*)(ws + pl.qpos);
+  c.kc = (int32_t*)(ws + pl.kc);
+  c.tile_group = (int32_t*)(ws + pl.tg);
+  c.srcq = (int32_t*)(ws + pl.srcq);
+  c.gmask = (uint32_t*)(ws + pl.gmask);
   c.counts = (int32_t*)(ws + pl.cnt);
   c.row_ptr = (int32_t*)(ws + pl.rp);
   c.col_idx = (int32_t*)(ws + pl.col);
   c.cap = pl.cap;
+  c.pairs = (unsigned long long*)(out_tile_pairs != nullptr ? (void*)out_tile_pairs
+                                                            : (void*)(ws + pl.pairs));
+  c.Qp = (uint16_t*)(ws + pl.qp);
+  c.Kp = (uint16_t*)(ws + pl.kp);
+  c.Vp = (uint16_t*)(ws + pl.vp);
   c.Op = ws + pl.op;
   c.Lp = (const float*)(ws + pl.lp);
   c.O = O;
   c.LSE = LSE;
-  int64_t* nnz = out_tile_pairs != nullptr ? out_tile_pairs : (int64_t*)(ws + pl.nnz);
+  int64_t* entries = (int64_t*)(ws + pl.nent);  // total chunk entries (unused)
   BSA_TRY(hip_status(bsa::launch_cluster_attn_plan(c, BH, D, st), "cluster plan launch"));
-  BSA_TRY(hip_status(bsa::launch_scan(c.counts, (int)(pl.BH * pl.nTP), c.row_ptr, nnz, st),
+  BSA_TRY(hip_status(bsa::launch_scan(c.counts, (int)(pl.BH * Nq), c.row_ptr, entries, st),
                      "scan launch"));
-  BSA_TRY(hip_status(bsa::launch_cluster_attn_emit(c, BH, st), "cluster emit launch"));
+  BSA_TRY(hip_status(bsa::launch_cluster_attn_emit(c, BH, D, st), "cluster emit launch"));
   // padded tensors: [BH, NP, D], contiguous
   const int64_t sn = D, sh = pl.NP * D, sb = shape->H * sh;
   bsa::TransposeArgs t{};
@@ -1060,10 +1124,68 @@ bsa_status bsa_cluster_attn_fwd(const uint16_t* Q, const uint16_t* K, const uint
   a.scale_log2 = scale * 1.4426950408889634f;
   a.rows = (int)(pl.BH * pl.nTP);
   a.per_xcd = (int)cdiv(a.rows, 8);
-  a.key_valid = c.key_valid;
-  BSA_TRY(hip_status(bsa::launch_attn_keymask(a, D, o_dtype == BSA_BF16, st), "attn launch"));
+  a.tile_group = c.tile_group;
+  a.ngroups = Nq;
+  BSA_TRY(hip_status(bsa::launch_attn_chunks(a, D, o_dtype == BSA_BF16, st), "attn launch"));
   return hip_status(bsa::launch_cluster_attn_scatter(c, BH, D, o_dtype == BSA_BF16, st),
                     "cluster scatter launch");
+}
+
+int64_t bsa_cluster_merge_workspace_bytes(int32_t B, int32_t H, int32_t N, int32_t Nq, int32_t Nk,
+                                          int32_t grain) {
+  ClusterMergePlan pl;
+  if (plan_cluster_merge(B, H, N, Nq, Nk, grain, &pl) != BSA_OK) return -1;
+  return pl.total;
+}
+
+bsa_status bsa_cluster_merge(const int32_t* off_q, const int32_t* off_k, const int32_t* crow_ptr,
+                             const int32_t* ccol, int32_t B, int32_t H, int32_t N, int32_t Nq,
+                             int32_t Nk, const uint8_t* sides, int32_t rounds, int32_t tau_q,
+                             int32_t tau_k, int32_t grain, int32_t* group_of, void* workspace,
+                             int64_t workspace_bytes, void* stream) {
+  ClusterMergePlan pl;
+  BSA_TRY(plan_cluster_merge(B, H, N, Nq, Nk, grain, &pl));
+  if (rounds < 0 || rounds > 64) return fail(BSA_ERR_INVALID_ARG, "rounds=%d (0..64)", rounds);
+  if (tau_q < 1 || tau_k < 1)
+    return fail(BSA_ERR_INVALID_ARG, "tau_q=%d, tau_k=%d must be >= 1", tau_q, tau_k);
+  BSA_TRY(check_ptr(off_q, "off_q", 4));
+  BSA_TRY(check_ptr(off_k, "off_k", 4));
+  BSA_TRY(check_ptr(crow_ptr, "crow_ptr", 4));
+  if (ccol == nullptr) return fail(BSA_ERR_INVALID_ARG, "ccol is NULL");
+  if (rounds > 0 && sides == nullptr) return fail(BSA_ERR_INVALID_ARG, "sides is NULL");
+  BSA_TRY(check_ptr(group_of, "group_of", 4));
+  BSA_TRY(check_ptr(workspace, "workspace", 256));
+  if (workspace_bytes < pl.total)
+    return fail(BSA_ERR_CAPACITY, "workspace %lld bytes < required %lld",
+                (long long)workspace_bytes, (long long)pl.total);
+  char* ws = (char*)workspace;
+  bsa::ClusterMergeArgs m{};
+  m.Nq = Nq;
+  m.Nk = Nk;
+  m.W = (int)pl.W;
+  m.nbits = (int)pl.nbits;
+  m.rounds = rounds;
+  m.tau_q = tau_q;
+  m.tau_k = tau_k;
+  m.grain = grain;
+  m.off_q = off_q;
+  m.off_k = off_k;
+  m.crow_ptr = crow_ptr;
+  m.ccol = ccol;
+  m.sides = sides;
+  m.grp = group_of;
+  m.gsq = (int32_t*)(ws + pl.gsq);
+  m.gk = (int32_t*)(ws + pl.gk);
+  m.alist = (int32_t*)(ws + pl.alist);
+  m.blist = (int32_t*)(ws + pl.blist);
+  m.nab = (int32_t*)(ws + pl.nab);
+  m.choice = (int32_t*)(ws + pl.choice);
+  m.gain = (int64_t*)(ws + pl.gain);
+  m.ukeys = (int32_t*)(ws + pl.ukeys);
+  m.gmask = (uint32_t*)(ws + pl.gmask);
+  m.planes = (uint32_t*)(ws + pl.planes);
+  return hip_status(bsa::launch_cluster_merge(m, (int)pl.BH, (hipStream_t)stream),
+                    "cluster merge launch");
 }
 
 }  // extern "C"

@@ -99,6 +99,10 @@ __device__ __forceinline__ uint32_t lds_addr(const uint16_t* p) {
   return (uint32_t)(uintptr_t)(const lds_u16*)p;
 }
 
+// Read-only index arrays in the constant address space: uniform loads of
+// them become scalar loads.
+typedef __attribute__((address_space(4))) const int32_t const_i32;
+
 // Compile-time loop: f(std::integral_constant<int, U>) for U in [B, E).
 template <int B, int E, typename F>
 __device__ __forceinline__ void static_for(F&& f) {
@@ -193,6 +197,28 @@ struct TileCopy {
       dma16<u * 2048>(vbase, base, voff[u]);
     });
   }
+
+  // Tiles gathered from four 16-key chunks (entries: chunk index in the low
+  // 24 bits).  Instruction u of either wave covers rows of chunk 64 u / D
+  // only, so its base moves to that chunk and the per-lane offsets stay the
+  // ones of a contiguous tile.
+  __device__ __forceinline__ void k_chunks(const uint16_t* Kh, int64_t sn, const_i32* ent) const {
+    static_for<0, NK>([&](auto uc) {
+      constexpr int u = decltype(uc)::value;
+      constexpr int cc = 64 * u / D;
+      const int64_t ch = ent[cc] & kChunkMask;
+      dma16<u * 2048>(kbase, Kh + (ch - cc) * 16 * sn, koff[u]);
+    });
+  }
+
+  __device__ __forceinline__ void v_chunks(const uint16_t* Vth, const_i32* ent) const {
+    static_for<0, NVI>([&](auto uc) {
+      constexpr int u = decltype(uc)::value;
+      constexpr int cc = 64 * u / D;
+      const int64_t ch = ent[cc] & kChunkMask;
+      dma16<u * 2048>(vbase, Vth + (ch - cc) * 16 * D, voff[u]);
+    });
+  }
 };
 
 // max(a, b, c) in one instruction.  (fmaxf on matrix-core results compiles
@@ -233,8 +259,6 @@ __device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xC07F
 // accesses across it.
 __device__ __forceinline__ void exec_barrier() { asm volatile("s_barrier" ::: "memory"); }
 
-typedef __attribute__((address_space(4))) const int32_t const_i32;
-
 // The sparse kernel interleaves its rows across the XCDs when they average
 // more key-tile bytes than twice the 4 MB L2 of one XCD and their runs of
 // consecutive blocks average fewer than kShortRun blocks.
@@ -249,11 +273,13 @@ constexpr int kShortRun = 8;
 // the iteration without a second buffer.  32 KB of LDS and at most 256
 // registers per lane leave room for four workgroups (two waves per SIMD)
 // per compute unit.
-// KEYMASK: every key tile j has its own count of valid keys (a.key_valid,
-// [B*H, nB]); keys at or beyond it are masked.  Used for tensors laid out
-// with padded segments (cluster-induced blocks); the tensors hold whole
-// tiles, so no load is clamped.
-template <int D, bool DENSE, bool OUT_BF16, bool KEYMASK = false>
+// CHUNK: rows are query tiles of groups; query tile L belongs to group
+// a.tile_group[L] (-1: no work) whose entries row_ptr[bh * ngroups + g] ..
+// are 16-key chunk codes (chunk | valid keys << 24), four per key tile; the
+// keys of a chunk past its valid count are masked.  Used for packed
+// cluster-induced blocks, whose tensors hold whole chunks, so no load is
+// clamped.
+template <int D, bool DENSE, bool OUT_BF16, bool CHUNK = false>
 __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2)))
 void attn_fwd_kernel(AttnArgs a) {
   constexpr int DC = D / 8;      // 16-byte chunks per K row
@@ -275,8 +301,8 @@ void attn_fwd_kernel(AttnArgs a) {
   // head, the same for every workgroup), so it needs no host round trip.
   const int w = blockIdx.x;
   const int xcd = w & 7, slot = w >> 3;
-  bool interleave = false;
-  if constexpr (!DENSE) {
+  bool interleave = CHUNK;  // long rows of scattered short runs
+  if constexpr (!DENSE && !CHUNK) {
     const_i32* rp = (const_i32*)a.row_ptr;
     const int64_t total = rp[a.rows];
     if (total * (kBlock * D * 2 * 2) > (int64_t)a.rows * kWideRowBytes) {
@@ -321,6 +347,10 @@ void attn_fwd_kernel(AttnArgs a) {
   if constexpr (DENSE) {
     e0 = 0;
     e1 = a.nB;
+  } else if constexpr (CHUNK) {
+    const int gi = a.tile_group[L];
+    e0 = gi < 0 ? 0 : row_ptr[(int64_t)bh * a.ngroups + gi];
+    e1 = gi < 0 ? 0 : row_ptr[(int64_t)bh * a.ngroups + gi + 1];
   } else {
     e0 = row_ptr[L];
     e1 = row_ptr[L + 1];
@@ -406,18 +436,22 @@ void attn_fwd_kernel(AttnArgs a) {
   f16x8 pf_prev[4];
 #pragma unroll
   for (int cc = 0; cc < 4; ++cc) pf_prev[cc] = f16x8{};
+  // j: the key block (CHUNK: the position of its first chunk entry)
+  constexpr int STEP = CHUNK ? 4 : 1;
   int j = 0, jprev = 0;
   if (e0 < e1) {
-    j = DENSE ? e0 : col_idx[e0];
+    j = (DENSE || CHUNK) ? e0 : col_idx[e0];
     jprev = j;
-    cp.k_tile(Kh, a.sn, j, a.nB);
+    if constexpr (CHUNK) cp.k_chunks(Kh, a.sn, col_idx + j);
+    else cp.k_tile(Kh, a.sn, j, a.nB);
   }
-  for (int e = e0; e < e1; ++e) {
-    const int jn = (e + 1 < e1) ? (DENSE ? e + 1 : col_idx[e + 1]) : j;
+  for (int e = e0; e < e1; e += STEP) {
+    const int jn = (e + STEP < e1) ? ((DENSE || CHUNK) ? e + STEP : col_idx[e + 1]) : j;
     wait_lgkm0();      // this wave's reads of sV (block e-2) have returned
     wait_vmcnt<0>();   // this wave's copy of K(e) has landed
     exec_barrier();    // ... and the other wave's; sV is free
-    cp.v_tile(Vth, jprev);
+    if constexpr (CHUNK) cp.v_chunks(Vth, col_idx + jprev);
+    else cp.v_tile(Vth, jprev);
 
     // S^T for keys 0..31 (s0) and 32..63 (s1) of the block.
     f32x16 s0, s1;
@@ -446,14 +480,34 @@ void attn_fwd_kernel(AttnArgs a) {
     wait_lgkm0();      // this wave's reads of sK have returned
     wait_vmcnt<0>();   // V(e-1) has landed
     exec_barrier();    // both waves are done with sK; sV holds V(e-1)
-    if (e + 1 < e1) cp.k_tile(Kh, a.sn, jn, a.nB);
+    if (e + STEP < e1) {
+      if constexpr (CHUNK) cp.k_chunks(Kh, a.sn, col_idx + jn);
+      else cp.k_tile(Kh, a.sn, jn, a.nB);
+    }
 
     f16x8 va0[4];  // V^T fragments of block e-1's first d tile, read early
     v_frags(0, va0);
     // Lane holds keys 8*(r/4) + 4*g + r%4 (+32 for s1) of query q.
-    if (KEYMASK || j == a.nB - 1) {
-      const int nvalid = KEYMASK ? ((const_i32*)a.key_valid)[(int64_t)bh * a.nB + j]
-                                 : a.N - j * kBlock;
+    if constexpr (CHUNK) {
+      // key 8*(r/4) + 4*g + r%4 of s0 lies in chunk r/8 at offset
+      // 8*((r/4)%2) + 4*g + r%4; s1 is chunks 2 and 3
+      int vc[4];
+      bool partial = false;
+#pragma unroll
+      for (int cc = 0; cc < 4; ++cc) {
+        vc[cc] = (int)((uint32_t)col_idx[j + cc] >> kChunkShift);
+        partial |= vc[cc] < 16;
+      }
+      if (partial) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int off = 8 * ((r >> 2) & 1) + 4 * g + (r & 3);
+          if (off >= vc[r >> 3]) s0[r] = -INFINITY;
+          if (off >= vc[2 + (r >> 3)]) s1[r] = -INFINITY;
+        }
+      }
+    } else if (j == a.nB - 1) {
+      const int nvalid = a.N - j * kBlock;
       if (nvalid < kBlock) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
@@ -509,7 +563,8 @@ void attn_fwd_kernel(AttnArgs a) {
   if (e0 < e1) {
     wait_lgkm0();
     exec_barrier();    // every wave is done with sV
-    cp.v_tile(Vth, jprev);
+    if constexpr (CHUNK) cp.v_chunks(Vth, col_idx + jprev);
+    else cp.v_tile(Vth, jprev);
     wait_vmcnt<0>();
     exec_barrier();
     f16x8 va0[4];
@@ -781,7 +836,7 @@ static void launch_attn_t(const AttnArgs& a, bool out_bf16, hipStream_t s) {
     hipLaunchKernelGGL((attn_fwd_kernel<D, DENSE, false>), grid, dim3(128), 0, s, a);
 }
 
-hipError_t launch_attn_keymask(const AttnArgs& a, int D, bool out_bf16, hipStream_t s) {
+hipError_t launch_attn_chunks(const AttnArgs& a, int D, bool out_bf16, hipStream_t s) {
   const dim3 grid(64 * ((a.rows + 63) / 64));
   if (D == 128) {
     if (out_bf16) hipLaunchKernelGGL((attn_fwd_kernel<128, false, true, true>), grid, dim3(128), 0, s, a);

@@ -78,8 +78,15 @@ struct AttnArgs {
   float scale_log2;  // softmax scale * log2(e)
   int rows;          // B*H*nB
   int per_xcd;       // ceil(rows / 8)
-  const int32_t* key_valid;  // [B*H, nB] valid keys per tile (masked kernel only)
+  // chunk kernel only: group of every query tile (-1: none), groups per head
+  const int32_t* tile_group;
+  int ngroups;
 };
+
+// 16-key chunk codes of packed cluster-induced blocks: chunk index in the low
+// 24 bits, its valid keys (0..16) above.
+constexpr int kChunkShift = 24;
+constexpr int32_t kChunkMask = (1 << kChunkShift) - 1;
 
 struct MicroAttnArgs {
   const uint16_t* Q;
@@ -158,29 +165,60 @@ struct ClusterAttnArgs {
   const uint16_t* V;
   int64_t sb, sh, sn;      // strides of Q, K, V, O
   int H, N, Nq, Nk;
-  int NP, nTP;             // padded length per head and its tiles (NP / 64)
+  int NP, nTP;             // padded length per head and its query tiles (NP / 64)
+  int W;                   // 32-bit words of a key-cluster mask
   const int32_t* perm_q;   // [BH, N]
   const int32_t* off_q;    // [BH, Nq + 1]
   const int32_t* perm_k;
   const int32_t* off_k;    // [BH, Nk + 1]
   const int32_t* crow_ptr; // cluster lists [BH * Nq + 1]
   const int32_t* ccol;
-  int32_t* tq;             // [BH, Nq + 1] tile offsets of the query clusters
-  int32_t* tk;             // [BH, Nk + 1]
-  uint16_t* Qp;            // [BH, NP, D] padded cluster order
+  const int32_t* group_of; // [BH, Nq] lowest member of each cluster's group, or NULL
+  int32_t* gtile;          // [BH, Nq + 1] first query tile of each group (at its lowest member)
+  int32_t* qpos;           // [BH, Nq] padded position of each query cluster's first token
+  int32_t* kc;             // [BH, Nk + 1] first 16-key chunk of each key cluster
+  int32_t* tile_group;     // [BH, nTP]
+  int32_t* srcq;           // [BH, NP] token at each padded query position, -1 in padding
+  uint32_t* gmask;         // [BH, Nq, W] key clusters of each group
+  int32_t* counts;         // [BH * Nq] chunk entries of each group (multiple of 4)
+  int32_t* row_ptr;        // [BH * Nq + 1]
+  int32_t* col_idx;        // chunk codes
+  int64_t cap;
+  unsigned long long* pairs;  // executed (query tile, key tile) pairs
+  uint16_t* Qp;            // [BH, NP, D] queries by group, keys by chunk
   uint16_t* Kp;
   uint16_t* Vp;
-  int32_t* key_valid;      // [BH, nTP]
-  int32_t* qtile_cluster;  // [BH, nTP]
-  int32_t* counts;         // [BH, nTP]
-  int32_t* row_ptr;        // [BH * nTP + 1] tile lists
-  int32_t* col_idx;
-  int64_t cap;
   const void* Op;          // [BH, NP, D] attention output in padded order
   const float* Lp;         // [BH, NP]
   void* O;
   float* LSE;
 };
+
+// HVA parallel agglomerative merging of query clusters.
+struct ClusterMergeArgs {
+  int Nq, Nk, W, nbits;    // W mask words, nbits bit planes of the key slot counts
+  int rounds, round;
+  int tau_q, tau_k, grain;
+  const int32_t* off_q;    // [BH, Nq + 1]
+  const int32_t* off_k;    // [BH, Nk + 1]
+  const int32_t* crow_ptr; // [BH * Nq + 1]
+  const int32_t* ccol;
+  const uint8_t* sides;    // [BH, rounds, Nq]
+  int32_t* grp;            // [BH, Nq] lowest member of each cluster's group (the output)
+  int32_t* gsq;            // [BH, Nq] query tokens of each group (at its lowest member)
+  int32_t* gk;             // [BH, Nq] key slots of each group
+  uint32_t* gmask;         // [BH, Nq, W]
+  uint32_t* planes;        // [BH, nbits, W] bit b of every key cluster's slot count
+  int32_t* alist;          // [BH, Nq] choosing groups of this round, then their count
+  int32_t* blist;          // [BH, Nq] target groups
+  int32_t* nab;            // [BH, 2]
+  int32_t* choice;         // [BH, Nq] best target of each chooser (-1 none)
+  int64_t* gain;           // [BH, Nq]
+  int32_t* ukeys;          // [BH, Nq] key slots of chooser + best target
+};
+// Most query or key clusters per head of the cluster attention plan and the
+// merging (per-head tables held in LDS; key masks of at most 128 words).
+constexpr int kMaxClusters = 4096;
 
 // Pooled rectification of omitted blocks.
 constexpr int kMaxRowWords = 128;  // bitmap words of a row of up to 4096 blocks
@@ -221,7 +259,7 @@ hipError_t launch_transpose_v(const TransposeArgs& a, int B, int D,
                               hipStream_t s);
 hipError_t launch_attn(const AttnArgs& a, int D, bool dense, bool out_bf16,
                        hipStream_t s);
-hipError_t launch_attn_keymask(const AttnArgs& a, int D, bool out_bf16, hipStream_t s);
+hipError_t launch_attn_chunks(const AttnArgs& a, int D, bool out_bf16, hipStream_t s);
 hipError_t launch_micro_attn(const MicroAttnArgs& a, int B, int D,
                              bool out_bf16, hipStream_t s);
 hipError_t launch_merge(const MergeArgs& a, int B, bool bf16, hipStream_t s);
@@ -230,7 +268,8 @@ hipError_t launch_cluster(const ClusterArgs& a, int BH, int iters, hipStream_t s
 hipError_t launch_cluster_permute(const ClusterArgs& a, int BH, const int32_t* gofs,
                                   int32_t* perm, int32_t* offsets, hipStream_t s);
 hipError_t launch_cluster_attn_plan(const ClusterAttnArgs& a, int BH, int D, hipStream_t s);
-hipError_t launch_cluster_attn_emit(const ClusterAttnArgs& a, int BH, hipStream_t s);
+hipError_t launch_cluster_attn_emit(const ClusterAttnArgs& a, int BH, int D, hipStream_t s);
+hipError_t launch_cluster_merge(const ClusterMergeArgs& a, int BH, hipStream_t s);
 hipError_t launch_cluster_attn_scatter(const ClusterAttnArgs& a, int BH, int D, bool out_bf16,
                                        hipStream_t s);
 hipError_t launch_rectify(const RectifyArgs& a, int BH, int D, bool out_bf16, hipStream_t s);

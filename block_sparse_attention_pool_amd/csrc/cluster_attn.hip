@@ -1,20 +1,24 @@
-// Attention over cluster-induced blocks (HyperVAttention section 2, Eq. 4):
-// every query of query cluster i attends over the tokens of the key clusters
-// its row selects; the output goes back to the original token order.
+// Attention over cluster-induced blocks (HyperVAttention section 2, Eq. 4),
+// executed as the page's hardware cost model describes it (section 4.3,
+// Eq. 7-8): every query of query cluster i attends over the tokens of the
+// key clusters its row selects; query clusters may be merged into groups
+// that share the union of their rows (Algorithm 1); the output goes back to
+// the original token order.
 //
-// Executed on the 64-token tile engine with every cluster padded to whole
-// tiles (the CTA-aligned cost of the page's Eq. 7 with a tile of 64 on both
-// sides): in the padded cluster order a query tile belongs to one query
-// cluster and a key tile to one key cluster, so the tile lists are exact --
-// query tile T of cluster i lists every tile of every key cluster in row i --
-// and the attention kernel masks each key tile's padding keys (its count of
-// valid keys per tile).  Queries and keys share one padded length NP per
-// head, 64 * (ceil(N / 64) + max(Nq, Nk)), which bounds both layouts.
+// Layout.  Queries: the groups one after another, ordered by their lowest
+// member, each group's clusters in ascending order and each padded to whole
+// 64-query tiles (the tau_q ceil(s^q / tau_q) of Eq. 8).  Keys: the key
+// clusters in order, each padded to whole 16-key chunks; a group's key tiles
+// are its selected clusters' chunks packed four to a 64-key tile (the
+// tau_k ceil(sum s^k / tau_k) of Eq. 8 at a 16-token grain), the last tile
+// completed with an all-padding chunk.  The attention kernel gathers every
+// key tile from its four chunks and masks each chunk's padding keys, so the
+// result is exactly Eq. 4.
 //
-// Kernels: per-head tile offsets of the clusters (a scan of ceil(size/64));
-// padded gathers of Q, K, V in cluster order; valid keys per key tile; the
-// tile lists (per-row counts, the row-pointer scan, emission); the masked
-// attention; the scatter of O and LSE back to token order.
+// Kernels: the per-head plan (group sizes and tiles, query positions, key
+// chunk offsets), the padded query source map, the group key masks, the
+// per-group chunk counts and lists, the padded gathers of Q, K, V, the
+// masked attention, the scatter of O and LSE back to token order.
 #include "bsa_device.h"
 #include "bsa_internal.h"
 
@@ -22,23 +26,19 @@ namespace bsa {
 
 namespace {
 
-// Exclusive scan of ceil(size_c / 64) over the clusters of one head (sizes
-// from the cluster offsets), one workgroup of 1024 per (head, tensor).
-__global__ __launch_bounds__(1024) void ctile_offsets_kernel(ClusterAttnArgs a) {
-  __shared__ int part[1024];
-  const int64_t bh = blockIdx.x;
-  const bool keys = blockIdx.y == 1;
-  const int n = keys ? a.Nk : a.Nq;
-  const int32_t* off = (keys ? a.off_k : a.off_q) + bh * (n + 1);
-  int32_t* tiles = (keys ? a.tk : a.tq) + bh * (n + 1);
+// Exclusive scan over n values val(c) by a workgroup of 1024: out[0..n],
+// out[n] the total; also written to lds_out when given.  Each thread scans a
+// contiguous segment and reads only its own values.
+template <typename F>
+__device__ void block_exscan(int n, F val, int32_t* out, int* lds_out, int* part) {
   const int tid = threadIdx.x;
   const int per = (n + 1023) / 1024;
-  const int c0 = tid * per, c1 = min(c0 + per, n);
+  const int c0 = min(tid * per, n), c1 = min(c0 + per, n);
   int s = 0;
-  for (int c = c0; c < c1; ++c) s += (off[c + 1] - off[c] + 63) / 64;
+  for (int c = c0; c < c1; ++c) s += val(c);
   part[tid] = s;
   __syncthreads();
-  for (int d = 1; d < 1024; d <<= 1) {  // inclusive scan of the partial sums
+  for (int d = 1; d < 1024; d <<= 1) {
     const int v = tid >= d ? part[tid - d] : 0;
     __syncthreads();
     part[tid] += v;
@@ -46,13 +46,28 @@ __global__ __launch_bounds__(1024) void ctile_offsets_kernel(ClusterAttnArgs a) 
   }
   int run = part[tid] - s;
   for (int c = c0; c < c1; ++c) {
-    tiles[c] = run;
-    run += (off[c + 1] - off[c] + 63) / 64;
+    const int v = val(c);
+    out[c] = run;
+    if (lds_out != nullptr) lds_out[c] = run;
+    run += v;
   }
-  if (tid == 1023) tiles[n] = part[1023];
+  if (tid == 1023) {
+    out[n] = part[1023];
+    if (lds_out != nullptr) lds_out[n] = part[1023];
+  }
+  __syncthreads();
 }
 
-// Largest c in [0, n) with t[c] <= x (t ascending, t[0] = 0 <= x).
+// Group label of query cluster i: its group's lowest member, or i itself
+// when no grouping is given (a label outside [0, i] also stands alone).
+__device__ __forceinline__ int group_label(const ClusterAttnArgs& a, int64_t bh, int i) {
+  if (a.group_of == nullptr) return i;
+  const int g = a.group_of[bh * a.Nq + i];
+  return (g >= 0 && g <= i) ? g : i;
+}
+
+// Largest c in [0, n) with t[c] <= x (t ascending, t[0] = 0 <= x).  With
+// repeated values it returns the last of them, the segment that holds x.
 __device__ __forceinline__ int seg_of(const int32_t* t, int n, int x) {
   int lo = 0, hi = n - 1;
   while (lo < hi) {
@@ -63,10 +78,141 @@ __device__ __forceinline__ int seg_of(const int32_t* t, int n, int x) {
   return lo;
 }
 
-// Padded cluster-order copies: position p of tensor (Q, K or V) holds token
-// perm[off[c] + k] where c is the cluster of tile p / 64 and k = p - 64
-// tq[c], or zeros in a cluster's padding and past the last tile.  One
-// thread per 16-byte chunk.
+// One workgroup of 1024 per head: group sizes, the groups' first query tiles
+// (scan of ceil(size / 64) over labels), every query cluster's padded start
+// (its group's start plus the sizes of the lower members), and the key
+// clusters' first chunks (scan of ceil(size / 16)).
+__global__ __launch_bounds__(1024) void cplan_kernel(ClusterAttnArgs a) {
+  __shared__ int sg[kMaxClusters + 1];
+  __shared__ int lab[kMaxClusters];
+  __shared__ int part[1024];
+  const int64_t bh = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int32_t* oq = a.off_q + bh * (a.Nq + 1);
+  const int32_t* ok = a.off_k + bh * (a.Nk + 1);
+  for (int i = tid; i < a.Nq; i += 1024) {
+    sg[i] = 0;
+    lab[i] = group_label(a, bh, i);
+  }
+  __syncthreads();
+  for (int i = tid; i < a.Nq; i += 1024) atomicAdd(&sg[lab[i]], oq[i + 1] - oq[i]);
+  __syncthreads();
+  // sg becomes the groups' first tiles
+  block_exscan(a.Nq, [&](int i) { return (sg[i] + kBlock - 1) / kBlock; },
+               a.gtile + bh * (a.Nq + 1), sg, part);
+  for (int i = tid; i < a.Nq; i += 1024) {
+    const int g = lab[i];
+    int off = 0;
+    for (int m = g; m < i; ++m)
+      if (lab[m] == g) off += oq[m + 1] - oq[m];
+    a.qpos[bh * a.Nq + i] = kBlock * sg[g] + off;
+  }
+  block_exscan(a.Nk, [&](int j) { return (ok[j + 1] - ok[j] + 15) / 16; }, a.kc + bh * (a.Nk + 1),
+               nullptr, part);
+}
+
+// Group of every query tile (-1 past the last tile).
+__global__ __launch_bounds__(256) void ctile_group_kernel(ClusterAttnArgs a) {
+  const int T = blockIdx.x * 256 + threadIdx.x;
+  const int64_t bh = blockIdx.y;
+  if (T >= a.nTP) return;
+  const int32_t* gt = a.gtile + bh * (a.Nq + 1);
+  a.tile_group[bh * a.nTP + T] = T < gt[a.Nq] ? seg_of(gt, a.Nq, T) : -1;
+}
+
+// The token at every padded query position (positions start at -1): query
+// order position n of cluster c goes to qpos[c] + n - off_q[c].
+__global__ __launch_bounds__(256) void cqsrc_kernel(ClusterAttnArgs a) {
+  const int n = blockIdx.x * 256 + threadIdx.x;
+  const int64_t bh = blockIdx.y;
+  if (n >= a.N) return;
+  const int32_t* oq = a.off_q + bh * (a.Nq + 1);
+  const int c = seg_of(oq, a.Nq, n);
+  a.srcq[bh * a.NP + a.qpos[bh * a.Nq + c] + n - oq[c]] = a.perm_q[bh * a.N + n];
+}
+
+// Key clusters of every group: the OR of its members' rows (masks start at
+// zero; integer OR, so the result does not depend on the order).  One wave
+// per query cluster.
+__global__ __launch_bounds__(256) void cgmask_kernel(ClusterAttnArgs a) {
+  const int i = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int64_t bh = blockIdx.y;
+  const int lane = threadIdx.x & 63;
+  if (i >= a.Nq) return;
+  const int g = group_label(a, bh, i);
+  uint32_t* m = a.gmask + (bh * a.Nq + g) * a.W;
+  const int64_t r = bh * a.Nq + i;
+  for (int e = a.crow_ptr[r] + lane; e < a.crow_ptr[r + 1]; e += 64) {
+    const int j = a.ccol[e];
+    if (j >= 0 && j < a.Nk) atomicOr(m + (j >> 5), 1u << (j & 31));
+  }
+}
+
+// Chunk entries of every group with query tiles: its key clusters' chunks,
+// rounded up to whole tiles of four; executed tile pairs added up (integer
+// atomics).  One wave per label.
+__global__ __launch_bounds__(256) void ccount_kernel(ClusterAttnArgs a) {
+  const int i = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int64_t bh = blockIdx.y;
+  const int lane = threadIdx.x & 63;
+  if (i >= a.Nq) return;
+  const int32_t* gt = a.gtile + bh * (a.Nq + 1);
+  const int tiles = gt[i + 1] - gt[i];
+  int chunks = 0;
+  if (tiles > 0) {
+    const uint32_t* m = a.gmask + (bh * a.Nq + i) * a.W;
+    const int32_t* kc = a.kc + bh * (a.Nk + 1);
+    for (int j = lane; j < a.Nk; j += 64)
+      if ((m[j >> 5] >> (j & 31)) & 1u) chunks += kc[j + 1] - kc[j];
+    chunks = wave_sum(chunks);
+  }
+  const int padded = (chunks + 3) & ~3;
+  if (lane == 0) {
+    a.counts[bh * a.Nq + i] = padded;
+    if (padded > 0) atomicAdd(a.pairs, (unsigned long long)tiles * (unsigned long long)(padded / 4));
+  }
+}
+
+// One wave per group: lanes take the key clusters 64 at a time and write the
+// chunks of the selected ones at wave-prefix positions, in ascending order;
+// the row is completed with the all-padding chunk (the last chunk of the
+// padded key layout, valid count 0).
+__global__ __launch_bounds__(256) void cemit_kernel(ClusterAttnArgs a) {
+  const int i = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int64_t bh = blockIdx.y;
+  const int lane = threadIdx.x & 63;
+  if (i >= a.Nq) return;
+  const int64_t r = bh * a.Nq + i;
+  const int64_t end = a.row_ptr[r + 1];
+  int64_t pos = a.row_ptr[r];
+  if (pos == end) return;
+  const uint32_t* m = a.gmask + r * a.W;
+  const int32_t* kc = a.kc + bh * (a.Nk + 1);
+  const int32_t* ok = a.off_k + bh * (a.Nk + 1);
+  for (int jb = 0; jb < a.Nk; jb += 64) {
+    const int j = jb + lane;
+    int nt = 0;
+    if (j < a.Nk && ((m[j >> 5] >> (j & 31)) & 1u)) nt = kc[j + 1] - kc[j];
+    const int incl = wave_inclusive_scan(nt);
+    int64_t at = pos + incl - nt;
+    if (nt > 0) {
+      const int size = ok[j + 1] - ok[j];
+      for (int k = 0; k < nt; ++k, ++at) {
+        const int valid = min(16, size - 16 * k);
+        if (at < a.cap) a.col_idx[at] = (kc[j] + k) | (valid << kChunkShift);
+      }
+    }
+    pos += __shfl(incl, 63);
+  }
+  const int null_chunk = a.NP / 16 - 1;
+  for (int64_t p = pos + lane; p < end; p += 64)
+    if (p < a.cap) a.col_idx[p] = null_chunk;
+}
+
+// Padded copies: query position p holds token srcq[p] (zeros where -1); key
+// position p of chunk p / 16 in key cluster j holds token perm_k[off_k[j] +
+// p - 16 kc[j]] while that is inside the cluster, zeros otherwise.  One
+// thread per 16-byte piece.
 template <int D>
 __global__ __launch_bounds__(256) void cgather_kernel(ClusterAttnArgs a) {
   constexpr int C = D / 8;
@@ -75,105 +221,40 @@ __global__ __launch_bounds__(256) void cgather_kernel(ClusterAttnArgs a) {
   const int which = blockIdx.z;  // 0 Q, 1 K, 2 V
   if (f >= (int64_t)a.NP * C) return;
   const int p = (int)(f / C), c = (int)(f % C);
-  const bool keys = which != 0;
-  const int n = keys ? a.Nk : a.Nq;
-  const int32_t* tl = (keys ? a.tk : a.tq) + bh * (n + 1);
-  const int32_t* off = (keys ? a.off_k : a.off_q) + bh * (n + 1);
-  const int32_t* perm = (keys ? a.perm_k : a.perm_q) + bh * a.N;
+  int64_t tok = -1;
+  if (which == 0) {
+    tok = a.srcq[bh * a.NP + p];
+  } else {
+    const int32_t* kc = a.kc + bh * (a.Nk + 1);
+    const int chunk = p / 16;
+    if (chunk < kc[a.Nk]) {
+      const int j = seg_of(kc, a.Nk, chunk);
+      const int32_t* ok = a.off_k + bh * (a.Nk + 1);
+      const int k = p - 16 * kc[j];
+      if (k < ok[j + 1] - ok[j]) tok = a.perm_k[bh * a.N + ok[j] + k];
+    }
+  }
   const uint16_t* src = which == 0 ? a.Q : which == 1 ? a.K : a.V;
   uint16_t* dst = (which == 0 ? a.Qp : which == 1 ? a.Kp : a.Vp) + (bh * a.NP + p) * D;
   u32x4 v = {0u, 0u, 0u, 0u};
-  const int T = p / kBlock;
-  if (T < tl[n]) {
-    const int cl = seg_of(tl, n, T);
-    const int k = p - kBlock * tl[cl];
-    if (k < off[cl + 1] - off[cl]) {
-      const int64_t tok = perm[off[cl] + k];
-      const int b = (int)(bh / a.H), h = (int)(bh % a.H);
-      v = *(const u32x4*)(src + (int64_t)b * a.sb + (int64_t)h * a.sh + tok * a.sn + 8 * c);
-    }
+  if (tok >= 0) {
+    const int b = (int)(bh / a.H), h = (int)(bh % a.H);
+    v = *(const u32x4*)(src + (int64_t)b * a.sb + (int64_t)h * a.sh + tok * a.sn + 8 * c);
   }
   *(u32x4*)(dst + 8 * c) = v;
 }
 
-// Valid keys of every key tile, and each query tile's cluster (-1 past the
-// last tile).
-__global__ __launch_bounds__(256) void ctile_info_kernel(ClusterAttnArgs a) {
-  const int T = blockIdx.x * 256 + threadIdx.x;
-  const int64_t bh = blockIdx.y;
-  if (T >= a.nTP) return;
-  const int32_t* tk = a.tk + bh * (a.Nk + 1);
-  const int32_t* ok = a.off_k + bh * (a.Nk + 1);
-  int valid = 0;
-  if (T < tk[a.Nk]) {
-    const int cl = seg_of(tk, a.Nk, T);
-    valid = min(kBlock, ok[cl + 1] - ok[cl] - kBlock * (T - tk[cl]));
-  }
-  a.key_valid[bh * a.nTP + T] = valid;
-  const int32_t* tq = a.tq + bh * (a.Nq + 1);
-  a.qtile_cluster[bh * a.nTP + T] = T < tq[a.Nq] ? seg_of(tq, a.Nq, T) : -1;
-}
-
-// Entries of every query tile's row: the tiles of the key clusters its
-// cluster selects.
-__global__ __launch_bounds__(256) void crow_count_kernel(ClusterAttnArgs a) {
-  const int T = blockIdx.x * 256 + threadIdx.x;
-  const int64_t bh = blockIdx.y;
-  if (T >= a.nTP) return;
-  const int cl = a.qtile_cluster[bh * a.nTP + T];
-  int cnt = 0;
-  if (cl >= 0) {
-    const int64_t r = bh * a.Nq + cl;
-    const int32_t* tk = a.tk + bh * (a.Nk + 1);
-    for (int e = a.crow_ptr[r]; e < a.crow_ptr[r + 1]; ++e) {
-      const int j = a.ccol[e];
-      cnt += tk[j + 1] - tk[j];
-    }
-  }
-  a.counts[bh * a.nTP + T] = cnt;
-}
-
-// One wave per query tile: lanes take the selected key clusters 64 at a time
-// and write their tiles at positions given by a wave prefix of tile counts.
-__global__ __launch_bounds__(256) void cemit_kernel(ClusterAttnArgs a) {
-  const int T = blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int64_t bh = blockIdx.y;
-  const int lane = threadIdx.x & 63;
-  if (T >= a.nTP) return;
-  const int cl = a.qtile_cluster[bh * a.nTP + T];
-  if (cl < 0) return;
-  const int64_t r = bh * a.Nq + cl;
-  const int32_t* tk = a.tk + bh * (a.Nk + 1);
-  int64_t pos = a.row_ptr[bh * a.nTP + T];
-  const int e0 = a.crow_ptr[r], e1 = a.crow_ptr[r + 1];
-  for (int eb = e0; eb < e1; eb += 64) {
-    const int e = eb + lane;
-    int j = 0, nt = 0;
-    if (e < e1) {
-      j = a.ccol[e];
-      nt = tk[j + 1] - tk[j];
-    }
-    const int incl = wave_inclusive_scan(nt);
-    int64_t at = pos + incl - nt;
-    for (int k = 0; k < nt; ++k, ++at)
-      if (at < a.cap) a.col_idx[at] = tk[j] + k;
-    pos += __shfl(incl, 63);
-  }
-}
-
-// O and LSE back to token order: position n of the query order is token
-// perm_q[n] of cluster c (off_q[c] <= n), found at padded position
-// 64 tq[c] + n - off_q[c].  One thread per 4 output elements.
+// O and LSE back to token order: padded query position p holding token
+// srcq[p] >= 0.  One thread per 4 output elements.
 template <int D, bool OUT_BF16>
 __global__ __launch_bounds__(256) void cscatter_kernel(ClusterAttnArgs a) {
   const int64_t f = (int64_t)blockIdx.x * 256 + threadIdx.x;
   const int64_t bh = blockIdx.y;
-  if (f >= (int64_t)a.N * (D / 4)) return;
-  const int n = (int)(f / (D / 4)), c = (int)(f % (D / 4));
-  const int32_t* oq = a.off_q + bh * (a.Nq + 1);
-  const int cl = seg_of(oq, a.Nq, n);
-  const int64_t src = bh * a.NP + (int64_t)kBlock * a.tq[bh * (a.Nq + 1) + cl] + (n - oq[cl]);
-  const int64_t tok = a.perm_q[bh * a.N + n];
+  if (f >= (int64_t)a.NP * (D / 4)) return;
+  const int p = (int)(f / (D / 4)), c = (int)(f % (D / 4));
+  const int64_t tok = a.srcq[bh * a.NP + p];
+  if (tok < 0) return;
+  const int64_t src = bh * a.NP + p;
   const int b = (int)(bh / a.H), h = (int)(bh % a.H);
   const int64_t dst = (int64_t)b * a.sb + (int64_t)h * a.sh + tok * a.sn + 4 * c;
   if constexpr (OUT_BF16) {
@@ -187,24 +268,33 @@ __global__ __launch_bounds__(256) void cscatter_kernel(ClusterAttnArgs a) {
 }  // namespace
 
 hipError_t launch_cluster_attn_plan(const ClusterAttnArgs& a, int BH, int D, hipStream_t s) {
-  hipLaunchKernelGGL(ctile_offsets_kernel, dim3(BH, 2), dim3(1024), 0, s, a);
-  const dim3 ggrid((unsigned)(((int64_t)a.NP * (D / 8) + 255) / 256), BH, 3);
-  if (D == 128) hipLaunchKernelGGL(cgather_kernel<128>, ggrid, dim3(256), 0, s, a);
-  else hipLaunchKernelGGL(cgather_kernel<64>, ggrid, dim3(256), 0, s, a);
-  const dim3 tgrid((a.nTP + 255) / 256, BH);
-  hipLaunchKernelGGL(ctile_info_kernel, tgrid, dim3(256), 0, s, a);
-  hipLaunchKernelGGL(crow_count_kernel, tgrid, dim3(256), 0, s, a);
+  (void)D;
+  hipError_t e = launch_fill_i32(a.srcq, (int64_t)BH * a.NP, -1, s);
+  if (e != hipSuccess) return e;
+  e = launch_fill_i32((int32_t*)a.gmask, (int64_t)BH * a.Nq * a.W, 0, s);
+  if (e != hipSuccess) return e;
+  e = launch_fill_i32((int32_t*)a.pairs, 2, 0, s);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(cplan_kernel, dim3(BH), dim3(1024), 0, s, a);
+  hipLaunchKernelGGL(ctile_group_kernel, dim3((a.nTP + 255) / 256, BH), dim3(256), 0, s, a);
+  hipLaunchKernelGGL(cqsrc_kernel, dim3((a.N + 255) / 256, BH), dim3(256), 0, s, a);
+  const dim3 wgrid((a.Nq + 3) / 4, BH);
+  hipLaunchKernelGGL(cgmask_kernel, wgrid, dim3(256), 0, s, a);
+  hipLaunchKernelGGL(ccount_kernel, wgrid, dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
-hipError_t launch_cluster_attn_emit(const ClusterAttnArgs& a, int BH, hipStream_t s) {
-  hipLaunchKernelGGL(cemit_kernel, dim3((a.nTP + 3) / 4, BH), dim3(256), 0, s, a);
+hipError_t launch_cluster_attn_emit(const ClusterAttnArgs& a, int BH, int D, hipStream_t s) {
+  hipLaunchKernelGGL(cemit_kernel, dim3((a.Nq + 3) / 4, BH), dim3(256), 0, s, a);
+  const dim3 ggrid((unsigned)(((int64_t)a.NP * (D / 8) + 255) / 256), BH, 3);
+  if (D == 128) hipLaunchKernelGGL(cgather_kernel<128>, ggrid, dim3(256), 0, s, a);
+  else hipLaunchKernelGGL(cgather_kernel<64>, ggrid, dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
 hipError_t launch_cluster_attn_scatter(const ClusterAttnArgs& a, int BH, int D, bool out_bf16,
                                        hipStream_t s) {
-  const dim3 grid((unsigned)(((int64_t)a.N * (D / 4) + 255) / 256), BH);
+  const dim3 grid((unsigned)(((int64_t)a.NP * (D / 4) + 255) / 256), BH);
   if (D == 128) {
     if (out_bf16) hipLaunchKernelGGL((cscatter_kernel<128, true>), grid, dim3(256), 0, s, a);
     else hipLaunchKernelGGL((cscatter_kernel<128, false>), grid, dim3(256), 0, s, a);

@@ -1,0 +1,252 @@
+// Hardware-aware cluster merging (HyperVAttention section 4.3, Eq. 7-10,
+// Algorithm 1): parallel agglomerative merging of query clusters that lowers
+// the CTA-aligned cost
+//   C(S) = tau_q ceil(s^q(S) / tau_q) * tau_k ceil(g * K(S) / tau_k),
+//   K(S) = sum_j chi_j(S) ceil(s_j^k / g),
+// where chi(S) is the union of the members' key-cluster rows and g the grain
+// at which the executor packs a key cluster (g = 1 is the page's form).
+//
+// A group is named by its lowest member.  Per round, the active groups are
+// split by the caller's side bits (read at each group's name); every side-0
+// group A picks the side-1 group B of smallest gain C(A u B) - C(A) - C(B)
+// (ties to the lower B); per target, the chooser of smallest negative gain
+// is kept (ties to the lower A) and all kept pairs merge at once.
+//
+// Key-cluster masks are bitsets of W words.  K of a union is a weighted
+// popcount: the slot counts are split into bit planes, so
+// K(u) = sum_b 2^b popcount(u & plane_b), one lane per mask word.  Integer
+// throughout: the result does not depend on scheduling.
+#include "bsa_device.h"
+#include "bsa_internal.h"
+
+namespace bsa {
+
+namespace {
+
+__device__ __forceinline__ int64_t group_cost(const ClusterMergeArgs& a, int64_t sq, int64_t k) {
+  const int64_t q = a.tau_q * ((sq + a.tau_q - 1) / a.tau_q);
+  const int64_t kk = a.tau_k * ((a.grain * k + a.tau_k - 1) / a.tau_k);
+  return q * kk;
+}
+
+// Bit planes of the key clusters' slot counts ceil(s_j / g).  One thread per
+// (head, mask word).
+__global__ __launch_bounds__(256) void merge_planes_kernel(ClusterMergeArgs a) {
+  const int w = blockIdx.x * 256 + threadIdx.x;
+  const int64_t bh = blockIdx.y;
+  if (w >= a.W) return;
+  const int32_t* ok = a.off_k + bh * (a.Nk + 1);
+  uint32_t* pl = a.planes + bh * a.nbits * a.W;
+  for (int b = 0; b < a.nbits; ++b) {
+    uint32_t word = 0;
+    for (int t = 0; t < 32; ++t) {
+      const int j = 32 * w + t;
+      if (j < a.Nk) {
+        const int c = (ok[j + 1] - ok[j] + a.grain - 1) / a.grain;
+        word |= (uint32_t)((c >> b) & 1) << t;
+      }
+    }
+    pl[b * a.W + w] = word;
+  }
+}
+
+// Weighted popcount of the union of two masks, one lane per word (W <= 128:
+// two words per lane); the plane words come from LDS.
+__device__ __forceinline__ int union_slots(const ClusterMergeArgs& a, const uint32_t* pl,
+                                           uint32_t u0, uint32_t u1, int lane) {
+  int s = 0;
+  for (int b = 0; b < a.nbits; ++b) {
+    int c = 0;
+    if (lane < a.W) c += __popc(u0 & pl[b * a.W + lane]);
+    if (lane + 64 < a.W) c += __popc(u1 & pl[b * a.W + lane + 64]);
+    s += c << b;
+  }
+  return wave_sum(s);
+}
+
+// Singleton groups: name, query size, mask of the row (built in LDS by
+// integer ORs), key slots.  One wave per query cluster.
+__global__ __launch_bounds__(256) void merge_init_kernel(ClusterMergeArgs a) {
+  __shared__ uint32_t words[4][128];
+  __shared__ uint32_t pl[32 * 128];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int i = blockIdx.x * 4 + wave;
+  const int64_t bh = blockIdx.y;
+  for (int t = threadIdx.x; t < a.nbits * a.W; t += 256) pl[t] = a.planes[bh * a.nbits * a.W + t];
+  for (int t = lane; t < 128; t += 64) words[wave][t] = 0u;
+  __syncthreads();
+  if (i >= a.Nq) return;
+  const int64_t r = bh * a.Nq + i;
+  for (int e = a.crow_ptr[r] + lane; e < a.crow_ptr[r + 1]; e += 64) {
+    const int j = a.ccol[e];
+    if (j >= 0 && j < a.Nk) atomicOr(&words[wave][j >> 5], 1u << (j & 31));
+  }
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+  const uint32_t u0 = lane < a.W ? words[wave][lane] : 0u;
+  const uint32_t u1 = lane + 64 < a.W ? words[wave][lane + 64] : 0u;
+  uint32_t* m = a.gmask + r * a.W;
+  if (lane < a.W) m[lane] = u0;
+  if (lane + 64 < a.W) m[lane + 64] = u1;
+  const int k = union_slots(a, pl, u0, u1, lane);
+  if (lane == 0) {
+    a.grp[r] = i;
+    a.gsq[r] = a.off_q[bh * (a.Nq + 1) + i + 1] - a.off_q[bh * (a.Nq + 1) + i];
+    a.gk[r] = k;
+  }
+}
+
+// The round's two sides, in ascending order of the groups' names (ordered
+// compaction by ballots).  One workgroup of 1024 per head.
+__global__ __launch_bounds__(1024) void merge_sides_kernel(ClusterMergeArgs a) {
+  __shared__ int cnt[2][16];
+  const int64_t bh = blockIdx.x;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const uint8_t* sd = a.sides + (bh * a.rounds + a.round) * a.Nq;
+  int done[2] = {0, 0};
+  for (int i0 = 0; i0 < a.Nq; i0 += 1024) {
+    const int i = i0 + tid;
+    bool act = false;
+    int side = 0;
+    if (i < a.Nq) {
+      act = a.grp[bh * a.Nq + i] == i;
+      side = sd[i] ? 1 : 0;
+    }
+    int pre[2], tot[2];
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      const uint64_t bal = __ballot(act && side == s);
+      if (lane == 0) cnt[s][wave] = __popcll(bal);
+      pre[s] = __popcll(bal & ((1ull << lane) - 1ull));
+    }
+    __syncthreads();
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      int before = 0;
+      tot[s] = 0;
+      for (int w = 0; w < 16; ++w) {
+        if (w < wave) before += cnt[s][w];
+        tot[s] += cnt[s][w];
+      }
+      pre[s] += before + done[s];
+    }
+    if (act) (side == 0 ? a.alist : a.blist)[bh * a.Nq + pre[side]] = i;
+    done[0] += tot[0];
+    done[1] += tot[1];
+    __syncthreads();  // cnt is rewritten by the next chunk
+  }
+  if (tid == 0) {
+    a.nab[bh * 2] = done[0];
+    a.nab[bh * 2 + 1] = done[1];
+  }
+}
+
+// One wave per chooser A: the target B of smallest gain over the side-1
+// groups in ascending order (strict <, so ties keep the lower B).
+__global__ __launch_bounds__(256) void merge_gain_kernel(ClusterMergeArgs a) {
+  __shared__ uint32_t pl[32 * 128];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int ai = blockIdx.x * 4 + wave;
+  const int64_t bh = blockIdx.y;
+  for (int t = threadIdx.x; t < a.nbits * a.W; t += 256) pl[t] = a.planes[bh * a.nbits * a.W + t];
+  __syncthreads();
+  const int na = a.nab[bh * 2], nb = a.nab[bh * 2 + 1];
+  if (ai >= na) return;
+  const int A = a.alist[bh * a.Nq + ai];
+  const int64_t ra = bh * a.Nq + A;
+  const uint32_t* ma = a.gmask + ra * a.W;
+  const uint32_t a0 = lane < a.W ? ma[lane] : 0u;
+  const uint32_t a1 = lane + 64 < a.W ? ma[lane + 64] : 0u;
+  const int64_t sqa = a.gsq[ra];
+  const int64_t ca = group_cost(a, sqa, a.gk[ra]);
+  int64_t best = 0;
+  int bestB = -1, bestK = 0;
+  for (int bi = 0; bi < nb; ++bi) {
+    const int B = a.blist[bh * a.Nq + bi];
+    const int64_t rb = bh * a.Nq + B;
+    const uint32_t* mb = a.gmask + rb * a.W;
+    const uint32_t u0 = a0 | (lane < a.W ? mb[lane] : 0u);
+    const uint32_t u1 = a1 | (lane + 64 < a.W ? mb[lane + 64] : 0u);
+    const int k = union_slots(a, pl, u0, u1, lane);
+    const int64_t sqb = a.gsq[rb];
+    const int64_t gain = group_cost(a, sqa + sqb, k) - ca - group_cost(a, sqb, a.gk[rb]);
+    if (bestB < 0 || gain < best) {
+      best = gain;
+      bestB = B;
+      bestK = k;
+    }
+  }
+  if (lane == 0) {
+    a.choice[ra] = bestB;
+    a.gain[ra] = best;
+    a.ukeys[ra] = bestK;
+  }
+}
+
+// Per target, the chooser of smallest negative gain (choosers scanned in
+// ascending order, strict <); kept pairs merge into the lower name: sizes
+// add, masks OR, key slots from the chooser's evaluation; then every
+// cluster's group name follows.  One workgroup of 1024 per head.
+__global__ __launch_bounds__(1024) void merge_apply_kernel(ClusterMergeArgs a) {
+  __shared__ int newname[kMaxClusters];
+  __shared__ int winner[kMaxClusters];
+  const int64_t bh = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int na = a.nab[bh * 2], nb = a.nab[bh * 2 + 1];
+  const int32_t* al = a.alist + bh * a.Nq;
+  const int32_t* bl = a.blist + bh * a.Nq;
+  for (int i = tid; i < a.Nq; i += 1024) newname[i] = i;
+  for (int bi = tid; bi < nb; bi += 1024) {
+    const int B = bl[bi];
+    int w = -1;
+    int64_t wg = 0;
+    for (int ai = 0; ai < na; ++ai) {
+      const int64_t ra = bh * a.Nq + al[ai];
+      if (a.choice[ra] != B) continue;
+      const int64_t g = a.gain[ra];
+      if (g < 0 && (w < 0 || g < wg)) {
+        w = al[ai];
+        wg = g;
+      }
+    }
+    winner[bi] = w;
+  }
+  __syncthreads();
+  for (int bi = tid; bi < nb; bi += 1024) {
+    const int A = winner[bi];
+    if (A < 0) continue;
+    const int B = bl[bi];
+    const int lo = min(A, B), hi = max(A, B);
+    const int64_t rl = bh * a.Nq + lo, rh = bh * a.Nq + hi;
+    const int sq = a.gsq[rl] + a.gsq[rh];
+    const int k = a.ukeys[bh * a.Nq + A];
+    for (int w = 0; w < a.W; ++w) a.gmask[rl * a.W + w] |= a.gmask[rh * a.W + w];
+    a.gsq[rl] = sq;
+    a.gk[rl] = k;
+    newname[A] = lo;
+    newname[B] = lo;
+  }
+  __syncthreads();
+  for (int i = tid; i < a.Nq; i += 1024) {
+    int32_t* g = a.grp + bh * a.Nq + i;
+    *g = newname[*g];
+  }
+}
+
+}  // namespace
+
+hipError_t launch_cluster_merge(const ClusterMergeArgs& a0, int BH, hipStream_t s) {
+  ClusterMergeArgs a = a0;
+  hipLaunchKernelGGL(merge_planes_kernel, dim3((a.W + 255) / 256, BH), dim3(256), 0, s, a);
+  const dim3 wgrid((a.Nq + 3) / 4, BH);
+  hipLaunchKernelGGL(merge_init_kernel, wgrid, dim3(256), 0, s, a);
+  for (int r = 0; r < a.rounds; ++r) {
+    a.round = r;
+    hipLaunchKernelGGL(merge_sides_kernel, dim3(BH), dim3(1024), 0, s, a);
+    hipLaunchKernelGGL(merge_gain_kernel, wgrid, dim3(256), 0, s, a);
+    hipLaunchKernelGGL(merge_apply_kernel, dim3(BH), dim3(1024), 0, s, a);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace bsa

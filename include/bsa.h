@@ -18,6 +18,7 @@
  *                         front end of cluster-induced blocks).
  *   bsa_cluster_permute   tokens in cluster order (HVA Eq. 1).
  *   bsa_cluster_select    key clusters per query cluster (HVA Eq. 2-3).
+ *   bsa_cluster_merge     merging of query clusters by tiled cost (HVA Alg. 1).
  *   bsa_cluster_attn_fwd  attention over cluster-induced blocks (HVA Eq. 4).
  *   bsa_omission_risk     per-head share of the full softmax mass a sparse
  *                         support omits (offline head calibration).
@@ -423,28 +424,73 @@ bsa_status bsa_cluster_select(const float* mu_q, const float* mu_k,
                               void* stream);
 
 /* ------------------------------------------------------------------------
+ * bsa_cluster_merge -- hardware-aware merging of query clusters
+ * (HyperVAttention section 4.3, Eq. 7-10, Algorithm 1).  A group S of query
+ * clusters costs
+ *   C(S) = tau_q ceil(s^q(S) / tau_q) * tau_k ceil(grain * K(S) / tau_k),
+ *   K(S) = sum over key clusters j in the union of the members' rows of
+ *          ceil(s_j^k / grain),
+ * the tiled work of executing the group with its key clusters packed one
+ * after another at a grain of `grain` tokens (grain = 1 is the page's Eq. 8;
+ * bsa_cluster_attn_fwd packs at 16 on 64 x 64 tiles, so tau_q = tau_k = 64,
+ * grain = 16 is the cost it executes).  Starting from singletons, each of
+ * `rounds` rounds (the page uses 3) splits the current groups by
+ * sides[b, h, round, name] (0 or 1, read at the group's name = its lowest
+ * member; the page draws them at random, the caller does here); every side-0
+ * group A takes the side-1 group B of smallest gain C(A u B) - C(A) - C(B)
+ * (ties to the lower B); for each B the A of smallest negative gain is kept
+ * (ties to the lower A), and all kept pairs merge.  Integer arithmetic:
+ * results are exact and repeatable.
+ *
+ * off_q [B,H,Nq+1], off_k [B,H,Nk+1]: cluster offsets (bsa_cluster_permute;
+ *   sizes are their differences).  crow_ptr / ccol: the cluster CSR of
+ *   bsa_cluster_select (rows (b * H + h) * Nq + i, key clusters in [0, Nk)).
+ * N: tokens per head (bounds the key cluster sizes).  Nq, Nk <= 4096.
+ * sides: uint8 [B, H, rounds, Nq] (may be NULL when rounds = 0); rounds 0..64.
+ * group_of (out): int32 [B, H, Nq], the name of every cluster's group.
+ * workspace: >= bsa_cluster_merge_workspace_bytes(B, H, N, Nq, Nk, grain)
+ *   bytes, 256-byte aligned.
+ * ---------------------------------------------------------------------- */
+int64_t bsa_cluster_merge_workspace_bytes(int32_t B, int32_t H, int32_t N,
+                                          int32_t Nq, int32_t Nk,
+                                          int32_t grain);
+
+bsa_status bsa_cluster_merge(const int32_t* off_q, const int32_t* off_k,
+                             const int32_t* crow_ptr, const int32_t* ccol,
+                             int32_t B, int32_t H, int32_t N, int32_t Nq,
+                             int32_t Nk, const uint8_t* sides, int32_t rounds,
+                             int32_t tau_q, int32_t tau_k, int32_t grain,
+                             int32_t* group_of, void* workspace,
+                             int64_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
  * bsa_cluster_attn_fwd -- attention over cluster-induced blocks
- * (HyperVAttention section 2, Eq. 4): every query of query cluster i
- * attends over the tokens of the key clusters in row i of the cluster CSR;
+ * (HyperVAttention section 2, Eq. 4; merged groups of section 4.3, Eq. 8):
+ * every query of query cluster i attends over the tokens of the key clusters
+ * in the union of the rows of its group (its own row when group_of is NULL);
  * O and LSE are written in the original token order (O = Pi_q^-1 O').
  *   LSE[t] = ln sum_tau exp(scale q_t . k_tau), O[t] = sum_tau softmax v_tau
- * over those keys; a query cluster with an empty row gets O = 0, LSE = -inf.
- * Executed on 64-token tiles with every cluster padded to whole tiles (the
- * tile-aligned cost of the page's Eq. 7 with tiles of 64 on both sides);
- * padding keys are masked, so the result is exactly Eq. 4.  Precision as
- * bsa_sparse_attn_fwd.
+ * over those keys; a group with no key cluster gets O = 0, LSE = -inf.
+ * Executed as Eq. 8 describes: each group's queries fill whole 64-query
+ * tiles; the key clusters are padded to whole 16-key chunks and a group's
+ * chunks are packed four to a 64-key tile; padding keys are masked, so the
+ * result is exactly Eq. 4.  Precision as bsa_sparse_attn_fwd.
  *
  * perm_q / off_q: bsa_cluster_permute of the query clustering ([B,H,N],
  *   [B,H,Nq+1]); perm_k / off_k the same for the keys ([B,H,Nk+1]).
+ *   Nq, Nk <= 4096.
  * crow_ptr / ccol: cluster CSR with rows (b * H + h) * Nq + i and key cluster
- *   indices in [0, Nk) (bsa_cluster_select).
+ *   indices in [0, Nk) (bsa_cluster_select); entries outside are ignored.
+ * group_of: int32 [B, H, Nq] group names (bsa_cluster_merge: the lowest
+ *   member) or NULL; a name outside [0, i] makes cluster i its own group.
  * O: [B, H, N, d] with the strides of `shape`, o_dtype BSA_F32 or BSA_BF16;
  *   LSE: float32 [B, H, N].
  * out_tile_pairs: device int64 or NULL; receives the number of executed
- *   (query tile, key tile) pairs.
+ *   (query tile, key tile) pairs, C(S) / 64^2 summed over the groups.
  * workspace: >= bsa_cluster_attn_workspace_bytes(shape, Nq, Nk, o_dtype)
  *   bytes, 256-byte aligned (padded copies of Q, K, V and the output, the
- *   tile lists): padded length per head 64 * (ceil(N/64) + max(Nq, Nk)).
+ *   chunk lists): padded length per head 64 * max(ceil(N/64) + Nq,
+ *   ceil((ceil(N/16) + Nk + 1) / 4)).
  * ---------------------------------------------------------------------- */
 int64_t bsa_cluster_attn_workspace_bytes(const bsa_shape* shape, int32_t Nq,
                                          int32_t Nk, int32_t o_dtype);
@@ -455,7 +501,8 @@ bsa_status bsa_cluster_attn_fwd(const uint16_t* Q, const uint16_t* K,
                                 const int32_t* perm_q, const int32_t* off_q,
                                 const int32_t* perm_k, const int32_t* off_k,
                                 const int32_t* crow_ptr, const int32_t* ccol,
-                                void* O, int32_t o_dtype, float* LSE,
+                                const int32_t* group_of, void* O,
+                                int32_t o_dtype, float* LSE,
                                 int64_t* out_tile_pairs, void* workspace,
                                 int64_t workspace_bytes, void* stream);
 

@@ -670,7 +670,7 @@ def merge_cost(sq: int, chi, sizes_k, tau_q: int = 64, tau_k: int = 64, g: int =
     key slots (g = 1 is the page's form)."""
     sk = np.asarray(sizes_k, dtype=np.int64)
     slots = g * (-(-sk // g))
-    keys = int(sum(int(slots[j]) for j in range(len(sk)) if chi[j]))
+    keys = int(slots[np.asarray(chi, dtype=bool)].sum())
     return (tau_q * (-(-int(sq) // tau_q))) * (tau_k * (-(-keys // tau_k)))
 
 

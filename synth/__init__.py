@@ -8,6 +8,7 @@ from .video_qkv import (  # noqa: F401
     VideoSpec,
     config_spec,
     gen_qkv,
+    merge_sides,
     micro_heads,
     mod_pattern_mask,
     rotation_offset,

@@ -22,7 +22,7 @@ interactions inside blocks whose 64-token pooled score stays low.
 Random streams: numpy PCG64 seeded by SeedSequence(0xB5A, spawn_key=(cfg,
 stream, index)); stream 0 = W, 1/2/3 = Q/K/V noise, 4 = spike codes and
 directions, 5 = micro-head subset, 6 = anchor rotation offsets, 7 = sample of
-pairs for the logit spread.
+pairs for the logit spread, 8 = the bipartition bits of cluster merging.
 """
 
 from __future__ import annotations
@@ -179,6 +179,12 @@ def micro_heads(cfg: int) -> list[int]:
 def rotation_offset(cfg: int, call: int, n_blocks: int) -> int:
     """Anchor rotation offset for call number ``call`` (drawn fresh per call)."""
     return int(_rng(CONFIGS[cfg]["spec"].key, 6, call).integers(0, n_blocks))
+
+
+def merge_sides(key: int, B: int, H: int, rounds: int, n: int) -> np.ndarray:
+    """The random bipartition bits of cluster merging: uint8 [B, H, rounds, n]
+    (0 or 1 per round and query cluster), drawn from stream 8."""
+    return _rng(key, 8, 0).integers(0, 2, size=(B, H, rounds, n), dtype=np.uint8)
 
 
 def spike_codes(spec: VideoSpec):

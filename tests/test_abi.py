@@ -274,3 +274,48 @@ def test_cluster_validation():
     st = bsa._lib.bsa_local_window_cluster(None, ctypes.byref(s), ctypes.byref(cp), p, p, p, p,
                                            256, None)
     assert st == 1 and "X is NULL" in bsa.bsa_last_error()
+
+
+def _align(n):
+    return -(-n // 256) * 256
+
+
+def test_cluster_attention_and_merge_validation_and_workspace():
+    L = bsa._lib
+    s = _shape(B=1, H=2, N=1000, d=128)
+    Nq, Nk = 12, 30
+    nTP = max(-(-1000 // 64) + Nq, -(-(-(-1000 // 16) + Nk + 1) // 4))
+    NP, W = 64 * nTP, 1
+    cap = 2 * Nq * (-(-1000 // 16) + Nk + 1 + 3)
+    want = sum(_align(x) for x in (
+        2 * (Nq + 1) * 4, 2 * Nq * 4, 2 * (Nk + 1) * 4, 2 * nTP * 4, 2 * NP * 4, 2 * Nq * W * 4,
+        2 * Nq * 4, (2 * Nq + 1) * 4, 8, 8, 2 * NP * 128 * 2, 2 * NP * 128 * 2, 2 * NP * 128 * 2,
+        2 * NP * 128 * 2, 2 * NP * 128 * 4, 2 * NP * 4, cap * 4))
+    assert L.bsa_cluster_attn_workspace_bytes(ctypes.byref(s), Nq, Nk, 0) == want
+    assert L.bsa_cluster_attn_workspace_bytes(ctypes.byref(s), 4097, Nk, 0) == -1
+    assert "4096" in bsa.bsa_last_error()
+    assert L.bsa_cluster_attn_workspace_bytes(ctypes.byref(s), Nq, 0, 0) == -1
+    p = ctypes.c_void_p(4096)
+    st = L.bsa_cluster_attn_fwd(p, p, p, ctypes.byref(s), 0.1, Nq, Nk, p, p, p, p, p, p, None, p,
+                                0, p, None, p, 255, None)
+    assert st == 3 and "workspace" in bsa.bsa_last_error()
+    st = L.bsa_cluster_attn_fwd(p, p, p, ctypes.byref(s), 0.1, Nq, Nk, p, p, p, p, p, None, None,
+                                p, 0, p, None, p, want, None)
+    assert st == 1 and "ccol" in bsa.bsa_last_error()
+    st = L.bsa_cluster_attn_fwd(p, p, p, ctypes.byref(s), 0.1, Nq, Nk, p, p, p, p, p, p,
+                                ctypes.c_void_p(4098), p, 0, p, None, p, want, None)
+    assert st == 1 and "group_of" in bsa.bsa_last_error()
+    # merging: slot counts up to ceil(1000 / 16) = 63 need 6 bit planes
+    mw = sum(_align(x) for x in (2 * Nq * 4, 2 * Nq * 4, 2 * Nq * 4, 2 * Nq * 4, 2 * 2 * 4,
+                                 2 * Nq * 4, 2 * Nq * 8, 2 * Nq * 4, 2 * Nq * W * 4, 2 * 6 * W * 4))
+    assert L.bsa_cluster_merge_workspace_bytes(1, 2, 1000, Nq, Nk, 16) == mw
+    assert L.bsa_cluster_merge_workspace_bytes(1, 2, 1000, Nq, Nk, 0) == -1
+    assert L.bsa_cluster_merge_workspace_bytes(1, 2, 1000, Nq, 5000, 16) == -1
+    st = L.bsa_cluster_merge(p, p, p, p, 1, 2, 1000, Nq, Nk, None, 3, 64, 64, 16, p, p, mw, None)
+    assert st == 1 and "sides" in bsa.bsa_last_error()
+    st = L.bsa_cluster_merge(p, p, p, p, 1, 2, 1000, Nq, Nk, p, 65, 64, 64, 16, p, p, mw, None)
+    assert st == 1 and "rounds" in bsa.bsa_last_error()
+    st = L.bsa_cluster_merge(p, p, p, p, 1, 2, 1000, Nq, Nk, p, 3, 0, 64, 16, p, p, mw, None)
+    assert st == 1 and "tau" in bsa.bsa_last_error()
+    st = L.bsa_cluster_merge(p, p, p, p, 1, 2, 1000, Nq, Nk, p, 3, 64, 64, 16, p, p, mw - 1, None)
+    assert st == 3 and "workspace" in bsa.bsa_last_error()

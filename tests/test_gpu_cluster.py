@@ -191,8 +191,11 @@ def test_cluster_select_hunyuanvideo_sizes():
 
 # ------------------------------------------------- attention over clusters
 
-def _cluster_attn_case(Q, K, V, aq, ak, Nq, Nk, rows, out_dtype=torch.float32, sample=None):
-    """GPU Eq. 4 on oracle-made clusterings and lists against the oracle."""
+def _cluster_attn_case(Q, K, V, aq, ak, Nq, Nk, rows, out_dtype=torch.float32, sample=None,
+                       groups=None):
+    """GPU Eq. 4 on oracle-made clusterings, lists (and merged groups)
+    against the oracle; the executed tile pairs against Eq. 8 at a 16-token
+    key grain."""
     import math
     import parity as PT
     N, d = Q.shape[2], Q.shape[3]
@@ -200,11 +203,20 @@ def _cluster_attn_case(Q, K, V, aq, ak, Nq, Nk, rows, out_dtype=torch.float32, s
     pk, ok = O.cluster_permutation(ak, Nk)
     rp, ci = PT.rows_to_csr(rows)
     t = lambda x: torch.from_numpy(np.asarray(x, dtype=np.int32)).to(DEV)
+    gof = None
+    if groups is not None:
+        name = np.zeros(Nq, dtype=np.int32)
+        for S in groups:
+            name[S] = min(S)
+        gof = t(name)[None, None]
+    else:
+        groups = [[i] for i in range(Nq)]
     Og, Lg, pairs = bsa.bsa_cluster_attn_fwd(
         Q.to(DEV), K.to(DEV), V.to(DEV), t(pq)[None, None], t(oq)[None, None], t(pk)[None, None],
-        t(ok)[None, None], rp.to(DEV), ci.to(DEV), out_dtype=out_dtype)
+        t(ok)[None, None], rp.to(DEV), ci.to(DEV), gof, out_dtype=out_dtype)
     torch.cuda.synchronize()
-    assert int(pairs.item()) == O.cluster_tile_pairs(oq, ok, rows)
+    rows = O.group_rows(groups, rows)
+    assert int(pairs.item()) == O.packed_tile_pairs(oq, ok, groups, rows, 64, 16)
     q, k, v = (X[0, 0].double().numpy() for X in (Q, K, V))
     scale = 1 / math.sqrt(d)
     if sample is None:
@@ -271,7 +283,8 @@ def test_cluster_pipeline_end_to_end():
     Oref, Lref = O.cluster_block_attention(x, y, V[0, 0].double().numpy(), pq_o, oq_o, pk_o,
                                            ok_o, rows, 1 / math.sqrt(d))
     PT.compare_o_lse(Og[0, 0], Lg[0, 0], Oref, Lref, "pipeline")
-    assert int(pairs.item()) == O.cluster_tile_pairs(oq_o, ok_o, rows)
+    assert int(pairs.item()) == O.packed_tile_pairs(oq_o, ok_o, [[i] for i in range(len(cq_o))],
+                                                    rows, 64, 16)
 
 
 def test_cluster_attention_hunyuanvideo_shape():
@@ -292,3 +305,126 @@ def test_cluster_attention_hunyuanvideo_shape():
     pairs = _cluster_attn_case(Q, K, V, aq, ak, 432, 1215, rows,
                                sample=sorted(rng.choice(432, 6, replace=False).tolist()) + [431])
     say(f"HunyuanVideo shape: {pairs} tile pairs")
+
+
+# ------------------------------------------------------- merging (Algorithm 1)
+
+def _merge_case(sizes_q, sizes_k, rows, sides, N, tau_q=64, tau_k=64, grain=16):
+    """GPU merging against the oracle's Algorithm 1: integer work, so the
+    group of every cluster must be identical."""
+    import parity as PT
+    t = lambda x: torch.from_numpy(np.asarray(x, dtype=np.int32)).to(DEV)
+    oq = np.concatenate([[0], np.cumsum(sizes_q)])
+    ok = np.concatenate([[0], np.cumsum(sizes_k)])
+    rp, ci = PT.rows_to_csr(rows)
+    sd = torch.from_numpy(np.ascontiguousarray(sides)).to(DEV)
+    gof = bsa.bsa_cluster_merge(t(oq)[None, None], t(ok)[None, None], rp.to(DEV), ci.to(DEV), sd,
+                                N=N, tau_q=tau_q, tau_k=tau_k, grain=grain)
+    torch.cuda.synchronize()
+    grp, groups = O.agglomerative_merge(list(sizes_q), rows, list(sizes_k),
+                                        np.asarray(sides)[0, 0].tolist(), tau_q, tau_k, grain)
+    np.testing.assert_array_equal(gof[0, 0].cpu().numpy(), grp)
+    return groups
+
+
+@pytest.mark.parametrize("seed", range(6))
+@pytest.mark.parametrize("tau_q,tau_k,grain", [(64, 64, 16), (64, 64, 1), (128, 96, 1)])
+def test_cluster_merge_random(seed, tau_q, tau_k, grain):
+    from synth import merge_sides
+    rng = np.random.default_rng(500 + seed)
+    Nq, Nk = int(rng.integers(2, 80)), int(rng.integers(1, 150))
+    N = int(rng.integers(max(Nq, Nk), 20000))
+    sq = rng.multinomial(N, np.ones(Nq) / Nq)
+    sk = rng.multinomial(N, np.ones(Nk) / Nk)
+    rows = [sorted(rng.choice(Nk, int(rng.integers(0, Nk + 1)), replace=False).tolist())
+            for _ in range(Nq)]
+    sides = merge_sides(600 + seed, 1, 1, 3, Nq)
+    say(f"merge Nq={Nq} Nk={Nk} N={N} tau=({tau_q},{tau_k}) grain={grain}")
+    groups = _merge_case(sq, sk, rows, sides, N, tau_q, tau_k, grain)
+    say(f"   {Nq} clusters -> {len(groups)} groups")
+
+
+def test_cluster_merge_hunyuanvideo_sizes():
+    """The page's HunyuanVideo setting: 432 query and 1215 key clusters (the
+    cells of the 118,800-token lattice), rows from cluster top-p 0.9 with
+    Min-kc 0.15 (183 key clusters) on the cells' mean vectors of the first
+    head, three rounds (the page's R = 3)."""
+    import math
+    from synth import merge_sides
+    spec = config_spec(3)
+    Q, K, _ = gen_qkv(spec, heads=[0])
+    T, H, W = spec.grid
+    t, y, x = np.meshgrid(np.arange(T), np.arange(H), np.arange(W), indexing="ij")
+    cell = lambda k: ((t // k[0]) * -(-H // k[1]) + y // k[1]) * -(-W // k[2]) + x // k[2]
+    aq, ak = cell((11, 5, 5)).reshape(-1), cell((11, 3, 3)).reshape(-1)
+    sq, sk = np.bincount(aq, minlength=432), np.bincount(ak, minlength=1215)
+    xq, xk = Q[0, 0].double().numpy(), K[0, 0].double().numpy()
+    mq = np.stack([np.bincount(aq, weights=xq[:, c], minlength=432) for c in range(128)], 1)
+    mk = np.stack([np.bincount(ak, weights=xk[:, c], minlength=1215) for c in range(128)], 1)
+    rows = O.cluster_topp_rows(mq / sq[:, None], mk / sk[:, None], sk, 1 / math.sqrt(128), 0.9,
+                               183, 1215)
+    groups = _merge_case(sq, sk, rows, merge_sides(511, 1, 1, 3, 432), spec.N)
+    before = O.partition_cost([[i] for i in range(432)], sq, rows, sk, 64, 64, 16)
+    after = O.partition_cost(groups, sq, rows, sk, 64, 64, 16)
+    say(f"   HunyuanVideo: {len(groups)} groups, cost {before} -> {after}")
+    assert len(groups) < 432 and after < before
+
+
+@pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16])
+def test_cluster_attention_merged_groups(out_dtype):
+    """Eq. 4 over merged groups (each member attends over the union of the
+    group's rows) on an oracle-made clustering, oracle-merged."""
+    import math
+    from synth import merge_sides
+    grid, d = (4, 16, 20), 128
+    spec = VideoSpec(1, 1, d, grid, 171)
+    Q, K, V = gen_qkv(spec)
+    x, y = Q[0, 0].double().numpy(), K[0, 0].double().numpy()
+    aq, mq, cnt_q = O.local_window_clustering(x, grid, (2, 4, 4), (2, 2, 2), 2)
+    ak, mk, cnt_k = O.local_window_clustering(y, grid, (1, 4, 4), (2, 2, 2), 2)
+    rows = O.cluster_topp_rows(mq, mk, cnt_k, 1 / math.sqrt(d), 0.8, 3, len(cnt_k))
+    sides = merge_sides(172, 1, 1, 3, len(cnt_q))[0, 0].tolist()
+    _, groups = O.agglomerative_merge(cnt_q.tolist(), rows, cnt_k.tolist(), sides, 64, 64, 16)
+    assert any(len(S) > 1 for S in groups), "no merge happened: pick other inputs"
+    say("merged attention", len(cnt_q), "clusters ->", len(groups), "groups")
+    _cluster_attn_case(Q, K, V, aq, ak, len(cnt_q), len(cnt_k), rows, out_dtype, groups=groups)
+
+
+def test_cluster_pipeline_with_merging():
+    """GPU clustering, permutation, cluster top-p, merging and Eq. 4 over the
+    groups, chained, against the oracle's chain (decisions equal here)."""
+    import math
+    import parity as PT
+    from synth import merge_sides
+    grid, d, cq, ck, win = (4, 12, 16), 128, (2, 3, 4), (2, 3, 2), (2, 3, 3)
+    spec = VideoSpec(1, 1, d, grid, 173)
+    Q, K, V = gen_qkv(spec)
+    Qd, Kd, Vd = (X.to(DEV) for X in (Q, K, V))
+    aq, mq, cnt_q = bsa.bsa_local_window_cluster(Qd, grid, cq, win, 2)
+    ak, mk, cnt_k = bsa.bsa_local_window_cluster(Kd, grid, ck, win, 2)
+    pq, oq = bsa.bsa_cluster_permute(aq, cnt_q, Qd, grid, cq, win)
+    pk, ok = bsa.bsa_cluster_permute(ak, cnt_k, Kd, grid, ck, win)
+    Nq, Nk = cnt_q.shape[2], cnt_k.shape[2]
+    rp, ci, nnz = bsa.bsa_cluster_select(mq, mk, cnt_k, p=0.85, k_min=2, k_cap=Nk)
+    sides = torch.from_numpy(merge_sides(174, 1, 1, 3, Nq)).to(DEV)
+    gof = bsa.bsa_cluster_merge(oq, ok, rp, ci, sides, N=spec.N)
+    Og, Lg, pairs = bsa.bsa_cluster_attn_fwd(Qd, Kd, Vd, pq, oq, pk, ok, rp, ci, gof)
+    torch.cuda.synchronize()
+    x, y = Q[0, 0].double().numpy(), K[0, 0].double().numpy()
+    aq_o, mq_o, cq_o = O.local_window_clustering(x, grid, cq, win, 2)
+    ak_o, mk_o, ck_o = O.local_window_clustering(y, grid, ck, win, 2)
+    assert np.array_equal(aq_o, aq[0, 0].cpu().numpy())
+    assert np.array_equal(ak_o, ak[0, 0].cpu().numpy())
+    rows = O.cluster_topp_rows(mq_o, mk_o, ck_o, 1 / math.sqrt(d), 0.85, 2, Nk)
+    assert bsa.csr_rows(rp, ci, nnz) == rows, "cluster lists differ (a tie): pick other inputs"
+    grp, groups = O.agglomerative_merge(cq_o.tolist(), rows, ck_o.tolist(),
+                                        sides[0, 0].cpu().numpy().tolist(), 64, 64, 16)
+    np.testing.assert_array_equal(gof[0, 0].cpu().numpy(), grp)
+    say("pipeline with merging:", Nq, "clusters ->", len(groups), "groups")
+    pq_o, oq_o = O.cluster_permutation(aq_o, len(cq_o))
+    pk_o, ok_o = O.cluster_permutation(ak_o, len(ck_o))
+    grows = O.group_rows(groups, rows)
+    Oref, Lref = O.cluster_block_attention(x, y, V[0, 0].double().numpy(), pq_o, oq_o, pk_o,
+                                           ok_o, grows, 1 / math.sqrt(d))
+    PT.compare_o_lse(Og[0, 0], Lg[0, 0], Oref, Lref, "pipeline with merging")
+    assert int(pairs.item()) == O.packed_tile_pairs(oq_o, ok_o, groups, grows, 64, 16)
