@@ -13,7 +13,8 @@ definitions below state.
 Sources (pages as titled):
   [HVA]   "HyperVAttention: Efficient Sparse Attention with Spatio-Temporal
           Clustering for Video Diffusion", section 2 (Preliminaries), Eq. 2-4,
-          section 4.1 (3D local-window clustering, Eq. 5), section 4.3
+          section 4.1 (3D local-window clustering, Eq. 5), section 4.2
+          (Lowe's ratio, Eq. 6), section 4.3
           (hardware cost, Eq. 7-10, Algorithm 1), Appendix A.1 (Top-p,
           Min-kc, R = 3 rounds) and A.2 (Algorithm 2).
   [RSA]   "Rectified SpaAttn: Revisiting Attention Sparsity for Efficient Video
@@ -55,6 +56,8 @@ design notes of the repository):
   * RSA's pooled rectification is read as attention over the pooled keys of
     the omitted blocks (log-size bias), LSE-merged with the sparse result;
     its gain-aware gate has no stated rule and is not modelled;
+  * [HVA] Eq. 6 (Lowe's ratio) is taken over each token's local window,
+    the candidates of its assignment, against the centroids given;
   * [HVA] Algorithm 1: the random bipartition is an input (a side bit per
     round for every group, read at the group's lowest member); side-0 groups
     choose, ties go to lower indices; a merged group is named by its lowest
@@ -660,6 +663,42 @@ def cluster_tile_pairs(off_q, off_k, rows, tile: int = 64) -> int:
     tq = -(-sq // tile)
     tk = -(-sk // tile)
     return int(sum(int(tq[i]) * int(sum(int(tk[j]) for j in sel)) for i, sel in enumerate(rows)))
+
+
+def lowe_ratios(X, thw, cell, window, mu) -> np.ndarray:
+    """[HVA] Eq. 6: rho = d_1 / d_2 per token, d_1 its Euclidean distance to
+    the nearest centroid and d_2 to the nearest other one, both over the
+    centroids of its local window (the candidates its assignment uses).
+    A token with one candidate has rho = 0; d_1 = d_2 = 0 gives rho = 1."""
+    X = np.asarray(X, np.float64)
+    mu = np.asarray(mu, np.float64)
+    T, H, W = thw
+    K, w = cluster_grid(thw, cell, window)
+    Kt, Kh, Kw = K
+    rho = np.zeros(X.shape[0])
+    for t in range(T):
+        for h in range(H):
+            for x in range(W):
+                g = (t // cell[0], h // cell[1], x // cell[2])
+                st = [window_start(g[i], w[i], K[i]) for i in range(3)]
+                cand = [(vt * Kh + vh) * Kw + vw for vt in range(st[0], st[0] + w[0])
+                        for vh in range(st[1], st[1] + w[1]) for vw in range(st[2], st[2] + w[2])]
+                n = (t * H + h) * W + x
+                dist = np.sort(np.sqrt(((X[n] - mu[cand]) ** 2).sum(axis=1)))
+                if len(dist) < 2:
+                    rho[n] = 0.0
+                elif dist[1] == 0.0:
+                    rho[n] = 1.0
+                else:
+                    rho[n] = dist[0] / dist[1]
+    return rho
+
+
+def lowe_subset(rho, n: int) -> np.ndarray:
+    """[HVA] section 4.2: the n tokens with the largest Lowe's ratio (the
+    most ambiguous assignments; equal ratios go to the lower index), in
+    ascending token order."""
+    return np.sort(rank_desc(np.asarray(rho, np.float64))[:max(0, n)])
 
 
 def merge_cost(sq: int, chi, sizes_k, tau_q: int = 64, tau_k: int = 64, g: int = 1) -> int:

@@ -1011,3 +1011,65 @@ def test_merge_pins_catch_planted_mistakes(mistake, monkeypatch):
     with pytest.raises(AssertionError):
         test_golden_merge_cost()
         test_golden_merge_rounds()
+
+
+# ------------------------------------------------------------ Lowe's ratio
+
+def test_golden_lowe_ratio():
+    g = _load("hva_lowe_ratio.json")
+    rho = O.lowe_ratios(np.array(g["X"]), tuple(g["thw"]), tuple(g["cell"]), tuple(g["window"]),
+                        np.array(g["mu"]))
+    np.testing.assert_allclose(rho, g["rho"], rtol=0, atol=1e-15)
+    assert O.lowe_subset(rho, 2).tolist() == g["subset_2"]
+    assert O.lowe_subset(rho, 3).tolist() == g["subset_3"]
+
+
+def test_lowe_ratio_with_a_global_window_is_cdist():
+    """A window covering the whole grid: the two smallest Euclidean distances
+    of scipy's cdist over every centroid."""
+    import scipy.spatial.distance as sd
+    thw, cell = (3, 6, 8), (1, 3, 4)
+    X, mu = _rand(81, 3 * 6 * 8, 5), _rand(82, 3 * 2 * 2, 5)
+    rho = O.lowe_ratios(X, thw, cell, (3, 2, 2), mu)
+    dd = np.sort(sd.cdist(X, mu), axis=1)
+    np.testing.assert_allclose(rho, dd[:, 0] / dd[:, 1], rtol=1e-14)
+
+
+def test_lowe_ratio_special_cases():
+    thw, cell = (1, 2, 2), (1, 1, 1)
+    mu = np.array([[0.0, 0.0], [4.0, 0.0], [0.0, 4.0], [4.0, 4.0]])
+    X = np.array([[0.0, 0.0], [2.0, 2.0], [1.0, 0.0], [4.0, 4.0]])
+    rho = O.lowe_ratios(X, thw, cell, (1, 2, 2), mu)
+    assert rho[0] == 0.0 and rho[3] == 0.0          # on a centroid
+    assert rho[1] == 1.0                            # equidistant from all four
+    assert abs(rho[2] - 1.0 / 3.0) < 1e-15          # 1 against 3
+    # one candidate per token: no second centroid
+    assert np.all(O.lowe_ratios(X, thw, cell, (1, 1, 1), mu) == 0.0)
+    # two coincident centroids at distance 0 from the token
+    assert O.lowe_ratios(np.zeros((2, 2)), (1, 1, 2), (1, 1, 1), (1, 1, 2), np.zeros((2, 2)))[0] == 1.0
+    # rho = 1 exactly where the assignment margin is 0
+    m = O.assignment_margins(X, thw, cell, (1, 2, 2), mu)
+    assert np.array_equal(rho == 1.0, m == 0.0)
+
+
+def test_lowe_subset_order_and_ties():
+    rho = np.array([0.5, 0.9, 0.5, 0.1, 0.9, 0.5])
+    assert O.lowe_subset(rho, 2).tolist() == [1, 4]
+    assert O.lowe_subset(rho, 3).tolist() == [0, 1, 4]       # tie at 0.5 -> lowest index
+    assert O.lowe_subset(rho, 4).tolist() == [0, 1, 2, 4]
+    assert O.lowe_subset(rho, 0).tolist() == []
+    assert O.lowe_subset(rho, 9).tolist() == list(range(6))
+
+
+@pytest.mark.parametrize("mistake", ["inverted", "squared"])
+def test_lowe_pins_catch_planted_mistakes(mistake, monkeypatch):
+    real = O.lowe_ratios
+
+    def wrong(X, thw, cell, window, mu):
+        r = real(X, thw, cell, window, mu)
+        if mistake == "inverted":
+            return np.where(r > 0, 1.0 / np.where(r > 0, r, 1.0), 0.0)
+        return r ** 2
+    monkeypatch.setattr(O, "lowe_ratios", wrong)
+    with pytest.raises(AssertionError):
+        test_golden_lowe_ratio()
