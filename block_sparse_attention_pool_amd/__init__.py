@@ -94,6 +94,7 @@ def _load(path: str = _LIB_PATH):
         "bsa_cluster_attn_fwd": ([P, P, P, SP, F32, I32, I32, P, P, P, P, P, P, P, P, I32, P, P, P,
                                   I64, P], I32),
         "bsa_cluster_merge_workspace_bytes": ([I32, I32, I32, I32, I32, I32], I64),
+        "bsa_lowe_ratio_subset": ([P, SP, CP, P, I32, P, P, P, I64, P], I32),
         "bsa_cluster_merge": ([P, P, P, P, I32, I32, I32, I32, I32, P, I32, I32, I32, I32, P, P,
                                I64, P], I32),
         "bsa_cluster_select": ([P, P, P, I32, I32, I32, I32, I32, F32, F32, I32, I32, P, P, I64,
@@ -118,7 +119,7 @@ EXPORTED = ("bsa_version", "bsa_last_error", "bsa_score_blocks", "bsa_select_wor
             "bsa_cluster_permute_workspace_bytes", "bsa_cluster_permute",
             "bsa_cluster_select_workspace_bytes", "bsa_cluster_select",
             "bsa_cluster_attn_workspace_bytes", "bsa_cluster_attn_fwd",
-            "bsa_cluster_merge_workspace_bytes", "bsa_cluster_merge")
+            "bsa_cluster_merge_workspace_bytes", "bsa_cluster_merge", "bsa_lowe_ratio_subset")
 
 
 def library_path() -> str:
@@ -433,6 +434,36 @@ def bsa_local_window_cluster(X, thw, cell, window, iters: int = 1, *, stream=Non
                                        _stream(stream, dev))
     _check(st, "bsa_local_window_cluster")
     return assign, mu, counts
+
+
+def bsa_lowe_ratio_subset(X, centroids, thw, cell, window, frac: float = 0.15, *,
+                          n_sub: int | None = None, stream=None):
+    """Lowe's ratio (HVA Eq. 6) of every token of X [B, H, N, d] bf16 over its
+    window's centroids, and the ceil(frac * N) tokens of largest ratio per
+    head (or ``n_sub`` of them).  Returns (rho float32 [B, H, N], subset
+    int32 [B, H, n_sub] ascending)."""
+    if X.dtype != torch.bfloat16:
+        raise ValueError("X must be bfloat16")
+    shp = shape_of(X)
+    cp = _ClusterParams(*thw, *cell, *window, 1)
+    B, H, N, d = X.shape
+    if n_sub is None:
+        n_sub = budget_blocks(frac, N)
+    nws = _lib.bsa_cluster_workspace_bytes(ctypes.byref(shp), ctypes.byref(cp))
+    if nws < 0:
+        raise BsaError(f"bsa_cluster_workspace_bytes: {bsa_last_error()}")
+    dev = X.device
+    rho = torch.empty((B, H, N), dtype=torch.float32, device=dev)
+    subset = torch.empty((B, H, max(n_sub, 1)), dtype=torch.int32, device=dev)
+    ws = torch.empty(max(nws, 256), dtype=torch.uint8, device=dev)
+    mu = centroids.contiguous()
+    if mu.dtype != torch.float32 or tuple(mu.shape[:2]) != (B, H) or mu.shape[3] != d:
+        raise ValueError("centroids must be float32 [B, H, cells, d]")
+    st = _lib.bsa_lowe_ratio_subset(_ptr(X), ctypes.byref(shp), ctypes.byref(cp),
+                                    _ptr(mu), n_sub, _ptr(rho), _ptr(subset),
+                                    _ptr(ws), ws.numel(), _stream(stream, dev))
+    _check(st, "bsa_lowe_ratio_subset")
+    return rho, subset[..., :n_sub]
 
 
 def bsa_cluster_permute(assign, counts, X_like, thw, cell, window, *, stream=None):

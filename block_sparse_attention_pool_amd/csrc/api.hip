@@ -836,7 +836,9 @@ int64_t bsa_cluster_cells(const bsa_shape* shape, const bsa_cluster_params* para
 int64_t bsa_cluster_workspace_bytes(const bsa_shape* shape, const bsa_cluster_params* params) {
   int64_t cells = 0;
   if (plan_cluster(shape, params, &cells) != BSA_OK) return -1;
-  return align256((int64_t)shape->B * shape->H * cells * 4);
+  // centroid norms, then the centroids' three bf16 parts
+  return align256((int64_t)shape->B * shape->H * cells * 4) +
+         align256((int64_t)shape->B * shape->H * cells * 3 * shape->d * 2);
 }
 
 bsa_status bsa_local_window_cluster(const uint16_t* X, const bsa_shape* shape,
@@ -852,7 +854,7 @@ bsa_status bsa_local_window_cluster(const uint16_t* X, const bsa_shape* shape,
   BSA_TRY(check_ptr(assign, "assign", 4));
   BSA_TRY(check_ptr(centroids, "centroids", 16));
   BSA_TRY(check_ptr(counts, "counts", 4));
-  BSA_TRY(check_ptr(workspace, "workspace", 4));
+  BSA_TRY(check_ptr(workspace, "workspace", 16));
   const int64_t need = bsa_cluster_workspace_bytes(shape, p);
   if (workspace_bytes < need)
     return fail(BSA_ERR_CAPACITY, "workspace %lld bytes < required %lld",
@@ -882,9 +884,59 @@ bsa_status bsa_local_window_cluster(const uint16_t* X, const bsa_shape* shape,
   a.assign = assign;
   a.mu = centroids;
   a.norm = (float*)workspace;
+  a.mu3 = (uint16_t*)((char*)workspace + align256((int64_t)shape->B * shape->H * cells * 4));
   a.counts = counts;
   return hip_status(bsa::launch_cluster(a, shape->B * shape->H, p->iters, (hipStream_t)stream),
                     "cluster launch");
+}
+
+bsa_status bsa_lowe_ratio_subset(const uint16_t* X, const bsa_shape* shape,
+                                 const bsa_cluster_params* p, const float* centroids,
+                                 int32_t n_sub, float* rho, int32_t* subset, void* workspace,
+                                 int64_t workspace_bytes, void* stream) {
+  int64_t cells = 0;
+  BSA_TRY(plan_cluster(shape, p, &cells));
+  if (shape->stride_n < shape->d || shape->stride_n % 8 || shape->stride_h % 8 ||
+      shape->stride_b % 8 || shape->stride_h < 0 || shape->stride_b < 0)
+    return fail(BSA_ERR_INVALID_ARG, "strides must be multiples of 8 elements (n >= d)");
+  if (n_sub < 0 || n_sub > shape->N)
+    return fail(BSA_ERR_INVALID_ARG, "n_sub=%d outside [0, N=%d]", n_sub, shape->N);
+  BSA_TRY(check_ptr(X, "X"));
+  BSA_TRY(check_ptr(centroids, "centroids", 16));
+  BSA_TRY(check_ptr(rho, "rho", 4));
+  if (n_sub > 0) BSA_TRY(check_ptr(subset, "subset", 4));
+  BSA_TRY(check_ptr(workspace, "workspace", 16));
+  const int64_t need = bsa_cluster_workspace_bytes(shape, p);
+  if (workspace_bytes < need)
+    return fail(BSA_ERR_CAPACITY, "workspace %lld bytes < required %lld",
+                (long long)workspace_bytes, (long long)need);
+  if (cells > INT32_MAX / 2) return fail(BSA_ERR_UNSUPPORTED, "too many cells");
+  bsa::ClusterArgs a{};
+  a.X = X;
+  a.sb = shape->stride_b;
+  a.sh = shape->stride_h;
+  a.sn = shape->stride_n;
+  a.H = shape->H;
+  a.N = shape->N;
+  a.D = shape->d;
+  a.T = p->T;
+  a.Hg = p->Hg;
+  a.W = p->W;
+  a.kt = p->kt;
+  a.kh = p->kh;
+  a.kw = p->kw;
+  a.Kt = (int)cdiv(p->T, p->kt);
+  a.Kh = (int)cdiv(p->Hg, p->kh);
+  a.Kw = (int)cdiv(p->W, p->kw);
+  a.Nc = (int)cells;
+  a.wt = std::min(p->wt, a.Kt);
+  a.wh = std::min(p->wh, a.Kh);
+  a.ww = std::min(p->ww, a.Kw);
+  a.mu = (float*)centroids;  // read only in this pass
+  a.norm = (float*)workspace;
+  a.rho = rho;
+  return hip_status(bsa::launch_lowe(a, shape->B * shape->H, n_sub, subset, (hipStream_t)stream),
+                    "lowe launch");
 }
 
 int64_t bsa_cluster_permute_workspace_bytes(const bsa_shape* shape,

@@ -156,6 +156,8 @@ struct ClusterArgs {
   float* mu;           // [BH, Nc, D]
   float* norm;         // [BH, Nc] squared norms of the centroids (workspace)
   int32_t* counts;     // [BH, Nc]
+  float* rho;          // [BH, N] Lowe's ratio (ratio pass only)
+  uint16_t* mu3;       // [BH, Nc, 3, D] bf16 hi, mid, lo parts of the centroids (workspace)
 };
 
 // Attention over cluster-induced blocks (padded cluster order).
@@ -270,6 +272,7 @@ hipError_t launch_cluster_permute(const ClusterArgs& a, int BH, const int32_t* g
 hipError_t launch_cluster_attn_plan(const ClusterAttnArgs& a, int BH, int D, hipStream_t s);
 hipError_t launch_cluster_attn_emit(const ClusterAttnArgs& a, int BH, int D, hipStream_t s);
 hipError_t launch_cluster_merge(const ClusterMergeArgs& a, int BH, hipStream_t s);
+hipError_t launch_lowe(const ClusterArgs& a, int BH, int n_sub, int32_t* subset, hipStream_t s);
 hipError_t launch_cluster_attn_scatter(const ClusterAttnArgs& a, int BH, int D, bool out_bf16,
                                        hipStream_t s);
 hipError_t launch_rectify(const RectifyArgs& a, int BH, int D, bool out_bf16, hipStream_t s);

@@ -59,7 +59,12 @@ __global__ __launch_bounds__(D) void cluster_init_kernel(ClusterArgs a) {
   }
 }
 
-template <int D>
+// LOWE: instead of the assignment, Lowe's ratio (HVA Eq. 6) of every token
+// over the same candidates: the two smallest ||mu||^2 - 2 x.mu pick the
+// nearest and the nearest other centroid, whose distances are then taken
+// directly as sum (x - mu)^2 (the short form cancels when a token sits on a
+// centroid); rho = d_1 / d_2, 0 with a single candidate, 1 when d_2 is 0.
+template <int D, bool LOWE = false>
 __global__ __launch_bounds__(512) void cluster_assign_kernel(ClusterArgs a) {
   __shared__ __attribute__((aligned(16))) float cm[kCandChunk][D];
   __shared__ float cn[kCandChunk];
@@ -101,8 +106,8 @@ __global__ __launch_bounds__(512) void cluster_assign_kernel(ClusterArgs a) {
 #pragma unroll
       for (int e = 0; e < D; ++e) x[e] = 0.f;
     }
-    float best = INFINITY;
-    int best_u = -1;
+    float best = INFINITY, second = INFINITY;
+    int best_u = -1, second_u = -1;
     for (int c0 = 0; c0 < ncand; c0 += kCandChunk) {
       const int nc = min(kCandChunk, ncand - c0);
       __syncthreads();  // the previous chunk is no longer read
@@ -129,13 +134,247 @@ __global__ __launch_bounds__(512) void cluster_assign_kernel(ClusterArgs a) {
           dot = __builtin_fmaf(x[e + 3], m[3], dot);
         }
         const float dist = __builtin_fmaf(-2.f, dot, cn[c]);
+        if constexpr (LOWE) {
+          if (dist < best) {
+            second = best;
+            second_u = best_u;
+          } else if (dist < second) {
+            second = dist;
+            second_u = cid[c];
+          }
+        }
         if (dist < best) {  // candidates ascend: ties keep the lower index
           best = dist;
           best_u = cid[c];
         }
       }
     }
-    if (has) a.assign[bh * a.N + tok] = best_u;
+    if constexpr (LOWE) {
+      if (has) {
+        float r = 0.f;
+        if (ncand > 1) {
+          const float* m1 = mu + (int64_t)best_u * D;
+          const float* m2 = mu + (int64_t)second_u * D;
+          float d1 = 0.f, d2 = 0.f;
+#pragma unroll
+          for (int e = 0; e < D; e += 4) {
+            const f32x4 p1 = *(const f32x4*)(m1 + e), p2 = *(const f32x4*)(m2 + e);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              const float u1 = x[e + q] - p1[q], u2 = x[e + q] - p2[q];
+              d1 = __builtin_fmaf(u1, u1, d1);
+              d2 = __builtin_fmaf(u2, u2, d2);
+            }
+          }
+          r = d2 > 0.f ? sqrtf(d1 / d2) : 1.f;
+          if (!(r > 0.f)) r = 0.f;  // +0: the subset search orders the bit patterns
+        }
+        a.rho[bh * a.N + tok] = r;
+      }
+    } else {
+      if (has) a.assign[bh * a.N + tok] = best_u;
+    }
+  }
+}
+
+// Every centroid as three bf16 parts hi + mid + lo: hi = bf16(mu), mid =
+// bf16(mu - hi), lo = bf16(mu - hi - mid) (each difference exact in fp32),
+// which carry the float32 value.  Token vectors are bf16, so the products
+// of the matrix-core assignment are exact and only its float32 sums round.
+template <int D>
+__global__ __launch_bounds__(D) void centroid_split_kernel(ClusterArgs a) {
+  const int u = blockIdx.x;
+  const int64_t bh = blockIdx.y;
+  const int e = threadIdx.x;
+  const float v = a.mu[(bh * a.Nc + u) * D + e];
+  const uint16_t hi = f32_to_bf16_bits(v);
+  const float r = v - bf16_bits_to_f32(hi);
+  const uint16_t mid = f32_to_bf16_bits(r);
+  const uint16_t lo = f32_to_bf16_bits(r - bf16_bits_to_f32(mid));
+  uint16_t* o = a.mu3 + (bh * a.Nc + u) * 3 * D;
+  o[e] = hi;
+  o[D + e] = mid;
+  o[2 * D + e] = lo;
+}
+
+// Assignment on the matrix cores: one workgroup per cell, one wave per 32
+// tokens (B operand: the token's bf16 row, held in registers); the window's
+// centroids are staged 32 at a time in LDS as their three bf16 parts (A
+// operand, 16-byte pieces XOR-swizzled by row), and S^T = mu x^T accumulates
+// hi, mid and lo products in float32 (32x32x16 bf16).  A lane then holds 16
+// candidates of one token (its lane pair the other 16): distance ||mu||^2 -
+// 2 S, lowest (distance, index) wins, so ties keep the lower index.
+template <int D>
+__global__ __launch_bounds__(1024) void cluster_assign_mfma_kernel(ClusterArgs a) {
+  constexpr int DC = D / 8;   // 16-byte pieces per row
+  constexpr int KS = D / 16;  // k-steps
+  __shared__ __attribute__((aligned(16))) uint16_t cm[3 * 32 * D];
+  __shared__ __attribute__((aligned(16))) float cn[32];
+  __shared__ int cid[32];
+  const int u = blockIdx.x;
+  const int64_t bh = blockIdx.y;
+  const int b = (int)(bh / a.H), h = (int)(bh % a.H);
+  const int uw = u % a.Kw, uh = (u / a.Kw) % a.Kh, ut = u / (a.Kw * a.Kh);
+  const int st = win_start(ut, a.wt, a.Kt), sh = win_start(uh, a.wh, a.Kh),
+            sw = win_start(uw, a.ww, a.Kw);
+  const int ncand = a.wt * a.wh * a.ww;
+  const int t0 = ut * a.kt, h0 = uh * a.kh, w0 = uw * a.kw;
+  const int lt = min(a.kt, a.T - t0), lh = min(a.kh, a.Hg - h0), lw = min(a.kw, a.W - w0);
+  const int ntok = lt * lh * lw;
+  const uint16_t* Xh = a.X + (int64_t)b * a.sb + (int64_t)h * a.sh;
+  const uint16_t* m3 = a.mu3 + bh * a.Nc * 3 * D;
+  const float* nrm = a.norm + bh * a.Nc;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int nwaves = blockDim.x >> 6;
+  const int n = lane & 31, g = lane >> 5;
+
+  for (int tb = 0; tb < ntok; tb += 32 * nwaves) {
+    const int p = tb + 32 * wave + n;  // this lane's token (column n)
+    const bool active = tb + 32 * wave < ntok;  // wave-uniform
+    int64_t tok = 0;
+    bf16x8 xf[KS];
+#pragma unroll
+    for (int s2 = 0; s2 < KS; ++s2) xf[s2] = bf16x8{};
+    if (p < ntok) {
+      const int pt = p / (lh * lw), ph = (p / lw) % lh, pw = p % lw;
+      tok = ((int64_t)(t0 + pt) * a.Hg + (h0 + ph)) * a.W + (w0 + pw);
+      const uint16_t* xr = Xh + tok * a.sn + 8 * g;
+#pragma unroll
+      for (int s2 = 0; s2 < KS; ++s2)
+        xf[s2] = __builtin_bit_cast(bf16x8, *(const u32x4*)(xr + 16 * s2));
+    }
+    float best = INFINITY;
+    int best_u = 0x7fffffff;
+    for (int c0 = 0; c0 < ncand; c0 += 32) {
+      const int nc = min(32, ncand - c0);
+      __syncthreads();  // the previous chunk is no longer read
+      for (int f = tid; f < 3 * 32 * DC; f += blockDim.x) {
+        const int part = f / (32 * DC), m = (f / DC) % 32, c = f % DC;
+        u32x4 v = {0u, 0u, 0u, 0u};
+        int vid = 0;
+        if (m < nc) {
+          const int k = c0 + m;
+          const int vw = sw + k % a.ww, vh = sh + (k / a.ww) % a.wh, vt = st + k / (a.ww * a.wh);
+          vid = (vt * a.Kh + vh) * a.Kw + vw;
+          v = *(const u32x4*)(m3 + ((int64_t)vid * 3 + part) * D + 8 * c);
+        }
+        *(u32x4*)&cm[(part * 32 + m) * D + ((c ^ (m % DC)) * 8)] = v;
+        if (part == 0 && c == 0) {
+          cn[m] = m < nc ? nrm[vid] : 0.f;
+          cid[m] = m < nc ? vid : 0x7fffffff;
+        }
+      }
+      __syncthreads();
+      if (!active) continue;
+      f32x16 acc;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[r] = 0.f;
+#pragma unroll
+      for (int part = 0; part < 3; ++part)
+#pragma unroll
+        for (int s2 = 0; s2 < KS; ++s2) {
+          const bf16x8 af = *(const bf16x8*)&cm[(part * 32 + n) * D + (((2 * s2 + g) ^ (n % DC)) * 8)];
+          acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, xf[s2], acc, 0, 0, 0);
+        }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const f32x4 nn = *(const f32x4*)&cn[8 * j + 4 * g];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int m = 8 * j + 4 * g + q;
+          const float dist = __builtin_fmaf(-2.f, acc[4 * j + q], nn[q]);
+          const int id = cid[m];
+          if (m < nc && (dist < best || (dist == best && id < best_u))) {
+            best = dist;
+            best_u = id;
+          }
+        }
+      }
+    }
+    if (!active) continue;
+    // the other 16 candidates of this token sit in lane n ^ 32
+    const float ob = __shfl_xor(best, 32);
+    const int ou = __shfl_xor(best_u, 32);
+    if (ob < best || (ob == best && ou < best_u)) best_u = ou;
+    if (g == 0 && p < ntok) a.assign[bh * a.N + tok] = best_u;
+  }
+}
+
+// Squared norms of given centroids (for the ratio pass).
+template <int D>
+__global__ __launch_bounds__(D) void centroid_norm_kernel(ClusterArgs a) {
+  __shared__ float red[D / 64];
+  const int u = blockIdx.x;
+  const int64_t bh = blockIdx.y;
+  const int e = threadIdx.x;
+  const float v = a.mu[(bh * a.Nc + u) * D + e];
+  const float sq = wave_sum(v * v);
+  if ((e & 63) == 0) red[e >> 6] = sq;
+  __syncthreads();
+  if (e == 0) {
+    float s = 0.f;
+    for (int k = 0; k < D / 64; ++k) s += red[k];
+    a.norm[bh * a.Nc + u] = s;
+  }
+}
+
+// The n_sub tokens of largest ratio per head (equal ratios to the lower
+// index), ascending: the threshold is found by a bitwise descent over the
+// ratios' bit patterns (order-preserving for values >= 0), then the tokens
+// above it and the first of those equal to it are compacted in token order.
+// One workgroup of 1024 per head.
+__global__ __launch_bounds__(1024) void lowe_subset_kernel(ClusterArgs a, int n_sub,
+                                                           int32_t* subset) {
+  __shared__ int red[16];
+  __shared__ int wc[2][16];
+  const int64_t bh = blockIdx.x;
+  const float* r = a.rho + bh * a.N;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  auto block_count = [&](int c) {
+    c = wave_sum(c);
+    if (lane == 0) red[wave] = c;
+    __syncthreads();
+    int tot = 0;
+    for (int w = 0; w < 16; ++w) tot += red[w];
+    __syncthreads();
+    return tot;
+  };
+  uint32_t T = 0;
+  for (int bit = 31; bit >= 0 && n_sub > 0; --bit) {
+    const uint32_t cand = T | (1u << bit);
+    int c = 0;
+    for (int i = tid; i < a.N; i += 1024) c += __float_as_uint(r[i]) >= cand ? 1 : 0;
+    if (block_count(c) >= n_sub) T = cand;
+  }
+  int c = 0;
+  for (int i = tid; i < a.N; i += 1024) c += __float_as_uint(r[i]) > T ? 1 : 0;
+  const int need_eq = n_sub - block_count(c);
+  int done = 0, eq_done = 0;
+  for (int i0 = 0; i0 < a.N && done < n_sub; i0 += 1024) {
+    const int i = i0 + tid;
+    const uint32_t key = i < a.N ? __float_as_uint(r[i]) : 0u;
+    const bool gt = i < a.N && key > T, eq = i < a.N && key == T;
+    const uint64_t beq = __ballot(eq);
+    if (lane == 0) wc[0][wave] = __popcll(beq);
+    __syncthreads();
+    int eq_before = eq_done + __popcll(beq & ((1ull << lane) - 1ull)), eq_tot = 0;
+    for (int w = 0; w < 16; ++w) {
+      if (w < wave) eq_before += wc[0][w];
+      eq_tot += wc[0][w];
+    }
+    const bool sel = gt || (eq && eq_before < need_eq);
+    const uint64_t bsel = __ballot(sel);
+    if (lane == 0) wc[1][wave] = __popcll(bsel);
+    __syncthreads();
+    int pos = done + __popcll(bsel & ((1ull << lane) - 1ull)), tot = 0;
+    for (int w = 0; w < 16; ++w) {
+      if (w < wave) pos += wc[1][w];
+      tot += wc[1][w];
+    }
+    if (sel && pos < n_sub) subset[bh * n_sub + pos] = i;
+    done += tot;
+    eq_done += eq_tot;
+    __syncthreads();  // wc is rewritten by the next chunk
   }
 }
 
@@ -280,6 +519,21 @@ __global__ __launch_bounds__(256) void cluster_permute_kernel(ClusterArgs a,
 
 }  // namespace
 
+hipError_t launch_lowe(const ClusterArgs& a, int BH, int n_sub, int32_t* subset, hipStream_t s) {
+  const dim3 grid(a.Nc, BH);
+  const int ctok = a.kt * a.kh * a.kw;
+  const int threads = min(512, ((ctok + 63) / 64) * 64);
+  if (a.D == 128) {
+    hipLaunchKernelGGL(centroid_norm_kernel<128>, grid, dim3(128), 0, s, a);
+    hipLaunchKernelGGL((cluster_assign_kernel<128, true>), grid, dim3(threads), 0, s, a);
+  } else {
+    hipLaunchKernelGGL(centroid_norm_kernel<64>, grid, dim3(64), 0, s, a);
+    hipLaunchKernelGGL((cluster_assign_kernel<64, true>), grid, dim3(threads), 0, s, a);
+  }
+  hipLaunchKernelGGL(lowe_subset_kernel, dim3(BH), dim3(1024), 0, s, a, n_sub, subset);
+  return hipGetLastError();
+}
+
 hipError_t launch_cluster_permute(const ClusterArgs& a, int BH, const int32_t* gofs,
                                   int32_t* perm, int32_t* offsets, hipStream_t s) {
   hipLaunchKernelGGL(cluster_permute_kernel, dim3(a.Nc, BH), dim3(256), 0, s, a, gofs, perm,
@@ -291,16 +545,21 @@ hipError_t launch_cluster(const ClusterArgs& a, int BH, int iters, hipStream_t s
   const dim3 grid(a.Nc, BH);
   const int ctok = a.kt * a.kh * a.kw;
   const int threads = min(512, ((ctok + 63) / 64) * 64);
+  // one wave per 32 tokens of a cell, at most 16
+  const int mthreads = 64 * min(16, (ctok + 31) / 32);
+  (void)threads;
   if (a.D == 128) {
     hipLaunchKernelGGL(cluster_init_kernel<128>, grid, dim3(128), 0, s, a);
     for (int it = 0; it < iters; ++it) {
-      hipLaunchKernelGGL(cluster_assign_kernel<128>, grid, dim3(threads), 0, s, a);
+      hipLaunchKernelGGL(centroid_split_kernel<128>, grid, dim3(128), 0, s, a);
+      hipLaunchKernelGGL(cluster_assign_mfma_kernel<128>, grid, dim3(mthreads), 0, s, a);
       hipLaunchKernelGGL(cluster_update_kernel<128>, grid, dim3(256), 0, s, a);
     }
   } else {
     hipLaunchKernelGGL(cluster_init_kernel<64>, grid, dim3(64), 0, s, a);
     for (int it = 0; it < iters; ++it) {
-      hipLaunchKernelGGL(cluster_assign_kernel<64>, grid, dim3(threads), 0, s, a);
+      hipLaunchKernelGGL(centroid_split_kernel<64>, grid, dim3(64), 0, s, a);
+      hipLaunchKernelGGL(cluster_assign_mfma_kernel<64>, grid, dim3(mthreads), 0, s, a);
       hipLaunchKernelGGL(cluster_update_kernel<64>, grid, dim3(256), 0, s, a);
     }
   }

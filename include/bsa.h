@@ -18,6 +18,7 @@
  *                         front end of cluster-induced blocks).
  *   bsa_cluster_permute   tokens in cluster order (HVA Eq. 1).
  *   bsa_cluster_select    key clusters per query cluster (HVA Eq. 2-3).
+ *   bsa_lowe_ratio_subset Lowe's ratio and the most ambiguous tokens (HVA Eq. 6).
  *   bsa_cluster_merge     merging of query clusters by tiled cost (HVA Alg. 1).
  *   bsa_cluster_attn_fwd  attention over cluster-induced blocks (HVA Eq. 4).
  *   bsa_omission_risk     per-head share of the full softmax mass a sparse
@@ -347,11 +348,13 @@ bsa_status bsa_pooled_rectify(const uint16_t* Q, const uint16_t* K,
  * assign: int32 [B, H, N], the last iteration's centroid of every token.
  * centroids: float32 [B, H, cells, d] after the last update.
  * counts: int32 [B, H, cells], tokens per centroid in the last assignment.
- * workspace: >= bsa_cluster_workspace_bytes bytes (the centroids' squared
- *   norms).
- * Precision: distances as ||mu||^2 - 2 x.mu in float32 (near-ties within
- *   float32 rounding may resolve either way); centroid sums in float32 in
- *   token order, so repeated calls give identical results.
+ * workspace: >= bsa_cluster_workspace_bytes bytes, 16-byte aligned (the
+ *   centroids' squared norms and their three bf16 parts).
+ * Precision: distances as ||mu||^2 - 2 x.mu with x.mu from bf16 matrix
+ *   products of the bf16 token and the centroid split exactly into three
+ *   bf16 parts, summed in float32 (near-ties within float32 rounding may
+ *   resolve either way); centroid sums in float32 in token order, so
+ *   repeated calls give identical results.
  * ---------------------------------------------------------------------- */
 typedef struct bsa_cluster_params {
   int32_t T, Hg, W;     /* token lattice, T * Hg * W == N                  */
@@ -422,6 +425,31 @@ bsa_status bsa_cluster_select(const float* mu_q, const float* mu_k,
                               int64_t col_cap, int64_t* out_nnz,
                               void* workspace, int64_t workspace_bytes,
                               void* stream);
+
+/* ------------------------------------------------------------------------
+ * bsa_lowe_ratio_subset -- Lowe's ratio of every token and the subset of the
+ * most ambiguous ones (HyperVAttention section 4.2, Eq. 6): per token,
+ *   rho = d_1 / d_2,
+ * d_1 its Euclidean distance to the nearest of the given centroids and d_2
+ * to the nearest other one, both over the centroids of its local window
+ * (the candidates of bsa_local_window_cluster with the same params; 0 with
+ * a single candidate, 1 when d_2 = 0).  Then, per (b, h), the n_sub tokens
+ * of largest rho (equal ratios to the lower token index), ascending: the
+ * subset the page re-assigns against all centroids between full
+ * clusterings (the page caches the top 15%).  Distances in float32 as
+ * ||mu||^2 - 2 x.mu + ||x||^2.
+ *
+ * X, shape, params: as bsa_local_window_cluster (params->iters unused, >= 1).
+ * centroids: float32 [B, H, Nc, d] (typically bsa_local_window_cluster's).
+ * n_sub: 0 .. N.  rho (out): float32 [B, H, N].  subset (out): int32
+ *   [B, H, n_sub] (may be NULL when n_sub = 0).
+ * workspace: >= bsa_cluster_workspace_bytes(shape, params) bytes.
+ * ---------------------------------------------------------------------- */
+bsa_status bsa_lowe_ratio_subset(const uint16_t* X, const bsa_shape* shape,
+                                 const bsa_cluster_params* params,
+                                 const float* centroids, int32_t n_sub,
+                                 float* rho, int32_t* subset, void* workspace,
+                                 int64_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------
  * bsa_cluster_merge -- hardware-aware merging of query clusters

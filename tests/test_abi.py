@@ -258,7 +258,9 @@ def test_cluster_validation():
     s = _shape(B=1, H=2, N=3 * 8 * 10)
     cp = bsa._ClusterParams(3, 8, 10, 1, 3, 4, 2, 2, 2, 1)
     assert bsa._lib.bsa_cluster_cells(ctypes.byref(s), ctypes.byref(cp)) == 3 * 3 * 3
-    assert bsa._lib.bsa_cluster_workspace_bytes(ctypes.byref(s), ctypes.byref(cp)) == 256
+    # norms (2 heads x 27 cells) + three bf16 parts of every centroid
+    assert bsa._lib.bsa_cluster_workspace_bytes(ctypes.byref(s), ctypes.byref(cp)) == \
+        256 + 2 * 27 * 3 * 128 * 2
     bad = bsa._ClusterParams(3, 8, 11, 1, 3, 4, 2, 2, 2, 1)   # 264 != 240 tokens
     assert bsa._lib.bsa_cluster_cells(ctypes.byref(s), ctypes.byref(bad)) == -1
     assert "lattice" in bsa.bsa_last_error()
@@ -319,3 +321,22 @@ def test_cluster_attention_and_merge_validation_and_workspace():
     assert st == 1 and "tau" in bsa.bsa_last_error()
     st = L.bsa_cluster_merge(p, p, p, p, 1, 2, 1000, Nq, Nk, p, 3, 64, 64, 16, p, p, mw - 1, None)
     assert st == 3 and "workspace" in bsa.bsa_last_error()
+
+
+def test_lowe_ratio_validation():
+    L = bsa._lib
+    s = _shape(B=1, H=2, N=3 * 8 * 10)
+    cp = bsa._ClusterParams(3, 8, 10, 1, 3, 4, 2, 2, 2, 1)
+    p = ctypes.c_void_p(4096)
+    st = L.bsa_lowe_ratio_subset(p, ctypes.byref(s), ctypes.byref(cp), p, 241, p, p, p, 256, None)
+    assert st == 1 and "n_sub" in bsa.bsa_last_error()
+    st = L.bsa_lowe_ratio_subset(p, ctypes.byref(s), ctypes.byref(cp), p, -1, p, p, p, 256, None)
+    assert st == 1 and "n_sub" in bsa.bsa_last_error()
+    st = L.bsa_lowe_ratio_subset(p, ctypes.byref(s), ctypes.byref(cp), p, 36, p, None, p, 256,
+                                 None)
+    assert st == 1 and "subset is NULL" in bsa.bsa_last_error()
+    st = L.bsa_lowe_ratio_subset(p, ctypes.byref(s), ctypes.byref(cp), p, 36, p, p, p, 255, None)
+    assert st == 3 and "workspace" in bsa.bsa_last_error()
+    st = L.bsa_lowe_ratio_subset(p, ctypes.byref(s), ctypes.byref(cp), None, 36, p, p, p, 256,
+                                 None)
+    assert st == 1 and "centroids is NULL" in bsa.bsa_last_error()

@@ -428,3 +428,76 @@ def test_cluster_pipeline_with_merging():
                                            ok_o, grows, 1 / math.sqrt(d))
     PT.compare_o_lse(Og[0, 0], Lg[0, 0], Oref, Lref, "pipeline with merging")
     assert int(pairs.item()) == O.packed_tile_pairs(oq_o, ok_o, groups, grows, 64, 16)
+
+
+# ------------------------------------------------------------ Lowe's ratio
+
+# The two distances of a ratio are float32 sums of d <= 128 squared
+# differences: a relative error of about d * 2^-24 ~ 1e-5 on each squared
+# distance, about 1e-5 on rho in [0, 1] (a second-nearest centroid picked
+# among candidates within float32 rounding of each other moves d_2 by less).
+# 1e-4 leaves a tenfold margin.
+RHO_TOL = 1e-4
+
+
+def _lowe_case(X, thw, cell, window, iters, frac):
+    """GPU ratios against the oracle's on the GPU's own float32 centroids
+    (so the clustering's decisions do not enter), and the subset against the
+    oracle's with the ratios within 2 RHO_TOL of the cut exempt."""
+    Xd = X.to(DEV)
+    _, mu, _ = bsa.bsa_local_window_cluster(Xd, thw, cell, window, iters)
+    rho, sub = bsa.bsa_lowe_ratio_subset(Xd, mu, thw, cell, window, frac)
+    torch.cuda.synchronize()
+    B, H, N, _ = X.shape
+    n = bsa.budget_blocks(frac, N)
+    assert sub.shape[2] == n
+    for h in range(H):
+        ro = O.lowe_ratios(X[0, h].double().numpy(), thw, cell, window,
+                           mu[0, h].double().cpu().numpy())
+        rg = rho[0, h].double().cpu().numpy()
+        err = np.abs(rg - ro).max()
+        assert err <= RHO_TOL, f"head {h}: max |d rho| {err}"
+        want = O.lowe_subset(ro, n)
+        got = sub[0, h].cpu().numpy()
+        assert np.all(np.diff(got) > 0), "subset not ascending"
+        if n:
+            cut = np.sort(ro)[::-1][n - 1]
+            diff = set(got.tolist()) ^ set(want.tolist())
+            assert all(abs(ro[i] - cut) <= 2 * RHO_TOL for i in diff), "subset differs off the tie band"
+        say(f"   head {h}: max |d rho| {err:.2e}, subset {n} of {N}")
+
+
+@pytest.mark.parametrize("grid,H,d,key,cell,window,iters", CASES)
+def test_lowe_ratio_small(grid, H, d, key, cell, window, iters):
+    spec = VideoSpec(1, H, d, grid, key)
+    Q, _, _ = gen_qkv(spec)
+    say("lowe", grid, cell, window)
+    _lowe_case(Q, grid, cell, window, iters, 0.15)
+
+
+def test_lowe_ratio_edges():
+    """A window of one cell (every ratio 0, the subset the lowest indices),
+    an empty and a full subset."""
+    spec = VideoSpec(1, 1, 64, (2, 6, 8), 181)
+    Q, _, _ = gen_qkv(spec)
+    Qd = Q.to(DEV)
+    thw, cell = (2, 6, 8), (1, 3, 4)
+    _, mu, _ = bsa.bsa_local_window_cluster(Qd, thw, cell, (1, 1, 1), 2)
+    rho, sub = bsa.bsa_lowe_ratio_subset(Qd, mu, thw, cell, (1, 1, 1), n_sub=10)
+    torch.cuda.synchronize()
+    assert bool((rho == 0).all()) and sub[0, 0].tolist() == list(range(10))
+    _, mu, _ = bsa.bsa_local_window_cluster(Qd, thw, cell, (2, 2, 2), 2)
+    rho0, sub0 = bsa.bsa_lowe_ratio_subset(Qd, mu, thw, cell, (2, 2, 2), n_sub=0)
+    rho1, sub1 = bsa.bsa_lowe_ratio_subset(Qd, mu, thw, cell, (2, 2, 2), n_sub=96)
+    torch.cuda.synchronize()
+    assert sub0.shape[2] == 0 and sub1[0, 0].tolist() == list(range(96))
+    assert torch.equal(rho0, rho1) and bool(((rho0 >= 0) & (rho0 <= 1)).all())
+
+
+def test_lowe_ratio_hunyuanvideo_layer():
+    """The 118,800-token HunyuanVideo lattice with the page's key grid (1215
+    cells), window (3, 8, 8), the page's top 15% (17,820 tokens)."""
+    spec = config_spec(3)
+    _, K, _ = gen_qkv(spec, heads=[0])
+    say("lowe on the HunyuanVideo key grid")
+    _lowe_case(K[:, :1], spec.grid, (11, 3, 3), (3, 8, 8), 2, 0.15)
