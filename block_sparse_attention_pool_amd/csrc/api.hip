@@ -119,6 +119,40 @@ MicroOrderPlan plan_micro_order(const bsa_shape* s) {
   return m;
 }
 
+// Tokens of a whole cell, and cells of a window (clipped to the grid).
+int64_t cell_tokens(const bsa_cluster_params* p) { return (int64_t)p->kt * p->kh * p->kw; }
+
+int64_t window_slots(const bsa_cluster_params* p) {
+  return std::min<int64_t>(p->wt, cdiv(p->T, p->kt)) * std::min<int64_t>(p->wh, cdiv(p->Hg, p->kh)) *
+         std::min<int64_t>(p->ww, cdiv(p->W, p->kw));
+}
+
+// Largest number of cells whose windows contain one cell, along one axis of
+// K cells with windows of w (shifted to stay inside the grid).
+int64_t max_covering(int64_t K, int64_t w) {
+  w = std::min(w, K);
+  int64_t best = 0;
+  for (int64_t v = 0; v < K; ++v) {
+    int64_t n = 0;
+    for (int64_t g = 0; g < K; ++g) {
+      const int64_t s = std::min(std::max(g - w / 2, (int64_t)0), K - w);
+      if (s <= v && v < s + w) ++n;
+    }
+    best = std::max(best, n);
+  }
+  return best;
+}
+
+// The bucketed centroid update keeps a cell's tokens, a window's slots and a
+// centroid's covering cells in LDS tables of fixed size.
+bool bucket_update_fits(const bsa_cluster_params* p) {
+  const int64_t cov = max_covering(cdiv(p->T, p->kt), p->wt) *
+                      max_covering(cdiv(p->Hg, p->kh), p->wh) *
+                      max_covering(cdiv(p->W, p->kw), p->ww);
+  return cell_tokens(p) <= bsa::kMaxBucketCell && window_slots(p) <= bsa::kMaxBucketSlots &&
+         cov <= bsa::kMaxBucketSlots;
+}
+
 bsa_status plan_cluster(const bsa_shape* s, const bsa_cluster_params* p, int64_t* cells) {
   if (s == nullptr || p == nullptr) return fail(BSA_ERR_INVALID_ARG, "shape or params is NULL");
   if (s->B < 1 || s->H < 1 || s->N < 1)
@@ -836,9 +870,13 @@ int64_t bsa_cluster_cells(const bsa_shape* shape, const bsa_cluster_params* para
 int64_t bsa_cluster_workspace_bytes(const bsa_shape* shape, const bsa_cluster_params* params) {
   int64_t cells = 0;
   if (plan_cluster(shape, params, &cells) != BSA_OK) return -1;
-  // centroid norms, then the centroids' three bf16 parts
-  return align256((int64_t)shape->B * shape->H * cells * 4) +
-         align256((int64_t)shape->B * shape->H * cells * 3 * shape->d * 2);
+  const int64_t BH = (int64_t)shape->B * shape->H;
+  // centroid norms, the centroids' three bf16 parts, then the update buckets
+  int64_t bytes = align256(BH * cells * 4) + align256(BH * cells * 3 * shape->d * 2);
+  if (bucket_update_fits(params))
+    bytes += align256(BH * cells * cell_tokens(params) * 4) +
+             align256(BH * cells * (window_slots(params) + 1) * 4);
+  return bytes;
 }
 
 bsa_status bsa_local_window_cluster(const uint16_t* X, const bsa_shape* shape,
@@ -884,7 +922,17 @@ bsa_status bsa_local_window_cluster(const uint16_t* X, const bsa_shape* shape,
   a.assign = assign;
   a.mu = centroids;
   a.norm = (float*)workspace;
-  a.mu3 = (uint16_t*)((char*)workspace + align256((int64_t)shape->B * shape->H * cells * 4));
+  {
+    const int64_t BH = (int64_t)shape->B * shape->H;
+    char* w = (char*)workspace + align256(BH * cells * 4);
+    a.mu3 = (uint16_t*)w;
+    w += align256(BH * cells * 3 * shape->d * 2);
+    if (bucket_update_fits(p)) {
+      a.bucket = (int32_t*)w;
+      w += align256(BH * cells * cell_tokens(p) * 4);
+      a.bstart = (int32_t*)w;
+    }
+  }
   a.counts = counts;
   return hip_status(bsa::launch_cluster(a, shape->B * shape->H, p->iters, (hipStream_t)stream),
                     "cluster launch");

@@ -158,7 +158,12 @@ struct ClusterArgs {
   int32_t* counts;     // [BH, Nc]
   float* rho;          // [BH, N] Lowe's ratio (ratio pass only)
   uint16_t* mu3;       // [BH, Nc, 3, D] bf16 hi, mid, lo parts of the centroids (workspace)
+  int32_t* bucket;     // [BH, Nc, kt*kh*kw] tokens of each cell by window slot, or NULL
+  int32_t* bstart;     // [BH, Nc, wt*wh*ww + 1] slot starts
 };
+// Bucketed update limits: tokens per cell and window slots.
+constexpr int kMaxBucketCell = 2048;
+constexpr int kMaxBucketSlots = 1023;
 
 // Attention over cluster-induced blocks (padded cluster order).
 struct ClusterAttnArgs {

@@ -461,6 +461,144 @@ __global__ __launch_bounds__(256) void cluster_update_kernel(ClusterArgs a) {
   }
 }
 
+// Update through per-cell buckets.  cell_bucket_kernel: one workgroup per
+// cell sorts the cell's tokens by the slot of their centroid in the cell's
+// window (a counting sort; ties in token order): bucket[c][...] holds token
+// indices, bstart[c][k] the start of slot k.  cluster_update_bucket_kernel:
+// one workgroup per centroid walks the cells whose windows contain it in
+// ascending order, gathers the tokens of its slot in each, and sums their
+// rows in that order -- a fixed order, so results do not vary from run to
+// run, and only member rows are read (the box scan reads an assignment for
+// every token of the box).
+__global__ __launch_bounds__(256) void cell_bucket_kernel(ClusterArgs a) {
+  __shared__ int slot[kMaxBucketCell];
+  __shared__ int hist[kMaxBucketSlots + 1];
+  const int c = blockIdx.x;
+  const int64_t bh = blockIdx.y;
+  const int uw = c % a.Kw, uh = (c / a.Kw) % a.Kh, ut = c / (a.Kw * a.Kh);
+  const int st = win_start(ut, a.wt, a.Kt), sh = win_start(uh, a.wh, a.Kh),
+            sw = win_start(uw, a.ww, a.Kw);
+  const int ncand = a.wt * a.wh * a.ww;
+  const int t0 = ut * a.kt, h0 = uh * a.kh, w0 = uw * a.kw;
+  const int lt = min(a.kt, a.T - t0), lh = min(a.kh, a.Hg - h0), lw = min(a.kw, a.W - w0);
+  const int ntok = lt * lh * lw;
+  const int cmax = a.kt * a.kh * a.kw;
+  const int32_t* asg = a.assign + bh * a.N;
+  const int tid = threadIdx.x;
+  for (int k = tid; k <= ncand; k += 256) hist[k] = 0;
+  __syncthreads();
+  for (int p = tid; p < ntok; p += 256) {
+    const int pt = p / (lh * lw), ph = (p / lw) % lh, pw = p % lw;
+    const int64_t tok = ((int64_t)(t0 + pt) * a.Hg + (h0 + ph)) * a.W + (w0 + pw);
+    const int v = asg[tok];
+    const int vw = v % a.Kw, vh = (v / a.Kw) % a.Kh, vt = v / (a.Kw * a.Kh);
+    const int k = ((vt - st) * a.wh + (vh - sh)) * a.ww + (vw - sw);
+    const bool in = vt >= st && vt < st + a.wt && vh >= sh && vh < sh + a.wh && vw >= sw &&
+                    vw < sw + a.ww;
+    slot[p] = in ? k : ncand;  // outside the window (never, for this clustering): dropped
+    atomicAdd(&hist[in ? k : ncand], 1);
+  }
+  __syncthreads();
+  if (tid == 0) {  // exclusive scan of at most kMaxBucketSlots counts
+    int run = 0;
+    for (int k = 0; k <= ncand; ++k) {
+      const int v = hist[k];
+      hist[k] = run;
+      run += v;
+    }
+  }
+  __syncthreads();
+  int32_t* bs = a.bstart + (bh * a.Nc + c) * (ncand + 1);
+  for (int k = tid; k <= ncand; k += 256) bs[k] = hist[k];
+  int32_t* bk = a.bucket + (bh * a.Nc + c) * cmax;
+  for (int p = tid; p < ntok; p += 256) {
+    const int k = slot[p];
+    if (k == ncand) continue;
+    int rank = 0;
+    for (int q = 0; q < p; ++q) rank += slot[q] == k ? 1 : 0;
+    const int pt = p / (lh * lw), ph = (p / lw) % lh, pw = p % lw;
+    bk[hist[k] + rank] = (int32_t)(((int64_t)(t0 + pt) * a.Hg + (h0 + ph)) * a.W + (w0 + pw));
+  }
+}
+
+template <int D>
+__global__ __launch_bounds__(256) void cluster_update_bucket_kernel(ClusterArgs a) {
+  __shared__ int cb0[kMaxBucketSlots], ccnt[kMaxBucketSlots], cofs[kMaxBucketSlots + 1];
+  __shared__ int ccell[kMaxBucketSlots];
+  __shared__ int list[1024];
+  __shared__ float red[4];
+  const int u = blockIdx.x;
+  const int64_t bh = blockIdx.y;
+  const int b = (int)(bh / a.H), h = (int)(bh % a.H);
+  const int uw = u % a.Kw, uh = (u / a.Kw) % a.Kh, ut = u / (a.Kw * a.Kh);
+  int glt, ght, glh, ghh, glw, ghw;
+  covering_cells(ut, a.wt, a.Kt, glt, ght);
+  covering_cells(uh, a.wh, a.Kh, glh, ghh);
+  covering_cells(uw, a.ww, a.Kw, glw, ghw);
+  const int nt = max(ght - glt + 1, 0), nh = max(ghh - glh + 1, 0), nw = max(ghw - glw + 1, 0);
+  const int ncov = nt * nh * nw;  // <= the window's cell count
+  const int ncand = a.wt * a.wh * a.ww;
+  const int cmax = a.kt * a.kh * a.kw;
+  const uint16_t* Xh = a.X + (int64_t)b * a.sb + (int64_t)h * a.sh;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // covering cells in ascending order; u's slot in each one's window
+  for (int i = tid; i < ncov; i += 256) {
+    const int gt = glt + i / (nh * nw), gh = glh + (i / nw) % nh, gw = glw + i % nw;
+    const int c = (gt * a.Kh + gh) * a.Kw + gw;
+    const int st = win_start(gt, a.wt, a.Kt), sh = win_start(gh, a.wh, a.Kh),
+              sw = win_start(gw, a.ww, a.Kw);
+    const int k = ((ut - st) * a.wh + (uh - sh)) * a.ww + (uw - sw);
+    const int32_t* bs = a.bstart + (bh * a.Nc + c) * (ncand + 1);
+    ccell[i] = c;
+    cb0[i] = bs[k];
+    ccnt[i] = bs[k + 1] - bs[k];
+  }
+  __syncthreads();
+  if (tid == 0) {
+    int run = 0;
+    for (int i = 0; i < ncov; ++i) {
+      cofs[i] = run;
+      run += ccnt[i];
+    }
+    cofs[ncov] = run;
+  }
+  __syncthreads();
+  const int count = cofs[ncov];
+  float acc = 0.f;  // thread e < D owns dimension e
+  for (int base = 0; base < count; base += 1024) {
+    const int nb = min(1024, count - base);
+    for (int j = tid; j < nb; j += 256) {
+      const int x = base + j;
+      int lo = 0, hi = ncov - 1;  // covering cell holding member x
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (cofs[mid] <= x) lo = mid;
+        else hi = mid - 1;
+      }
+      list[j] = a.bucket[(bh * a.Nc + ccell[lo]) * cmax + cb0[lo] + (x - cofs[lo])];
+    }
+    __syncthreads();
+    if (tid < D)
+      for (int j = 0; j < nb; ++j) acc += bf16_bits_to_f32(Xh[(int64_t)list[j] * a.sn + tid]);
+    __syncthreads();  // list is rewritten by the next batch
+  }
+  if (tid == 0) a.counts[bh * a.Nc + u] = count;
+  if (count == 0) return;  // the centroid keeps its position (and norm)
+  float v = 0.f;
+  if (tid < D) {
+    v = acc / (float)count;
+    a.mu[(bh * a.Nc + u) * D + tid] = v;
+  }
+  const float sq = wave_sum(tid < D ? v * v : 0.f);
+  if (lane == 0) red[wave] = sq;
+  __syncthreads();
+  if (tid == 0) {
+    float s2 = 0.f;
+    for (int k = 0; k < 4; ++k) s2 += red[k];
+    a.norm[bh * a.Nc + u] = s2;
+  }
+}
+
 // Eq. 1: the tokens of centroid u, in token order, at its place in the
 // head's permutation.  The same box of cells as the update is scanned; the
 // cluster's start comes from the scan of all heads' counts (minus the head's
@@ -548,19 +686,32 @@ hipError_t launch_cluster(const ClusterArgs& a, int BH, int iters, hipStream_t s
   // one wave per 32 tokens of a cell, at most 16
   const int mthreads = 64 * min(16, (ctok + 31) / 32);
   (void)threads;
+  // bucketed update when a cell's tokens and a window's slots fit the LDS
+  // tables (the workspace then holds the buckets), else the box scan
+  const bool buckets = a.bucket != nullptr;
   if (a.D == 128) {
     hipLaunchKernelGGL(cluster_init_kernel<128>, grid, dim3(128), 0, s, a);
     for (int it = 0; it < iters; ++it) {
       hipLaunchKernelGGL(centroid_split_kernel<128>, grid, dim3(128), 0, s, a);
       hipLaunchKernelGGL(cluster_assign_mfma_kernel<128>, grid, dim3(mthreads), 0, s, a);
-      hipLaunchKernelGGL(cluster_update_kernel<128>, grid, dim3(256), 0, s, a);
+      if (buckets) {
+        hipLaunchKernelGGL(cell_bucket_kernel, grid, dim3(256), 0, s, a);
+        hipLaunchKernelGGL(cluster_update_bucket_kernel<128>, grid, dim3(256), 0, s, a);
+      } else {
+        hipLaunchKernelGGL(cluster_update_kernel<128>, grid, dim3(256), 0, s, a);
+      }
     }
   } else {
     hipLaunchKernelGGL(cluster_init_kernel<64>, grid, dim3(64), 0, s, a);
     for (int it = 0; it < iters; ++it) {
       hipLaunchKernelGGL(centroid_split_kernel<64>, grid, dim3(64), 0, s, a);
       hipLaunchKernelGGL(cluster_assign_mfma_kernel<64>, grid, dim3(mthreads), 0, s, a);
-      hipLaunchKernelGGL(cluster_update_kernel<64>, grid, dim3(256), 0, s, a);
+      if (buckets) {
+        hipLaunchKernelGGL(cell_bucket_kernel, grid, dim3(256), 0, s, a);
+        hipLaunchKernelGGL(cluster_update_bucket_kernel<64>, grid, dim3(256), 0, s, a);
+      } else {
+        hipLaunchKernelGGL(cluster_update_kernel<64>, grid, dim3(256), 0, s, a);
+      }
     }
   }
   return hipGetLastError();

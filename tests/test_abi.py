@@ -258,9 +258,11 @@ def test_cluster_validation():
     s = _shape(B=1, H=2, N=3 * 8 * 10)
     cp = bsa._ClusterParams(3, 8, 10, 1, 3, 4, 2, 2, 2, 1)
     assert bsa._lib.bsa_cluster_cells(ctypes.byref(s), ctypes.byref(cp)) == 3 * 3 * 3
-    # norms (2 heads x 27 cells) + three bf16 parts of every centroid
+    # norms (2 heads x 27 cells), three bf16 parts of every centroid, the
+    # update buckets (12 tokens per cell) and their slot starts (8 + 1)
+    al = lambda n: -(-n // 256) * 256
     assert bsa._lib.bsa_cluster_workspace_bytes(ctypes.byref(s), ctypes.byref(cp)) == \
-        256 + 2 * 27 * 3 * 128 * 2
+        al(2 * 27 * 4) + al(2 * 27 * 3 * 128 * 2) + al(2 * 27 * 12 * 4) + al(2 * 27 * 9 * 4)
     bad = bsa._ClusterParams(3, 8, 11, 1, 3, 4, 2, 2, 2, 1)   # 264 != 240 tokens
     assert bsa._lib.bsa_cluster_cells(ctypes.byref(s), ctypes.byref(bad)) == -1
     assert "lattice" in bsa.bsa_last_error()
