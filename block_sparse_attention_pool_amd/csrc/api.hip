@@ -991,7 +991,14 @@ int64_t bsa_cluster_permute_workspace_bytes(const bsa_shape* shape,
                                             const bsa_cluster_params* params) {
   int64_t cells = 0;
   if (plan_cluster(shape, params, &cells) != BSA_OK) return -1;
-  return align256(((int64_t)shape->B * shape->H * cells + 1) * 4) + 256;
+  const int64_t BH = (int64_t)shape->B * shape->H;
+  // cluster starts, the scan total, then (bucketed path) the cell buckets,
+  // their slot starts and the flags of clusters too large for LDS
+  int64_t bytes = align256((BH * cells + 1) * 4) + 256;
+  if (bucket_update_fits(params))
+    bytes += align256(BH * cells * cell_tokens(params) * 4) +
+             align256(BH * cells * (window_slots(params) + 1) * 4) + align256(BH * cells * 4);
+  return bytes;
 }
 
 bsa_status bsa_cluster_permute(const int32_t* assign, const int32_t* counts,
@@ -1033,9 +1040,19 @@ bsa_status bsa_cluster_permute(const int32_t* assign, const int32_t* counts,
   hipStream_t st = (hipStream_t)stream;
   int32_t* gofs = (int32_t*)workspace;
   int64_t* total = (int64_t*)((char*)workspace + align256((rows + 1) * 4));
+  int32_t* big = nullptr;
+  if (bucket_update_fits(p)) {
+    char* w = (char*)workspace + align256((rows + 1) * 4) + 256;
+    a.bucket = (int32_t*)w;
+    w += align256(rows * cell_tokens(p) * 4);
+    a.bstart = (int32_t*)w;
+    w += align256(rows * (window_slots(p) + 1) * 4);
+    big = (int32_t*)w;
+  }
   BSA_TRY(hip_status(bsa::launch_scan(counts, (int)rows, gofs, total, st), "scan launch"));
-  return hip_status(bsa::launch_cluster_permute(a, shape->B * shape->H, gofs, perm, offsets, st),
-                    "permute launch");
+  return hip_status(
+      bsa::launch_cluster_permute(a, shape->B * shape->H, gofs, perm, offsets, big, st),
+      "permute launch");
 }
 
 int64_t bsa_cluster_select_workspace_bytes(int32_t B, int32_t H, int32_t Nq, int32_t Nk) {

@@ -273,7 +273,7 @@ hipError_t launch_merge(const MergeArgs& a, int B, bool bf16, hipStream_t s);
 hipError_t launch_risk(const RiskArgs& a, hipStream_t s);
 hipError_t launch_cluster(const ClusterArgs& a, int BH, int iters, hipStream_t s);
 hipError_t launch_cluster_permute(const ClusterArgs& a, int BH, const int32_t* gofs,
-                                  int32_t* perm, int32_t* offsets, hipStream_t s);
+                                  int32_t* perm, int32_t* offsets, int32_t* big, hipStream_t s);
 hipError_t launch_cluster_attn_plan(const ClusterAttnArgs& a, int BH, int D, hipStream_t s);
 hipError_t launch_cluster_attn_emit(const ClusterAttnArgs& a, int BH, int D, hipStream_t s);
 hipError_t launch_cluster_merge(const ClusterMergeArgs& a, int BH, hipStream_t s);

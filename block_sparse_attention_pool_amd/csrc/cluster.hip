@@ -521,28 +521,20 @@ __global__ __launch_bounds__(256) void cell_bucket_kernel(ClusterArgs a) {
   }
 }
 
-template <int D>
-__global__ __launch_bounds__(256) void cluster_update_bucket_kernel(ClusterArgs a) {
-  __shared__ int cb0[kMaxBucketSlots], ccnt[kMaxBucketSlots], cofs[kMaxBucketSlots + 1];
-  __shared__ int ccell[kMaxBucketSlots];
-  __shared__ int list[1024];
-  __shared__ float red[4];
-  const int u = blockIdx.x;
-  const int64_t bh = blockIdx.y;
-  const int b = (int)(bh / a.H), h = (int)(bh % a.H);
+// The cells whose windows contain centroid u, ascending, with u's slot range
+// in each one's bucket: ccell[i], cb0[i], and exclusive member offsets
+// cofs[0..ncov] (cofs[ncov] = members).  Block of 256 threads; returns ncov.
+__device__ int gather_covering(const ClusterArgs& a, int64_t bh, int u, int* ccell, int* cb0,
+                               int* ccnt, int* cofs) {
   const int uw = u % a.Kw, uh = (u / a.Kw) % a.Kh, ut = u / (a.Kw * a.Kh);
   int glt, ght, glh, ghh, glw, ghw;
   covering_cells(ut, a.wt, a.Kt, glt, ght);
   covering_cells(uh, a.wh, a.Kh, glh, ghh);
   covering_cells(uw, a.ww, a.Kw, glw, ghw);
   const int nt = max(ght - glt + 1, 0), nh = max(ghh - glh + 1, 0), nw = max(ghw - glw + 1, 0);
-  const int ncov = nt * nh * nw;  // <= the window's cell count
+  const int ncov = nt * nh * nw;
   const int ncand = a.wt * a.wh * a.ww;
-  const int cmax = a.kt * a.kh * a.kw;
-  const uint16_t* Xh = a.X + (int64_t)b * a.sb + (int64_t)h * a.sh;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  // covering cells in ascending order; u's slot in each one's window
-  for (int i = tid; i < ncov; i += 256) {
+  for (int i = threadIdx.x; i < ncov; i += blockDim.x) {
     const int gt = glt + i / (nh * nw), gh = glh + (i / nw) % nh, gw = glw + i % nw;
     const int c = (gt * a.Kh + gh) * a.Kw + gw;
     const int st = win_start(gt, a.wt, a.Kt), sh = win_start(gh, a.wh, a.Kh),
@@ -554,7 +546,7 @@ __global__ __launch_bounds__(256) void cluster_update_bucket_kernel(ClusterArgs 
     ccnt[i] = bs[k + 1] - bs[k];
   }
   __syncthreads();
-  if (tid == 0) {
+  if (threadIdx.x == 0) {
     int run = 0;
     for (int i = 0; i < ncov; ++i) {
       cofs[i] = run;
@@ -563,20 +555,40 @@ __global__ __launch_bounds__(256) void cluster_update_bucket_kernel(ClusterArgs 
     cofs[ncov] = run;
   }
   __syncthreads();
+  return ncov;
+}
+
+// Member x (0 <= x < cofs[ncov]) of the gathered covering cells.
+__device__ __forceinline__ int32_t covering_member(const ClusterArgs& a, int64_t bh, int ncov,
+                                                   const int* ccell, const int* cb0,
+                                                   const int* cofs, int x) {
+  int lo = 0, hi = ncov - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (cofs[mid] <= x) lo = mid;
+    else hi = mid - 1;
+  }
+  return a.bucket[(bh * a.Nc + ccell[lo]) * (a.kt * a.kh * a.kw) + cb0[lo] + (x - cofs[lo])];
+}
+
+template <int D>
+__global__ __launch_bounds__(256) void cluster_update_bucket_kernel(ClusterArgs a) {
+  __shared__ int cb0[kMaxBucketSlots], ccnt[kMaxBucketSlots], cofs[kMaxBucketSlots + 1];
+  __shared__ int ccell[kMaxBucketSlots];
+  __shared__ int list[1024];
+  __shared__ float red[4];
+  const int u = blockIdx.x;
+  const int64_t bh = blockIdx.y;
+  const int b = (int)(bh / a.H), h = (int)(bh % a.H);
+  const uint16_t* Xh = a.X + (int64_t)b * a.sb + (int64_t)h * a.sh;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int ncov = gather_covering(a, bh, u, ccell, cb0, ccnt, cofs);
   const int count = cofs[ncov];
   float acc = 0.f;  // thread e < D owns dimension e
   for (int base = 0; base < count; base += 1024) {
     const int nb = min(1024, count - base);
-    for (int j = tid; j < nb; j += 256) {
-      const int x = base + j;
-      int lo = 0, hi = ncov - 1;  // covering cell holding member x
-      while (lo < hi) {
-        const int mid = (lo + hi + 1) >> 1;
-        if (cofs[mid] <= x) lo = mid;
-        else hi = mid - 1;
-      }
-      list[j] = a.bucket[(bh * a.Nc + ccell[lo]) * cmax + cb0[lo] + (x - cofs[lo])];
-    }
+    for (int j = tid; j < nb; j += 256)
+      list[j] = covering_member(a, bh, ncov, ccell, cb0, cofs, base + j);
     __syncthreads();
     if (tid < D)
       for (int j = 0; j < nb; ++j) acc += bf16_bits_to_f32(Xh[(int64_t)list[j] * a.sn + tid]);
@@ -599,6 +611,48 @@ __global__ __launch_bounds__(256) void cluster_update_bucket_kernel(ClusterArgs 
   }
 }
 
+// Eq. 1 through the buckets: centroid u's members gathered from its covering
+// cells into LDS, each placed at its rank in token order (tokens are
+// distinct), so the output equals the box scan's.  A cluster with more than
+// kMaxPermMembers members takes the box scan below.
+constexpr int kMaxPermMembers = 2048;
+
+__global__ __launch_bounds__(256) void cluster_permute_bucket_kernel(ClusterArgs a,
+                                                                     const int32_t* gofs,
+                                                                     int32_t* perm,
+                                                                     int32_t* offsets,
+                                                                     int32_t* big) {
+  __shared__ int cb0[kMaxBucketSlots], ccnt[kMaxBucketSlots], cofs[kMaxBucketSlots + 1];
+  __shared__ int ccell[kMaxBucketSlots];
+  __shared__ int mem[kMaxPermMembers];
+  const int u = blockIdx.x;
+  const int64_t bh = blockIdx.y;
+  const int64_t base = gofs[bh * a.Nc];
+  const int start = (int)(gofs[bh * a.Nc + u] - base);
+  const int end = u + 1 < a.Nc ? (int)(gofs[bh * a.Nc + u + 1] - base) : a.N;
+  if (threadIdx.x == 0) {
+    offsets[bh * (a.Nc + 1) + u] = start;
+    if (u + 1 == a.Nc) offsets[bh * (a.Nc + 1) + a.Nc] = a.N;
+  }
+  const int ncov = gather_covering(a, bh, u, ccell, cb0, ccnt, cofs);
+  const int n = cofs[ncov];
+  if (n > kMaxPermMembers) {  // too many for LDS: the box scan handles it
+    if (threadIdx.x == 0) big[bh * a.Nc + u] = 1;
+    return;
+  }
+  if (threadIdx.x == 0) big[bh * a.Nc + u] = 0;
+  for (int j = threadIdx.x; j < n; j += blockDim.x)
+    mem[j] = covering_member(a, bh, ncov, ccell, cb0, cofs, j);
+  __syncthreads();
+  int32_t* pr = perm + bh * a.N;
+  for (int j = threadIdx.x; j < n; j += blockDim.x) {
+    const int t = mem[j];
+    int rank = 0;
+    for (int q = 0; q < n; ++q) rank += mem[q] < t ? 1 : 0;
+    if (start + rank < end) pr[start + rank] = t;
+  }
+}
+
 // Eq. 1: the tokens of centroid u, in token order, at its place in the
 // head's permutation.  The same box of cells as the update is scanned; the
 // cluster's start comes from the scan of all heads' counts (minus the head's
@@ -606,10 +660,12 @@ __global__ __launch_bounds__(256) void cluster_update_bucket_kernel(ClusterArgs 
 __global__ __launch_bounds__(256) void cluster_permute_kernel(ClusterArgs a,
                                                               const int32_t* gofs,
                                                               int32_t* perm,
-                                                              int32_t* offsets) {
+                                                              int32_t* offsets,
+                                                              const int32_t* big) {
   __shared__ int wcnt[4];
   const int u = blockIdx.x;
   const int64_t bh = blockIdx.y;
+  if (big != nullptr && big[bh * a.Nc + u] == 0) return;  // placed through the buckets
   const int uw = u % a.Kw, uh = (u / a.Kw) % a.Kh, ut = u / (a.Kw * a.Kh);
   const int64_t base = gofs[bh * a.Nc];
   const int start = (int)(gofs[bh * a.Nc + u] - base);
@@ -673,9 +729,19 @@ hipError_t launch_lowe(const ClusterArgs& a, int BH, int n_sub, int32_t* subset,
 }
 
 hipError_t launch_cluster_permute(const ClusterArgs& a, int BH, const int32_t* gofs,
-                                  int32_t* perm, int32_t* offsets, hipStream_t s) {
-  hipLaunchKernelGGL(cluster_permute_kernel, dim3(a.Nc, BH), dim3(256), 0, s, a, gofs, perm,
-                     offsets);
+                                  int32_t* perm, int32_t* offsets, int32_t* big, hipStream_t s) {
+  const dim3 grid(a.Nc, BH);
+  if (a.bucket != nullptr) {
+    hipLaunchKernelGGL(cell_bucket_kernel, grid, dim3(256), 0, s, a);
+    hipLaunchKernelGGL(cluster_permute_bucket_kernel, grid, dim3(256), 0, s, a, gofs, perm,
+                       offsets, big);
+    // clusters too large for LDS (rare): the box scan, which skips the rest
+    hipLaunchKernelGGL(cluster_permute_kernel, grid, dim3(256), 0, s, a, gofs, perm, offsets,
+                       (const int32_t*)big);
+  } else {
+    hipLaunchKernelGGL(cluster_permute_kernel, grid, dim3(256), 0, s, a, gofs, perm, offsets,
+                       (const int32_t*)nullptr);
+  }
   return hipGetLastError();
 }
 
