@@ -2,9 +2,10 @@
 """Benchmark of the block-sparse video-DiT attention hot path on one MI355X.
 
 One step = pooled scoring (bsa_score_blocks) + block selection
-(bsa_select_blocks) + block-sparse attention (bsa_sparse_attn_fwd, including
-its fp16 V^T staging), plus micro-tile selection, residual and LSE merge where
-the workload has them.  The default workload is one layer shaped like
+(bsa_select_blocks) + block-sparse attention (bsa_sparse_attn_fwd) and its
+fp16 V^T staging (bsa_attn_stage_v, on a second stream beside scoring and
+selection; ``--serial`` keeps one stream), plus micro-tile selection, residual
+and LSE merge where the workload has them.  The default workload is one layer shaped like
 Wan-2.1-1.3B at 480p: B=1, H=12, d=128, 21x30x52 = 32760 tokens, 64-token
 blocks, top-k at 25% density (k = 128 of 512 key blocks).  ``--config N``
 selects another of the five workloads (0 tiny reference, 1 the default,
@@ -79,6 +80,8 @@ def parse():
                     help="also run the cluster-induced block pipeline (local-window clustering, "
                          "permutation, cluster top-p 0.9 with the page's Min-kc, attention over "
                          "the clusters) and report its stages")
+    ap.add_argument("--serial", action="store_true",
+                    help="run every stage of a step on one stream (no overlap)")
     ap.add_argument("--calibration-copy", action="store_true",
                     help="first run a plain 256 MiB device copy (reads 256 MiB, writes "
                          "256 MiB) three times, to scale hardware byte counters")
@@ -244,11 +247,24 @@ def main():
             micro=dict(m=micro["m"], scale=scale, head_mask=micro["mask"], macro=(rp, ci),
                        qpool16=sc["qpool16"], kpool16=sc["kpool16"]))
 
-    def step(call=0):
+    main = torch.cuda.current_stream(dev)
+    aux = torch.cuda.Stream(device=dev)  # default priority
+
+    def step(call=0, overlap=not args.serial):
+        # The V^T staging runs on a second stream beside scoring and
+        # selection (running the micro branch beside the macro attention as
+        # well measured no gain: both fill the chip).
+        if overlap:
+            aux.wait_stream(main)
+            with torch.cuda.stream(aux):
+                bsa.bsa_attn_stage_v(V, workspace=ws)
         # the static window needs no scores: the selection runs on the mask alone
         sc = score() if (mode != "static" or micro) else {"scores": None}
         rp, ci, nnz = select(sc, call)
-        bsa.bsa_sparse_attn_fwd(Q, K, V, rp, ci, out=O_buf, lse=L_buf, workspace=ws)
+        if overlap:
+            main.wait_stream(aux)
+        bsa.bsa_sparse_attn_fwd(Q, K, None if overlap else V, rp, ci, out=O_buf, lse=L_buf,
+                                workspace=ws)
         if args.rectify:
             bsa.bsa_pooled_rectify(Q, K, V, rp, ci, O_buf, L_buf, workspace=ws_rect)
         mnnz = None
@@ -259,6 +275,15 @@ def main():
             bsa.bsa_lse_merge(O_buf, L_buf, Om_buf, Lm_buf, head_mask=micro["mask"],
                               out=O_buf, lse_out=L_buf)
         return sc, rp, ci, nnz, mnnz
+
+    # the two-stream step must give the one-stream step's bits
+    step(0, overlap=False)
+    ref = (O_buf.clone(), L_buf.clone())
+    step(0, overlap=True)
+    torch.cuda.synchronize()
+    if not (torch.equal(ref[0], O_buf) and torch.equal(ref[1], L_buf)):
+        raise RuntimeError("two-stream step differs from the one-stream step")
+    del ref
 
     for w in range(args.warmup):
         step(w)
@@ -521,6 +546,7 @@ def main():
                    "B": B, "H": H, "N": N, "d": d, "block": blk,
                    "selection": sel_desc,
                    "density": round(nnz_mean / (B * H * bsa.n_blocks(N) ** 2), 4)},
+        "step_streams": 1 if args.serial else 2,
         "attn_kernel_ms": round(attn_ms, 4),
         "attn_kernel_tflops": round(attn_tflops, 2),
         "attn_kernel_ms_cold_cache": round(attn_cold_ms, 4),

@@ -95,6 +95,7 @@ def _load(path: str = _LIB_PATH):
                                   I64, P], I32),
         "bsa_cluster_merge_workspace_bytes": ([I32, I32, I32, I32, I32, I32], I64),
         "bsa_lowe_ratio_subset": ([P, SP, CP, P, I32, P, P, P, I64, P], I32),
+        "bsa_attn_stage_v": ([P, SP, P, I64, P], I32),
         "bsa_cluster_merge": ([P, P, P, P, I32, I32, I32, I32, I32, P, I32, I32, I32, I32, P, P,
                                I64, P], I32),
         "bsa_cluster_select": ([P, P, P, I32, I32, I32, I32, I32, F32, F32, I32, I32, P, P, I64,
@@ -119,7 +120,8 @@ EXPORTED = ("bsa_version", "bsa_last_error", "bsa_score_blocks", "bsa_select_wor
             "bsa_cluster_permute_workspace_bytes", "bsa_cluster_permute",
             "bsa_cluster_select_workspace_bytes", "bsa_cluster_select",
             "bsa_cluster_attn_workspace_bytes", "bsa_cluster_attn_fwd",
-            "bsa_cluster_merge_workspace_bytes", "bsa_cluster_merge", "bsa_lowe_ratio_subset")
+            "bsa_cluster_merge_workspace_bytes", "bsa_cluster_merge", "bsa_lowe_ratio_subset",
+            "bsa_attn_stage_v")
 
 
 def library_path() -> str:
@@ -333,6 +335,16 @@ def bsa_sparse_attn_fwd(Q, K, V, row_ptr, col_idx, *, block: int = BLOCK,
                                   _ptr(ws), ws.numel(), _stream(stream, Q.device))
     _check(st, "bsa_sparse_attn_fwd")
     return O, L
+
+
+def bsa_attn_stage_v(V, *, workspace, stream=None):
+    """Stage the fp16 V^T of V [B,H,N,d] bf16 into an attention workspace, on
+    its own (the attention calls then take V=None)."""
+    shp = shape_of(V)
+    st = _lib.bsa_attn_stage_v(_ptr(V), ctypes.byref(shp), _ptr(workspace), workspace.numel(),
+                               _stream(stream, V.device))
+    _check(st, "bsa_attn_stage_v")
+    return workspace
 
 
 def bsa_dense_attn_fwd(Q, K, V, *, scale: float | None = None, out_dtype=torch.float32,

@@ -643,6 +643,31 @@ int64_t bsa_attn_workspace_bytes(const bsa_shape* shape) {
   return m.vt_bytes + m.order_bytes;
 }
 
+bsa_status bsa_attn_stage_v(const uint16_t* V, const bsa_shape* shape, void* workspace,
+                            int64_t workspace_bytes, void* stream) {
+  BSA_TRY(check_shape(shape));
+  BSA_TRY(check_ptr(V, "V"));
+  BSA_TRY(check_ptr(workspace, "workspace", 256));
+  const int64_t need = bsa_attn_workspace_bytes(shape);
+  if (workspace_bytes < need)
+    return fail(BSA_ERR_CAPACITY, "workspace %lld bytes < required %lld",
+                (long long)workspace_bytes, (long long)need);
+  const int nB = (int)cdiv(shape->N, 64);
+  bsa::TransposeArgs t{};
+  t.V = V;
+  t.Vt = (uint16_t*)workspace;
+  t.sb = shape->stride_b;
+  t.sh = shape->stride_h;
+  t.sn = shape->stride_n;
+  t.H = shape->H;
+  t.N = shape->N;
+  t.nB = nB;
+  t.Npad = nB * 64;
+  t.heads = all_heads(shape->H);
+  return hip_status(bsa::launch_transpose_v(t, shape->B, shape->d, (hipStream_t)stream),
+                    "transpose_v launch");
+}
+
 bsa_status bsa_sparse_attn_fwd(const uint16_t* Q, const uint16_t* K, const uint16_t* V,
                                const bsa_shape* shape, int32_t block, float scale,
                                const int32_t* row_ptr, const int32_t* col_idx, void* O,

@@ -12,6 +12,8 @@
  *   bsa_micro_residual_fwd attention over the selected 16x16 micro tiles;
  *   bsa_lse_merge         exact merge of two partial softmax results.
  *   bsa_dense_attn_fwd    the same attention engine over every key (baseline).
+ *   bsa_attn_stage_v      the attention calls' V^T staging on its own (to
+ *                         overlap it with scoring on another stream).
  *   bsa_pooled_rectify    add the pooled estimate of the omitted blocks to a
  *                         sparse result (exact LSE merge).
  *   bsa_local_window_cluster  3D local-window clustering of Q or K (the
@@ -262,6 +264,21 @@ bsa_status bsa_dense_attn_fwd(const uint16_t* Q, const uint16_t* K,
                               float scale, void* O, int32_t o_dtype,
                               float* LSE, void* workspace,
                               int64_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * bsa_attn_stage_v -- the fp16 V^T staging that bsa_sparse_attn_fwd,
+ * bsa_dense_attn_fwd and bsa_micro_residual_fwd perform when given V, as a
+ * call of its own, so that a caller can run it on another stream while the
+ * scores and selections of the same step are computed, then pass V = NULL
+ * to the attention calls (ordering between the streams is the caller's).
+ * Writes only the V^T region of the workspace: [B*H, nB, 4, d, 16] fp16,
+ * every 16-key chunk in the order the matrix-core operand reads it, zero
+ * beyond N.  Same V layout rules as the attention calls.
+ * workspace: >= bsa_attn_workspace_bytes(shape) bytes, 256-byte aligned.
+ * ---------------------------------------------------------------------- */
+bsa_status bsa_attn_stage_v(const uint16_t* V, const bsa_shape* shape,
+                            void* workspace, int64_t workspace_bytes,
+                            void* stream);
 
 /* ------------------------------------------------------------------------
  * bsa_micro_residual_fwd -- HyMoR Micro residual: each 16-row query sub-tile

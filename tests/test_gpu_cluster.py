@@ -501,3 +501,43 @@ def test_lowe_ratio_hunyuanvideo_layer():
     _, K, _ = gen_qkv(spec, heads=[0])
     say("lowe on the HunyuanVideo key grid")
     _lowe_case(K[:, :1], spec.grid, (11, 3, 3), (3, 8, 8), 2, 0.15)
+
+
+# ------------------------------------------------ fallback paths of the kernels
+
+def test_cluster_cells_beyond_the_bucket_tables():
+    """Cells of 2,560 tokens exceed the per-cell LDS table of the bucketed
+    update and permutation: the box-scan kernels run instead; clustering and
+    permutation against the oracle."""
+    grid, cell, window = (2, 40, 96), (2, 40, 32), (1, 1, 2)
+    spec = VideoSpec(1, 1, 64, grid, 191)
+    Q, _, _ = gen_qkv(spec)
+    Qd = Q.to(DEV)
+    a, mu, c = bsa.bsa_local_window_cluster(Qd, grid, cell, window, 2)
+    perm, off = bsa.bsa_cluster_permute(a, c, Qd, grid, cell, window)
+    torch.cuda.synchronize()
+    x = Q[0, 0].double().numpy()
+    compare_head(x, grid, cell, window, 2, a[0, 0].cpu().numpy(), mu[0, 0].double().cpu().numpy(),
+                 c[0, 0].cpu().numpy(), "large cells")
+    po, offo = O.cluster_permutation(a[0, 0].cpu().numpy(), c.shape[2])
+    np.testing.assert_array_equal(perm[0, 0].cpu().numpy(), po)
+    np.testing.assert_array_equal(off[0, 0].cpu().numpy(), offo)
+
+
+def test_cluster_permutation_of_a_cluster_beyond_lds():
+    """Identical tokens: every distance ties and each token takes the lowest
+    index of its window, so centroid 0 collects all 4,096 tokens of the 2 x 2
+    cells of 1,024 -- more members than the bucketed permutation holds in
+    LDS; the box scan places that cluster.  Both sides agree with the
+    oracle."""
+    grid, cell, window = (1, 64, 64), (1, 32, 32), (1, 3, 3)
+    X = torch.full((1, 1, 64 * 64, 64), 0.5, dtype=torch.bfloat16)
+    Xd = X.to(DEV)
+    a, mu, c = bsa.bsa_local_window_cluster(Xd, grid, cell, window, 2)
+    perm, off = bsa.bsa_cluster_permute(a, c, Xd, grid, cell, window)
+    torch.cuda.synchronize()
+    ao, _, co = O.local_window_clustering(X[0, 0].double().numpy(), grid, cell, window, 2)
+    assert np.array_equal(ao, a[0, 0].cpu().numpy()) and co[0] == 4096
+    po, offo = O.cluster_permutation(ao, len(co))
+    np.testing.assert_array_equal(perm[0, 0].cpu().numpy(), po)
+    np.testing.assert_array_equal(off[0, 0].cpu().numpy(), offo)
