@@ -342,3 +342,17 @@ def test_lowe_ratio_validation():
     st = L.bsa_lowe_ratio_subset(p, ctypes.byref(s), ctypes.byref(cp), None, 36, p, p, p, 256,
                                  None)
     assert st == 1 and "centroids is NULL" in bsa.bsa_last_error()
+
+
+def test_stage_v_validation():
+    L = bsa._lib
+    s = _shape(B=1, H=2, N=1000, d=128)
+    need = L.bsa_attn_workspace_bytes(ctypes.byref(s))
+    p = ctypes.c_void_p(4096)
+    assert L.bsa_attn_stage_v(p, ctypes.byref(s), p, need - 1, None) == 3
+    assert "workspace" in bsa.bsa_last_error()
+    assert L.bsa_attn_stage_v(None, ctypes.byref(s), p, need, None) == 1
+    assert "V is NULL" in bsa.bsa_last_error()
+    assert L.bsa_attn_stage_v(ctypes.c_void_p(4098), ctypes.byref(s), p, need, None) == 1
+    bad = _shape(B=1, H=2, N=1000, d=96)
+    assert L.bsa_attn_stage_v(p, ctypes.byref(bad), p, need, None) == 2

@@ -541,3 +541,52 @@ def test_cluster_permutation_of_a_cluster_beyond_lds():
     po, offo = O.cluster_permutation(ao, len(co))
     np.testing.assert_array_equal(perm[0, 0].cpu().numpy(), po)
     np.testing.assert_array_equal(off[0, 0].cpu().numpy(), offo)
+
+
+def test_cluster_pipeline_multi_head():
+    """Two batches x two heads through the whole GPU chain (clustering,
+    permutation, cluster top-p, merging, attention over the groups): every
+    (b, h) against the oracle's chain on its own head, so that per-head
+    offsets of every kernel are exercised."""
+    import math
+    import parity as PT
+    from synth import merge_sides
+    grid, d, cq, ck, win = (4, 12, 16), 64, (2, 3, 4), (2, 3, 2), (2, 3, 3)
+    spec = VideoSpec(2, 2, d, grid, 175)
+    Q, K, V = gen_qkv(spec)
+    Qd, Kd, Vd = (X.to(DEV) for X in (Q, K, V))
+    aq, mq, cnt_q = bsa.bsa_local_window_cluster(Qd, grid, cq, win, 2)
+    ak, mk, cnt_k = bsa.bsa_local_window_cluster(Kd, grid, ck, win, 2)
+    pq, oq = bsa.bsa_cluster_permute(aq, cnt_q, Qd, grid, cq, win)
+    pk, ok = bsa.bsa_cluster_permute(ak, cnt_k, Kd, grid, ck, win)
+    Nq, Nk = cnt_q.shape[2], cnt_k.shape[2]
+    rp, ci, nnz = bsa.bsa_cluster_select(mq, mk, cnt_k, p=0.85, k_min=2, k_cap=Nk)
+    sides_np = merge_sides(176, 2, 2, 3, Nq)
+    gof = bsa.bsa_cluster_merge(oq, ok, rp, ci, torch.from_numpy(sides_np).to(DEV), N=spec.N)
+    Og, Lg, pairs = bsa.bsa_cluster_attn_fwd(Qd, Kd, Vd, pq, oq, pk, ok, rp, ci, gof)
+    torch.cuda.synchronize()
+    rows_gpu = bsa.csr_rows(rp, ci, nnz)
+    total_pairs = 0
+    for b in range(2):
+        for h in range(2):
+            z = b * 2 + h
+            x, y = Q[b, h].double().numpy(), K[b, h].double().numpy()
+            aq_o, mq_o, cq_o = O.local_window_clustering(x, grid, cq, win, 2)
+            ak_o, mk_o, ck_o = O.local_window_clustering(y, grid, ck, win, 2)
+            assert np.array_equal(aq_o, aq[b, h].cpu().numpy()), f"b{b} h{h} query clusters"
+            assert np.array_equal(ak_o, ak[b, h].cpu().numpy()), f"b{b} h{h} key clusters"
+            rows = O.cluster_topp_rows(mq_o, mk_o, ck_o, 1 / math.sqrt(d), 0.85, 2, Nk)
+            assert rows_gpu[z * Nq:(z + 1) * Nq] == rows, f"b{b} h{h}: cluster lists differ"
+            grp, groups = O.agglomerative_merge(cq_o.tolist(), rows, ck_o.tolist(),
+                                                sides_np[b, h].tolist(), 64, 64, 16)
+            np.testing.assert_array_equal(gof[b, h].cpu().numpy(), grp)
+            pq_o, oq_o = O.cluster_permutation(aq_o, len(cq_o))
+            pk_o, ok_o = O.cluster_permutation(ak_o, len(ck_o))
+            np.testing.assert_array_equal(pq[b, h].cpu().numpy(), pq_o)
+            grows = O.group_rows(groups, rows)
+            Oref, Lref = O.cluster_block_attention(x, y, V[b, h].double().numpy(), pq_o, oq_o,
+                                                   pk_o, ok_o, grows, 1 / math.sqrt(d))
+            PT.compare_o_lse(Og[b, h], Lg[b, h], Oref, Lref, f"b{b} h{h}")
+            total_pairs += O.packed_tile_pairs(oq_o, ok_o, groups, grows, 64, 16)
+            say(f"   b{b} h{h}: {Nq} clusters -> {len(groups)} groups")
+    assert int(pairs.item()) == total_pairs

@@ -252,6 +252,28 @@ def test_sparse_attention_random_rows(grid, H, d, key):
     _attn_case(spec, rows_of)
 
 
+def test_staged_v_equals_inline_staging():
+    """bsa_attn_stage_v on its own stream, then the attention with V=None,
+    gives the bits of the attention that stages V itself (strided V too)."""
+    spec = VideoSpec(2, 3, 128, (3, 9, 21), 109)
+    Q, K, V = (x.to(DEV) for x in gen_qkv(spec))
+    Vs = V.transpose(1, 2).contiguous().transpose(1, 2)  # [B, N, H, d] storage
+    nB = O.n_blocks(spec.N, 64)
+    rows = [sorted({i, (i * 7) % nB, 0}) for i in range(nB)]
+    rp, ci = PT.rows_to_csr([r for _ in range(spec.B * spec.H) for r in rows])
+    rp, ci = rp.to(DEV), ci.to(DEV)
+    O1, L1 = bsa.bsa_sparse_attn_fwd(Q, K, V, rp, ci)
+    ws = bsa.attn_workspace(Q)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        bsa.bsa_attn_stage_v(Vs, workspace=ws)
+    torch.cuda.current_stream().wait_stream(side)
+    O2, L2 = bsa.bsa_sparse_attn_fwd(Q, K, None, rp, ci, workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(O1, O2) and torch.equal(L1, L2)
+
+
 def test_sparse_attention_bf16_out_strided_and_empty_rows():
     spec = VideoSpec(2, 2, 128, (4, 9, 11), 108)
     say("sparse attn bf16/strided/empty")
