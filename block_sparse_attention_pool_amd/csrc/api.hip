@@ -176,7 +176,7 @@ bsa_status plan_cluster(const bsa_shape* s, const bsa_cluster_params* p, int64_t
 // most ceil(N/16) + Nk + 1 chunks); both layouts share one length NP.
 struct ClusterAttnPlan {
   int64_t NP, nTP, BH, W;
-  int64_t gt, qpos, kc, tg, srcq, gmask, cnt, rp, pairs, nent, qp, kp, vp, vt, op, lp, col, total, cap;
+  int64_t gt, qpos, kc, tg, srcq, gmask, cnt, rp, pairs, nent, kp, vp, vt, col, total, cap;
 };
 
 bsa_status plan_cluster_attn(const bsa_shape* s, int32_t Nq, int32_t Nk, int32_t o_dtype,
@@ -201,7 +201,7 @@ bsa_status plan_cluster_attn(const bsa_shape* s, int32_t Nq, int32_t Nk, int32_t
   if (p.cap >= INT32_MAX || p.BH * p.NP * s->d >= ((int64_t)1 << 40))
     return fail(BSA_ERR_UNSUPPORTED, "cluster layout too large (%lld chunk entries)",
                 (long long)p.cap);
-  const int64_t d = s->d, osz = o_dtype == BSA_BF16 ? 2 : 4;
+  const int64_t d = s->d;
   int64_t at = 0;
   auto take = [&](int64_t bytes) {
     const int64_t here = at;
@@ -218,12 +218,9 @@ bsa_status plan_cluster_attn(const bsa_shape* s, int32_t Nq, int32_t Nk, int32_t
   p.rp = take((p.BH * Nq + 1) * 4);
   p.pairs = take(8);
   p.nent = take(8);
-  p.qp = take(p.BH * p.NP * d * 2);
   p.kp = take(p.BH * p.NP * d * 2);
   p.vp = take(p.BH * p.NP * d * 2);
   p.vt = take(p.BH * p.NP * d * 2);
-  p.op = take(p.BH * p.NP * d * osz);
-  p.lp = take(p.BH * p.NP * 4);
   p.col = take(p.cap * 4);
   p.total = at;
   *pl = p;
@@ -1221,13 +1218,8 @@ bsa_status bsa_cluster_attn_fwd(const uint16_t* Q, const uint16_t* K, const uint
   c.cap = pl.cap;
   c.pairs = (unsigned long long*)(out_tile_pairs != nullptr ? (void*)out_tile_pairs
                                                             : (void*)(ws + pl.pairs));
-  c.Qp = (uint16_t*)(ws + pl.qp);
   c.Kp = (uint16_t*)(ws + pl.kp);
   c.Vp = (uint16_t*)(ws + pl.vp);
-  c.Op = ws + pl.op;
-  c.Lp = (const float*)(ws + pl.lp);
-  c.O = O;
-  c.LSE = LSE;
   int64_t* entries = (int64_t*)(ws + pl.nent);  // total chunk entries (unused)
   BSA_TRY(hip_status(bsa::launch_cluster_attn_plan(c, BH, D, st), "cluster plan launch"));
   BSA_TRY(hip_status(bsa::launch_scan(c.counts, (int)(pl.BH * Nq), c.row_ptr, entries, st),
@@ -1247,17 +1239,24 @@ bsa_status bsa_cluster_attn_fwd(const uint16_t* Q, const uint16_t* K, const uint
   t.Npad = c.NP;
   t.heads = all_heads(shape->H);
   BSA_TRY(hip_status(bsa::launch_transpose_v(t, shape->B, D, st), "transpose_v launch"));
+  // queries and outputs in the caller's layout (rows through the source
+  // map), keys and staged values in the padded layout
   bsa::AttnArgs a{};
-  a.Q = c.Qp;
+  a.Q = Q;
   a.K = c.Kp;
   a.Vt = t.Vt;
-  a.O = ws + pl.op;
-  a.LSE = (float*)(ws + pl.lp);
+  a.O = O;
+  a.LSE = LSE;
   a.row_ptr = c.row_ptr;
   a.col_idx = c.col_idx;
-  a.sb = sb;
-  a.sh = sh;
-  a.sn = sn;
+  a.sb = shape->stride_b;
+  a.sh = shape->stride_h;
+  a.sn = shape->stride_n;
+  a.ksb = sb;
+  a.ksh = sh;
+  a.ksn = sn;
+  a.qsrc = c.srcq;
+  a.Nout = shape->N;
   a.B = shape->B;
   a.H = shape->H;
   a.N = c.NP;
@@ -1268,9 +1267,7 @@ bsa_status bsa_cluster_attn_fwd(const uint16_t* Q, const uint16_t* K, const uint
   a.per_xcd = (int)cdiv(a.rows, 8);
   a.tile_group = c.tile_group;
   a.ngroups = Nq;
-  BSA_TRY(hip_status(bsa::launch_attn_chunks(a, D, o_dtype == BSA_BF16, st), "attn launch"));
-  return hip_status(bsa::launch_cluster_attn_scatter(c, BH, D, o_dtype == BSA_BF16, st),
-                    "cluster scatter launch");
+  return hip_status(bsa::launch_attn_chunks(a, D, o_dtype == BSA_BF16, st), "attn launch");
 }
 
 int64_t bsa_cluster_merge_workspace_bytes(int32_t B, int32_t H, int32_t N, int32_t Nq, int32_t Nk,

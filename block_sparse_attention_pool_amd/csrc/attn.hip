@@ -277,8 +277,9 @@ constexpr int kShortRun = 8;
 // a.tile_group[L] (-1: no work) whose entries row_ptr[bh * ngroups + g] ..
 // are 16-key chunk codes (chunk | valid keys << 24), four per key tile; the
 // keys of a chunk past its valid count are masked.  Used for packed
-// cluster-induced blocks, whose tensors hold whole chunks, so no load is
-// clamped.
+// cluster-induced blocks: K and the staged V^T hold whole chunks (so no load
+// is clamped); query position q of a head is token a.qsrc[bh * N + q] of the
+// caller's Q (-1: padding), whose O row and LSE (of a.Nout tokens) it writes.
 template <int D, bool DENSE, bool OUT_BF16, bool CHUNK = false>
 __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2)))
 void attn_fwd_kernel(AttnArgs a) {
@@ -336,7 +337,10 @@ void attn_fwd_kernel(AttnArgs a) {
   const int n = lane & 31, g = lane >> 5;
   const int64_t base = (int64_t)b * a.sb + (int64_t)h * a.sh;
   const uint16_t* Qh = a.Q + base;
-  const uint16_t* Kh = a.K + base;
+  // CHUNK: K lives in the padded chunk layout (its own strides); Q and O
+  // keep the caller's layout, rows found through the query source map
+  const uint16_t* Kh = a.K + (CHUNK ? (int64_t)b * a.ksb + (int64_t)h * a.ksh : base);
+  const int64_t ksn = CHUNK ? a.ksn : a.sn;
   const uint16_t* Vth = a.Vt + (int64_t)bh * D * a.Npad;
 
   // Row pointers and column indices are read-only for the kernel's
@@ -357,11 +361,18 @@ void attn_fwd_kernel(AttnArgs a) {
   }
 
   const int q = i * kBlock + wave * 32 + n;
+  // the row this lane's query is read from and written to
+  int64_t qrow = q;
+  bool has_q = q < a.N;
+  if constexpr (CHUNK) {
+    qrow = has_q ? a.qsrc[(int64_t)bh * a.N + q] : -1;
+    has_q = qrow >= 0;
+  }
   bf16x8 qf[KS];
 #pragma unroll
   for (int s = 0; s < KS; ++s) {
     u32x4 v = {0u, 0u, 0u, 0u};
-    if (q < a.N) v = *(const u32x4*)(Qh + (int64_t)q * a.sn + 16 * s + 8 * g);
+    if (has_q) v = *(const u32x4*)(Qh + qrow * a.sn + 16 * s + 8 * g);
     qf[s] = __builtin_bit_cast(bf16x8, v);
   }
 
@@ -378,7 +389,7 @@ void attn_fwd_kernel(AttnArgs a) {
   // the tile copies in flight.
   wait_vmcnt<0>();
   TileCopy<D> cp;
-  cp.init(a.sn, wave, lane, sK, sV, a.N, a.nB);
+  cp.init(ksn, wave, lane, sK, sV, a.N, a.nB);
 
   // O^T += V^T P^T for one key block whose V^T tile is in sV.
   // The V^T fragments of d tile t+1 are read while the products of tile t run.
@@ -442,7 +453,7 @@ void attn_fwd_kernel(AttnArgs a) {
   if (e0 < e1) {
     j = (DENSE || CHUNK) ? e0 : col_idx[e0];
     jprev = j;
-    if constexpr (CHUNK) cp.k_chunks(Kh, a.sn, col_idx + j);
+    if constexpr (CHUNK) cp.k_chunks(Kh, ksn, col_idx + j);
     else cp.k_tile(Kh, a.sn, j, a.nB);
   }
   for (int e = e0; e < e1; e += STEP) {
@@ -481,7 +492,7 @@ void attn_fwd_kernel(AttnArgs a) {
     wait_vmcnt<0>();   // V(e-1) has landed
     exec_barrier();    // both waves are done with sK; sV holds V(e-1)
     if (e + STEP < e1) {
-      if constexpr (CHUNK) cp.k_chunks(Kh, a.sn, col_idx + jn);
+      if constexpr (CHUNK) cp.k_chunks(Kh, ksn, col_idx + jn);
       else cp.k_tile(Kh, a.sn, jn, a.nB);
     }
 
@@ -575,8 +586,8 @@ void attn_fwd_kernel(AttnArgs a) {
   const float l_tot = l_run + __shfl_xor(l_run, 32);
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
   const float lse = l_tot > 0.f ? (m_run + __builtin_log2f(l_tot)) * kLn2 : -INFINITY;
-  if (q < a.N) {
-    const int64_t orow = base + (int64_t)q * a.sn;
+  if (has_q) {
+    const int64_t orow = base + qrow * a.sn;
 #pragma unroll
     for (int t = 0; t < DT; ++t)
 #pragma unroll
@@ -585,7 +596,7 @@ void attn_fwd_kernel(AttnArgs a) {
         store4<OUT_BF16>(a.O, orow + d0, o[t][4 * rr] * inv, o[t][4 * rr + 1] * inv,
                          o[t][4 * rr + 2] * inv, o[t][4 * rr + 3] * inv);
       }
-    if (g == 0) a.LSE[(int64_t)bh * a.N + q] = lse;
+    if (g == 0) a.LSE[(int64_t)bh * (CHUNK ? a.Nout : a.N) + qrow] = lse;
   }
 }
 

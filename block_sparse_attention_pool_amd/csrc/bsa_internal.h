@@ -78,9 +78,14 @@ struct AttnArgs {
   float scale_log2;  // softmax scale * log2(e)
   int rows;          // B*H*nB
   int per_xcd;       // ceil(rows / 8)
-  // chunk kernel only: group of every query tile (-1: none), groups per head
+  // chunk kernel only: group of every query tile (-1: none), groups per
+  // head, the token of every padded query position (-1: none) and the
+  // tokens per head of Q, O and LSE, and the strides of the padded K
   const int32_t* tile_group;
   int ngroups;
+  const int32_t* qsrc;
+  int Nout;
+  int64_t ksb, ksh, ksn;
 };
 
 // 16-key chunk codes of packed cluster-induced blocks: chunk index in the low
@@ -192,13 +197,8 @@ struct ClusterAttnArgs {
   int32_t* col_idx;        // chunk codes
   int64_t cap;
   unsigned long long* pairs;  // executed (query tile, key tile) pairs
-  uint16_t* Qp;            // [BH, NP, D] queries by group, keys by chunk
-  uint16_t* Kp;
+  uint16_t* Kp;            // [BH, NP, D] keys and values by chunk
   uint16_t* Vp;
-  const void* Op;          // [BH, NP, D] attention output in padded order
-  const float* Lp;         // [BH, NP]
-  void* O;
-  float* LSE;
 };
 
 // HVA parallel agglomerative merging of query clusters.
@@ -278,8 +278,7 @@ hipError_t launch_cluster_attn_plan(const ClusterAttnArgs& a, int BH, int D, hip
 hipError_t launch_cluster_attn_emit(const ClusterAttnArgs& a, int BH, int D, hipStream_t s);
 hipError_t launch_cluster_merge(const ClusterMergeArgs& a, int BH, hipStream_t s);
 hipError_t launch_lowe(const ClusterArgs& a, int BH, int n_sub, int32_t* subset, hipStream_t s);
-hipError_t launch_cluster_attn_scatter(const ClusterAttnArgs& a, int BH, int D, bool out_bf16,
-                                       hipStream_t s);
+
 hipError_t launch_rectify(const RectifyArgs& a, int BH, int D, bool out_bf16, hipStream_t s);
 
 }  // namespace bsa

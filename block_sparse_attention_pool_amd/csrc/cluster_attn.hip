@@ -17,8 +17,9 @@
 //
 // Kernels: the per-head plan (group sizes and tiles, query positions, key
 // chunk offsets), the padded query source map, the group key masks, the
-// per-group chunk counts and lists, the padded gathers of Q, K, V, the
-// masked attention, the scatter of O and LSE back to token order.
+// per-group chunk counts and lists, the padded gathers of K and V, and the
+// masked attention, which reads every query row through the source map and
+// writes O and LSE straight to token order.
 #include "bsa_device.h"
 #include "bsa_internal.h"
 
@@ -209,60 +210,34 @@ __global__ __launch_bounds__(256) void cemit_kernel(ClusterAttnArgs a) {
     if (p < a.cap) a.col_idx[p] = null_chunk;
 }
 
-// Padded copies: query position p holds token srcq[p] (zeros where -1); key
-// position p of chunk p / 16 in key cluster j holds token perm_k[off_k[j] +
-// p - 16 kc[j]] while that is inside the cluster, zeros otherwise.  One
-// thread per 16-byte piece.
+// Padded copies of K and V: key position p of chunk p / 16 in key cluster j
+// holds token perm_k[off_k[j] + p - 16 kc[j]] while that is inside the
+// cluster, zeros otherwise.  One thread per 16-byte piece.
 template <int D>
 __global__ __launch_bounds__(256) void cgather_kernel(ClusterAttnArgs a) {
   constexpr int C = D / 8;
   const int64_t f = (int64_t)blockIdx.x * 256 + threadIdx.x;
   const int64_t bh = blockIdx.y;
-  const int which = blockIdx.z;  // 0 Q, 1 K, 2 V
+  const bool values = blockIdx.z == 1;
   if (f >= (int64_t)a.NP * C) return;
   const int p = (int)(f / C), c = (int)(f % C);
   int64_t tok = -1;
-  if (which == 0) {
-    tok = a.srcq[bh * a.NP + p];
-  } else {
-    const int32_t* kc = a.kc + bh * (a.Nk + 1);
-    const int chunk = p / 16;
-    if (chunk < kc[a.Nk]) {
-      const int j = seg_of(kc, a.Nk, chunk);
-      const int32_t* ok = a.off_k + bh * (a.Nk + 1);
-      const int k = p - 16 * kc[j];
-      if (k < ok[j + 1] - ok[j]) tok = a.perm_k[bh * a.N + ok[j] + k];
-    }
+  const int32_t* kc = a.kc + bh * (a.Nk + 1);
+  const int chunk = p / 16;
+  if (chunk < kc[a.Nk]) {
+    const int j = seg_of(kc, a.Nk, chunk);
+    const int32_t* ok = a.off_k + bh * (a.Nk + 1);
+    const int k = p - 16 * kc[j];
+    if (k < ok[j + 1] - ok[j]) tok = a.perm_k[bh * a.N + ok[j] + k];
   }
-  const uint16_t* src = which == 0 ? a.Q : which == 1 ? a.K : a.V;
-  uint16_t* dst = (which == 0 ? a.Qp : which == 1 ? a.Kp : a.Vp) + (bh * a.NP + p) * D;
+  const uint16_t* src = values ? a.V : a.K;
+  uint16_t* dst = (values ? a.Vp : a.Kp) + (bh * a.NP + p) * D;
   u32x4 v = {0u, 0u, 0u, 0u};
   if (tok >= 0) {
     const int b = (int)(bh / a.H), h = (int)(bh % a.H);
     v = *(const u32x4*)(src + (int64_t)b * a.sb + (int64_t)h * a.sh + tok * a.sn + 8 * c);
   }
   *(u32x4*)(dst + 8 * c) = v;
-}
-
-// O and LSE back to token order: padded query position p holding token
-// srcq[p] >= 0.  One thread per 4 output elements.
-template <int D, bool OUT_BF16>
-__global__ __launch_bounds__(256) void cscatter_kernel(ClusterAttnArgs a) {
-  const int64_t f = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  const int64_t bh = blockIdx.y;
-  if (f >= (int64_t)a.NP * (D / 4)) return;
-  const int p = (int)(f / (D / 4)), c = (int)(f % (D / 4));
-  const int64_t tok = a.srcq[bh * a.NP + p];
-  if (tok < 0) return;
-  const int64_t src = bh * a.NP + p;
-  const int b = (int)(bh / a.H), h = (int)(bh % a.H);
-  const int64_t dst = (int64_t)b * a.sb + (int64_t)h * a.sh + tok * a.sn + 4 * c;
-  if constexpr (OUT_BF16) {
-    *(u32x2*)((uint16_t*)a.O + dst) = *(const u32x2*)((const uint16_t*)a.Op + src * D + 4 * c);
-  } else {
-    *(f32x4*)((float*)a.O + dst) = *(const f32x4*)((const float*)a.Op + src * D + 4 * c);
-  }
-  if (c == 0) a.LSE[bh * a.N + tok] = a.Lp[src];
 }
 
 }  // namespace
@@ -286,22 +261,9 @@ hipError_t launch_cluster_attn_plan(const ClusterAttnArgs& a, int BH, int D, hip
 
 hipError_t launch_cluster_attn_emit(const ClusterAttnArgs& a, int BH, int D, hipStream_t s) {
   hipLaunchKernelGGL(cemit_kernel, dim3((a.Nq + 3) / 4, BH), dim3(256), 0, s, a);
-  const dim3 ggrid((unsigned)(((int64_t)a.NP * (D / 8) + 255) / 256), BH, 3);
+  const dim3 ggrid((unsigned)(((int64_t)a.NP * (D / 8) + 255) / 256), BH, 2);
   if (D == 128) hipLaunchKernelGGL(cgather_kernel<128>, ggrid, dim3(256), 0, s, a);
   else hipLaunchKernelGGL(cgather_kernel<64>, ggrid, dim3(256), 0, s, a);
-  return hipGetLastError();
-}
-
-hipError_t launch_cluster_attn_scatter(const ClusterAttnArgs& a, int BH, int D, bool out_bf16,
-                                       hipStream_t s) {
-  const dim3 grid((unsigned)(((int64_t)a.NP * (D / 4) + 255) / 256), BH);
-  if (D == 128) {
-    if (out_bf16) hipLaunchKernelGGL((cscatter_kernel<128, true>), grid, dim3(256), 0, s, a);
-    else hipLaunchKernelGGL((cscatter_kernel<128, false>), grid, dim3(256), 0, s, a);
-  } else {
-    if (out_bf16) hipLaunchKernelGGL((cscatter_kernel<64, true>), grid, dim3(256), 0, s, a);
-    else hipLaunchKernelGGL((cscatter_kernel<64, false>), grid, dim3(256), 0, s, a);
-  }
   return hipGetLastError();
 }
 

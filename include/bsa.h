@@ -533,9 +533,10 @@ bsa_status bsa_cluster_merge(const int32_t* off_q, const int32_t* off_k,
  * out_tile_pairs: device int64 or NULL; receives the number of executed
  *   (query tile, key tile) pairs, C(S) / 64^2 summed over the groups.
  * workspace: >= bsa_cluster_attn_workspace_bytes(shape, Nq, Nk, o_dtype)
- *   bytes, 256-byte aligned (padded copies of Q, K, V and the output, the
- *   chunk lists): padded length per head 64 * max(ceil(N/64) + Nq,
- *   ceil((ceil(N/16) + Nk + 1) / 4)).
+ *   bytes, 256-byte aligned (padded copies of K and V, the staged V^T, the
+ *   query source map and the chunk lists): padded length per head
+ *   64 * max(ceil(N/64) + Nq, ceil((ceil(N/16) + Nk + 1) / 4)).  Queries are
+ *   read, and O and LSE written, in the caller's layout.
  * ---------------------------------------------------------------------- */
 int64_t bsa_cluster_attn_workspace_bytes(const bsa_shape* shape, int32_t Nq,
                                          int32_t Nk, int32_t o_dtype);

@@ -192,7 +192,7 @@ def test_cluster_select_hunyuanvideo_sizes():
 # ------------------------------------------------- attention over clusters
 
 def _cluster_attn_case(Q, K, V, aq, ak, Nq, Nk, rows, out_dtype=torch.float32, sample=None,
-                       groups=None):
+                       groups=None, strided=False):
     """GPU Eq. 4 on oracle-made clusterings, lists (and merged groups)
     against the oracle; the executed tile pairs against Eq. 8 at a 16-token
     key grain."""
@@ -211,8 +211,12 @@ def _cluster_attn_case(Q, K, V, aq, ak, Nq, Nk, rows, out_dtype=torch.float32, s
         gof = t(name)[None, None]
     else:
         groups = [[i] for i in range(Nq)]
+    if strided:  # [B, N, H, d] storage: Q, K, V and O through their strides
+        Qd, Kd, Vd = (X.transpose(1, 2).contiguous().to(DEV).transpose(1, 2) for X in (Q, K, V))
+    else:
+        Qd, Kd, Vd = (X.to(DEV) for X in (Q, K, V))
     Og, Lg, pairs = bsa.bsa_cluster_attn_fwd(
-        Q.to(DEV), K.to(DEV), V.to(DEV), t(pq)[None, None], t(oq)[None, None], t(pk)[None, None],
+        Qd, Kd, Vd, t(pq)[None, None], t(oq)[None, None], t(pk)[None, None],
         t(ok)[None, None], rp.to(DEV), ci.to(DEV), gof, out_dtype=out_dtype)
     torch.cuda.synchronize()
     rows = O.group_rows(groups, rows)
@@ -370,8 +374,9 @@ def test_cluster_merge_hunyuanvideo_sizes():
     assert len(groups) < 432 and after < before
 
 
-@pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16])
-def test_cluster_attention_merged_groups(out_dtype):
+@pytest.mark.parametrize("out_dtype,strided", [(torch.float32, False), (torch.bfloat16, False),
+                                               (torch.float32, True)])
+def test_cluster_attention_merged_groups(out_dtype, strided):
     """Eq. 4 over merged groups (each member attends over the union of the
     group's rows) on an oracle-made clustering, oracle-merged."""
     import math
@@ -387,7 +392,8 @@ def test_cluster_attention_merged_groups(out_dtype):
     _, groups = O.agglomerative_merge(cnt_q.tolist(), rows, cnt_k.tolist(), sides, 64, 64, 16)
     assert any(len(S) > 1 for S in groups), "no merge happened: pick other inputs"
     say("merged attention", len(cnt_q), "clusters ->", len(groups), "groups")
-    _cluster_attn_case(Q, K, V, aq, ak, len(cnt_q), len(cnt_k), rows, out_dtype, groups=groups)
+    _cluster_attn_case(Q, K, V, aq, ak, len(cnt_q), len(cnt_k), rows, out_dtype, groups=groups,
+                       strided=strided)
 
 
 def test_cluster_pipeline_with_merging():
