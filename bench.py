@@ -161,9 +161,9 @@ def traffic_entry(kernel_src):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(json.dumps({"error": "this benchmark measures one GPU; runs on more than one "
-                                   "GPU are not part of this build (heads shard with no "
-                                   "exchange; see the design notes)"}))
+        print(json.dumps({"error": "this benchmark measures one GPU only; the path shards "
+                                   "by (batch, head) with no exchange between GPUs, and no "
+                                   "multi-GPU run is implemented"}))
         sys.exit(2)
 
     import torch
