@@ -30,8 +30,7 @@ Sources (pages as titled):
           (density = computed B x B blocks / total) and Block-wise Attention
           Computation (block size 128).
 
-Readings where the pages are silent (each one is listed with its reason in the
-design notes of the repository):
+Readings where the pages are silent:
   * the ragged tail block holds only valid tokens; pooling averages over them
     and attention never sees a padded key;
   * top-k keeps ``k`` blocks ordered by (score descending, index ascending);
