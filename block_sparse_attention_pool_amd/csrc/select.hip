@@ -446,7 +446,7 @@ __device__ uint32_t block_radix_select(int& remaining, Each each, uint32_t* hist
 // selection (a few spills, in the tie pass, cost less than the lost overlap:
 // 3.56 -> 2.97 ms for the micro selection of the HunyuanVideo layer).
 template <int E>
-__global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(8)))
+__global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(E <= 32 ? 8 : 1)))
 void micro_select_kernel(MicroSelectArgs a) {
   __shared__ uint32_t omask[128];
   __shared__ uint32_t hist[256];
