@@ -86,7 +86,10 @@ __device__ __forceinline__ f32x4 load4(const void* O, int64_t off) {
 }
 
 template <int D, bool OUT_BF16>
-__global__ __launch_bounds__(256) void rectify_kernel(RectifyArgs a) {
+// Scheduled for four waves per SIMD (the compiler otherwise plans for three):
+// 0.59 -> 0.51 ms on the 32K layer, 7.4 -> 6.9 ms on the 14B layer.
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4)))
+void rectify_kernel(RectifyArgs a) {
   constexpr int KS = D / 32;
   constexpr int DT = D / 16;
   constexpr int KP = D + 8;             // padded LDS row of a pooled key (conflict-free reads)
