@@ -596,3 +596,54 @@ def test_cluster_pipeline_multi_head():
             total_pairs += O.packed_tile_pairs(oq_o, ok_o, groups, grows, 64, 16)
             say(f"   b{b} h{h}: {Nq} clusters -> {len(groups)} groups")
     assert int(pairs.item()) == total_pairs
+
+
+def test_cluster_merge_and_attention_at_the_cluster_limit():
+    """4096 query and 4096 key clusters (the per-head maximum) over 65,536
+    tokens with random assignments and rows: merging checked by what
+    Algorithm 1 guarantees (a partition named by lowest members whose Eq. 9
+    cost is not above the singletons'), attention over the GPU's groups
+    against the oracle on sampled query clusters, executed pairs against
+    Eq. 8."""
+    import parity as PT
+    from synth import merge_sides
+    rng = np.random.default_rng(777)
+    N, Nq, Nk, d = 65536, 4096, 4096, 64
+    spec = VideoSpec(1, 1, d, (1, 64, 1024), 178)
+    Q, K, V = gen_qkv(spec)
+    aq = rng.integers(0, Nq, N)
+    ak = rng.integers(0, Nk, N)
+    rows = [sorted(rng.choice(Nk, int(rng.integers(1, 40)), replace=False).tolist())
+            for _ in range(Nq)]
+    pq, oq = O.cluster_permutation(aq, Nq)
+    pk, ok = O.cluster_permutation(ak, Nk)
+    t = lambda x: torch.from_numpy(np.asarray(x, dtype=np.int32)).to(DEV)[None, None]
+    rp, ci = PT.rows_to_csr(rows)
+    rp, ci = rp.to(DEV), ci.to(DEV)
+    sides = torch.from_numpy(merge_sides(179, 1, 1, 3, Nq)).to(DEV)
+    gof = bsa.bsa_cluster_merge(t(oq), t(ok), rp, ci, sides, N=N)
+    Og, Lg, pairs = bsa.bsa_cluster_attn_fwd(Q.to(DEV), K.to(DEV), V.to(DEV), t(pq), t(oq), t(pk),
+                                             t(ok), rp, ci, gof)
+    torch.cuda.synchronize()
+    g = gof[0, 0].cpu().numpy()
+    groups = {}
+    for i, name in enumerate(g.tolist()):
+        groups.setdefault(name, []).append(i)
+    assert all(name == min(S) for name, S in groups.items())
+    groups = [groups[k] for k in sorted(groups)]
+    sq, sk = np.diff(oq), np.diff(ok)
+    before = O.partition_cost([[i] for i in range(Nq)], sq, rows, sk, 64, 64, 16)
+    after = O.partition_cost(groups, sq, rows, sk, 64, 64, 16)
+    say(f"cluster limit: {Nq} clusters -> {len(groups)} groups, cost {before} -> {after}")
+    assert after <= before
+    grows = O.group_rows(groups, rows)
+    assert int(pairs.item()) == O.packed_tile_pairs(oq, ok, groups, grows, 64, 16)
+    q, k, v = (X[0, 0].double().numpy() for X in (Q, K, V))
+    for i in sorted(rng.choice(Nq, 6, replace=False).tolist()) + [Nq - 1]:
+        qi = pq[oq[i]:oq[i + 1]]
+        if len(qi) == 0:
+            continue
+        keys = np.concatenate([pk[ok[j]:ok[j + 1]] for j in grows[i]])
+        Oref, Lref = O.attend(q[qi], k[keys], v[keys], 1 / np.sqrt(d))
+        idx = torch.from_numpy(qi.astype(np.int64)).to(DEV)
+        PT.compare_o_lse(Og[0, 0][idx], Lg[0, 0][idx], Oref, Lref, f"query cluster {i}")
