@@ -5,7 +5,9 @@ One step = pooled scoring (bsa_score_blocks) + block selection
 (bsa_select_blocks) + block-sparse attention (bsa_sparse_attn_fwd) and its
 fp16 V^T staging (bsa_attn_stage_v, on a second stream beside scoring and
 selection; ``--serial`` keeps one stream), plus micro-tile selection, residual
-and LSE merge where the workload has them.  The default workload is one layer shaped like
+and LSE merge where the workload has them.  The timed steps replay the step
+captured as a HIP graph, checked bit for bit against the eager step first
+(``--no-graph`` launches every kernel eagerly).  The default workload is one layer shaped like
 Wan-2.1-1.3B at 480p: B=1, H=12, d=128, 21x30x52 = 32760 tokens, 64-token
 blocks, top-k at 25% density (k = 128 of 512 key blocks).  ``--config N``
 selects another of the five workloads (0 tiny reference, 1 the default,
@@ -80,6 +82,8 @@ def parse():
                     help="also run the cluster-induced block pipeline (local-window clustering, "
                          "permutation, cluster top-p 0.9 with the page's Min-kc, attention over "
                          "the clusters) and report its stages")
+    ap.add_argument("--no-graph", action="store_true",
+                    help="launch every step's kernels eagerly instead of replaying a HIP graph")
     ap.add_argument("--serial", action="store_true",
                     help="run every stage of a step on one stream (no overlap)")
     ap.add_argument("--calibration-copy", action="store_true",
@@ -290,10 +294,49 @@ def main():
     for w in range(args.warmup):
         step(w)
     torch.cuda.synchronize()
+
+    # The step as a HIP graph (one per anchor rotation): its kernels replay
+    # without launch gaps.  Every graph is replayed three times, with eager
+    # work between the replays, and must give its eager step's bits.
+    run = step
+    graphs = []
+    if not args.no_graph:
+        variants = N_ROTATIONS if (mode == "static" and not args.mod_mask) else 1
+        refs = []
+        for r in range(variants):
+            step(r, overlap=False)
+            torch.cuda.synchronize()
+            refs.append((O_buf.clone(), L_buf.clone()))
+        capture = torch.cuda.Stream(device=dev)
+        for r in range(variants):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=capture):
+                # the side stream forks from and joins the capture stream
+                outs = step(r, overlap=two_streams)
+            graphs.append((g, outs))
+        for _ in range(3):
+            for r, (g, _outs) in enumerate(graphs):
+                O_buf.zero_()
+                L_buf.zero_()
+                g.replay()
+                torch.cuda.synchronize()
+                if not (torch.equal(O_buf, refs[r][0]) and torch.equal(L_buf, refs[r][1])):
+                    raise RuntimeError("graph replay differs from the eager step")
+        del refs
+
+        def run(call):
+            g, outs = graphs[call % len(graphs)]
+            g.replay()
+            return outs
+
+        for w in range(args.warmup):
+            run(w)
+        torch.cuda.synchronize()
+
     nnz_all, mnnz_all = [], []
     t0 = time.perf_counter()
     for s_i in range(args.steps):
-        sc, rp, ci, nnz, mnnz = step(s_i)
+        sc, rp, ci, nnz, mnnz = run(s_i)
         nnz_all.append(nnz)
         if mnnz is not None:
             mnnz_all.append(mnnz)
@@ -549,6 +592,7 @@ def main():
                    "selection": sel_desc,
                    "density": round(nnz_mean / (B * H * bsa.n_blocks(N) ** 2), 4)},
         "step_streams": 2 if two_streams else 1,
+        "step_graph": bool(graphs),
         "attn_kernel_ms": round(attn_ms, 4),
         "attn_kernel_tflops": round(attn_tflops, 2),
         "attn_kernel_ms_cold_cache": round(attn_cold_ms, 4),
