@@ -5,9 +5,10 @@ One step = pooled scoring (bsa_score_blocks) + block selection
 (bsa_select_blocks) + block-sparse attention (bsa_sparse_attn_fwd) and its
 fp16 V^T staging (bsa_attn_stage_v, on a second stream beside scoring and
 selection; ``--serial`` keeps one stream), plus micro-tile selection, residual
-and LSE merge where the workload has them.  The timed steps replay the step
-captured as a HIP graph, checked bit for bit against the eager step first
-(``--no-graph`` launches every kernel eagerly).  The default workload is one layer shaped like
+and LSE merge where the workload has them.  On small (launch-bound) layers
+the timed steps replay the step captured as a HIP graph, checked bit for bit
+against the eager step first (``--no-graph`` launches eagerly, ``--graph``
+replays large layers too).  The default workload is one layer shaped like
 Wan-2.1-1.3B at 480p: B=1, H=12, d=128, 21x30x52 = 32760 tokens, 64-token
 blocks, top-k at 25% density (k = 128 of 512 key blocks).  ``--config N``
 selects another of the five workloads (0 tiny reference, 1 the default,
@@ -83,7 +84,9 @@ def parse():
                          "permutation, cluster top-p 0.9 with the page's Min-kc, attention over "
                          "the clusters) and report its stages")
     ap.add_argument("--no-graph", action="store_true",
-                    help="launch every step's kernels eagerly instead of replaying a HIP graph")
+                    help="launch every step's kernels eagerly (small layers replay a HIP graph)")
+    ap.add_argument("--graph", action="store_true",
+                    help="replay the step as a HIP graph on large layers too")
     ap.add_argument("--serial", action="store_true",
                     help="run every stage of a step on one stream (no overlap)")
     ap.add_argument("--calibration-copy", action="store_true",
@@ -251,24 +254,30 @@ def main():
             micro=dict(m=micro["m"], scale=scale, head_mask=micro["mask"], macro=(rp, ci),
                        qpool16=sc["qpool16"], kpool16=sc["kpool16"]))
 
-    main = torch.cuda.current_stream(dev)
     aux = torch.cuda.Stream(device=dev)  # default priority
-    # launch-bound layers lose more to the cross-stream join than they gain
-    two_streams = not args.serial and B * H * N * d >= (1 << 24)
+    # Small layers are launch-bound: one stream, the step replayed as a HIP
+    # graph.  Large layers: eager launches with the V staging on a side
+    # stream (replaying them as graphs measured no gain).
+    small = B * H * N * d < (1 << 24)
+    two_streams = not args.serial and not small
+    use_graph = (small or args.graph) and not args.no_graph
 
     def step(call=0, overlap=two_streams):
         # The V^T staging runs on a second stream beside scoring and
         # selection (running the micro branch beside the macro attention as
         # well measured no gain: both fill the chip).
+        # fork from and join to the stream the step is issued on (the capture
+        # stream while a graph is recorded)
+        cur = torch.cuda.current_stream(dev)
         if overlap:
-            aux.wait_stream(main)
+            aux.wait_stream(cur)
             with torch.cuda.stream(aux):
                 bsa.bsa_attn_stage_v(V, workspace=ws)
         # the static window needs no scores: the selection runs on the mask alone
         sc = score() if (mode != "static" or micro) else {"scores": None}
         rp, ci, nnz = select(sc, call)
         if overlap:
-            main.wait_stream(aux)
+            cur.wait_stream(aux)
         bsa.bsa_sparse_attn_fwd(Q, K, None if overlap else V, rp, ci, out=O_buf, lse=L_buf,
                                 workspace=ws)
         if args.rectify:
@@ -300,7 +309,7 @@ def main():
     # work between the replays, and must give its eager step's bits.
     run = step
     graphs = []
-    if not args.no_graph:
+    if use_graph:
         variants = N_ROTATIONS if (mode == "static" and not args.mod_mask) else 1
         refs = []
         for r in range(variants):
@@ -316,8 +325,10 @@ def main():
             graphs.append((g, outs))
         for _ in range(3):
             for r, (g, _outs) in enumerate(graphs):
+                # clear what a replay must rewrite: outputs and the staged V^T
                 O_buf.zero_()
                 L_buf.zero_()
+                ws.zero_()
                 g.replay()
                 torch.cuda.synchronize()
                 if not (torch.equal(O_buf, refs[r][0]) and torch.equal(L_buf, refs[r][1])):

@@ -59,6 +59,7 @@ def test_graph_replay_equals_eager(grid, H, d):
     for rep in range(4):
         O.fill_(float(rep))
         L.zero_()
+        ws.zero_()  # the replay must stage V^T again
         g.replay()
         torch.cuda.synchronize()
         assert torch.equal(O, ref[0]) and torch.equal(L, ref[1]), f"replay {rep}"
