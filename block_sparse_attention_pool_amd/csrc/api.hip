@@ -230,7 +230,7 @@ bsa_status plan_cluster_attn(const bsa_shape* s, int32_t Nq, int32_t Nk, int32_t
 // Workspace of bsa_cluster_merge.
 struct ClusterMergePlan {
   int64_t BH, W, nbits;
-  int64_t gsq, gk, alist, blist, nab, choice, gain, ukeys, gmask, planes, total;
+  int64_t gsq, gk, alist, blist, nab, choice, gain, ukeys, gmask, planes, hbits, total;
 };
 
 bsa_status plan_cluster_merge(int32_t B, int32_t H, int32_t N, int32_t Nq, int32_t Nk,
@@ -264,6 +264,7 @@ bsa_status plan_cluster_merge(int32_t B, int32_t H, int32_t N, int32_t Nq, int32
   p.ukeys = take(p.BH * Nq * 4);
   p.gmask = take(p.BH * Nq * p.W * 4);
   p.planes = take(p.BH * p.nbits * p.W * 4);
+  p.hbits = take(p.BH * 4);
   p.total = at;
   *pl = p;
   return BSA_OK;
@@ -1323,6 +1324,7 @@ bsa_status bsa_cluster_merge(const int32_t* off_q, const int32_t* off_k, const i
   m.ukeys = (int32_t*)(ws + pl.ukeys);
   m.gmask = (uint32_t*)(ws + pl.gmask);
   m.planes = (uint32_t*)(ws + pl.planes);
+  m.hbits = (int32_t*)(ws + pl.hbits);
   return hip_status(bsa::launch_cluster_merge(m, (int)pl.BH, (hipStream_t)stream),
                     "cluster merge launch");
 }

@@ -222,6 +222,7 @@ struct ClusterMergeArgs {
   int32_t* choice;         // [BH, Nq] best target of each chooser (-1 none)
   int64_t* gain;           // [BH, Nq]
   int32_t* ukeys;          // [BH, Nq] key slots of chooser + best target
+  int32_t* hbits;          // [BH] bit planes in use per head (largest slot count)
 };
 // Most query or key clusters per head of the cluster attention plan and the
 // merging (per-head tables held in LDS; key masks of at most 128 words).

@@ -50,12 +50,32 @@ __global__ __launch_bounds__(256) void merge_planes_kernel(ClusterMergeArgs a) {
   }
 }
 
+// Bits of the largest key-slot count of each head (planes above it are
+// zero and are skipped).  One workgroup of 256 per head.
+__global__ __launch_bounds__(256) void merge_bits_kernel(ClusterMergeArgs a) {
+  __shared__ int red[4];
+  const int64_t bh = blockIdx.x;
+  const int32_t* ok = a.off_k + bh * (a.Nk + 1);
+  int m = 0;
+  for (int j = threadIdx.x; j < a.Nk; j += 256)
+    m = max(m, (ok[j + 1] - ok[j] + a.grain - 1) / a.grain);
+  for (int off = 32; off > 0; off >>= 1) m = max(m, __shfl_xor(m, off));
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    m = max(max(red[0], red[1]), max(red[2], red[3]));
+    int bits = 0;
+    while (bits < a.nbits && (m >> bits) != 0) ++bits;
+    a.hbits[bh] = bits;
+  }
+}
+
 // Weighted popcount of the union of two masks, one lane per word (W <= 128:
-// two words per lane); the plane words come from LDS.
+// two words per lane); the plane words come from LDS; nb planes.
 __device__ __forceinline__ int union_slots(const ClusterMergeArgs& a, const uint32_t* pl,
-                                           uint32_t u0, uint32_t u1, int lane) {
+                                           uint32_t u0, uint32_t u1, int lane, int nb) {
   int s = 0;
-  for (int b = 0; b < a.nbits; ++b) {
+  for (int b = 0; b < nb; ++b) {
     int c = 0;
     if (lane < a.W) c += __popc(u0 & pl[b * a.W + lane]);
     if (lane + 64 < a.W) c += __popc(u1 & pl[b * a.W + lane + 64]);
@@ -88,7 +108,7 @@ __global__ __launch_bounds__(256) void merge_init_kernel(ClusterMergeArgs a) {
   uint32_t* m = a.gmask + r * a.W;
   if (lane < a.W) m[lane] = u0;
   if (lane + 64 < a.W) m[lane + 64] = u1;
-  const int k = union_slots(a, pl, u0, u1, lane);
+  const int k = union_slots(a, pl, u0, u1, lane, a.hbits[bh]);
   if (lane == 0) {
     a.grp[r] = i;
     a.gsq[r] = a.off_q[bh * (a.Nq + 1) + i + 1] - a.off_q[bh * (a.Nq + 1) + i];
@@ -151,6 +171,7 @@ __global__ __launch_bounds__(256) void merge_gain_kernel(ClusterMergeArgs a) {
   for (int t = threadIdx.x; t < a.nbits * a.W; t += 256) pl[t] = a.planes[bh * a.nbits * a.W + t];
   __syncthreads();
   const int na = a.nab[bh * 2], nb = a.nab[bh * 2 + 1];
+  const int hb = a.hbits[bh];
   if (ai >= na) return;
   const int A = a.alist[bh * a.Nq + ai];
   const int64_t ra = bh * a.Nq + A;
@@ -167,7 +188,7 @@ __global__ __launch_bounds__(256) void merge_gain_kernel(ClusterMergeArgs a) {
     const uint32_t* mb = a.gmask + rb * a.W;
     const uint32_t u0 = a0 | (lane < a.W ? mb[lane] : 0u);
     const uint32_t u1 = a1 | (lane + 64 < a.W ? mb[lane + 64] : 0u);
-    const int k = union_slots(a, pl, u0, u1, lane);
+    const int k = union_slots(a, pl, u0, u1, lane, hb);
     const int64_t sqb = a.gsq[rb];
     const int64_t gain = group_cost(a, sqa + sqb, k) - ca - group_cost(a, sqb, a.gk[rb]);
     if (bestB < 0 || gain < best) {
@@ -238,6 +259,7 @@ __global__ __launch_bounds__(1024) void merge_apply_kernel(ClusterMergeArgs a) {
 hipError_t launch_cluster_merge(const ClusterMergeArgs& a0, int BH, hipStream_t s) {
   ClusterMergeArgs a = a0;
   hipLaunchKernelGGL(merge_planes_kernel, dim3((a.W + 255) / 256, BH), dim3(256), 0, s, a);
+  hipLaunchKernelGGL(merge_bits_kernel, dim3(BH), dim3(256), 0, s, a);
   const dim3 wgrid((a.Nq + 3) / 4, BH);
   hipLaunchKernelGGL(merge_init_kernel, wgrid, dim3(256), 0, s, a);
   for (int r = 0; r < a.rounds; ++r) {

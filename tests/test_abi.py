@@ -311,7 +311,8 @@ def test_cluster_attention_and_merge_validation_and_workspace():
     assert st == 1 and "group_of" in bsa.bsa_last_error()
     # merging: slot counts up to ceil(1000 / 16) = 63 need 6 bit planes
     mw = sum(_align(x) for x in (2 * Nq * 4, 2 * Nq * 4, 2 * Nq * 4, 2 * Nq * 4, 2 * 2 * 4,
-                                 2 * Nq * 4, 2 * Nq * 8, 2 * Nq * 4, 2 * Nq * W * 4, 2 * 6 * W * 4))
+                                 2 * Nq * 4, 2 * Nq * 8, 2 * Nq * 4, 2 * Nq * W * 4, 2 * 6 * W * 4,
+                                 2 * 4))
     assert L.bsa_cluster_merge_workspace_bytes(1, 2, 1000, Nq, Nk, 16) == mw
     assert L.bsa_cluster_merge_workspace_bytes(1, 2, 1000, Nq, Nk, 0) == -1
     assert L.bsa_cluster_merge_workspace_bytes(1, 2, 1000, Nq, 5000, 16) == -1
