@@ -491,6 +491,11 @@ void micro_select_kernel(MicroSelectArgs a) {
       }
     }
   };
+  // every score load issued before any is used (in-bounds addresses, so the
+  // loads need no branch and all of them are in flight at once)
+  float sv[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) sv[e] = sig[min(e * 1024 + tid, ncand - 1)];
   uint32_t key[E];
   int nvalid = 0;
   for_codes([&](int e, int beta, uint32_t) {
@@ -498,7 +503,7 @@ void micro_select_kernel(MicroSelectArgs a) {
     key[e] = 0u;
     if (c < ncand) {
       const int blk = beta >> 2;
-      if (((omask[blk >> 5] >> (blk & 31)) & 1u) == 0u) key[e] = max(1u, float_order_key(sig[c]));
+      if (((omask[blk >> 5] >> (blk & 31)) & 1u) == 0u) key[e] = max(1u, float_order_key(sv[e]));
     }
     nvalid += key[e] != 0u;
   });
