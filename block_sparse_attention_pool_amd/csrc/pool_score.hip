@@ -36,15 +36,21 @@ __global__ __launch_bounds__(256) void pool_kernel(PoolArgs a) {
   float acc[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) acc[e] = 0.f;
+  // All of the group's rows are loaded before any is added (clamped to the
+  // last token, so every address is in bounds); rows past N add nothing.
+  u32x4 v[TPG];
 #pragma unroll
   for (int t = 0; t < TPG; ++t) {
-    const int tok = i * BLK + g * TPG + t;
-    if (tok < a.N) {
-      const u32x4 v = *(const u32x4*)(X + (int64_t)tok * a.sn + c * 8);
+    const int tok = min(i * BLK + g * TPG + t, a.N - 1);
+    v[t] = *(const u32x4*)(X + (int64_t)tok * a.sn + c * 8);
+  }
+#pragma unroll
+  for (int t = 0; t < TPG; ++t) {
+    if (i * BLK + g * TPG + t < a.N) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        acc[2 * e] += bf16_bits_to_f32(v[e] & 0xFFFFu);
-        acc[2 * e + 1] += bf16_bits_to_f32(v[e] >> 16);
+        acc[2 * e] += bf16_bits_to_f32(v[t][e] & 0xFFFFu);
+        acc[2 * e + 1] += bf16_bits_to_f32(v[t][e] >> 16);
       }
     }
   }

@@ -131,12 +131,17 @@ void rectify_kernel(RectifyArgs a) {
 
   const int64_t base = (int64_t)b * a.sb + (int64_t)h * a.sh;
   const int q = q0 + n16;
+  // the query rows are loaded together from clamped (in-bounds) rows, then
+  // rows past N are zeroed
+  const uint16_t* qrow = a.Q + base + (int64_t)min(q, a.N - 1) * a.sn + 8 * g4;
+  u32x4 qv[KS];
+#pragma unroll
+  for (int s = 0; s < KS; ++s) qv[s] = *(const u32x4*)(qrow + 32 * s);
   bf16x8 qf[KS];
 #pragma unroll
   for (int s = 0; s < KS; ++s) {
-    u32x4 v = {0u, 0u, 0u, 0u};
-    if (q < a.N) v = *(const u32x4*)(a.Q + base + (int64_t)q * a.sn + 32 * s + 8 * g4);
-    qf[s] = __builtin_bit_cast(bf16x8, v);
+    if (q >= a.N) qv[s] = u32x4{0u, 0u, 0u, 0u};
+    qf[s] = __builtin_bit_cast(bf16x8, qv[s]);
   }
   f32x4 o[DT];
 #pragma unroll
@@ -256,10 +261,15 @@ void rectify_kernel(RectifyArgs a) {
     wp = ep > 0.f ? ep / (sum * l_tot) : 0.f;  // l_tot > 0 whenever ep > 0
   }
   const int64_t orow = base + (int64_t)q * a.sn;
+  // the sparse output row is read whole before any of it is used; it is
+  // taken only when its weight is positive (otherwise it may be unwritten)
+  f32x4 osv[DT];
+#pragma unroll
+  for (int t = 0; t < DT; ++t) osv[t] = load4<OUT_BF16>(a.O, orow + 16 * t + 4 * g4);
 #pragma unroll
   for (int t = 0; t < DT; ++t) {
     const int64_t off = orow + 16 * t + 4 * g4;
-    const f32x4 os = ws > 0.f ? load4<OUT_BF16>(a.O, off) : f32x4{0.f, 0.f, 0.f, 0.f};
+    const f32x4 os = ws > 0.f ? osv[t] : f32x4{0.f, 0.f, 0.f, 0.f};
     store4<OUT_BF16>(a.O, off, ws * os[0] + wp * o[t][0], ws * os[1] + wp * o[t][1],
                      ws * os[2] + wp * o[t][2], ws * os[3] + wp * o[t][3]);
   }

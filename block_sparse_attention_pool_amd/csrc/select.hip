@@ -100,27 +100,35 @@ __global__ __launch_bounds__(256) void select_wave_kernel(SelectArgs a, int rows
   float val[E];  // top-p: the size-weighted exponentials
   if (scored) {
     const float* row = a.scores + (int64_t)r * a.nB;
+    // Every load is issued before any is used, from clamped (in-bounds)
+    // addresses, so the lane waits once instead of once per candidate.
     float x[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e) x[e] = row[min(64 * e + lane, a.nB - 1)];
     float mx = -INFINITY;
 #pragma unroll
     for (int e = 0; e < E; ++e) {
-      const int j = 64 * e + lane;
-      x[e] = j < a.nB ? row[j] : -INFINITY;
+      if (64 * e + lane >= a.nB) x[e] = -INFINITY;
       mx = fmaxf(mx, x[e]);
     }
-    if (a.mode == kTopP) mx = wave_max(mx);
-    const float tail_size = (float)(a.N - (a.nB - 1) * a.block);
+    float sz[E];  // top-p weight: the key block's valid tokens, or the given cluster size
+    if (a.mode == kTopP) {
+      const float tail_size = (float)(a.N - (a.nB - 1) * a.block);
+      if (a.col_sizes != nullptr) {
+        const int32_t* cs = a.col_sizes + (int64_t)(r / a.rows_per_head) * a.nB;
+#pragma unroll
+        for (int e = 0; e < E; ++e) sz[e] = (float)cs[min(64 * e + lane, a.nB - 1)];
+      } else {
+#pragma unroll
+        for (int e = 0; e < E; ++e) sz[e] = 64 * e + lane == a.nB - 1 ? tail_size : (float)a.block;
+      }
+      mx = wave_max(mx);
+    }
 #pragma unroll
     for (int e = 0; e < E; ++e) {
       const int j = 64 * e + lane;
       float v = x[e];
-      if (a.mode == kTopP) {
-        // weight: the key block's valid tokens, or the given cluster size
-        const float n = a.col_sizes != nullptr
-                            ? (float)a.col_sizes[(int64_t)(r / a.rows_per_head) * a.nB + min(j, a.nB - 1)]
-                            : (j == a.nB - 1 ? tail_size : (float)a.block);
-        v = n * expf(v - mx);
-      }
+      if (a.mode == kTopP) v = sz[e] * expf(v - mx);
       val[e] = j < a.nB ? v : 0.f;
       key[e] = j < a.nB ? float_order_key(v) : 0u;
     }
