@@ -176,7 +176,7 @@ bsa_status plan_cluster(const bsa_shape* s, const bsa_cluster_params* p, int64_t
 // most ceil(N/16) + Nk + 1 chunks); both layouts share one length NP.
 struct ClusterAttnPlan {
   int64_t NP, nTP, BH, W;
-  int64_t gt, qpos, kc, tg, srcq, gmask, cnt, rp, pairs, nent, kp, vp, vt, col, total, cap;
+  int64_t gt, qpos, kc, tg, srcq, gmask, cnt, rp, pairs, nent, kp, vt, col, total, cap;
 };
 
 bsa_status plan_cluster_attn(const bsa_shape* s, int32_t Nq, int32_t Nk, int32_t o_dtype,
@@ -219,7 +219,6 @@ bsa_status plan_cluster_attn(const bsa_shape* s, int32_t Nq, int32_t Nk, int32_t
   p.pairs = take(8);
   p.nent = take(8);
   p.kp = take(p.BH * p.NP * d * 2);
-  p.vp = take(p.BH * p.NP * d * 2);
   p.vt = take(p.BH * p.NP * d * 2);
   p.col = take(p.cap * 4);
   p.total = at;
@@ -1220,32 +1219,20 @@ bsa_status bsa_cluster_attn_fwd(const uint16_t* Q, const uint16_t* K, const uint
   c.pairs = (unsigned long long*)(out_tile_pairs != nullptr ? (void*)out_tile_pairs
                                                             : (void*)(ws + pl.pairs));
   c.Kp = (uint16_t*)(ws + pl.kp);
-  c.Vp = (uint16_t*)(ws + pl.vp);
+  c.Vt = (uint16_t*)(ws + pl.vt);
   int64_t* entries = (int64_t*)(ws + pl.nent);  // total chunk entries (unused)
   BSA_TRY(hip_status(bsa::launch_cluster_attn_plan(c, BH, D, st), "cluster plan launch"));
   BSA_TRY(hip_status(bsa::launch_scan(c.counts, (int)(pl.BH * Nq), c.row_ptr, entries, st),
                      "scan launch"));
   BSA_TRY(hip_status(bsa::launch_cluster_attn_emit(c, BH, D, st), "cluster emit launch"));
-  // padded tensors: [BH, NP, D], contiguous
+  // padded keys: [BH, NP, D], contiguous; V^T staged by the gather
   const int64_t sn = D, sh = pl.NP * D, sb = shape->H * sh;
-  bsa::TransposeArgs t{};
-  t.V = c.Vp;
-  t.Vt = (uint16_t*)(ws + pl.vt);
-  t.sb = sb;
-  t.sh = sh;
-  t.sn = sn;
-  t.H = shape->H;
-  t.N = c.NP;
-  t.nB = c.nTP;
-  t.Npad = c.NP;
-  t.heads = all_heads(shape->H);
-  BSA_TRY(hip_status(bsa::launch_transpose_v(t, shape->B, D, st), "transpose_v launch"));
   // queries and outputs in the caller's layout (rows through the source
   // map), keys and staged values in the padded layout
   bsa::AttnArgs a{};
   a.Q = Q;
   a.K = c.Kp;
-  a.Vt = t.Vt;
+  a.Vt = c.Vt;
   a.O = O;
   a.LSE = LSE;
   a.row_ptr = c.row_ptr;

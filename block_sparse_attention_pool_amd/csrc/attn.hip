@@ -29,14 +29,6 @@
 
 namespace bsa {
 
-// Position p (0..15) inside a 16-key chunk of V^T holds key
-// 8*((p%8)/4) + 4*(p/8) + (p%4): lane group g = p/8, slot j = p%8 of the
-// 32x32x16 operand maps to key 8*(j/4) + 4*g + j%4, which is the key order
-// of the 32x32 accumulator rows the lane holds.
-__device__ __forceinline__ int vt_key_of_pos(int p) {
-  return 8 * ((p & 7) >> 2) + 4 * (p >> 3) + (p & 3);
-}
-
 // ---------------------------------------------------------------- V^T
 
 template <int D>
@@ -51,13 +43,21 @@ __global__ __launch_bounds__(256) void transpose_v_kernel(TransposeArgs a) {
   const uint16_t* V = a.V + (int64_t)b * a.sb + (int64_t)h * a.sh;
   uint16_t* Vt = a.Vt + ((int64_t)b * a.H + h) * D * a.Npad;
 
-  for (int f = tid; f < 64 * C; f += 256) {
-    const int row = f / C, c = f % C;
-    const int key = j * kBlock + row;
-    u32x4 v = {0u, 0u, 0u, 0u};
-    if (key < a.N) v = *(const u32x4*)(V + (int64_t)key * a.sn + c * 8);
+  // every row load is issued before any is stored (rows past N read the
+  // last row, then zeros are stored)
+  constexpr int PER = 64 * C / 256;
+  u32x4 v[PER];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) tile[row][c * 4 + e] = v[e];
+  for (int u = 0; u < PER; ++u) {
+    const int f = tid + 256 * u;
+    v[u] = *(const u32x4*)(V + (int64_t)min(j * kBlock + f / C, a.N - 1) * a.sn + (f % C) * 8);
+  }
+#pragma unroll
+  for (int u = 0; u < PER; ++u) {
+    const int f = tid + 256 * u, row = f / C, c = f % C;
+    if (j * kBlock + row >= a.N) v[u] = u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) tile[row][c * 4 + e] = v[u][e];
   }
   __syncthreads();
   const uint16_t* t16 = (const uint16_t*)&tile[0][0];

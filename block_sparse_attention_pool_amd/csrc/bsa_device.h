@@ -55,6 +55,14 @@ __device__ __forceinline__ uint32_t bf16_bits_to_f16_bits(uint32_t h) {
   return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)bf16_bits_to_f32(h));
 }
 
+// Staged V^T: position p (0..15) inside a 16-key chunk holds key
+// 8*((p%8)/4) + 4*(p/8) + (p%4): lane group g = p/8, slot j = p%8 of the
+// 32x32x16 operand maps to key 8*(j/4) + 4*g + j%4, which is the key order
+// of the 32x32 accumulator rows the lane holds.
+__device__ __forceinline__ int vt_key_of_pos(int p) {
+  return 8 * ((p & 7) >> 2) + 4 * (p >> 3) + (p & 3);
+}
+
 // Monotone map of a float to uint32: a < b  <=>  key(a) < key(b).
 __device__ __forceinline__ uint32_t float_order_key(float x) {
   uint32_t u = __float_as_uint(x);

@@ -197,8 +197,8 @@ struct ClusterAttnArgs {
   int32_t* col_idx;        // chunk codes
   int64_t cap;
   unsigned long long* pairs;  // executed (query tile, key tile) pairs
-  uint16_t* Kp;            // [BH, NP, D] keys and values by chunk
-  uint16_t* Vp;
+  uint16_t* Kp;            // [BH, NP, D] keys by chunk
+  uint16_t* Vt;            // [BH, NP / 16, D, 16] staged fp16 V^T by chunk
 };
 
 // HVA parallel agglomerative merging of query clusters.

@@ -210,34 +210,88 @@ __global__ __launch_bounds__(256) void cemit_kernel(ClusterAttnArgs a) {
     if (p < a.cap) a.col_idx[p] = null_chunk;
 }
 
-// Padded copies of K and V: key position p of chunk p / 16 in key cluster j
-// holds token perm_k[off_k[j] + p - 16 kc[j]] while that is inside the
-// cluster, zeros otherwise.  One thread per 16-byte piece.
+// Keys and staged values by chunk.  Key position p of chunk p / 16 in key
+// cluster j holds token perm_k[off_k[j] + p - 16 kc[j]] while that is inside
+// the cluster, zeros otherwise; the same chunk of V^T holds those tokens'
+// values as fp16, transposed to [d][16] with the keys in the order the
+// attention's PV operand takes them.  One workgroup per key cluster (z = 0
+// keys, z = 1 values) takes its rows 64 at a time: all permutation entries
+// are loaded, then all rows, so each pass waits on memory twice.  Workgroup
+// Nk writes the all-padding chunk (the last chunk, zeros).  Chunks that no
+// cluster owns are never read and stay unwritten.
 template <int D>
 __global__ __launch_bounds__(256) void cgather_kernel(ClusterAttnArgs a) {
-  constexpr int C = D / 8;
-  const int64_t f = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  constexpr int C = D / 8;            // 16-byte pieces per row
+  constexpr int PER = 64 * C / 256;   // pieces per thread per 64-row pass
+  __shared__ uint32_t tile[64][D / 2 + 1];  // bf16 pairs; +1 word breaks bank aliasing
+  const int j = blockIdx.x;
   const int64_t bh = blockIdx.y;
   const bool values = blockIdx.z == 1;
-  if (f >= (int64_t)a.NP * C) return;
-  const int p = (int)(f / C), c = (int)(f % C);
-  int64_t tok = -1;
+  const int tid = threadIdx.x;
   const int32_t* kc = a.kc + bh * (a.Nk + 1);
-  const int chunk = p / 16;
-  if (chunk < kc[a.Nk]) {
-    const int j = seg_of(kc, a.Nk, chunk);
-    const int32_t* ok = a.off_k + bh * (a.Nk + 1);
-    const int k = p - 16 * kc[j];
-    if (k < ok[j + 1] - ok[j]) tok = a.perm_k[bh * a.N + ok[j] + k];
+  const int32_t* ok = a.off_k + bh * (a.Nk + 1);
+  int chunk0, nch, size = 0;
+  const int32_t* perm = a.perm_k + bh * a.N;
+  if (j < a.Nk) {
+    chunk0 = kc[j];
+    nch = kc[j + 1] - chunk0;
+    size = ok[j + 1] - ok[j];
+    perm += ok[j];
+  } else {
+    chunk0 = a.NP / 16 - 1;
+    nch = 1;
   }
-  const uint16_t* src = values ? a.V : a.K;
-  uint16_t* dst = (values ? a.Vp : a.Kp) + (bh * a.NP + p) * D;
-  u32x4 v = {0u, 0u, 0u, 0u};
-  if (tok >= 0) {
-    const int b = (int)(bh / a.H), h = (int)(bh % a.H);
-    v = *(const u32x4*)(src + (int64_t)b * a.sb + (int64_t)h * a.sh + tok * a.sn + 8 * c);
+  const int b = (int)(bh / a.H), h = (int)(bh % a.H);
+  const uint16_t* src = (values ? a.V : a.K) + (int64_t)b * a.sb + (int64_t)h * a.sh;
+  uint16_t* Kp = a.Kp + (bh * a.NP + 16 * (int64_t)chunk0) * D;
+  uint16_t* Vt = a.Vt + (bh * (a.NP / 16) + chunk0) * (int64_t)D * 16;
+  for (int r0 = 0; r0 < 16 * nch; r0 += 64) {
+    int tok[PER];
+    u32x4 v[PER];
+    if (size > 0) {  // uniform; rows past the cluster read its last token, then zero
+#pragma unroll
+      for (int u = 0; u < PER; ++u) tok[u] = perm[min(r0 + (tid + 256 * u) / C, size - 1)];
+#pragma unroll
+      for (int u = 0; u < PER; ++u)
+        v[u] = *(const u32x4*)(src + (int64_t)tok[u] * a.sn + 8 * ((tid + 256 * u) % C));
+    }
+#pragma unroll
+    for (int u = 0; u < PER; ++u)
+      if (size == 0 || r0 + (tid + 256 * u) / C >= size) v[u] = u32x4{0u, 0u, 0u, 0u};
+    if (!values) {
+#pragma unroll
+      for (int u = 0; u < PER; ++u) {
+        const int f = tid + 256 * u, row = r0 + f / C;
+        if (row < 16 * nch) *(u32x4*)(Kp + (int64_t)row * D + 8 * (f % C)) = v[u];
+      }
+      continue;
+    }
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      const int f = tid + 256 * u;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) tile[f / C][(f % C) * 4 + e] = v[u][e];
+    }
+    __syncthreads();
+    const uint16_t* t16 = (const uint16_t*)&tile[0][0];
+    constexpr int RS = D + 2;  // row stride of the tile in bf16 elements
+    for (int f = tid; f < D * 8; f += 256) {
+      const int d = f >> 3, q = f & 7;  // 8 output keys at positions 8q..8q+7 of the pass
+      const int c = r0 / 16 + (q >> 1);
+      if (c >= nch) continue;
+      uint32_t w[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int p0 = 8 * q + 2 * e;
+        const int k0 = 16 * (p0 >> 4) + vt_key_of_pos(p0 & 15);
+        const int k1 = 16 * ((p0 + 1) >> 4) + vt_key_of_pos((p0 + 1) & 15);
+        w[e] = bf16_bits_to_f16_bits(t16[k0 * RS + d]) |
+               (bf16_bits_to_f16_bits(t16[k1 * RS + d]) << 16);
+      }
+      *(u32x4*)(Vt + ((int64_t)c * D + d) * 16 + 8 * (q & 1)) = u32x4{w[0], w[1], w[2], w[3]};
+    }
+    __syncthreads();
   }
-  *(u32x4*)(dst + 8 * c) = v;
 }
 
 }  // namespace
@@ -261,7 +315,7 @@ hipError_t launch_cluster_attn_plan(const ClusterAttnArgs& a, int BH, int D, hip
 
 hipError_t launch_cluster_attn_emit(const ClusterAttnArgs& a, int BH, int D, hipStream_t s) {
   hipLaunchKernelGGL(cemit_kernel, dim3((a.Nq + 3) / 4, BH), dim3(256), 0, s, a);
-  const dim3 ggrid((unsigned)(((int64_t)a.NP * (D / 8) + 255) / 256), BH, 2);
+  const dim3 ggrid(a.Nk + 1, BH, 2);
   if (D == 128) hipLaunchKernelGGL(cgather_kernel<128>, ggrid, dim3(256), 0, s, a);
   else hipLaunchKernelGGL(cgather_kernel<64>, ggrid, dim3(256), 0, s, a);
   return hipGetLastError();

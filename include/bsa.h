@@ -533,8 +533,8 @@ bsa_status bsa_cluster_merge(const int32_t* off_q, const int32_t* off_k,
  * out_tile_pairs: device int64 or NULL; receives the number of executed
  *   (query tile, key tile) pairs, C(S) / 64^2 summed over the groups.
  * workspace: >= bsa_cluster_attn_workspace_bytes(shape, Nq, Nk, o_dtype)
- *   bytes, 256-byte aligned (padded copies of K and V, the staged V^T, the
- *   query source map and the chunk lists): padded length per head
+ *   bytes, 256-byte aligned (the padded copy of K, the staged V^T by chunk,
+ *   the query source map and the chunk lists): padded length per head
  *   64 * max(ceil(N/64) + Nq, ceil((ceil(N/16) + Nk + 1) / 4)).  Queries are
  *   read, and O and LSE written, in the caller's layout.
  * ---------------------------------------------------------------------- */

@@ -293,8 +293,7 @@ def test_cluster_attention_and_merge_validation_and_workspace():
     cap = 2 * Nq * (-(-1000 // 16) + Nk + 1 + 3)
     want = sum(_align(x) for x in (
         2 * (Nq + 1) * 4, 2 * Nq * 4, 2 * (Nk + 1) * 4, 2 * nTP * 4, 2 * NP * 4, 2 * Nq * W * 4,
-        2 * Nq * 4, (2 * Nq + 1) * 4, 8, 8, 2 * NP * 128 * 2, 2 * NP * 128 * 2,
-        2 * NP * 128 * 2, cap * 4))
+        2 * Nq * 4, (2 * Nq + 1) * 4, 8, 8, 2 * NP * 128 * 2, 2 * NP * 128 * 2, cap * 4))
     assert L.bsa_cluster_attn_workspace_bytes(ctypes.byref(s), Nq, Nk, 0) == want
     assert L.bsa_cluster_attn_workspace_bytes(ctypes.byref(s), 4097, Nk, 0) == -1
     assert "4096" in bsa.bsa_last_error()
