@@ -169,6 +169,7 @@ struct ClusterArgs {
 // Bucketed update limits: tokens per cell and window slots.
 constexpr int kMaxBucketCell = 2048;
 constexpr int kMaxBucketSlots = 1023;
+constexpr int kMaxAssignWindow = 1024;  // window cells the prefetching assignment tabulates
 
 // Attention over cluster-induced blocks (padded cluster order).
 struct ClusterAttnArgs {

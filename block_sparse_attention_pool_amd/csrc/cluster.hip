@@ -300,6 +300,134 @@ __global__ __launch_bounds__(1024) void cluster_assign_mfma_kernel(ClusterArgs a
   }
 }
 
+// The same assignment with the window's centroid ids and norms tabulated
+// once per cell (windows of at most kMaxAssignWindow cells) and the next
+// 32-centroid chunk loaded into registers while the current one is
+// multiplied, so the chunk copies overlap the matrix work.  PER 16-byte
+// pieces per thread cover a chunk's three parts; the results are those of
+// cluster_assign_mfma_kernel bit for bit (same products in the same order).
+template <int D, int PER>
+__global__ __launch_bounds__(PER >= 4 ? 512 : 1024) void cluster_assign_pf_kernel(ClusterArgs a) {
+  constexpr int DC = D / 8;          // 16-byte pieces per row
+  constexpr int KS = D / 16;         // k-steps
+  constexpr int NPC = 3 * 32 * DC;   // pieces per chunk
+  __shared__ __attribute__((aligned(16))) uint16_t cm[3 * 32 * D];
+  __shared__ int tid_of[kMaxAssignWindow];
+  __shared__ float tnorm[kMaxAssignWindow];
+  const int u = blockIdx.x;
+  const int64_t bh = blockIdx.y;
+  const int b = (int)(bh / a.H), h = (int)(bh % a.H);
+  const int uw = u % a.Kw, uh = (u / a.Kw) % a.Kh, ut = u / (a.Kw * a.Kh);
+  const int st = win_start(ut, a.wt, a.Kt), sh = win_start(uh, a.wh, a.Kh),
+            sw = win_start(uw, a.ww, a.Kw);
+  const int ncand = a.wt * a.wh * a.ww;
+  const int t0 = ut * a.kt, h0 = uh * a.kh, w0 = uw * a.kw;
+  const int lt = min(a.kt, a.T - t0), lh = min(a.kh, a.Hg - h0), lw = min(a.kw, a.W - w0);
+  const int ntok = lt * lh * lw;
+  const uint16_t* Xh = a.X + (int64_t)b * a.sb + (int64_t)h * a.sh;
+  const uint16_t* m3 = a.mu3 + bh * a.Nc * 3 * D;
+  const float* nrm = a.norm + bh * a.Nc;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int nthr = blockDim.x, nwaves = nthr >> 6;
+  const int n = lane & 31, g = lane >> 5;
+
+  for (int k = tid; k < ncand; k += nthr) {
+    const int vw = sw + k % a.ww, vh = sh + (k / a.ww) % a.wh, vt = st + k / (a.ww * a.wh);
+    const int vid = (vt * a.Kh + vh) * a.Kw + vw;
+    tid_of[k] = vid;
+    tnorm[k] = nrm[vid];
+  }
+  __syncthreads();
+  // one chunk's pieces: loads from clamped (in-bounds) candidates, then the
+  // LDS stores with zeros past the window
+  u32x4 stage[PER];
+  auto gload = [&](int c0) {
+#pragma unroll
+    for (int q = 0; q < PER; ++q) {
+      const int f = min(tid + nthr * q, NPC - 1);
+      const int part = f / (32 * DC), m = (f / DC) % 32, c = f % DC;
+      const int vid = tid_of[min(c0 + m, ncand - 1)];
+      stage[q] = *(const u32x4*)(m3 + ((int64_t)vid * 3 + part) * D + 8 * c);
+    }
+  };
+  auto lstore = [&](int c0) {
+#pragma unroll
+    for (int q = 0; q < PER; ++q) {
+      const int f = tid + nthr * q;
+      if (f < NPC) {
+        const int part = f / (32 * DC), m = (f / DC) % 32, c = f % DC;
+        const u32x4 v = c0 + m < ncand ? stage[q] : u32x4{0u, 0u, 0u, 0u};
+        *(u32x4*)&cm[(part * 32 + m) * D + ((c ^ (m % DC)) * 8)] = v;
+      }
+    }
+  };
+
+  for (int tb = 0; tb < ntok; tb += 32 * nwaves) {
+    const int p = tb + 32 * wave + n;  // this lane's token (column n)
+    const bool active = tb + 32 * wave < ntok;  // wave-uniform
+    int64_t tok = 0;
+    bf16x8 xf[KS];
+#pragma unroll
+    for (int s2 = 0; s2 < KS; ++s2) xf[s2] = bf16x8{};
+    if (p < ntok) {
+      const int pt = p / (lh * lw), ph = (p / lw) % lh, pw = p % lw;
+      tok = ((int64_t)(t0 + pt) * a.Hg + (h0 + ph)) * a.W + (w0 + pw);
+      const uint16_t* xr = Xh + tok * a.sn + 8 * g;
+#pragma unroll
+      for (int s2 = 0; s2 < KS; ++s2)
+        xf[s2] = __builtin_bit_cast(bf16x8, *(const u32x4*)(xr + 16 * s2));
+    }
+    float best = INFINITY;
+    int best_u = 0x7fffffff;
+    __syncthreads();  // the previous token batch no longer reads the chunk buffer
+    gload(0);
+    lstore(0);
+    __syncthreads();
+    for (int c0 = 0; c0 < ncand; c0 += 32) {
+      const bool more = c0 + 32 < ncand;
+      if (more) gload(c0 + 32);
+      if (active) {
+        f32x16 acc;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[r] = 0.f;
+#pragma unroll
+        for (int part = 0; part < 3; ++part)
+#pragma unroll
+          for (int s2 = 0; s2 < KS; ++s2) {
+            const bf16x8 af =
+                *(const bf16x8*)&cm[(part * 32 + n) * D + (((2 * s2 + g) ^ (n % DC)) * 8)];
+            acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, xf[s2], acc, 0, 0, 0);
+          }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int m = 8 * j + 4 * g + q;
+            const int k = min(c0 + m, ncand - 1);
+            const float dist = __builtin_fmaf(-2.f, acc[4 * j + q], tnorm[k]);
+            const int id = tid_of[k];
+            if (c0 + m < ncand && (dist < best || (dist == best && id < best_u))) {
+              best = dist;
+              best_u = id;
+            }
+          }
+        }
+      }
+      __syncthreads();  // every wave is done with this chunk
+      if (more) {
+        lstore(c0 + 32);
+        __syncthreads();
+      }
+    }
+    if (!active) continue;
+    // the other 16 candidates of this token sit in lane n ^ 32
+    const float ob = __shfl_xor(best, 32);
+    const int ou = __shfl_xor(best_u, 32);
+    if (ob < best || (ob == best && ou < best_u)) best_u = ou;
+    if (g == 0 && p < ntok) a.assign[bh * a.N + tok] = best_u;
+  }
+}
+
 // Squared norms of given centroids (for the ratio pass).
 template <int D>
 __global__ __launch_bounds__(D) void centroid_norm_kernel(ClusterArgs a) {
@@ -745,12 +873,33 @@ hipError_t launch_cluster_permute(const ClusterArgs& a, int BH, const int32_t* g
   return hipGetLastError();
 }
 
+// The prefetching assignment for windows of at most kMaxAssignWindow cells
+// (4 to 16 waves, one per 32 tokens of a cell; four or more pieces per
+// thread only with at most 448 threads), else the plain one.
+template <int D>
+void launch_assign(const ClusterArgs& a, dim3 grid, int ncand, int ctok, hipStream_t s) {
+  const int waves = min(16, (ctok + 31) / 32);
+  if (ncand > kMaxAssignWindow) {
+    hipLaunchKernelGGL(cluster_assign_mfma_kernel<D>, grid, dim3(64 * waves), 0, s, a);
+    return;
+  }
+  const int threads = 64 * max(4, waves);
+  const int per = (3 * 32 * (D / 8) + threads - 1) / threads;
+  switch (per) {
+    case 1: hipLaunchKernelGGL((cluster_assign_pf_kernel<D, 1>), grid, dim3(threads), 0, s, a); break;
+    case 2: hipLaunchKernelGGL((cluster_assign_pf_kernel<D, 2>), grid, dim3(threads), 0, s, a); break;
+    case 3: hipLaunchKernelGGL((cluster_assign_pf_kernel<D, 3>), grid, dim3(threads), 0, s, a); break;
+    case 4: hipLaunchKernelGGL((cluster_assign_pf_kernel<D, 4>), grid, dim3(threads), 0, s, a); break;
+    case 5: hipLaunchKernelGGL((cluster_assign_pf_kernel<D, 5>), grid, dim3(threads), 0, s, a); break;
+    default: hipLaunchKernelGGL((cluster_assign_pf_kernel<D, 6>), grid, dim3(threads), 0, s, a); break;
+  }
+}
+
 hipError_t launch_cluster(const ClusterArgs& a, int BH, int iters, hipStream_t s) {
   const dim3 grid(a.Nc, BH);
   const int ctok = a.kt * a.kh * a.kw;
   const int threads = min(512, ((ctok + 63) / 64) * 64);
-  // one wave per 32 tokens of a cell, at most 16
-  const int mthreads = 64 * min(16, (ctok + 31) / 32);
+  const int ncand = a.wt * a.wh * a.ww;
   (void)threads;
   // bucketed update when a cell's tokens and a window's slots fit the LDS
   // tables (the workspace then holds the buckets), else the box scan
@@ -759,7 +908,7 @@ hipError_t launch_cluster(const ClusterArgs& a, int BH, int iters, hipStream_t s
     hipLaunchKernelGGL(cluster_init_kernel<128>, grid, dim3(128), 0, s, a);
     for (int it = 0; it < iters; ++it) {
       hipLaunchKernelGGL(centroid_split_kernel<128>, grid, dim3(128), 0, s, a);
-      hipLaunchKernelGGL(cluster_assign_mfma_kernel<128>, grid, dim3(mthreads), 0, s, a);
+      launch_assign<128>(a, grid, ncand, ctok, s);
       if (buckets) {
         hipLaunchKernelGGL(cell_bucket_kernel, grid, dim3(256), 0, s, a);
         hipLaunchKernelGGL(cluster_update_bucket_kernel<128>, grid, dim3(256), 0, s, a);
@@ -771,7 +920,7 @@ hipError_t launch_cluster(const ClusterArgs& a, int BH, int iters, hipStream_t s
     hipLaunchKernelGGL(cluster_init_kernel<64>, grid, dim3(64), 0, s, a);
     for (int it = 0; it < iters; ++it) {
       hipLaunchKernelGGL(centroid_split_kernel<64>, grid, dim3(64), 0, s, a);
-      hipLaunchKernelGGL(cluster_assign_mfma_kernel<64>, grid, dim3(mthreads), 0, s, a);
+      launch_assign<64>(a, grid, ncand, ctok, s);
       if (buckets) {
         hipLaunchKernelGGL(cell_bucket_kernel, grid, dim3(256), 0, s, a);
         hipLaunchKernelGGL(cluster_update_bucket_kernel<64>, grid, dim3(256), 0, s, a);
