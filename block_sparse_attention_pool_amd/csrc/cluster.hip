@@ -674,14 +674,29 @@ __device__ int gather_covering(const ClusterArgs& a, int64_t bh, int u, int* cce
     ccnt[i] = bs[k + 1] - bs[k];
   }
   __syncthreads();
-  if (threadIdx.x == 0) {
-    int run = 0;
-    for (int i = 0; i < ncov; ++i) {
+  // exclusive offsets by a block scan: thread t takes items t*per .. t*per+per-1
+  __shared__ int wsum[16];
+  const int t = threadIdx.x, nthr = blockDim.x, lane = t & 63, wave = t >> 6;
+  const int per = (ncov + nthr - 1) / nthr;
+  int loc = 0;
+  for (int q = 0; q < per; ++q) {
+    const int i = t * per + q;
+    if (i < ncov) loc += ccnt[i];
+  }
+  const int inc = wave_inclusive_scan(loc);
+  if (lane == 63) wsum[wave] = inc;
+  __syncthreads();
+  int before = 0;
+  for (int w = 0; w < wave; ++w) before += wsum[w];
+  int run = before + inc - loc;
+  for (int q = 0; q < per; ++q) {
+    const int i = t * per + q;
+    if (i < ncov) {
       cofs[i] = run;
       run += ccnt[i];
     }
-    cofs[ncov] = run;
   }
+  if (t == nthr - 1) cofs[ncov] = before + inc;
   __syncthreads();
   return ncov;
 }
@@ -704,6 +719,7 @@ __global__ __launch_bounds__(256) void cluster_update_bucket_kernel(ClusterArgs 
   __shared__ int cb0[kMaxBucketSlots], ccnt[kMaxBucketSlots], cofs[kMaxBucketSlots + 1];
   __shared__ int ccell[kMaxBucketSlots];
   __shared__ int list[1024];
+  __shared__ float part[256 / (D / 8)][D + 1];
   __shared__ float red[4];
   const int u = blockIdx.x;
   const int64_t bh = blockIdx.y;
@@ -712,21 +728,48 @@ __global__ __launch_bounds__(256) void cluster_update_bucket_kernel(ClusterArgs 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int ncov = gather_covering(a, bh, u, ccell, cb0, ccnt, cofs);
   const int count = cofs[ncov];
-  float acc = 0.f;  // thread e < D owns dimension e
+  // member rows 16 bytes per thread: G members per pass, thread (g, c) adds
+  // dimensions 8c .. 8c+7 of members g, g + G, ... in order, four rows in
+  // flight; the G partial sums are then added in order of g (a fixed order)
+  constexpr int C = D / 8, G = 256 / C;
+  const int c = tid % C, gi = tid / C;
+  float acc[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) acc[e] = 0.f;
+  auto add = [&](const u32x4& w) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      acc[2 * e] += bf16_bits_to_f32(w[e] & 0xFFFFu);
+      acc[2 * e + 1] += bf16_bits_to_f32(w[e] >> 16);
+    }
+  };
   for (int base = 0; base < count; base += 1024) {
     const int nb = min(1024, count - base);
     for (int j = tid; j < nb; j += 256)
       list[j] = covering_member(a, bh, ncov, ccell, cb0, cofs, base + j);
     __syncthreads();
-    if (tid < D)
-      for (int j = 0; j < nb; ++j) acc += bf16_bits_to_f32(Xh[(int64_t)list[j] * a.sn + tid]);
+    int j = gi;
+    for (; j + 3 * G < nb; j += 4 * G) {
+      u32x4 w[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        w[q] = *(const u32x4*)(Xh + (int64_t)list[j + q * G] * a.sn + 8 * c);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) add(w[q]);
+    }
+    for (; j < nb; j += G) add(*(const u32x4*)(Xh + (int64_t)list[j] * a.sn + 8 * c));
     __syncthreads();  // list is rewritten by the next batch
   }
   if (tid == 0) a.counts[bh * a.Nc + u] = count;
   if (count == 0) return;  // the centroid keeps its position (and norm)
+#pragma unroll
+  for (int e = 0; e < 8; ++e) part[gi][8 * c + e] = acc[e];
+  __syncthreads();
   float v = 0.f;
   if (tid < D) {
-    v = acc / (float)count;
+    float sum = 0.f;
+    for (int k = 0; k < G; ++k) sum += part[k][tid];
+    v = sum / (float)count;
     a.mu[(bh * a.Nc + u) * D + tid] = v;
   }
   const float sq = wave_sum(tid < D ? v * v : 0.f);
