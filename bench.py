@@ -89,6 +89,9 @@ def parse():
                     help="replay the step as a HIP graph on large layers too")
     ap.add_argument("--serial", action="store_true",
                     help="run every stage of a step on one stream (no overlap)")
+    ap.add_argument("--torch-sdpa", action="store_true",
+                    help="also time torch's scaled_dot_product_attention on the same Q, K, V "
+                         "(flash backend only; reported for context)")
     ap.add_argument("--calibration-copy", action="store_true",
                     help="first run a plain 256 MiB device copy (reads 256 MiB, writes "
                          "256 MiB) three times, to scale hardware byte counters")
@@ -385,6 +388,20 @@ def main():
         lambda: bsa.bsa_dense_attn_fwd(Q, K, None, out=O_buf, lse=L_buf, workspace=ws),
         max(3, reps // 2) if dense_flops < 2e13 else 3, stream)
     L_full = L_buf.clone()
+    sdpa_out = None
+    if args.torch_sdpa:
+        # torch's fused attention on the same tensors, forced onto its flash
+        # backend (it raises rather than falling back to the unfused path)
+        from torch.nn.attention import SDPBackend, sdpa_kernel
+        try:
+            with sdpa_kernel([SDPBackend.FLASH_ATTENTION]):
+                sdpa_ms, _ = events_ms(
+                    lambda: torch.nn.functional.scaled_dot_product_attention(Q, K, V), 3, stream)
+            sdpa_out = {"backend": "flash", "ms": round(sdpa_ms, 4),
+                        "tflops": round(dense_flops / (sdpa_ms * 1e-3) / 1e12, 2),
+                        "dense_kernel_speedup": round(sdpa_ms / dense_ms, 3)}
+        except RuntimeError as ex:
+            sdpa_out = {"backend": "flash", "unavailable": str(ex)[:200]}
     score_ms, _ = events_ms(score, reps, stream) if mode != "static" else (0.0, None)
     select_ms, _ = events_ms(lambda: select(sc), reps, stream)
     attn_v_ms, _ = events_ms(
@@ -614,6 +631,7 @@ def main():
         "dense_kernel_tflops": round(dense_flops / (dense_ms * 1e-3) / 1e12, 2),
         "speedup_vs_dense": round(dense_ms / attn_ms, 3),
         "pipeline_speedup_vs_dense": round(dense_ms / (step_s * 1e3), 3),
+        **({"torch_sdpa": sdpa_out} if sdpa_out is not None else {}),
         "stages_ms": stages,
         "stage_gbs": gbs,
         "omission_risk": risk_out,
