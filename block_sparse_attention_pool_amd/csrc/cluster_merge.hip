@@ -23,10 +23,22 @@ namespace bsa {
 
 namespace {
 
+// t * ceil(x / t) for x >= 0, t >= 1: a 32-bit division whenever x fits
+// (the usual case; 64-bit division is a long instruction sequence).
+__device__ __forceinline__ int64_t ceil_multiple(uint64_t x, uint32_t t) {
+  uint64_t q;
+  if (x <= 0xFFFFFFFFull) {
+    const uint32_t x32 = (uint32_t)x;
+    q = x32 / t + (x32 % t != 0u ? 1u : 0u);
+  } else {
+    q = x / t + (x % t != 0u ? 1u : 0u);
+  }
+  return (int64_t)(q * t);
+}
+
 __device__ __forceinline__ int64_t group_cost(const ClusterMergeArgs& a, int64_t sq, int64_t k) {
-  const int64_t q = a.tau_q * ((sq + a.tau_q - 1) / a.tau_q);
-  const int64_t kk = a.tau_k * ((a.grain * k + a.tau_k - 1) / a.tau_k);
-  return q * kk;
+  return ceil_multiple((uint64_t)sq, (uint32_t)a.tau_q) *
+         ceil_multiple((uint64_t)a.grain * (uint64_t)k, (uint32_t)a.tau_k);
 }
 
 // Bit planes of the key clusters' slot counts ceil(s_j / g).  One thread per
@@ -163,41 +175,81 @@ __global__ __launch_bounds__(1024) void merge_sides_kernel(ClusterMergeArgs a) {
 
 // One wave per chooser A: the target B of smallest gain over the side-1
 // groups in ascending order (strict <, so ties keep the lower B).
+// The four choosers of a workgroup scan the same targets, so the workgroup
+// stages them together in LDS, kMergeChunk targets at a time (names, sizes
+// and masks in one pass); all plane and mask reads in the scan are then LDS
+// reads.
+constexpr int kMergeChunk = 32;
+
+__device__ __forceinline__ int union_slots_lds(const uint32_t* pl, int W, uint32_t u0,
+                                               uint32_t u1, int w0, int w1, int nb) {
+  // u0, u1 are zero on lanes past W, so the clamped plane words add nothing
+  int s = 0;
+  for (int b = 0; b < nb; ++b)
+    s += (__popc(u0 & pl[b * W + w0]) + __popc(u1 & pl[b * W + w1])) << b;
+  return wave_sum(s);
+}
+
 __global__ __launch_bounds__(256) void merge_gain_kernel(ClusterMergeArgs a) {
-  __shared__ uint32_t pl[32 * 128];
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  extern __shared__ uint32_t dyn[];
+  const int W = a.W;
+  uint32_t* pl = dyn;                                   // [nbits][W]
+  int* bl = (int*)(pl + a.nbits * W);                   // [kMergeChunk] target names
+  int* bsq = bl + kMergeChunk;                          // their query sizes
+  int* bgk = bsq + kMergeChunk;                         // their key slots
+  uint32_t* cmk = (uint32_t*)(bgk + kMergeChunk);       // [kMergeChunk][W] their masks
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int ai = blockIdx.x * 4 + wave;
   const int64_t bh = blockIdx.y;
-  for (int t = threadIdx.x; t < a.nbits * a.W; t += 256) pl[t] = a.planes[bh * a.nbits * a.W + t];
-  __syncthreads();
   const int na = a.nab[bh * 2], nb = a.nab[bh * 2 + 1];
+  const int32_t* blist = a.blist + bh * a.Nq;
+  for (int t = tid; t < a.nbits * W; t += 256) pl[t] = a.planes[bh * a.nbits * W + t];
   const int hb = a.hbits[bh];
-  if (ai >= na) return;
-  const int A = a.alist[bh * a.Nq + ai];
-  const int64_t ra = bh * a.Nq + A;
-  const uint32_t* ma = a.gmask + ra * a.W;
-  const uint32_t a0 = lane < a.W ? ma[lane] : 0u;
-  const uint32_t a1 = lane + 64 < a.W ? ma[lane + 64] : 0u;
-  const int64_t sqa = a.gsq[ra];
-  const int64_t ca = group_cost(a, sqa, a.gk[ra]);
+  const bool active = ai < na;  // inactive waves still stage and meet the barriers
+  const int w0 = min(lane, W - 1), w1 = min(lane + 64, W - 1);
+  uint32_t a0 = 0u, a1 = 0u;
+  int64_t sqa = 0, ca = 0, ra = 0;
+  if (active) {
+    ra = bh * a.Nq + a.alist[bh * a.Nq + ai];
+    const uint32_t* ma = a.gmask + ra * W;
+    a0 = lane < W ? ma[lane] : 0u;
+    a1 = lane + 64 < W ? ma[lane + 64] : 0u;
+    sqa = a.gsq[ra];
+    ca = group_cost(a, sqa, a.gk[ra]);
+  }
   int64_t best = 0;
   int bestB = -1, bestK = 0;
-  for (int bi = 0; bi < nb; ++bi) {
-    const int B = a.blist[bh * a.Nq + bi];
-    const int64_t rb = bh * a.Nq + B;
-    const uint32_t* mb = a.gmask + rb * a.W;
-    const uint32_t u0 = a0 | (lane < a.W ? mb[lane] : 0u);
-    const uint32_t u1 = a1 | (lane + 64 < a.W ? mb[lane + 64] : 0u);
-    const int k = union_slots(a, pl, u0, u1, lane, hb);
-    const int64_t sqb = a.gsq[rb];
-    const int64_t gain = group_cost(a, sqa + sqb, k) - ca - group_cost(a, sqb, a.gk[rb]);
-    if (bestB < 0 || gain < best) {
-      best = gain;
-      bestB = B;
-      bestK = k;
+  for (int c0 = 0; c0 < nb; c0 += kMergeChunk) {
+    const int nc = min(kMergeChunk, nb - c0);
+    for (int f = tid; f < nc * W; f += 256) {
+      const int t = f / W, w = f - t * W;
+      const int64_t rb = bh * a.Nq + blist[c0 + t];
+      cmk[f] = a.gmask[rb * W + w];
+      if (w == 0) {
+        bl[t] = (int)(rb - bh * a.Nq);
+        bsq[t] = a.gsq[rb];
+        bgk[t] = a.gk[rb];
+      }
     }
+    __syncthreads();
+    if (active) {
+      for (int t = 0; t < nc; ++t) {
+        const uint32_t* mb = cmk + t * W;
+        const uint32_t u0 = a0 | (lane < W ? mb[w0] : 0u);
+        const uint32_t u1 = a1 | (lane + 64 < W ? mb[w1] : 0u);
+        const int k = union_slots_lds(pl, W, u0, u1, w0, w1, hb);
+        const int64_t sqb = bsq[t];
+        const int64_t gain = group_cost(a, sqa + sqb, k) - ca - group_cost(a, sqb, bgk[t]);
+        if (bestB < 0 || gain < best) {
+          best = gain;
+          bestB = bl[t];
+          bestK = k;
+        }
+      }
+    }
+    __syncthreads();  // the mask chunk is rewritten next
   }
-  if (lane == 0) {
+  if (active && lane == 0) {
     a.choice[ra] = bestB;
     a.gain[ra] = best;
     a.ukeys[ra] = bestK;
@@ -261,11 +313,14 @@ hipError_t launch_cluster_merge(const ClusterMergeArgs& a0, int BH, hipStream_t 
   hipLaunchKernelGGL(merge_planes_kernel, dim3((a.W + 255) / 256, BH), dim3(256), 0, s, a);
   hipLaunchKernelGGL(merge_bits_kernel, dim3(BH), dim3(256), 0, s, a);
   const dim3 wgrid((a.Nq + 3) / 4, BH);
+  // planes and one chunk of targets (at most (32*128 + 3*32 + 32*128) * 4 bytes)
+  const size_t gain_lds =
+      sizeof(uint32_t) * ((size_t)a.nbits * a.W + 3 * kMergeChunk + kMergeChunk * (size_t)a.W);
   hipLaunchKernelGGL(merge_init_kernel, wgrid, dim3(256), 0, s, a);
   for (int r = 0; r < a.rounds; ++r) {
     a.round = r;
     hipLaunchKernelGGL(merge_sides_kernel, dim3(BH), dim3(1024), 0, s, a);
-    hipLaunchKernelGGL(merge_gain_kernel, wgrid, dim3(256), 0, s, a);
+    hipLaunchKernelGGL(merge_gain_kernel, wgrid, dim3(256), gain_lds, s, a);
     hipLaunchKernelGGL(merge_apply_kernel, dim3(BH), dim3(1024), 0, s, a);
   }
   return hipGetLastError();
