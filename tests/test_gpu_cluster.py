@@ -530,6 +530,27 @@ def test_cluster_cells_beyond_the_bucket_tables():
     np.testing.assert_array_equal(off[0, 0].cpu().numpy(), offo)
 
 
+def test_cluster_window_beyond_the_assignment_table():
+    """A window of 1,056 cells (more than the 1,024 the prefetching
+    assignment tabulates, and more than the bucketed update's slot table):
+    the plain matrix-core assignment and the box-scan update run instead;
+    clustering and permutation against the oracle."""
+    grid, cell, window = (1, 66, 64), (1, 2, 2), (1, 33, 32)
+    spec = VideoSpec(1, 1, 64, grid, 193)
+    Q, _, _ = gen_qkv(spec)
+    Qd = Q.to(DEV)
+    a, mu, c = bsa.bsa_local_window_cluster(Qd, grid, cell, window, 2)
+    perm, off = bsa.bsa_cluster_permute(a, c, Qd, grid, cell, window)
+    torch.cuda.synchronize()
+    assert c.shape[2] == 33 * 32
+    x = Q[0, 0].double().numpy()
+    compare_head(x, grid, cell, window, 2, a[0, 0].cpu().numpy(), mu[0, 0].double().cpu().numpy(),
+                 c[0, 0].cpu().numpy(), "window of 1056 cells")
+    po, offo = O.cluster_permutation(a[0, 0].cpu().numpy(), c.shape[2])
+    np.testing.assert_array_equal(perm[0, 0].cpu().numpy(), po)
+    np.testing.assert_array_equal(off[0, 0].cpu().numpy(), offo)
+
+
 def test_cluster_permutation_of_a_cluster_beyond_lds():
     """Identical tokens: every distance ties and each token takes the lowest
     index of its window, so centroid 0 collects all 4,096 tokens of the 2 x 2
