@@ -81,17 +81,22 @@ __global__ __launch_bounds__(256) void pool_kernel(PoolArgs a) {
   }
 }
 
-// Batched float32 C = scale * A B^T with A [M, D], B [Nc, D] per batch.
-// 64x64 output tile per workgroup, the shared dimension staged through LDS
-// in chunks of 32; each of the 4 waves computes one 32x32 quarter with the
-// float32 matrix-core product v_mfma_f32_32x32x2_f32 (fp32 products and
-// accumulation: no rounding of the means).  Batch z maps to the (b, h) pair
-// through the head list so the same kernel serves the pooled block scores
-// (all heads) and the micro tile scores (selected heads).
+// Batched C = scale * A B^T with A [M, D], B [Nc, D] float32 per batch, on
+// the bf16 matrix cores at float32 grade: every element is split exactly into
+// bf16 parts hi + mid + lo (hi = bf16(x), mid = bf16(x - hi), lo = bf16(x -
+// hi - mid), each difference exact in float32), and of the nine part products
+// the six down to relative order 2^-16 are summed (lo*hi, mid*mid, hi*lo,
+// mid*hi, hi*mid, hi*hi, smallest first) with float32 accumulation; the
+// dropped ones are below 2^-23 of the hi*hi term.  64x64 output tile per
+// workgroup, 4 waves of 32x32 (v_mfma_f32_32x32x16_bf16); the shared
+// dimension in chunks of 32, split while staged into LDS, the next chunk
+// loaded into registers while the current one is multiplied.  Batch z maps to
+// the (b, h) pair through the head list so the same kernel serves the pooled
+// block scores (all heads) and the micro tile scores (selected heads).
 __global__ __launch_bounds__(256) void score_gemm_kernel(GemmArgs a) {
-  constexpr int TK = 32;
-  __shared__ float As[TK][64 + 4];
-  __shared__ float Bs[TK][64 + 4];
+  constexpr int TK = 32, KP = TK + 8;  // chunk, padded LDS row (bf16 elements)
+  __shared__ __attribute__((aligned(16))) uint16_t As[3][64][KP];
+  __shared__ __attribute__((aligned(16))) uint16_t Bs[3][64][KP];
 
   const int z = blockIdx.z;
   const int b = z / a.heads.n;
@@ -106,33 +111,78 @@ __global__ __launch_bounds__(256) void score_gemm_kernel(GemmArgs a) {
   const int wave = tid >> 6, lane = tid & 63;
   const int wm = (wave >> 1) * 32, wn = (wave & 1) * 32;  // this wave's quarter
   const int l32 = lane & 31, kh = lane >> 5;
+  // staging: 64 rows x 32 floats per operand = 512 float4, 2 per thread each;
+  // rows past M or Nc read the last row and are zeroed when staged
+  f32x4 ra[2], rb[2];
+  const float* pa[2];
+  const float* pb[2];
+#pragma unroll
+  for (int it = 0; it < 2; ++it) {
+    const int f = tid + 256 * it, row = f >> 3, c4 = (f & 7) * 4;
+    pa[it] = A + (int64_t)min(m0 + row, a.M - 1) * a.D + c4;
+    pb[it] = Bm + (int64_t)min(n0 + row, a.Nc - 1) * a.D + c4;
+  }
+  auto gload = [&](int k0) {
+#pragma unroll
+    for (int it = 0; it < 2; ++it) {
+      ra[it] = *(const f32x4*)(pa[it] + k0);
+      rb[it] = *(const f32x4*)(pb[it] + k0);
+    }
+  };
+  // element pairs: one packed round-to-nearest-even conversion per part
+  auto split_store = [&](uint16_t(*dst)[64][KP], int row, int c4, f32x4 v, bool valid) {
+    uint32_t w[3][2];
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const float x0 = valid ? v[2 * e] : 0.f, x1 = valid ? v[2 * e + 1] : 0.f;
+      const uint32_t hi = pack_bf16x2(x0, x1);
+      const float r0 = x0 - __uint_as_float(hi << 16);
+      const float r1 = x1 - __uint_as_float(hi & 0xFFFF0000u);
+      const uint32_t mid = pack_bf16x2(r0, r1);
+      const float s0 = r0 - __uint_as_float(mid << 16);
+      const float s1 = r1 - __uint_as_float(mid & 0xFFFF0000u);
+      w[0][e] = hi;
+      w[1][e] = mid;
+      w[2][e] = pack_bf16x2(s0, s1);
+    }
+#pragma unroll
+    for (int part = 0; part < 3; ++part)
+      *(u32x2*)&dst[part][row][c4] = u32x2{w[part][0], w[part][1]};
+  };
+  auto lstore = [&]() {
+#pragma unroll
+    for (int it = 0; it < 2; ++it) {
+      const int f = tid + 256 * it, row = f >> 3, c4 = (f & 7) * 4;
+      split_store(As, row, c4, ra[it], m0 + row < a.M);
+      split_store(Bs, row, c4, rb[it], n0 + row < a.Nc);
+    }
+  };
+
   f32x16 acc;
 #pragma unroll
   for (int r = 0; r < 16; ++r) acc[r] = 0.f;
-
+  gload(0);
   for (int k0 = 0; k0 < a.D; k0 += TK) {
-    // 64 rows x 32 floats per operand = 512 float4; 2 per thread each.
+    lstore();
+    __syncthreads();
+    if (k0 + TK < a.D) gload(k0 + TK);
 #pragma unroll
-    for (int it = 0; it < 2; ++it) {
-      const int f = tid + 256 * it;
-      const int row = f >> 3, c4 = (f & 7) * 4;
-      f32x4 va = {0.f, 0.f, 0.f, 0.f}, vb = {0.f, 0.f, 0.f, 0.f};
-      if (m0 + row < a.M) va = *(const f32x4*)(A + (int64_t)(m0 + row) * a.D + k0 + c4);
-      if (n0 + row < a.Nc) vb = *(const f32x4*)(Bm + (int64_t)(n0 + row) * a.D + k0 + c4);
+    for (int s2 = 0; s2 < TK / 16; ++s2) {
+      const int kc = 16 * s2 + 8 * kh;
+      bf16x8 af[3], bf[3];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        As[c4 + e][row] = va[e];
-        Bs[c4 + e][row] = vb[e];
+      for (int part = 0; part < 3; ++part) {
+        af[part] = *(const bf16x8*)&As[part][wm + l32][kc];
+        bf[part] = *(const bf16x8*)&Bs[part][wn + l32][kc];
       }
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[2], bf[0], acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[1], bf[1], acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[0], bf[2], acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[1], bf[0], acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[0], bf[1], acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[0], bf[0], acc, 0, 0, 0);
     }
-    __syncthreads();
-    // k-step s covers shared indices 2s, 2s+1: lane holds A[wm + l32][2s + kh]
-    // and B[wn + l32][2s + kh]
-#pragma unroll
-    for (int s2 = 0; s2 < TK / 2; ++s2)
-      acc = __builtin_amdgcn_mfma_f32_32x32x2f32(As[2 * s2 + kh][wm + l32], Bs[2 * s2 + kh][wn + l32],
-                                                 acc, 0, 0, 0);
-    __syncthreads();
+    __syncthreads();  // the chunk is no longer read
   }
   // lane holds rows 8 (r/4) + 4 kh + r%4 of column l32 of the quarter
   const int n = n0 + wn + l32;
