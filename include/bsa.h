@@ -104,7 +104,9 @@ const char* bsa_last_error(void);
  * scores: float32 [B, H, nB, nB], or NULL to skip the score matrix.
  * micro: 0, or 16 to also write the 16-token tile means qpool16 / kpool16,
  *   float32 [B, H, nT, d] with nT = ceil(N / 16) (required when micro=16).
- * Accumulation is float32 (no bf16 rounding of the means or scores).
+ * Accumulation is float32 (no bf16 rounding of the means or scores); the
+ * dot products run on the bf16 matrix cores over exact three-part bf16
+ * splits of the means, with float32-grade error.
  * ---------------------------------------------------------------------- */
 bsa_status bsa_score_blocks(const uint16_t* Q, const uint16_t* K,
                             const bsa_shape* shape, int32_t block, float scale,
