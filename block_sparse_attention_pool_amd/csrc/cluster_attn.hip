@@ -17,9 +17,10 @@
 //
 // Kernels: the per-head plan (group sizes and tiles, query positions, key
 // chunk offsets), the padded query source map, the group key masks, the
-// per-group chunk counts and lists, the padded gathers of K and V, and the
-// masked attention, which reads every query row through the source map and
-// writes O and LSE straight to token order.
+// per-group chunk counts and lists, the gather of K by chunk and of V
+// straight into the staged fp16 V^T chunks, and the masked attention, which
+// reads every query row through the source map and writes O and LSE
+// straight to token order.
 #include "bsa_device.h"
 #include "bsa_internal.h"
 
