@@ -54,7 +54,10 @@ Readings where the pages are silent:
     returned;
   * RSA's pooled rectification is read as attention over the pooled keys of
     the omitted blocks (log-size bias), LSE-merged with the sparse result;
-    its gain-aware gate has no stated rule and is not modelled;
+    its gain-aware gate keeps block j for query q when the estimate's
+    pooling error under a normal isotropic key spread stays below its gain,
+    scale^2 |q|^2 v_j < 2 ln 2 (v_j the block's per-coordinate key
+    variance);
   * [HVA] Eq. 6 (Lowe's ratio) is taken over each token's local window,
     the candidates of its assignment, against the centroids given;
   * [HVA] Algorithm 1: the random bipartition is an input (a side bit per
@@ -357,6 +360,37 @@ def micro_select_row(Qt, Kt, macro_row, i, N, b, u, scale, m):
     return kept
 
 
+def micro_select_rows(Qt, Kt, macro_rows: list[list[int]], N: int, b: int, u: int,
+                      scale: float, m: int) -> list[list[int]]:
+    """``micro_select_row`` for every query block of a head at once: the
+    scores of all (query sub-tile, key tile) pairs are one matrix product
+    sigma = scale Qt Kt^T, then each block keeps its top-m candidates by
+    (sigma descending, code ascending), emitted in (a, beta) order."""
+    r = b // u
+    nT = n_blocks(N, u)
+    nB = n_blocks(N, b)
+    sig = scale * (np.asarray(Qt, np.float64) @ np.asarray(Kt, np.float64).T)
+    beta = np.arange(nT)
+    out = []
+    for i in range(nB):
+        omitted = np.ones(nB, dtype=bool)
+        omitted[list(macro_rows[i])] = False
+        bs = beta[omitted[beta // r]]
+        sg, cd = [], []
+        for a in range(r):
+            qa = r * i + a
+            if qa < nT:
+                sg.append(sig[qa, bs])
+                cd.append(r * bs + a)
+        if not sg or m <= 0:
+            out.append([])
+            continue
+        sg, cd = np.concatenate(sg), np.concatenate(cd)
+        kept = cd[np.lexsort((cd, -sg))[:m]]
+        out.append(sorted(kept.tolist(), key=lambda c: (c % r, c // r)))
+    return out
+
+
 def micro_attention(Q, K, V, micro_rows: list[list[int]], b: int, u: int,
                     scale: float):
     """Micro residual: each u-row query sub-tile attends over the union of its
@@ -409,43 +443,86 @@ def lse_merge(O1, L1, O2, L2):
 # n_j exp(scale q . Kbar_j) Vbar_j (exact when the block's keys are all
 # equal) -- and the estimate is combined with the sparse result by the
 # exact LSE merge, which also lowers the kept blocks' weights to their share
-# of the larger normaliser.  The page's gain-aware gate has no stated rule
-# and is not modelled.
+# of the larger normaliser.
+#
+# Gain-Aware Pooling Rectification ([RSA] abstract: the recovered gain must
+# exceed the pooling error it brings in) -- reading: for query q and omitted
+# block j the gain is the recovered mass w_hat = n_j exp(scale q . Kbar_j).
+# The block's true mass is w = w_hat * mean_tau exp(x_tau) with
+# x_tau = scale q . (k_tau - Kbar_j), a zero-mean spread; when the keys
+# scatter normally and isotropically about their mean with per-coordinate
+# variance v_j, x is normal with variance sigma^2 = scale^2 |q|^2 v_j and
+# mean_tau exp(x_tau) = exp(sigma^2 / 2), so the pooling error of the
+# estimate is w - w_hat = w_hat (exp(sigma^2 / 2) - 1).  The block is
+# rectified when gain > error, i.e. exp(sigma^2 / 2) < 2, i.e.
+#     scale^2 |q|^2 v_j < 2 ln 2,
+# with v_j = sum_tau |k_tau - Kbar_j|^2 / (n_j d) measured over the block's
+# valid keys.  The gate is per (query, block); the threshold has no free
+# parameter.
 # ----------------------------------------------------------------------------
 
-def pooled_omitted_attention(Q, K, V, rows: list[list[int]], b: int, scale: float):
+GATE_SIGMA2 = 2.0 * math.log(2.0)
+
+
+def block_key_spread(K, b: int) -> np.ndarray:
+    """v_j: mean squared deviation of block j's valid keys from their mean,
+    per coordinate, (1 / (n_j d)) sum_tau |k_tau - Kbar_j|^2."""
+    K = np.asarray(K, np.float64)
+    N, d = K.shape
+    Kb = pool_means(K, b)
+    return np.array([((K[block_tokens(N, b, j)] - Kb[j]) ** 2).sum() / (len(block_tokens(N, b, j)) * d)
+                     for j in range(n_blocks(N, b))])
+
+
+def rectify_gate(Q, K, b: int, scale: float) -> np.ndarray:
+    """[N, nB] booleans: True where query t's pooled estimate of block j
+    passes the gain-aware test scale^2 |q_t|^2 v_j < 2 ln 2."""
+    Q = np.asarray(Q, np.float64)
+    qn2 = (Q * Q).sum(axis=1)
+    v = block_key_spread(K, b)
+    return (scale * scale) * qn2[:, None] * v[None, :] < GATE_SIGMA2
+
+
+def pooled_omitted_attention(Q, K, V, rows: list[list[int]], b: int, scale: float,
+                             gate: bool = False):
     """For every valid query token t of block i, attention over the pooled
     keys of the blocks NOT in row i, each with log-size bias ln n_j:
         z_j = scale q_t . Kbar_j + ln n_j,
         LSE_t = ln sum_j e^{z_j},  O_t = sum_j e^{z_j - LSE_t} Vbar_j.
-    A row that keeps every block gets O = 0, LSE = -inf."""
+    With ``gate``, block j counts for token t only where ``rectify_gate``
+    passes.  A token with no block left gets O = 0, LSE = -inf."""
     Q = np.asarray(Q, np.float64)
     N = Q.shape[0]
     nB = n_blocks(N, b)
     Kb, Vb = pool_means(K, b), pool_means(V, b)
     logn = np.log(block_sizes(N, b))
+    G = rectify_gate(Q, K, b, scale) if gate else np.ones((N, nB), dtype=bool)
     O = np.zeros((N, Vb.shape[1]))
     L = np.full(N, NEG_INF)
     for i, sel in enumerate(rows):
         om = np.ones(nB, dtype=bool)
         om[list(sel)] = False
-        if not om.any():
-            continue
         qi = block_tokens(N, b, i)
-        z = scale * (Q[qi] @ Kb[om].T) + logn[om]
+        use = om[None, :] & G[qi]
+        live = use.any(axis=1)
+        if not live.any():
+            continue
+        z = np.where(use, scale * (Q[qi] @ Kb.T) + logn[None, :], NEG_INF)[live]
         mx = z.max(axis=1, keepdims=True)
         e = np.exp(z - mx)
         ssum = e.sum(axis=1)
-        L[qi] = mx[:, 0] + np.log(ssum)
-        O[qi] = (e @ Vb[om]) / ssum[:, None]
+        L[qi[live]] = mx[:, 0] + np.log(ssum)
+        O[qi[live]] = (e @ Vb) / ssum[:, None]
     return O, L
 
 
-def pooled_rectified_attention(Q, K, V, rows: list[list[int]], b: int, scale: float):
+def pooled_rectified_attention(Q, K, V, rows: list[list[int]], b: int, scale: float,
+                               gate: bool = False):
     """Sparse attention over the kept blocks, rectified by the pooled
-    estimate of the omitted ones through the exact LSE merge."""
+    estimate of the omitted ones (those passing the gain-aware test with
+    ``gate``) through the exact LSE merge."""
     Os, Ls = block_sparse_attention(Q, K, V, rows, b, scale)
-    Op, Lp = pooled_omitted_attention(Q, K, V, rows, b, scale)
+    Op, Lp = pooled_omitted_attention(Q, K, V, rows, b, scale, gate=gate)
     return lse_merge(Os, Ls, Op, Lp)
 
 

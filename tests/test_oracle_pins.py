@@ -693,6 +693,177 @@ def test_rectification_pin_catches_a_dropped_size_bias(monkeypatch):
     assert not np.allclose(Orc, ref, atol=1e-6)
 
 
+# ----------------------------------------------- gain-aware rectification
+
+def _golden_lse(vals):
+    return np.array([-np.inf if v == "-inf" else v for v in vals], float)
+
+
+def test_golden_rectify_gate():
+    g = _load("rectify_gate.json")
+    Q, K, V = (np.array(g[x], float) for x in ("Q", "K", "V"))
+    b, s = g["b"], g["scale"]
+    np.testing.assert_allclose(O.block_key_spread(K, b), g["spread"], atol=1e-15)
+    assert O.rectify_gate(Q, K, b, s).tolist() == g["gate"]
+    for case in g["cases"]:
+        Op, Lp = O.pooled_omitted_attention(Q, K, V, case["rows"], b, s, gate=True)
+        want_L = _golden_lse(case["LSE"])
+        assert np.array_equal(np.isneginf(Lp), np.isneginf(want_L))
+        fin = ~np.isneginf(want_L)
+        np.testing.assert_allclose(Lp[fin], want_L[fin], atol=1e-14)
+        np.testing.assert_allclose(Op, case["O"], atol=1e-14)
+        # no sparse part in these rows beyond the kept block: the rectified
+        # result of a row with nothing kept is the pooled part itself
+        Orc, Lrc = O.pooled_rectified_attention(Q, K, V, case["rows"], b, s, gate=True)
+        np.testing.assert_allclose(Orc[2:], Op[2:], atol=1e-14)
+
+
+@pytest.mark.parametrize("sigma2,passes", [(0.8 * math.log(4.0), True), (1.2 * math.log(4.0), False),
+                                           (0.3, True), (3.0, False)])
+def test_gate_threshold_is_where_the_measured_error_meets_the_gain(sigma2, passes):
+    # keys of one large block drawn isotropic normal (per-coordinate variance
+    # 1.5): the brute-force pooling error of the mass estimate, w - w_hat with
+    # w = sum_tau e^{s q.k_tau} and w_hat = n e^{s q.Kbar}, exceeds the gain
+    # w_hat exactly when the gate refuses the block
+    d, n, s = 8, 400_000, 1 / math.sqrt(8)
+    rng = np.random.default_rng(71)
+    K = 0.3 + math.sqrt(1.5) * rng.standard_normal((n, d))
+    u = rng.standard_normal(d)
+    v = float(O.block_key_spread(K, n)[0])
+    q = u / np.linalg.norm(u) * math.sqrt(sigma2 / (s * s * v))
+    kbar = K.mean(axis=0)
+    w_hat = n * math.exp(s * float(q @ kbar))
+    w = float(np.exp(s * (K @ q)).sum())
+    assert ((w - w_hat) < w_hat) == passes
+    assert bool(O.rectify_gate(q[None, :], K, n, s)[0, 0]) == passes
+
+
+def test_gate_passes_every_block_of_constant_keys():
+    # zero spread: the estimate is exact (gain, no error), the gated result is
+    # the ungated one and both equal full attention
+    N, b, d = 64 * 4 + 9, 64, 8
+    s = 1 / math.sqrt(d)
+    Q, V = 3.0 * _rand(62, N, d), _rand(63, N, d)
+    K = _blockwise_constant_keys(64, N, b, d)
+    # (the mean of equal keys carries rounding: the spread is ~1e-30, not 0)
+    assert np.all(O.block_key_spread(K, b) < 1e-25)
+    assert O.rectify_gate(Q, K, b, s).all()
+    rows = [[i] for i in range(O.n_blocks(N, b))]
+    Og, Lg = O.pooled_rectified_attention(Q, K, V, rows, b, s, gate=True)
+    Ou, Lu = O.pooled_rectified_attention(Q, K, V, rows, b, s)
+    np.testing.assert_array_equal(Og, Ou)
+    np.testing.assert_array_equal(Lg, Lu)
+
+
+def test_gated_part_is_the_mixture_over_passing_blocks():
+    # brute force with explicit loops: per token, the size-weighted mixture of
+    # value means over the omitted blocks whose spread test passes
+    N, b, d, s = 64 * 3 + 7, 64, 4, 0.45
+    Q, K, V = _rand(65, N, d), _rand(66, N, d), _rand(67, N, d)
+    Q[::3] *= 2.5                      # some tokens fail for some blocks
+    rows = [[0], [], [1, 3], [2]]
+    Op, Lp = O.pooled_omitted_attention(Q, K, V, rows, b, s, gate=True)
+    n_pass = n_fail = 0
+    for t in range(N):
+        i = t // b
+        num, den = np.zeros(d), 0.0
+        for j in range(O.n_blocks(N, b)):
+            if j in rows[i]:
+                continue
+            toks = range(b * j, min(b * j + b, N))
+            kb = sum(K[x] for x in toks) / len(toks)
+            vj = sum(float((K[x] - kb) @ (K[x] - kb)) for x in toks) / (len(toks) * d)
+            if s * s * float(Q[t] @ Q[t]) * vj >= 2 * math.log(2):
+                n_fail += 1
+                continue
+            n_pass += 1
+            w = len(toks) * math.exp(s * float(Q[t] @ kb))
+            num += w * sum(V[x] for x in toks) / len(toks)
+            den += w
+        if den == 0.0:
+            assert np.isneginf(Lp[t]) and np.all(Op[t] == 0)
+        else:
+            np.testing.assert_allclose(Op[t], num / den, atol=1e-13)
+            assert abs(Lp[t] - math.log(den)) < 1e-13
+    assert n_pass > 50 and n_fail > 50
+
+
+@pytest.mark.parametrize("mistake", ["threshold", "no_d", "norm_not_squared"])
+def test_gate_pins_catch_planted_mistakes(mistake, monkeypatch):
+    real_spread = O.block_key_spread
+    if mistake == "threshold":
+        monkeypatch.setattr(O, "GATE_SIGMA2", math.log(2.0))
+    elif mistake == "no_d":
+        monkeypatch.setattr(O, "block_key_spread",
+                            lambda K_, b_: real_spread(K_, b_) * np.asarray(K_).shape[1])
+    else:
+        def bad_gate(Q_, K_, b_, s_):
+            Q_ = np.asarray(Q_, np.float64)
+            qn = np.sqrt((Q_ * Q_).sum(axis=1))
+            return (s_ * s_) * qn[:, None] * real_spread(K_, b_)[None, :] < O.GATE_SIGMA2
+        monkeypatch.setattr(O, "rectify_gate", bad_gate)
+    with pytest.raises(AssertionError):
+        test_golden_rectify_gate()
+
+
+# ------------------------------------------------------------------ density
+
+def test_density_counts_blocks_over_the_whole_map():
+    # MOD-DiT, Metrics: computed B x B blocks over all blocks of every head's
+    # map.  Two heads of a 3 x 3 block map: 1 + 2 + 3 and 3 + 1 + 0 kept
+    # blocks, 10 of 18.
+    rows = [[[0], [0, 1], [0, 1, 2]], [[0, 1, 2], [1], []]]
+    assert O.density(rows, 3) == 10 / 18
+    # closed forms: the diagonal alone is 1/nB, every block is 1, top-k rows
+    # of length k are k/nB
+    nB = 16
+    assert O.density([[[i] for i in range(nB)]], nB) == 1 / nB
+    assert O.density([[list(range(nB))] * nB] * 3, nB) == 1.0
+    S = _rand(68, nB, nB)
+    rows_k = O.select_rows(S, 64 * nB, 64, "topk", k=4)
+    assert O.density([rows_k, rows_k], nB) == 4 / nB
+
+
+def test_density_of_the_long_horizon_window():
+    # the +-1-frame window with 4 anchors over 3072 blocks keeps about 2.55%
+    N, b, ft = 126 * 30 * 52, 64, 30 * 52
+    nB = O.n_blocks(N, b)
+    rows = [sorted(O.window_anchor_set(N, b, i, ft, 1, 4, 5)) for i in range(nB)]
+    dens = O.density([rows], nB)
+    assert 0.0245 < dens < 0.0265
+    # counted directly: every row's length over nB, averaged
+    assert abs(dens - np.mean([len(r) / nB for r in rows])) < 1e-15
+
+
+# ---------------------------------------------------- micro selection, all rows
+
+@pytest.mark.parametrize("N,m,seed", [(64 * 5 + 23, 7, 81), (64 * 3, 1000, 82), (64 * 6 + 1, 0, 83),
+                                      (64 * 4 + 40, 30, 84)])
+def test_micro_select_rows_equals_the_per_row_definition(N, m, seed):
+    b, u, d = 64, 16, 8
+    s = 1 / math.sqrt(d)
+    Q, K = _rand(seed, N, d), _rand(seed + 100, N, d)
+    S = O.pooled_scores(O.pool_means(Q, b), O.pool_means(K, b), s)
+    rows = O.select_rows(S, N, b, "topk", k=2, force_diag=True)
+    rows[1] = []
+    Qt, Kt = O.pool_means(Q, u), O.pool_means(K, u)
+    got = O.micro_select_rows(Qt, Kt, rows, N, b, u, s, m)
+    want = [O.micro_select_row(Qt, Kt, rows[i], i, N, b, u, s, m) for i in range(len(rows))]
+    assert got == want
+
+
+def test_micro_select_rows_breaks_exact_ties_by_code():
+    # every key tile equal: all candidates tie, the lowest codes 4 beta + a win
+    N, b, u = 64 * 3, 64, 16
+    Qt = np.ones((12, 2))
+    Kt = np.ones((12, 2))
+    rows = [[0], [1], [2]]
+    got = O.micro_select_rows(Qt, Kt, rows, N, b, u, 1.0, 5)
+    # block 0 omits blocks 1, 2 (tiles 4..11): codes 16, 17, 18, 19, 20 win
+    assert got[0] == [16, 20, 17, 18, 19]
+    assert got[1] == [0, 4, 1, 2, 3]
+
+
 # ------------------------------------------------------------ omission risk
 
 def test_golden_omission_three_keys():
