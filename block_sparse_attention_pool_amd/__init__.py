@@ -100,8 +100,12 @@ def _load(path: str = _LIB_PATH):
                                I64, P], I32),
         "bsa_cluster_select": ([P, P, P, I32, I32, I32, I32, I32, F32, F32, I32, I32, P, P, I64,
                                 P, P, I64, P], I32),
-        "bsa_pooled_rectify": ([P, P, P, SP, I32, F32, P, P, P, I32, P, P, I64, P], I32),
+        "bsa_pooled_rectify": ([P, P, P, SP, I32, F32, I32, P, P, P, I32, P, P, I64, P], I32),
         "bsa_omission_risk": ([P, P, P, SP, P, P, I64, P], I32),
+        "bsa_heads_at_risk": ([P, I32, I32, P], I32),
+        "bsa_attn_take_status": ([P, I64, SP, P, P], I32),
+        "bsa_check_csr": ([P, I64, P, I64, I32, P, P], I32),
+        "bsa_validate_csr_host": ([P, I64, P, I64, I32, P], I32),
     }
     for name, (args, res) in sig.items():
         fn = getattr(lib, name)
@@ -121,7 +125,8 @@ EXPORTED = ("bsa_version", "bsa_last_error", "bsa_score_blocks", "bsa_select_wor
             "bsa_cluster_select_workspace_bytes", "bsa_cluster_select",
             "bsa_cluster_attn_workspace_bytes", "bsa_cluster_attn_fwd",
             "bsa_cluster_merge_workspace_bytes", "bsa_cluster_merge", "bsa_lowe_ratio_subset",
-            "bsa_attn_stage_v")
+            "bsa_attn_stage_v", "bsa_heads_at_risk", "bsa_attn_take_status", "bsa_check_csr",
+            "bsa_validate_csr_host")
 
 
 def library_path() -> str:
@@ -311,11 +316,53 @@ def bsa_select_blocks(scores, Q_like, *, block: int = BLOCK, mode: str = "topk",
 
 
 def attn_workspace(Q) -> torch.Tensor:
+    """The attention calls' workspace, its status word (last 256 bytes)
+    zeroed."""
     shp = shape_of(Q)
     n = _lib.bsa_attn_workspace_bytes(ctypes.byref(shp))
     if n < 0:
         raise BsaError(f"bsa_attn_workspace_bytes: {bsa_last_error()}")
-    return torch.empty(max(n, 256), dtype=torch.uint8, device=Q.device)
+    ws = torch.empty(max(n, 256), dtype=torch.uint8, device=Q.device)
+    ws[-256:].zero_()
+    return ws
+
+
+def bsa_attn_take_status(workspace, Q_like, *, stream=None) -> torch.Tensor:
+    """The attention workspace's status word (device int32 [1]), cleared in
+    the workspace.  Bit 1: an out-of-range column or tile index was skipped
+    since the last clear."""
+    shp = shape_of(Q_like)
+    out = torch.empty(1, dtype=torch.int32, device=workspace.device)
+    st = _lib.bsa_attn_take_status(_ptr(workspace), workspace.numel(), ctypes.byref(shp),
+                                   _ptr(out), _stream(stream, workspace.device))
+    _check(st, "bsa_attn_take_status")
+    return out
+
+
+def bsa_check_csr(row_ptr, col_idx, n_cols: int, *, stream=None) -> torch.Tensor:
+    """Checks a device CSR (int32 row_ptr [rows + 1], int32 col_idx [cap]).
+    Returns device int32 [3]: rows with bad pointers, entries outside
+    [0, n_cols), entries not strictly ascending."""
+    counts = torch.empty(3, dtype=torch.int32, device=row_ptr.device)
+    st = _lib.bsa_check_csr(_ptr(row_ptr), row_ptr.numel() - 1, _ptr(col_idx), col_idx.numel(),
+                            n_cols, _ptr(counts), _stream(stream, row_ptr.device))
+    _check(st, "bsa_check_csr")
+    return counts
+
+
+def bsa_validate_csr_host(row_ptr, col_idx, n_cols: int) -> int:
+    """Validates a host CSR (int32 numpy arrays or CPU tensors).  Returns -1
+    when valid, else raises BsaError naming the first bad row."""
+    import numpy as np
+    rp = np.ascontiguousarray(np.asarray(row_ptr), dtype=np.int32)
+    ci = np.ascontiguousarray(np.asarray(col_idx), dtype=np.int32)
+    bad = ctypes.c_int64(-1)
+    st = _lib.bsa_validate_csr_host(rp.ctypes.data_as(ctypes.c_void_p), rp.size - 1,
+                                    ci.ctypes.data_as(ctypes.c_void_p), ci.size, n_cols,
+                                    ctypes.byref(bad))
+    if st != BSA_OK:
+        raise BsaError(f"bsa_validate_csr_host: row {bad.value}: {bsa_last_error()}")
+    return bad.value
 
 
 def bsa_sparse_attn_fwd(Q, K, V, row_ptr, col_idx, *, block: int = BLOCK,
@@ -407,9 +454,12 @@ def rectify_workspace(Q) -> torch.Tensor:
 
 
 def bsa_pooled_rectify(Q, K, V, row_ptr, col_idx, O, LSE, *, block: int = BLOCK,
-                       scale: float | None = None, workspace=None, stream=None):
+                       scale: float | None = None, gain_gate: bool = False, workspace=None,
+                       stream=None):
     """Adds the pooled estimate of every row's omitted key blocks to the
-    sparse result (O, LSE) of the same CSR, in place.  Returns (O, LSE)."""
+    sparse result (O, LSE) of the same CSR, in place; with ``gain_gate``
+    only the (query, block) pairs whose estimate passes the gain-aware test.
+    Returns (O, LSE)."""
     _same_layout(Q, K, V)
     shp = shape_of(Q)
     if O.shape != Q.shape or O.stride() != Q.stride():
@@ -417,8 +467,9 @@ def bsa_pooled_rectify(Q, K, V, row_ptr, col_idx, O, LSE, *, block: int = BLOCK,
     scale = 1.0 / math.sqrt(shp.d) if scale is None else scale
     ws = rectify_workspace(Q) if workspace is None else workspace
     st = _lib.bsa_pooled_rectify(_ptr(Q), _ptr(K), _ptr(V), ctypes.byref(shp), block, scale,
-                                 _ptr(row_ptr), _ptr(col_idx), _ptr(O), _odt(O.dtype), _ptr(LSE),
-                                 _ptr(ws), ws.numel(), _stream(stream, Q.device))
+                                 1 if gain_gate else 0, _ptr(row_ptr), _ptr(col_idx), _ptr(O),
+                                 _odt(O.dtype), _ptr(LSE), _ptr(ws), ws.numel(),
+                                 _stream(stream, Q.device))
     _check(st, "bsa_pooled_rectify")
     return O, LSE
 
@@ -605,12 +656,17 @@ def bsa_omission_risk(lse_sparse, lse_full, lse_repaired=None, *, out=None, stre
 
 
 def heads_at_risk(mean_omitted, n: int) -> list[int]:
-    """Offline calibration: the ``n`` heads with the largest mean omitted
-    share (equal values go to the lower head index), in ascending order --
-    the head set handed to the Micro residual."""
+    """Offline calibration (bsa_heads_at_risk): the ``n`` heads with the
+    largest mean omitted share (equal values go to the lower head index), in
+    ascending order -- the head set handed to the Micro residual."""
     vals = [float(v) for v in mean_omitted]
-    ranked = sorted(range(len(vals)), key=lambda h: (-vals[h], h))
-    return sorted(ranked[:max(0, n)])
+    H = len(vals)
+    arr = (ctypes.c_double * max(H, 1))(*vals)
+    mask = (ctypes.c_uint8 * max(H, 1))()
+    st = _lib.bsa_heads_at_risk(ctypes.cast(arr, ctypes.c_void_p), H, n,
+                                ctypes.cast(mask, ctypes.c_void_p))
+    _check(st, "bsa_heads_at_risk")
+    return [h for h in range(H) if mask[h]]
 
 
 def csr_rows(row_ptr: torch.Tensor, col_idx: torch.Tensor, nnz: torch.Tensor):

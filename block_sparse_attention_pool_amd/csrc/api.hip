@@ -2,6 +2,7 @@
 // any HIP call), workspace carving and kernel launches on the caller's
 // stream.  No state is kept between calls and nothing is allocated.
 #include <algorithm>
+#include <cmath>
 #include <cstdarg>
 #include <cstdio>
 #include <string>
@@ -79,7 +80,7 @@ bsa_status check_risk_shape(const bsa_shape* s, int64_t* chunks) {
 }
 
 struct RectifyPlan {
-  int64_t nB, nBp, BH, bytes_f, bytes_h, total;
+  int64_t nB, nBp, BH, bytes_f, bytes_h, bytes_s, total;
 };
 
 bsa_status plan_rectify(const bsa_shape* s, RectifyPlan* pl) {
@@ -93,7 +94,8 @@ bsa_status plan_rectify(const bsa_shape* s, RectifyPlan* pl) {
   pl->nBp = cdiv(pl->nB, 16) * 16;
   pl->bytes_f = align256(pl->BH * pl->nB * s->d * 4);   // each of Kbar, Vbar (float32)
   pl->bytes_h = align256(pl->BH * pl->nBp * s->d * 2);  // each of Khi, Klo, Vbar^T (16-bit)
-  pl->total = 2 * pl->bytes_f + 3 * pl->bytes_h;
+  pl->bytes_s = align256(pl->BH * pl->nBp * 4);          // key spread per block (gate)
+  pl->total = 2 * pl->bytes_f + 3 * pl->bytes_h + pl->bytes_s;
   return BSA_OK;
 }
 
@@ -101,7 +103,7 @@ bsa_status plan_rectify(const bsa_shape* s, RectifyPlan* pl) {
 // sub-tile ordering (signatures, order, bin counts and offsets, a total),
 // sized for every head.
 struct MicroOrderPlan {
-  int64_t vt_bytes, sig_off, order_off, hist_off, offs_off, nnz_off, order_bytes;
+  int64_t vt_bytes, sig_off, order_off, hist_off, offs_off, nnz_off, status_off, order_bytes;
 };
 
 MicroOrderPlan plan_micro_order(const bsa_shape* s) {
@@ -115,7 +117,8 @@ MicroOrderPlan plan_micro_order(const bsa_shape* s) {
   m.hist_off = m.order_off + align256(slots * 4);
   m.offs_off = m.hist_off + align256(bins * 4);
   m.nnz_off = m.offs_off + align256((bins + 1) * 4);
-  m.order_bytes = m.nnz_off + 256 - m.vt_bytes;
+  m.status_off = m.nnz_off + 256;  // the status word: the last 256 bytes
+  m.order_bytes = m.status_off + 256 - m.vt_bytes;
   return m;
 }
 
@@ -435,6 +438,7 @@ bsa_status run_attn(const uint16_t* Q, const uint16_t* K, const uint16_t* V, con
   a.scale_log2 = scale * 1.4426950408889634f;
   a.rows = s->B * s->H * nB;
   a.per_xcd = (int)cdiv(a.rows, 8);
+  a.status = (int32_t*)((char*)ws + plan_micro_order(s).status_off);
   return hip_status(bsa::launch_attn(a, s->d, dense, o_dtype == BSA_BF16, st), "attn launch");
 }
 
@@ -678,6 +682,73 @@ bsa_status bsa_sparse_attn_fwd(const uint16_t* Q, const uint16_t* K, const uint1
                   (hipStream_t)stream);
 }
 
+bsa_status bsa_attn_take_status(void* workspace, int64_t workspace_bytes,
+                                const bsa_shape* shape, int32_t* status_out, void* stream) {
+  BSA_TRY(check_shape(shape));
+  BSA_TRY(check_ptr(workspace, "workspace", 256));
+  BSA_TRY(check_ptr(status_out, "status_out", 4));
+  const int64_t need = bsa_attn_workspace_bytes(shape);
+  if (workspace_bytes < need)
+    return fail(BSA_ERR_CAPACITY, "workspace %lld bytes < required %lld",
+                (long long)workspace_bytes, (long long)need);
+  int32_t* status = (int32_t*)((char*)workspace + plan_micro_order(shape).status_off);
+  return hip_status(bsa::launch_take_status(status, status_out, (hipStream_t)stream),
+                    "status launch");
+}
+
+bsa_status bsa_check_csr(const int32_t* row_ptr, int64_t rows, const int32_t* col_idx,
+                         int64_t col_cap, int32_t n_cols, int32_t* counts, void* stream) {
+  if (rows < 0 || rows > INT32_MAX - 1) return fail(BSA_ERR_INVALID_ARG, "rows=%lld", (long long)rows);
+  if (col_cap < 0) return fail(BSA_ERR_INVALID_ARG, "col_cap < 0");
+  if (n_cols < 0) return fail(BSA_ERR_INVALID_ARG, "n_cols < 0");
+  BSA_TRY(check_ptr(row_ptr, "row_ptr", 4));
+  BSA_TRY(check_ptr(counts, "counts", 4));
+  if (col_cap > 0) BSA_TRY(check_ptr(col_idx, "col_idx", 4));
+  bsa::CsrCheckArgs a{};
+  a.row_ptr = row_ptr;
+  a.col_idx = col_idx;
+  a.cap = col_cap;
+  a.rows = (int)rows;
+  a.n_cols = n_cols;
+  a.counts = counts;
+  return hip_status(bsa::launch_csr_check(a, (hipStream_t)stream), "csr check launch");
+}
+
+bsa_status bsa_validate_csr_host(const int32_t* row_ptr, int64_t rows, const int32_t* col_idx,
+                                 int64_t col_cap, int32_t n_cols, int64_t* bad_row) {
+  if (bad_row != nullptr) *bad_row = -1;
+  if (rows < 0) return fail(BSA_ERR_INVALID_ARG, "rows=%lld < 0", (long long)rows);
+  if (row_ptr == nullptr) return fail(BSA_ERR_INVALID_ARG, "row_ptr is NULL");
+  if (col_cap < 0) return fail(BSA_ERR_INVALID_ARG, "col_cap < 0");
+  if (col_cap > 0 && col_idx == nullptr) return fail(BSA_ERR_INVALID_ARG, "col_idx is NULL");
+  if (row_ptr[0] != 0) {
+    if (bad_row != nullptr) *bad_row = 0;
+    return fail(BSA_ERR_INVALID_ARG, "row_ptr[0] = %d, not 0", row_ptr[0]);
+  }
+  for (int64_t r = 0; r < rows; ++r) {
+    const int64_t b = row_ptr[r], e = row_ptr[r + 1];
+    if (e < b || e > col_cap) {
+      if (bad_row != nullptr) *bad_row = r;
+      return fail(BSA_ERR_INVALID_ARG, "row %lld: row_ptr %lld..%lld out of order or past col_cap %lld",
+                  (long long)r, (long long)b, (long long)e, (long long)col_cap);
+    }
+    for (int64_t k = b; k < e; ++k) {
+      const int32_t v = col_idx[k];
+      if (v < 0 || v >= n_cols) {
+        if (bad_row != nullptr) *bad_row = r;
+        return fail(BSA_ERR_INVALID_ARG, "row %lld: column %d outside [0, %d)", (long long)r, v,
+                    n_cols);
+      }
+      if (k > b && v <= col_idx[k - 1]) {
+        if (bad_row != nullptr) *bad_row = r;
+        return fail(BSA_ERR_INVALID_ARG, "row %lld: columns not strictly ascending (%d after %d)",
+                    (long long)r, v, col_idx[k - 1]);
+      }
+    }
+  }
+  return BSA_OK;
+}
+
 bsa_status bsa_dense_attn_fwd(const uint16_t* Q, const uint16_t* K, const uint16_t* V,
                               const bsa_shape* shape, float scale, void* O, int32_t o_dtype,
                               float* LSE, void* workspace, int64_t workspace_bytes,
@@ -741,6 +812,7 @@ bsa_status bsa_micro_residual_fwd(const uint16_t* Q, const uint16_t* K, const ui
   a.hist = (int32_t*)(ws + m.hist_off);
   a.offsets = (int32_t*)(ws + m.offs_off);
   a.nnz = (int64_t*)(ws + m.nnz_off);
+  a.status = (int32_t*)(ws + m.status_off);
   a.nT = (int)cdiv(shape->N, 16);
   a.slots = (int)((int64_t)shape->B * heads.n * nB * 4);
   a.bins = shape->B * heads.n * (a.nT + 1);
@@ -813,6 +885,24 @@ bsa_status bsa_omission_risk(const float* lse_sparse, const float* lse_full,
   return hip_status(bsa::launch_risk(a, (hipStream_t)stream), "omission risk launch");
 }
 
+bsa_status bsa_heads_at_risk(const double* mean_omitted, int32_t H, int32_t n,
+                             uint8_t* head_mask) {
+  if (H <= 0) return fail(BSA_ERR_INVALID_ARG, "H=%d must be >= 1", H);
+  if (mean_omitted == nullptr || head_mask == nullptr)
+    return fail(BSA_ERR_INVALID_ARG, "mean_omitted / head_mask is NULL");
+  for (int h = 0; h < H; ++h)
+    if (std::isnan(mean_omitted[h])) return fail(BSA_ERR_INVALID_ARG, "share of head %d is NaN", h);
+  const int take = std::max(0, std::min(n, H));
+  // rank of head h in the order (share descending, index ascending)
+  for (int h = 0; h < H; ++h) {
+    int before = 0;
+    for (int g = 0; g < H; ++g)
+      before += mean_omitted[g] > mean_omitted[h] || (mean_omitted[g] == mean_omitted[h] && g < h);
+    head_mask[h] = before < take ? 1 : 0;
+  }
+  return BSA_OK;
+}
+
 int64_t bsa_pooled_rectify_workspace_bytes(const bsa_shape* shape) {
   RectifyPlan pl;
   if (plan_rectify(shape, &pl) != BSA_OK) return -1;
@@ -821,9 +911,9 @@ int64_t bsa_pooled_rectify_workspace_bytes(const bsa_shape* shape) {
 
 bsa_status bsa_pooled_rectify(const uint16_t* Q, const uint16_t* K, const uint16_t* V,
                               const bsa_shape* shape, int32_t block, float scale,
-                              const int32_t* row_ptr, const int32_t* col_idx, void* O,
-                              int32_t o_dtype, float* LSE, void* workspace,
-                              int64_t workspace_bytes, void* stream) {
+                              int32_t gain_gate, const int32_t* row_ptr,
+                              const int32_t* col_idx, void* O, int32_t o_dtype, float* LSE,
+                              void* workspace, int64_t workspace_bytes, void* stream) {
   RectifyPlan pl;
   BSA_TRY(plan_rectify(shape, &pl));
   if (block != 64) return fail(BSA_ERR_UNSUPPORTED, "block=%d unsupported (64)", block);
@@ -837,6 +927,10 @@ bsa_status bsa_pooled_rectify(const uint16_t* Q, const uint16_t* K, const uint16
   BSA_TRY(check_ptr(workspace, "workspace", 256));
   if (o_dtype != BSA_F32 && o_dtype != BSA_BF16)
     return fail(BSA_ERR_INVALID_ARG, "o_dtype=%d (BSA_F32 or BSA_BF16)", o_dtype);
+  if (gain_gate != 0 && gain_gate != 1)
+    return fail(BSA_ERR_INVALID_ARG, "gain_gate=%d (0 or 1)", gain_gate);
+  if (gain_gate && !(scale > 0.f))
+    return fail(BSA_ERR_INVALID_ARG, "the gain-aware gate needs scale > 0 (scale=%g)", scale);
   if (workspace_bytes < pl.total)
     return fail(BSA_ERR_CAPACITY, "workspace %lld bytes < required %lld",
                 (long long)workspace_bytes, (long long)pl.total);
@@ -867,6 +961,10 @@ bsa_status bsa_pooled_rectify(const uint16_t* Q, const uint16_t* K, const uint16
   a.Khi = (uint16_t*)(ws + 2 * pl.bytes_f);
   a.Klo = (uint16_t*)(ws + 2 * pl.bytes_f + pl.bytes_h);
   a.Vt = (uint16_t*)(ws + 2 * pl.bytes_f + 2 * pl.bytes_h);
+  a.K = K;
+  a.spread = (float*)(ws + 2 * pl.bytes_f + 3 * pl.bytes_h);
+  a.gate = gain_gate;
+  a.gate_thr = gain_gate ? (float)(2.0 * 0.6931471805599453 / ((double)scale * scale)) : 0.f;
   a.row_ptr = row_ptr;
   a.col_idx = col_idx;
   a.O = O;

@@ -447,22 +447,35 @@ void attn_fwd_kernel(AttnArgs a) {
   f16x8 pf_prev[4];
 #pragma unroll
   for (int cc = 0; cc < 4; ++cc) pf_prev[cc] = f16x8{};
-  // j: the key block (CHUNK: the position of its first chunk entry)
+  // j: the key block (CHUNK: the position of its first chunk entry).  A
+  // caller's column index outside [0, nB) becomes -1: its tiles are read
+  // from block 0 (in bounds), its scores are masked out and the status word
+  // records it, so such an entry adds nothing instead of reading outside K
+  // and V^T.
   constexpr int STEP = CHUNK ? 4 : 1;
+  auto key_block = [&](int e) {
+    if constexpr (DENSE || CHUNK) {
+      return e;
+    } else {
+      const int jr = col_idx[e];
+      return (unsigned)jr < (unsigned)a.nB ? jr : -1;
+    }
+  };
+  auto tile_of = [](int jj) { return jj < 0 ? 0 : jj; };
   int j = 0, jprev = 0;
   if (e0 < e1) {
-    j = (DENSE || CHUNK) ? e0 : col_idx[e0];
+    j = key_block(e0);
     jprev = j;
     if constexpr (CHUNK) cp.k_chunks(Kh, ksn, col_idx + j);
-    else cp.k_tile(Kh, a.sn, j, a.nB);
+    else cp.k_tile(Kh, a.sn, tile_of(j), a.nB);
   }
   for (int e = e0; e < e1; e += STEP) {
-    const int jn = (e + STEP < e1) ? ((DENSE || CHUNK) ? e + STEP : col_idx[e + 1]) : j;
+    const int jn = (e + STEP < e1) ? key_block(e + STEP) : j;
     wait_lgkm0();      // this wave's reads of sV (block e-2) have returned
     wait_vmcnt<0>();   // this wave's copy of K(e) has landed
     exec_barrier();    // ... and the other wave's; sV is free
     if constexpr (CHUNK) cp.v_chunks(Vth, col_idx + jprev);
-    else cp.v_tile(Vth, jprev);
+    else cp.v_tile(Vth, tile_of(jprev));
 
     // S^T for keys 0..31 (s0) and 32..63 (s1) of the block.
     f32x16 s0, s1;
@@ -493,7 +506,7 @@ void attn_fwd_kernel(AttnArgs a) {
     exec_barrier();    // both waves are done with sK; sV holds V(e-1)
     if (e + STEP < e1) {
       if constexpr (CHUNK) cp.k_chunks(Kh, ksn, col_idx + jn);
-      else cp.k_tile(Kh, a.sn, jn, a.nB);
+      else cp.k_tile(Kh, a.sn, tile_of(jn), a.nB);
     }
 
     f16x8 va0[4];  // V^T fragments of block e-1's first d tile, read early
@@ -517,6 +530,13 @@ void attn_fwd_kernel(AttnArgs a) {
           if (off >= vc[2 + (r >> 3)]) s1[r] = -INFINITY;
         }
       }
+    } else if (!DENSE && j < 0) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        s0[r] = -INFINITY;
+        s1[r] = -INFINITY;
+      }
+      if (threadIdx.x == 0) atomicOr(a.status, kStatusBadIndex);
     } else if (j == a.nB - 1) {
       const int nvalid = a.N - j * kBlock;
       if (nvalid < kBlock) {
@@ -575,7 +595,7 @@ void attn_fwd_kernel(AttnArgs a) {
     wait_lgkm0();
     exec_barrier();    // every wave is done with sV
     if constexpr (CHUNK) cp.v_chunks(Vth, col_idx + jprev);
-    else cp.v_tile(Vth, jprev);
+    else cp.v_tile(Vth, tile_of(jprev));
     wait_vmcnt<0>();
     exec_barrier();
     f16x8 va0[4];
@@ -674,10 +694,13 @@ void micro_attn_kernel(MicroAttnArgs a) {
     bf16x8 k[KS];
     u32x2 v[DT];
     int beta;
+    bool bad;  // the caller's tile index lay outside [0, nT): tile 0 read, masked out
   };
   const_i32* idx = (const_i32*)a.idx;
   auto load = [&](int e, Frags& f) {
-    f.beta = idx[e] >> 2;
+    const int raw = idx[e] >> 2;
+    f.bad = (unsigned)raw >= (unsigned)a.nT;
+    f.beta = f.bad ? 0 : raw;
     const int key = f.beta * kMicro + n16;
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
@@ -698,7 +721,8 @@ void micro_attn_kernel(MicroAttnArgs a) {
     // lane holds keys beta*16 + 4*g4 + rr of query q
 #pragma unroll
     for (int rr = 0; rr < 4; ++rr)
-      if (f.beta * kMicro + 4 * g4 + rr >= a.N) sacc[rr] = -INFINITY;
+      if (f.bad || f.beta * kMicro + 4 * g4 + rr >= a.N) sacc[rr] = -INFINITY;
+    if (f.bad && lane == 0) atomicOr(a.status, kStatusBadIndex);
     float mx = fmaxf(fmaxf(sacc[0], sacc[1]), fmaxf(sacc[2], sacc[3]));
     mx = fmaxf(mx, __shfl_xor(mx, 16));
     mx = fmaxf(mx, __shfl_xor(mx, 32));
@@ -766,7 +790,9 @@ __global__ __launch_bounds__(256) void micro_sig_kernel(MicroAttnArgs a) {
     if ((a.idx[mid] & 3) < sub) lo = mid + 1;
     else hi = mid;
   }
-  const int first = (lo < end && (a.idx[lo] & 3) == sub) ? (a.idx[lo] >> 2) : a.nT;
+  // (a tile index outside [0, nT) sorts with the empty sub-tiles)
+  int first = (lo < end && (a.idx[lo] & 3) == sub) ? (a.idx[lo] >> 2) : a.nT;
+  if ((unsigned)first > (unsigned)a.nT) first = a.nT;
   const int bin = z * (a.nT + 1) + first;
   a.sig[sid] = bin;
   atomicAdd(&a.hist[bin], 1);

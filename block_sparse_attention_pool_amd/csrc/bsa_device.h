@@ -63,9 +63,11 @@ __device__ __forceinline__ int vt_key_of_pos(int p) {
   return 8 * ((p & 7) >> 2) + 4 * (p >> 3) + (p & 3);
 }
 
-// Monotone map of a float to uint32: a < b  <=>  key(a) < key(b).
+// Monotone map of a float to uint32: a < b  <=>  key(a) < key(b), and
+// a == b  <=>  key(a) == key(b): adding +0 turns -0 into +0, so the two
+// zeros (equal values) get one key and tie like any other equal scores.
 __device__ __forceinline__ uint32_t float_order_key(float x) {
-  uint32_t u = __float_as_uint(x);
+  uint32_t u = __float_as_uint(x + 0.0f);
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 

@@ -86,7 +86,13 @@ struct AttnArgs {
   const int32_t* qsrc;
   int Nout;
   int64_t ksb, ksh, ksn;
+  // sparse kernel: bit kStatusBadIndex is OR-ed in when a column index lies
+  // outside [0, nB) (that entry is skipped); a word of the workspace
+  int32_t* status;
 };
+
+// Status bits of the attention workspace's status word.
+constexpr int32_t kStatusBadIndex = 1;
 
 // 16-key chunk codes of packed cluster-induced blocks: chunk index in the low
 // 24 bits, its valid keys (0..16) above.
@@ -113,7 +119,16 @@ struct MicroAttnArgs {
   int32_t* hist;     // [bins] counts, then (after the scan) cursors
   int32_t* offsets;  // [bins + 1] (workspace)
   int64_t* nnz;      // scan total (workspace)
+  int32_t* status;   // kStatusBadIndex when a tile index lies outside [0, nT)
   int slots, bins, nT, per_xcd;
+};
+
+struct CsrCheckArgs {
+  const int32_t* row_ptr;  // [rows + 1]
+  const int32_t* col_idx;  // [cap]
+  int64_t cap;
+  int rows, n_cols;
+  int32_t* counts;         // [3]: bad row pointers, entries out of range, entries not ascending
 };
 
 struct TransposeArgs {
@@ -243,14 +258,20 @@ struct RectifyArgs {
   const int32_t* col_idx;
   void* O;           // in: sparse result; out: rectified
   float* LSE;
+  const uint16_t* K;  // the keys (gain-aware gate: spread of each block)
+  float* spread;      // [BH, nBp] per-coordinate key variance of each block
   int64_t sb, sh, sn;
   int H, N, nB, nBp;
   float scale_log2;
+  int gate;           // 1: keep block j for query q only if |q|^2 spread_j < gate_thr
+  float gate_thr;     // 2 ln 2 / scale^2
 };
 
 hipError_t launch_pool(const PoolArgs& a, int B, hipStream_t s);
 hipError_t launch_score_gemm(const GemmArgs& a, int nbatch, hipStream_t s);
 hipError_t launch_fill_i32(int32_t* p, int64_t n, int32_t v, hipStream_t s);
+hipError_t launch_csr_check(const CsrCheckArgs& a, hipStream_t s);
+hipError_t launch_take_status(int32_t* status, int32_t* out, hipStream_t s);
 hipError_t launch_select(const SelectArgs& a, int rows, hipStream_t s);
 hipError_t launch_expand_bits(const uint32_t* bits_sel, int W_sel, int nB_sel,
                               uint32_t* bits64, int32_t* counts64, int W64, int nB64,

@@ -7,7 +7,18 @@
 // equal -- and that pooled attention is merged into the sparse (O, LSE)
 // by the exact LSE merge, in place.
 //
-// Three launches: the 64-token means of K and V (pool_kernel, float32,
+// Gain-Aware Pooling Rectification (the abstract asks that the recovered
+// gain exceed the pooling error it brings in), as read here: the estimate
+// of block j for query q recovers the mass n_j exp(scale q . Kbar_j); with
+// the block's keys spread normally and isotropically about their mean, the
+// true mass is that estimate times exp(sigma^2 / 2), sigma^2 =
+// scale^2 |q|^2 v_j (v_j the per-coordinate variance of the block's keys),
+// so the estimate's error stays below its gain while exp(sigma^2 / 2) < 2:
+// the gate keeps block j for query q when |q|^2 v_j < 2 ln 2 / scale^2.
+// v_j comes from rect_spread_kernel (one more pass over K); |q|^2 is summed
+// from the query fragments the kernel already holds.
+//
+// Three launches (four with the gate): the 64-token means of K and V (pool_kernel, float32,
 // into the workspace); their conversion to the matrix-core operands
 // (Kbar as bf16 high + low parts, so that q . Kbar carries about 16
 // mantissa bits; Vbar as fp16 in 16-key chunks [d][16]); and the rectify
@@ -60,6 +71,56 @@ __global__ __launch_bounds__(256) void rect_convert_kernel(RectifyArgs a, int64_
   a.Klo[(bh * a.nBp + j) * D + d] = lo;
   a.Vt[((bh * (a.nBp / 16) + j / 16) * D + d) * 16 + (j % 16)] =
       __builtin_bit_cast(uint16_t, (_Float16)v);
+}
+
+// One workgroup per (head, padded block j): v_j = sum over the block's valid
+// keys of |k - Kbar_j|^2 / (n_j D), summed in a fixed order (each thread
+// its 16-byte chunks, then the block sum), 0 for padding blocks.
+template <int D>
+__global__ __launch_bounds__(256) void rect_spread_kernel(RectifyArgs a) {
+  constexpr int C = D / 8;             // 16-byte chunks per key row
+  constexpr int PER = 64 * C / 256;    // chunks per thread
+  __shared__ float red[4];
+  const int j = blockIdx.x;
+  const int64_t bh = blockIdx.y;
+  const int tid = threadIdx.x;
+  const int b = (int)(bh / a.H), h = (int)(bh % a.H);
+  float acc = 0.f;
+  const int n = j < a.nB ? min(kBlock, a.N - j * kBlock) : 0;
+  if (n > 0) {
+    const int c = tid % C;  // the same coordinates for every chunk of this thread
+    const float* mean = a.Kf + (bh * a.nB + j) * D + 8 * c;
+    float mu[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) mu[e] = mean[e];
+    const uint16_t* Kh = a.K + (int64_t)b * a.sb + (int64_t)h * a.sh;
+    u32x4 v[PER];
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      const int t = (tid + 256 * u) / C;  // token of the block
+      v[u] = *(const u32x4*)(Kh + (int64_t)(j * kBlock + min(t, n - 1)) * a.sn + 8 * c);
+    }
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      const int t = (tid + 256 * u) / C;
+      if (t < n) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float x0 = bf16_bits_to_f32(v[u][e] & 0xFFFFu) - mu[2 * e];
+          const float x1 = bf16_bits_to_f32(v[u][e] >> 16) - mu[2 * e + 1];
+          acc = __builtin_fmaf(x0, x0, acc);
+          acc = __builtin_fmaf(x1, x1, acc);
+        }
+      }
+    }
+  }
+  acc = wave_sum(acc);
+  if ((tid & 63) == 0) red[tid >> 6] = acc;
+  __syncthreads();
+  if (tid == 0) {
+    const float tot = (red[0] + red[1]) + (red[2] + red[3]);
+    a.spread[bh * a.nBp + j] = n > 0 ? tot / (float)(n * D) : 0.f;
+  }
 }
 
 template <bool BF16>
@@ -138,11 +199,22 @@ void rectify_kernel(RectifyArgs a) {
 #pragma unroll
   for (int s = 0; s < KS; ++s) qv[s] = *(const u32x4*)(qrow + 32 * s);
   bf16x8 qf[KS];
+  float qn2 = 0.f;  // |q|^2 of this lane's query (gate), from the fragments of all 4 lane groups
 #pragma unroll
   for (int s = 0; s < KS; ++s) {
     if (q >= a.N) qv[s] = u32x4{0u, 0u, 0u, 0u};
     qf[s] = __builtin_bit_cast(bf16x8, qv[s]);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float x0 = bf16_bits_to_f32(qv[s][e] & 0xFFFFu), x1 = bf16_bits_to_f32(qv[s][e] >> 16);
+      qn2 = __builtin_fmaf(x0, x0, qn2);
+      qn2 = __builtin_fmaf(x1, x1, qn2);
+    }
   }
+  qn2 += __shfl_xor(qn2, 16);
+  qn2 += __shfl_xor(qn2, 32);
+  const bool gated = a.gate != 0;
+  const float* spread = a.spread + bh * a.nBp;
   f32x4 o[DT];
 #pragma unroll
   for (int t = 0; t < DT; ++t) o[t] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -183,16 +255,26 @@ void rectify_kernel(RectifyArgs a) {
     }
   };
 
+  // the spread of the lane's four pooled keys of a step (gate only)
+  auto sload = [&](int j0) {
+    return gated ? *(const f32x4*)(spread + j0 + 4 * g4) : f32x4{0.f, 0.f, 0.f, 0.f};
+  };
   int j = next_active(0);
   int cur = 0;
+  f32x4 sp = {0.f, 0.f, 0.f, 0.f};
   if (j < a.nB) {
     gload(j);
+    sp = sload(j);
     lstore(tiles[0]);
   }
   __syncthreads();
   while (j < a.nB) {
     const int jn = next_active(j + 16);
-    if (jn < a.nB) gload(jn);
+    f32x4 sp_next = sp;
+    if (jn < a.nB) {
+      gload(jn);
+      sp_next = sload(jn);
+    }
     if (live) {
       const uint16_t* tk = tiles[cur];
       const uint32_t omitted = omitted_of(j);
@@ -210,7 +292,8 @@ void rectify_kernel(RectifyArgs a) {
       for (int rr = 0; rr < 4; ++rr) {
         const int jj = 4 * g4 + rr;
         const float lg = j + jj == a.nB - 1 ? lg_tail : 6.0f;  // log2 of the block size
-        x[rr] = (omitted >> jj) & 1u ? __builtin_fmaf(sacc[rr], c, lg) : -INFINITY;
+        const bool keep = ((omitted >> jj) & 1u) && (!gated || qn2 * sp[rr] < a.gate_thr);
+        x[rr] = keep ? __builtin_fmaf(sacc[rr], c, lg) : -INFINITY;
       }
       float mx = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
       mx = fmaxf(mx, __shfl_xor(mx, 16));
@@ -241,6 +324,7 @@ void rectify_kernel(RectifyArgs a) {
     __syncthreads();
     cur ^= 1;
     j = jn;
+    sp = sp_next;
   }
   if (!live) return;
 
@@ -286,6 +370,11 @@ hipError_t launch_rectify(const RectifyArgs& a, int BH, int D, bool out_bf16, hi
   else
     hipLaunchKernelGGL(rect_convert_kernel<64>, cgrid, dim3(256), 0, s, a, total);
   const dim3 grid(a.nB, BH);
+  if (a.gate) {
+    const dim3 sgrid(a.nBp, BH);
+    if (D == 128) hipLaunchKernelGGL(rect_spread_kernel<128>, sgrid, dim3(256), 0, s, a);
+    else hipLaunchKernelGGL(rect_spread_kernel<64>, sgrid, dim3(256), 0, s, a);
+  }
   if (D == 128) {
     if (out_bf16) hipLaunchKernelGGL((rectify_kernel<128, true>), grid, dim3(256), 0, s, a);
     else hipLaunchKernelGGL((rectify_kernel<128, false>), grid, dim3(256), 0, s, a);

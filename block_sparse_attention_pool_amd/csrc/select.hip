@@ -384,6 +384,42 @@ __global__ __launch_bounds__(256) void emit_bits_kernel(const uint32_t* bits, in
   }
 }
 
+// One wave per row of a caller's CSR: counts rows whose pointers are out of
+// order or out of [0, cap] (row 0 must start at 0), entries outside
+// [0, n_cols), and entries not above their predecessor.  Entries are read
+// only inside [row_ptr[r], row_ptr[r+1]) of rows whose pointers pass.
+__global__ __launch_bounds__(256) void csr_check_kernel(CsrCheckArgs a) {
+  const int r = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (r >= a.rows) return;
+  const int lane = threadIdx.x & 63;
+  const int64_t b = a.row_ptr[r], e = a.row_ptr[r + 1];
+  const bool bad_ptr = b < 0 || b > e || e > a.cap || (r == 0 && b != 0);
+  if (bad_ptr) {
+    if (lane == 0) atomicAdd(&a.counts[0], 1);
+    return;
+  }
+  int out = 0, order = 0;
+  for (int64_t k = b + lane; k < e; k += 64) {
+    const int v = a.col_idx[k];
+    out += (unsigned)v >= (unsigned)a.n_cols;
+    order += k > b && v <= a.col_idx[k - 1];
+  }
+  out = wave_sum(out);
+  order = wave_sum(order);
+  if (lane == 0) {
+    if (out) atomicAdd(&a.counts[1], out);
+    if (order) atomicAdd(&a.counts[2], order);
+  }
+}
+
+// Copies a status word out and clears it (one thread).
+__global__ void take_status_kernel(int32_t* status, int32_t* out) {
+  if (threadIdx.x == 0) {
+    out[0] = status[0];
+    status[0] = 0;
+  }
+}
+
 __global__ void fill_i32_kernel(int32_t* p, int64_t n, int32_t v) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (i < n) p[i] = v;
@@ -592,6 +628,18 @@ __global__ __launch_bounds__(256) void emit_slots_kernel(const int32_t* slots, i
 hipError_t launch_fill_i32(int32_t* p, int64_t n, int32_t v, hipStream_t s) {
   if (n <= 0) return hipSuccess;
   hipLaunchKernelGGL(fill_i32_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, p, n, v);
+  return hipGetLastError();
+}
+
+hipError_t launch_csr_check(const CsrCheckArgs& a, hipStream_t s) {
+  hipError_t e = launch_fill_i32(a.counts, 3, 0, s);
+  if (e != hipSuccess || a.rows <= 0) return e;
+  hipLaunchKernelGGL(csr_check_kernel, dim3((a.rows + 3) / 4), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_take_status(int32_t* status, int32_t* out, hipStream_t s) {
+  hipLaunchKernelGGL(take_status_kernel, dim3(1), dim3(64), 0, s, status, out);
   return hipGetLastError();
 }
 

@@ -224,7 +224,11 @@ bsa_status bsa_select_blocks(const float* scores, const bsa_shape* shape,
                              void* stream);
 
 /* Bytes of device workspace the attention entry points need (the key-major
- * copy of V the PV products read).  Returns -1 on invalid arguments. */
+ * copy of V the PV products read, the micro residual's sub-tile order, and
+ * a status word in the last 256 bytes).  Returns -1 on invalid arguments.
+ * The status word (int32 at byte bsa_attn_workspace_bytes(shape) - 256)
+ * must be zero when the workspace is first used: zero those bytes once
+ * after allocating it, or call bsa_attn_take_status once. */
 int64_t bsa_attn_workspace_bytes(const bsa_shape* shape);
 
 /* ------------------------------------------------------------------------
@@ -239,7 +243,12 @@ int64_t bsa_attn_workspace_bytes(const bsa_shape* shape);
  * an empty list get O = 0 and LSE = -inf.
  *
  * row_ptr / col_idx: a CSR from bsa_select_blocks (or the caller); column
- *   indices must lie in [0, nB).  Order within a row does not matter.
+ *   indices must lie in [0, nB).  Order within a row does not matter.  A
+ *   column index outside [0, nB) adds nothing to its row (the kernel reads
+ *   an in-bounds tile instead and masks it out) and sets bit 1 of the
+ *   workspace's status word (see bsa_attn_take_status).  row_ptr itself is
+ *   trusted: rows must be in order and lie within col_idx (checked by
+ *   bsa_check_csr / bsa_validate_csr_host, not by this call).
  * O: [B, H, N, d] with the strides of `shape`, element type o_dtype
  *   (BSA_F32 or BSA_BF16, round-to-nearest-even).
  * LSE: float32 [B, H, N].
@@ -266,6 +275,41 @@ bsa_status bsa_dense_attn_fwd(const uint16_t* Q, const uint16_t* K,
                               float scale, void* O, int32_t o_dtype,
                               float* LSE, void* workspace,
                               int64_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * bsa_attn_take_status -- copies the attention workspace's status word to
+ * status_out (device int32) and clears it, in stream order.  Bit 1: some
+ * call since the last clear met a column index (bsa_sparse_attn_fwd) or a
+ * micro tile index (bsa_micro_residual_fwd) outside its range and skipped
+ * it.  The word is sticky: every call ORs into it; nothing else clears it.
+ * ---------------------------------------------------------------------- */
+bsa_status bsa_attn_take_status(void* workspace, int64_t workspace_bytes,
+                                const bsa_shape* shape, int32_t* status_out,
+                                void* stream);
+
+/* ------------------------------------------------------------------------
+ * bsa_check_csr -- validates a device CSR of `rows` rows before attention:
+ * counts[0] = rows whose pointers are out of order, negative or past
+ * col_cap (row_ptr[0] must be 0), counts[1] = entries outside [0, n_cols),
+ * counts[2] = entries not strictly above their predecessor in the row.
+ * counts: device int32 [3], overwritten (zeroed by the call itself); read
+ * it after a stream synchronisation.  Reads row_ptr [rows + 1] and, for
+ * rows whose pointers pass, only col_idx[row_ptr[r] .. row_ptr[r+1]) within
+ * [0, col_cap).  All zero means the CSR is safe for the attention calls
+ * (n_cols = nB64 for macro lists, ceil(N / 16) * 4 codes for micro lists,
+ * whose order rule is (a, beta) -- use counts[1] only there).
+ * ---------------------------------------------------------------------- */
+bsa_status bsa_check_csr(const int32_t* row_ptr, int64_t rows,
+                         const int32_t* col_idx, int64_t col_cap,
+                         int32_t n_cols, int32_t* counts, void* stream);
+
+/* bsa_validate_csr_host -- the same rules on a HOST CSR, synchronously:
+ * BSA_OK, or BSA_ERR_INVALID_ARG with the first failing row in *bad_row
+ * (may be NULL; -1 when the arrays themselves are invalid) and the reason
+ * in bsa_last_error().  Needs no GPU. */
+bsa_status bsa_validate_csr_host(const int32_t* row_ptr, int64_t rows,
+                                 const int32_t* col_idx, int64_t col_cap,
+                                 int32_t n_cols, int64_t* bad_row);
 
 /* ------------------------------------------------------------------------
  * bsa_attn_stage_v -- the fp16 V^T staging that bsa_sparse_attn_fwd,
@@ -325,8 +369,19 @@ bsa_status bsa_lse_merge(const void* O1, const float* L1, const void* O2,
  *   O_p[t]   = sum_j n_j exp(scale q_t . Kbar_j - LSE_p[t]) Vbar_j
  * (exact when block j's keys are all equal), and the call replaces the
  * sparse result (O, LSE) by its exact LSE merge with (O_p, LSE_p), as
- * bsa_lse_merge would.  A row that keeps every block is left as it is.  The
- * page's gain-aware gate has no stated rule and is not applied.
+ * bsa_lse_merge would.  A row that keeps every block is left as it is.
+ *
+ * gain_gate (0 or 1): the page's Gain-Aware Pooling Rectification (the
+ *   recovered gain must exceed the pooling error it brings in), read as: the
+ *   estimate of block j for query t recovers n_j exp(scale q_t . Kbar_j);
+ *   if the block's keys scatter normally and isotropically about Kbar_j
+ *   with per-coordinate variance v_j = sum |k - Kbar_j|^2 / (n_j d), the
+ *   block's true mass is that estimate times exp(sigma^2 / 2), sigma^2 =
+ *   scale^2 |q_t|^2 v_j, so the error stays below the gain while
+ *   sigma^2 < 2 ln 2.  With gain_gate = 1 block j enters LSE_p[t] and
+ *   O_p[t] only where |q_t|^2 v_j < 2 ln 2 / scale^2 (float32, |q_t|^2
+ *   from the bf16 query, v_j from one more pass over K); a query with no
+ *   block left keeps its sparse result.  scale must be > 0 with the gate.
  *
  * O, LSE: on entry the bsa_sparse_attn_fwd result for the same Q, K, V and
  *   CSR (o_dtype BSA_F32 or BSA_BF16); on return the rectified result.
@@ -342,7 +397,7 @@ int64_t bsa_pooled_rectify_workspace_bytes(const bsa_shape* shape);
 
 bsa_status bsa_pooled_rectify(const uint16_t* Q, const uint16_t* K,
                               const uint16_t* V, const bsa_shape* shape,
-                              int32_t block, float scale,
+                              int32_t block, float scale, int32_t gain_gate,
                               const int32_t* row_ptr, const int32_t* col_idx,
                               void* O, int32_t o_dtype, float* LSE,
                               void* workspace, int64_t workspace_bytes,
@@ -583,6 +638,16 @@ bsa_status bsa_omission_risk(const float* lse_sparse, const float* lse_full,
                              const float* lse_repaired, const bsa_shape* shape,
                              double* risk, void* workspace,
                              int64_t workspace_bytes, void* stream);
+
+/* bsa_heads_at_risk -- the offline calibration step that follows
+ * bsa_omission_risk: head_mask[h] = 1 for the n heads of largest mean
+ * omitted share (equal shares to the lower head index), 0 for the others;
+ * the mask bsa_select_blocks (MICRO) and bsa_micro_residual_fwd take.
+ * mean_omitted: host float64 [H] (risk[b, h, 0] of one batch, copied to
+ * the host); head_mask: host uint8 [H].  n is clamped to [0, H].  NaN
+ * shares are rejected (BSA_ERR_INVALID_ARG).  Needs no GPU. */
+bsa_status bsa_heads_at_risk(const double* mean_omitted, int32_t H, int32_t n,
+                             uint8_t* head_mask);
 
 #ifdef __cplusplus
 }

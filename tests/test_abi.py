@@ -69,7 +69,8 @@ def test_workspace_sizes():
     # (2 heads x 64 bins, + 1), a total
     a256 = lambda x: -(-x // 256) * 256
     vt = 2 * 128 * npad * 2
-    order = 2 * a256(128 * 4) + a256(128 * 4) + a256(129 * 4) + 256
+    # ... and the status word in the last 256 bytes
+    order = 2 * a256(128 * 4) + a256(128 * 4) + a256(129 * 4) + 256 + 256
     assert bsa._lib.bsa_attn_workspace_bytes(ctypes.byref(s)) == vt + order
     sp, _ = bsa.make_select_params("topk", k=4, nB=16)
     rows, W = 2 * 16, 1
@@ -236,18 +237,25 @@ def test_pooled_rectify_validation_and_workspace():
     need = bsa._lib.bsa_pooled_rectify_workspace_bytes(ctypes.byref(s))
     f32 = -(-(2 * 16 * 128 * 4) // 256) * 256
     h16 = -(-(2 * 16 * 128 * 2) // 256) * 256
-    assert need == 2 * f32 + 3 * h16
+    spread = -(-(2 * 16 * 4) // 256) * 256  # key spread per block (gain-aware gate)
+    assert need == 2 * f32 + 3 * h16 + spread
     p = ctypes.c_void_p(4096)
-    st = bsa._lib.bsa_pooled_rectify(p, p, p, ctypes.byref(s), 64, 0.1, p, p, p, 0, p, p,
+    st = bsa._lib.bsa_pooled_rectify(p, p, p, ctypes.byref(s), 64, 0.1, 0, p, p, p, 0, p, p,
                                      need - 1, None)
     assert st == 3 and "workspace" in bsa.bsa_last_error()
-    st = bsa._lib.bsa_pooled_rectify(p, p, None, ctypes.byref(s), 64, 0.1, p, p, p, 0, p, p,
+    st = bsa._lib.bsa_pooled_rectify(p, p, p, ctypes.byref(s), 64, 0.1, 2, p, p, p, 0, p, p,
+                                     need, None)
+    assert st == 1 and "gain_gate" in bsa.bsa_last_error()
+    st = bsa._lib.bsa_pooled_rectify(p, p, p, ctypes.byref(s), 64, 0.0, 1, p, p, p, 0, p, p,
+                                     need, None)
+    assert st == 1 and "scale" in bsa.bsa_last_error()
+    st = bsa._lib.bsa_pooled_rectify(p, p, None, ctypes.byref(s), 64, 0.1, 0, p, p, p, 0, p, p,
                                      need, None)
     assert st == 1 and "V is NULL" in bsa.bsa_last_error()
-    st = bsa._lib.bsa_pooled_rectify(p, p, p, ctypes.byref(s), 128, 0.1, p, p, p, 0, p, p,
+    st = bsa._lib.bsa_pooled_rectify(p, p, p, ctypes.byref(s), 128, 0.1, 0, p, p, p, 0, p, p,
                                      need, None)
     assert st == 2 and "block" in bsa.bsa_last_error()
-    st = bsa._lib.bsa_pooled_rectify(p, p, p, ctypes.byref(s), 64, 0.1, p, p, p, 5, p, p,
+    st = bsa._lib.bsa_pooled_rectify(p, p, p, ctypes.byref(s), 64, 0.1, 0, p, p, p, 5, p, p,
                                      need, None)
     assert st == 1 and "o_dtype" in bsa.bsa_last_error()
     big = _shape(N=4097 * 64)
@@ -356,3 +364,93 @@ def test_stage_v_validation():
     assert L.bsa_attn_stage_v(ctypes.c_void_p(4098), ctypes.byref(s), p, need, None) == 1
     bad = _shape(B=1, H=2, N=1000, d=96)
     assert L.bsa_attn_stage_v(p, ctypes.byref(bad), p, need, None) == 2
+
+
+# ------------------------------------------------------------ CSR validation
+
+def _csr(rows):
+    import numpy as np
+    rp = np.zeros(len(rows) + 1, np.int32)
+    rp[1:] = np.cumsum([len(r) for r in rows])
+    ci = np.array([j for r in rows for j in r] or [0], np.int32)
+    return rp, ci
+
+
+def test_validate_csr_host_accepts_valid_lists():
+    import numpy as np
+    rp, ci = _csr([[0, 3, 5], [], [1], [0, 1, 2, 3, 4, 5, 6, 7]])
+    assert bsa.bsa_validate_csr_host(rp, ci, 8) == -1
+    # an empty CSR (no rows) and rows with no entries at all
+    assert bsa.bsa_validate_csr_host(np.zeros(1, np.int32), np.zeros(1, np.int32), 8) == -1
+    assert bsa.bsa_validate_csr_host(np.zeros(4, np.int32), np.zeros(1, np.int32), 8) == -1
+
+
+@pytest.mark.parametrize("case,row,msg", [
+    ("col_high", 1, "outside"), ("col_negative", 0, "outside"), ("unsorted", 2, "ascending"),
+    ("duplicate", 2, "ascending"), ("ptr_back", 1, "out of order"), ("ptr_past_cap", 2, "col_cap"),
+    ("ptr0", 0, "row_ptr[0]"),
+])
+def test_validate_csr_host_names_the_first_bad_row(case, row, msg):
+    import numpy as np
+    rows = [[0, 3], [1, 2], [4, 6], [7]]
+    if case == "col_high":
+        rows[1] = [1, 8]
+    elif case == "col_negative":
+        rows[0] = [-1, 3]
+    elif case == "unsorted":
+        rows[2] = [6, 4]
+    elif case == "duplicate":
+        rows[2] = [4, 4]
+    rp, ci = _csr(rows)
+    if case == "ptr_back":
+        rp[2] = 1                # row 1 ends before it starts
+    elif case == "ptr_past_cap":
+        ci = ci[:5]              # row 2 ends at 6, past the 5 entries there are
+    elif case == "ptr0":
+        rp = rp + 1
+        ci = np.concatenate([[0], ci]).astype(np.int32)
+    with pytest.raises(bsa.BsaError) as e:
+        bsa.bsa_validate_csr_host(rp, ci, 8)
+    assert f"row {row}:" in str(e.value) and msg in str(e.value)
+
+
+def test_validate_csr_host_matches_a_plain_rule_on_random_lists():
+    import numpy as np
+    rng = np.random.default_rng(11)
+    for trial in range(200):
+        n_rows, n_cols = int(rng.integers(1, 9)), int(rng.integers(1, 12))
+        rows = [sorted(rng.choice(n_cols, size=int(rng.integers(0, n_cols + 1)), replace=False).tolist())
+                for _ in range(n_rows)]
+        if trial % 3 == 1 and any(rows):
+            r = next(i for i, x in enumerate(rows) if x)
+            rows[r][-1] = n_cols + int(rng.integers(0, 3))       # out of range
+        elif trial % 3 == 2 and any(len(x) > 1 for x in rows):
+            r = next(i for i, x in enumerate(rows) if len(x) > 1)
+            rows[r][0], rows[r][1] = rows[r][1], rows[r][0]      # unsorted
+        ok = all(all(0 <= j < n_cols for j in x) and all(a < b for a, b in zip(x, x[1:]))
+                 for x in rows)
+        rp, ci = _csr(rows)
+        if ok:
+            assert bsa.bsa_validate_csr_host(rp, ci, n_cols) == -1
+        else:
+            with pytest.raises(bsa.BsaError):
+                bsa.bsa_validate_csr_host(rp, ci, n_cols)
+
+
+def test_check_csr_and_take_status_validate_before_any_launch():
+    s = _shape(B=1, H=2, N=1000)
+    p = ctypes.c_void_p(4096)
+    assert bsa._lib.bsa_check_csr(p, -1, p, 10, 16, p, None) == 1
+    assert bsa._lib.bsa_check_csr(p, 4, p, -1, 16, p, None) == 1
+    assert bsa._lib.bsa_check_csr(None, 4, p, 10, 16, p, None) == 1
+    need = bsa._lib.bsa_attn_workspace_bytes(ctypes.byref(s))
+    assert bsa._lib.bsa_attn_take_status(p, need - 1, ctypes.byref(s), p, None) == 3
+    assert bsa._lib.bsa_attn_take_status(p, need, ctypes.byref(s), None, None) == 1
+
+
+def test_heads_at_risk_rejects_nan_and_bad_sizes():
+    import numpy as np
+    with pytest.raises(bsa.BsaError):
+        bsa.heads_at_risk(np.array([0.1, float("nan")]), 1)
+    assert bsa._lib.bsa_heads_at_risk(None, 3, 1, None) == 1
+
