@@ -76,6 +76,12 @@ def parse():
     ap.add_argument("--rectify", action="store_true",
                     help="add the pooled rectification of omitted blocks to the step and "
                          "report its cost and its effect on the error against dense attention")
+    ap.add_argument("--gain-gate", action="store_true",
+                    help="with --rectify: the step's rectification applies the gain-aware gate "
+                         "(both variants are reported either way)")
+    ap.add_argument("--no-per-workload", action="store_true",
+                    help="skip the summary lines of the other four workloads (run by default "
+                         "with the default workload)")
     ap.add_argument("--cluster", action="store_true",
                     help="also time the 3D local-window clustering of Q and K (all heads) with "
                          "the page's grids and (3, 8, 8) windows, 3 iterations")
@@ -168,33 +174,22 @@ def traffic_entry(kernel_src):
     return rec.get("hbm_bytes_per_launch")
 
 
-def main():
-    args = parse()
-    if args.gpus != 1:
-        print(json.dumps({"error": "this benchmark measures one GPU only; the path shards "
-                                   "by (batch, head) with no exchange between GPUs, and no "
-                                   "multi-GPU run is implemented"}))
-        sys.exit(2)
-
-    import torch
-    import block_sparse_attention_pool_amd as bsa
-    from synth import (CONFIGS, config_spec, gen_qkv, merge_sides, micro_heads, mod_pattern_mask,
+def build_workload(cfg, args, torch, bsa, keep_host=False):
+    """Inputs of workload ``cfg`` resident on the GPU, its selection and the
+    step (eager, or replayed as a HIP graph on small layers after a bit-for-
+    bit check against the eager step).  Returns a namespace."""
+    from types import SimpleNamespace
+    from synth import (CONFIGS, config_spec, gen_qkv, micro_heads, mod_pattern_mask,
                        rotation_offset)
 
-    if args.calibration_copy:
-        src = torch.ones(64 << 20, dtype=torch.float32, device="cuda:0")
-        dst = torch.empty_like(src)
-        for _ in range(3):
-            torch.mul(src, 1.0, out=dst)
-        torch.cuda.synchronize()
-        del src, dst
-
-    cfg = args.config
     c = CONFIGS[cfg]
     spec = config_spec(cfg)
     Qc, Kc, Vc = gen_qkv(spec)
     dev = torch.device("cuda:0")
     Q, K, V = (x.to(dev) for x in (Qc, Kc, Vc))
+    if not keep_host:
+        del Qc, Kc, Vc
+        Qc = Kc = Vc = None
     B, H, N, d = Q.shape
     blk = args.block
     nB = bsa.n_blocks(N, blk)      # selection blocks
@@ -235,6 +230,7 @@ def main():
     ws_rect = bsa.rectify_workspace(Q) if args.rectify else None
     O_buf = torch.empty(Q.shape, dtype=torch.float32, device=dev)
     L_buf = torch.empty(Q.shape[:3], dtype=torch.float32, device=dev)
+    Om_buf = Lm_buf = None
     if micro is not None:
         Om_buf = torch.empty_like(O_buf)
         Lm_buf = torch.empty_like(L_buf)
@@ -284,7 +280,8 @@ def main():
         bsa.bsa_sparse_attn_fwd(Q, K, None if overlap else V, rp, ci, out=O_buf, lse=L_buf,
                                 workspace=ws)
         if args.rectify:
-            bsa.bsa_pooled_rectify(Q, K, V, rp, ci, O_buf, L_buf, workspace=ws_rect)
+            bsa.bsa_pooled_rectify(Q, K, V, rp, ci, O_buf, L_buf, gain_gate=args.gain_gate,
+                                   workspace=ws_rect)
         mnnz = None
         if micro is not None:
             mrp, mci, mnnz = micro_select(sc, rp, ci)
@@ -347,18 +344,121 @@ def main():
             run(w)
         torch.cuda.synchronize()
 
+    return SimpleNamespace(**{k: v for k, v in locals().items() if k not in ("torch", "bsa")})
+
+
+def time_steps(W, steps, torch):
+    """Times `steps` steps of a built workload (synchronised on both sides);
+    returns (seconds per step, mean macro entries, mean micro entries, the
+    last step's outputs)."""
     nnz_all, mnnz_all = [], []
-    t0 = time.perf_counter()
-    for s_i in range(args.steps):
-        sc, rp, ci, nnz, mnnz = run(s_i)
-        nnz_all.append(nnz)
-        if mnnz is not None:
-            mnnz_all.append(mnnz)
     torch.cuda.synchronize()
-    step_s = (time.perf_counter() - t0) / args.steps
-    # executed work of the timed steps (rows differ per call when the anchors rotate)
+    t0 = time.perf_counter()
+    for s_i in range(steps):
+        last = W.run(s_i)
+        nnz_all.append(last[3])
+        if last[4] is not None:
+            mnnz_all.append(last[4])
+    torch.cuda.synchronize()
+    step_s = (time.perf_counter() - t0) / steps
     nnz_mean = sum(int(x.item()) for x in nnz_all) / len(nnz_all)
     mnnz_mean = sum(int(x.item()) for x in mnnz_all) / len(mnnz_all) if mnnz_all else 0.0
+    return step_s, nnz_mean, mnnz_mean, last
+
+
+def workload_summary(cfg, args, torch, bsa):
+    """One line of figures for a workload other than the headline one: step
+    time over a few steps, the attention kernel alone (HIP events on its
+    stream), the dense kernel of the same library, and the micro stages where
+    the workload has them."""
+    W = build_workload(cfg, args, torch, bsa)
+    steps = 20 if cfg == 0 else 5
+    step_s, nnz_mean, mnnz_mean, (sc, rp, ci, nnz, mnnz) = time_steps(W, steps, torch)
+    B, H, N, d = W.B, W.H, W.N, W.d
+    nnz_v = int(nnz.item())
+    macro_flops = 4 * d * 64 * 64 * nnz_v
+    dense_flops = 4 * B * H * N * N * d
+    exec_flops = 4 * d * (64 * 64 * nnz_mean + 16 * 16 * mnnz_mean)
+    reps = 3 if cfg != 0 else 10
+    attn_ms, _ = events_ms(
+        lambda: bsa.bsa_sparse_attn_fwd(W.Q, W.K, None, rp, ci, out=W.O_buf, lse=W.L_buf,
+                                        workspace=W.ws), reps, W.stream)
+    dense_ms, _ = events_ms(
+        lambda: bsa.bsa_dense_attn_fwd(W.Q, W.K, None, out=W.O_buf, lse=W.L_buf,
+                                       workspace=W.ws), 2 if cfg != 0 else 10, W.stream)
+    attn_tflops = macro_flops / (attn_ms * 1e-3) / 1e12
+    res = {"workload": W.c["name"], "B": B, "H": H, "N": N, "d": d, "selection": W.sel_desc,
+           "density": round(nnz_mean / (B * H * bsa.n_blocks(N) ** 2), 4),
+           "steps": steps, "step_graph": bool(W.graphs),
+           "ms_per_step": round(step_s * 1e3, 4),
+           "value_tflops": round(exec_flops / step_s / 1e12, 2),
+           "attn_kernel_ms": round(attn_ms, 4),
+           "attn_kernel_tflops": round(attn_tflops, 2),
+           "pct_mfma_peak": round(100 * attn_tflops / PEAK_TFLOPS, 2),
+           "dense_kernel_ms": round(dense_ms, 4),
+           "dense_kernel_tflops": round(dense_flops / (dense_ms * 1e-3) / 1e12, 2),
+           "speedup_vs_dense": round(dense_ms / attn_ms, 3),
+           "pipeline_speedup_vs_dense": round(dense_ms / (step_s * 1e3), 3)}
+    if W.micro is not None:
+        mrp, mci, mn = W.micro_select(sc, rp, ci)
+        msel_ms, _ = events_ms(lambda: W.micro_select(sc, rp, ci), reps, W.stream)
+        mattn_ms, _ = events_ms(
+            lambda: bsa.bsa_micro_residual_fwd(W.Q, W.K, None, mrp, mci,
+                                               head_mask=W.micro["mask"], out=W.Om_buf,
+                                               lse=W.Lm_buf, workspace=W.ws), reps, W.stream)
+        merge_ms, _ = events_ms(
+            lambda: bsa.bsa_lse_merge(W.O_buf, W.L_buf, W.Om_buf, W.Lm_buf,
+                                      head_mask=W.micro["mask"], out=W.O_buf, lse_out=W.L_buf),
+            reps, W.stream)
+        mnv = int(mn.item())
+        res["micro"] = {"m": W.micro["m"], "heads": list(W.micro["heads"]),
+                        "tiles": mnv, "micro_select_ms": round(msel_ms, 4),
+                        "micro_residual_ms": round(mattn_ms, 4),
+                        "micro_residual_tflops": round(4 * d * 256 * mnv / (mattn_ms * 1e-3)
+                                                       / 1e12, 2),
+                        "lse_merge_ms": round(merge_ms, 4)}
+    del W
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return res
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this benchmark measures one GPU only; the path shards "
+                                   "by (batch, head) with no exchange between GPUs, and no "
+                                   "multi-GPU run is implemented"}))
+        sys.exit(2)
+
+    import torch
+    import block_sparse_attention_pool_amd as bsa
+    from synth import merge_sides
+
+    if args.calibration_copy:
+        src = torch.ones(64 << 20, dtype=torch.float32, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            torch.mul(src, 1.0, out=dst)
+        torch.cuda.synchronize()
+        del src, dst
+
+    cfg = args.config
+    W = build_workload(cfg, args, torch, bsa, keep_host=True)
+    c, spec = W.c, W.spec
+    Qc, Kc, Vc = W.Qc, W.Kc, W.Vc
+    Q, K, V = W.Q, W.K, W.V
+    B, H, N, d = W.B, W.H, W.N, W.d
+    blk, nB, scale, stream, mode = W.blk, W.nB, W.scale, W.stream, W.mode
+    sel, sel_desc, micro = W.sel, W.sel_desc, W.micro
+    ws, ws_rect = W.ws, W.ws_rect
+    O_buf, L_buf, Om_buf, Lm_buf = W.O_buf, W.L_buf, W.Om_buf, W.Lm_buf
+    score, select, micro_select = W.score, W.select, W.micro_select
+    graphs, two_streams = W.graphs, W.two_streams
+    dev = torch.device("cuda:0")
+
+    # executed work of the timed steps (rows differ per call when the anchors rotate)
+    step_s, nnz_mean, mnnz_mean, (sc, rp, ci, nnz, mnnz) = time_steps(W, args.steps, torch)
     exec_flops = 4 * d * (64 * 64 * nnz_mean + 16 * 16 * mnnz_mean)
     # kernel-level figures below use the lists of the last step
     nnz_v = int(nnz.item())
@@ -470,21 +570,50 @@ def main():
         Ld = torch.empty_like(L_buf)
         bsa.bsa_dense_attn_fwd(Q, K, None, out=Od, lse=Ld, workspace=ws)
 
-        def rect_once():
+        def rect_once(gate):
             Or.copy_(Os)
             Lr.copy_(Ls)
-            bsa.bsa_pooled_rectify(Q, K, V, rp, ci, Or, Lr, workspace=ws_rect)
+            bsa.bsa_pooled_rectify(Q, K, V, rp, ci, Or, Lr, gain_gate=gate, workspace=ws_rect)
 
         copy_ms, _ = events_ms(lambda: (Or.copy_(Os), Lr.copy_(Ls)), reps, stream)
-        rect_ms, _ = events_ms(rect_once, reps, stream)
-        rect_ms = max(rect_ms - copy_ms, 1e-6)
         omitted_pairs = B * H * bsa.n_blocks(N) ** 2 - nnz_v
-        rect_out = {"kernel_ms": round(rect_ms, 4),
-                    "tflops": round(4 * d * 64 * omitted_pairs / (rect_ms * 1e-3) / 1e12, 2),
+        rect_out = {"gain_gate_in_step": bool(args.gain_gate),
                     "mean_abs_err_vs_dense_sparse": float((Os - Od).abs().mean()),
-                    "mean_abs_err_vs_dense_rectified": float((Or - Od).abs().mean()),
-                    "mean_abs_lse_err_vs_dense_sparse": float((Ls - Ld).abs().mean()),
-                    "mean_abs_lse_err_vs_dense_rectified": float((Lr - Ld).abs().mean())}
+                    "mean_abs_lse_err_vs_dense_sparse": float((Ls - Ld).abs().mean())}
+        for gate in (False, True):
+            rect_ms, _ = events_ms(lambda: rect_once(gate), reps, stream)
+            rect_ms = max(rect_ms - copy_ms, 1e-6)
+            rect_once(gate)
+            key = "gated" if gate else "ungated"
+            rect_out[key] = {
+                "kernel_ms": round(rect_ms, 4),
+                "tflops": round(4 * d * 64 * omitted_pairs / (rect_ms * 1e-3) / 1e12, 2),
+                "mean_abs_err_vs_dense_rectified": float((Or - Od).abs().mean()),
+                "mean_abs_lse_err_vs_dense_rectified": float((Lr - Ld).abs().mean())}
+        # share of (query, omitted block) pairs the gate keeps, on two heads'
+        # rows: |q|^2 v_j < 2 ln 2 / scale^2 with v_j the block's key spread
+        kept = total = 0
+        rows_all = bsa.csr_rows(rp, ci, nnz)
+        nB64 = bsa.n_blocks(N)
+        for h in (0, H - 1):
+            Kh = K[0, h].float()
+            nfull = nB64 * 64
+            Kp = torch.zeros((nfull, d), device=dev)
+            Kp[:N] = Kh
+            cnt = torch.full((nB64,), 64.0, device=dev)
+            cnt[-1] = N - 64 * (nB64 - 1)
+            mean = Kp.view(nB64, 64, d).sum(1) / cnt[:, None]
+            valid = (torch.arange(nfull, device=dev) < N).float().view(nB64, 64, 1)
+            spread = (((Kp.view(nB64, 64, d) - mean[:, None]) ** 2) * valid).sum((1, 2)) / (cnt * d)
+            qn2 = (Q[0, h].float() ** 2).sum(1)
+            G = qn2[:, None] * spread[None, :] < 2 * math.log(2) / (scale * scale)
+            for i in range(nB64):
+                om = torch.ones(nB64, dtype=torch.bool, device=dev)
+                om[rows_all[h * nB64 + i]] = False
+                g = G[64 * i:min(64 * i + 64, N)][:, om]
+                kept += int(g.sum())
+                total += g.numel()
+        rect_out["gate_pass_share_two_heads"] = round(kept / max(total, 1), 4)
         del Os, Or, Od
 
     cluster_out = None
@@ -646,6 +775,18 @@ def main():
             and not args.rectify:
         rows = {"k": sel["k"]}
         out["cpu_baseline"] = cpu_oracle_sample(Qc, Kc, Vc, rows, args.cpu_seconds)
+    headline_only = (args.no_per_workload or cfg != 1 or blk != 64 or args.mod_mask
+                     or args.rectify or args.cluster or args.hva or args.window_frames is not None)
+    if not headline_only:
+        # the other four workloads, one summary each (their inputs generated
+        # once, a few steps each); the headline workload's buffers are freed first
+        del W, Q, K, V, O_buf, L_buf, Om_buf, Lm_buf, ws
+        torch.cuda.empty_cache()
+        per = {}
+        for other in (0, 2, 3, 4):
+            print(f"[bench] per-workload summary of workload {other}", file=sys.stderr, flush=True)
+            per[str(other)] = workload_summary(other, args, torch, bsa)
+        out["per_workload"] = per
     print(json.dumps(out), flush=True)
 
 

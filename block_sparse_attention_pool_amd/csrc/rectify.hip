@@ -307,8 +307,11 @@ void rectify_kernel(RectifyArgs a) {
         m_run = m_new;
       }
       float p[4];
+      // a query whose blocks are all masked or gated so far keeps m_run = -inf:
+      // its exponents are then taken against 0 (p = 0, not NaN)
+      const float msafe = m_run == -INFINITY ? 0.f : m_run;
 #pragma unroll
-      for (int rr = 0; rr < 4; ++rr) p[rr] = __builtin_amdgcn_exp2f(x[rr] - m_run);
+      for (int rr = 0; rr < 4; ++rr) p[rr] = __builtin_amdgcn_exp2f(x[rr] - msafe);
       const u32x2 pk = {pack_f16x2(p[0], p[1]), pack_f16x2(p[2], p[3])};
       l_run = sum_f16x2(pk[0], sum_f16x2(pk[1], l_run));
       const f16x4 pb = __builtin_bit_cast(f16x4, pk);

@@ -454,3 +454,4 @@ def test_heads_at_risk_rejects_nan_and_bad_sizes():
         bsa.heads_at_risk(np.array([0.1, float("nan")]), 1)
     assert bsa._lib.bsa_heads_at_risk(None, 3, 1, None) == 1
 
+

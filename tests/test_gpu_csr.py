@@ -44,13 +44,14 @@ def test_check_csr_counts_each_fault():
     say("check_csr on planted faults")
     good = [[0, 3, 5], [], [1], list(range(8)), [7]]
     assert _counts(good, 8) == [0, 0, 0]
-    assert _counts([[0, 9], [1, -2, 3], [4]], 8) == [0, 2, 0]          # two out of range
+    assert _counts([[0, 9], [1, 2, 30], [4]], 8) == [0, 2, 0]          # two out of range
+    assert _counts([[0, 9], [1, -2, 3], [4]], 8) == [0, 2, 1]          # -2 also breaks the order
     assert _counts([[5, 1], [2, 2], [4, 6]], 8) == [0, 0, 2]           # unsorted, duplicate
-    assert _counts(good, 8, cap_cut=10) == [1, 0, 0]                   # last row past the cap
+    assert _counts(good, 8, cap_cut=10) == [2, 0, 0]                   # rows 3 and 4 end past the cap
 
     def back(rp):
-        rp[2] = 1   # row 1 ends before it starts; row 2 starts before its predecessor ends
-    assert _counts(good, 8, ptr_edit=back) == [1, 0, 0]
+        rp[2] = 1   # row 1 ends before it starts; row 2 then reads 3, 5, 1 (not ascending)
+    assert _counts(good, 8, ptr_edit=back) == [1, 0, 1]
     # many rows (several workgroups) with one fault per 97 rows
     rng = np.random.default_rng(3)
     rows = [sorted(rng.choice(300, size=int(rng.integers(0, 40)), replace=False).tolist())

@@ -254,7 +254,8 @@ def test_rectify_gated_workload_sampled():
     rows = {(0, h): (oracle_rows(Q, K, 0, h, kk_, False) if h in heads else [[] for _ in range(nB)])
             for h in range(H)}
     Og, Lg, _, Ls = _gated_case(Q, K, V, rows)
-    assert torch.isfinite(Lg).all() and bool((Lg >= Ls - 1e-6).all())
+    # (heads with empty rows may have every block refused: LSE -inf, O 0)
+    assert not torch.isnan(Og).any() and bool((Lg >= Ls - 1e-6).all())
     rng = np.random.default_rng(401)
     scale = 1 / math.sqrt(d)
     for h in heads:
