@@ -103,6 +103,8 @@ def _load(path: str = _LIB_PATH):
         "bsa_pooled_rectify": ([P, P, P, SP, I32, F32, I32, P, P, P, I32, P, P, I64, P], I32),
         "bsa_omission_risk": ([P, P, P, SP, P, P, I64, P], I32),
         "bsa_heads_at_risk": ([P, I32, I32, P], I32),
+        "bsa_select_blocks_noalloc": ([P, SP, I32, PP, P, P, I64, P, P], I32),
+        "bsa_select_scratch_limit": ([], I64),
         "bsa_attn_take_status": ([P, I64, SP, P, P], I32),
         "bsa_check_csr": ([P, I64, P, I64, I32, P, P], I32),
         "bsa_validate_csr_host": ([P, I64, P, I64, I32, P], I32),
@@ -126,7 +128,7 @@ EXPORTED = ("bsa_version", "bsa_last_error", "bsa_score_blocks", "bsa_select_wor
             "bsa_cluster_attn_workspace_bytes", "bsa_cluster_attn_fwd",
             "bsa_cluster_merge_workspace_bytes", "bsa_cluster_merge", "bsa_lowe_ratio_subset",
             "bsa_attn_stage_v", "bsa_heads_at_risk", "bsa_attn_take_status", "bsa_check_csr",
-            "bsa_validate_csr_host")
+            "bsa_validate_csr_host", "bsa_select_blocks_noalloc", "bsa_select_scratch_limit")
 
 
 def library_path() -> str:
@@ -311,6 +313,28 @@ def bsa_select_blocks(scores, Q_like, *, block: int = BLOCK, mode: str = "topk",
                                 _ptr(row_ptr), _ptr(col_idx), cap, _ptr(nnz), _ptr(ws),
                                 ws.numel(), _stream(stream, dev))
     _check(st, "bsa_select_blocks")
+    del keep
+    return row_ptr, col_idx, nnz
+
+
+def bsa_select_blocks_noalloc(scores, Q_like, *, row_ptr, col_idx, nnz, block: int = BLOCK,
+                              mode: str = "topk", k: int = 0, p: float = 0.9, k_min: int = 1,
+                              k_cap: int | None = None, force_diag: bool = False,
+                              static: dict | None = None, micro: dict | None = None,
+                              patterns: dict | None = None, stream=None):
+    """bsa_select_blocks into caller-given outputs (row_ptr int32
+    [B*H*ceil(N/64)+1], col_idx int32 [capacity], nnz int64 [1]) with the
+    library's static scratch: nothing is allocated here or in the library.
+    Returns (row_ptr, col_idx, nnz)."""
+    shp = shape_of(Q_like)
+    nB = n_blocks(shp.N, block)
+    sp, keep = make_select_params(mode, k=k, p=p, k_min=k_min, k_cap=k_cap,
+                                  force_diag=force_diag, static=static, micro=micro,
+                                  patterns=patterns, nB=nB)
+    st = _lib.bsa_select_blocks_noalloc(_ptr(scores), ctypes.byref(shp), block, ctypes.byref(sp),
+                                        _ptr(row_ptr), _ptr(col_idx), col_idx.numel(), _ptr(nnz),
+                                        _stream(stream, Q_like.device))
+    _check(st, "bsa_select_blocks_noalloc")
     del keep
     return row_ptr, col_idx, nnz
 

@@ -5,6 +5,7 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <mutex>
 #include <string>
 
 #include "bsa.h"
@@ -442,6 +443,36 @@ bsa_status run_attn(const uint16_t* Q, const uint16_t* K, const uint16_t* V, con
   return hip_status(bsa::launch_attn(a, s->d, dense, o_dtype == BSA_BF16, st), "attn launch");
 }
 
+// Scratch of the no-allocation selection entry point: a file-scope device
+// array that every GPU the library runs on holds until the process ends.
+// Host code uses only the device address hipGetSymbolAddress returns for it
+// (one per device, taken with that device current), never the array's name.
+constexpr int64_t kScratchBytes = int64_t(32) << 20;
+constexpr int kMaxDevices = 64;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+bsa_status scratch_of_current_device(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(BSA_ERR_UNSUPPORTED, "device %d beyond the %d the scratch table holds", dev,
+                kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_status(e, "hipGetSymbolAddress(scratch)");
+    if (ptr == nullptr) return fail(BSA_ERR_HIP, "hipGetSymbolAddress(scratch) gave NULL");
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return BSA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -636,6 +667,25 @@ bsa_status bsa_select_blocks(const float* scores, const bsa_shape* shape, int32_
   BSA_TRY(hip_status(bsa::launch_emit_bits(bits, (int)pl.W, rows, row_ptr, col_idx, col_cap, st),
                      "emit launch"));
   return BSA_OK;
+}
+
+int64_t bsa_select_scratch_limit(void) { return kScratchBytes; }
+
+bsa_status bsa_select_blocks_noalloc(const float* scores, const bsa_shape* shape, int32_t block,
+                                     const bsa_select_params* p, int32_t* row_ptr,
+                                     int32_t* col_idx, int64_t col_cap, int64_t* out_nnz,
+                                     void* stream) {
+  SelectPlan pl;
+  BSA_TRY(plan_select(shape, block, p, &pl));
+  if (pl.total > kScratchBytes)
+    return fail(BSA_ERR_CAPACITY,
+                "selection needs %lld bytes of scratch, more than the %lld the no-allocation "
+                "entry point holds (use bsa_select_blocks with a workspace)",
+                (long long)pl.total, (long long)kScratchBytes);
+  void* ws = nullptr;
+  BSA_TRY(scratch_of_current_device(&ws));
+  return bsa_select_blocks(scores, shape, block, p, row_ptr, col_idx, col_cap, out_nnz, ws,
+                           kScratchBytes, stream);
 }
 
 int64_t bsa_attn_workspace_bytes(const bsa_shape* shape) {

@@ -223,6 +223,34 @@ bsa_status bsa_select_blocks(const float* scores, const bsa_shape* shape,
                              void* workspace, int64_t workspace_bytes,
                              void* stream);
 
+/* ------------------------------------------------------------------------
+ * bsa_select_blocks_noalloc -- bsa_select_blocks for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc): the same arguments, results and
+ * errors without the workspace.  Its scratch is a static device array of
+ * bsa_select_scratch_limit() bytes (32 MiB) that each GPU the library runs
+ * on holds until the process ends; the call allocates nothing (no
+ * hipMalloc, no allocating library routine).  Selections whose
+ * bsa_select_workspace_bytes exceeds the limit are refused with
+ * BSA_ERR_CAPACITY before any HIP call (every TOPK, TOPP and STATIC
+ * selection of up to 4096 blocks per row for B*H*nB up to ~60,000 rows
+ * fits; MICRO fits only small layers: its tile scores take 4 (B*heads)
+ * ceil(N/16)^2 bytes).  All calls on one GPU share its array: calls that
+ * overlap in time on one GPU (several streams or host threads) race and
+ * must be serialised by the caller.  The first call on a device looks up
+ * the array's device address (hipGetSymbolAddress) with that device
+ * current.
+ * ---------------------------------------------------------------------- */
+bsa_status bsa_select_blocks_noalloc(const float* scores,
+                                     const bsa_shape* shape, int32_t block,
+                                     const bsa_select_params* params,
+                                     int32_t* row_ptr, int32_t* col_idx,
+                                     int64_t col_cap, int64_t* out_nnz,
+                                     void* stream);
+
+/* Bytes of the no-allocation entry point's static scratch (32 MiB). */
+int64_t bsa_select_scratch_limit(void);
+
 /* Bytes of device workspace the attention entry points need (the key-major
  * copy of V the PV products read, the micro residual's sub-tile order, and
  * a status word in the last 256 bytes).  Returns -1 on invalid arguments.

@@ -455,3 +455,24 @@ def test_heads_at_risk_rejects_nan_and_bad_sizes():
     assert bsa._lib.bsa_heads_at_risk(None, 3, 1, None) == 1
 
 
+
+def test_noalloc_select_refuses_oversized_work_before_any_hip_call():
+    # micro tile scores of 8 heads of 65,536 tokens need 512 MiB > 32 MiB;
+    # the refusal comes from the size check, before any HIP call (no GPU here)
+    assert bsa._lib.bsa_select_scratch_limit() == 32 << 20
+    s = _shape(B=1, H=8, N=65536, d=64)
+    sp, keep = bsa.make_select_params("micro", micro=dict(
+        m=4, scale=0.125, macro=(_AddrOnly(), _AddrOnly()), qpool16=_AddrOnly(), kpool16=_AddrOnly()))
+    p = ctypes.c_void_p(4096)
+    st = bsa._lib.bsa_select_blocks_noalloc(None, ctypes.byref(s), 64, ctypes.byref(sp), p, p, 10,
+                                            p, None)
+    assert st == 3 and "scratch" in bsa.bsa_last_error()
+
+
+class _AddrOnly:
+    """Stands in for a device tensor in the parameter struct (only its
+    address is stored)."""
+    shape = (1, 8, 1, 1)
+
+    def data_ptr(self):
+        return 4096
