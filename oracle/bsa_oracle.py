@@ -653,39 +653,75 @@ def window_start(g: int, w: int, K: int) -> int:
     return min(max(g - w // 2, 0), K - w)
 
 
+def window_candidates(thw, cell, window) -> np.ndarray:
+    """[HVA] Eq. 5's candidate set N(g(l)) for every token l: the centroids
+    of the (wt, wh, ww) window of cells around the token's own cell g(l),
+    the window clipped to the grid.  Returns [N, wt*wh*ww] centroid ids in
+    ascending order (cells numbered t-major)."""
+    T, H, W = thw
+    K, w = cluster_grid(thw, cell, window)
+    t, h, x = np.meshgrid(np.arange(T), np.arange(H), np.arange(W), indexing="ij")
+    g = [ax.reshape(-1) // cell[a] for a, ax in enumerate((t, h, x))]   # token's cell per axis
+    st = [np.array([window_start(int(v), w[a], K[a]) for v in range(K[a])])[g[a]]
+          for a in range(3)]                                           # window start per axis
+    ot, oh, ow = np.meshgrid(np.arange(w[0]), np.arange(w[1]), np.arange(w[2]), indexing="ij")
+    ct = st[0][:, None] + ot.reshape(-1)[None, :]
+    ch = st[1][:, None] + oh.reshape(-1)[None, :]
+    cw = st[2][:, None] + ow.reshape(-1)[None, :]
+    return (ct * K[1] + ch) * K[2] + cw
+
+
+def nearest_centroid(X, mu, cand) -> np.ndarray:
+    """[HVA] Eq. 5: every token's nearest centroid (squared Euclidean
+    distance) among its candidates; equal distances go to the lower
+    centroid index (candidates are listed ascending, the first minimum
+    wins)."""
+    best_d = np.full(X.shape[0], np.inf)
+    best = np.zeros(X.shape[0], dtype=np.int64)
+    for s in range(cand.shape[1]):
+        c = cand[:, s]
+        dist = ((X - mu[c]) ** 2).sum(axis=1)
+        better = dist < best_d
+        best_d = np.where(better, dist, best_d)
+        best = np.where(better, c, best)
+    return best
+
+
+def member_means(X, a, mu):
+    """[HVA] section 4.1: every centroid moves to the mean of the tokens
+    assigned to it; a centroid with no token keeps its position.  Returns
+    (centroids, counts)."""
+    n = mu.shape[0]
+    counts = np.bincount(a, minlength=n)
+    sums = np.zeros_like(mu)
+    np.add.at(sums, a, X)
+    out = mu.copy()
+    moved = counts > 0
+    out[moved] = sums[moved] / counts[moved, None]
+    return out, counts
+
+
 def local_window_clustering(X, thw, cell, window, iters: int):
-    """Returns (assignment [N] int, centroids [Nc, d], counts [Nc])."""
+    """[HVA] section 4.1 (Eq. 5) and Appendix A.2: 3D local-window
+    clustering.  A fixed grid of (kt, kh, kw) cells gives one centroid per
+    cell, started at the cell's centre token (clamped to the lattice); each
+    iteration assigns every token to its nearest centroid within the window
+    of cells around its own cell (``nearest_centroid`` over
+    ``window_candidates``), then moves the centroids to their members' means.
+    Returns (assignment [N] int, centroids [Nc, d], counts [Nc]) after the
+    last iteration."""
     X = np.asarray(X, np.float64)
     T, H, W = thw
     N, d = X.shape
     assert N == T * H * W and iters >= 1
-    K, w = cluster_grid(thw, cell, window)
-    Kt, Kh, Kw = K
-    cells = [(ut, uh, uw) for ut in range(Kt) for uh in range(Kh) for uw in range(Kw)]
-    cid = lambda ut, uh, uw: (ut * Kh + uh) * Kw + uw
-    tok = lambda t, h, x: (t * H + h) * W + x
-    mu = np.stack([X[tok(min(ut * cell[0] + cell[0] // 2, T - 1),
-                         min(uh * cell[1] + cell[1] // 2, H - 1),
-                         min(uw * cell[2] + cell[2] // 2, W - 1))]
-                   for ut, uh, uw in cells])
-    a = np.zeros(N, dtype=np.int64)
+    K, _ = cluster_grid(thw, cell, window)
+    centre = [np.minimum(np.arange(K[a]) * cell[a] + cell[a] // 2, thw[a] - 1) for a in range(3)]
+    ut, uh, uw = np.meshgrid(*centre, indexing="ij")
+    mu = X[((ut * H + uh) * W + uw).reshape(-1)].copy()
+    cand = window_candidates(thw, cell, window)
     for _ in range(iters):
-        for ut, uh, uw in cells:
-            ts = range(ut * cell[0], min(ut * cell[0] + cell[0], T))
-            hs = range(uh * cell[1], min(uh * cell[1] + cell[1], H))
-            ws = range(uw * cell[2], min(uw * cell[2] + cell[2], W))
-            toks = np.array([tok(t, h, x) for t in ts for h in hs for x in ws])
-            st, sh, sw = (window_start(ut, w[0], Kt), window_start(uh, w[1], Kh),
-                          window_start(uw, w[2], Kw))
-            cand = np.array([cid(vt, vh, vw) for vt in range(st, st + w[0])
-                             for vh in range(sh, sh + w[1]) for vw in range(sw, sw + w[2])])
-            dist = ((X[toks][:, None, :] - mu[cand][None, :, :]) ** 2).sum(axis=2)
-            a[toks] = cand[np.argmin(dist, axis=1)]   # first minimum = lowest index
-        counts = np.bincount(a, minlength=len(cells))
-        sums = np.zeros_like(mu)
-        np.add.at(sums, a, X)
-        moved = counts > 0
-        mu[moved] = sums[moved] / counts[moved, None]
+        a = nearest_centroid(X, mu, cand)
+        mu, counts = member_means(X, a, mu)
     return a, mu, counts
 
 
