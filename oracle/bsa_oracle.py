@@ -60,6 +60,10 @@ Readings where the pages are silent:
     variance);
   * [HVA] Eq. 6 (Lowe's ratio) is taken over each token's local window,
     the candidates of its assignment, against the centroids given;
+  * [HVA] section 4.2's intermediate-step update: the subset tokens are
+    reassigned against every centroid, then the centroids any of them left
+    or joined become the means of their members (current embeddings); the
+    others keep their anchor-step positions;
   * [HVA] Algorithm 1: the random bipartition is an input (a side bit per
     round for every group, read at the group's lowest member); side-0 groups
     choose, ties go to lower indices; a merged group is named by its lowest
@@ -811,6 +815,35 @@ def lowe_subset(rho, n: int) -> np.ndarray:
     most ambiguous assignments; equal ratios go to the lower index), in
     ascending token order."""
     return np.sort(rank_desc(np.asarray(rho, np.float64))[:max(0, n)])
+
+
+def subset_refinement(X, assign, mu, subset):
+    """[HVA] section 4.2, the intermediate-step update of the hybrid
+    clustering: only the cached subset of tokens (the largest Lowe's
+    ratios of the anchor step) is revisited.  Each subset token is reassigned
+    by a standard k-means step against the whole current centroid set (its
+    squared Euclidean distance to every centroid; equal distances to the
+    lower index), not only its local window.  Then the corresponding
+    centroids -- every centroid a subset token left or joined -- move to the
+    mean of their members under the new assignment, with the current token
+    embeddings X; a centroid left without members keeps its position, every
+    other centroid is untouched.  Returns (assignment [N], centroids [Nc, d],
+    members per centroid [Nc]).  ``subset`` holds distinct token indices."""
+    X = np.asarray(X, np.float64)
+    a = np.asarray(assign, dtype=np.int64).copy()
+    mu = np.asarray(mu, np.float64).copy()
+    S = np.asarray(subset, dtype=np.int64)
+    old = a[S]
+    new = np.array([int(np.argmin(((mu - X[t]) ** 2).sum(axis=1))) for t in S], dtype=np.int64)
+    a[S] = new
+    moved = new != old
+    touched = np.union1d(old[moved], new[moved])
+    counts = np.bincount(a, minlength=mu.shape[0])
+    for c in touched:
+        members = np.nonzero(a == c)[0]
+        if members.size:
+            mu[c] = X[members].mean(axis=0)
+    return a, mu, counts
 
 
 def merge_cost(sq: int, chi, sizes_k, tau_q: int = 64, tau_k: int = 64, g: int = 1) -> int:

@@ -1244,3 +1244,88 @@ def test_lowe_pins_catch_planted_mistakes(mistake, monkeypatch):
     monkeypatch.setattr(O, "lowe_ratios", wrong)
     with pytest.raises(AssertionError):
         test_golden_lowe_ratio()
+
+
+# ------------------------------------------------ HVA subset refinement (4.2)
+
+def test_golden_subset_refinement():
+    g = _load("hva_subset_refine.json")
+    a, mu, n = O.subset_refinement(np.array(g["X"]), g["assign"], np.array(g["mu"]), g["subset"])
+    assert a.tolist() == g["assign_out"]
+    np.testing.assert_allclose(mu, g["mu_out"], atol=1e-15)
+    assert n.tolist() == g["counts_out"]
+
+
+def test_subset_refinement_of_every_token_is_one_lloyd_step():
+    # with the whole lattice as the subset and centroids that are their
+    # members' means, the update is one step of Lloyd's k-means: assign to
+    # the nearest centroid, then move every centroid that changed members to
+    # its members' mean (scikit-learn's single Lloyd iteration moves all of
+    # them; the untouched ones are already their members' means)
+    from sklearn.cluster import KMeans
+    rng = np.random.default_rng(91)
+    X = np.concatenate([rng.standard_normal((60, 5)) + 4 * rng.standard_normal(5) for _ in range(6)])
+    a0 = rng.integers(0, 6, X.shape[0])
+    mu0 = np.stack([X[a0 == c].mean(axis=0) for c in range(6)])
+    a, mu, n = O.subset_refinement(X, a0, mu0, np.arange(X.shape[0]))
+    km = KMeans(n_clusters=6, init=mu0, n_init=1, max_iter=1, algorithm="lloyd").fit(X)
+    # scikit-learn's labels_ come from one more assignment after the update;
+    # compare the centroids and recompute the first assignment directly
+    np.testing.assert_allclose(mu, km.cluster_centers_, atol=1e-12)
+    first = np.argmin(((X[:, None, :] - mu0[None]) ** 2).sum(-1), axis=1)
+    assert np.array_equal(a, first)
+    assert n.tolist() == np.bincount(first, minlength=6).tolist()
+
+
+def test_subset_refinement_leaves_other_tokens_and_centroids_alone():
+    rng = np.random.default_rng(92)
+    X = rng.standard_normal((200, 4))
+    mu = rng.standard_normal((9, 4)) * 2
+    a0 = rng.integers(0, 9, 200)
+    S = rng.choice(200, 30, replace=False)
+    a, mu2, n = O.subset_refinement(X, a0, mu, S)
+    rest = np.setdiff1d(np.arange(200), S)
+    assert np.array_equal(a[rest], a0[rest])
+    # brute force: nearest of all centroids with explicit loops, ties low
+    for t in S:
+        best, bd = 0, math.inf
+        for c in range(9):
+            dd = sum((X[t, k] - mu[c, k]) ** 2 for k in range(4))
+            if dd < bd:
+                best, bd = c, dd
+        assert a[t] == best
+    moved = S[a[S] != a0[S]]
+    touched = set(a0[moved]) | set(a[moved])
+    for c in range(9):
+        if c in touched and n[c] > 0:
+            np.testing.assert_allclose(mu2[c], X[a == c].mean(axis=0), atol=1e-13)
+        else:
+            assert np.array_equal(mu2[c], mu[c])
+    assert n.sum() == 200
+    # an empty subset changes nothing
+    a3, mu3, _ = O.subset_refinement(X, a0, mu, [])
+    assert np.array_equal(a3, a0) and np.array_equal(mu3, mu)
+
+
+def test_subset_refinement_pin_catches_a_stale_or_local_update(monkeypatch):
+    g = _load("hva_subset_refine.json")
+    X = np.array(g["X"])
+    # a planted mistake: centroids updated from the anchor-step means by the
+    # moved tokens only (the stale-sum transfer) instead of their members
+    real = O.subset_refinement
+
+    def transfer(X_, assign, mu, subset):
+        a, _, n = real(X_, assign, mu, subset)
+        mu = np.asarray(mu, float).copy()
+        old = np.bincount(np.asarray(assign), minlength=len(mu))
+        sums = old[:, None] * mu
+        for t in subset:
+            sums[assign[t]] -= X_[t]
+            sums[a[t]] += X_[t]
+        ok = n > 0
+        mu[ok] = sums[ok] / n[ok, None]
+        return a, mu, n
+    monkeypatch.setattr(O, "subset_refinement", transfer)
+    with pytest.raises(AssertionError):
+        test_golden_subset_refinement()
+
