@@ -103,6 +103,8 @@ def _load(path: str = _LIB_PATH):
         "bsa_pooled_rectify": ([P, P, P, SP, I32, F32, I32, P, P, P, I32, P, P, I64, P], I32),
         "bsa_omission_risk": ([P, P, P, SP, P, P, I64, P], I32),
         "bsa_heads_at_risk": ([P, I32, I32, P], I32),
+        "bsa_subset_refine_workspace_bytes": ([SP, I32], I64),
+        "bsa_subset_refine": ([P, SP, I32, P, I32, P, P, P, P, I64, P], I32),
         "bsa_select_blocks_noalloc": ([P, SP, I32, PP, P, P, I64, P, P], I32),
         "bsa_select_scratch_limit": ([], I64),
         "bsa_attn_take_status": ([P, I64, SP, P, P], I32),
@@ -128,7 +130,8 @@ EXPORTED = ("bsa_version", "bsa_last_error", "bsa_score_blocks", "bsa_select_wor
             "bsa_cluster_attn_workspace_bytes", "bsa_cluster_attn_fwd",
             "bsa_cluster_merge_workspace_bytes", "bsa_cluster_merge", "bsa_lowe_ratio_subset",
             "bsa_attn_stage_v", "bsa_heads_at_risk", "bsa_attn_take_status", "bsa_check_csr",
-            "bsa_validate_csr_host", "bsa_select_blocks_noalloc", "bsa_select_scratch_limit")
+            "bsa_validate_csr_host", "bsa_select_blocks_noalloc", "bsa_select_scratch_limit",
+            "bsa_subset_refine_workspace_bytes", "bsa_subset_refine")
 
 
 def library_path() -> str:
@@ -653,6 +656,31 @@ def bsa_cluster_attn_fwd(Q, K, V, perm_q, off_q, perm_k, off_k, crow_ptr, ccol, 
                                    _ptr(ws), ws.numel(), _stream(stream, dev))
     _check(st, "bsa_cluster_attn_fwd")
     return O, L, pairs
+
+
+def bsa_subset_refine(X, subset, assign, centroids, counts, *, stream=None):
+    """HVA intermediate-step update: the subset tokens (int32 [B, H, n_sub])
+    reassigned against every centroid, the centroids they left or joined
+    moved to their members' means.  assign [B, H, N] int32, centroids
+    [B, H, cells, d] float32 and counts [B, H, cells] int32 are updated in
+    place and returned."""
+    if X.dtype != torch.bfloat16:
+        raise ValueError("X must be bfloat16")
+    shp = shape_of(X)
+    cells = centroids.shape[2]
+    for t, dt in ((subset, torch.int32), (assign, torch.int32), (centroids, torch.float32),
+                  (counts, torch.int32)):
+        if t.dtype != dt or not t.is_contiguous():
+            raise ValueError("subset, assign, counts int32 and centroids float32, contiguous")
+    n = _lib.bsa_subset_refine_workspace_bytes(ctypes.byref(shp), cells)
+    if n < 0:
+        raise BsaError(f"bsa_subset_refine_workspace_bytes: {bsa_last_error()}")
+    ws = torch.empty(max(n, 256), dtype=torch.uint8, device=X.device)
+    st = _lib.bsa_subset_refine(_ptr(X), ctypes.byref(shp), cells, _ptr(subset), subset.shape[2],
+                                _ptr(assign), _ptr(centroids), _ptr(counts), _ptr(ws), ws.numel(),
+                                _stream(stream, X.device))
+    _check(st, "bsa_subset_refine")
+    return assign, centroids, counts
 
 
 def bsa_omission_risk(lse_sparse, lse_full, lse_repaired=None, *, out=None, stream=None):

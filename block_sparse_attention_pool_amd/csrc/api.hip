@@ -1157,6 +1157,59 @@ bsa_status bsa_lowe_ratio_subset(const uint16_t* X, const bsa_shape* shape,
                     "lowe launch");
 }
 
+int64_t bsa_subset_refine_workspace_bytes(const bsa_shape* shape, int32_t cells) {
+  if (check_shape(shape) != BSA_OK) return -1;
+  if (cells < 1) {
+    fail(BSA_ERR_INVALID_ARG, "cells=%d must be >= 1", cells);
+    return -1;
+  }
+  const int64_t bh = (int64_t)shape->B * shape->H;
+  return align256(bh * cdiv(cells, 32) * 4) + align256(bh * cells * 4) +
+         align256(bh * cells * shape->d * 8);
+}
+
+bsa_status bsa_subset_refine(const uint16_t* X, const bsa_shape* shape, int32_t cells,
+                             const int32_t* subset, int32_t n_sub, int32_t* assign,
+                             float* centroids, int32_t* counts, void* workspace,
+                             int64_t workspace_bytes, void* stream) {
+  BSA_TRY(check_shape(shape));
+  if (cells < 1) return fail(BSA_ERR_INVALID_ARG, "cells=%d must be >= 1", cells);
+  if (n_sub < 0 || n_sub > shape->N)
+    return fail(BSA_ERR_INVALID_ARG, "n_sub=%d outside [0, N=%d]", n_sub, shape->N);
+  if ((int64_t)shape->B * shape->H > 65535) return fail(BSA_ERR_UNSUPPORTED, "B*H exceeds 65535");
+  BSA_TRY(check_ptr(X, "X"));
+  if (n_sub > 0) BSA_TRY(check_ptr(subset, "subset", 4));
+  BSA_TRY(check_ptr(assign, "assign", 4));
+  BSA_TRY(check_ptr(centroids, "centroids", 16));
+  BSA_TRY(check_ptr(counts, "counts", 4));
+  BSA_TRY(check_ptr(workspace, "workspace", 256));
+  const int64_t need = bsa_subset_refine_workspace_bytes(shape, cells);
+  if (workspace_bytes < need)
+    return fail(BSA_ERR_CAPACITY, "workspace %lld bytes < required %lld",
+                (long long)workspace_bytes, (long long)need);
+  const int64_t bh = (int64_t)shape->B * shape->H;
+  char* ws = (char*)workspace;
+  bsa::RefineArgs a{};
+  a.X = X;
+  a.sb = shape->stride_b;
+  a.sh = shape->stride_h;
+  a.sn = shape->stride_n;
+  a.H = shape->H;
+  a.N = shape->N;
+  a.Nc = cells;
+  a.W = (int)cdiv(cells, 32);
+  a.subset = subset;
+  a.n_sub = n_sub;
+  a.assign = assign;
+  a.mu = centroids;
+  a.counts = counts;
+  a.touched = (uint32_t*)ws;
+  a.tcount = (int32_t*)(ws + align256(bh * a.W * 4));
+  a.sums = (double*)(ws + align256(bh * a.W * 4) + align256(bh * cells * 4));
+  return hip_status(bsa::launch_subset_refine(a, (int)bh, shape->d, (hipStream_t)stream),
+                    "subset refine launch");
+}
+
 int64_t bsa_cluster_permute_workspace_bytes(const bsa_shape* shape,
                                             const bsa_cluster_params* params) {
   int64_t cells = 0;

@@ -632,11 +632,11 @@ void attn_fwd_kernel(AttnArgs a) {
 // registers.  A tile's K rows (4 KB) and V^T chunk (4 KB) are contiguous;
 // the fragments of tile e+1 are loaded while tile e is computed.
 //
-// Sub-tiles run in the order of `order`: sorted, per head, by the MinHash
-// representative of the key tiles each one selects (micro_sig_kernel), and
-// dealt to the XCDs in contiguous ranges, so that sub-tiles gathering mostly
-// the same tiles run together on one XCD and share them through its L2.
-// Each sub-tile is computed on its own, so the order changes no result.
+// Sub-tiles run in the order of `order`: sorted, per head, by the first key
+// tile each one selects, and dealt to the XCDs in contiguous ranges, so that
+// sub-tiles gathering the same tiles run together on one XCD and share them
+// through its L2.  Each sub-tile is computed on its own, so the order changes
+// no result.
 template <int D, bool OUT_BF16>
 // Three waves per SIMD (152 VGPRs, no accumulation registers) keep more
 // tile gathers in flight than the two the compiler plans for by default:
@@ -775,24 +775,9 @@ void micro_attn_kernel(MicroAttnArgs a) {
   }
 }
 
-// A fixed bijective mix of 32-bit tile indices (a random-looking order).
-__device__ __forceinline__ uint32_t tile_hash(uint32_t x) {
-  x *= 0x9E3779B1u;
-  x ^= x >> 15;
-  x *= 0x85EBCA77u;
-  x ^= x >> 13;
-  return x;
-}
-
-// Signature of every sub-tile: its global bin (z, key tile), nT for an
-// empty sub-tile.  The key tile is the MinHash representative of the
-// sub-tile's selected set: the member of smallest tile_hash.  Two sub-tiles
-// get the same representative with probability equal to the Jaccard overlap
-// of their sets, so sub-tiles that gather mostly the same tiles land in one
-// bin and run together (the lowest member would instead follow each query
-// block's macro row, which removes different low tiles from otherwise equal
-// sets).  A row's entries are sorted by (sub-tile, key tile): sub-tile a's
-// segment starts where a binary search finds it.
+// Signature of every sub-tile: its global bin (z, first key tile selected),
+// nT for an empty sub-tile; a row's entries are sorted by (sub-tile, key
+// tile), so the first entry of sub-tile a is found by binary search.
 __global__ __launch_bounds__(256) void micro_sig_kernel(MicroAttnArgs a) {
   const int sid = blockIdx.x * 256 + threadIdx.x;
   if (sid >= a.slots) return;
@@ -809,21 +794,10 @@ __global__ __launch_bounds__(256) void micro_sig_kernel(MicroAttnArgs a) {
     if ((a.idx[mid] & 3) < sub) lo = mid + 1;
     else hi = mid;
   }
-  int rep = a.nT;
-  uint32_t best = 0xFFFFFFFFu;
-  for (int e = lo; e < end; ++e) {
-    const int code = a.idx[e];
-    if ((code & 3) != sub) break;
-    const int beta = code >> 2;
-    // (a tile index outside [0, nT) sorts with the empty sub-tiles)
-    if ((unsigned)beta >= (unsigned)a.nT) continue;
-    const uint32_t hv = tile_hash((uint32_t)beta);
-    if (rep == a.nT || hv < best) {
-      best = hv;
-      rep = beta;
-    }
-  }
-  const int bin = z * (a.nT + 1) + rep;
+  // (a tile index outside [0, nT) sorts with the empty sub-tiles)
+  int first = (lo < end && (a.idx[lo] & 3) == sub) ? (a.idx[lo] >> 2) : a.nT;
+  if ((unsigned)first > (unsigned)a.nT) first = a.nT;
+  const int bin = z * (a.nT + 1) + first;
   a.sig[sid] = bin;
   atomicAdd(&a.hist[bin], 1);
 }

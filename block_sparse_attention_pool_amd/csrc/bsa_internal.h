@@ -244,6 +244,23 @@ struct ClusterMergeArgs {
 // merging (per-head tables held in LDS; key masks of at most 128 words).
 constexpr int kMaxClusters = 4096;
 
+// HVA subset refinement (intermediate-step update of the hybrid clustering).
+struct RefineArgs {
+  const uint16_t* X;        // [B, H, N, D] with strides
+  int64_t sb, sh, sn;
+  int H, N, Nc, W;          // W: 32-bit words of a head's touched bitmap
+  const int32_t* subset;    // [BH, n_sub] token indices
+  int n_sub;
+  int32_t* assign;          // [BH, N] in/out
+  float* mu;                // [BH, Nc, D] in/out
+  int32_t* counts;          // [BH, Nc] in/out
+  uint32_t* touched;        // [BH, W] (workspace)
+  int32_t* tcount;          // [BH, Nc] (workspace)
+  double* sums;             // [BH, Nc, D] (workspace)
+};
+
+hipError_t launch_subset_refine(const RefineArgs& a, int BH, int D, hipStream_t s);
+
 // Pooled rectification of omitted blocks.
 constexpr int kMaxRowWords = 128;  // bitmap words of a row of up to 4096 blocks
 

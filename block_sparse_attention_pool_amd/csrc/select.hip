@@ -427,6 +427,47 @@ __global__ void fill_i32_kernel(int32_t* p, int64_t n, int32_t v) {
 
 // ---------------------------------------------------------- micro select
 
+// Value-binned selection: bins of the score range, and the candidates of the
+// threshold bin the LDS list holds at most.
+constexpr int kMicroBins = 2048;
+constexpr int kMicroList = 1024;
+
+// The float a (nonzero) order key came from: the inverse of float_order_key.
+__device__ __forceinline__ float key_to_float(uint32_t k) {
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
+}
+
+__device__ __forceinline__ float wave_min(float v) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v = fminf(v, __shfl_xor(v, off));
+  return v;
+}
+
+// Exclusive prefix over the threads of the block in reversed thread order
+// (thread t gets the sum over threads t' > t); also returns the total.
+template <typename T>
+__device__ T block_exclusive_scan_rev(T v, T* red, T* total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int nw = blockDim.x >> 6;
+  // suffix sum within the wave: lanes above this one
+  T suf = v;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const T o = __shfl_down(suf, off);
+    if (lane + off < 64) suf += o;
+  }
+  __syncthreads();
+  if (lane == 0) red[wave] = suf;  // the whole wave's sum
+  __syncthreads();
+  T off = 0, tot = 0;
+  for (int w = 0; w < nw; ++w) {
+    if (w > wave) off += red[w];
+    tot += red[w];
+  }
+  *total = tot;
+  return off + suf - v;
+}
+
 // Radix selection, most significant byte first, of the `remaining`-th
 // largest 32-bit key among the keys each thread hands to the visitor
 // (each(f) calls f(key) for every candidate key of the calling thread).
@@ -497,6 +538,12 @@ void micro_select_kernel(MicroSelectArgs a) {
   __shared__ int sh_out[2];
   __shared__ int ired[16];
   __shared__ int wcnt[16][E];
+  __shared__ uint32_t hist2[kMicroBins];
+  __shared__ float fred[32];
+  __shared__ uint32_t list_n;
+  __shared__ uint32_t list_key[kMicroList];
+  __shared__ uint32_t list_code[kMicroList];
+  __shared__ uint32_t sh_tc[2];
 
   const int i = blockIdx.x;
   const int z = blockIdx.y;
@@ -556,7 +603,97 @@ void micro_select_kernel(MicroSelectArgs a) {
   const int m = a.m;
   uint32_t T = 0u, C = 0xFFFFFFFFu;  // threshold key; largest code taken at T
   const bool all = nvalid <= m;
+  // The m-th best candidate by (score descending, code ascending) is (T, C).
+  // Fast path: a histogram of the scores over kMicroBins equal-width bins
+  // between the row's smallest and largest score (a monotone map, so every
+  // candidate of a higher bin beats every candidate of a lower one; equal
+  // scores share a bin) finds the bin holding the m-th best; its few
+  // candidates are ranked exactly in LDS.  Bins by value, not by the top bits
+  // of the key: scores of one row share their sign and exponent, so bit bins
+  // would put most candidates on a handful of LDS counters.  When that bin
+  // holds more than kMicroList candidates (many equal scores) the radix
+  // selection over the keys runs instead.
+  bool exact_done = all;
   if (!all) {
+    float vmin = INFINITY, vmax = -INFINITY;
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      if (key[e] != 0u) {
+        const float v = key_to_float(key[e]);
+        vmin = fminf(vmin, v);
+        vmax = fmaxf(vmax, v);
+      }
+    }
+    vmin = wave_min(vmin);
+    vmax = wave_max(vmax);
+    if (lane == 0) {
+      fred[wave] = vmin;
+      fred[16 + wave] = vmax;
+    }
+    for (int q = tid; q < kMicroBins; q += 1024) hist2[q] = 0u;
+    if (tid == 0) list_n = 0;
+    __syncthreads();
+    vmin = INFINITY;
+    vmax = -INFINITY;
+    for (int w = 0; w < 16; ++w) {
+      vmin = fminf(vmin, fred[w]);
+      vmax = fmaxf(vmax, fred[16 + w]);
+    }
+    if (vmax > vmin) {
+      const float sc = (float)kMicroBins / (vmax - vmin);
+      auto bin_of = [&](uint32_t k) {
+        return min(kMicroBins - 1, (int)((key_to_float(k) - vmin) * sc));
+      };
+#pragma unroll
+      for (int e = 0; e < E; ++e)
+        if (key[e] != 0u) atomicAdd(&hist2[bin_of(key[e])], 1u);
+      __syncthreads();
+      // bins 2t, 2t+1 per thread; candidates in the bins above them
+      const int b0 = 2 * tid;
+      const int h0 = (int)hist2[b0], h1 = (int)hist2[b0 + 1];
+      int tot;
+      // exclusive prefix in reversed thread order = suffix over higher bins
+      const int above = block_exclusive_scan_rev(h0 + h1, ired, &tot);
+      if (above < m && above + h1 >= m) {
+        sh_out[0] = b0 + 1;
+        sh_out[1] = above;
+      } else if (above + h1 < m && above + h1 + h0 >= m) {
+        sh_out[0] = b0;
+        sh_out[1] = above + h1;
+      }
+      __syncthreads();
+      const int bstar = sh_out[0];
+      const int need = m - sh_out[1];
+      const int cstar = (int)hist2[bstar];
+      if (cstar <= kMicroList) {
+        for_codes([&](int e, int, uint32_t code) {
+          if (key[e] != 0u && bin_of(key[e]) == bstar) {
+            const int pos = (int)atomicAdd(&list_n, 1u);
+            list_key[pos] = key[e];
+            list_code[pos] = code;
+          }
+        });
+        __syncthreads();
+        for (int t = tid; t < cstar; t += 1024) {
+          const uint32_t kt = list_key[t], ct = list_code[t];
+          int rank = 0;
+          for (int u2 = 0; u2 < cstar; ++u2) {
+            const uint32_t ku = list_key[u2];
+            rank += ku > kt || (ku == kt && list_code[u2] < ct);
+          }
+          if (rank == need - 1) {
+            sh_tc[0] = kt;
+            sh_tc[1] = ct;
+          }
+        }
+        __syncthreads();
+        T = sh_tc[0];
+        C = sh_tc[1];
+        exact_done = true;
+      }
+    }
+  }
+  if (!exact_done) {
     int remaining = m;
     T = block_radix_select(remaining, [&](auto f) {
 #pragma unroll

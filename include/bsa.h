@@ -21,6 +21,8 @@
  *   bsa_cluster_permute   tokens in cluster order (HVA Eq. 1).
  *   bsa_cluster_select    key clusters per query cluster (HVA Eq. 2-3).
  *   bsa_lowe_ratio_subset Lowe's ratio and the most ambiguous tokens (HVA Eq. 6).
+ *   bsa_subset_refine     the intermediate-step update of those tokens
+ *                         against every centroid (HVA section 4.2).
  *   bsa_cluster_merge     merging of query clusters by tiled cost (HVA Alg. 1).
  *   bsa_cluster_attn_fwd  attention over cluster-induced blocks (HVA Eq. 4).
  *   bsa_omission_risk     per-head share of the full softmax mass a sparse
@@ -476,6 +478,45 @@ bsa_status bsa_local_window_cluster(const uint16_t* X, const bsa_shape* shape,
                                     int32_t* assign, float* centroids,
                                     int32_t* counts, void* workspace,
                                     int64_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * bsa_subset_refine -- HyperVAttention section 4.2, the intermediate-step
+ * update of its hybrid clustering: full local-window clustering runs only
+ * at anchor steps, which also cache the tokens of largest Lowe's ratio
+ * (bsa_lowe_ratio_subset); at the steps in between only that subset is
+ * revisited.  Each subset token is reassigned by a standard k-means step
+ * against EVERY centroid of its head (not only its local window): the
+ * nearest by squared Euclidean distance, ties to the lower index.  Then the
+ * centroids that a subset token left or joined move to the mean of their
+ * members under the new assignment, using the current embeddings X; one
+ * left without members keeps its position; every other centroid (and every
+ * token outside the subset) is left as it is.
+ *
+ * X: bf16 [B, H, N, d] with the strides of `shape`: the CURRENT step's
+ *   queries or keys.
+ * cells: centroids per head.
+ * subset: int32 [B, H, n_sub], distinct token indices per head (e.g. the
+ *   output of bsa_lowe_ratio_subset at the anchor step); an index outside
+ *   [0, N) is ignored.
+ * assign: int32 [B, H, N], centroids: float32 [B, H, cells, d], counts: int32
+ *   [B, H, cells]: the clustering state (bsa_local_window_cluster's outputs
+ *   or a previous refinement), updated in place; counts must be the member
+ *   counts of `assign`.
+ * workspace: >= bsa_subset_refine_workspace_bytes(shape, cells) bytes,
+ *   256-byte aligned (touched-centroid bitmaps, member counts and float64
+ *   member sums).
+ * Precision: distances as float32 sums of (x - mu)^2 (near-ties within
+ *   float32 rounding may resolve either way); member sums in float64 (exact
+ *   for bf16 members within a 2^40 range of magnitudes, so repeated calls
+ *   agree), means rounded to float32.
+ * ---------------------------------------------------------------------- */
+int64_t bsa_subset_refine_workspace_bytes(const bsa_shape* shape, int32_t cells);
+
+bsa_status bsa_subset_refine(const uint16_t* X, const bsa_shape* shape,
+                             int32_t cells, const int32_t* subset,
+                             int32_t n_sub, int32_t* assign, float* centroids,
+                             int32_t* counts, void* workspace,
+                             int64_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------
  * bsa_cluster_permute -- HyperVAttention Eq. 1: the permutation that places

@@ -668,3 +668,95 @@ def test_cluster_merge_and_attention_at_the_cluster_limit():
         Oref, Lref = O.attend(q[qi], k[keys], v[keys], 1 / np.sqrt(d))
         idx = torch.from_numpy(qi.astype(np.int64)).to(DEV)
         PT.compare_o_lse(Og[0, 0][idx], Lg[0, 0][idx], Oref, Lref, f"query cluster {i}")
+
+
+# ------------------------------------------- subset refinement (HVA 4.2)
+
+def _refine_case(X0, X1, thw, cell, window, iters, frac, what):
+    """Anchor step on X0 (clustering and Lowe subset on the GPU), refinement
+    with X1 on the GPU against the oracle's refinement of the same state.
+    A subset token whose oracle margin over all centroids is below BAND is
+    exempt together with the centroids it touches."""
+    X0d, X1d = X0.to(DEV), X1.to(DEV)
+    a0, mu0, c0 = bsa.bsa_local_window_cluster(X0d, thw, cell, window, iters)
+    _, sub = bsa.bsa_lowe_ratio_subset(X0d, mu0, thw, cell, window, frac)
+    a1, mu1, c1 = bsa.bsa_subset_refine(X1d, sub, a0.clone(), mu0.clone(), c0.clone())
+    torch.cuda.synchronize()
+    B, H, N, _ = X0.shape
+    moved_tot = 0
+    for h in range(H):
+        x = X1[0, h].double().numpy()
+        a_in = a0[0, h].cpu().numpy()
+        mu_in = mu0[0, h].double().cpu().numpy()
+        S = sub[0, h].cpu().numpy()
+        a, mu, c = O.subset_refinement(x, a_in, mu_in, S)
+        ag, mug, cg = a1[0, h].cpu().numpy(), mu1[0, h].double().cpu().numpy(), c1[0, h].cpu().numpy()
+        # margins over every centroid for the subset tokens
+        d2 = ((x[S][:, None, :] - mu_in[None]) ** 2).sum(-1)
+        d2.sort(axis=1)
+        margin = d2[:, 1] - d2[:, 0] if d2.shape[1] > 1 else np.full(len(S), np.inf)
+        diff = np.nonzero(a != ag)[0]
+        assert np.all(np.isin(diff, S)), f"{what} h{h}: a token outside the subset changed"
+        sub_pos = {int(t): k for k, t in enumerate(S)}
+        assert all(margin[sub_pos[int(t)]] < BAND for t in diff), \
+            f"{what} h{h}: {len(diff)} refined assignments differ outside the tie band"
+        touched = set(a[diff].tolist()) | set(ag[diff].tolist()) | set(a_in[diff].tolist())
+        keep = np.array([u not in touched for u in range(len(c))])
+        np.testing.assert_array_equal(c[keep], cg[keep], err_msg=what)
+        np.testing.assert_allclose(mug[keep], mu[keep], atol=CENT_TOL, rtol=0, err_msg=what)
+        assert cg.sum() == N
+        moved = int((a[S] != a_in[S]).sum())
+        moved_tot += moved
+        say(f"   {what} h{h}: subset {len(S)}, moved {moved}, {len(diff)} near-tie differences")
+    return moved_tot
+
+
+REFINE_CASES = [
+    # (grid, H, d, key, cell, window, iters, perturbation)
+    ((3, 7, 9), 2, 128, 251, (1, 3, 3), (2, 2, 2), 2, 0.5),
+    ((4, 16, 16), 1, 64, 252, (2, 4, 4), (2, 3, 3), 3, 0.8),
+    ((2, 9, 50), 1, 128, 253, (1, 3, 7), (2, 3, 5), 2, 0.5),
+]
+
+
+@pytest.mark.parametrize("grid,H,d,key,cell,window,iters,pert", REFINE_CASES)
+def test_subset_refine_small(grid, H, d, key, cell, window, iters, pert):
+    spec = VideoSpec(1, H, d, grid, key)
+    Q, _, _ = gen_qkv(spec)
+    g = torch.Generator().manual_seed(key)
+    # a later denoising step: the same tokens, perturbed
+    Q1 = (Q.float() + pert * torch.randn(Q.shape, generator=g)).to(torch.bfloat16)
+    say("subset refine", grid, H, d)
+    moved = _refine_case(Q, Q1, grid, cell, window, iters, 0.15, f"{grid}")
+    assert moved > 0, "the perturbation should move some subset tokens"
+
+
+def test_subset_refine_empty_and_full_subsets():
+    spec = VideoSpec(1, 1, 64, (3, 8, 8), 254)
+    Q, _, _ = gen_qkv(spec)
+    Qd = Q.to(DEV)
+    thw, cell, window = (3, 8, 8), (1, 4, 4), (2, 2, 2)
+    a0, mu0, c0 = bsa.bsa_local_window_cluster(Qd, thw, cell, window, 2)
+    empty = torch.zeros((1, 1, 0), dtype=torch.int32, device=DEV)
+    a1, mu1, c1 = bsa.bsa_subset_refine(Qd, empty, a0.clone(), mu0.clone(), c0.clone())
+    torch.cuda.synchronize()
+    assert torch.equal(a1, a0) and torch.equal(mu1, mu0) and torch.equal(c1, c0)
+    # every token in the subset, centroids the members' means: one Lloyd step
+    full = torch.arange(spec.N, dtype=torch.int32, device=DEV).view(1, 1, -1)
+    Q1 = (Q.float() + 0.7 * torch.randn(Q.shape, generator=torch.Generator().manual_seed(3))).to(
+        torch.bfloat16)
+    _refine_case(Q, Q1, thw, cell, window, 2, 1.0, "full subset")
+
+
+def test_subset_refine_hunyuanvideo_key_grid():
+    """The 118,800-token HunyuanVideo lattice with the page's key grid (1215
+    cells), window (3, 8, 8), 2 iterations at the anchor step, the page's top
+    15% (17,820 tokens) refined against all 1215 centroids at a perturbed
+    later step."""
+    spec = config_spec(3)
+    _, K, _ = gen_qkv(spec, heads=[0])
+    K = K[:, :1]
+    K1 = (K.float() + 0.3 * torch.randn(K.shape, generator=torch.Generator().manual_seed(31))).to(
+        torch.bfloat16)
+    say("subset refine on the HunyuanVideo key grid")
+    _refine_case(K, K1, spec.grid, (11, 3, 3), (3, 8, 8), 2, 0.15, "hunyuanvideo")
