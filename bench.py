@@ -633,6 +633,30 @@ def main():
             # assignment work: one d-long dot product per (token, window centroid)
             flops += 2 * d * N * wv * B * H * CLUSTER_ITERS
             res[name] = {"cells": int(mu_.shape[2]), "cell": list(cell), "ms": round(ms, 4)}
+        # HVA section 4.2 on the keys' clustering: Lowe's ratio and its 15%
+        # subset, then one intermediate-step refinement of that subset (the
+        # subset reassigned against every centroid, the touched centroids
+        # re-averaged), each call timed alone from the same clustering
+        lowe_ms, _ = events_ms(lambda: bsa.bsa_lowe_ratio_subset(K, mu_, thw, ck, CLUSTER_WINDOW,
+                                                                 0.15), reps, stream)
+        _, sub = bsa.bsa_lowe_ratio_subset(K, mu_, thw, ck, CLUSTER_WINDOW, 0.15)
+        ev0 = torch.cuda.Event(enable_timing=True)
+        ev1 = torch.cuda.Event(enable_timing=True)
+        rt = []
+        moved = 0
+        for _ in range(reps):
+            a2, m2, c2 = a_.clone(), mu_.clone(), c_.clone()
+            ev0.record(stream)
+            bsa.bsa_subset_refine(K, sub, a2, m2, c2)
+            ev1.record(stream)
+            ev1.synchronize()
+            rt.append(ev0.elapsed_time(ev1))
+            moved = int((a2 != a_).sum())
+        rt.sort()
+        res["K_subset"] = {"n_sub_per_head": int(sub.shape[2]),
+                           "lowe_ratio_subset_ms": round(lowe_ms, 4),
+                           "subset_refine_ms": round(rt[len(rt) // 2], 4),
+                           "tokens_reassigned": moved}
         tot = res["Q"]["ms"] + res["K"]["ms"]
         # the assignment runs three bf16 matrix products per dot product (the
         # centroid's hi, mid and lo parts); rates over the whole call (updates

@@ -1164,8 +1164,11 @@ int64_t bsa_subset_refine_workspace_bytes(const bsa_shape* shape, int32_t cells)
     return -1;
   }
   const int64_t bh = (int64_t)shape->B * shape->H;
+  // touched bitmaps, member counts, member ranges, the scan total, the
+  // member list, the centroids' bf16 parts and their squared norms
   return align256(bh * cdiv(cells, 32) * 4) + align256(bh * cells * 4) +
-         align256(bh * cells * shape->d * 8);
+         align256((bh * cells + 1) * 4) + 256 + align256(bh * shape->N * 4) +
+         align256(bh * cells * 3 * shape->d * 2) + align256(bh * cells * 4);
 }
 
 bsa_status bsa_subset_refine(const uint16_t* X, const bsa_shape* shape, int32_t cells,
@@ -1177,6 +1180,9 @@ bsa_status bsa_subset_refine(const uint16_t* X, const bsa_shape* shape, int32_t 
   if (n_sub < 0 || n_sub > shape->N)
     return fail(BSA_ERR_INVALID_ARG, "n_sub=%d outside [0, N=%d]", n_sub, shape->N);
   if ((int64_t)shape->B * shape->H > 65535) return fail(BSA_ERR_UNSUPPORTED, "B*H exceeds 65535");
+  if ((int64_t)shape->B * shape->H * shape->N >= INT32_MAX ||
+      (int64_t)shape->B * shape->H * cells >= INT32_MAX)
+    return fail(BSA_ERR_UNSUPPORTED, "too many tokens or centroids for int32 member offsets");
   BSA_TRY(check_ptr(X, "X"));
   if (n_sub > 0) BSA_TRY(check_ptr(subset, "subset", 4));
   BSA_TRY(check_ptr(assign, "assign", 4));
@@ -1203,9 +1209,19 @@ bsa_status bsa_subset_refine(const uint16_t* X, const bsa_shape* shape, int32_t 
   a.assign = assign;
   a.mu = centroids;
   a.counts = counts;
-  a.touched = (uint32_t*)ws;
-  a.tcount = (int32_t*)(ws + align256(bh * a.W * 4));
-  a.sums = (double*)(ws + align256(bh * a.W * 4) + align256(bh * cells * 4));
+  int64_t off = 0;
+  auto take = [&](int64_t bytes) {
+    char* p = ws + off;
+    off += align256(bytes);
+    return p;
+  };
+  a.touched = (uint32_t*)take(bh * a.W * 4);
+  a.tcount = (int32_t*)take(bh * cells * 4);
+  a.offs = (int32_t*)take((bh * cells + 1) * 4);
+  a.total = (int64_t*)take(256);
+  a.list = (int32_t*)take(bh * shape->N * 4);
+  a.mu3 = (uint16_t*)take(bh * cells * 3 * shape->d * 2);
+  a.norm = (float*)take(bh * cells * 4);
   return hip_status(bsa::launch_subset_refine(a, (int)bh, shape->d, (hipStream_t)stream),
                     "subset refine launch");
 }

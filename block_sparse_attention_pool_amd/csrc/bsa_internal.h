@@ -255,8 +255,12 @@ struct RefineArgs {
   float* mu;                // [BH, Nc, D] in/out
   int32_t* counts;          // [BH, Nc] in/out
   uint32_t* touched;        // [BH, W] (workspace)
-  int32_t* tcount;          // [BH, Nc] (workspace)
-  double* sums;             // [BH, Nc, D] (workspace)
+  int32_t* tcount;          // [BH, Nc] members of touched centroids (workspace)
+  int32_t* offs;            // [BH * Nc + 1] their ranges in `list` (workspace)
+  int64_t* total;           // the scan's total (workspace)
+  int32_t* list;            // [BH * N] members of touched centroids (workspace)
+  uint16_t* mu3;            // [BH, Nc, 3, D] bf16 parts of the centroids (workspace)
+  float* norm;              // [BH, Nc] squared norms of the centroids (workspace)
 };
 
 hipError_t launch_subset_refine(const RefineArgs& a, int BH, int D, hipStream_t s);

@@ -1,7 +1,9 @@
 // Block pooling and pooled block scores (Rectified SpaAttn: pooled query-key
 // interactions; HyperVAttention section 2, Eq. 2 left, centroids = member
-// means).  Both are HBM/ALU bound; no matrix cores: the scores feed an exact
-// selection, so they stay in float32 end to end.
+// means).  Pooling is HBM bound and runs on the vector ALUs in float32.  The
+// scores feed an exact selection, so they are computed at float32 grade: the
+// product runs on the bf16 matrix cores with every float32 operand split into
+// three bf16 parts (score_gemm_kernel below).
 #include "bsa_device.h"
 #include "bsa_internal.h"
 

@@ -503,12 +503,15 @@ bsa_status bsa_local_window_cluster(const uint16_t* X, const bsa_shape* shape,
  *   or a previous refinement), updated in place; counts must be the member
  *   counts of `assign`.
  * workspace: >= bsa_subset_refine_workspace_bytes(shape, cells) bytes,
- *   256-byte aligned (touched-centroid bitmaps, member counts and float64
- *   member sums).
- * Precision: distances as float32 sums of (x - mu)^2 (near-ties within
- *   float32 rounding may resolve either way); member sums in float64 (exact
- *   for bf16 members within a 2^40 range of magnitudes, so repeated calls
- *   agree), means rounded to float32.
+ *   256-byte aligned (touched-centroid bitmaps, member counts and ranges, a
+ *   member list of up to B*H*N tokens, the centroids' bf16 parts and norms).
+ * Precision: distances as ||mu||^2 - 2 x.mu with float32-grade dot products
+ *   (each centroid split exactly into three bf16 parts on the matrix cores,
+ *   float32 sums; near-ties within that rounding may resolve either way);
+ *   member sums in float64, exact while one coordinate's nonzero magnitudes
+ *   over a centroid's n members lie within a factor 2^(45 - log2 n), so
+ *   repeated calls agree; means rounded to float32.
+ * Errors: BSA_ERR_UNSUPPORTED when B*H*N or B*H*cells reaches 2^31.
  * ---------------------------------------------------------------------- */
 int64_t bsa_subset_refine_workspace_bytes(const bsa_shape* shape, int32_t cells);
 
