@@ -866,7 +866,7 @@ bsa_status bsa_micro_residual_fwd(const uint16_t* Q, const uint16_t* K, const ui
   a.nT = (int)cdiv(shape->N, 16);
   a.slots = (int)((int64_t)shape->B * heads.n * nB * 4);
   a.bins = shape->B * heads.n * (a.nT + 1);
-  a.per_xcd = (int)cdiv(cdiv(a.slots, 4), 8);
+  a.per_xcd = (int)cdiv(cdiv(a.slots, bsa::kMicroWaves), 8);
   return hip_status(bsa::launch_micro_attn(a, shape->B, shape->d, o_dtype == BSA_BF16, st),
                     "micro attn launch");
 }

@@ -125,6 +125,15 @@ __device__ __forceinline__ void dma16(uint32_t m0base, const void* sbase, uint32
                : "memory", "m0", "scc");
 }
 
+// A pointer whose value is the same in every lane, moved to scalar registers.
+template <typename T>
+__device__ __forceinline__ const T* uniform_ptr(const T* p) {
+  const uint64_t v = (uint64_t)(uintptr_t)p;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return (const T*)(uintptr_t)(((uint64_t)hi << 32) | lo);
+}
+
 // Per-lane byte offsets of the tile copies of one wave (loop invariant).
 // K tile (64 x D bf16): instruction t covers rows t*RPI .. t*RPI+RPI-1; lane
 // l of it lands at LDS row t*RPI + l/DC, 16-byte position l%DC, so it fetches
@@ -625,12 +634,19 @@ void attn_fwd_kernel(AttnArgs a) {
 
 // ---------------------------------------------------------------- micro
 
-// One workgroup per (b, micro head, query block); wave a handles query
-// sub-tile a (16 rows) over its selected 16-key tiles.  16x16x32 products
-// for S^T = K Q^T (lane holds 4 keys of one query), 16x16x16 products for
-// O^T = V^T P^T (fp16) whose P^T operand is exactly those 4 accumulator
-// registers.  A tile's K rows (4 KB) and V^T chunk (4 KB) are contiguous;
-// the fragments of tile e+1 are loaded while tile e is computed.
+// One wave per 16-row query sub-tile over its selected 16-key tiles,
+// kMicroWaves sub-tiles per workgroup.  16x16x32 products for S^T = K Q^T
+// (lane holds 4 keys of one query), 16x16x16 products for O^T = V^T P^T
+// (fp16) whose P^T operand is exactly those 4 accumulator registers.  A
+// tile's K rows (4 KB) and V^T chunk (4 KB) are copied straight from global
+// memory into one of two LDS slots of the wave (no registers, no barrier:
+// each wave owns its slots), so the copies of tiles e+1 and e+2 are in
+// flight while tile e is read from its slot and computed.  The kernel waits
+// on memory latency: two slots of 8 KB per wave and 32 KB per workgroup
+// leave room for ten waves per compute unit (20 tiles in flight); against
+// one tile prefetched in registers (12 waves) that took the HunyuanVideo
+// micro heads from 5.63 to 4.40 ms, bit-identical, while three slots per
+// wave (6 waves) gave 5.12 ms and four (5 waves) 6.25 ms.
 //
 // Sub-tiles run in the order of `order`: sorted, per head, by the first key
 // tile each one selects, and dealt to the XCDs in contiguous ranges, so that
@@ -638,18 +654,18 @@ void attn_fwd_kernel(AttnArgs a) {
 // through its L2.  Each sub-tile is computed on its own, so the order changes
 // no result.
 template <int D, bool OUT_BF16>
-// Three waves per SIMD (152 VGPRs, no accumulation registers) keep more
-// tile gathers in flight than the two the compiler plans for by default:
-// 6.50 -> 5.58 ms on the HunyuanVideo micro heads.
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3)))
-void micro_attn_kernel(MicroAttnArgs a) {
+__global__ __launch_bounds__(64 * kMicroWaves) void micro_attn_kernel(MicroAttnArgs a) {
   constexpr int KS = D / 32;
   constexpr int DT = D / 16;
+  constexpr int DC = D / 8;             // 16-byte pieces per K row
+  constexpr int NI = D / 32;            // 1 KB copies per K tile (and per V^T chunk)
+  constexpr int SLOT = 2 * kMicro * D;  // uint16 elements of one slot: K rows, then V^T chunk
+  __shared__ __attribute__((aligned(1024))) uint16_t ring[kMicroWaves][2][SLOT];
   const int w = blockIdx.x;
   const int Lw = (w & 7) * a.per_xcd + (w >> 3);
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int slot = 4 * Lw + wave;
-  if (Lw >= (a.slots + 3) / 4 || slot >= a.slots) return;
+  const int slot = kMicroWaves * Lw + wave;
+  if (Lw >= (a.slots + kMicroWaves - 1) / kMicroWaves || slot >= a.slots) return;
   const int sid = a.order[slot];
   const int sub = sid & 3;
   const int i = (sid >> 2) % a.nB;
@@ -672,7 +688,8 @@ void micro_attn_kernel(MicroAttnArgs a) {
   }
   lt = wave_sum(lt);
   le = wave_sum(le);
-  const int es = rb + lt, ee = rb + le;
+  const int es = __builtin_amdgcn_readfirstlane(rb + lt);
+  const int ee = __builtin_amdgcn_readfirstlane(rb + le);
 
   const int64_t base = (int64_t)b * a.sb + (int64_t)h * a.sh;
   const uint16_t* Qh = a.Q + base;
@@ -692,40 +709,75 @@ void micro_attn_kernel(MicroAttnArgs a) {
   float m_run = -INFINITY, l_run = 0.f;
   const float c = a.scale_log2;
   const int vpos = 4 * (2 * (g4 & 1) + (g4 >> 1));  // position of keys 4*g4.. in the chunk
+  // The Q fragments must have arrived before the copies start: the loop's
+  // explicit waits count the copies only.
+  wait_vmcnt<0>();
 
-  struct Frags {
-    bf16x8 k[KS];
-    u32x2 v[DT];
-    int beta;
-    bool bad;  // the caller's tile index lay outside [0, nT): tile 0 read, masked out
-  };
+  // Tile copies straight into this wave's two LDS slots.  K: copy u, lane l
+  // fills LDS byte 1024 u + 16 l = row (that / 2D), 16-byte position p of
+  // the row, with global piece p ^ (row % DC) (rows XOR-swizzled, so the 16
+  // rows a fragment read touches fall on distinct banks); rows past N read
+  // row N-1 (their scores are masked).  V^T: the 16-key chunk is contiguous
+  // and lands as it is.
+  const int lastrow = a.N - 1 - (a.nT - 1) * kMicro;
+  uint32_t koff[NI], kroff[NI];
+#pragma unroll
+  for (int u = 0; u < NI; ++u) {
+    const int byte = 1024 * u + 16 * lane;
+    const int row = byte / (2 * D), pc = (byte % (2 * D)) / 16;
+    const int gp = pc ^ (row % DC);
+    koff[u] = (uint32_t)(((int64_t)row * a.sn + gp * 8) * 2);
+    kroff[u] = (uint32_t)(((int64_t)min(row, lastrow) * a.sn + gp * 8) * 2);
+  }
+  const uint32_t ring0 = __builtin_amdgcn_readfirstlane(lds_addr(&ring[wave][0][0]));
   const_i32* idx = (const_i32*)a.idx;
-  auto load = [&](int e, Frags& f) {
+  // tile index and validity of an entry: an index outside [0, nT) reads
+  // tile 0 and is masked out
+  auto tile_of = [&](int e, bool& bad) {
     const int raw = idx[e] >> 2;
-    f.bad = (unsigned)raw >= (unsigned)a.nT;
-    f.beta = f.bad ? 0 : raw;
-    const int key = f.beta * kMicro + n16;
-#pragma unroll
-    for (int s = 0; s < KS; ++s) {
-      u32x4 v = {0u, 0u, 0u, 0u};
-      if (key < a.N) v = *(const u32x4*)(Kh + (int64_t)key * a.sn + 32 * s + 8 * g4);
-      f.k[s] = __builtin_bit_cast(bf16x8, v);
-    }
-    // chunk beta of the head: [d][16] fp16, rows 16t + n16
-    const uint16_t* vc = Vth + (int64_t)f.beta * D * kMicro;
-#pragma unroll
-    for (int t = 0; t < DT; ++t) f.v[t] = *(const u32x2*)(vc + (16 * t + n16) * kMicro + vpos);
+    bad = (unsigned)raw >= (unsigned)a.nT;
+    return bad ? 0 : raw;
   };
-  auto compute = [&](const Frags& f) {
+  auto issue = [&](int e, int sl) {
+    bool bad;
+    const int beta = tile_of(e, bad);
+    const uint32_t kb = ring0 + sl * (SLOT * 2);
+    const uint32_t vb = kb + kMicro * D * 2;
+    // every lane holds the same sub-tile, so the tile's addresses are uniform
+    const uint16_t* ksrc = uniform_ptr(Kh + (int64_t)beta * kMicro * a.sn);
+    const uint16_t* vsrc = uniform_ptr(Vth + (int64_t)beta * D * kMicro);
+    const bool rag = beta == a.nT - 1;
+    static_for<0, NI>([&](auto uc) {
+      constexpr int u = decltype(uc)::value;
+      dma16<u * 1024>(kb, ksrc, rag ? kroff[u] : koff[u]);
+    });
+    static_for<0, NI>([&](auto uc) {
+      constexpr int u = decltype(uc)::value;
+      dma16<u * 1024>(vb, vsrc, (uint32_t)(1024 * u + 16 * lane));
+    });
+  };
+
+  auto compute = [&](int e, int sl) {
+    bool bad;
+    const int beta = tile_of(e, bad);
+    const uint16_t* ks = &ring[wave][sl][0];
+    const uint16_t* vs = ks + kMicro * D;
+    bf16x8 kf[KS];
+    u32x2 vf[DT];
+#pragma unroll
+    for (int s = 0; s < KS; ++s)
+      kf[s] = *(const bf16x8*)(ks + n16 * D + (((4 * s + g4) ^ (n16 % DC)) * 8));
+#pragma unroll
+    for (int t = 0; t < DT; ++t) vf[t] = *(const u32x2*)(vs + (16 * t + n16) * kMicro + vpos);
     f32x4 sacc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int s = 0; s < KS; ++s)
-      sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(f.k[s], qf[s], sacc, 0, 0, 0);
+      sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[s], qf[s], sacc, 0, 0, 0);
     // lane holds keys beta*16 + 4*g4 + rr of query q
 #pragma unroll
     for (int rr = 0; rr < 4; ++rr)
-      if (f.bad || f.beta * kMicro + 4 * g4 + rr >= a.N) sacc[rr] = -INFINITY;
-    if (f.bad && lane == 0) atomicOr(a.status, kStatusBadIndex);
+      if (bad || beta * kMicro + 4 * g4 + rr >= a.N) sacc[rr] = -INFINITY;
+    if (bad && lane == 0) atomicOr(a.status, kStatusBadIndex);
     float mx = fmaxf(fmaxf(sacc[0], sacc[1]), fmaxf(sacc[2], sacc[3]));
     mx = fmaxf(mx, __shfl_xor(mx, 16));
     mx = fmaxf(mx, __shfl_xor(mx, 32));
@@ -747,19 +799,24 @@ void micro_attn_kernel(MicroAttnArgs a) {
     const f16x4 pb = __builtin_bit_cast(f16x4, pk);
 #pragma unroll
     for (int t = 0; t < DT; ++t)
-      o[t] = __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4, f.v[t]), pb, o[t], 0, 0, 0);
+      o[t] = __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4, vf[t]), pb, o[t], 0, 0, 0);
   };
-  // two fragment sets, alternating
-  Frags fa, fb;
-  int e = es;
-  if (e < ee) load(e, fa);
-  for (; e + 1 < ee; e += 2) {
-    load(e + 1, fb);
-    compute(fa);
-    if (e + 2 < ee) load(e + 2, fa);
-    compute(fb);
+
+  // Two tiles in flight: tile e+1 and e+2 are being copied while tile e is
+  // computed.  A slot is refilled once this wave's reads of it returned.
+  if (es < ee) issue(es, 0);
+  if (es + 1 < ee) issue(es + 1, 1);
+  for (int e = es; e < ee; ++e) {
+    const int sl = (e - es) & 1;
+    if (e + 1 < ee) wait_vmcnt<2 * NI>();  // tile e has landed (e+1 may not)
+    else wait_vmcnt<0>();
+    asm volatile("" ::: "memory");         // the slot's reads stay behind the wait
+    compute(e, sl);
+    if (e + 2 < ee) {
+      wait_lgkm0();                        // this wave's reads of the slot returned
+      issue(e + 2, sl);
+    }
   }
-  if (e < ee) compute(fa);
 
   float l_tot = l_run + __shfl_xor(l_run, 16);
   l_tot += __shfl_xor(l_tot, 32);
@@ -915,11 +972,11 @@ hipError_t launch_micro_attn(const MicroAttnArgs& a, int B, int D, bool out_bf16
   hipLaunchKernelGGL(micro_scatter_kernel, sgrid, dim3(256), 0, s, a);
   dim3 grid(8 * a.per_xcd);
   if (D == 128) {
-    if (out_bf16) hipLaunchKernelGGL((micro_attn_kernel<128, true>), grid, dim3(256), 0, s, a);
-    else hipLaunchKernelGGL((micro_attn_kernel<128, false>), grid, dim3(256), 0, s, a);
+    if (out_bf16) hipLaunchKernelGGL((micro_attn_kernel<128, true>), grid, dim3(64 * kMicroWaves), 0, s, a);
+    else hipLaunchKernelGGL((micro_attn_kernel<128, false>), grid, dim3(64 * kMicroWaves), 0, s, a);
   } else {
-    if (out_bf16) hipLaunchKernelGGL((micro_attn_kernel<64, true>), grid, dim3(256), 0, s, a);
-    else hipLaunchKernelGGL((micro_attn_kernel<64, false>), grid, dim3(256), 0, s, a);
+    if (out_bf16) hipLaunchKernelGGL((micro_attn_kernel<64, true>), grid, dim3(64 * kMicroWaves), 0, s, a);
+    else hipLaunchKernelGGL((micro_attn_kernel<64, false>), grid, dim3(64 * kMicroWaves), 0, s, a);
   }
   return hipGetLastError();
 }

@@ -99,6 +99,9 @@ constexpr int32_t kStatusBadIndex = 1;
 constexpr int kChunkShift = 24;
 constexpr int32_t kChunkMask = (1 << kChunkShift) - 1;
 
+// waves (query sub-tiles) per workgroup of the micro residual
+constexpr int kMicroWaves = 2;
+
 struct MicroAttnArgs {
   const uint16_t* Q;
   const uint16_t* K;

@@ -510,10 +510,8 @@ def test_workload_lists_and_attention(workload):
 
 def test_workload_dense_sampled(workload):
     cfg, spec, (Q, K, V), (Qd, Kd, Vd) = workload
-    if cfg not in (0, 1):
-        pytest.skip("dense check on the tiny and the 32K workloads")
     B, H, N, d = Q.shape
-    say(f"workload {cfg}: dense attention")
+    say(f"workload {cfg}: dense attention (the speedup baseline) on sampled query blocks")
     Og, Lg = bsa.bsa_dense_attn_fwd(Qd, Kd, Vd)
     torch.cuda.synchronize()
     for h in sorted({0, H - 1}):
