@@ -1152,6 +1152,7 @@ bsa_status bsa_lowe_ratio_subset(const uint16_t* X, const bsa_shape* shape,
   a.ww = std::min(p->ww, a.Kw);
   a.mu = (float*)centroids;  // read only in this pass
   a.norm = (float*)workspace;
+  a.mu3 = (uint16_t*)((char*)workspace + align256((int64_t)shape->B * shape->H * cells * 4));
   a.rho = rho;
   return hip_status(bsa::launch_lowe(a, shape->B * shape->H, n_sub, subset, (hipStream_t)stream),
                     "lowe launch");

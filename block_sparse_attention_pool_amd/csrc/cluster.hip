@@ -306,7 +306,12 @@ __global__ __launch_bounds__(1024) void cluster_assign_mfma_kernel(ClusterArgs a
 // multiplied, so the chunk copies overlap the matrix work.  PER 16-byte
 // pieces per thread cover a chunk's three parts; the results are those of
 // cluster_assign_mfma_kernel bit for bit (same products in the same order).
-template <int D, int PER>
+// LOWE: Lowe's ratio (HVA Eq. 6) instead of the assignment: the two
+// smallest (||mu||^2 - 2 x.mu, index) pick the nearest and the nearest other
+// centroid, whose distances are then taken directly as sum (x - mu)^2 over
+// the float32 centroids (the short form cancels when a token sits on a
+// centroid); rho = sqrt(d_1 / d_2), 0 with a single candidate, 1 when d_2 is 0.
+template <int D, int PER, bool LOWE = false>
 __global__ __launch_bounds__(PER >= 4 ? 512 : 1024) void cluster_assign_pf_kernel(ClusterArgs a) {
   constexpr int DC = D / 8;          // 16-byte pieces per row
   constexpr int KS = D / 16;         // k-steps
@@ -377,8 +382,8 @@ __global__ __launch_bounds__(PER >= 4 ? 512 : 1024) void cluster_assign_pf_kerne
       for (int s2 = 0; s2 < KS; ++s2)
         xf[s2] = __builtin_bit_cast(bf16x8, *(const u32x4*)(xr + 16 * s2));
     }
-    float best = INFINITY;
-    int best_u = 0x7fffffff;
+    float best = INFINITY, second = INFINITY;
+    int best_u = 0x7fffffff, second_u = 0x7fffffff;
     __syncthreads();  // the previous token batch no longer reads the chunk buffer
     gload(0);
     lstore(0);
@@ -406,7 +411,19 @@ __global__ __launch_bounds__(PER >= 4 ? 512 : 1024) void cluster_assign_pf_kerne
             const int k = min(c0 + m, ncand - 1);
             const float dist = __builtin_fmaf(-2.f, acc[4 * j + q], tnorm[k]);
             const int id = tid_of[k];
-            if (c0 + m < ncand && (dist < best || (dist == best && id < best_u))) {
+            if constexpr (LOWE) {
+              if (c0 + m < ncand) {
+                if (dist < best || (dist == best && id < best_u)) {
+                  second = best;
+                  second_u = best_u;
+                  best = dist;
+                  best_u = id;
+                } else if (dist < second || (dist == second && id < second_u)) {
+                  second = dist;
+                  second_u = id;
+                }
+              }
+            } else if (c0 + m < ncand && (dist < best || (dist == best && id < best_u))) {
               best = dist;
               best_u = id;
             }
@@ -423,8 +440,62 @@ __global__ __launch_bounds__(PER >= 4 ? 512 : 1024) void cluster_assign_pf_kerne
     // the other 16 candidates of this token sit in lane n ^ 32
     const float ob = __shfl_xor(best, 32);
     const int ou = __shfl_xor(best_u, 32);
-    if (ob < best || (ob == best && ou < best_u)) best_u = ou;
-    if (g == 0 && p < ntok) a.assign[bh * a.N + tok] = best_u;
+    if constexpr (LOWE) {
+      const float os = __shfl_xor(second, 32);
+      const int osu = __shfl_xor(second_u, 32);
+      auto lt = [](float d1, int u1, float d2, int u2) { return d1 < d2 || (d1 == d2 && u1 < u2); };
+      // merge the lane pair's two ordered pairs
+      if (lt(ob, ou, best, best_u)) {
+        if (lt(best, best_u, os, osu)) {
+          second = best;
+          second_u = best_u;
+        } else {
+          second = os;
+          second_u = osu;
+        }
+        best = ob;
+        best_u = ou;
+      } else if (lt(ob, ou, second, second_u)) {
+        second = ob;
+        second_u = ou;
+      }
+      // direct squared distances over this lane's half of the row (elements
+      // 16 s + 8 g .. +7), the halves added across the lane pair
+      const bool two = (unsigned)second_u < (unsigned)a.Nc && (unsigned)best_u < (unsigned)a.Nc;
+      float d1 = 0.f, d2 = 0.f;
+      if (two) {
+        const float* m1 = a.mu + (bh * a.Nc + best_u) * D + 8 * g;
+        const float* m2 = a.mu + (bh * a.Nc + second_u) * D + 8 * g;
+#pragma unroll
+        for (int s2 = 0; s2 < KS; ++s2) {
+          const u32x4 xv = __builtin_bit_cast(u32x4, xf[s2]);
+#pragma unroll
+          for (int hq = 0; hq < 2; ++hq) {
+            const f32x4 p1 = *(const f32x4*)(m1 + 16 * s2 + 4 * hq);
+            const f32x4 p2 = *(const f32x4*)(m2 + 16 * s2 + 4 * hq);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const uint32_t w2 = xv[2 * hq + (e >> 1)];
+              const float xe = bf16_bits_to_f32((e & 1) ? (w2 >> 16) : (w2 & 0xFFFFu));
+              const float u1 = xe - p1[e], u2 = xe - p2[e];
+              d1 = __builtin_fmaf(u1, u1, d1);
+              d2 = __builtin_fmaf(u2, u2, d2);
+            }
+          }
+        }
+      }
+      d1 += __shfl_xor(d1, 32);
+      d2 += __shfl_xor(d2, 32);
+      float r = 0.f;
+      if (two) {
+        r = d2 > 0.f ? sqrtf(d1 / d2) : 1.f;
+        if (!(r > 0.f)) r = 0.f;  // +0: the subset search orders the bit patterns
+      }
+      if (g == 0 && p < ntok) a.rho[bh * a.N + tok] = r;
+    } else {
+      if (ob < best || (ob == best && ou < best_u)) best_u = ou;
+      if (g == 0 && p < ntok) a.assign[bh * a.N + tok] = best_u;
+    }
   }
 }
 
@@ -447,10 +518,10 @@ __global__ __launch_bounds__(D) void centroid_norm_kernel(ClusterArgs a) {
 }
 
 // The n_sub tokens of largest ratio per head (equal ratios to the lower
-// index), ascending: the threshold is found by a bitwise descent over the
-// ratios' bit patterns (order-preserving for values >= 0), then the tokens
-// above it and the first of those equal to it are compacted in token order.
-// One workgroup of 1024 per head.
+// index), ascending: the threshold is found by a radix selection, a byte at
+// a time, over the ratios' bit patterns (order-preserving for values >= 0),
+// then the tokens above it and the first of those equal to it are compacted
+// in token order.  One workgroup of 1024 per head.
 __global__ __launch_bounds__(1024) void lowe_subset_kernel(ClusterArgs a, int n_sub,
                                                            int32_t* subset) {
   __shared__ int red[16];
@@ -467,12 +538,48 @@ __global__ __launch_bounds__(1024) void lowe_subset_kernel(ClusterArgs a, int n_
     __syncthreads();
     return tot;
   };
-  uint32_t T = 0;
-  for (int bit = 31; bit >= 0 && n_sub > 0; --bit) {
-    const uint32_t cand = T | (1u << bit);
-    int c = 0;
-    for (int i = tid; i < a.N; i += 1024) c += __float_as_uint(r[i]) >= cand ? 1 : 0;
-    if (block_count(c) >= n_sub) T = cand;
+  // the n_sub-th largest bit pattern, one byte at a time (most significant
+  // first): a 256-bin histogram of the patterns that match the bytes found so
+  // far, and the bin where the count from the top reaches what remains
+  __shared__ uint32_t hist[256];
+  __shared__ int pick[2];
+  uint32_t T = 0, pmask = 0;
+  int remaining = n_sub;
+  for (int shift = 24; shift >= 0 && n_sub > 0; shift -= 8) {
+    if (tid < 256) hist[tid] = 0u;
+    __syncthreads();
+    for (int i = tid; i < a.N; i += 1024) {
+      const uint32_t k = __float_as_uint(r[i]);
+      if ((k & pmask) == T) atomicAdd(&hist[(k >> shift) & 255u], 1u);
+    }
+    __syncthreads();
+    if (wave == 0) {
+      const int b0 = 4 * lane;
+      const int hq[4] = {(int)hist[b0], (int)hist[b0 + 1], (int)hist[b0 + 2], (int)hist[b0 + 3]};
+      const int mine = hq[0] + hq[1] + hq[2] + hq[3];
+      int suf = mine;  // patterns in bins >= b0
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const int o = __shfl_down(suf, off);
+        if (lane + off < 64) suf += o;
+      }
+      int above = suf - mine;  // patterns in bins >= b0 + 4
+      if (above < remaining && suf >= remaining) {
+        for (int q = 3; q >= 0; --q) {
+          if (above + hq[q] >= remaining) {
+            pick[0] = b0 + q;
+            pick[1] = above;
+            break;
+          }
+          above += hq[q];
+        }
+      }
+    }
+    __syncthreads();
+    T |= (uint32_t)pick[0] << shift;
+    pmask |= 0xFFu << shift;
+    remaining -= pick[1];
+    __syncthreads();
   }
   int c = 0;
   for (int i = tid; i < a.N; i += 1024) c += __float_as_uint(r[i]) > T ? 1 : 0;
@@ -884,21 +991,6 @@ __global__ __launch_bounds__(256) void cluster_permute_kernel(ClusterArgs a,
 
 }  // namespace
 
-hipError_t launch_lowe(const ClusterArgs& a, int BH, int n_sub, int32_t* subset, hipStream_t s) {
-  const dim3 grid(a.Nc, BH);
-  const int ctok = a.kt * a.kh * a.kw;
-  const int threads = min(512, ((ctok + 63) / 64) * 64);
-  if (a.D == 128) {
-    hipLaunchKernelGGL(centroid_norm_kernel<128>, grid, dim3(128), 0, s, a);
-    hipLaunchKernelGGL((cluster_assign_kernel<128, true>), grid, dim3(threads), 0, s, a);
-  } else {
-    hipLaunchKernelGGL(centroid_norm_kernel<64>, grid, dim3(64), 0, s, a);
-    hipLaunchKernelGGL((cluster_assign_kernel<64, true>), grid, dim3(threads), 0, s, a);
-  }
-  hipLaunchKernelGGL(lowe_subset_kernel, dim3(BH), dim3(1024), 0, s, a, n_sub, subset);
-  return hipGetLastError();
-}
-
 hipError_t launch_cluster_permute(const ClusterArgs& a, int BH, const int32_t* gofs,
                                   int32_t* perm, int32_t* offsets, int32_t* big, hipStream_t s) {
   const dim3 grid(a.Nc, BH);
@@ -919,6 +1011,21 @@ hipError_t launch_cluster_permute(const ClusterArgs& a, int BH, const int32_t* g
 // The prefetching assignment for windows of at most kMaxAssignWindow cells
 // (4 to 16 waves, one per 32 tokens of a cell; four or more pieces per
 // thread only with at most 448 threads), else the plain one.
+template <int D, bool LOWE = false>
+void launch_assign_pf(const ClusterArgs& a, dim3 grid, int ctok, hipStream_t s) {
+  const int waves = min(16, (ctok + 31) / 32);
+  const int threads = 64 * max(4, waves);
+  const int per = (3 * 32 * (D / 8) + threads - 1) / threads;
+  switch (per) {
+    case 1: hipLaunchKernelGGL((cluster_assign_pf_kernel<D, 1, LOWE>), grid, dim3(threads), 0, s, a); break;
+    case 2: hipLaunchKernelGGL((cluster_assign_pf_kernel<D, 2, LOWE>), grid, dim3(threads), 0, s, a); break;
+    case 3: hipLaunchKernelGGL((cluster_assign_pf_kernel<D, 3, LOWE>), grid, dim3(threads), 0, s, a); break;
+    case 4: hipLaunchKernelGGL((cluster_assign_pf_kernel<D, 4, LOWE>), grid, dim3(threads), 0, s, a); break;
+    case 5: hipLaunchKernelGGL((cluster_assign_pf_kernel<D, 5, LOWE>), grid, dim3(threads), 0, s, a); break;
+    default: hipLaunchKernelGGL((cluster_assign_pf_kernel<D, 6, LOWE>), grid, dim3(threads), 0, s, a); break;
+  }
+}
+
 template <int D>
 void launch_assign(const ClusterArgs& a, dim3 grid, int ncand, int ctok, hipStream_t s) {
   const int waves = min(16, (ctok + 31) / 32);
@@ -926,16 +1033,35 @@ void launch_assign(const ClusterArgs& a, dim3 grid, int ncand, int ctok, hipStre
     hipLaunchKernelGGL(cluster_assign_mfma_kernel<D>, grid, dim3(64 * waves), 0, s, a);
     return;
   }
-  const int threads = 64 * max(4, waves);
-  const int per = (3 * 32 * (D / 8) + threads - 1) / threads;
-  switch (per) {
-    case 1: hipLaunchKernelGGL((cluster_assign_pf_kernel<D, 1>), grid, dim3(threads), 0, s, a); break;
-    case 2: hipLaunchKernelGGL((cluster_assign_pf_kernel<D, 2>), grid, dim3(threads), 0, s, a); break;
-    case 3: hipLaunchKernelGGL((cluster_assign_pf_kernel<D, 3>), grid, dim3(threads), 0, s, a); break;
-    case 4: hipLaunchKernelGGL((cluster_assign_pf_kernel<D, 4>), grid, dim3(threads), 0, s, a); break;
-    case 5: hipLaunchKernelGGL((cluster_assign_pf_kernel<D, 5>), grid, dim3(threads), 0, s, a); break;
-    default: hipLaunchKernelGGL((cluster_assign_pf_kernel<D, 6>), grid, dim3(threads), 0, s, a); break;
+  launch_assign_pf<D>(a, grid, ctok, s);
+}
+
+// Lowe's ratios on the matrix cores for windows of at most kMaxAssignWindow
+// cells (the centroids split into bf16 parts first), else with float32 FMAs.
+hipError_t launch_lowe(const ClusterArgs& a, int BH, int n_sub, int32_t* subset, hipStream_t s) {
+  const dim3 grid(a.Nc, BH);
+  const int ctok = a.kt * a.kh * a.kw;
+  const int threads = min(512, ((ctok + 63) / 64) * 64);
+  const bool mfma = a.wt * a.wh * a.ww <= kMaxAssignWindow;
+  if (a.D == 128) {
+    hipLaunchKernelGGL(centroid_norm_kernel<128>, grid, dim3(128), 0, s, a);
+    if (mfma) {
+      hipLaunchKernelGGL(centroid_split_kernel<128>, grid, dim3(128), 0, s, a);
+      launch_assign_pf<128, true>(a, grid, ctok, s);
+    } else {
+      hipLaunchKernelGGL((cluster_assign_kernel<128, true>), grid, dim3(threads), 0, s, a);
+    }
+  } else {
+    hipLaunchKernelGGL(centroid_norm_kernel<64>, grid, dim3(64), 0, s, a);
+    if (mfma) {
+      hipLaunchKernelGGL(centroid_split_kernel<64>, grid, dim3(64), 0, s, a);
+      launch_assign_pf<64, true>(a, grid, ctok, s);
+    } else {
+      hipLaunchKernelGGL((cluster_assign_kernel<64, true>), grid, dim3(threads), 0, s, a);
+    }
   }
+  hipLaunchKernelGGL(lowe_subset_kernel, dim3(BH), dim3(1024), 0, s, a, n_sub, subset);
+  return hipGetLastError();
 }
 
 hipError_t launch_cluster(const ClusterArgs& a, int BH, int iters, hipStream_t s) {

@@ -12,16 +12,21 @@
 //   refine_assign_kernel   32 subset tokens per wave, their bf16 rows the B
 //                          operand (in registers); the head's centroids
 //                          staged 32 at a time in LDS as their three parts
-//                          (16-byte pieces XOR-swizzled by row), S^T = mu x^T
+//                          (16-byte pieces XOR-swizzled by row; the next
+//                          chunk loaded into registers while the current
+//                          one is multiplied), S^T = mu x^T
 //                          on 32x32x16 bf16 products (exact products, float32
 //                          sums); distance ||mu||^2 - 2 S (||x||^2 is the
 //                          same for every candidate), lowest (distance,
 //                          index) wins; a token whose centroid changes marks
 //                          both centroids touched;
-//   refine_count_kernel    the members of touched centroids counted;
+//   refine_count_kernel    the members of touched centroids counted (one
+//                          atomic per group of a wave's lanes that share a
+//                          centroid);
 //   scan                   each touched centroid's range in a member list;
 //   refine_scatter_kernel  each such member's token index written into its
-//                          centroid's range (in no particular order);
+//                          centroid's range (in no particular order; again
+//                          one atomic per group);
 //   refine_mean_kernel     one workgroup per touched centroid: its members'
 //                          bf16 rows gathered (16 bytes per thread, four rows
 //                          in flight) and summed in float64, then the count
@@ -96,44 +101,77 @@ __global__ __launch_bounds__(64 * kRefineWaves) void refine_assign_kernel(Refine
   }
   const uint16_t* m3 = a.mu3 + bh * a.Nc * 3 * D;
   const float* nrm = a.norm + bh * a.Nc;
+  // one chunk's pieces, loaded into registers (from clamped, in-bounds
+  // centroids) while the previous chunk is multiplied, then stored to LDS
+  // with zeros past the last centroid
+  constexpr int NT = 64 * kRefineWaves;
+  constexpr int NPC = 3 * 32 * DC;             // 16-byte pieces per chunk
+  constexpr int PER = (NPC + NT - 1) / NT;
+  u32x4 stage[PER];
+  float nstage = 0.f;
+  auto gload = [&](int c0) {
+#pragma unroll
+    for (int q = 0; q < PER; ++q) {
+      const int f = min(tid + NT * q, NPC - 1);
+      const int part = f / (32 * DC), m = (f / DC) % 32, c = f % DC;
+      const int cu = min(c0 + m, a.Nc - 1);
+      stage[q] = *(const u32x4*)(m3 + ((int64_t)cu * 3 + part) * D + 8 * c);
+    }
+    if (tid < 32) nstage = nrm[min(c0 + tid, a.Nc - 1)];
+  };
+  auto lstore = [&](int c0) {
+#pragma unroll
+    for (int q = 0; q < PER; ++q) {
+      const int f = tid + NT * q;
+      if (f < NPC) {
+        const int part = f / (32 * DC), m = (f / DC) % 32, c = f % DC;
+        const u32x4 v = c0 + m < a.Nc ? stage[q] : u32x4{0u, 0u, 0u, 0u};
+        *(u32x4*)&cm[(part * 32 + m) * D + ((c ^ (m % DC)) * 8)] = v;
+      }
+    }
+    if (tid < 32) cn[tid] = c0 + tid < a.Nc ? nstage : 0.f;
+  };
   float best = INFINITY;
   int best_u = 0x7fffffff;
+  gload(0);
+  lstore(0);
+  __syncthreads();
   for (int c0 = 0; c0 < a.Nc; c0 += 32) {
     const int nc = min(32, a.Nc - c0);
-    __syncthreads();  // the previous chunk is no longer read
-    for (int f = tid; f < 3 * 32 * DC; f += 64 * kRefineWaves) {
-      const int part = f / (32 * DC), m = (f / DC) % 32, c = f % DC;
-      u32x4 v = {0u, 0u, 0u, 0u};
-      if (m < nc) v = *(const u32x4*)(m3 + ((int64_t)(c0 + m) * 3 + part) * D + 8 * c);
-      *(u32x4*)&cm[(part * 32 + m) * D + ((c ^ (m % DC)) * 8)] = v;
-    }
-    if (tid < 32) cn[tid] = tid < nc ? nrm[c0 + tid] : 0.f;
-    __syncthreads();
-    if (!active) continue;
-    f32x16 acc;
+    const bool more = c0 + 32 < a.Nc;
+    if (more) gload(c0 + 32);
+    if (active) {
+      f32x16 acc;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) acc[r] = 0.f;
+      for (int r = 0; r < 16; ++r) acc[r] = 0.f;
 #pragma unroll
-    for (int part = 0; part < 3; ++part)
+      for (int part = 0; part < 3; ++part)
 #pragma unroll
-      for (int s = 0; s < KS; ++s) {
-        const bf16x8 af = *(const bf16x8*)&cm[(part * 32 + n) * D + (((2 * s + g) ^ (n % DC)) * 8)];
-        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, xf[s], acc, 0, 0, 0);
-      }
-    // lane (n, g) holds candidates m = 8 j + 4 g + q of token n, visited in
-    // ascending order, so a strict improvement keeps the lower index
+        for (int s = 0; s < KS; ++s) {
+          const bf16x8 af =
+              *(const bf16x8*)&cm[(part * 32 + n) * D + (((2 * s + g) ^ (n % DC)) * 8)];
+          acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, xf[s], acc, 0, 0, 0);
+        }
+      // lane (n, g) holds candidates m = 8 j + 4 g + q of token n, visited in
+      // ascending order, so a strict improvement keeps the lower index
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const f32x4 nn = *(const f32x4*)&cn[8 * j + 4 * g];
+      for (int j = 0; j < 4; ++j) {
+        const f32x4 nn = *(const f32x4*)&cn[8 * j + 4 * g];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int m = 8 * j + 4 * g + q;
-        const float dist = __builtin_fmaf(-2.f, acc[4 * j + q], nn[q]);
-        if (m < nc && dist < best) {
-          best = dist;
-          best_u = c0 + m;
+        for (int q = 0; q < 4; ++q) {
+          const int m = 8 * j + 4 * g + q;
+          const float dist = __builtin_fmaf(-2.f, acc[4 * j + q], nn[q]);
+          if (m < nc && dist < best) {
+            best = dist;
+            best_u = c0 + m;
+          }
         }
       }
+    }
+    __syncthreads();  // every wave is done with this chunk
+    if (more) {
+      lstore(c0 + 32);
+      __syncthreads();
     }
   }
   if (!active) return;
@@ -155,26 +193,66 @@ __global__ __launch_bounds__(64 * kRefineWaves) void refine_assign_kernel(Refine
   }
 }
 
+// Lanes of a wave whose tokens belong to the same touched centroid are
+// served by one atomic (consecutive tokens mostly share a few centroids, so
+// per-lane atomics would queue on the same counters): the lowest pending
+// lane's centroid is taken each round, with every lane of that centroid.
+// f(key, n, rank, first) runs on the group's lanes: key = bh * Nc + c, n
+// lanes in the group, this lane's rank among them, first the group's lowest
+// lane.
+template <class F>
+__device__ __forceinline__ void per_centroid_group(bool pending, int key, F f) {
+  const int lane = threadIdx.x & 63;
+  const uint64_t below = (1ull << lane) - 1ull;
+  uint64_t pend = __ballot(pending);
+  while (pend) {
+    const int first = __ffsll((unsigned long long)pend) - 1;
+    const int k0 = __shfl(key, first);
+    const bool mine = pending && key == k0;
+    const uint64_t same = __ballot(mine);
+    if (mine) f(k0, __popcll(same), __popcll(same & below), first);
+    pending = pending && !mine;
+    pend &= ~same;
+  }
+}
+
 // One thread per (head, token).
 __global__ __launch_bounds__(256) void refine_count_kernel(RefineArgs a, int64_t total) {
   const int64_t f = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (f >= total) return;
-  const int64_t bh = f / a.N;
-  const int c = a.assign[f];
-  if ((unsigned)c >= (unsigned)a.Nc || !is_touched(a, bh, c)) return;
-  atomicAdd(&a.tcount[bh * a.Nc + c], 1);
+  bool pending = false;
+  int key = 0;
+  if (f < total) {
+    const int64_t bh = f / a.N;
+    const int c = a.assign[f];
+    pending = (unsigned)c < (unsigned)a.Nc && is_touched(a, bh, c);
+    key = (int)(bh * a.Nc + c);
+  }
+  const int lane = threadIdx.x & 63;
+  per_centroid_group(pending, key, [&](int k, int n, int, int first) {
+    if (lane == first) atomicAdd(&a.tcount[k], n);
+  });
 }
 
-// One thread per (head, token); consumes the counts.
+// One thread per (head, token); consumes the counts: each group takes the
+// top n free places of its centroid's range.
 __global__ __launch_bounds__(256) void refine_scatter_kernel(RefineArgs a, int64_t total) {
   const int64_t f = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (f >= total) return;
-  const int64_t bh = f / a.N;
-  const int c = a.assign[f];
-  if ((unsigned)c >= (unsigned)a.Nc || !is_touched(a, bh, c)) return;
-  const int64_t bc = bh * a.Nc + c;
-  const int pos = atomicSub(&a.tcount[bc], 1) - 1;
-  a.list[a.offs[bc] + pos] = (int32_t)(f - bh * a.N);
+  bool pending = false;
+  int key = 0;
+  int64_t bh = 0;
+  if (f < total) {
+    bh = f / a.N;
+    const int c = a.assign[f];
+    pending = (unsigned)c < (unsigned)a.Nc && is_touched(a, bh, c);
+    key = (int)(bh * a.Nc + c);
+  }
+  const int lane = threadIdx.x & 63;
+  per_centroid_group(pending, key, [&](int k, int n, int rank, int first) {
+    int top = 0;
+    if (lane == first) top = atomicSub(&a.tcount[k], n);
+    top = __shfl(top, first);  // the group's lanes are active: first holds the count
+    a.list[a.offs[k] + top - 1 - rank] = (int32_t)(f - bh * a.N);
+  });
 }
 
 // One workgroup per (centroid, head).
