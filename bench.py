@@ -162,13 +162,17 @@ def cpu_oracle_sample(Q, K, V, rows_by_head, budget_s):
 
 def traffic_entry(kernel_src):
     """HBM bytes per launch of the attention kernel from the committed
-    rocprofv3 counter summary, or None when the kernel changed since."""
+    rocprofv3 counter summary, or None when the kernel's sources (the files
+    in ``kernel_src``, hashed in order) changed since."""
     path = os.path.join(ROOT, "profiles", "attn_fwd_traffic.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
         rec = json.load(f)
-    sha = hashlib.sha256(open(kernel_src, "rb").read()).hexdigest()
+    h = hashlib.sha256()
+    for f in kernel_src:
+        h.update(open(f, "rb").read())
+    sha = h.hexdigest()
     if rec.get("kernel_src_sha256") != sha:
         return None
     return rec.get("hbm_bytes_per_launch")
@@ -751,7 +755,8 @@ def main():
                    "speedup_pipeline_vs_dense": round(dense_ms / total, 3)}
 
     attn_tflops = macro_flops / (attn_ms * 1e-3) / 1e12
-    kernel_src = os.path.join(ROOT, "block_sparse_attention_pool_amd", "csrc", "attn.hip")
+    csrc = os.path.join(ROOT, "block_sparse_attention_pool_amd", "csrc")
+    kernel_src = [os.path.join(csrc, "attn.hip"), os.path.join(csrc, "attn_util.h")]
     # the committed counters were taken on the default workload and selection
     traffic = (traffic_entry(kernel_src)
                if (cfg == 1 and blk == 64 and not args.mod_mask and not args.rectify) else None)
