@@ -22,8 +22,9 @@ namespace bsa {
 // one tile prefetched in registers (12 waves) that took the HunyuanVideo
 // micro heads from 5.63 to 4.40 ms, bit-identical, while three slots per
 // wave (6 waves) gave 5.12 ms and four (5 waves) 6.25 ms.  The V^T rows are
-// placed in the slot so that the fragment reads meet no bank conflicts
-// (4.33 -> 4.15-4.28 ms).
+// placed in the slot so that rows r and r + 8 of a fragment read fall on
+// different banks (bank conflicts 7.4e8 -> 2.5e8 cycles per launch, 4.33 ->
+// 4.15-4.28 ms).
 //
 // Sub-tiles run in the order of `order`: sorted, per head, by the first key
 // tile each one selects, and dealt to the XCDs in contiguous ranges, so that

@@ -551,6 +551,17 @@ def test_cluster_window_beyond_the_assignment_table():
     np.testing.assert_array_equal(off[0, 0].cpu().numpy(), offo)
 
 
+def test_lowe_ratio_window_beyond_the_assignment_table():
+    """Lowe's ratios over a window of 1,056 cells: the float32-FMA ratio pass
+    runs instead of the matrix-core one; ratios and subset against the
+    oracle."""
+    grid, cell, window = (1, 66, 64), (1, 2, 2), (1, 33, 32)
+    spec = VideoSpec(1, 1, 64, grid, 194)
+    Q, _, _ = gen_qkv(spec)
+    say("lowe, window of 1056 cells")
+    _lowe_case(Q, grid, cell, window, 2, 0.15)
+
+
 def test_cluster_permutation_of_a_cluster_beyond_lds():
     """Identical tokens: every distance ties and each token takes the lowest
     index of its window, so centroid 0 collects all 4,096 tokens of the 2 x 2
