@@ -82,9 +82,38 @@ __device__ T block_exclusive_scan(T v, T* red, T* total) {
 //     block indices, so ties go to the lower index.
 // The forced blocks (diagonal, window, anchors) are a union on top.  The
 // ballot of element e is words 2e and 2e+1 of the row's bitmask.
+
+// Sum over the wave, left in every lane, without LDS round trips: the two
+// halves of the double move through DPP (partner lane l^1, l^2, then the
+// mirrored lane within 8 and within 16) and the permlane swaps (rows l^16,
+// l^32).  Every step adds the same two values in both partner lanes, so all
+// lanes end with the same bits.
+template <int CTRL>
+__device__ __forceinline__ double dpp_f64(double v) {
+  const uint64_t u = __double_as_longlong(v);
+  const uint32_t lo = __builtin_amdgcn_mov_dpp((int)(uint32_t)u, CTRL, 0xF, 0xF, false);
+  const uint32_t hi = __builtin_amdgcn_mov_dpp((int)(uint32_t)(u >> 32), CTRL, 0xF, 0xF, false);
+  return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
+}
 __device__ __forceinline__ double wave_sum_f64(double v) {
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off);
+  v += dpp_f64<0xB1>(v);   // quad_perm(1, 0, 3, 2): lane l ^ 1
+  v += dpp_f64<0x4E>(v);   // quad_perm(2, 3, 0, 1): lane l ^ 2
+  v += dpp_f64<0x141>(v);  // row_half_mirror: the other quad of the 8
+  v += dpp_f64<0x140>(v);  // row_mirror: the other 8 of the row
+  {
+    const uint64_t u = __double_as_longlong(v);
+    const auto lo = __builtin_amdgcn_permlane16_swap((uint32_t)u, (uint32_t)u, false, false);
+    const auto hi = __builtin_amdgcn_permlane16_swap((uint32_t)(u >> 32), (uint32_t)(u >> 32), false, false);
+    v = __longlong_as_double((long long)(((uint64_t)hi[0] << 32) | lo[0])) +
+        __longlong_as_double((long long)(((uint64_t)hi[1] << 32) | lo[1]));
+  }
+  {
+    const uint64_t u = __double_as_longlong(v);
+    const auto lo = __builtin_amdgcn_permlane32_swap((uint32_t)u, (uint32_t)u, false, false);
+    const auto hi = __builtin_amdgcn_permlane32_swap((uint32_t)(u >> 32), (uint32_t)(u >> 32), false, false);
+    v = __longlong_as_double((long long)(((uint64_t)hi[0] << 32) | lo[0])) +
+        __longlong_as_double((long long)(((uint64_t)hi[1] << 32) | lo[1]));
+  }
   return v;
 }
 
