@@ -20,6 +20,7 @@
 // of the top-m candidate scores with ties to the lower code, emitted in
 // (sub-tile, key tile) order.
 #include <climits>
+#include <type_traits>
 
 #include "bsa_device.h"
 #include "bsa_internal.h"
@@ -550,15 +551,19 @@ __device__ uint32_t block_radix_select(int& remaining, Each each, uint32_t* hist
   return prefix;
 }
 
-// The row's candidates are read once into registers, E per thread
-// (candidate c = e * 1024 + thread, c = a * nT + beta); key 0 marks a
-// candidate inside a selected macro block (valid keys are made >= 1).  The
-// m-th largest key T is found by radix selection over the registers; of
-// the keys equal to T the lowest codes 4 beta + a are taken.
-// Registers are capped at 8 waves per SIMD so that two 1024-thread
-// workgroups share a compute unit and one's score loads overlap the other's
-// selection (a few spills, in the tie pass, cost less than the lost overlap:
-// 3.56 -> 2.97 ms for the micro selection of the HunyuanVideo layer).
+// One workgroup per query block.  The row's scores are read once, E per
+// thread (candidate c = e * 1024 + thread, c = a * nT + beta): the first
+// E - KL into registers, the last KL into LDS, since 64 registers per lane
+// (two 1024-thread workgroups per compute unit, so that one's score loads
+// overlap the other's selection) do not hold all E with the pass state
+// without spills.  A bitmask per thread marks the candidates (inside the
+// row, outside the blocks the macro selection kept).  The m best by (score
+// descending, code 4 beta + a ascending) are found from a histogram of the
+// scores; a radix selection over the order-preserving keys is the fallback.
+// Each pass walks the codes again from an opaque start (otherwise the
+// compiler keeps all E codes live from the first pass and spills).  On the
+// HunyuanVideo micro heads this took the micro-selection stage from 2.02 to
+// 1.70 ms (identical lists) against keeping every score in registers.
 template <int E>
 __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(E <= 32 ? 8 : 1)))
 void micro_select_kernel(MicroSelectArgs a) {
@@ -572,7 +577,7 @@ void micro_select_kernel(MicroSelectArgs a) {
   __shared__ uint32_t list_n;
   __shared__ uint32_t list_key[kMicroList];
   __shared__ uint32_t list_code[kMicroList];
-  __shared__ uint32_t sh_tc[2];
+  __shared__ uint32_t won[E * 32];  // bit c: candidate c won its place in the threshold bin
 
   const int i = blockIdx.x;
   const int z = blockIdx.y;
@@ -599,60 +604,80 @@ void micro_select_kernel(MicroSelectArgs a) {
   // codes 4 beta + a of the thread's candidates, walked in element order
   // (c grows by 1024 per element: beta and a advance without a division)
   const int beta0 = tid % nT, a0 = tid / nT;
-  auto for_codes = [&](auto f) {
-    int beta = beta0, sub = a0;
-#pragma unroll
-    for (int e = 0; e < E; ++e) {
-      f(e, beta, 4u * (uint32_t)beta + (uint32_t)sub);
-      beta += 1024;
+  auto advance = [&](int& beta, int& sub) {
+    beta += 1024;
+    if constexpr (E > 8) {  // rows of more than 8192 candidates: nT > 2048
+      if (beta >= nT) {
+        beta -= nT;
+        ++sub;
+      }
+    } else {
       while (beta >= nT) {
         beta -= nT;
         ++sub;
       }
     }
   };
-  // every score load issued before any is used (in-bounds addresses, so the
-  // loads need no branch and all of them are in flight at once)
-  float sv[E];
-#pragma unroll
-  for (int e = 0; e < E; ++e) sv[e] = sig[min(e * 1024 + tid, ncand - 1)];
-  uint32_t key[E];
-  int nvalid = 0;
-  for_codes([&](int e, int beta, uint32_t) {
-    const int c = e * 1024 + tid;
-    key[e] = 0u;
-    if (c < ncand) {
-      const int blk = beta >> 2;
-      if (((omask[blk >> 5] >> (blk & 31)) & 1u) == 0u) key[e] = max(1u, float_order_key(sv[e]));
-    }
-    nvalid += key[e] != 0u;
-  });
-  nvalid = block_sum(nvalid, ired);
-
-  const int m = a.m;
-  uint32_t T = 0u, C = 0xFFFFFFFFu;  // threshold key; largest code taken at T
-  const bool all = nvalid <= m;
-  // The m-th best candidate by (score descending, code ascending) is (T, C).
-  // Fast path: a histogram of the scores over kMicroBins equal-width bins
-  // between the row's smallest and largest score (a monotone map, so every
-  // candidate of a higher bin beats every candidate of a lower one; equal
-  // scores share a bin) finds the bin holding the m-th best; its few
-  // candidates are ranked exactly in LDS.  Bins by value, not by the top bits
-  // of the key: scores of one row share their sign and exponent, so bit bins
-  // would put most candidates on a handful of LDS counters.  When that bin
-  // holds more than kMicroList candidates (many equal scores) the radix
-  // selection over the keys runs instead.
-  bool exact_done = all;
-  if (!all) {
-    float vmin = INFINITY, vmax = -INFINITY;
+  auto for_codes = [&](auto f) {
+    int beta = beta0, sub = a0;
+    // opaque to the compiler, so that each pass walks the codes again
+    // instead of keeping every element's code live from the first pass
+    asm volatile("" : "+v"(beta), "+v"(sub));
 #pragma unroll
     for (int e = 0; e < E; ++e) {
-      if (key[e] != 0u) {
-        const float v = key_to_float(key[e]);
-        vmin = fminf(vmin, v);
-        vmax = fmaxf(vmax, v);
-      }
+      f(e, beta, 4u * (uint32_t)beta + (uint32_t)sub);
+      advance(beta, sub);
     }
+  };
+  // elements e < ne of this thread lie inside the row (a count, so that the
+  // test needs no per-element candidate index kept live)
+  const int ne = ncand > tid ? (ncand - tid + 1023) >> 10 : 0;
+  // Every score load is issued before any is used (in-bounds addresses, so
+  // the loads need no branch and all of them are in flight at once).  With
+  // 64 registers per lane (E = 32) the last KL = 12 elements go to LDS
+  // (48 KB; 73 KB per workgroup in all, two per compute unit); each thread
+  // reads back only its own, so they need no barrier.
+  constexpr int KL = E == 32 ? 12 : 0;
+  constexpr int ER = E - KL;
+  __shared__ float sl[KL > 0 ? KL * 1024 : 1];
+  float sv[ER];
+#pragma unroll
+  for (int e = 0; e < ER; ++e) sv[e] = sig[min(e * 1024 + tid, ncand - 1)];
+#pragma unroll
+  for (int e = ER; e < E; ++e) sl[(e - ER) * 1024 + tid] = sig[min(e * 1024 + tid, ncand - 1)];
+  auto val = [&](int e) { return e < ER ? sv[e] : sl[(e - ER) * 1024 + tid]; };
+  // bit e: element e is a candidate (inside the row, outside every block the
+  // macro selection kept); the row's score range over the candidates
+  using Mask = std::conditional_t<(E > 32), uint64_t, uint32_t>;
+  Mask valid = 0u;
+  float vmin = INFINITY, vmax = -INFINITY;
+  for_codes([&](int e, int beta, uint32_t) {
+    const int blk = beta >> 2;
+    if (e < ne && ((omask[blk >> 5] >> (blk & 31)) & 1u) == 0u) {
+      valid |= Mask(1) << e;
+      vmin = fminf(vmin, val(e));
+      vmax = fmaxf(vmax, val(e));
+    }
+  });
+  const int nvalid = block_sum((int)__popcll((uint64_t)valid), ired);
+  auto is_valid = [&](int e) { return ((valid >> e) & 1u) != 0u; };
+  auto key_of = [&](int e) { return is_valid(e) ? max(1u, float_order_key(val(e))) : 0u; };
+
+  const int m = a.m;
+  Mask chosen = valid;  // bit e: element e is selected
+  bool done = nvalid <= m;  // every candidate fits
+  // The m best candidates by (score descending, code ascending).  Fast
+  // path: a histogram of the scores over kMicroBins equal-width bins between
+  // the row's smallest and largest candidate score (a monotone map, so every
+  // candidate of a higher bin beats every candidate of a lower one; equal
+  // scores share a bin) finds the bin holding the m-th best; the bins above
+  // it are taken whole and its own few candidates are ranked exactly in LDS.
+  // Bins by value, not by the top bits of the key: scores of one row share
+  // their sign and exponent, so bit bins would put most candidates on a
+  // handful of LDS counters.  When that bin holds more than kMicroList
+  // candidates (many equal scores) a radix selection over the keys runs
+  // instead.
+  if (!done) {
     vmin = wave_min(vmin);
     vmax = wave_max(vmax);
     if (lane == 0) {
@@ -660,6 +685,7 @@ void micro_select_kernel(MicroSelectArgs a) {
       fred[16 + wave] = vmax;
     }
     for (int q = tid; q < kMicroBins; q += 1024) hist2[q] = 0u;
+    for (int q = tid; q < E * 32; q += 1024) won[q] = 0u;
     if (tid == 0) list_n = 0;
     __syncthreads();
     vmin = INFINITY;
@@ -670,12 +696,10 @@ void micro_select_kernel(MicroSelectArgs a) {
     }
     if (vmax > vmin) {
       const float sc = (float)kMicroBins / (vmax - vmin);
-      auto bin_of = [&](uint32_t k) {
-        return min(kMicroBins - 1, (int)((key_to_float(k) - vmin) * sc));
-      };
+      auto bin_of = [&](float v) { return min(kMicroBins - 1, (int)((v - vmin) * sc)); };
 #pragma unroll
       for (int e = 0; e < E; ++e)
-        if (key[e] != 0u) atomicAdd(&hist2[bin_of(key[e])], 1u);
+        if (is_valid(e)) atomicAdd(&hist2[bin_of(val(e))], 1u);
       __syncthreads();
       // bins 2t, 2t+1 per thread; candidates in the bins above them
       const int b0 = 2 * tid;
@@ -695,14 +719,21 @@ void micro_select_kernel(MicroSelectArgs a) {
       const int need = m - sh_out[1];
       const int cstar = (int)hist2[bstar];
       if (cstar <= kMicroList) {
+        Mask upper = 0u, inb = 0u;  // elements above the bin, in the bin
         for_codes([&](int e, int, uint32_t code) {
-          if (key[e] != 0u && bin_of(key[e]) == bstar) {
-            const int pos = (int)atomicAdd(&list_n, 1u);
-            list_key[pos] = key[e];
-            list_code[pos] = code;
+          if (is_valid(e)) {
+            const int bn = bin_of(val(e));
+            upper |= Mask(bn > bstar) << e;
+            inb |= Mask(bn == bstar) << e;
+            if (bn == bstar) {
+              const int pos = (int)atomicAdd(&list_n, 1u);
+              list_key[pos] = max(1u, float_order_key(val(e)));
+              list_code[pos] = code;
+            }
           }
         });
         __syncthreads();
+        // the need best of the threshold bin by (key descending, code ascending)
         for (int t = tid; t < cstar; t += 1024) {
           const uint32_t kt = list_key[t], ct = list_code[t];
           int rank = 0;
@@ -710,21 +741,29 @@ void micro_select_kernel(MicroSelectArgs a) {
             const uint32_t ku = list_key[u2];
             rank += ku > kt || (ku == kt && list_code[u2] < ct);
           }
-          if (rank == need - 1) {
-            sh_tc[0] = kt;
-            sh_tc[1] = ct;
+          if (rank < need) {
+            const int cw = (int)(ct & 3u) * nT + (int)(ct >> 2);
+            atomicOr(&won[cw >> 5], 1u << (cw & 31));
           }
         }
         __syncthreads();
-        T = sh_tc[0];
-        C = sh_tc[1];
-        exact_done = true;
+        for (Mask rest = inb; rest != 0u; rest &= rest - 1u) {
+          const int e = (int)__builtin_ctzll((uint64_t)rest);
+          const int cw = e * 1024 + tid;
+          upper |= Mask((won[cw >> 5] >> (cw & 31)) & 1u) << e;
+        }
+        chosen = upper;
+        done = true;
       }
     }
   }
-  if (!exact_done) {
+  if (!done) {
+    // the order-preserving keys of the candidates, 0 for the rest
+    uint32_t key[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e) key[e] = key_of(e);
     int remaining = m;
-    T = block_radix_select(remaining, [&](auto f) {
+    const uint32_t T = block_radix_select(remaining, [&](auto f) {
 #pragma unroll
       for (int e = 0; e < E; ++e)
         if (key[e] != 0u) f(key[e]);
@@ -733,6 +772,7 @@ void micro_select_kernel(MicroSelectArgs a) {
 #pragma unroll
     for (int e = 0; e < E; ++e) n_eq += key[e] == T;
     n_eq = block_sum(n_eq, ired);
+    uint32_t C = 0xFFFFFFFFu;  // largest code taken at T
     if (remaining < n_eq) {
       // ties at the threshold: the lowest codes win (largest ~code)
       int rem2 = remaining;
@@ -742,17 +782,20 @@ void micro_select_kernel(MicroSelectArgs a) {
         });
       }, hist, sh_out);
     }
+    chosen = 0u;
+    for_codes([&](int e, int, uint32_t code) {
+      chosen |= Mask(key[e] != 0u && (key[e] > T || (key[e] == T && code <= C))) << e;
+    });
   }
 
   // Compaction in candidate order (sub-tile a major, key tile beta minor):
   // candidate e * 1024 + 64 w + lane comes after every candidate of
   // element e' < e and of wave w' < w at element e.
-  bool sel[E];
-  for_codes([&](int e, int, uint32_t code) {
-    sel[e] = key[e] != 0u && (all || key[e] > T || (key[e] == T && code <= C));
-    const int cnt = __popcll(__ballot(sel[e]));
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const int cnt = __popcll(__ballot((chosen >> e) & 1u));
     if (lane == 0) wcnt[wave][e] = cnt;
-  });
+  }
   __syncthreads();
   // lane e: exclusive offset of (element e, this wave) and the row total
   int before_w = 0, tot_e = 0;
@@ -769,9 +812,10 @@ void micro_select_kernel(MicroSelectArgs a) {
   const uint64_t below = (1ull << lane) - 1ull;
   int32_t* out = a.slots + r * (int64_t)m;
   for_codes([&](int e, int, uint32_t code) {
-    const uint64_t bal = __ballot(sel[e]);
+    const bool sel = (chosen >> e) & 1u;
+    const uint64_t bal = __ballot(sel);
     const int pos = __shfl(off_e, e) + __popcll(bal & below);
-    if (sel[e] && pos < m) out[pos] = (int32_t)code;
+    if (sel && pos < m) out[pos] = (int32_t)code;
   });
   if (tid == 0) a.counts[r] = min(total, m);
 }

@@ -312,12 +312,14 @@ def _micro_oracle(Q, K, spec, rows, m, heads):
     return out
 
 
-def compare_micro_rows(got_rows, ora_rows, Qt, Kt, macro_rows, N, scale, m):
+def compare_micro_rows(got_rows, ora_rows, Qt, Kt, macro_rows, N, scale, m, blocks=None):
+    """Rows given in query-block order, or for the query blocks ``blocks``."""
     exempt = 0
     for i, (g, o) in enumerate(zip(got_rows, ora_rows)):
         if g == o:
             continue
-        cand = O.micro_candidates(Qt, Kt, macro_rows[i], i, N, 64, 16, scale)
+        blk = i if blocks is None else blocks[i]
+        cand = O.micro_candidates(Qt, Kt, macro_rows[i], blk, N, 64, 16, scale)
         cand.sort(key=lambda t: (-t[0], t[1]))
         thr = cand[min(m, len(cand)) - 1][0]
         sig = {c: s for s, c in cand}
@@ -384,6 +386,39 @@ def test_micro_select_attention_and_merge(grid, H, d, key, m):
     torch.cuda.synchronize()
     for h in heads:
         PT.compare_o_lse(Ob[0, h], Lb[0, h], refs[h][0], refs[h][1], f"merged h{h}")
+
+
+def test_micro_select_rows_of_more_than_32768_candidates():
+    """Query blocks over more than 8192 16-token key tiles (the selection
+    kernel that holds 64 candidates per thread), ragged in both tile sizes:
+    sampled rows, the first and the last, against the oracle."""
+    spec = VideoSpec(1, 1, 64, (7, 73, 258), 114, spikes=True)
+    say("micro long rows", spec.grid)
+    Q, K, _ = gen_qkv(spec)
+    Qd, Kd = to_dev(Q, K)
+    N = spec.N
+    nB, nT = O.n_blocks(N, 64), O.n_blocks(N, 16)
+    assert 4 * nT > 32768 and N % 64 and N % 16
+    scale = 1 / math.sqrt(spec.d)
+    m = 300
+    rows = oracle_rows_all(Q, K, spec, "topk", k=bsa.budget_blocks(0.1, nB))[(0, 0)][1]
+    rp, ci = PT.rows_to_csr(rows)
+    sc = bsa.bsa_score_blocks(Qd, Kd, scores=False, micro=16)
+    mrp, mci, mnnz = bsa.bsa_select_blocks(
+        None, Qd, mode="micro",
+        micro=dict(m=m, scale=scale, head_mask=[True], macro=(rp.to(DEV), ci.to(DEV)),
+                   qpool16=sc["qpool16"], kpool16=sc["kpool16"]))
+    torch.cuda.synchronize()
+    got = gpu_rows_by_head(mrp, mci, mnnz, 1, 1, nB)[(0, 0)]
+    q, k = PT.head64(Q, 0, 0), PT.head64(K, 0, 0)
+    Qt, Kt = O.pool_means(q, 16), O.pool_means(k, 16)
+    rng = np.random.default_rng(114)
+    blocks = sorted(set(rng.choice(nB, size=24, replace=False).tolist()) | {0, nB - 1})
+    ora = [O.micro_select_row(Qt, Kt, rows[i], i, N, 64, 16, scale, m) for i in blocks]
+    assert all(len(got[i]) == m for i in blocks)
+    exempt = compare_micro_rows([got[i] for i in blocks], ora, Qt, Kt, [rows[i] for i in blocks],
+                                N, scale, m, blocks=blocks)
+    assert exempt <= 1
 
 
 def test_merge_kernel_on_oracle_inputs():
