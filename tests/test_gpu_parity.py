@@ -170,7 +170,8 @@ def test_static_select(grid, r, na, off):
 @pytest.mark.parametrize("grid,k,diag", [((3, 10, 640), 75, False), ((3, 10, 640), 400, True),
                                          ((7, 40, 160), 175, True), ((5, 50, 300), 293, False),
                                          ((5, 50, 512), 500, True), ((5, 64, 512), 384, False),
-                                         ((7, 64, 512), 540, True)])
+                                         ((7, 64, 512), 540, True), ((6, 50, 300), 300, False),
+                                         ((6, 64, 480), 700, True), ((8, 64, 512), 1000, False)])
 def test_topk_select_long_rows(grid, k, diag):
     spec = VideoSpec(1, 1, 64, grid, 108)
     say("topk long rows", grid, k, diag)
@@ -181,7 +182,9 @@ def test_topk_select_long_rows(grid, k, diag):
 
 
 @pytest.mark.parametrize("grid,p,kmin,kcap", [((7, 40, 160), 0.9, 1, 140), ((5, 50, 512), 0.9, 1, 400),
-                                               ((5, 50, 512), 0.5, 3, 2000), ((3, 10, 640), 0.99, 1, 60)])
+                                               ((5, 50, 512), 0.5, 3, 2000), ((3, 10, 640), 0.99, 1, 60),
+                                               ((6, 50, 350), 0.9, 1, 330), ((5, 50, 300), 0.8, 2, 240),
+                                               ((8, 64, 512), 0.9, 1, 820)])
 def test_topp_select_long_rows(grid, p, kmin, kcap):
     spec = VideoSpec(1, 1, 64, grid, 110)
     say("topp long rows", grid, p, kmin, kcap)
