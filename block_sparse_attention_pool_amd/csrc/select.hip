@@ -16,9 +16,10 @@
 // becomes its 2 x 2 tiles), through expand_bits_kernel.
 //
 // Micro rows (HyMoR-Attn Micro selection, 16-token tiles inside omitted
-// blocks): one workgroup per (b, micro head, query block); radix selection
-// of the top-m candidate scores with ties to the lower code, emitted in
-// (sub-tile, key tile) order.
+// blocks): one workgroup per (b, micro head, query block); the top-m
+// candidate scores by a value histogram and an exact ranking of the
+// threshold bin (a radix selection when that bin is too full), ties to the
+// lower code, emitted in (sub-tile, key tile) order.
 #include <climits>
 #include <type_traits>
 
