@@ -651,6 +651,19 @@ bsa_status bsa_select_blocks(const float* scores, const bsa_shape* shape, int32_
   a.n_col = p->n_columns;
   for (int t = 0; t < a.n_diag; ++t) a.diag[t] = p->diagonals[t];
   for (int t = 0; t < a.n_col; ++t) a.col[t] = p->columns[t];
+  // Plain top-k on 64-token blocks keeps exactly min(k, nB) blocks per row:
+  // the selection kernel writes the CSR directly (no count, scan or emit)
+  if (pl.block == 64 && p->mode == BSA_SELECT_TOPK && p->k > 0 && !p->force_diag &&
+      !p->use_static && p->n_diagonals == 0 && p->n_columns == 0) {
+    a.direct = std::min(p->k, (int)pl.nB);
+    a.rows = rows;
+    a.row_ptr = row_ptr;
+    a.col_idx = col_idx;
+    a.col_cap = col_cap;
+    a.out_nnz = out_nnz;
+    BSA_TRY(hip_status(bsa::launch_select(a, (int)pl.rows_sel, st), "select launch"));
+    return BSA_OK;
+  }
   BSA_TRY(hip_status(bsa::launch_select(a, (int)pl.rows_sel, st), "select launch"));
   const uint32_t* bits = a.bits;
   const int32_t* counts = a.counts;

@@ -53,6 +53,15 @@ struct SelectArgs {
   int n_diag, n_col;                 // MOD-DiT parallel-diagonal / vertical patterns
   int32_t diag[kMaxPatterns];        // offsets: key block i + diag[t]
   int32_t col[kMaxPatterns];         // key blocks
+  // direct > 0: every row holds exactly `direct` blocks (plain top-k on
+  // 64-token blocks), so the kernel writes the CSR itself: row r starts at
+  // r * direct, no bitmask, count or scan
+  int direct;
+  int rows;
+  int32_t* row_ptr;
+  int32_t* col_idx;
+  int64_t col_cap;
+  int64_t* out_nnz;
 };
 
 struct MicroSelectArgs {

@@ -244,6 +244,33 @@ __global__ __launch_bounds__(256) void select_wave_kernel(SelectArgs a, int rows
       if (lane == (2 * e + 1) % 64) word[e / 32] = (uint32_t)(m >> 32);
     }
   }
+  if (a.direct > 0) {
+    // ascending indices of the set bits: words 64q + lane, q = 0 then 1
+    const int64_t base = (int64_t)r * a.direct;
+    int before = 0;
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const int w = 64 * q + lane;
+      uint32_t v = w < a.W ? word[q] : 0u;
+      const int c = __popc(v);
+      const int incl = wave_inclusive_scan(c);
+      int64_t pos = base + before + incl - c;
+      before += __shfl(incl, 63);
+      while (v) {
+        if (pos < a.col_cap) a.col_idx[pos] = 32 * w + __ffs(v) - 1;
+        ++pos;
+        v &= v - 1;
+      }
+    }
+    if (lane == 0) {
+      a.row_ptr[r] = (int32_t)base;
+      if (r == rows - 1) {
+        a.row_ptr[rows] = (int32_t)((int64_t)rows * a.direct);
+        *a.out_nnz = (int64_t)rows * a.direct;
+      }
+    }
+    return;
+  }
   // Forced blocks, OR-ed word by word.  The window is an interval of key
   // blocks [ja, jb]: a block's first and last frames never decrease with its
   // index, so lo_j <= hi_i + r and hi_j >= lo_i - r each cut the row once.
