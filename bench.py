@@ -3,7 +3,7 @@
 
 One step = pooled scoring (bsa_score_blocks) + block selection
 (bsa_select_blocks) + block-sparse attention (bsa_sparse_attn_fwd) and its
-fp16 V^T staging (bsa_attn_stage_v, on a second stream beside scoring and
+fp16 V^T staging (bsa_attn_stage_v, on a second stream beside the
 selection; ``--serial`` keeps one stream), plus micro-tile selection, residual
 and LSE merge where the workload has them.  On small (launch-bound) layers
 the timed steps replay the step captured as a HIP graph, checked bit for bit
@@ -266,18 +266,20 @@ def build_workload(cfg, args, torch, bsa, keep_host=False):
     use_graph = (small or args.graph) and not args.no_graph
 
     def step(call=0, overlap=two_streams):
-        # The V^T staging runs on a second stream beside scoring and
-        # selection (running the micro branch beside the macro attention as
-        # well measured no gain: both fill the chip).
+        # The V^T staging runs on a second stream beside the selection, after
+        # the scoring: pooling and staging both stream their tensors from
+        # HBM, so running them together only shares the bandwidth, while the
+        # selection leaves it free (running the micro branch beside the macro
+        # attention as well measured no gain: both fill the chip).
         # fork from and join to the stream the step is issued on (the capture
         # stream while a graph is recorded)
         cur = torch.cuda.current_stream(dev)
+        # the static window needs no scores: the selection runs on the mask alone
+        sc = score() if (mode != "static" or micro) else {"scores": None}
         if overlap:
             aux.wait_stream(cur)
             with torch.cuda.stream(aux):
                 bsa.bsa_attn_stage_v(V, workspace=ws)
-        # the static window needs no scores: the selection runs on the mask alone
-        sc = score() if (mode != "static" or micro) else {"scores": None}
         rp, ci, nnz = select(sc, call)
         if overlap:
             cur.wait_stream(aux)
