@@ -11,9 +11,11 @@
 //           offsets, vertical key columns).
 // The row is built as a bitmask (one ballot per 64 key blocks), counted,
 // prefix-summed across rows into row_ptr, and emitted as ascending column
-// indices.  Blocks are 64 or 128 tokens; a 128-token selection is emitted
-// on the 64-token tiles the attention kernels run (each kept 128 x 128 pair
-// becomes its 2 x 2 tiles), through expand_bits_kernel.
+// indices; plain top-k rows, which all hold the same count, are emitted by
+// the selection kernel itself.  Blocks are 64 or 128 tokens; a 128-token
+// selection is emitted on the 64-token tiles the attention kernels run
+// (each kept 128 x 128 pair becomes its 2 x 2 tiles), through
+// expand_bits_kernel.
 //
 // Micro rows (HyMoR-Attn Micro selection, 16-token tiles inside omitted
 // blocks): one workgroup per (b, micro head, query block); the top-m
