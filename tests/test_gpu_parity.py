@@ -164,14 +164,33 @@ def test_static_select(grid, r, na, off):
         assert got[bh] == rows
 
 
-# Rows of 300, 700, 1172, 2000, 2560 and 3584 key blocks: the
-# one-wave-per-row selection with a partial last bitmask word (300 = 9 words
-# + 12 bits) and with 8, 16, 24, 32, 48 and 64 keys per lane.
+@pytest.mark.parametrize("mode,kw", [("topk", dict(k=3)), ("topk", dict(k=2, force_diag=True)),
+                                     ("topp", dict(p=0.8, k_min=1, k_cap=6))])
+def test_select_two_batches(mode, kw):
+    """B = 2: rows of both batches (plain top-k takes the direct CSR path,
+    the others the counted one)."""
+    spec = VideoSpec(2, 2, 64, (3, 9, 21), 119)
+    say("select two batches", mode, kw)
+    _, _, _, got, ora = _select_case(spec, mode, **kw)
+    assert len(ora) == 4
+    for bh, (S, rows) in ora.items():
+        if mode == "topk":
+            PT.compare_topk_rows(got[bh], rows, S, kw["k"],
+                                 forced_rows(spec.N, kw.get("force_diag", False), None))
+        else:
+            PT.compare_topp_rows(got[bh], rows, S, O.block_sizes(spec.N, 64), kw["p"],
+                                 kw["k_min"], kw["k_cap"])
+
+
+# Rows of 300 to 4096 key blocks: the one-wave-per-row selection with a
+# partial last bitmask word (300 = 9 words + 12 bits) and with 8, 12, 16,
+# 20, 24, 28, 32, 40, 48, 56 and 64 keys per lane.
 @pytest.mark.parametrize("grid,k,diag", [((3, 10, 640), 75, False), ((3, 10, 640), 400, True),
                                          ((7, 40, 160), 175, True), ((5, 50, 300), 293, False),
                                          ((5, 50, 512), 500, True), ((5, 64, 512), 384, False),
                                          ((7, 64, 512), 540, True), ((6, 50, 300), 300, False),
-                                         ((6, 64, 480), 700, True), ((8, 64, 512), 1000, False)])
+                                         ((6, 64, 480), 700, True), ((8, 64, 512), 1000, False),
+                                         ((4, 40, 380), 250, True)])
 def test_topk_select_long_rows(grid, k, diag):
     spec = VideoSpec(1, 1, 64, grid, 108)
     say("topk long rows", grid, k, diag)
@@ -389,6 +408,61 @@ def test_micro_select_attention_and_merge(grid, H, d, key, m):
     torch.cuda.synchronize()
     for h in heads:
         PT.compare_o_lse(Ob[0, h], Lb[0, h], refs[h][0], refs[h][1], f"merged h{h}")
+
+
+def test_micro_two_batches_head_subset():
+    """Micro selection, residual and merge with B = 2 and a head subset: the
+    (batch, micro head) slots of the tile-score product and of the lists
+    against the oracle, every row of both batches."""
+    spec = VideoSpec(2, 3, 64, (3, 8, 13), 118, spikes=True)
+    say("micro two batches", spec.grid)
+    Q, K, V = gen_qkv(spec)
+    Qd, Kd, Vd = to_dev(Q, K, V)
+    B, H, N, d = Q.shape
+    nB = O.n_blocks(N, 64)
+    scale = 1 / math.sqrt(d)
+    m = 12
+    heads = [0, 2]
+    mask = [h in heads for h in range(H)]
+    ora = oracle_rows_all(Q, K, spec, "topk", k=2, force_diag=True)
+    rp, ci = PT.rows_to_csr([ora[(b, h)][1][i] for b in range(B) for h in range(H)
+                             for i in range(nB)])
+    rp, ci = rp.to(DEV), ci.to(DEV)
+    sc = bsa.bsa_score_blocks(Qd, Kd, scores=False, micro=16)
+    mrp, mci, mnnz = bsa.bsa_select_blocks(
+        None, Qd, mode="micro",
+        micro=dict(m=m, scale=scale, head_mask=mask, macro=(rp, ci),
+                   qpool16=sc["qpool16"], kpool16=sc["kpool16"]))
+    torch.cuda.synchronize()
+    got = gpu_rows_by_head(mrp, mci, mnnz, B, H, nB)
+    mo = {}
+    for b in range(B):
+        for h in range(H):
+            if h not in heads:
+                assert all(len(r) == 0 for r in got[(b, h)])
+                continue
+            q, k = PT.head64(Q, b, h), PT.head64(K, b, h)
+            Qt, Kt = O.pool_means(q, 16), O.pool_means(k, 16)
+            rows = ora[(b, h)][1]
+            mo[(b, h)] = [O.micro_select_row(Qt, Kt, rows[i], i, N, 64, 16, scale, m)
+                          for i in range(nB)]
+            compare_micro_rows(got[(b, h)], mo[(b, h)], Qt, Kt, rows, N, scale, m)
+    # the residual on the oracle's lists, then the merge into the macro result
+    allm = [mo[(b, h)][i] if h in heads else [] for b in range(B) for h in range(H)
+            for i in range(nB)]
+    mrp_o, mci_o = PT.rows_to_csr(allm)
+    Om, Lm = bsa.bsa_micro_residual_fwd(Qd, Kd, Vd, mrp_o.to(DEV), mci_o.to(DEV), head_mask=mask)
+    Ob, Lb = bsa.bsa_sparse_attn_fwd(Qd, Kd, Vd, rp, ci)
+    bsa.bsa_lse_merge(Ob, Lb, Om, Lm, head_mask=mask, out=Ob, lse_out=Lb)
+    torch.cuda.synchronize()
+    for b in range(B):
+        for h in heads:
+            q, k, v = PT.head64(Q, b, h), PT.head64(K, b, h), PT.head64(V, b, h)
+            Ou, Lu = O.micro_attention(q, k, v, mo[(b, h)], 64, 16, scale)
+            PT.compare_o_lse(Om[b, h], Lm[b, h], Ou, Lu, f"micro b{b} h{h}")
+            Oa, La = O.block_sparse_attention(q, k, v, ora[(b, h)][1], 64, scale)
+            Or, Lr = O.lse_merge(Oa, La, Ou, Lu)
+            PT.compare_o_lse(Ob[b, h], Lb[b, h], Or, Lr, f"merged b{b} h{h}")
 
 
 def test_micro_select_rows_of_more_than_32768_candidates():
