@@ -108,8 +108,11 @@ constexpr int32_t kStatusBadIndex = 1;
 constexpr int kChunkShift = 24;
 constexpr int32_t kChunkMask = (1 << kChunkShift) - 1;
 
-// waves (query sub-tiles) per workgroup of the micro residual
-constexpr int kMicroWaves = 2;
+// waves (query sub-tiles) per workgroup of the micro residual: one, so that
+// a sub-tile that ends early frees its LDS slots at once (4.13-4.18 ms with
+// two per workgroup, 3.98-4.11 with one, 4.50-4.52 with four on the
+// HunyuanVideo micro heads, bit-identical)
+constexpr int kMicroWaves = 1;
 
 struct MicroAttnArgs {
   const uint16_t* Q;

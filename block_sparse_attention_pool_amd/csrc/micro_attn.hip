@@ -17,8 +17,8 @@ namespace bsa {
 // memory into one of two LDS slots of the wave (no registers, no barrier:
 // each wave owns its slots), so the copies of tiles e+1 and e+2 are in
 // flight while tile e is read from its slot and computed.  The kernel waits
-// on memory latency: two slots of 8 KB per wave and 32 KB per workgroup
-// leave room for ten waves per compute unit (20 tiles in flight); against
+// on memory latency: two slots of 8 KB per wave leave room for ten waves
+// per compute unit (20 tiles in flight); against
 // one tile prefetched in registers (12 waves) that took the HunyuanVideo
 // micro heads from 5.63 to 4.40 ms, bit-identical, while three slots per
 // wave (6 waves) gave 5.12 ms and four (5 waves) 6.25 ms.  The V^T rows are
